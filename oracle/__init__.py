@@ -1,0 +1,210 @@
+"""CPU oracle for SageAttention-style quantized attention (TEST INFRASTRUCTURE).
+
+Only ``tests/``, the package smoke check and the benchmark's CPU-baseline leg
+may import this module.  It shares no code with the HIP path; its arithmetic
+lives in ``oracle.c`` (see the header there for the passages each step
+follows), and this wrapper only marshals numpy arrays.
+
+Two modes:
+  * ``attn_emulate``: the quantisation scheme replayed step by step (K mean
+    smoothing, per-64-token INT8 Q/K, exact int32 scores, online exp2 softmax,
+    P rounded to FP16 or FP8-e4m3, fp64 accumulation);
+  * ``attn_exact``: softmax(sm_scale * Q K^T + mask) V in fp64.
+Both work on a caller-chosen subset of query rows, given as (b, h, i) triples.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+FP16, BF16, E4M3 = 0, 1, 2
+BLK = 64
+
+_f32p = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
+_f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
+_i8p = np.ctypeslib.ndpointer(np.int8, flags="C_CONTIGUOUS")
+_i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
+_i64p = np.ctypeslib.ndpointer(np.int64, flags="C_CONTIGUOUS")
+_L = ctypes.c_long
+
+
+def lib() -> ctypes.CDLL:
+    """Load liboracle.so, building it with gcc first if it is not there."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _build
+        _build.build()
+    L = ctypes.CDLL(_LIB_PATH)
+    L.orc_version.restype = ctypes.c_int
+    L.orc_threads.restype = ctypes.c_int
+    L.orc_round.restype = ctypes.c_double
+    L.orc_round.argtypes = [ctypes.c_double, ctypes.c_int, ctypes.c_int]
+    L.orc_round_array.argtypes = [_f64p, _L, ctypes.c_int, ctypes.c_int, _f64p]
+    L.orc_k_mean.argtypes = [_f32p, _L, _L, _L, _L, _f32p]
+    L.orc_quant_blocks.argtypes = [_f32p, ctypes.c_void_p, _L, _L, _L, _L, _i8p, _f32p]
+    L.orc_quant_v.argtypes = [_f32p, _L, _L, _L, _L, ctypes.c_int, _f32p, _f32p]
+    L.orc_scores_i32.argtypes = [_i8p, _i8p, _L, _L, _L, _L, _L, _L, _i64p, _L, _i32p]
+    L.orc_attn_emulate.argtypes = [_i8p, _f32p, _i8p, _f32p, _f32p, _f32p, ctypes.c_int, _L, _L, _L, _L, _L,
+                                   _L, ctypes.c_int, ctypes.c_double, _i64p, _L, _f64p]
+    L.orc_attn_exact.argtypes = [_f32p, _f32p, _f32p, _L, _L, _L, _L, _L, _L, ctypes.c_int, ctypes.c_double,
+                                 _i64p, _L, _f64p]
+    _lib = L
+    return L
+
+
+def threads() -> int:
+    return int(lib().orc_threads())
+
+
+# ----------------------------------------------------------------------------- helpers
+
+def to_hnd_f32(x, layout: str) -> np.ndarray:
+    """fp16/bf16 torch tensor in HND or NHD -> float32 numpy (B, H, N, D) (exact upcast)."""
+    a = x.float().cpu().numpy()
+    if layout == "NHD":
+        a = a.transpose(0, 2, 1, 3)
+    elif layout != "HND":
+        raise ValueError(layout)
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def round_to(x: np.ndarray, fmt: int, sat: bool = False) -> np.ndarray:
+    """Round reals to fp16 / bf16 / e4m3fn values (RNE); returns float64 values."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    lib().orc_round_array(x.reshape(-1), x.size, int(fmt), int(bool(sat)), out.reshape(-1))
+    return out
+
+
+def all_rows(B: int, H: int, N: int) -> np.ndarray:
+    b, h, i = np.meshgrid(np.arange(B), np.arange(H), np.arange(N), indexing="ij")
+    return np.ascontiguousarray(np.stack([b.ravel(), h.ravel(), i.ravel()], 1).astype(np.int64))
+
+
+def sample_rows(B: int, H: int, N: int, per_head: int = 64, seed: int = 0) -> np.ndarray:
+    """Per (b, h): first and last row of 8 evenly spaced 64-row blocks, the last
+    row of the sequence, plus seeded random rows, ``per_head`` rows in total."""
+    rng = np.random.default_rng(seed)
+    nblk = (N + BLK - 1) // BLK
+    out = []
+    for b in range(B):
+        for h in range(H):
+            sel = set()
+            for t in np.linspace(0, nblk - 1, num=min(8, nblk)).astype(int):
+                sel.add(int(t) * BLK)
+                sel.add(min(int(t) * BLK + BLK - 1, N - 1))
+            sel.add(N - 1)
+            while len(sel) < min(per_head, N):
+                sel.add(int(rng.integers(0, N)))
+            out.extend((b, h, i) for i in sorted(sel))
+    return np.asarray(out, dtype=np.int64)
+
+
+# ----------------------------------------------------------------------------- quantisation
+
+def k_mean(k: np.ndarray) -> np.ndarray:
+    B, H, N, D = k.shape
+    out = np.empty((B, H, D), np.float32)
+    lib().orc_k_mean(np.ascontiguousarray(k, np.float32), B, H, N, D, out)
+    return out
+
+
+def quant_blocks(x: np.ndarray, mean: Optional[np.ndarray] = None):
+    """Per-64-token INT8 quantisation; returns (int8 [B,H,N,D], scale [B,H,NB])."""
+    B, H, N, D = x.shape
+    nb = (N + BLK - 1) // BLK
+    xq = np.empty((B, H, N, D), np.int8)
+    sc = np.empty((B, H, nb), np.float32)
+    mp = None
+    if mean is not None:
+        mean = np.ascontiguousarray(mean, np.float32)
+        assert mean.shape == (B, H, D)
+        mp = mean.ctypes.data_as(ctypes.c_void_p)
+    lib().orc_quant_blocks(np.ascontiguousarray(x, np.float32), mp, B, H, N, D, xq, sc)
+    return xq, sc
+
+
+def quant_v(v: np.ndarray, pv_fp8: bool):
+    """V operand: (values float32 [B,H,N,D], vscale float32 [B,H,D] or None)."""
+    B, H, N, D = v.shape
+    vh = np.empty((B, H, N, D), np.float32)
+    vs = np.zeros((B, H, D), np.float32)
+    lib().orc_quant_v(np.ascontiguousarray(v, np.float32), B, H, N, D, int(bool(pv_fp8)), vh, vs)
+    return vh, (vs if pv_fp8 else None)
+
+
+@dataclasses.dataclass
+class Quantized:
+    q_i8: np.ndarray
+    q_scale: np.ndarray
+    k_i8: np.ndarray
+    k_scale: np.ndarray
+    k_mean: np.ndarray
+    v_hat: np.ndarray            # exact values of the fp16 / e4m3 codes, float32
+    v_scale: Optional[np.ndarray]
+    pv_fp8: bool
+    Hq: int
+    Hkv: int
+
+
+def quantize(q: np.ndarray, k: np.ndarray, v: np.ndarray, pv_fp8: bool) -> Quantized:
+    """q, k, v: float32 (B, H, N, D) arrays holding the exact fp16/bf16 inputs."""
+    mu = k_mean(k)
+    q8, sq = quant_blocks(q)
+    k8, sk = quant_blocks(k, mu)
+    vh, vs = quant_v(v, pv_fp8)
+    return Quantized(q8, sq, k8, sk, mu, vh, vs, bool(pv_fp8), q.shape[1], k.shape[1])
+
+
+def v_hat_bits(vals: np.ndarray, pv_fp8: bool) -> np.ndarray:
+    """Storage bits (uint8 e4m3fn or uint16 fp16) of exactly representable values."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(vals, np.float32))
+    if pv_fp8:
+        return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return t.to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+
+
+# ----------------------------------------------------------------------------- scores / attention
+
+def scores_i32(Q: Quantized, tiles: Sequence[Sequence[int]]) -> np.ndarray:
+    """INT32 score tiles [T, 64, 64] for (b, h, q_block, k_block) quadruples."""
+    B, Hq, Nq, D = Q.q_i8.shape
+    Nkv = Q.k_i8.shape[2]
+    t = np.ascontiguousarray(np.asarray(tiles, np.int64).reshape(-1, 4))
+    out = np.empty((t.shape[0], BLK, BLK), np.int32)
+    lib().orc_scores_i32(Q.q_i8, Q.k_i8, B, Hq, Q.Hkv, Nq, Nkv, D, t, t.shape[0], out)
+    return out
+
+
+def attn_emulate(Q: Quantized, causal: bool, sm_scale: float, rows: np.ndarray) -> np.ndarray:
+    B, Hq, Nq, D = Q.q_i8.shape
+    Nkv = Q.k_i8.shape[2]
+    rows = np.ascontiguousarray(rows, np.int64).reshape(-1, 3)
+    out = np.empty((rows.shape[0], D), np.float64)
+    vs = Q.v_scale if Q.v_scale is not None else np.zeros((B, Q.Hkv, D), np.float32)
+    lib().orc_attn_emulate(Q.q_i8, Q.q_scale, Q.k_i8, Q.k_scale, Q.v_hat, vs, int(Q.pv_fp8), B, Hq, Q.Hkv, Nq,
+                           Nkv, D, int(bool(causal)), float(sm_scale), rows, rows.shape[0], out)
+    return out
+
+
+def attn_exact(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, sm_scale: float,
+               rows: np.ndarray) -> np.ndarray:
+    B, Hq, Nq, D = q.shape
+    Hkv, Nkv = k.shape[1], k.shape[2]
+    rows = np.ascontiguousarray(rows, np.int64).reshape(-1, 3)
+    out = np.empty((rows.shape[0], D), np.float64)
+    lib().orc_attn_exact(np.ascontiguousarray(q, np.float32), np.ascontiguousarray(k, np.float32),
+                         np.ascontiguousarray(v, np.float32), B, Hq, Hkv, Nq, Nkv, D, int(bool(causal)),
+                         float(sm_scale), rows, rows.shape[0], out)
+    return out

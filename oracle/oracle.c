@@ -1,0 +1,359 @@
+/*
+ * oracle.c -- plain, slow CPU oracle for SageAttention-style quantized attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or load
+ * this file; only the tests, the package's smoke check and the benchmark's CPU
+ * baseline leg do.  It shares no code, header, table or constant with the HIP
+ * kernels.
+ *
+ * What it computes (sources: the SageAttention project README on the
+ * gittoolsai.com tool page, sections "Current Features", "How to Use",
+ * "Available APIs" and the note under "Speed of Kernels"; the qwbw.cn article
+ * "SageAttention one-line integration", its paragraphs on tensor layout, GQA,
+ * head-dim padding and sm_scale; the trdm.cn 9070XT build blog, section 2.2 on
+ * quantising QK^T and compensating the error):
+ *
+ *   exact mode      O = softmax(sm_scale * Q K^T + M) V in fp64, M = 0 or -inf
+ *                   (causal: key j visible to query i iff j <= i);
+ *   emulation mode  the quantisation scheme step by step:
+ *                   K mean smoothing -> INT8 Q / K per 64-token block ->
+ *                   exact int32 scores -> dequant -> online exp2 softmax over
+ *                   64-key blocks in ascending order -> P rounded to FP16 or
+ *                   FP8-e4m3 -> P.V accumulated in fp64 -> normalise.
+ *
+ * Every floating-point step whose rounding matters for a bit-exact comparison
+ * (the K mean, the fp32 subtract, the block scale, the reciprocal, the rounding
+ * to int8 / fp16 / e4m3) is spelt out below in the precision it is defined in.
+ * Build with -O2 -ffp-contract=off and without -ffast-math.
+ *
+ * Tensor convention here: every tensor is logical (B, H, N, D) row-major at the
+ * TRUE head dim D (no padding); callers convert layouts before calling.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define BLK 64 /* token block: one quantisation scale per 64 consecutive tokens */
+
+int orc_version(void) { return 1; }
+
+int orc_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ---------------------------------------------------------------------------
+ * Rounding of a real number to a small binary floating-point format with
+ * round-to-nearest, ties-to-even.  p = significand bits including the implicit
+ * one, emin = exponent of the smallest normal, maxv = largest finite value.
+ *   fp16      p=11 emin=-14  max 65504
+ *   bf16      p=8  emin=-126 max (2 - 2^-7) * 2^127
+ *   e4m3fn    p=4  emin=-6   max 448 (OCP FP8 E4M3, no infinities)
+ * With sat != 0 results beyond maxv clamp to +-maxv; otherwise they become
+ * +-inf (fp16/bf16) or NaN (e4m3fn has no infinity).
+ * ------------------------------------------------------------------------- */
+enum { ORC_FP16 = 0, ORC_BF16 = 1, ORC_E4M3 = 2 };
+
+static void fmt_params(int fmt, int* p, int* emin, double* maxv) {
+    switch (fmt) {
+    case ORC_FP16: *p = 11; *emin = -14; *maxv = 65504.0; break;
+    case ORC_BF16: *p = 8; *emin = -126; *maxv = ldexp(2.0 - ldexp(1.0, -7), 127); break;
+    default: *p = 4; *emin = -6; *maxv = 448.0; break;
+    }
+}
+
+double orc_round(double x, int fmt, int sat) {
+    int p, emin;
+    double maxv;
+    fmt_params(fmt, &p, &emin, &maxv);
+    if (isnan(x) || x == 0.0) return x;
+    if (isinf(x)) {
+        if (sat) return copysign(maxv, x);
+        return fmt == ORC_E4M3 ? NAN : x;
+    }
+    double ax = fabs(x);
+    int e2;
+    frexp(ax, &e2);         /* ax = f * 2^e2, f in [0.5, 1): leading bit has exponent e2 - 1 */
+    int ex = e2 - 1;
+    if (ex < emin) ex = emin; /* subnormal range: fixed quantum */
+    double quantum = ldexp(1.0, ex - (p - 1));
+    double r = nearbyint(ax / quantum) * quantum; /* division by a power of two is exact */
+    if (r > maxv) {
+        if (sat) r = maxv;
+        else return fmt == ORC_E4M3 ? NAN : copysign(INFINITY, x);
+    }
+    return copysign(r, x);
+}
+
+void orc_round_array(const double* x, long n, int fmt, int sat, double* out) {
+    for (long i = 0; i < n; i++) out[i] = orc_round(x[i], fmt, sat);
+}
+
+/* ---------------------------------------------------------------------------
+ * K channel mean (the smoothing of K).  For every (b, h, channel c):
+ *   part_j = sum over the tokens of 64-token block j, ascending, in fp64;
+ *   total  = sum of part_j over blocks, ascending, in fp64;
+ *   mean   = fp32(total / N)   (fp64 division, then one rounding to fp32).
+ * Subtracting a per-channel constant from every key leaves softmax(q.k) of each
+ * query unchanged, because q.mean is the same for all keys of that query.
+ * ------------------------------------------------------------------------- */
+void orc_k_mean(const float* k, long B, long H, long N, long D, float* mean) {
+    long nblk = (N + BLK - 1) / BLK;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (long b = 0; b < B; b++)
+        for (long h = 0; h < H; h++) {
+            const float* kb = k + (b * H + h) * N * D;
+            for (long c = 0; c < D; c++) {
+                double total = 0.0;
+                for (long j = 0; j < nblk; j++) {
+                    double part = 0.0;
+                    long t1 = (j + 1) * BLK < N ? (j + 1) * BLK : N;
+                    for (long t = j * BLK; t < t1; t++) part += (double)kb[t * D + c];
+                    total += part;
+                }
+                mean[(b * H + h) * D + c] = (float)(total / (double)N);
+            }
+        }
+}
+
+/* ---------------------------------------------------------------------------
+ * Per-block symmetric INT8 quantisation (one fp32 scale per 64 consecutive
+ * tokens of one (b, head), covering all D channels).  With mean != NULL the
+ * smoothed value y = fp32(x - mean[c]) is quantised instead of x.
+ *   amax  = max |y| over the block's real tokens and all channels (exact);
+ *   scale = fp32(amax / 127)       (IEEE fp32 division);
+ *   inv   = fp32(127 / amax)       (IEEE fp32 division);
+ *   q     = clamp(rne(fp32(y * inv)), -127, 127);
+ *   amax == 0  ->  scale = 0 and q = 0.
+ * ------------------------------------------------------------------------- */
+void orc_quant_blocks(const float* x, const float* mean, long B, long H, long N, long D,
+                      int8_t* xq, float* scale) {
+    long nblk = (N + BLK - 1) / BLK;
+#pragma omp parallel for collapse(3) schedule(static)
+    for (long b = 0; b < B; b++)
+        for (long h = 0; h < H; h++)
+            for (long j = 0; j < nblk; j++) {
+                const float* xb = x + (b * H + h) * N * D;
+                const float* mu = mean ? mean + (b * H + h) * D : NULL;
+                int8_t* qb = xq + (b * H + h) * N * D;
+                long t0 = j * BLK, t1 = (j + 1) * BLK < N ? (j + 1) * BLK : N;
+                float amax = 0.0f;
+                for (long t = t0; t < t1; t++)
+                    for (long c = 0; c < D; c++) {
+                        float y = mu ? xb[t * D + c] - mu[c] : xb[t * D + c];
+                        float a = fabsf(y);
+                        if (a > amax) amax = a;
+                    }
+                float* s = scale + (b * H + h) * nblk + j;
+                if (amax == 0.0f) {
+                    *s = 0.0f;
+                    for (long t = t0; t < t1; t++)
+                        for (long c = 0; c < D; c++) qb[t * D + c] = 0;
+                    continue;
+                }
+                *s = amax / 127.0f;
+                float inv = 127.0f / amax;
+                for (long t = t0; t < t1; t++)
+                    for (long c = 0; c < D; c++) {
+                        float y = mu ? xb[t * D + c] - mu[c] : xb[t * D + c];
+                        float r = rintf(y * inv);
+                        if (r > 127.0f) r = 127.0f;
+                        if (r < -127.0f) r = -127.0f;
+                        qb[t * D + c] = (int8_t)r;
+                    }
+            }
+}
+
+/* ---------------------------------------------------------------------------
+ * The P.V operand.
+ *  pv_fp8 == 0  (FP16 PV): vhat = fp16(v), round-to-nearest-even, saturating
+ *               to +-65504; no scale.
+ *  pv_fp8 == 1  (FP8 PV):  per (b, h, channel c) over all N tokens:
+ *               amax = max |v|; vscale = fp32(amax / 448); inv = fp32(448 / amax);
+ *               vhat = e4m3(fp32(v * inv)) with saturating round-to-nearest-even;
+ *               amax == 0 -> vscale = 0, vhat = 0.
+ * vhat is returned as the exact real value of each code (as float).
+ * ------------------------------------------------------------------------- */
+void orc_quant_v(const float* v, long B, long H, long N, long D, int pv_fp8, float* vhat, float* vscale) {
+#pragma omp parallel for collapse(2) schedule(static)
+    for (long b = 0; b < B; b++)
+        for (long h = 0; h < H; h++) {
+            const float* vb = v + (b * H + h) * N * D;
+            float* ob = vhat + (b * H + h) * N * D;
+            if (!pv_fp8) {
+                for (long i = 0; i < N * D; i++) ob[i] = (float)orc_round((double)vb[i], ORC_FP16, 1);
+                continue;
+            }
+            for (long c = 0; c < D; c++) {
+                float amax = 0.0f;
+                for (long t = 0; t < N; t++) {
+                    float a = fabsf(vb[t * D + c]);
+                    if (a > amax) amax = a;
+                }
+                float* s = vscale + (b * H + h) * D + c;
+                if (amax == 0.0f) {
+                    *s = 0.0f;
+                    for (long t = 0; t < N; t++) ob[t * D + c] = 0.0f;
+                    continue;
+                }
+                *s = amax / 448.0f;
+                float inv = 448.0f / amax;
+                for (long t = 0; t < N; t++) {
+                    float y = vb[t * D + c] * inv;
+                    ob[t * D + c] = (float)orc_round((double)y, ORC_E4M3, 1);
+                }
+            }
+        }
+}
+
+/* ---------------------------------------------------------------------------
+ * INT32 score tiles: out[t][i][j] = sum_c q8[b,h,64*qb+i,c] * k8[b,hk,64*kb+j,c]
+ * (exact integers), zero where the row or column lies beyond the sequence.
+ * tiles holds T quadruples (b, h, qb, kb); hk = h / (Hq / Hkv).
+ * ------------------------------------------------------------------------- */
+void orc_scores_i32(const int8_t* q8, const int8_t* k8, long B, long Hq, long Hkv, long Nq, long Nkv,
+                    long D, const int64_t* tiles, long T, int32_t* out) {
+    long group = Hq / Hkv;
+    (void)B;
+#pragma omp parallel for schedule(static)
+    for (long t = 0; t < T; t++) {
+        long b = tiles[4 * t], h = tiles[4 * t + 1], qb = tiles[4 * t + 2], kb = tiles[4 * t + 3];
+        long hk = h / group;
+        for (long i = 0; i < BLK; i++)
+            for (long j = 0; j < BLK; j++) {
+                long qi = qb * BLK + i, kj = kb * BLK + j;
+                int64_t s = 0;
+                if (qi < Nq && kj < Nkv)
+                    for (long c = 0; c < D; c++)
+                        s += (int64_t)q8[((b * Hq + h) * Nq + qi) * D + c] *
+                             (int64_t)k8[((b * Hkv + hk) * Nkv + kj) * D + c];
+                out[(t * BLK + i) * BLK + j] = (int32_t)s;
+            }
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Emulation-mode attention for selected query rows.  rows holds R triples
+ * (b, h, i); out is [R, D] in fp64 (before the cast to the output dtype).
+ * For each row, for each 64-key block in ascending order (blocks whose keys all
+ * lie beyond i are skipped when causal):
+ *   S32  = sum_c q8 * k8                                   (exact integer)
+ *   S2   = S32 * sq * sk * sm_scale * log2(e)              (fp64, left to right)
+ *   masked keys (causal j > i) get S2 = -inf
+ *   m'   = max(m, max_j S2);  alpha = 2^(m - m')  (0 when m = -inf)
+ *   p_j  = 2^(S2_j - m')
+ *   l    = alpha * l + sum_j p_j                           (unrounded p)
+ *   p^_j = fp16(p_j)  or  e4m3(p_j * 448)                   (RNE, saturating)
+ *   acc  = alpha * acc + sum_j p^_j * vhat_j                (fp64)
+ * Finally o = acc / l, times vscale[c] / 448 in FP8 mode.
+ * Both PV accumulation modes (single-level fp32 and two-level) are modelled by
+ * the same fp64 accumulation: they differ only in how the hardware rounds.
+ * ------------------------------------------------------------------------- */
+void orc_attn_emulate(const int8_t* q8, const float* sq, const int8_t* k8, const float* sk,
+                      const float* vhat, const float* vscale, int pv_fp8, long B, long Hq, long Hkv,
+                      long Nq, long Nkv, long D, int causal, double sm_scale, const int64_t* rows,
+                      long R, double* out) {
+    const double LOG2E = 1.4426950408889634074;
+    long group = Hq / Hkv;
+    long nqb = (Nq + BLK - 1) / BLK, nkb = (Nkv + BLK - 1) / BLK;
+    (void)B;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (long r = 0; r < R; r++) {
+        long b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+        long hk = h / group;
+        const int8_t* qrow = q8 + ((b * Hq + h) * Nq + i) * D;
+        double sqi = (double)sq[(b * Hq + h) * nqb + i / BLK];
+        double* acc = (double*)calloc((size_t)D, sizeof(double));
+        double s2[BLK], pj[BLK];
+        double m = -INFINITY, l = 0.0;
+        for (long kb = 0; kb < nkb; kb++) {
+            long j0 = kb * BLK;
+            if (causal && j0 > i) break;
+            long j1 = j0 + BLK < Nkv ? j0 + BLK : Nkv;
+            double skj = (double)sk[(b * Hkv + hk) * nkb + kb];
+            double bmax = -INFINITY;
+            for (long j = j0; j < j1; j++) {
+                if (causal && j > i) {
+                    s2[j - j0] = -INFINITY;
+                    continue;
+                }
+                const int8_t* krow = k8 + ((b * Hkv + hk) * Nkv + j) * D;
+                int64_t s32 = 0;
+                for (long c = 0; c < D; c++) s32 += (int64_t)qrow[c] * (int64_t)krow[c];
+                double v = (double)s32 * sqi * skj * sm_scale * LOG2E;
+                s2[j - j0] = v;
+                if (v > bmax) bmax = v;
+            }
+            double mnew = m > bmax ? m : bmax;
+            double alpha = (m == -INFINITY) ? 0.0 : exp2(m - mnew);
+            double psum = 0.0;
+            for (long j = j0; j < j1; j++) {
+                double p = (s2[j - j0] == -INFINITY) ? 0.0 : exp2(s2[j - j0] - mnew);
+                psum += p;
+                pj[j - j0] = pv_fp8 ? orc_round(p * 448.0, ORC_E4M3, 1) : orc_round(p, ORC_FP16, 1);
+            }
+            l = alpha * l + psum;
+            for (long c = 0; c < D; c++) {
+                double a = 0.0;
+                for (long j = j0; j < j1; j++) a += pj[j - j0] * (double)vhat[((b * Hkv + hk) * Nkv + j) * D + c];
+                acc[c] = alpha * acc[c] + a;
+            }
+            m = mnew;
+        }
+        for (long c = 0; c < D; c++) {
+            double o = acc[c] / l;
+            if (pv_fp8) o *= (double)vscale[(b * Hkv + hk) * D + c] / 448.0;
+            out[r * D + c] = o;
+        }
+        free(acc);
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Exact attention for selected rows, in fp64 from the exactly upcast inputs:
+ *   s_j = sm_scale * sum_c q_c k_jc  (-inf where masked),  w_j = exp(s_j - max s),
+ *   o   = sum_j w_j v_j / sum_j w_j.
+ * ------------------------------------------------------------------------- */
+void orc_attn_exact(const float* q, const float* k, const float* v, long B, long Hq, long Hkv, long Nq,
+                    long Nkv, long D, int causal, double sm_scale, const int64_t* rows, long R,
+                    double* out) {
+    long group = Hq / Hkv;
+    (void)B;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (long r = 0; r < R; r++) {
+        long b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+        long hk = h / group;
+        const float* qrow = q + ((b * Hq + h) * Nq + i) * D;
+        double* s = (double*)malloc((size_t)Nkv * sizeof(double));
+        double smax = -INFINITY;
+        for (long j = 0; j < Nkv; j++) {
+            if (causal && j > i) {
+                s[j] = -INFINITY;
+                continue;
+            }
+            const float* krow = k + ((b * Hkv + hk) * Nkv + j) * D;
+            double d = 0.0;
+            for (long c = 0; c < D; c++) d += (double)qrow[c] * (double)krow[c];
+            s[j] = sm_scale * d;
+            if (s[j] > smax) smax = s[j];
+        }
+        double wsum = 0.0;
+        for (long c = 0; c < D; c++) out[r * D + c] = 0.0;
+        for (long j = 0; j < Nkv; j++) {
+            if (s[j] == -INFINITY) continue;
+            double w = exp(s[j] - smax);
+            wsum += w;
+            const float* vrow = v + ((b * Hkv + hk) * Nkv + j) * D;
+            for (long c = 0; c < D; c++) out[r * D + c] += w * (double)vrow[c];
+        }
+        for (long c = 0; c < D; c++) out[r * D + c] /= wsum;
+        free(s);
+    }
+}

@@ -1,0 +1,158 @@
+/*
+ * sage.h -- C ABI of the MI355X (gfx950) SageAttention-style quantized attention forward.
+ *
+ * The operation: O = softmax(sm_scale * Q K^T [+ causal mask]) V, computed as
+ *   1. smoothing: subtract from K its per-channel mean over all tokens of each
+ *      (batch, kv-head) -- softmax is unchanged because q.mean is constant along a
+ *      row (SageAttention project README, "Current Features": INT8 quantization
+ *      and smoothing for QK^T);
+ *   2. INT8 quantisation of Q and of smoothed K, one fp32 scale per 64-token block
+ *      (same section; "varying granularities");
+ *   3. INT8 x INT8 -> INT32 scores on the matrix cores, dequantised with the two
+ *      block scales, online base-2 softmax over 64-key blocks;
+ *   4. P.V with P and V in FP16 or FP8-e4m3 (README "Current Features": FP8
+ *      quantization for PV; "Available APIs": the qk_int8_pv_fp16 / pv_fp8 kernels
+ *      and pv_accum_dtype), accumulated in fp32 or in two levels (README: two-level
+ *      accumulation strategy for PV);
+ * with q/k/v in FP16/BF16, tensor layout HND (batch, heads, seq, dim) or NHD
+ * (batch, seq, heads, dim), is_causal, sm_scale (SDPA semantics, default
+ * 1/sqrt(head_dim) -- qwbw.cn one-line integration article), grouped-query
+ * attention with num_qo_heads a multiple of num_kv_heads (same article), and head
+ * dims other than 64/128 zero-padded (same article, pad_qkv paragraph).
+ *
+ * Conventions for every call:
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates nothing, keeps no state between calls other than a per-device
+ *    architecture check, never synchronises the stream, and is re-entrant.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *    enqueued; asynchronous faults surface at the caller's next synchronisation.
+ *  - Arguments are validated before any HIP call: on error nothing is written and
+ *    no kernel is launched; sage_last_error_detail() explains the failure.
+ *  - Shapes: B batch, H_qo query heads, H_kv kv heads, Nq / Nkv sequence lengths,
+ *    D true head dim (1..128).  Dp = 64 if D <= 64 else 128 (the padded head dim),
+ *    NB(N) = ceil(N / 64), N_pad(N) = 64 * NB(N).  Query head h reads kv head
+ *    h / (H_qo / H_kv).
+ *  - Every padding element of an output buffer (tokens >= N, channels >= D) is
+ *    written with zero, so outputs are deterministic bytes.
+ *  - Layouts of the quantised intermediates (all row-major, innermost last):
+ *      q_i8     int8   [B][H_qo][N_pad(Nq)][Dp]
+ *      q_scale  float  [B][H_qo][NB(Nq)]
+ *      k_i8     int8   [B][H_kv][N_pad(Nkv)][Dp]      (smoothed K)
+ *      k_scale  float  [B][H_kv][NB(Nkv)]
+ *      k_mean   float  [B][H_kv][D]
+ *      v_hat    fp16 or e4m3 bytes [B][H_kv][NB(Nkv)][Dp][64]
+ *               (each 64-key block stored channel-major: element (c, t) of block
+ *               j holds token 64*j + t of channel c)
+ *      v_scale  float  [B][H_kv][Dp]                   (FP8 mode only)
+ */
+#ifndef SAGE_H_
+#define SAGE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SAGE_ABI_VERSION 1
+
+typedef enum sage_status {
+    SAGE_OK = 0,
+    SAGE_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad enum, H_qo % H_kv != 0, bad sm_scale */
+    SAGE_ERR_UNSUPPORTED = 2, /* D > 128, SAGE_ACC_FP16, causal with Nq != Nkv, size overflow */
+    SAGE_ERR_WORKSPACE = 3,   /* workspace pointer NULL or smaller than required */
+    SAGE_ERR_DEVICE = 4,      /* no HIP device, or the current device is not gfx950 */
+    SAGE_ERR_HIP = 5          /* a kernel launch failed (hipGetLastError) */
+} sage_status;
+
+typedef enum sage_dtype { SAGE_FP16 = 0, SAGE_BF16 = 1 } sage_dtype;
+typedef enum sage_layout { SAGE_HND = 0, SAGE_NHD = 1 } sage_layout;
+typedef enum sage_pv { SAGE_PV_FP16 = 0, SAGE_PV_FP8 = 1 } sage_pv;
+/* PV accumulation: fp32 single level; two-level (per-64-key-block fp32 partial sums
+ * added into the fp32 output accumulator -- the pages' "fp32+fp16" mode, whose
+ * fp16 inner accumulator is an fp32 one on gfx950 matrix cores); fp16 single level
+ * is not offered (the gfx950 FP16/FP8 matrix instructions accumulate in fp32). */
+typedef enum sage_accum { SAGE_ACC_FP32 = 0, SAGE_ACC_FP16_FP32 = 1, SAGE_ACC_FP16 = 2 } sage_accum;
+
+int sage_abi_version(void);
+const char* sage_status_string(sage_status s);
+/* Thread-local text describing the last failure of a call made on this thread. */
+const char* sage_last_error_detail(void);
+
+/* Dp for a head dim (64 or 128), 0 when D is outside 1..128. */
+int sage_padded_dim(int D);
+/* NB(N) = ceil(N / 64). */
+int sage_num_blocks(int N);
+
+/* Workspace of sage_quant_qk: fp64 per-block channel partial sums of K,
+ * B * H_kv * NB(Nkv) * D * 8 bytes.  0 for invalid sizes. */
+size_t sage_quant_qk_workspace_bytes(int B, int H_kv, int Nkv, int D);
+
+/*
+ * Smoothing + INT8 quantisation of Q and K (steps 1-2 above).
+ *   q: [B,H_qo,Nq,D] (HND) or [B,Nq,H_qo,D] (NHD), k likewise with H_kv, Nkv;
+ *      both fp16 or bf16 (`dtype`), contiguous.
+ *   K mean, per (b, kv head, channel c): fp64 sum over each 64-token block in
+ *   ascending token order, fp64 sum of those block sums in ascending block order,
+ *   fp64 division by Nkv, one rounding to fp32 -> k_mean.
+ *   Per 64-token block of Q, and of y = fp32(K - k_mean): amax = max|y| over the
+ *   block's real tokens and channels, scale = fp32(amax / 127), inv = fp32(127 /
+ *   amax), code = clamp(round_half_even(fp32(y * inv)), -127, 127); an all-zero
+ *   block gets scale 0 and codes 0.
+ *   Outputs: q_i8, q_scale, k_i8, k_scale, k_mean (layouts above).
+ *   workspace: device buffer of at least sage_quant_qk_workspace_bytes(...) bytes,
+ *   contents on entry ignored and on exit unspecified.
+ */
+sage_status sage_quant_qk(const void* q, const void* k, sage_dtype dtype, sage_layout layout, int B, int H_qo,
+                          int H_kv, int Nq, int Nkv, int D, int8_t* q_i8, float* q_scale, int8_t* k_i8,
+                          float* k_scale, float* k_mean, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace of sage_quant_v: B * H_kv * Dp * 4 bytes in FP8 mode (per-channel amax), 0 in FP16 mode. */
+size_t sage_quant_v_workspace_bytes(int B, int H_kv, int D, sage_pv pv);
+
+/*
+ * The P.V operand (step 4 above).
+ *   v: [B,H_kv,Nkv,D] (HND) or [B,Nkv,H_kv,D] (NHD), fp16 or bf16, contiguous.
+ *   SAGE_PV_FP16: v_hat = fp16(v) (round half even, saturating at +-65504);
+ *                 v_scale and workspace are ignored (may be NULL).
+ *   SAGE_PV_FP8:  per (b, kv head, channel c) over all Nkv tokens: amax = max|v|,
+ *                 v_scale = fp32(amax / 448), inv = fp32(448 / amax),
+ *                 v_hat = e4m3fn(fp32(v * inv)) (round half even, saturating at
+ *                 +-448); an all-zero channel gets scale 0 and codes 0.
+ *   v_hat layout above (2 bytes per element in FP16 mode, 1 in FP8 mode).
+ */
+sage_status sage_quant_v(const void* v, sage_dtype dtype, sage_layout layout, int B, int H_kv, int Nkv, int D,
+                         sage_pv pv, void* v_hat, float* v_scale, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * Attention on the quantised operands (step 3-4 above).
+ *   Reads q_i8/q_scale/k_i8/k_scale/v_hat/v_scale as produced by the two calls
+ *   above (v_scale only in FP8 mode, may be NULL otherwise).
+ *   out: [B,H_qo,Nq,D] (HND) or [B,Nq,H_qo,D] (NHD) in out_dtype; every element
+ *   is written.
+ *   is_causal: key j is visible to query i iff j <= i; requires Nq == Nkv.
+ *   sm_scale: finite and > 0 (callers pass 1/sqrt(D) for SDPA semantics).
+ *   accum: SAGE_ACC_FP32 or SAGE_ACC_FP16_FP32.
+ */
+sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                          const void* v_hat, const float* v_scale, void* out, sage_dtype out_dtype,
+                          sage_layout out_layout, int B, int H_qo, int H_kv, int Nq, int Nkv, int D, int is_causal,
+                          float sm_scale, sage_pv pv, sage_accum accum, void* stream);
+
+/*
+ * Debug dump of INT32 score tiles through the attention kernel's own operand
+ * path (LDS staging, MFMA operand order of the given PV mode).
+ *   tiles: device int32 [T][4] = (b, h_qo, q_block, k_block), each in range.
+ *   out:   device int32 [T][64][64]; out[t][i][j] = sum_c q_i8[b,h,64*qb+i,c] *
+ *          k_i8[b,h_kv,64*kb+j,c] (padding rows/columns give 0).
+ */
+sage_status sage_debug_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int B, int H_qo, int H_kv, int Nq, int Nkv,
+                                int D, sage_pv pv, const int32_t* tiles, int T, int32_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGE_H_ */

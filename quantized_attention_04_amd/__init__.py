@@ -1,0 +1,262 @@
+"""MI355X (gfx950) SageAttention-style quantized attention forward.
+
+Thin Python binding over the C-ABI library ``libsage.so`` (include/sage.h).  The
+binding only marshals arguments: every step of the computation runs in the HIP
+kernels.  PyTorch provides device memory and the current stream.
+
+Low level (same names as the C ABI; raw device pointers as ints):
+    sage_quant_qk, sage_quant_v, sage_attn_fwd, sage_debug_qk_int32, ...
+Tensor level:
+    quant_qk(q, k, layout) -> QKQuant
+    quant_v(v, layout, pv) -> VQuant
+    attn_fwd(qk, vq, ...) -> out
+    debug_qk_int32(qk, tiles, pv) -> int32 [T, 64, 64]
+    sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None,
+             pv="fp8", accum="fp32")   -- the composition of the three calls
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "SageError", "lib", "library_path", "QKQuant", "VQuant", "quant_qk", "quant_v", "attn_fwd", "debug_qk_int32",
+    "sageattn", "padded_dim", "num_blocks", "SAGE_OK", "SAGE_ERR_INVALID_ARG", "SAGE_ERR_UNSUPPORTED",
+    "SAGE_ERR_WORKSPACE", "SAGE_ERR_DEVICE", "SAGE_ERR_HIP",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libsage.so")
+
+SAGE_OK, SAGE_ERR_INVALID_ARG, SAGE_ERR_UNSUPPORTED, SAGE_ERR_WORKSPACE, SAGE_ERR_DEVICE, SAGE_ERR_HIP = range(6)
+SAGE_FP16, SAGE_BF16 = 0, 1
+SAGE_HND, SAGE_NHD = 0, 1
+SAGE_PV_FP16, SAGE_PV_FP8 = 0, 1
+SAGE_ACC_FP32, SAGE_ACC_FP16_FP32, SAGE_ACC_FP16 = 0, 1, 2
+
+_EXPORTS = {
+    # name: (restype, argtypes)
+    "sage_abi_version": (ctypes.c_int, []),
+    "sage_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "sage_last_error_detail": (ctypes.c_char_p, []),
+    "sage_padded_dim": (ctypes.c_int, [ctypes.c_int]),
+    "sage_num_blocks": (ctypes.c_int, [ctypes.c_int]),
+    "sage_quant_qk_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
+    "sage_quant_qk": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int] + [ctypes.c_int] * 6
+                      + [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "sage_quant_v_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
+    "sage_quant_v": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int] + [ctypes.c_int] * 5
+                     + [ctypes.c_void_p] * 3 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "sage_attn_fwd": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int, ctypes.c_int] + [ctypes.c_int] * 7
+                      + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+    "sage_debug_qk_int32": (ctypes.c_int, [ctypes.c_void_p] * 2 + [ctypes.c_int] * 7
+                            + [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]),
+}
+
+_lib = None
+
+
+class SageError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{_status_string(status)} -- {detail}")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsage.so.  Raises if it has not been built: there is no fallback path."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m quantized_attention_04_amd.build` "
+                          "(the HIP library is the only implementation)")
+    L = ctypes.CDLL(_LIB_PATH)
+    for name, (res, args) in _EXPORTS.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    if L.sage_abi_version() != 1:
+        raise ImportError("libsage ABI version mismatch")
+    _lib = L
+    return L
+
+
+def _status_string(s: int) -> str:
+    try:
+        return lib().sage_status_string(s).decode()
+    except Exception:  # pragma: no cover
+        return f"status {s}"
+
+
+def _check(status: int) -> None:
+    if status != SAGE_OK:
+        raise SageError(status, lib().sage_last_error_detail().decode())
+
+
+def padded_dim(D: int) -> int:
+    return int(lib().sage_padded_dim(D))
+
+
+def num_blocks(N: int) -> int:
+    return int(lib().sage_num_blocks(N))
+
+
+# ----------------------------------------------------------------------------- tensor helpers
+
+_DT = {torch.float16: SAGE_FP16, torch.bfloat16: SAGE_BF16}
+_LAYOUT = {"HND": SAGE_HND, "NHD": SAGE_NHD}
+_PV = {"fp16": SAGE_PV_FP16, "fp8": SAGE_PV_FP8}
+_ACC = {"fp32": SAGE_ACC_FP32, "fp16+fp32": SAGE_ACC_FP16_FP32, "fp32+fp16": SAGE_ACC_FP16_FP32,
+        "fp16": SAGE_ACC_FP16}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _dims(x: torch.Tensor, layout: str):
+    if x.dim() != 4:
+        raise ValueError(f"expected a 4-D tensor, got shape {tuple(x.shape)}")
+    if layout == "HND":
+        B, H, N, D = x.shape
+    elif layout == "NHD":
+        B, N, H, D = x.shape
+    else:
+        raise ValueError(f"tensor_layout must be 'HND' or 'NHD', got {layout!r}")
+    return B, H, N, D
+
+
+def _check_input(x: torch.Tensor, name: str) -> None:
+    if x.dtype not in _DT:
+        raise ValueError(f"{name}: dtype must be float16 or bfloat16, got {x.dtype}")
+    if not x.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor")
+    if not x.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+@dataclasses.dataclass
+class QKQuant:
+    q_i8: torch.Tensor      # int8 [B, Hq, N_pad(Nq), Dp]
+    q_scale: torch.Tensor   # f32  [B, Hq, NB(Nq)]
+    k_i8: torch.Tensor      # int8 [B, Hkv, N_pad(Nkv), Dp]
+    k_scale: torch.Tensor   # f32  [B, Hkv, NB(Nkv)]
+    k_mean: torch.Tensor    # f32  [B, Hkv, D]
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nkv: int
+    D: int
+
+
+@dataclasses.dataclass
+class VQuant:
+    v_hat: torch.Tensor               # uint8 [B, Hkv, NB, Dp, 64*elt] (fp16 or e4m3 bytes)
+    v_scale: Optional[torch.Tensor]   # f32 [B, Hkv, Dp] (FP8 only)
+    pv: str
+
+
+def quant_qk(q: torch.Tensor, k: torch.Tensor, layout: str = "HND", workspace: Optional[torch.Tensor] = None,
+             out: Optional[QKQuant] = None) -> QKQuant:
+    _check_input(q, "q")
+    _check_input(k, "k")
+    if q.dtype != k.dtype or q.device != k.device:
+        raise ValueError("q and k must share dtype and device")
+    B, Hq, Nq, D = _dims(q, layout)
+    Bk, Hkv, Nkv, Dk = _dims(k, layout)
+    if Bk != B or Dk != D:
+        raise ValueError("q and k disagree on batch or head_dim")
+    L = lib()
+    Dp, nbq, nbk = padded_dim(D), num_blocks(Nq), num_blocks(Nkv)
+    dev = q.device
+    if out is None:
+        out = QKQuant(torch.empty(B, Hq, nbq * 64, max(Dp, 1), dtype=torch.int8, device=dev),
+                      torch.empty(B, Hq, nbq, dtype=torch.float32, device=dev),
+                      torch.empty(B, Hkv, nbk * 64, max(Dp, 1), dtype=torch.int8, device=dev),
+                      torch.empty(B, Hkv, nbk, dtype=torch.float32, device=dev),
+                      torch.empty(B, Hkv, D, dtype=torch.float32, device=dev), B, Hq, Hkv, Nq, Nkv, D)
+    need = L.sage_quant_qk_workspace_bytes(B, Hkv, Nkv, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=dev)
+    _check(L.sage_quant_qk(q.data_ptr(), k.data_ptr(), _DT[q.dtype], _LAYOUT[layout], B, Hq, Hkv, Nq, Nkv, D,
+                           out.q_i8.data_ptr(), out.q_scale.data_ptr(), out.k_i8.data_ptr(), out.k_scale.data_ptr(),
+                           out.k_mean.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(dev)))
+    return out
+
+
+def quant_v(v: torch.Tensor, layout: str = "HND", pv: str = "fp8", workspace: Optional[torch.Tensor] = None,
+            out: Optional[VQuant] = None) -> VQuant:
+    _check_input(v, "v")
+    if pv not in _PV:
+        raise ValueError(f"pv must be 'fp16' or 'fp8', got {pv!r}")
+    B, Hkv, Nkv, D = _dims(v, layout)
+    L = lib()
+    Dp, nb = padded_dim(D), num_blocks(Nkv)
+    dev = v.device
+    elt = 1 if pv == "fp8" else 2
+    if out is None:
+        out = VQuant(torch.empty(B, Hkv, nb, max(Dp, 1), 64 * elt, dtype=torch.uint8, device=dev),
+                     torch.empty(B, Hkv, max(Dp, 1), dtype=torch.float32, device=dev) if pv == "fp8" else None, pv)
+    need = L.sage_quant_v_workspace_bytes(B, Hkv, D, _PV[pv])
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(L.sage_quant_v(v.data_ptr(), _DT[v.dtype], _LAYOUT[layout], B, Hkv, Nkv, D, _PV[pv], out.v_hat.data_ptr(),
+                          _ptr(out.v_scale), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                          _stream(dev)))
+    return out
+
+
+def attn_fwd(qk: QKQuant, vq: VQuant, out_dtype: torch.dtype, layout: str = "HND", is_causal: bool = False,
+             sm_scale: Optional[float] = None, accum: str = "fp32", out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    if out_dtype not in _DT:
+        raise ValueError("out_dtype must be float16 or bfloat16")
+    if accum not in _ACC:
+        raise ValueError(f"accum must be one of {sorted(_ACC)}, got {accum!r}")
+    B, Hq, Hkv, Nq, Nkv, D = qk.B, qk.Hq, qk.Hkv, qk.Nq, qk.Nkv, qk.D
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    dev = qk.q_i8.device
+    if out is None:
+        shape = (B, Hq, Nq, D) if layout == "HND" else (B, Nq, Hq, D)
+        out = torch.empty(shape, dtype=out_dtype, device=dev)
+    _check(lib().sage_attn_fwd(qk.q_i8.data_ptr(), qk.q_scale.data_ptr(), qk.k_i8.data_ptr(), qk.k_scale.data_ptr(),
+                               vq.v_hat.data_ptr(), _ptr(vq.v_scale), out.data_ptr(), _DT[out_dtype], _LAYOUT[layout],
+                               B, Hq, Hkv, Nq, Nkv, D, int(bool(is_causal)), float(sm_scale), _PV[vq.pv], _ACC[accum],
+                               _stream(dev)))
+    return out
+
+
+def debug_qk_int32(qk: QKQuant, tiles: torch.Tensor, pv: str = "fp8") -> torch.Tensor:
+    """INT32 score tiles through the attention kernel's operand path; tiles int32 [T, 4] on the GPU."""
+    tiles = tiles.to(torch.int32).contiguous()
+    T = tiles.shape[0]
+    out = torch.empty(T, 64, 64, dtype=torch.int32, device=qk.q_i8.device)
+    _check(lib().sage_debug_qk_int32(qk.q_i8.data_ptr(), qk.k_i8.data_ptr(), qk.B, qk.Hq, qk.Hkv, qk.Nq, qk.Nkv, qk.D,
+                                     _PV[pv], tiles.data_ptr(), T, out.data_ptr(), _stream(qk.q_i8.device)))
+    return out
+
+
+def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: str = "HND", is_causal: bool = False,
+             sm_scale: Optional[float] = None, pv: str = "fp8", accum: str = "fp32") -> torch.Tensor:
+    """softmax(sm_scale * q k^T [causal]) v with INT8 QK^T and FP8/FP16 PV; returns q's dtype and layout."""
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _check_input(x, name)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must share a dtype")
+    qk = quant_qk(q, k, tensor_layout)
+    vq = quant_v(v, tensor_layout, pv)
+    return attn_fwd(qk, vq, q.dtype, tensor_layout, is_causal, sm_scale, accum)

@@ -1,0 +1,215 @@
+// api.cpp -- the C ABI (include/sage.h): argument validation, device check, dispatch.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+#include <cmath>
+
+#include "../../include/sage.h"
+#include "internal.hpp"
+
+namespace {
+
+thread_local char g_detail[512] = "";
+
+sage_status fail(sage_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+sage_status ok() {
+    g_detail[0] = '\0';
+    return SAGE_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+sage_status check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return fail(SAGE_ERR_DEVICE, "no HIP device is available");
+    }
+    if (dev >= kMaxDevices) return fail(SAGE_ERR_DEVICE, "device index %d out of range", dev);
+    int st = g_arch[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(SAGE_ERR_DEVICE, "hipGetDeviceProperties failed for device %d", dev);
+        }
+        st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_arch[dev].store(st, std::memory_order_relaxed);
+        if (st != 1) return fail(SAGE_ERR_DEVICE, "device %d is %s, this library is built for gfx950 only", dev,
+                                 prop.gcnArchName);
+    }
+    if (st != 1) return fail(SAGE_ERR_DEVICE, "device %d is not gfx950", dev);
+    return SAGE_OK;
+}
+
+sage_status launch_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(SAGE_ERR_HIP, "%s: kernel launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int kMaxN = 1 << 28;     // tokens per sequence
+constexpr int kMaxGridYZ = 65535;  // batch and head grid dimensions
+
+// Shared shape checks.  Returns SAGE_OK or the failing status (with detail set).
+sage_status check_shape(int B, int Hq, int Hkv, int Nq, int Nkv, int D) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nkv <= 0 || D <= 0)
+        return fail(SAGE_ERR_INVALID_ARG, "sizes must be positive (B=%d H_qo=%d H_kv=%d Nq=%d Nkv=%d D=%d)", B, Hq,
+                    Hkv, Nq, Nkv, D);
+    if (Hq % Hkv != 0)
+        return fail(SAGE_ERR_INVALID_ARG, "num_qo_heads (%d) must be a multiple of num_kv_heads (%d)", Hq, Hkv);
+    if (D > 128) return fail(SAGE_ERR_UNSUPPORTED, "head_dim %d > 128 is not supported", D);
+    if (Nq > kMaxN || Nkv > kMaxN) return fail(SAGE_ERR_UNSUPPORTED, "sequence length above %d", kMaxN);
+    if (B > kMaxGridYZ || Hq > kMaxGridYZ) return fail(SAGE_ERR_UNSUPPORTED, "batch or head count above %d", kMaxGridYZ);
+    const double elems = double(B) * Hq * double(Nq > Nkv ? Nq : Nkv) * 128.0;
+    if (elems > 9.0e15) return fail(SAGE_ERR_UNSUPPORTED, "tensor too large");
+    return SAGE_OK;
+}
+
+int padded_dim(int D) { return D <= 0 || D > 128 ? 0 : (D <= 64 ? 64 : 128); }
+int nblocks(int N) { return N <= 0 ? 0 : (N + 63) / 64; }
+
+}  // namespace
+
+extern "C" {
+
+int sage_abi_version(void) { return SAGE_ABI_VERSION; }
+
+const char* sage_status_string(sage_status s) {
+    switch (s) {
+    case SAGE_OK: return "SAGE_OK";
+    case SAGE_ERR_INVALID_ARG: return "SAGE_ERR_INVALID_ARG: invalid argument";
+    case SAGE_ERR_UNSUPPORTED: return "SAGE_ERR_UNSUPPORTED: unsupported configuration";
+    case SAGE_ERR_WORKSPACE: return "SAGE_ERR_WORKSPACE: workspace missing or too small";
+    case SAGE_ERR_DEVICE: return "SAGE_ERR_DEVICE: no gfx950 device";
+    case SAGE_ERR_HIP: return "SAGE_ERR_HIP: HIP launch failure";
+    }
+    return "unknown sage_status";
+}
+
+const char* sage_last_error_detail(void) { return g_detail; }
+
+int sage_padded_dim(int D) { return padded_dim(D); }
+int sage_num_blocks(int N) { return nblocks(N); }
+
+size_t sage_quant_qk_workspace_bytes(int B, int H_kv, int Nkv, int D) {
+    if (B <= 0 || H_kv <= 0 || Nkv <= 0 || D <= 0 || D > 128) return 0;
+    return size_t(B) * size_t(H_kv) * size_t(nblocks(Nkv)) * size_t(D) * sizeof(double);
+}
+
+size_t sage_quant_v_workspace_bytes(int B, int H_kv, int D, sage_pv pv) {
+    if (B <= 0 || H_kv <= 0 || D <= 0 || D > 128) return 0;
+    if (pv != SAGE_PV_FP8) return 0;
+    return size_t(B) * size_t(H_kv) * size_t(padded_dim(D)) * sizeof(uint32_t);
+}
+
+sage_status sage_quant_qk(const void* q, const void* k, sage_dtype dtype, sage_layout layout, int B, int H_qo,
+                          int H_kv, int Nq, int Nkv, int D, int8_t* q_i8, float* q_scale, int8_t* k_i8,
+                          float* k_scale, float* k_mean, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!q || !k || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean)
+        return fail(SAGE_ERR_INVALID_ARG, "sage_quant_qk: null tensor pointer");
+    if (dtype != SAGE_FP16 && dtype != SAGE_BF16) return fail(SAGE_ERR_INVALID_ARG, "bad dtype %d", int(dtype));
+    if (layout != SAGE_HND && layout != SAGE_NHD) return fail(SAGE_ERR_INVALID_ARG, "bad layout %d", int(layout));
+    sage_status s = check_shape(B, H_qo, H_kv, Nq, Nkv, D);
+    if (s != SAGE_OK) return s;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_i8, 16) || !aligned(k_i8, 16) || !aligned(q_scale, 4) ||
+        !aligned(k_scale, 4) || !aligned(k_mean, 4))
+        return fail(SAGE_ERR_INVALID_ARG, "sage_quant_qk: tensors must be 16-byte aligned (scales 4-byte)");
+    const size_t need = sage_quant_qk_workspace_bytes(B, H_kv, Nkv, D);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 8))
+        return fail(SAGE_ERR_WORKSPACE, "sage_quant_qk: workspace of %zu bytes (8-byte aligned) required, got %zu",
+                    need, workspace ? workspace_bytes : size_t(0));
+    s = check_device();
+    if (s != SAGE_OK) return s;
+    sage::QuantQKArgs a{q, k, dtype == SAGE_BF16, layout == SAGE_NHD, B, H_qo, H_kv, Nq, Nkv, D,
+                        q_i8, q_scale, k_i8, k_scale, k_mean, workspace};
+    return launch_status(sage::launch_quant_qk(a, (hipStream_t)stream), "sage_quant_qk");
+}
+
+sage_status sage_quant_v(const void* v, sage_dtype dtype, sage_layout layout, int B, int H_kv, int Nkv, int D,
+                         sage_pv pv, void* v_hat, float* v_scale, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    if (!v || !v_hat) return fail(SAGE_ERR_INVALID_ARG, "sage_quant_v: null tensor pointer");
+    if (dtype != SAGE_FP16 && dtype != SAGE_BF16) return fail(SAGE_ERR_INVALID_ARG, "bad dtype %d", int(dtype));
+    if (layout != SAGE_HND && layout != SAGE_NHD) return fail(SAGE_ERR_INVALID_ARG, "bad layout %d", int(layout));
+    if (pv != SAGE_PV_FP16 && pv != SAGE_PV_FP8) return fail(SAGE_ERR_INVALID_ARG, "bad pv mode %d", int(pv));
+    sage_status s = check_shape(B, H_kv, H_kv, Nkv, Nkv, D);
+    if (s != SAGE_OK) return s;
+    if (!aligned(v, 16) || !aligned(v_hat, 16)) return fail(SAGE_ERR_INVALID_ARG, "sage_quant_v: tensors must be 16-byte aligned");
+    if (pv == SAGE_PV_FP8) {
+        if (!v_scale || !aligned(v_scale, 4)) return fail(SAGE_ERR_INVALID_ARG, "sage_quant_v: FP8 mode needs v_scale");
+        const size_t need = sage_quant_v_workspace_bytes(B, H_kv, D, pv);
+        if (!workspace || workspace_bytes < need || !aligned(workspace, 4))
+            return fail(SAGE_ERR_WORKSPACE, "sage_quant_v: workspace of %zu bytes required, got %zu", need,
+                        workspace ? workspace_bytes : size_t(0));
+    }
+    s = check_device();
+    if (s != SAGE_OK) return s;
+    sage::QuantVArgs a{v, dtype == SAGE_BF16, layout == SAGE_NHD, B, H_kv, Nkv, D, pv == SAGE_PV_FP8,
+                       v_hat, v_scale, workspace};
+    return launch_status(sage::launch_quant_v(a, (hipStream_t)stream), "sage_quant_v");
+}
+
+sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                          const void* v_hat, const float* v_scale, void* out, sage_dtype out_dtype,
+                          sage_layout out_layout, int B, int H_qo, int H_kv, int Nq, int Nkv, int D, int is_causal,
+                          float sm_scale, sage_pv pv, sage_accum accum, void* stream) {
+    if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v_hat || !out)
+        return fail(SAGE_ERR_INVALID_ARG, "sage_attn_fwd: null tensor pointer");
+    if (out_dtype != SAGE_FP16 && out_dtype != SAGE_BF16)
+        return fail(SAGE_ERR_INVALID_ARG, "bad out dtype %d", int(out_dtype));
+    if (out_layout != SAGE_HND && out_layout != SAGE_NHD)
+        return fail(SAGE_ERR_INVALID_ARG, "bad layout %d", int(out_layout));
+    if (pv != SAGE_PV_FP16 && pv != SAGE_PV_FP8) return fail(SAGE_ERR_INVALID_ARG, "bad pv mode %d", int(pv));
+    if (accum != SAGE_ACC_FP32 && accum != SAGE_ACC_FP16_FP32 && accum != SAGE_ACC_FP16)
+        return fail(SAGE_ERR_INVALID_ARG, "bad accum mode %d", int(accum));
+    if (is_causal != 0 && is_causal != 1) return fail(SAGE_ERR_INVALID_ARG, "is_causal must be 0 or 1");
+    if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
+        return fail(SAGE_ERR_INVALID_ARG, "sm_scale must be finite and > 0 (got %g)", double(sm_scale));
+    sage_status s = check_shape(B, H_qo, H_kv, Nq, Nkv, D);
+    if (s != SAGE_OK) return s;
+    if (accum == SAGE_ACC_FP16)
+        return fail(SAGE_ERR_UNSUPPORTED, "single-level fp16 PV accumulation is not offered: gfx950 matrix cores "
+                                          "accumulate FP16/FP8 products in fp32");
+    if (is_causal && Nq != Nkv) return fail(SAGE_ERR_UNSUPPORTED, "causal attention requires Nq == Nkv");
+    if (pv == SAGE_PV_FP8 && (!v_scale || !aligned(v_scale, 4)))
+        return fail(SAGE_ERR_INVALID_ARG, "sage_attn_fwd: FP8 mode needs v_scale");
+    if (!aligned(q_i8, 16) || !aligned(k_i8, 16) || !aligned(v_hat, 16) || !aligned(q_scale, 4) ||
+        !aligned(k_scale, 4) || !aligned(out, (D % 4) == 0 ? 8 : 2))
+        return fail(SAGE_ERR_INVALID_ARG, "sage_attn_fwd: misaligned tensor");
+    s = check_device();
+    if (s != SAGE_OK) return s;
+    sage::AttnArgs a{q_i8, q_scale, k_i8, k_scale, v_hat, v_scale, out, out_dtype == SAGE_BF16,
+                     out_layout == SAGE_NHD, B, H_qo, H_kv, Nq, Nkv, D, is_causal, sm_scale, pv == SAGE_PV_FP8,
+                     accum == SAGE_ACC_FP16_FP32};
+    return launch_status(sage::launch_attn_fwd(a, (hipStream_t)stream), "sage_attn_fwd");
+}
+
+sage_status sage_debug_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int B, int H_qo, int H_kv, int Nq, int Nkv,
+                                int D, sage_pv pv, const int32_t* tiles, int T, int32_t* out, void* stream) {
+    if (!q_i8 || !k_i8 || !tiles || !out) return fail(SAGE_ERR_INVALID_ARG, "sage_debug_qk_int32: null pointer");
+    if (pv != SAGE_PV_FP16 && pv != SAGE_PV_FP8) return fail(SAGE_ERR_INVALID_ARG, "bad pv mode %d", int(pv));
+    if (T <= 0) return fail(SAGE_ERR_INVALID_ARG, "tile count must be positive");
+    sage_status s = check_shape(B, H_qo, H_kv, Nq, Nkv, D);
+    if (s != SAGE_OK) return s;
+    if (!aligned(q_i8, 16) || !aligned(k_i8, 16) || !aligned(tiles, 4) || !aligned(out, 4))
+        return fail(SAGE_ERR_INVALID_ARG, "sage_debug_qk_int32: misaligned tensor");
+    s = check_device();
+    if (s != SAGE_OK) return s;
+    sage::DebugQKArgs a{q_i8, k_i8, B, H_qo, H_kv, Nq, Nkv, D, pv == SAGE_PV_FP8, tiles, T, out};
+    return launch_status(sage::launch_debug_qk(a, (hipStream_t)stream), "sage_debug_qk_int32");
+}
+
+}  // extern "C"

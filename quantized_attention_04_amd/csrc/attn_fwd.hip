@@ -1,0 +1,558 @@
+// attn_fwd.hip -- fused INT8-QK / FP16-or-FP8-PV attention forward for gfx950.
+//
+// Method (SageAttention project README, "Current Features" and "Available APIs";
+// trdm.cn 9070XT blog, section 2.2): scores S32 = Q^ K^T come from INT8 x INT8 -> INT32
+// matrix-core products, are dequantised with the per-64-token block scales of Q and
+// K, and feed an online base-2 softmax (running row max m, running row sum l); P is
+// rounded to FP16 or FP8-e4m3 and multiplied with V^ on the matrix cores with fp32
+// accumulation, either straight into the rescaled output accumulator or in two
+// levels (a fresh per-64-key-block partial added into it).
+//
+// gfx950 design:
+//  * workgroup = 4 waves = 256 queries; each wave owns 64 queries (one Q
+//    quantisation block, so the Q scale is wave-uniform) and loops over 64-key tiles
+//    (one K block, so the K scale is uniform too);
+//  * K^ and V^ tiles stream HBM -> LDS with direct-to-LDS 16-byte loads, double
+//    buffered, XOR-swizzled so that every 16-byte operand read is bank-conflict free;
+//  * S^T = K^ Q^T on v_mfma_i32_32x32x32_i8 (keys on the M side): each lane then holds
+//    whole query columns, so row max / row sum are lane-local plus one exchange
+//    between the two lane halves;
+//  * the K^ rows fed to each MFMA row are permuted so that the INT32 result lands in
+//    exactly the register order the P.V MFMA wants for its B operand: P never leaves
+//    registers; V^ tiles are stored channel-major so the A operand is contiguous;
+//  * P.V on v_mfma_scale_f32_32x32x64_f8f6f4 (FP8, unit scales) or
+//    v_mfma_f32_32x32x16_f16 (FP16), output O^T accumulated in fp32 registers.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace sage {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+// log2(448) = 8.8073549..., rounded down by ~1e-6 so that 2^(t + c) stays below 448
+// for t <= 0 even with a one-ulp exp2 error: FP8 P is produced directly as p * 448
+// (the e4m3 maximum), with a relative bias of about 6e-7.
+constexpr float kLog2_448 = 8.807354f;
+
+__device__ __forceinline__ int parity(uint32_t x) { return __builtin_popcount(x) & 1; }
+
+// Workgroup barrier without the memory fence of __syncthreads(): the fence would make
+// the compiler wait for every outstanding global load, including the prefetch of the
+// next tile.  LDS visibility is ensured by the explicit vmcnt waits before it; the
+// signal fences keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void block_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Mode constants.  DP = padded head dim (64 | 128); FP8 = P.V in e4m3 (else fp16).
+template <int DP, bool FP8>
+struct Cfg {
+    static constexpr int WAVES = 4;
+    static constexpr int THREADS = WAVES * kWave;
+    static constexpr int BM = WAVES * kBlk;  // queries per workgroup
+    static constexpr int VELT = FP8 ? 1 : 2;
+    static constexpr int KROW = DP;          // bytes per K^ row (one key)
+    static constexpr int VROW = kBlk * VELT; // bytes per V^ row (one channel of 64 keys)
+    static constexpr int KBYTES = kBlk * KROW;
+    static constexpr int VBYTES = DP * VROW;
+    static constexpr int STAGE = KBYTES + VBYTES;
+    static constexpr int KROUNDS = KBYTES / 16 / THREADS;
+    static constexpr int VROUNDS = VBYTES / 16 / THREADS;
+    static constexpr int LOADS = KROUNDS + VROUNDS;  // 16-byte loads per thread per tile
+    static constexpr int KS = DP / 32;               // MFMA k-steps of QK^T
+    static constexpr int DT = DP / 32;               // 32-channel tiles of O^T
+    // XOR swizzles: bit c of the chunk flip is parity(row & mask_c); each is
+    // conflict-free for the operand reads below with 8 lanes x 128 B or 16 lanes x
+    // 256 B served per LDS cycle.
+    static constexpr uint32_t KM0 = DP == 128 ? 0x2u : (FP8 ? 0x6u : 0x6u);
+    static constexpr uint32_t KM1 = DP == 128 ? 0x5u : (FP8 ? 0x20u : 0x8u);
+    static constexpr uint32_t KM2 = DP == 128 ? (FP8 ? 0x20u : 0x8u) : 0x0u;
+    static constexpr uint32_t VM0 = FP8 ? 0x4u : 0x2u;
+    static constexpr uint32_t VM1 = FP8 ? 0xAu : 0x4u;
+    static constexpr uint32_t VM2 = FP8 ? 0x0u : 0x9u;
+    static_assert(KROUNDS >= 1 && VROUNDS >= 1, "tile must cover the workgroup");
+};
+
+template <class C>
+__device__ __forceinline__ int kswz(int row) {
+    return parity(row & C::KM0) | (parity(row & C::KM1) << 1) | (parity(row & C::KM2) << 2);
+}
+template <class C>
+__device__ __forceinline__ int vswz(int row) {
+    return parity(row & C::VM0) | (parity(row & C::VM1) << 1) | (parity(row & C::VM2) << 2);
+}
+
+// Key (0..63 within a tile) whose K^ row feeds row i (0..31) of QK^T MFMA tile kt.
+// Chosen so that the C-layout of the result (lane half g, register r) equals the
+// B-operand layout of the P.V MFMA over keys:
+//   FP8:  lane half g holds keys 32g .. 32g+31 (tile kt: +16kt + r);
+//   FP16: MFMA m (16 keys) takes keys 16m + 8g + e from tile m/2, registers 8(m%2)+e.
+template <bool FP8>
+__device__ __forceinline__ int key_of_row(int kt, int i) {
+    const int a = i >> 3, g = (i >> 2) & 1, b = i & 3;
+    if constexpr (FP8) return 32 * g + 16 * kt + 4 * a + b;
+    else return 32 * kt + 16 * (a >> 1) + 8 * g + 4 * (a & 1) + b;
+}
+// Key held by lane half g, register r of result tile kt (C layout row 8(r/4)+4g+r%4).
+template <bool FP8>
+__device__ __forceinline__ int key_of_reg(int kt, int g, int r) {
+    return key_of_row<FP8>(kt, 8 * (r >> 2) + 4 * g + (r & 3));
+}
+
+// Direct-to-LDS loads of one K^ tile / one V^ tile into stage buffer `st`.  LDS chunk
+// (row, c) receives the global chunk (row, c ^ swizzle(row)).
+template <class C>
+__device__ __forceinline__ void issue_k_loads(uint8_t* __restrict__ st, const int8_t* ktile, int tid) {
+    const int wave = tid / kWave;
+#pragma unroll
+    for (int u = 0; u < C::KROUNDS; u++) {
+        const int ci = u * C::THREADS + tid;
+        const int row = ci / (C::KROW / 16), cpos = ci % (C::KROW / 16);
+        const int8_t* src = ktile + row * C::KROW + 16 * (cpos ^ kswz<C>(row));
+        load_lds_16(src, st + (u * C::THREADS + wave * kWave) * 16);
+    }
+}
+template <class C>
+__device__ __forceinline__ void issue_v_loads(uint8_t* __restrict__ st, const uint8_t* vtile, int tid) {
+    const int wave = tid / kWave;
+#pragma unroll
+    for (int u = 0; u < C::VROUNDS; u++) {
+        const int ci = u * C::THREADS + tid;
+        const int row = ci / (C::VROW / 16), cpos = ci % (C::VROW / 16);
+        const uint8_t* src = vtile + row * C::VROW + 16 * (cpos ^ vswz<C>(row));
+        load_lds_16(src, st + C::KBYTES + (u * C::THREADS + wave * kWave) * 16);
+    }
+}
+template <class C>
+__device__ __forceinline__ void issue_tile_loads(uint8_t* __restrict__ st, const int8_t* ktile, const uint8_t* vtile,
+                                                 int tid) {
+    issue_k_loads<C>(st, ktile, tid);
+    issue_v_loads<C>(st, vtile, tid);
+}
+
+__device__ __forceinline__ v16f fma16(v16f a, float s, v16f c) {
+    v16f r;
+#pragma unroll
+    for (int e = 0; e < 16; e++) r[e] = __builtin_fmaf(a[e], s, c[e]);
+    return r;
+}
+
+// S^T tiles of one 64-key tile for this wave's 64 queries: S[kt][nt] (keys 32kt.. on M
+// through the permutation above, queries 32nt + lane%32 on N).
+template <class C, bool FP8>
+__device__ __forceinline__ void qk_tile(const uint8_t* __restrict__ kst, const v4i (&qf)[2][C::KS], v16i (&S)[2][2],
+                                        int lane) {
+    const int i = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++) {
+        const int row = key_of_row<FP8>(kt, i);
+        const int sw = kswz<C>(row);
+        const uint8_t* rbase = kst + row * C::KROW;
+#pragma unroll
+        for (int s = 0; s < C::KS; s++) {
+            const v4i a = lds_read_16(rbase + 16 * ((2 * s + g) ^ sw));
+#pragma unroll
+            for (int nt = 0; nt < 2; nt++) {
+                if (s == 0) {
+                    const v16i z = {};
+                    S[kt][nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[nt][s], z, 0, 0, 0);
+                } else {
+                    S[kt][nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[nt][s], S[kt][nt], 0, 0, 0);
+                }
+            }
+        }
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void load_q_frags(v4i (&qf)[2][C::KS], const int8_t* qblk, int lane) {
+    const int i = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int nt = 0; nt < 2; nt++)
+#pragma unroll
+        for (int s = 0; s < C::KS; s++) qf[nt][s] = *(const v4i*)(qblk + (32 * nt + i) * C::KROW + 32 * s + 16 * g);
+}
+
+struct KParams {
+    const int8_t* q_i8;
+    const float* q_scale;
+    const int8_t* k_i8;
+    const float* k_scale;
+    const uint8_t* v_hat;
+    const float* v_scale;
+    void* out;
+    int64_t osb, osh, osq;  // output element strides (batch, head, token)
+    int B, Hq, Hkv, G, Nq, Nkv, D, NBq, NBk, QT;
+    float cscale;  // sm_scale * log2(e)
+};
+
+template <int DP, bool FP8, bool CAUSAL, bool TWO, bool OBF16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_fwd_kernel(KParams p) {
+    using C = Cfg<DP, FP8>;
+    // Two LDS stages as distinct objects, so that the compiler can tell the prefetch
+    // into one stage from the operand reads of the other.
+    __shared__ __attribute__((aligned(16))) uint8_t lds0[C::STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t lds1[C::STAGE];
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform (SGPR)
+    const int g = lane >> 5;
+
+    // ---- workgroup -> (b, h, q tile)
+    const int nwg = gridDim.x;
+    int b, h, qt;
+    {
+        int L, qtl;
+        if constexpr (CAUSAL) {
+            L = blockIdx.x;  // heaviest (last) query tiles first
+            const int per = p.B * p.Hq;
+            qtl = p.QT - 1 - L / per;
+            L = L % per;
+            const int hg = L % p.G, bhk = L / p.G;
+            b = bhk / p.Hkv;
+            h = (bhk % p.Hkv) * p.G + hg;
+        } else {
+            L = xcd_remap(blockIdx.x, nwg);  // one (b, kv head) per XCD run
+            const int hg = L % p.G;
+            qtl = (L / p.G) % p.QT;
+            const int bhk = L / (p.G * p.QT);
+            b = bhk / p.Hkv;
+            h = (bhk % p.Hkv) * p.G + hg;
+        }
+        qt = qtl;
+    }
+    const int hk = h / p.G;
+    const int q0 = qt * C::BM + wave * kBlk;  // this wave's first query
+    const bool active = q0 < p.Nq;
+    const int qb = q0 / kBlk;
+
+    const int64_t bhk = int64_t(b) * p.Hkv + hk;
+    const int8_t* kbase = p.k_i8 + bhk * int64_t(p.NBk) * kBlk * DP;
+    const uint8_t* vbase = p.v_hat + bhk * int64_t(p.NBk) * C::VBYTES;
+
+    int jend = p.NBk;
+    if constexpr (CAUSAL) jend = min(p.NBk, (min(qt * C::BM + C::BM, p.Nq) - 1) / kBlk + 1);
+    const bool ktail = (p.Nkv % kBlk) != 0;
+
+    // ---- per-wave state
+    v4i qf[2][C::KS];
+    float sq = 0.0f;
+    if (active) {
+        load_q_frags<C>(qf, p.q_i8 + ((int64_t(b) * p.Hq + h) * p.NBq * kBlk + q0) * DP, lane);
+        sq = scalar_load_f32(p.q_scale + (int64_t(b) * p.Hq + h) * p.NBq + qb);
+    } else {
+#pragma unroll
+        for (int nt = 0; nt < 2; nt++)
+#pragma unroll
+            for (int s = 0; s < C::KS; s++) qf[nt][s] = v4i{0, 0, 0, 0};
+    }
+    const float* ks_row = p.k_scale + bhk * p.NBk;
+    wait_vmcnt<0>();  // Q fragments resident before the tile pipeline starts
+    v16f O[C::DT][2];
+#pragma unroll
+    for (int dt = 0; dt < C::DT; dt++)
+#pragma unroll
+        for (int nt = 0; nt < 2; nt++) O[dt][nt] = v16f{};
+    float m[2] = {-1e30f, -1e30f}, l[2] = {0.0f, 0.0f};
+
+    auto compute = [&](const uint8_t* __restrict__ st, int j, float ksj) {
+        if (!active) return;
+        if (CAUSAL && j > qb) return;  // whole tile above this wave's diagonal
+        v16i S[2][2];
+        qk_tile<C, FP8>(st, qf, S, lane);
+        const float c = sq * ksj * p.cscale;
+        const bool need_mask = (CAUSAL && j == qb) || (ktail && j == p.NBk - 1);
+        float alpha[2];
+        float P[2][2][16];  // probabilities (FP8: p * 448)
+#pragma unroll
+        for (int nt = 0; nt < 2; nt++) {
+            const int qidx = q0 + 32 * nt + (lane & 31);
+            int imax = INT32_MIN;
+            if (need_mask) {
+#pragma unroll
+                for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) {
+                        const int key = j * kBlk + key_of_reg<FP8>(kt, g, r);
+                        const bool vis = key < p.Nkv && (!CAUSAL || key <= qidx);
+                        if (!vis) S[kt][nt][r] = INT32_MIN;
+                    }
+            }
+#pragma unroll
+            for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) imax = max(imax, S[kt][nt][r]);
+            float tmax = imax == INT32_MIN ? -1e30f : float(imax) * c;
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+            const float mnew = fmaxf(m[nt], tmax);
+            alpha[nt] = __builtin_amdgcn_exp2f(m[nt] - mnew);
+            m[nt] = mnew;
+            const float negm = FP8 ? kLog2_448 - mnew : -mnew;
+            float psum = 0.0f;
+#pragma unroll
+            for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(float(S[kt][nt][r]), c, negm));
+                    if (need_mask && S[kt][nt][r] == INT32_MIN) pv = 0.0f;
+                    P[nt][kt][r] = pv;
+                    psum += pv;
+                }
+            l[nt] = l[nt] * alpha[nt] + psum;
+        }
+        if constexpr (!TWO) {
+            // single level: rescale the accumulator only when some row max moved
+            if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.0f || alpha[1] != 1.0f)) {
+#pragma unroll
+                for (int dt = 0; dt < C::DT; dt++)
+#pragma unroll
+                    for (int nt = 0; nt < 2; nt++) O[dt][nt] *= alpha[nt];
+            }
+        }
+        const uint8_t* vst = st + C::KBYTES;
+        const int i = lane & 31;
+        if constexpr (FP8) {
+            v8i pb[2];
+#pragma unroll
+            for (int nt = 0; nt < 2; nt++)
+#pragma unroll
+                for (int w = 0; w < 8; w++) {
+                    const float* pp = &P[nt][w >> 2][4 * (w & 3)];
+                    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(pp[0], pp[1], 0, false);
+                    pb[nt][w] = __builtin_amdgcn_cvt_pk_fp8_f32(pp[2], pp[3], lo, true);
+                }
+#pragma unroll
+            for (int dt = 0; dt < C::DT; dt++) {
+                const int d = 32 * dt + i;
+                const int sw = vswz<C>(d);
+                const uint8_t* rb = vst + d * C::VROW;
+                const v4i a0 = lds_read_16(rb + 16 * ((2 * g) ^ sw));
+                const v4i a1 = lds_read_16(rb + 16 * ((2 * g + 1) ^ sw));
+                const v8i a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+#pragma unroll
+                for (int nt = 0; nt < 2; nt++) {
+                    if constexpr (TWO) {
+                        const v16f z = {};
+                        const v16f part =
+                            __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb[nt], z, 0, 0, 0, 127, 0, 127);
+                        O[dt][nt] = fma16(O[dt][nt], alpha[nt], part);
+                    } else {
+                        O[dt][nt] =
+                            __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb[nt], O[dt][nt], 0, 0, 0, 127, 0, 127);
+                    }
+                }
+            }
+        } else {
+            v8h ph[2][4];
+#pragma unroll
+            for (int nt = 0; nt < 2; nt++)
+#pragma unroll
+                for (int mm = 0; mm < 4; mm++)
+#pragma unroll
+                    for (int e = 0; e < 8; e++) ph[nt][mm][e] = (_Float16)P[nt][mm >> 1][8 * (mm & 1) + e];
+#pragma unroll
+            for (int dt = 0; dt < C::DT; dt++) {
+                const int d = 32 * dt + i;
+                const int sw = vswz<C>(d);
+                const uint8_t* rb = vst + d * C::VROW;
+                v16f part[2];
+                if constexpr (TWO) part[0] = part[1] = v16f{};
+#pragma unroll
+                for (int mm = 0; mm < 4; mm++) {
+                    const v4i araw = lds_read_16(rb + 16 * ((2 * mm + g) ^ sw));
+                    v8h a;
+                    __builtin_memcpy(&a, &araw, 16);
+#pragma unroll
+                    for (int nt = 0; nt < 2; nt++) {
+                        if constexpr (TWO)
+                            part[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, ph[nt][mm], part[nt], 0, 0, 0);
+                        else
+                            O[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, ph[nt][mm], O[dt][nt], 0, 0, 0);
+                    }
+                }
+                if constexpr (TWO) {
+#pragma unroll
+                    for (int nt = 0; nt < 2; nt++) O[dt][nt] = fma16(O[dt][nt], alpha[nt], part[nt]);
+                }
+            }
+        }
+    };
+
+    // ---- main loop: two LDS stages, ping-pong.  Each wave waits for its own
+    // direct-to-LDS loads of the current tile (vmcnt: all but the LOADS most recent
+    // ones, i.e. the prefetch of the next tile, are complete), then a bare barrier
+    // publishes the tile; a second barrier retires the stage before it is refilled.
+    issue_tile_loads<C>(lds0, kbase, vbase, tid);
+    for (int j = 0; j < jend; j += 2) {
+        if (j + 1 < jend) {
+            issue_tile_loads<C>(lds1, kbase + int64_t(j + 1) * kBlk * DP, vbase + int64_t(j + 1) * C::VBYTES, tid);
+            wait_vmcnt<C::LOADS>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        block_barrier();
+        compute(lds0, j, scalar_load_f32(ks_row + j));
+        block_barrier();
+        if (j + 1 >= jend) break;
+        if (j + 2 < jend) {
+            issue_tile_loads<C>(lds0, kbase + int64_t(j + 2) * kBlk * DP, vbase + int64_t(j + 2) * C::VBYTES, tid);
+            wait_vmcnt<C::LOADS>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        block_barrier();
+        compute(lds1, j + 1, scalar_load_f32(ks_row + j + 1));
+        block_barrier();
+    }
+
+    // ---- epilogue: O^T / l (x v_scale in FP8 mode) -> out dtype, input layout
+    if (!active) return;
+    const int i = lane & 31;
+    const float* vsc = FP8 ? p.v_scale + bhk * DP : nullptr;
+    const bool vec4 = (p.D & 3) == 0;
+#pragma unroll
+    for (int nt = 0; nt < 2; nt++) {
+        const float ltot = l[nt] + __shfl_xor(l[nt], 32, 64);
+        const float inv = 1.0f / ltot;
+        const int q = q0 + 32 * nt + i;
+        if (q >= p.Nq) continue;
+        uint16_t* orow = (uint16_t*)p.out + b * p.osb + h * p.osh + q * p.osq;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; dt++)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; a4++) {
+                const int d0 = 32 * dt + 8 * a4 + 4 * g;
+                if (d0 >= p.D) continue;
+                uint16_t hv[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    float o = O[dt][nt][4 * a4 + e] * inv;
+                    if constexpr (FP8) o *= vsc[d0 + e];
+                    hv[e] = OBF16 ? f32_to_bf16_bits(o) : f32_to_f16_bits(o);
+                }
+                if (vec4) {
+                    *(uint2*)(orow + d0) = make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16),
+                                                      uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        if (d0 + e < p.D) orow[d0 + e] = hv[e];
+                }
+            }
+    }
+}
+
+// ---- debug dump of INT32 score tiles through the same loader / operand path ----------
+template <int DP, bool FP8>
+__global__ __launch_bounds__(256) void debug_qk_kernel(const int8_t* __restrict__ q_i8,
+                                                       const int8_t* __restrict__ k_i8, int B, int Hq, int Hkv,
+                                                       int NBq, int NBk, const int32_t* __restrict__ tiles,
+                                                       int32_t* __restrict__ out) {
+    using C = Cfg<DP, FP8>;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[C::STAGE];
+    const int t = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int b = tiles[4 * t], h = tiles[4 * t + 1], qb = tiles[4 * t + 2], kb = tiles[4 * t + 3];
+    int32_t* o = out + int64_t(t) * kBlk * kBlk;
+    const bool ok = b >= 0 && b < B && h >= 0 && h < Hq && qb >= 0 && qb < NBq && kb >= 0 && kb < NBk;
+    if (!ok) {  // out-of-range tuple: fill with INT32_MIN, touch nothing else
+        for (int e = tid; e < kBlk * kBlk; e += C::THREADS) o[e] = INT32_MIN;
+        return;
+    }
+    const int hk = h / (Hq / Hkv);
+    const int8_t* ktile = k_i8 + ((int64_t(b) * Hkv + hk) * NBk + kb) * kBlk * DP;
+    issue_k_loads<C>(smem, ktile, tid);
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (wave != 0) return;
+    v4i qf[2][C::KS];
+    load_q_frags<C>(qf, q_i8 + ((int64_t(b) * Hq + h) * NBq + qb) * kBlk * DP, lane);
+    v16i S[2][2];
+    qk_tile<C, FP8>(smem, qf, S, lane);
+    const int g = lane >> 5, i = lane & 31;
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+        for (int nt = 0; nt < 2; nt++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) o[(32 * nt + i) * kBlk + key_of_reg<FP8>(kt, g, r)] = S[kt][nt][r];
+}
+
+template <int DP, bool FP8, bool CAUSAL, bool TWO, bool OBF16>
+hipError_t launch_attn_t(const KParams& p, int nwg, hipStream_t s) {
+    using C = Cfg<DP, FP8>;
+    auto kern = attn_fwd_kernel<DP, FP8, CAUSAL, TWO, OBF16>;
+    hipLaunchKernelGGL(kern, dim3(nwg), dim3(C::THREADS), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int DP, bool FP8>
+hipError_t dispatch_rest(const AttnArgs& a, const KParams& p, int nwg, hipStream_t s) {
+    const int key = (a.causal ? 4 : 0) | (a.two_level ? 2 : 0) | (a.out_bf16 ? 1 : 0);
+    switch (key) {
+    case 0: return launch_attn_t<DP, FP8, false, false, false>(p, nwg, s);
+    case 1: return launch_attn_t<DP, FP8, false, false, true>(p, nwg, s);
+    case 2: return launch_attn_t<DP, FP8, false, true, false>(p, nwg, s);
+    case 3: return launch_attn_t<DP, FP8, false, true, true>(p, nwg, s);
+    case 4: return launch_attn_t<DP, FP8, true, false, false>(p, nwg, s);
+    case 5: return launch_attn_t<DP, FP8, true, false, true>(p, nwg, s);
+    case 6: return launch_attn_t<DP, FP8, true, true, false>(p, nwg, s);
+    default: return launch_attn_t<DP, FP8, true, true, true>(p, nwg, s);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s) {
+    KParams p;
+    p.q_i8 = a.q_i8;
+    p.q_scale = a.q_scale;
+    p.k_i8 = a.k_i8;
+    p.k_scale = a.k_scale;
+    p.v_hat = (const uint8_t*)a.v_hat;
+    p.v_scale = a.v_scale;
+    p.out = a.out;
+    p.B = a.B;
+    p.Hq = a.Hq;
+    p.Hkv = a.Hkv;
+    p.G = a.Hq / a.Hkv;
+    p.Nq = a.Nq;
+    p.Nkv = a.Nkv;
+    p.D = a.D;
+    p.NBq = (a.Nq + kBlk - 1) / kBlk;
+    p.NBk = (a.Nkv + kBlk - 1) / kBlk;
+    const int BM = 4 * kBlk;
+    p.QT = (a.Nq + BM - 1) / BM;
+    p.cscale = a.sm_scale * kLog2e;
+    if (a.out_nhd) {
+        p.osb = int64_t(a.Nq) * a.Hq * a.D;
+        p.osh = a.D;
+        p.osq = int64_t(a.Hq) * a.D;
+    } else {
+        p.osb = int64_t(a.Hq) * a.Nq * a.D;
+        p.osh = int64_t(a.Nq) * a.D;
+        p.osq = a.D;
+    }
+    const int nwg = a.B * a.Hq * p.QT;
+    const bool dp64 = a.D <= 64;
+    if (dp64) return a.fp8 ? dispatch_rest<64, true>(a, p, nwg, s) : dispatch_rest<64, false>(a, p, nwg, s);
+    return a.fp8 ? dispatch_rest<128, true>(a, p, nwg, s) : dispatch_rest<128, false>(a, p, nwg, s);
+}
+
+template <int DP, bool FP8>
+hipError_t launch_debug_t(const DebugQKArgs& a, int NBq, int NBk, hipStream_t s) {
+    using C = Cfg<DP, FP8>;
+    auto kern = debug_qk_kernel<DP, FP8>;
+    hipLaunchKernelGGL(kern, dim3(a.T), dim3(C::THREADS), 0, s, a.q_i8, a.k_i8, a.B, a.Hq, a.Hkv, NBq, NBk,
+                       a.tiles, a.out);
+    return hipGetLastError();
+}
+
+hipError_t launch_debug_qk(const DebugQKArgs& a, hipStream_t s) {
+    const int NBq = (a.Nq + kBlk - 1) / kBlk, NBk = (a.Nkv + kBlk - 1) / kBlk;
+    if (a.D <= 64) return a.fp8 ? launch_debug_t<64, true>(a, NBq, NBk, s) : launch_debug_t<64, false>(a, NBq, NBk, s);
+    return a.fp8 ? launch_debug_t<128, true>(a, NBq, NBk, s) : launch_debug_t<128, false>(a, NBq, NBk, s);
+}
+
+}  // namespace sage

@@ -1,0 +1,96 @@
+// common.hpp -- shared device helpers for the gfx950 kernels (internal header).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sage {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef unsigned short v8u16 __attribute__((ext_vector_type(8)));
+
+constexpr int kBlk = 64;  // tokens per quantisation block and per KV tile
+constexpr int kWave = 64;
+
+// ---- element conversions -------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
+    _Float16 h;
+    __builtin_memcpy(&h, &b, 2);
+    return float(h);
+}
+template <bool BF16>
+__device__ __forceinline__ float in_to_f32(uint16_t b) {
+    if constexpr (BF16) return bf16_bits_to_f32(b);
+    else return f16_bits_to_f32(b);
+}
+// float -> bf16 bits, round half to even (finite inputs)
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+    uint32_t u = __float_as_uint(x);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return uint16_t(u >> 16);
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+    _Float16 h = (_Float16)x;
+    uint16_t b;
+    __builtin_memcpy(&b, &h, 2);
+    return b;
+}
+
+// ---- wave reductions --------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// ---- waits --------------------------------------------------------------------------
+// s_waitcnt vmcnt(n) with the other counters left at their maximum (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// ---- direct global -> LDS copy of 16 bytes per lane ----------------------------------
+// The LDS destination of lane i is lds_base + 16 * i (lds_base is wave-uniform).  Issued
+// as inline asm: the instruction writes no VGPR, and keeping it opaque stops the
+// compiler from guarding every later LDS read with a wait for ALL outstanding loads
+// (it cannot tell a prefetch into one LDS stage from reads of the other).  Callers
+// order it with explicit vmcnt waits and barriers.  Loads complete in issue order.
+__device__ __forceinline__ void load_lds_16(const void* gptr, void* lds_base) {
+    const uint32_t lds =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
+}
+
+__device__ __forceinline__ v4i lds_read_16(const void* p) { return *(const v4i*)p; }
+
+// Scalar (SMEM) load of a wave-uniform float: counted by lgkmcnt, so it never waits on
+// (or forces the completion of) outstanding vector-memory prefetches.
+__device__ __forceinline__ float scalar_load_f32(const float* p) {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const __attribute__((address_space(4))) float* c =
+        (const __attribute__((address_space(4))) float*)(((uint64_t)hi << 32) | lo);
+    return *c;
+}
+
+// XCD-aware remap: consecutive logical ids land on the same XCD (the hardware hands
+// workgroup i to XCD i % 8), so workgroups that share K/V tiles share an L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+    constexpr int kXcd = 8;
+    int xcd = bid % kXcd, idx = bid / kXcd;
+    int per = nblocks / kXcd, rem = nblocks % kXcd;
+    return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+}
+
+}  // namespace sage

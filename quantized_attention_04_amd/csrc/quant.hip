@@ -1,0 +1,322 @@
+// quant.hip -- smoothing and quantisation kernels for gfx950 (HBM-bound).
+//
+// K mean (the smoothing of K): fp64 per-64-token-block channel sums, then an ordered
+// fp64 sum over blocks; INT8 block quantisation of Q and smoothed K; the P.V operand
+// V^ in FP16 or FP8-e4m3 with per-channel scales.  The arithmetic of each step is the
+// one stated in include/sage.h (SageAttention project README, "Current Features":
+// INT8 quantization and smoothing for QK^T, FP8 quantization for PV).
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace sage {
+
+struct Strides {
+    int64_t b, h, t;  // element strides of batch, head, token (channel stride is 1)
+};
+
+__host__ __device__ inline Strides make_strides(int layout_nhd, int H, int N, int D) {
+    Strides s;
+    if (layout_nhd) {
+        s.b = int64_t(N) * H * D;
+        s.h = D;
+        s.t = int64_t(H) * D;
+    } else {
+        s.b = int64_t(H) * N * D;
+        s.h = int64_t(N) * D;
+        s.t = D;
+    }
+    return s;
+}
+
+// ------------------------------------------------------------------------------------------
+// K mean, pass 1: part[b][h][j][c] = sum of K[b,h,t,c] over the tokens t of block j,
+// ascending, in fp64.  grid (NB, H, B), block 128 threads, thread = channel.
+template <bool BF16>
+__global__ __launch_bounds__(128) void k_mean_partial_kernel(const uint16_t* __restrict__ k, Strides st, int N,
+                                                             int D, int NB, double* __restrict__ part) {
+    const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, c = threadIdx.x;
+    if (c >= D) return;
+    const uint16_t* base = k + b * st.b + h * st.h + c;
+    const int t0 = j * kBlk, t1 = min(N, t0 + kBlk);
+    uint16_t raw[kBlk];
+#pragma unroll
+    for (int i = 0; i < kBlk; i++) raw[i] = (t0 + i < t1) ? base[int64_t(t0 + i) * st.t] : 0;
+    double s = 0.0;
+#pragma unroll
+    for (int i = 0; i < kBlk; i++)
+        if (t0 + i < t1) s += double(in_to_f32<BF16>(raw[i]));
+    part[((int64_t(b) * gridDim.y + h) * NB + j) * D + c] = s;
+}
+
+// K mean, pass 2: mean = fp32((sum over blocks, ascending, of part) / N).
+__global__ __launch_bounds__(256) void k_mean_final_kernel(const double* __restrict__ part, int total, int NB, int D,
+                                                           int N, float* __restrict__ mean) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    const int bh = i / D, c = i % D;
+    const double* p = part + int64_t(bh) * NB * D + c;
+    double s = 0.0;
+    for (int j = 0; j < NB; j++) s += p[int64_t(j) * D];
+    mean[i] = float(s / double(N));
+}
+
+// ------------------------------------------------------------------------------------------
+// INT8 block quantisation.  One wave per 64-token block of one (b, head); 4 waves per
+// workgroup.  Lane l covers 8 consecutive channels (chunk l % CH, CH = Dp / 8) of the
+// token rows l / CH + p * (64 / CH), p = 0 .. CH-1.
+//   y = x (Q) or fp32(x - mean[c]) (K); amax = max |y|; scale = amax / 127;
+//   inv = 127 / amax; code = clamp(rne(y * inv), -127, 127).
+template <bool BF16, int DP, bool VEC8>
+__global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __restrict__ x, Strides st, int B, int H,
+                                                           int N, int D, int NB, const float* __restrict__ mean,
+                                                           int8_t* __restrict__ xq, float* __restrict__ scale) {
+    constexpr int CH = DP / 8;        // 8-channel chunks per row
+    constexpr int RPP = kWave / CH;   // rows per pass
+    constexpr int PASSES = kBlk / RPP;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int64_t blk = int64_t(blockIdx.x) * 4 + wave;
+    const int64_t total = int64_t(B) * H * NB;
+    if (blk >= total) return;
+    const int j = int(blk % NB);
+    const int64_t bh = blk / NB;
+    const int h = int(bh % H), b = int(bh / H);
+    const int ch = lane % CH, r0 = lane / CH;
+    const int c0 = ch * 8;
+    const uint16_t* base = x + b * st.b + h * st.h;
+
+    float mu[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) mu[e] = (mean != nullptr && c0 + e < D) ? mean[int64_t(bh) * D + c0 + e] : 0.0f;
+
+    v8u16 raw[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; p++) {
+        const int t = j * kBlk + p * RPP + r0;
+        v8u16 r = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (t < N && c0 < D) {
+            const uint16_t* src = base + int64_t(t) * st.t + c0;
+            if constexpr (VEC8) {
+                r = *(const v8u16*)src;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; e++) r[e] = (c0 + e < D) ? src[e] : (unsigned short)0;
+            }
+        }
+        raw[p] = r;
+    }
+    // amax over the block's real elements
+    float amax = 0.0f;
+#pragma unroll
+    for (int p = 0; p < PASSES; p++) {
+        const int t = j * kBlk + p * RPP + r0;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            if (t < N && c0 + e < D) {
+                const float y = in_to_f32<BF16>(raw[p][e]) - mu[e];
+                amax = fmaxf(amax, fabsf(y));
+            }
+        }
+    }
+    amax = wave_max(amax);
+    const bool zero = !(amax > 0.0f);
+    const float sc = zero ? 0.0f : amax / 127.0f;
+    const float inv = zero ? 0.0f : 127.0f / amax;
+    if (lane == 0) scale[int64_t(bh) * NB + j] = sc;
+    const int64_t npad = int64_t(NB) * kBlk;
+#pragma unroll
+    for (int p = 0; p < PASSES; p++) {
+        const int t = j * kBlk + p * RPP + r0;
+        uint32_t w[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            int code = 0;
+            if (!zero && t < N && c0 + e < D) {
+                const float y = in_to_f32<BF16>(raw[p][e]) - mu[e];
+                float r = rintf(y * inv);
+                r = fminf(fmaxf(r, -127.0f), 127.0f);
+                code = int(r);
+            }
+            w[e / 4] |= uint32_t(code & 0xff) << (8 * (e % 4));
+        }
+        int8_t* dst = xq + (bh * npad + j * kBlk + p * RPP + r0) * DP + c0;
+        *(uint2*)dst = make_uint2(w[0], w[1]);
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// V operand, FP8 mode, pass 0: clear the per-channel amax buffer (a fill kernel rather
+// than a memset so the sequence can be captured into a graph).
+__global__ void fill_zero_kernel(uint32_t* __restrict__ p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+// FP8 pass 1: per-channel amax over all tokens.  grid (ceil(N/256), H, B), 256 threads;
+// thread covers 8 channels of every (256 / CH)-th token of its 256-token slab.  The
+// non-negative float maxima are combined with an integer atomic max on their bits.
+template <bool BF16, int DP, bool VEC8>
+__global__ __launch_bounds__(256) void v_amax_kernel(const uint16_t* __restrict__ v, Strides st, int N, int D,
+                                                     uint32_t* __restrict__ amax_bits) {
+    constexpr int CH = DP / 8, RSTEP = 256 / CH;
+    __shared__ float red[RSTEP][DP];
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int ch = threadIdx.x % CH, r0 = threadIdx.x / CH, c0 = ch * 8;
+    const uint16_t* base = v + b * st.b + h * st.h;
+    float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const int t_end = min(N, int(blockIdx.x + 1) * 256);
+    if (c0 < D) {
+        for (int t = blockIdx.x * 256 + r0; t < t_end; t += RSTEP) {
+            const uint16_t* src = base + int64_t(t) * st.t + c0;
+            v8u16 r;
+            if constexpr (VEC8) {
+                r = *(const v8u16*)src;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; e++) r[e] = (c0 + e < D) ? src[e] : (unsigned short)0;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; e++) m[e] = fmaxf(m[e], fabsf(in_to_f32<BF16>(r[e])));
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; e++) red[r0][c0 + e] = m[e];
+    __syncthreads();
+    for (int c = threadIdx.x; c < D; c += 256) {
+        float mx = 0.0f;
+        for (int r = 0; r < RSTEP; r++) mx = fmaxf(mx, red[r][c]);
+        atomicMax(amax_bits + (int64_t(b) * gridDim.y + h) * DP + c, __float_as_uint(mx));
+    }
+}
+
+// V operand pass 2 (both modes): one workgroup per 64-token block; convert, transpose
+// through LDS, write the block channel-major ([Dp][64]) with 16-byte stores.
+//   FP16: v^ = fp16(clamp(v, +-65504)) (round half even).
+//   FP8:  v^ = e4m3(clamp(fp32(v * inv[c]), +-448)), inv = fp32(448 / amax[c]);
+//         the block-0 workgroup also writes v_scale[c] = fp32(amax[c] / 448).
+template <bool BF16, int DP, bool VEC8, bool FP8>
+__global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict__ v, Strides st, int N, int D,
+                                                      int NB, const uint32_t* __restrict__ amax_bits,
+                                                      void* __restrict__ vhat, float* __restrict__ vscale) {
+    constexpr int ELT = FP8 ? 1 : 2;
+    constexpr int CH = DP / 8, RSTEP = 256 / CH;  // RSTEP token rows per pass
+    constexpr int ROWB = kBlk * ELT + 16;         // padded LDS row (bytes) per channel
+    __shared__ __attribute__((aligned(16))) uint8_t tile[DP * ROWB];
+    const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int64_t bh = int64_t(b) * gridDim.y + h;
+    const int ch = threadIdx.x % CH, r0 = threadIdx.x / CH, c0 = ch * 8;
+    const uint16_t* base = v + b * st.b + h * st.h;
+
+    float inv[8];
+    if constexpr (FP8) {
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            const float a = __uint_as_float(amax_bits[bh * DP + c0 + e]);
+            inv[e] = a > 0.0f ? 448.0f / a : 0.0f;
+        }
+        if (j == 0 && threadIdx.x < DP) {
+            const float a = __uint_as_float(amax_bits[bh * DP + threadIdx.x]);
+            vscale[bh * DP + threadIdx.x] = a / 448.0f;
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < kBlk / RSTEP; p++) {
+        const int tl = p * RSTEP + r0, t = j * kBlk + tl;
+        v8u16 r = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (t < N && c0 < D) {
+            const uint16_t* src = base + int64_t(t) * st.t + c0;
+            if constexpr (VEC8) {
+                r = *(const v8u16*)src;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; e++) r[e] = (c0 + e < D) ? src[e] : (unsigned short)0;
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            const float x = in_to_f32<BF16>(r[e]);  // padding elements are +0
+            if constexpr (FP8) {
+                float y = x * inv[e];
+                y = fminf(fmaxf(y, -448.0f), 448.0f);
+                const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false);
+                tile[(c0 + e) * ROWB + tl] = uint8_t(pk & 0xff);
+            } else {
+                const float y = fminf(fmaxf(x, -65504.0f), 65504.0f);
+                *(uint16_t*)&tile[(c0 + e) * ROWB + 2 * tl] = f32_to_f16_bits(y);
+            }
+        }
+    }
+    __syncthreads();
+    constexpr int CHUNKS_PER_ROW = kBlk * ELT / 16;
+    constexpr int TOTAL = DP * CHUNKS_PER_ROW;
+    uint8_t* dst = (uint8_t*)vhat + (bh * NB + j) * int64_t(DP * kBlk * ELT);
+    for (int i = threadIdx.x; i < TOTAL; i += 256) {
+        const int c = i / CHUNKS_PER_ROW, q = i % CHUNKS_PER_ROW;
+        *(uint4*)(dst + int64_t(i) * 16) = *(const uint4*)&tile[c * ROWB + q * 16];
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Launchers
+namespace {
+template <bool BF16, int DP, bool VEC8>
+hipError_t launch_qk_t(const QuantQKArgs& a, hipStream_t s) {
+    const Strides sq = make_strides(a.layout_nhd, a.Hq, a.Nq, a.D);
+    const Strides sk = make_strides(a.layout_nhd, a.Hkv, a.Nkv, a.D);
+    const int nbq = (a.Nq + kBlk - 1) / kBlk, nbk = (a.Nkv + kBlk - 1) / kBlk;
+    k_mean_partial_kernel<BF16><<<dim3(nbk, a.Hkv, a.B), 128, 0, s>>>((const uint16_t*)a.k, sk, a.Nkv, a.D, nbk,
+                                                                        (double*)a.workspace);
+    const int tot = a.B * a.Hkv * a.D;
+    k_mean_final_kernel<<<(tot + 255) / 256, 256, 0, s>>>((const double*)a.workspace, tot, nbk, a.D, a.Nkv,
+                                                          a.k_mean);
+    const int64_t qblocks = int64_t(a.B) * a.Hq * nbq, kblocks = int64_t(a.B) * a.Hkv * nbk;
+    quant_blocks_kernel<BF16, DP, VEC8><<<unsigned((qblocks + 3) / 4), 256, 0, s>>>(
+        (const uint16_t*)a.q, sq, a.B, a.Hq, a.Nq, a.D, nbq, nullptr, a.q_i8, a.q_scale);
+    quant_blocks_kernel<BF16, DP, VEC8><<<unsigned((kblocks + 3) / 4), 256, 0, s>>>(
+        (const uint16_t*)a.k, sk, a.B, a.Hkv, a.Nkv, a.D, nbk, a.k_mean, a.k_i8, a.k_scale);
+    return hipGetLastError();
+}
+
+template <bool BF16, int DP, bool VEC8>
+hipError_t launch_v_t(const QuantVArgs& a, hipStream_t s) {
+    const Strides sv = make_strides(a.layout_nhd, a.Hkv, a.Nkv, a.D);
+    const int nb = (a.Nkv + kBlk - 1) / kBlk;
+    if (a.fp8) {
+        const int n = a.B * a.Hkv * DP;
+        uint32_t* amax = (uint32_t*)a.workspace;
+        fill_zero_kernel<<<(n + 255) / 256, 256, 0, s>>>(amax, n);
+        v_amax_kernel<BF16, DP, VEC8><<<dim3((a.Nkv + 255) / 256, a.Hkv, a.B), 256, 0, s>>>(
+            (const uint16_t*)a.v, sv, a.Nkv, a.D, amax);
+        quant_v_kernel<BF16, DP, VEC8, true><<<dim3(nb, a.Hkv, a.B), 256, 0, s>>>(
+            (const uint16_t*)a.v, sv, a.Nkv, a.D, nb, amax, a.v_hat, a.v_scale);
+    } else {
+        quant_v_kernel<BF16, DP, VEC8, false><<<dim3(nb, a.Hkv, a.B), 256, 0, s>>>(
+            (const uint16_t*)a.v, sv, a.Nkv, a.D, nb, nullptr, a.v_hat, nullptr);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_qk(const QuantQKArgs& a, hipStream_t s) {
+    const bool vec = (a.D % 8) == 0;
+    const int dp = a.D <= 64 ? 64 : 128;
+    if (a.bf16) {
+        if (dp == 64) return vec ? launch_qk_t<true, 64, true>(a, s) : launch_qk_t<true, 64, false>(a, s);
+        return vec ? launch_qk_t<true, 128, true>(a, s) : launch_qk_t<true, 128, false>(a, s);
+    }
+    if (dp == 64) return vec ? launch_qk_t<false, 64, true>(a, s) : launch_qk_t<false, 64, false>(a, s);
+    return vec ? launch_qk_t<false, 128, true>(a, s) : launch_qk_t<false, 128, false>(a, s);
+}
+
+hipError_t launch_quant_v(const QuantVArgs& a, hipStream_t s) {
+    const bool vec = (a.D % 8) == 0;
+    const int dp = a.D <= 64 ? 64 : 128;
+    if (a.bf16) {
+        if (dp == 64) return vec ? launch_v_t<true, 64, true>(a, s) : launch_v_t<true, 64, false>(a, s);
+        return vec ? launch_v_t<true, 128, true>(a, s) : launch_v_t<true, 128, false>(a, s);
+    }
+    if (dp == 64) return vec ? launch_v_t<false, 64, true>(a, s) : launch_v_t<false, 64, false>(a, s);
+    return vec ? launch_v_t<false, 128, true>(a, s) : launch_v_t<false, 128, false>(a, s);
+}
+
+}  // namespace sage

@@ -1,0 +1,160 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching HIP."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import quantized_attention_04_amd as qa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sage.h")
+
+# A fake, 256-byte aligned device address: every call below fails validation before
+# any pointer is dereferenced or any HIP call is made.
+FAKE = 0x7F0000000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sage_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = qa.lib()
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+    # and the binding declares a signature for each of them
+    assert set(names) <= set(qa._EXPORTS)
+
+
+def test_abi_version_and_strings():
+    L = qa.lib()
+    assert L.sage_abi_version() == 1
+    for s in range(6):
+        assert L.sage_status_string(s).decode().startswith("SAGE_")
+    assert qa.padded_dim(1) == 64 and qa.padded_dim(64) == 64 and qa.padded_dim(65) == 128
+    assert qa.padded_dim(128) == 128 and qa.padded_dim(129) == 0 and qa.padded_dim(0) == 0
+    assert qa.num_blocks(1) == 1 and qa.num_blocks(64) == 1 and qa.num_blocks(65) == 2 and qa.num_blocks(17776) == 278
+
+
+def test_workspace_sizes():
+    L = qa.lib()
+    assert L.sage_quant_qk_workspace_bytes(2, 8, 8192, 128) == 2 * 8 * 128 * 128 * 8
+    assert L.sage_quant_qk_workspace_bytes(1, 1, 100, 96) == 2 * 96 * 8
+    assert L.sage_quant_qk_workspace_bytes(1, 1, 100, 129) == 0
+    assert L.sage_quant_v_workspace_bytes(2, 8, 96, qa.SAGE_PV_FP8) == 2 * 8 * 128 * 4
+    assert L.sage_quant_v_workspace_bytes(2, 8, 96, qa.SAGE_PV_FP16) == 0
+
+
+def _qk(**kw):
+    a = dict(q=FAKE, k=FAKE, dtype=0, layout=0, B=1, Hq=2, Hkv=2, Nq=128, Nkv=128, D=64, q_i8=FAKE, q_scale=FAKE,
+             k_i8=FAKE, k_scale=FAKE, k_mean=FAKE, ws=FAKE, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return qa.lib().sage_quant_qk(a["q"], a["k"], a["dtype"], a["layout"], a["B"], a["Hq"], a["Hkv"], a["Nq"],
+                                  a["Nkv"], a["D"], a["q_i8"], a["q_scale"], a["k_i8"], a["k_scale"], a["k_mean"],
+                                  a["ws"], a["ws_bytes"], a["stream"])
+
+
+def _attn(**kw):
+    a = dict(q_i8=FAKE, q_scale=FAKE, k_i8=FAKE, k_scale=FAKE, v_hat=FAKE, v_scale=FAKE, out=FAKE, odt=0, olay=0,
+             B=1, Hq=2, Hkv=2, Nq=128, Nkv=128, D=64, causal=0, sm=0.125, pv=1, acc=0, stream=None)
+    a.update(kw)
+    return qa.lib().sage_attn_fwd(a["q_i8"], a["q_scale"], a["k_i8"], a["k_scale"], a["v_hat"], a["v_scale"],
+                                  a["out"], a["odt"], a["olay"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nkv"], a["D"],
+                                  a["causal"], a["sm"], a["pv"], a["acc"], a["stream"])
+
+
+def _v(**kw):
+    a = dict(v=FAKE, dtype=1, layout=1, B=1, Hkv=2, Nkv=100, D=96, pv=1, v_hat=FAKE, v_scale=FAKE, ws=FAKE,
+             ws_bytes=1 << 16, stream=None)
+    a.update(kw)
+    return qa.lib().sage_quant_v(a["v"], a["dtype"], a["layout"], a["B"], a["Hkv"], a["Nkv"], a["D"], a["pv"],
+                                 a["v_hat"], a["v_scale"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def _detail():
+    return qa.lib().sage_last_error_detail().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"q": None}, qa.SAGE_ERR_INVALID_ARG),
+    ({"k_mean": None}, qa.SAGE_ERR_INVALID_ARG),
+    ({"dtype": 2}, qa.SAGE_ERR_INVALID_ARG),
+    ({"layout": 7}, qa.SAGE_ERR_INVALID_ARG),
+    ({"B": 0}, qa.SAGE_ERR_INVALID_ARG),
+    ({"Nkv": -1}, qa.SAGE_ERR_INVALID_ARG),
+    ({"Hq": 6, "Hkv": 4}, qa.SAGE_ERR_INVALID_ARG),
+    ({"D": 129}, qa.SAGE_ERR_UNSUPPORTED),
+    ({"D": 256}, qa.SAGE_ERR_UNSUPPORTED),
+    ({"q": FAKE + 2}, qa.SAGE_ERR_INVALID_ARG),
+    ({"ws": None}, qa.SAGE_ERR_WORKSPACE),
+    ({"ws_bytes": 2 * 64 * 8 - 1}, qa.SAGE_ERR_WORKSPACE),
+])
+def test_quant_qk_rejects(kw, code):
+    assert _qk(**kw) == code
+    assert _detail()
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"v": None}, qa.SAGE_ERR_INVALID_ARG),
+    ({"pv": 5}, qa.SAGE_ERR_INVALID_ARG),
+    ({"v_scale": None}, qa.SAGE_ERR_INVALID_ARG),
+    ({"ws": None}, qa.SAGE_ERR_WORKSPACE),
+    ({"ws_bytes": 2 * 128 * 4 - 4}, qa.SAGE_ERR_WORKSPACE),
+    ({"D": 200}, qa.SAGE_ERR_UNSUPPORTED),
+    ({"v_hat": FAKE + 8}, qa.SAGE_ERR_INVALID_ARG),
+])
+def test_quant_v_rejects(kw, code):
+    assert _v(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"out": None}, qa.SAGE_ERR_INVALID_ARG),
+    ({"sm": 0.0}, qa.SAGE_ERR_INVALID_ARG),
+    ({"sm": -1.0}, qa.SAGE_ERR_INVALID_ARG),
+    ({"sm": float("inf")}, qa.SAGE_ERR_INVALID_ARG),
+    ({"sm": float("nan")}, qa.SAGE_ERR_INVALID_ARG),
+    ({"pv": 2}, qa.SAGE_ERR_INVALID_ARG),
+    ({"acc": 3}, qa.SAGE_ERR_INVALID_ARG),
+    ({"causal": 2}, qa.SAGE_ERR_INVALID_ARG),
+    ({"acc": qa.SAGE_ACC_FP16}, qa.SAGE_ERR_UNSUPPORTED),
+    ({"causal": 1, "Nkv": 256}, qa.SAGE_ERR_UNSUPPORTED),
+    ({"v_scale": None}, qa.SAGE_ERR_INVALID_ARG),
+    ({"Hq": 32, "Hkv": 6}, qa.SAGE_ERR_INVALID_ARG),
+    ({"out": FAKE + 2}, qa.SAGE_ERR_INVALID_ARG),
+])
+def test_attn_fwd_rejects(kw, code):
+    assert _attn(**kw) == code
+    assert _detail()
+
+
+def test_fp16_pv_needs_no_scale_or_workspace_validation_order():
+    # FP16 mode ignores v_scale; without a GPU the call reaches the device check.
+    if torch.cuda.is_available():
+        pytest.skip("would launch kernels on fake pointers")
+    assert _attn(pv=0, v_scale=None) == qa.SAGE_ERR_DEVICE
+    assert _v(pv=0, v_scale=None, ws=None, ws_bytes=0) == qa.SAGE_ERR_DEVICE
+    assert "device" in _detail()
+
+
+def test_valid_arguments_reach_the_device_check_only():
+    if torch.cuda.is_available():
+        pytest.skip("would launch kernels on fake pointers")
+    assert _qk() == qa.SAGE_ERR_DEVICE
+    assert _attn() == qa.SAGE_ERR_DEVICE
+    assert _v() == qa.SAGE_ERR_DEVICE
+
+
+def test_python_layer_rejects_fp32_and_cpu_tensors():
+    x = torch.zeros(1, 1, 64, 64)
+    with pytest.raises(ValueError, match="float16 or bfloat16"):
+        qa.sageattn(x, x, x)
+    h = x.half()
+    with pytest.raises(ValueError, match="GPU"):
+        qa.sageattn(h, h, h)

@@ -9,14 +9,16 @@
 // levels (a fresh per-64-key-block partial added into it).
 //
 // gfx950 design:
-//  * workgroup = 4 waves = 256 queries; each wave owns 64 queries (one Q
-//    quantisation block, so the Q scale is wave-uniform) and loops over 64-key tiles
-//    (one K block, so the K scale is uniform too);
+//  * workgroup = 8 waves = 256 queries, two waves per SIMD: while one wave runs the
+//    softmax on the vector ALUs the other keeps the matrix cores busy (one wave per
+//    SIMD cannot overlap the two); each wave owns 32 queries inside one 64-token Q
+//    block (wave-uniform Q scale) and walks 64-key tiles (one K block: uniform K scale);
 //  * K^ and V^ tiles stream HBM -> LDS with direct-to-LDS 16-byte loads, double
-//    buffered, XOR-swizzled so that every 16-byte operand read is bank-conflict free;
-//  * S^T = K^ Q^T on v_mfma_i32_32x32x32_i8 (keys on the M side): each lane then holds
-//    whole query columns, so row max / row sum are lane-local plus one exchange
-//    between the two lane halves;
+//    buffered, the same number of loads per thread per tile (so explicit vmcnt waits
+//    are exact), XOR-swizzled so every 16-byte operand read is bank-conflict free;
+//  * S^T = K^ Q^T on v_mfma_i32_32x32x32_i8 (keys on the M side): each lane holds one
+//    query column, so row max / row sum are lane-local plus one exchange between the
+//    two lane halves;
 //  * the K^ rows fed to each MFMA row are permuted so that the INT32 result lands in
 //    exactly the register order the P.V MFMA wants for its B operand: P never leaves
 //    registers; V^ tiles are stored channel-major so the A operand is contiguous;
@@ -50,30 +52,33 @@ __device__ __forceinline__ void block_barrier() {
 // Mode constants.  DP = padded head dim (64 | 128); FP8 = P.V in e4m3 (else fp16).
 template <int DP, bool FP8>
 struct Cfg {
-    static constexpr int WAVES = 4;
+    static constexpr int WAVES = 8;
     static constexpr int THREADS = WAVES * kWave;
-    static constexpr int BM = WAVES * kBlk;  // queries per workgroup
+    static constexpr int QW = 32;            // queries per wave
+    static constexpr int BM = WAVES * QW;    // queries per workgroup
     static constexpr int VELT = FP8 ? 1 : 2;
     static constexpr int KROW = DP;          // bytes per K^ row (one key)
     static constexpr int VROW = kBlk * VELT; // bytes per V^ row (one channel of 64 keys)
     static constexpr int KBYTES = kBlk * KROW;
     static constexpr int VBYTES = DP * VROW;
-    static constexpr int STAGE = KBYTES + VBYTES;
-    static constexpr int KROUNDS = KBYTES / 16 / THREADS;
-    static constexpr int VROUNDS = VBYTES / 16 / THREADS;
-    static constexpr int LOADS = KROUNDS + VROUNDS;  // 16-byte loads per thread per tile
-    static constexpr int KS = DP / 32;               // MFMA k-steps of QK^T
-    static constexpr int DT = DP / 32;               // 32-channel tiles of O^T
+    static constexpr int KCHUNKS = KBYTES / 16;
+    static constexpr int VCHUNKS = VBYTES / 16;
+    // every thread issues ROUNDS 16-byte loads per tile; a short last round re-reads V
+    // into a padding area so that the count stays uniform
+    static constexpr int ROUNDS = (KCHUNKS + VCHUNKS + THREADS - 1) / THREADS;
+    static constexpr int STAGE = ROUNDS * THREADS * 16;
+    static constexpr int KS = DP / 32;  // MFMA k-steps of QK^T
+    static constexpr int DT = DP / 32;  // 32-channel tiles of O^T
     // XOR swizzles: bit c of the chunk flip is parity(row & mask_c); each is
     // conflict-free for the operand reads below with 8 lanes x 128 B or 16 lanes x
     // 256 B served per LDS cycle.
-    static constexpr uint32_t KM0 = DP == 128 ? 0x2u : (FP8 ? 0x6u : 0x6u);
+    static constexpr uint32_t KM0 = DP == 128 ? 0x2u : 0x6u;
     static constexpr uint32_t KM1 = DP == 128 ? 0x5u : (FP8 ? 0x20u : 0x8u);
     static constexpr uint32_t KM2 = DP == 128 ? (FP8 ? 0x20u : 0x8u) : 0x0u;
     static constexpr uint32_t VM0 = FP8 ? 0x4u : 0x2u;
     static constexpr uint32_t VM1 = FP8 ? 0xAu : 0x4u;
     static constexpr uint32_t VM2 = FP8 ? 0x0u : 0x9u;
-    static_assert(KROUNDS >= 1 && VROUNDS >= 1, "tile must cover the workgroup");
+    static_assert(KCHUNKS % kWave == 0 && VCHUNKS % kWave == 0, "regions must be whole-wave aligned");
 };
 
 template <class C>
@@ -102,35 +107,29 @@ __device__ __forceinline__ int key_of_reg(int kt, int g, int r) {
     return key_of_row<FP8>(kt, 8 * (r >> 2) + 4 * g + (r & 3));
 }
 
-// Direct-to-LDS loads of one K^ tile / one V^ tile into stage buffer `st`.  LDS chunk
-// (row, c) receives the global chunk (row, c ^ swizzle(row)).
+// Global address of LDS chunk ci of a stage: K^ rows, then V^ rows, then padding (a
+// re-read of V^, never consumed).  LDS chunk (row, c) holds global chunk (row, c ^ swz).
 template <class C>
-__device__ __forceinline__ void issue_k_loads(uint8_t* __restrict__ st, const int8_t* ktile, int tid) {
-    const int wave = tid / kWave;
-#pragma unroll
-    for (int u = 0; u < C::KROUNDS; u++) {
-        const int ci = u * C::THREADS + tid;
-        const int row = ci / (C::KROW / 16), cpos = ci % (C::KROW / 16);
-        const int8_t* src = ktile + row * C::KROW + 16 * (cpos ^ kswz<C>(row));
-        load_lds_16(src, st + (u * C::THREADS + wave * kWave) * 16);
-    }
+__device__ __forceinline__ const int8_t* k_chunk_src(int ci, const int8_t* ktile) {
+    const int row = ci / (C::KROW / 16), cpos = ci % (C::KROW / 16);
+    return ktile + row * C::KROW + 16 * (cpos ^ kswz<C>(row));
 }
 template <class C>
-__device__ __forceinline__ void issue_v_loads(uint8_t* __restrict__ st, const uint8_t* vtile, int tid) {
-    const int wave = tid / kWave;
-#pragma unroll
-    for (int u = 0; u < C::VROUNDS; u++) {
-        const int ci = u * C::THREADS + tid;
-        const int row = ci / (C::VROW / 16), cpos = ci % (C::VROW / 16);
-        const uint8_t* src = vtile + row * C::VROW + 16 * (cpos ^ vswz<C>(row));
-        load_lds_16(src, st + C::KBYTES + (u * C::THREADS + wave * kWave) * 16);
-    }
+__device__ __forceinline__ const void* stage_src(int ci, const int8_t* ktile, const uint8_t* vtile) {
+    if (ci < C::KCHUNKS) return k_chunk_src<C>(ci, ktile);
+    const int vi = (ci - C::KCHUNKS) % C::VCHUNKS;
+    const int row = vi / (C::VROW / 16), cpos = vi % (C::VROW / 16);
+    return vtile + row * C::VROW + 16 * (cpos ^ vswz<C>(row));
 }
+
 template <class C>
-__device__ __forceinline__ void issue_tile_loads(uint8_t* __restrict__ st, const int8_t* ktile, const uint8_t* vtile,
-                                                 int tid) {
-    issue_k_loads<C>(st, ktile, tid);
-    issue_v_loads<C>(st, vtile, tid);
+__device__ __forceinline__ void issue_stage(uint8_t* __restrict__ st, const int8_t* ktile, const uint8_t* vtile,
+                                            int tid, int wave) {
+#pragma unroll
+    for (int u = 0; u < C::ROUNDS; u++) {
+        const int ci = u * C::THREADS + tid;
+        load_lds_16(stage_src<C>(ci, ktile, vtile), st + (u * C::THREADS + wave * kWave) * 16);
+    }
 }
 
 __device__ __forceinline__ v16f fma16(v16f a, float s, v16f c) {
@@ -140,10 +139,10 @@ __device__ __forceinline__ v16f fma16(v16f a, float s, v16f c) {
     return r;
 }
 
-// S^T tiles of one 64-key tile for this wave's 64 queries: S[kt][nt] (keys 32kt.. on M
-// through the permutation above, queries 32nt + lane%32 on N).
+// S^T tiles of one 64-key tile for this wave's 32 queries: S[kt] (keys through the
+// permutation above on M, queries lane%32 on N).
 template <class C, bool FP8>
-__device__ __forceinline__ void qk_tile(const uint8_t* __restrict__ kst, const v4i (&qf)[2][C::KS], v16i (&S)[2][2],
+__device__ __forceinline__ void qk_tile(const uint8_t* __restrict__ kst, const v4i (&qf)[C::KS], v16i (&S)[2],
                                         int lane) {
     const int i = lane & 31, g = lane >> 5;
 #pragma unroll
@@ -154,26 +153,60 @@ __device__ __forceinline__ void qk_tile(const uint8_t* __restrict__ kst, const v
 #pragma unroll
         for (int s = 0; s < C::KS; s++) {
             const v4i a = lds_read_16(rbase + 16 * ((2 * s + g) ^ sw));
-#pragma unroll
-            for (int nt = 0; nt < 2; nt++) {
-                if (s == 0) {
-                    const v16i z = {};
-                    S[kt][nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[nt][s], z, 0, 0, 0);
-                } else {
-                    S[kt][nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[nt][s], S[kt][nt], 0, 0, 0);
-                }
+            if (s == 0) {
+                const v16i z = {};
+                S[kt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[s], z, 0, 0, 0);
+            } else {
+                S[kt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[s], S[kt], 0, 0, 0);
             }
         }
     }
 }
 
 template <class C>
-__device__ __forceinline__ void load_q_frags(v4i (&qf)[2][C::KS], const int8_t* qblk, int lane) {
+__device__ __forceinline__ void load_q_frags(v4i (&qf)[C::KS], const int8_t* qrows, int lane) {
     const int i = lane & 31, g = lane >> 5;
 #pragma unroll
-    for (int nt = 0; nt < 2; nt++)
+    for (int s = 0; s < C::KS; s++) qf[s] = *(const v4i*)(qrows + i * C::KROW + 32 * s + 16 * g);
+}
+
+// Online softmax step for one tile: updates m, l; returns alpha; fills P (FP8: p*448).
+template <bool FP8, bool MASK, bool CAUSAL>
+__device__ __forceinline__ float softmax_tile(v16i (&S)[2], float (&P)[2][16], float c, float& m, float& l, int g,
+                                              int key0, int qidx, int Nkv) {
+    if constexpr (MASK) {
 #pragma unroll
-        for (int s = 0; s < C::KS; s++) qf[nt][s] = *(const v4i*)(qblk + (32 * nt + i) * C::KROW + 32 * s + 16 * g);
+        for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int key = key0 + key_of_reg<FP8>(kt, g, r);
+                const bool vis = key < Nkv && (!CAUSAL || key <= qidx);
+                if (!vis) S[kt][r] = INT32_MIN;
+            }
+    }
+    int imax = S[0][0];
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) imax = max(imax, S[kt][r]);
+    float tmax = (MASK && imax == INT32_MIN) ? -1e30f : float(imax) * c;
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float mnew = fmaxf(m, tmax);
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    m = mnew;
+    const float negm = FP8 ? kLog2_448 - mnew : -mnew;
+    float psum = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(float(S[kt][r]), c, negm));
+            if constexpr (MASK) pv = S[kt][r] == INT32_MIN ? 0.0f : pv;
+            P[kt][r] = pv;
+            psum += pv;
+        }
+    l = l * alpha + psum;
+    return alpha;
 }
 
 struct KParams {
@@ -190,7 +223,7 @@ struct KParams {
 };
 
 template <int DP, bool FP8, bool CAUSAL, bool TWO, bool OBF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_fwd_kernel(KParams p) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(KParams p) {
     using C = Cfg<DP, FP8>;
     // Two LDS stages as distinct objects, so that the compiler can tell the prefetch
     // into one stage from the operand reads of the other.
@@ -198,35 +231,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     __shared__ __attribute__((aligned(16))) uint8_t lds1[C::STAGE];
     const int tid = threadIdx.x, lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform (SGPR)
-    const int g = lane >> 5;
+    const int g = lane >> 5, i = lane & 31;
 
     // ---- workgroup -> (b, h, q tile)
-    const int nwg = gridDim.x;
     int b, h, qt;
     {
-        int L, qtl;
+        int L;
         if constexpr (CAUSAL) {
             L = blockIdx.x;  // heaviest (last) query tiles first
             const int per = p.B * p.Hq;
-            qtl = p.QT - 1 - L / per;
+            qt = p.QT - 1 - L / per;
             L = L % per;
             const int hg = L % p.G, bhk = L / p.G;
             b = bhk / p.Hkv;
             h = (bhk % p.Hkv) * p.G + hg;
         } else {
-            L = xcd_remap(blockIdx.x, nwg);  // one (b, kv head) per XCD run
+            L = xcd_remap(blockIdx.x, gridDim.x);  // one (b, kv head) per XCD run
             const int hg = L % p.G;
-            qtl = (L / p.G) % p.QT;
+            qt = (L / p.G) % p.QT;
             const int bhk = L / (p.G * p.QT);
             b = bhk / p.Hkv;
             h = (bhk % p.Hkv) * p.G + hg;
         }
-        qt = qtl;
     }
     const int hk = h / p.G;
-    const int q0 = qt * C::BM + wave * kBlk;  // this wave's first query
+    const int q0 = qt * C::BM + wave * C::QW;  // this wave's first query
     const bool active = q0 < p.Nq;
     const int qb = q0 / kBlk;
+    const int qidx = q0 + i;  // this lane's query
 
     const int64_t bhk = int64_t(b) * p.Hkv + hk;
     const int8_t* kbase = p.k_i8 + bhk * int64_t(p.NBk) * kBlk * DP;
@@ -237,92 +269,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const bool ktail = (p.Nkv % kBlk) != 0;
 
     // ---- per-wave state
-    v4i qf[2][C::KS];
+    v4i qf[C::KS];
     float sq = 0.0f;
     if (active) {
         load_q_frags<C>(qf, p.q_i8 + ((int64_t(b) * p.Hq + h) * p.NBq * kBlk + q0) * DP, lane);
         sq = scalar_load_f32(p.q_scale + (int64_t(b) * p.Hq + h) * p.NBq + qb);
     } else {
 #pragma unroll
-        for (int nt = 0; nt < 2; nt++)
-#pragma unroll
-            for (int s = 0; s < C::KS; s++) qf[nt][s] = v4i{0, 0, 0, 0};
+        for (int s = 0; s < C::KS; s++) qf[s] = v4i{0, 0, 0, 0};
     }
     const float* ks_row = p.k_scale + bhk * p.NBk;
     wait_vmcnt<0>();  // Q fragments resident before the tile pipeline starts
-    v16f O[C::DT][2];
+    v16f O[C::DT];
 #pragma unroll
-    for (int dt = 0; dt < C::DT; dt++)
-#pragma unroll
-        for (int nt = 0; nt < 2; nt++) O[dt][nt] = v16f{};
-    float m[2] = {-1e30f, -1e30f}, l[2] = {0.0f, 0.0f};
+    for (int dt = 0; dt < C::DT; dt++) O[dt] = v16f{};
+    float m = -1e30f, l = 0.0f;
 
     auto compute = [&](const uint8_t* __restrict__ st, int j, float ksj) {
         if (!active) return;
         if (CAUSAL && j > qb) return;  // whole tile above this wave's diagonal
-        v16i S[2][2];
+        v16i S[2];
         qk_tile<C, FP8>(st, qf, S, lane);
         const float c = sq * ksj * p.cscale;
         const bool need_mask = (CAUSAL && j == qb) || (ktail && j == p.NBk - 1);
-        float alpha[2];
-        float P[2][2][16];  // probabilities (FP8: p * 448)
-#pragma unroll
-        for (int nt = 0; nt < 2; nt++) {
-            const int qidx = q0 + 32 * nt + (lane & 31);
-            int imax = INT32_MIN;
-            if (need_mask) {
-#pragma unroll
-                for (int kt = 0; kt < 2; kt++)
-#pragma unroll
-                    for (int r = 0; r < 16; r++) {
-                        const int key = j * kBlk + key_of_reg<FP8>(kt, g, r);
-                        const bool vis = key < p.Nkv && (!CAUSAL || key <= qidx);
-                        if (!vis) S[kt][nt][r] = INT32_MIN;
-                    }
-            }
-#pragma unroll
-            for (int kt = 0; kt < 2; kt++)
-#pragma unroll
-                for (int r = 0; r < 16; r++) imax = max(imax, S[kt][nt][r]);
-            float tmax = imax == INT32_MIN ? -1e30f : float(imax) * c;
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-            const float mnew = fmaxf(m[nt], tmax);
-            alpha[nt] = __builtin_amdgcn_exp2f(m[nt] - mnew);
-            m[nt] = mnew;
-            const float negm = FP8 ? kLog2_448 - mnew : -mnew;
-            float psum = 0.0f;
-#pragma unroll
-            for (int kt = 0; kt < 2; kt++)
-#pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(float(S[kt][nt][r]), c, negm));
-                    if (need_mask && S[kt][nt][r] == INT32_MIN) pv = 0.0f;
-                    P[nt][kt][r] = pv;
-                    psum += pv;
-                }
-            l[nt] = l[nt] * alpha[nt] + psum;
-        }
+        float P[2][16];  // probabilities (FP8: p * 448)
+        float alpha;
+        if (need_mask) alpha = softmax_tile<FP8, true, CAUSAL>(S, P, c, m, l, g, j * kBlk, qidx, p.Nkv);
+        else alpha = softmax_tile<FP8, false, CAUSAL>(S, P, c, m, l, g, j * kBlk, qidx, p.Nkv);
         if constexpr (!TWO) {
             // single level: rescale the accumulator only when some row max moved
-            if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.0f || alpha[1] != 1.0f)) {
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
-                for (int dt = 0; dt < C::DT; dt++)
-#pragma unroll
-                    for (int nt = 0; nt < 2; nt++) O[dt][nt] *= alpha[nt];
+                for (int dt = 0; dt < C::DT; dt++) O[dt] *= alpha;
             }
         }
         const uint8_t* vst = st + C::KBYTES;
-        const int i = lane & 31;
         if constexpr (FP8) {
-            v8i pb[2];
+            v8i pb;
 #pragma unroll
-            for (int nt = 0; nt < 2; nt++)
-#pragma unroll
-                for (int w = 0; w < 8; w++) {
-                    const float* pp = &P[nt][w >> 2][4 * (w & 3)];
-                    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(pp[0], pp[1], 0, false);
-                    pb[nt][w] = __builtin_amdgcn_cvt_pk_fp8_f32(pp[2], pp[3], lo, true);
-                }
+            for (int w = 0; w < 8; w++) {
+                const float* pp = &P[w >> 2][4 * (w & 3)];
+                const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(pp[0], pp[1], 0, false);
+                pb[w] = __builtin_amdgcn_cvt_pk_fp8_f32(pp[2], pp[3], lo, true);
+            }
 #pragma unroll
             for (int dt = 0; dt < C::DT; dt++) {
                 const int d = 32 * dt + i;
@@ -331,64 +320,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 const v4i a0 = lds_read_16(rb + 16 * ((2 * g) ^ sw));
                 const v4i a1 = lds_read_16(rb + 16 * ((2 * g + 1) ^ sw));
                 const v8i a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-#pragma unroll
-                for (int nt = 0; nt < 2; nt++) {
-                    if constexpr (TWO) {
-                        const v16f z = {};
-                        const v16f part =
-                            __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb[nt], z, 0, 0, 0, 127, 0, 127);
-                        O[dt][nt] = fma16(O[dt][nt], alpha[nt], part);
-                    } else {
-                        O[dt][nt] =
-                            __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb[nt], O[dt][nt], 0, 0, 0, 127, 0, 127);
-                    }
+                if constexpr (TWO) {
+                    const v16f z = {};
+                    const v16f part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, z, 0, 0, 0, 127, 0, 127);
+                    O[dt] = fma16(O[dt], alpha, part);
+                } else {
+                    O[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, O[dt], 0, 0, 0, 127, 0, 127);
                 }
             }
         } else {
-            v8h ph[2][4];
+            v8h ph[4];
 #pragma unroll
-            for (int nt = 0; nt < 2; nt++)
+            for (int mm = 0; mm < 4; mm++)
 #pragma unroll
-                for (int mm = 0; mm < 4; mm++)
-#pragma unroll
-                    for (int e = 0; e < 8; e++) ph[nt][mm][e] = (_Float16)P[nt][mm >> 1][8 * (mm & 1) + e];
+                for (int e = 0; e < 8; e++) ph[mm][e] = (_Float16)P[mm >> 1][8 * (mm & 1) + e];
 #pragma unroll
             for (int dt = 0; dt < C::DT; dt++) {
                 const int d = 32 * dt + i;
                 const int sw = vswz<C>(d);
                 const uint8_t* rb = vst + d * C::VROW;
-                v16f part[2];
-                if constexpr (TWO) part[0] = part[1] = v16f{};
+                v16f part = {};
+                if constexpr (!TWO) part = O[dt];
 #pragma unroll
                 for (int mm = 0; mm < 4; mm++) {
                     const v4i araw = lds_read_16(rb + 16 * ((2 * mm + g) ^ sw));
                     v8h a;
                     __builtin_memcpy(&a, &araw, 16);
-#pragma unroll
-                    for (int nt = 0; nt < 2; nt++) {
-                        if constexpr (TWO)
-                            part[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, ph[nt][mm], part[nt], 0, 0, 0);
-                        else
-                            O[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, ph[nt][mm], O[dt][nt], 0, 0, 0);
-                    }
+                    part = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, ph[mm], part, 0, 0, 0);
                 }
-                if constexpr (TWO) {
-#pragma unroll
-                    for (int nt = 0; nt < 2; nt++) O[dt][nt] = fma16(O[dt][nt], alpha[nt], part[nt]);
-                }
+                if constexpr (TWO) O[dt] = fma16(O[dt], alpha, part);
+                else O[dt] = part;
             }
         }
     };
 
     // ---- main loop: two LDS stages, ping-pong.  Each wave waits for its own
-    // direct-to-LDS loads of the current tile (vmcnt: all but the LOADS most recent
+    // direct-to-LDS loads of the current tile (vmcnt: all but the ROUNDS most recent
     // ones, i.e. the prefetch of the next tile, are complete), then a bare barrier
     // publishes the tile; a second barrier retires the stage before it is refilled.
-    issue_tile_loads<C>(lds0, kbase, vbase, tid);
+    issue_stage<C>(lds0, kbase, vbase, tid, wave);
     for (int j = 0; j < jend; j += 2) {
         if (j + 1 < jend) {
-            issue_tile_loads<C>(lds1, kbase + int64_t(j + 1) * kBlk * DP, vbase + int64_t(j + 1) * C::VBYTES, tid);
-            wait_vmcnt<C::LOADS>();
+            issue_stage<C>(lds1, kbase + int64_t(j + 1) * kBlk * DP, vbase + int64_t(j + 1) * C::VBYTES, tid, wave);
+            wait_vmcnt<C::ROUNDS>();
         } else {
             wait_vmcnt<0>();
         }
@@ -397,8 +371,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         block_barrier();
         if (j + 1 >= jend) break;
         if (j + 2 < jend) {
-            issue_tile_loads<C>(lds0, kbase + int64_t(j + 2) * kBlk * DP, vbase + int64_t(j + 2) * C::VBYTES, tid);
-            wait_vmcnt<C::LOADS>();
+            issue_stage<C>(lds0, kbase + int64_t(j + 2) * kBlk * DP, vbase + int64_t(j + 2) * C::VBYTES, tid, wave);
+            wait_vmcnt<C::ROUNDS>();
         } else {
             wait_vmcnt<0>();
         }
@@ -409,50 +383,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     // ---- epilogue: O^T / l (x v_scale in FP8 mode) -> out dtype, input layout
     if (!active) return;
-    const int i = lane & 31;
+    const float ltot = l + __shfl_xor(l, 32, 64);
+    const float inv = 1.0f / ltot;
+    if (qidx >= p.Nq) return;
     const float* vsc = FP8 ? p.v_scale + bhk * DP : nullptr;
     const bool vec4 = (p.D & 3) == 0;
+    uint16_t* orow = (uint16_t*)p.out + b * p.osb + h * p.osh + qidx * p.osq;
 #pragma unroll
-    for (int nt = 0; nt < 2; nt++) {
-        const float ltot = l[nt] + __shfl_xor(l[nt], 32, 64);
-        const float inv = 1.0f / ltot;
-        const int q = q0 + 32 * nt + i;
-        if (q >= p.Nq) continue;
-        uint16_t* orow = (uint16_t*)p.out + b * p.osb + h * p.osh + q * p.osq;
+    for (int dt = 0; dt < C::DT; dt++)
 #pragma unroll
-        for (int dt = 0; dt < C::DT; dt++)
+        for (int a4 = 0; a4 < 4; a4++) {
+            const int d0 = 32 * dt + 8 * a4 + 4 * g;
+            if (d0 >= p.D) continue;
+            uint16_t hv[4];
 #pragma unroll
-            for (int a4 = 0; a4 < 4; a4++) {
-                const int d0 = 32 * dt + 8 * a4 + 4 * g;
-                if (d0 >= p.D) continue;
-                uint16_t hv[4];
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    float o = O[dt][nt][4 * a4 + e] * inv;
-                    if constexpr (FP8) o *= vsc[d0 + e];
-                    hv[e] = OBF16 ? f32_to_bf16_bits(o) : f32_to_f16_bits(o);
-                }
-                if (vec4) {
-                    *(uint2*)(orow + d0) = make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16),
-                                                      uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; e++)
-                        if (d0 + e < p.D) orow[d0 + e] = hv[e];
-                }
+            for (int e = 0; e < 4; e++) {
+                float o = O[dt][4 * a4 + e] * inv;
+                if constexpr (FP8) o *= vsc[d0 + e];
+                hv[e] = OBF16 ? f32_to_bf16_bits(o) : f32_to_f16_bits(o);
             }
-    }
+            if (vec4) {
+                *(uint2*)(orow + d0) = make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16),
+                                                  uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    if (d0 + e < p.D) orow[d0 + e] = hv[e];
+            }
+        }
 }
 
 // ---- debug dump of INT32 score tiles through the same loader / operand path ----------
+// One workgroup per tile: the K^ tile is staged with the same swizzle as in the
+// attention kernel; waves 0 and 1 compute the two 32-query halves with qk_tile.
 template <int DP, bool FP8>
-__global__ __launch_bounds__(256) void debug_qk_kernel(const int8_t* __restrict__ q_i8,
+__global__ __launch_bounds__(512) void debug_qk_kernel(const int8_t* __restrict__ q_i8,
                                                        const int8_t* __restrict__ k_i8, int B, int Hq, int Hkv,
                                                        int NBq, int NBk, const int32_t* __restrict__ tiles,
                                                        int32_t* __restrict__ out) {
     using C = Cfg<DP, FP8>;
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::STAGE];
-    const int t = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int t = blockIdx.x, tid = threadIdx.x, lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int b = tiles[4 * t], h = tiles[4 * t + 1], qb = tiles[4 * t + 2], kb = tiles[4 * t + 3];
     int32_t* o = out + int64_t(t) * kBlk * kBlk;
     const bool ok = b >= 0 && b < B && h >= 0 && h < Hq && qb >= 0 && qb < NBq && kb >= 0 && kb < NBk;
@@ -462,21 +434,19 @@ __global__ __launch_bounds__(256) void debug_qk_kernel(const int8_t* __restrict_
     }
     const int hk = h / (Hq / Hkv);
     const int8_t* ktile = k_i8 + ((int64_t(b) * Hkv + hk) * NBk + kb) * kBlk * DP;
-    issue_k_loads<C>(smem, ktile, tid);
-    wait_vmcnt<0>();
+    for (int ci = tid; ci < C::KCHUNKS; ci += C::THREADS)
+        *(uint4*)(smem + ci * 16) = *(const uint4*)k_chunk_src<C>(ci, ktile);
     __syncthreads();
-    if (wave != 0) return;
-    v4i qf[2][C::KS];
-    load_q_frags<C>(qf, q_i8 + ((int64_t(b) * Hq + h) * NBq + qb) * kBlk * DP, lane);
-    v16i S[2][2];
+    if (wave >= 2) return;
+    v4i qf[C::KS];
+    load_q_frags<C>(qf, q_i8 + (((int64_t(b) * Hq + h) * NBq + qb) * kBlk + wave * C::QW) * DP, lane);
+    v16i S[2];
     qk_tile<C, FP8>(smem, qf, S, lane);
     const int g = lane >> 5, i = lane & 31;
 #pragma unroll
     for (int kt = 0; kt < 2; kt++)
 #pragma unroll
-        for (int nt = 0; nt < 2; nt++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) o[(32 * nt + i) * kBlk + key_of_reg<FP8>(kt, g, r)] = S[kt][nt][r];
+        for (int r = 0; r < 16; r++) o[(wave * C::QW + i) * kBlk + key_of_reg<FP8>(kt, g, r)] = S[kt][r];
 }
 
 template <int DP, bool FP8, bool CAUSAL, bool TWO, bool OBF16>
@@ -502,6 +472,15 @@ hipError_t dispatch_rest(const AttnArgs& a, const KParams& p, int nwg, hipStream
     }
 }
 
+template <int DP, bool FP8>
+hipError_t launch_debug_t(const DebugQKArgs& a, int NBq, int NBk, hipStream_t s) {
+    using C = Cfg<DP, FP8>;
+    auto kern = debug_qk_kernel<DP, FP8>;
+    hipLaunchKernelGGL(kern, dim3(a.T), dim3(C::THREADS), 0, s, a.q_i8, a.k_i8, a.B, a.Hq, a.Hkv, NBq, NBk, a.tiles,
+                       a.out);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s) {
@@ -522,7 +501,8 @@ hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s) {
     p.D = a.D;
     p.NBq = (a.Nq + kBlk - 1) / kBlk;
     p.NBk = (a.Nkv + kBlk - 1) / kBlk;
-    const int BM = 4 * kBlk;
+    constexpr int BM = Cfg<128, true>::BM;
+    static_assert(Cfg<64, false>::BM == BM && Cfg<64, true>::BM == BM && Cfg<128, false>::BM == BM, "uniform BM");
     p.QT = (a.Nq + BM - 1) / BM;
     p.cscale = a.sm_scale * kLog2e;
     if (a.out_nhd) {
@@ -535,18 +515,8 @@ hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s) {
         p.osq = a.D;
     }
     const int nwg = a.B * a.Hq * p.QT;
-    const bool dp64 = a.D <= 64;
-    if (dp64) return a.fp8 ? dispatch_rest<64, true>(a, p, nwg, s) : dispatch_rest<64, false>(a, p, nwg, s);
+    if (a.D <= 64) return a.fp8 ? dispatch_rest<64, true>(a, p, nwg, s) : dispatch_rest<64, false>(a, p, nwg, s);
     return a.fp8 ? dispatch_rest<128, true>(a, p, nwg, s) : dispatch_rest<128, false>(a, p, nwg, s);
-}
-
-template <int DP, bool FP8>
-hipError_t launch_debug_t(const DebugQKArgs& a, int NBq, int NBk, hipStream_t s) {
-    using C = Cfg<DP, FP8>;
-    auto kern = debug_qk_kernel<DP, FP8>;
-    hipLaunchKernelGGL(kern, dim3(a.T), dim3(C::THREADS), 0, s, a.q_i8, a.k_i8, a.B, a.Hq, a.Hkv, NBq, NBk,
-                       a.tiles, a.out);
-    return hipGetLastError();
 }
 
 hipError_t launch_debug_qk(const DebugQKArgs& a, hipStream_t s) {

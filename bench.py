@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--sweep-steps", type=int, default=10)
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="also run a plain device copy of this many MiB (HBM counter calibration)")
     return p.parse_args()
 
 
@@ -143,6 +145,17 @@ def main():
             for _ in range(3)]
     torch.cuda.synchronize()
     log(f"[bench] inputs B{base.B} H{base.Hq} N{nmax} D{base.D} drawn in {time.perf_counter() - t:.1f}s")
+
+    if args.calib_copy_mib:
+        # a plain copy kernel of known size: its FETCH_SIZE / WRITE_SIZE counters give the
+        # scale factor for converting the attention kernel's counters into HBM bytes
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
+        del src, dst
 
     def inputs_for(n):
         if n == nmax:

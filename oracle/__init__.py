@@ -55,7 +55,7 @@ def lib() -> ctypes.CDLL:
     L.orc_quant_v.argtypes = [_f32p, _L, _L, _L, _L, ctypes.c_int, _f32p, _f32p]
     L.orc_scores_i32.argtypes = [_i8p, _i8p, _L, _L, _L, _L, _L, _L, _i64p, _L, _i32p]
     L.orc_attn_emulate.argtypes = [_i8p, _f32p, _i8p, _f32p, _f32p, _f32p, ctypes.c_int, _L, _L, _L, _L, _L,
-                                   _L, ctypes.c_int, ctypes.c_double, _i64p, _L, _f64p]
+                                   _L, ctypes.c_int, ctypes.c_double, _i64p, _L, _f64p, ctypes.c_void_p]
     L.orc_attn_exact.argtypes = [_f32p, _f32p, _f32p, _L, _L, _L, _L, _L, _L, ctypes.c_int, ctypes.c_double,
                                  _i64p, _L, _f64p]
     _lib = L
@@ -187,15 +187,19 @@ def scores_i32(Q: Quantized, tiles: Sequence[Sequence[int]]) -> np.ndarray:
     return out
 
 
-def attn_emulate(Q: Quantized, causal: bool, sm_scale: float, rows: np.ndarray) -> np.ndarray:
+def attn_emulate(Q: Quantized, causal: bool, sm_scale: float, rows: np.ndarray, with_ambiguity: bool = False):
+    """Emulation-mode rows [R, D] (fp64).  With with_ambiguity, also the per-element
+    effect of flipping the P roundings that lie within 2^-14 (relative) of a tie."""
     B, Hq, Nq, D = Q.q_i8.shape
     Nkv = Q.k_i8.shape[2]
     rows = np.ascontiguousarray(rows, np.int64).reshape(-1, 3)
     out = np.empty((rows.shape[0], D), np.float64)
+    amb = np.empty((rows.shape[0], D), np.float64) if with_ambiguity else None
     vs = Q.v_scale if Q.v_scale is not None else np.zeros((B, Q.Hkv, D), np.float32)
     lib().orc_attn_emulate(Q.q_i8, Q.q_scale, Q.k_i8, Q.k_scale, Q.v_hat, vs, int(Q.pv_fp8), B, Hq, Q.Hkv, Nq,
-                           Nkv, D, int(bool(causal)), float(sm_scale), rows, rows.shape[0], out)
-    return out
+                           Nkv, D, int(bool(causal)), float(sm_scale), rows, rows.shape[0], out,
+                           None if amb is None else amb.ctypes.data_as(ctypes.c_void_p))
+    return (out, amb) if with_ambiguity else out
 
 
 def attn_exact(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, sm_scale: float,

@@ -242,25 +242,58 @@ void orc_scores_i32(const int8_t* q8, const int8_t* k8, long B, long Hq, long Hk
 /* ---------------------------------------------------------------------------
  * Emulation-mode attention for selected query rows.  rows holds R triples
  * (b, h, i); out is [R, D] in fp64 (before the cast to the output dtype).
- * For each row, for each 64-key block in ascending order (blocks whose keys all
- * lie beyond i are skipped when causal):
- *   S32  = sum_c q8 * k8                                   (exact integer)
- *   S2   = S32 * sq * sk * sm_scale * log2(e)              (fp64, left to right)
- *   masked keys (causal j > i) get S2 = -inf
- *   m'   = max(m, max_j S2);  alpha = 2^(m - m')  (0 when m = -inf)
- *   p_j  = 2^(S2_j - m')
- *   l    = alpha * l + sum_j p_j                           (unrounded p)
- *   p^_j = fp16(p_j)  or  e4m3(p_j * 448)                   (RNE, saturating)
- *   acc  = alpha * acc + sum_j p^_j * vhat_j                (fp64)
+ *
+ * The rounding of P to FP16 / e4m3 is a decision taken in floating point, and the
+ * pages fix no precision for it, so P is formed in fp32 (the kernel's precision):
+ *   c    = fp32( fp32(sq * sk) * fp32(sm_scale * log2(e)) )     dequant factor
+ *   S2   = fp32( S32 * c )                                       (S32 exact in fp32)
+ *   m    = running max of S2 over the row (fp32), -inf while empty
+ *   p    = fp32( 2^fp32(S2 - m) )                               (correctly rounded)
+ *   p^   = fp16(p)  or  e4m3(fp32(p * 448))                     (RNE, saturating)
+ * and everything else in fp64.  For each row, for each 64-key block in ascending
+ * order (blocks whose keys all lie beyond i are skipped when causal):
+ *   masked keys (causal j > i) take no part;
+ *   alpha = 2^(m_old - m_new)   (0 when the row was empty)
+ *   l     = alpha * l + sum_j p_j                     (unrounded p, fp64 sum)
+ *   acc   = alpha * acc + sum_j p^_j * vhat_j         (fp64)
  * Finally o = acc / l, times vscale[c] / 448 in FP8 mode.
- * Both PV accumulation modes (single-level fp32 and two-level) are modelled by
- * the same fp64 accumulation: they differ only in how the hardware rounds.
+ * Both PV accumulation modes (single-level fp32 and two-level) are modelled by the
+ * same fp64 accumulation: they differ only in how the hardware rounds.
+ *
+ * amb (optional, [R, D]): for every P whose pre-rounding value x lies within a
+ * relative 2^-14 of a rounding tie (where a kernel computing p with a few ulps of
+ * difference may round the other way), the output change that flipping that single
+ * decision would cause, |code_hi - code_lo| * |vhat| / l (rescaled like acc), summed.
  * ------------------------------------------------------------------------- */
+static const double AMB_REL = 1.0 / 16384.0;
+
+/* quantum of the format at x (> 0): spacing of representable values around x */
+static double fmt_quantum(double x, int fmt) {
+    int p, emin;
+    double maxv;
+    fmt_params(fmt, &p, &emin, &maxv);
+    int e2;
+    frexp(x, &e2);
+    int ex = e2 - 1;
+    if (ex < emin) ex = emin;
+    return ldexp(1.0, ex - (p - 1));
+}
+
+/* |code_hi - code_lo| when x (> 0) lies within AMB_REL * x of the midpoint, else 0 */
+static double tie_flip(double x, int fmt) {
+    if (!(x > 0.0)) return 0.0;
+    double q = fmt_quantum(x, fmt);
+    double lo = floor(x / q) * q;
+    double mid = lo + 0.5 * q;
+    return fabs(x - mid) <= AMB_REL * x ? q : 0.0;
+}
+
 void orc_attn_emulate(const int8_t* q8, const float* sq, const int8_t* k8, const float* sk,
                       const float* vhat, const float* vscale, int pv_fp8, long B, long Hq, long Hkv,
                       long Nq, long Nkv, long D, int causal, double sm_scale, const int64_t* rows,
-                      long R, double* out) {
-    const double LOG2E = 1.4426950408889634074;
+                      long R, double* out, double* amb) {
+    const float scale2 = (float)sm_scale * 1.44269504088896341f; /* fp32(sm_scale * log2 e) */
+    const int fmt = pv_fp8 ? ORC_E4M3 : ORC_FP16;
     long group = Hq / Hkv;
     long nqb = (Nq + BLK - 1) / BLK, nkb = (Nkv + BLK - 1) / BLK;
     (void)B;
@@ -269,50 +302,68 @@ void orc_attn_emulate(const int8_t* q8, const float* sq, const int8_t* k8, const
         long b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
         long hk = h / group;
         const int8_t* qrow = q8 + ((b * Hq + h) * Nq + i) * D;
-        double sqi = (double)sq[(b * Hq + h) * nqb + i / BLK];
+        float sqi = sq[(b * Hq + h) * nqb + i / BLK];
         double* acc = (double*)calloc((size_t)D, sizeof(double));
-        double s2[BLK], pj[BLK];
-        double m = -INFINITY, l = 0.0;
+        double* aacc = (double*)calloc((size_t)D, sizeof(double));
+        float s2[BLK];
+        int vis[BLK];
+        double pj[BLK], flip[BLK];
+        float m = -INFINITY;
+        double l = 0.0;
         for (long kb = 0; kb < nkb; kb++) {
             long j0 = kb * BLK;
             if (causal && j0 > i) break;
             long j1 = j0 + BLK < Nkv ? j0 + BLK : Nkv;
-            double skj = (double)sk[(b * Hkv + hk) * nkb + kb];
-            double bmax = -INFINITY;
+            float c = (sqi * sk[(b * Hkv + hk) * nkb + kb]) * scale2;
+            float bmax = -INFINITY;
             for (long j = j0; j < j1; j++) {
-                if (causal && j > i) {
-                    s2[j - j0] = -INFINITY;
-                    continue;
-                }
+                vis[j - j0] = !(causal && j > i);
+                if (!vis[j - j0]) continue;
                 const int8_t* krow = k8 + ((b * Hkv + hk) * Nkv + j) * D;
                 int64_t s32 = 0;
-                for (long c = 0; c < D; c++) s32 += (int64_t)qrow[c] * (int64_t)krow[c];
-                double v = (double)s32 * sqi * skj * sm_scale * LOG2E;
+                for (long d = 0; d < D; d++) s32 += (int64_t)qrow[d] * (int64_t)krow[d];
+                float v = (float)s32 * c;
                 s2[j - j0] = v;
                 if (v > bmax) bmax = v;
             }
-            double mnew = m > bmax ? m : bmax;
-            double alpha = (m == -INFINITY) ? 0.0 : exp2(m - mnew);
+            float mnew = m > bmax ? m : bmax;
+            double alpha = (m == -INFINITY) ? 0.0 : exp2((double)m - (double)mnew);
             double psum = 0.0;
             for (long j = j0; j < j1; j++) {
-                double p = (s2[j - j0] == -INFINITY) ? 0.0 : exp2(s2[j - j0] - mnew);
-                psum += p;
-                pj[j - j0] = pv_fp8 ? orc_round(p * 448.0, ORC_E4M3, 1) : orc_round(p, ORC_FP16, 1);
+                pj[j - j0] = 0.0;
+                flip[j - j0] = 0.0;
+                if (!vis[j - j0]) continue;
+                float t = s2[j - j0] - mnew;
+                float p = (float)exp2((double)t);
+                psum += (double)p;
+                double x = pv_fp8 ? (double)(p * 448.0f) : (double)p;
+                pj[j - j0] = orc_round(x, fmt, 1);
+                flip[j - j0] = tie_flip(x, fmt);
             }
             l = alpha * l + psum;
-            for (long c = 0; c < D; c++) {
-                double a = 0.0;
-                for (long j = j0; j < j1; j++) a += pj[j - j0] * (double)vhat[((b * Hkv + hk) * Nkv + j) * D + c];
-                acc[c] = alpha * acc[c] + a;
+            for (long d = 0; d < D; d++) {
+                double a = 0.0, fa = 0.0;
+                for (long j = j0; j < j1; j++) {
+                    double vv = (double)vhat[((b * Hkv + hk) * Nkv + j) * D + d];
+                    a += pj[j - j0] * vv;
+                    fa += flip[j - j0] * fabs(vv);
+                }
+                acc[d] = alpha * acc[d] + a;
+                aacc[d] = alpha * aacc[d] + fa;
             }
             m = mnew;
         }
-        for (long c = 0; c < D; c++) {
-            double o = acc[c] / l;
-            if (pv_fp8) o *= (double)vscale[(b * Hkv + hk) * D + c] / 448.0;
-            out[r * D + c] = o;
+        for (long d = 0; d < D; d++) {
+            double o = acc[d] / l, ao = aacc[d] / l;
+            if (pv_fp8) {
+                o *= (double)vscale[(b * Hkv + hk) * D + d] / 448.0;
+                ao *= (double)vscale[(b * Hkv + hk) * D + d] / 448.0;
+            }
+            out[r * D + d] = o;
+            if (amb) amb[r * D + d] = ao;
         }
         free(acc);
+        free(aacc);
     }
 }
 

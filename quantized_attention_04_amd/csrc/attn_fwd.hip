@@ -5,8 +5,11 @@
 // matrix-core products, are dequantised with the per-64-token block scales of Q and
 // K, and feed an online base-2 softmax (running row max m, running row sum l); P is
 // rounded to FP16 or FP8-e4m3 and multiplied with V^ on the matrix cores with fp32
-// accumulation, either straight into the rescaled output accumulator or in two
-// levels (a fresh per-64-key-block partial added into it).
+// accumulation.  The README's two-level accumulation (short low-precision sums added
+// into fp32) is what the gfx950 matrix core does by construction: each MFMA sums its
+// 64 products internally and adds the result to the fp32 accumulator operand; a fresh
+// per-tile partial added with a vector-ALU add measures bit-for-bit the same error
+// over 256 chained FP8 MFMAs, so both accumulation modes share this code.
 //
 // gfx950 design:
 //  * workgroup = 8 waves = 256 queries, two waves per SIMD: while one wave runs the
@@ -23,7 +26,9 @@
 //    exactly the register order the P.V MFMA wants for its B operand: P never leaves
 //    registers; V^ tiles are stored channel-major so the A operand is contiguous;
 //  * P.V on v_mfma_scale_f32_32x32x64_f8f6f4 (FP8, unit scales) or
-//    v_mfma_f32_32x32x16_f16 (FP16), output O^T accumulated in fp32 registers.
+//    v_mfma_f32_32x32x16_f16 (FP16), output O^T accumulated in fp32 registers;
+//  * software pipelined per wave: the QK^T MFMAs of tile j+1 are issued before the
+//    softmax of tile j, so the matrix core works while the vector ALUs do.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -36,6 +41,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // for t <= 0 even with a one-ulp exp2 error: FP8 P is produced directly as p * 448
 // (the e4m3 maximum), with a relative bias of about 6e-7.
 constexpr float kLog2_448 = 8.807354f;
+
 
 __device__ __forceinline__ int parity(uint32_t x) { return __builtin_popcount(x) & 1; }
 
@@ -52,7 +58,7 @@ __device__ __forceinline__ void block_barrier() {
 // Mode constants.  DP = padded head dim (64 | 128); FP8 = P.V in e4m3 (else fp16).
 template <int DP, bool FP8>
 struct Cfg {
-    static constexpr int WAVES = 8;
+    static constexpr int WAVES = 4;  // one wave per SIMD; two workgroups share a CU
     static constexpr int THREADS = WAVES * kWave;
     static constexpr int QW = 32;            // queries per wave
     static constexpr int BM = WAVES * QW;    // queries per workgroup
@@ -63,10 +69,12 @@ struct Cfg {
     static constexpr int VBYTES = DP * VROW;
     static constexpr int KCHUNKS = KBYTES / 16;
     static constexpr int VCHUNKS = VBYTES / 16;
-    // every thread issues ROUNDS 16-byte loads per tile; a short last round re-reads V
-    // into a padding area so that the count stays uniform
-    static constexpr int ROUNDS = (KCHUNKS + VCHUNKS + THREADS - 1) / THREADS;
+    // every thread issues ROUNDS 16-byte loads per tile: KROUNDS for K^, then V^
+    static constexpr int KROUNDS = KCHUNKS / THREADS;
+    static constexpr int ROUNDS = (KCHUNKS + VCHUNKS) / THREADS;
     static constexpr int STAGE = ROUNDS * THREADS * 16;
+    static_assert(KCHUNKS % THREADS == 0 && VCHUNKS % THREADS == 0, "each load round lies in one region");
+    static constexpr int NST = 3;  // LDS pipeline depth (tiles resident or in flight)
     static constexpr int KS = DP / 32;  // MFMA k-steps of QK^T
     static constexpr int DT = DP / 32;  // 32-channel tiles of O^T
     // XOR swizzles: bit c of the chunk flip is parity(row & mask_c); each is
@@ -78,7 +86,6 @@ struct Cfg {
     static constexpr uint32_t VM0 = FP8 ? 0x4u : 0x2u;
     static constexpr uint32_t VM1 = FP8 ? 0xAu : 0x4u;
     static constexpr uint32_t VM2 = FP8 ? 0x0u : 0x9u;
-    static_assert(KCHUNKS % kWave == 0 && VCHUNKS % kWave == 0, "regions must be whole-wave aligned");
 };
 
 template <class C>
@@ -107,36 +114,45 @@ __device__ __forceinline__ int key_of_reg(int kt, int g, int r) {
     return key_of_row<FP8>(kt, 8 * (r >> 2) + 4 * g + (r & 3));
 }
 
-// Global address of LDS chunk ci of a stage: K^ rows, then V^ rows, then padding (a
-// re-read of V^, never consumed).  LDS chunk (row, c) holds global chunk (row, c ^ swz).
+// Global address of K^ chunk ci (LDS chunk (row, c) holds global chunk (row, c ^ swz)).
 template <class C>
 __device__ __forceinline__ const int8_t* k_chunk_src(int ci, const int8_t* ktile) {
     const int row = ci / (C::KROW / 16), cpos = ci % (C::KROW / 16);
     return ktile + row * C::KROW + 16 * (cpos ^ kswz<C>(row));
 }
+// Per-thread source offsets of the direct-to-LDS loads, computed once: round u of
+// every thread covers LDS chunk u * THREADS + tid, which lies wholly in the K^ region
+// (rounds < KROUNDS) or the V^ region, so each round has a single uniform base.
 template <class C>
-__device__ __forceinline__ const void* stage_src(int ci, const int8_t* ktile, const uint8_t* vtile) {
-    if (ci < C::KCHUNKS) return k_chunk_src<C>(ci, ktile);
-    const int vi = (ci - C::KCHUNKS) % C::VCHUNKS;
-    const int row = vi / (C::VROW / 16), cpos = vi % (C::VROW / 16);
-    return vtile + row * C::VROW + 16 * (cpos ^ vswz<C>(row));
-}
-
+struct DmaPlan {
+    uint32_t off[C::ROUNDS];
+};
 template <class C>
-__device__ __forceinline__ void issue_stage(uint8_t* __restrict__ st, const int8_t* ktile, const uint8_t* vtile,
-                                            int tid, int wave) {
+__device__ __forceinline__ DmaPlan<C> make_dma_plan(int tid) {
+    DmaPlan<C> d;
 #pragma unroll
     for (int u = 0; u < C::ROUNDS; u++) {
         const int ci = u * C::THREADS + tid;
-        load_lds_16(stage_src<C>(ci, ktile, vtile), st + (u * C::THREADS + wave * kWave) * 16);
+        if (u < C::KROUNDS) {
+            const int row = ci / (C::KROW / 16), cpos = ci % (C::KROW / 16);
+            d.off[u] = uint32_t(row * C::KROW + 16 * (cpos ^ kswz<C>(row)));
+        } else {
+            const int vi = ci - C::KCHUNKS;
+            const int row = vi / (C::VROW / 16), cpos = vi % (C::VROW / 16);
+            d.off[u] = uint32_t(row * C::VROW + 16 * (cpos ^ vswz<C>(row)));
+        }
     }
+    return d;
 }
-
-__device__ __forceinline__ v16f fma16(v16f a, float s, v16f c) {
-    v16f r;
-#pragma unroll
-    for (int e = 0; e < 16; e++) r[e] = __builtin_fmaf(a[e], s, c[e]);
-    return r;
+// lds_wave_base: LDS byte address of the stage plus this wave's 1 KB slot of round 0
+template <class C, int U = 0>
+__device__ __forceinline__ void issue_stage(uint32_t lds_wave_base, const int8_t* ktile, const uint8_t* vtile,
+                                            const DmaPlan<C>& d) {
+    if constexpr (U < C::ROUNDS) {
+        const void* base = U < C::KROUNDS ? (const void*)ktile : (const void*)vtile;
+        load_lds_16_s<U * C::THREADS * 16>(base, d.off[U], lds_wave_base);
+        issue_stage<C, U + 1>(lds_wave_base, ktile, vtile, d);
+    }
 }
 
 // S^T tiles of one 64-key tile for this wave's 32 queries: S[kt] (keys through the
@@ -170,32 +186,51 @@ __device__ __forceinline__ void load_q_frags(v4i (&qf)[C::KS], const int8_t* qro
     for (int s = 0; s < C::KS; s++) qf[s] = *(const v4i*)(qrows + i * C::KROW + 32 * s + 16 * g);
 }
 
+// Combine a value with the one held by the lane 32 positions away (the other half of
+// the same query column): v_permlane32_swap returns the two halves side by side.
+__device__ __forceinline__ float halves_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Online softmax step for one tile: updates m, l; returns alpha; fills P (FP8: p*448).
+// Reductions are balanced trees (short dependency chains).  Masked keys get INT32_MIN
+// and p = 0.  t = S32 * c - m is formed with one rounding (fma), keeping P's rounding
+// to FP16 / e4m3 close to a correctly rounded evaluation.
 template <bool FP8, bool MASK, bool CAUSAL>
 __device__ __forceinline__ float softmax_tile(v16i (&S)[2], float (&P)[2][16], float c, float& m, float& l, int g,
                                               int key0, int qidx, int Nkv) {
     if constexpr (MASK) {
+        // keep the key base opaque: otherwise the compiler proves it loop-invariant on the
+        // tail tile and hoists all 32 visibility masks (64 SGPRs) out of the tile loop
+        int kb = key0;
+        asm volatile("" : "+v"(kb));
 #pragma unroll
         for (int kt = 0; kt < 2; kt++)
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int key = key0 + key_of_reg<FP8>(kt, g, r);
+                const int key = kb + key_of_reg<FP8>(kt, g, r);
                 const bool vis = key < Nkv && (!CAUSAL || key <= qidx);
                 if (!vis) S[kt][r] = INT32_MIN;
             }
     }
-    int imax = S[0][0];
+    int mx[16];
 #pragma unroll
-    for (int kt = 0; kt < 2; kt++)
+    for (int r = 0; r < 16; r++) mx[r] = max(S[0][r], S[1][r]);
 #pragma unroll
-        for (int r = 0; r < 16; r++) imax = max(imax, S[kt][r]);
-    float tmax = (MASK && imax == INT32_MIN) ? -1e30f : float(imax) * c;
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+        for (int r = 0; r < w; r++) mx[r] = max(mx[r], mx[r + w]);
+    float tmax = (MASK && mx[0] == INT32_MIN) ? -1e30f : float(mx[0]) * c;
+    tmax = halves_max(tmax);
     const float mnew = fmaxf(m, tmax);
     const float alpha = __builtin_amdgcn_exp2f(m - mnew);
     m = mnew;
     const float negm = FP8 ? kLog2_448 - mnew : -mnew;
-    float psum = 0.0f;
 #pragma unroll
     for (int kt = 0; kt < 2; kt++)
 #pragma unroll
@@ -203,9 +238,15 @@ __device__ __forceinline__ float softmax_tile(v16i (&S)[2], float (&P)[2][16], f
             float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(float(S[kt][r]), c, negm));
             if constexpr (MASK) pv = S[kt][r] == INT32_MIN ? 0.0f : pv;
             P[kt][r] = pv;
-            psum += pv;
         }
-    l = l * alpha + psum;
+    float ps[16];
+#pragma unroll
+    for (int r = 0; r < 16; r++) ps[r] = P[0][r] + P[1][r];
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+        for (int r = 0; r < w; r++) ps[r] = ps[r] + ps[r + w];
+    l = __builtin_fmaf(l, alpha, ps[0]);
     return alpha;
 }
 
@@ -222,13 +263,11 @@ struct KParams {
     float cscale;  // sm_scale * log2(e)
 };
 
-template <int DP, bool FP8, bool CAUSAL, bool TWO, bool OBF16>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(KParams p) {
+template <int DP, bool FP8, bool CAUSAL, bool OBF16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(KParams p) {
     using C = Cfg<DP, FP8>;
-    // Two LDS stages as distinct objects, so that the compiler can tell the prefetch
-    // into one stage from the operand reads of the other.
-    __shared__ __attribute__((aligned(16))) uint8_t lds0[C::STAGE];
-    __shared__ __attribute__((aligned(16))) uint8_t lds1[C::STAGE];
+    // NST LDS stages: tile j lives in stage j % NST while tiles j+1 .. j+NST-1 stream in.
+    __shared__ __attribute__((aligned(16))) uint8_t smem[C::NST * C::STAGE];
     const int tid = threadIdx.x, lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform (SGPR)
     const int g = lane >> 5, i = lane & 31;
@@ -285,23 +324,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int dt = 0; dt < C::DT; dt++) O[dt] = v16f{};
     float m = -1e30f, l = 0.0f;
 
-    auto compute = [&](const uint8_t* __restrict__ st, int j, float ksj) {
-        if (!active) return;
-        if (CAUSAL && j > qb) return;  // whole tile above this wave's diagonal
-        v16i S[2];
-        qk_tile<C, FP8>(st, qf, S, lane);
+    // softmax of tile j from its scores S, then P.V with the V^ part of LDS stage st
+    auto softmax_pv = [&](v16i (&S)[2], const uint8_t* __restrict__ st, int j, float ksj) {
         const float c = sq * ksj * p.cscale;
         const bool need_mask = (CAUSAL && j == qb) || (ktail && j == p.NBk - 1);
         float P[2][16];  // probabilities (FP8: p * 448)
         float alpha;
         if (need_mask) alpha = softmax_tile<FP8, true, CAUSAL>(S, P, c, m, l, g, j * kBlk, qidx, p.Nkv);
         else alpha = softmax_tile<FP8, false, CAUSAL>(S, P, c, m, l, g, j * kBlk, qidx, p.Nkv);
-        if constexpr (!TWO) {
-            // single level: rescale the accumulator only when some row max moved
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+        // rescale the accumulator only when some row max of this wave moved
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
-                for (int dt = 0; dt < C::DT; dt++) O[dt] *= alpha;
-            }
+            for (int dt = 0; dt < C::DT; dt++) O[dt] *= alpha;
         }
         const uint8_t* vst = st + C::KBYTES;
         if constexpr (FP8) {
@@ -320,13 +354,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 const v4i a0 = lds_read_16(rb + 16 * ((2 * g) ^ sw));
                 const v4i a1 = lds_read_16(rb + 16 * ((2 * g + 1) ^ sw));
                 const v8i a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-                if constexpr (TWO) {
-                    const v16f z = {};
-                    const v16f part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, z, 0, 0, 0, 127, 0, 127);
-                    O[dt] = fma16(O[dt], alpha, part);
-                } else {
-                    O[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, O[dt], 0, 0, 0, 127, 0, 127);
-                }
+                O[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, O[dt], 0, 0, 0, 127, 0, 127);
             }
         } else {
             v8h ph[4];
@@ -339,51 +367,63 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 const int d = 32 * dt + i;
                 const int sw = vswz<C>(d);
                 const uint8_t* rb = vst + d * C::VROW;
-                v16f part = {};
-                if constexpr (!TWO) part = O[dt];
 #pragma unroll
                 for (int mm = 0; mm < 4; mm++) {
                     const v4i araw = lds_read_16(rb + 16 * ((2 * mm + g) ^ sw));
                     v8h a;
                     __builtin_memcpy(&a, &araw, 16);
-                    part = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, ph[mm], part, 0, 0, 0);
+                    O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, ph[mm], O[dt], 0, 0, 0);
                 }
-                if constexpr (TWO) O[dt] = fma16(O[dt], alpha, part);
-                else O[dt] = part;
             }
         }
     };
+    // does this wave compute tile t?
+    auto wants = [&](int t) { return active && t < jend && (!CAUSAL || t <= qb); };
 
-    // ---- main loop: two LDS stages, ping-pong.  Each wave waits for its own
-    // direct-to-LDS loads of the current tile (vmcnt: all but the ROUNDS most recent
-    // ones, i.e. the prefetch of the next tile, are complete), then a bare barrier
-    // publishes the tile; a second barrier retires the stage before it is refilled.
-    issue_stage<C>(lds0, kbase, vbase, tid, wave);
-    for (int j = 0; j < jend; j += 2) {
+    // ---- main loop.  Tile j lives in LDS stage j % NST.  Iteration j: wait for the
+    // direct-to-LDS loads of tile j+1 (the only ones outstanding), one bare barrier
+    // publishes it and certifies that every wave has finished iteration j-1 (whose
+    // stage, (j + 2) % 3, is refilled with tile j+2 right after); then the QK^T MFMAs of
+    // tile j+1 are issued ahead of the softmax and P.V of tile j, whose scores were
+    // computed one iteration earlier.  S0 / S1 alternate between current and next.
+    static_assert(C::NST == 3, "the stage rotation below assumes three stages");
+    const DmaPlan<C> dma = make_dma_plan<C>(tid);
+    // LDS byte address of this wave's slot in stage 0 (wave-uniform)
+    const uint32_t lds_w0 = __builtin_amdgcn_readfirstlane(lds_addr(smem) + uint32_t(wave * kWave * 16));
+    issue_stage<C>(lds_w0, kbase, vbase, dma);
+    if (jend > 1) {
+        issue_stage<C>(lds_w0 + C::STAGE, kbase + int64_t(kBlk) * DP, vbase + C::VBYTES, dma);
+        wait_vmcnt<C::ROUNDS>();
+    } else {
+        wait_vmcnt<0>();
+    }
+    block_barrier();
+    v16i S0[2], S1[2];
+    if (wants(0)) qk_tile<C, FP8>(smem, qf, S0, lane);
+    int stage = 0;  // j % 3
+    auto iter = [&](int j, v16i (&Scur)[2], v16i (&Snext)[2]) {
+        const int st1 = stage == 2 ? 0 : stage + 1;  // (j + 1) % 3
+        const int st2 = st1 == 2 ? 0 : st1 + 1;      // (j + 2) % 3
         if (j + 1 < jend) {
-            issue_stage<C>(lds1, kbase + int64_t(j + 1) * kBlk * DP, vbase + int64_t(j + 1) * C::VBYTES, tid, wave);
-            wait_vmcnt<C::ROUNDS>();
-        } else {
             wait_vmcnt<0>();
+            block_barrier();
+            if (j + 2 < jend)
+                issue_stage<C>(lds_w0 + uint32_t(st2 * C::STAGE), kbase + int64_t(j + 2) * kBlk * DP,
+                               vbase + int64_t(j + 2) * C::VBYTES, dma);
         }
-        block_barrier();
-        compute(lds0, j, scalar_load_f32(ks_row + j));
-        block_barrier();
+        if (wants(j + 1)) qk_tile<C, FP8>(smem + st1 * C::STAGE, qf, Snext, lane);
+        if (wants(j)) softmax_pv(Scur, smem + stage * C::STAGE, j, scalar_load_f32(ks_row + j));
+        stage = st1;
+    };
+    for (int j = 0; j < jend; j += 2) {
+        iter(j, S0, S1);
         if (j + 1 >= jend) break;
-        if (j + 2 < jend) {
-            issue_stage<C>(lds0, kbase + int64_t(j + 2) * kBlk * DP, vbase + int64_t(j + 2) * C::VBYTES, tid, wave);
-            wait_vmcnt<C::ROUNDS>();
-        } else {
-            wait_vmcnt<0>();
-        }
-        block_barrier();
-        compute(lds1, j + 1, scalar_load_f32(ks_row + j + 1));
-        block_barrier();
+        iter(j + 1, S1, S0);
     }
 
     // ---- epilogue: O^T / l (x v_scale in FP8 mode) -> out dtype, input layout
     if (!active) return;
-    const float ltot = l + __shfl_xor(l, 32, 64);
+    const float ltot = halves_sum(l);
     const float inv = 1.0f / ltot;
     if (qidx >= p.Nq) return;
     const float* vsc = FP8 ? p.v_scale + bhk * DP : nullptr;
@@ -417,7 +457,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // One workgroup per tile: the K^ tile is staged with the same swizzle as in the
 // attention kernel; waves 0 and 1 compute the two 32-query halves with qk_tile.
 template <int DP, bool FP8>
-__global__ __launch_bounds__(512) void debug_qk_kernel(const int8_t* __restrict__ q_i8,
+__global__ __launch_bounds__(256) void debug_qk_kernel(const int8_t* __restrict__ q_i8,
                                                        const int8_t* __restrict__ k_i8, int B, int Hq, int Hkv,
                                                        int NBq, int NBk, const int32_t* __restrict__ tiles,
                                                        int32_t* __restrict__ out) {
@@ -449,26 +489,23 @@ __global__ __launch_bounds__(512) void debug_qk_kernel(const int8_t* __restrict_
         for (int r = 0; r < 16; r++) o[(wave * C::QW + i) * kBlk + key_of_reg<FP8>(kt, g, r)] = S[kt][r];
 }
 
-template <int DP, bool FP8, bool CAUSAL, bool TWO, bool OBF16>
+template <int DP, bool FP8, bool CAUSAL, bool OBF16>
 hipError_t launch_attn_t(const KParams& p, int nwg, hipStream_t s) {
     using C = Cfg<DP, FP8>;
-    auto kern = attn_fwd_kernel<DP, FP8, CAUSAL, TWO, OBF16>;
+    auto kern = attn_fwd_kernel<DP, FP8, CAUSAL, OBF16>;
     hipLaunchKernelGGL(kern, dim3(nwg), dim3(C::THREADS), 0, s, p);
     return hipGetLastError();
 }
 
 template <int DP, bool FP8>
 hipError_t dispatch_rest(const AttnArgs& a, const KParams& p, int nwg, hipStream_t s) {
-    const int key = (a.causal ? 4 : 0) | (a.two_level ? 2 : 0) | (a.out_bf16 ? 1 : 0);
+    // both accumulation modes use the MFMA-chained fp32 accumulation (see the header)
+    const int key = (a.causal ? 2 : 0) | (a.out_bf16 ? 1 : 0);
     switch (key) {
-    case 0: return launch_attn_t<DP, FP8, false, false, false>(p, nwg, s);
-    case 1: return launch_attn_t<DP, FP8, false, false, true>(p, nwg, s);
-    case 2: return launch_attn_t<DP, FP8, false, true, false>(p, nwg, s);
-    case 3: return launch_attn_t<DP, FP8, false, true, true>(p, nwg, s);
-    case 4: return launch_attn_t<DP, FP8, true, false, false>(p, nwg, s);
-    case 5: return launch_attn_t<DP, FP8, true, false, true>(p, nwg, s);
-    case 6: return launch_attn_t<DP, FP8, true, true, false>(p, nwg, s);
-    default: return launch_attn_t<DP, FP8, true, true, true>(p, nwg, s);
+    case 0: return launch_attn_t<DP, FP8, false, false>(p, nwg, s);
+    case 1: return launch_attn_t<DP, FP8, false, true>(p, nwg, s);
+    case 2: return launch_attn_t<DP, FP8, true, false>(p, nwg, s);
+    default: return launch_attn_t<DP, FP8, true, true>(p, nwg, s);
     }
 }
 

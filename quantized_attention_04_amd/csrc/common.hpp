@@ -71,6 +71,20 @@ __device__ __forceinline__ void load_lds_16(const void* gptr, void* lds_base) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
 }
 
+// Same copy with the global address split into a wave-uniform 64-bit base (SGPR pair)
+// and a per-lane 32-bit byte offset, and the LDS destination given as a wave-uniform
+// LDS byte address plus a compile-time offset: no per-load 64-bit address arithmetic
+// and a single live SGPR for the LDS side.
+template <int LDS_OFF>
+__device__ __forceinline__ void load_lds_16_s(const void* sbase, uint32_t voff, uint32_t lds_wave_base) {
+    asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+                 "s"(lds_wave_base), "i"(LDS_OFF)
+                 : "memory", "m0", "scc");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
 __device__ __forceinline__ v4i lds_read_16(const void* p) { return *(const v4i*)p; }
 
 // Scalar (SMEM) load of a wave-uniform float: counted by lgkmcnt, so it never waits on

@@ -301,7 +301,7 @@ def test_emulate_hand_worked_example():
     l = 1 + w
     w16 = float(np.float16(w))
     out = oracle.attn_emulate(Q, False, 2.0 ** -14, np.array([[0, 0, 0]]))[0]
-    np.testing.assert_allclose(out, [1 / l, w16 / l, 0, 0], rtol=1e-14)
+    np.testing.assert_allclose(out, [1 / l, w16 / l, 0, 0], rtol=1e-6)  # p is formed in fp32
     # FP8 PV: the V scale is amax/448 = 1/448 per used channel, P is coded as e4m3(448 p)
     Q8 = oracle.quantize(q, k, v, pv_fp8=True)
     assert Q8.v_scale[0, 0, 0] == np.float32(1 / 448) and Q8.v_hat[0, 0, 0, 0] == 448
@@ -332,9 +332,11 @@ def test_emulate_single_block_equals_one_shot_softmax(pv_fp8):
         if pv_fp8:
             ref = ref * Q.v_scale[0, h].astype(np.float64) / 448
         rows = np.array([[0, h, i] for i in range(50)])
-        got = oracle.attn_emulate(Q, False, sc, rows)
-        # p*448 is rounded to fp32 before torch's e4m3 cast: rare ties may differ by one code
-        np.testing.assert_allclose(got, ref, rtol=1e-9 if not pv_fp8 else 1e-2, atol=1e-12)
+        got, amb = oracle.attn_emulate(Q, False, sc, rows, with_ambiguity=True)
+        # p is formed in fp32 in the oracle (relative 1e-7 from this fp64 reference): only P
+        # roundings that sit within 2^-14 of a tie may differ, and amb bounds their effect
+        assert (np.abs(got - ref) <= 1e-6 * np.abs(ref) + amb + 1e-12).all()
+        assert amb.max() < (1e-3 if not pv_fp8 else 5e-2)  # the allowance stays small
 
 
 def test_emulate_multiblock_with_fixed_max():
@@ -355,7 +357,7 @@ def test_emulate_multiblock_with_fixed_max():
     p = np.exp2(s2 - s2[:, :1])
     ref = p.astype(np.float16).astype(np.float64) @ Q.v_hat[0, 0].astype(np.float64) / p.sum(1, keepdims=True)
     got = oracle.attn_emulate(Q, False, 0.5, oracle.all_rows(1, 1, 64))
-    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(got, ref, rtol=1e-6, atol=1e-12)  # p in fp32
 
 
 def test_emulate_online_rescale_tracks_one_shot():

@@ -12,13 +12,21 @@
 // over 256 chained FP8 MFMAs, so both accumulation modes share this code.
 //
 // gfx950 design:
-//  * workgroup = 8 waves = 256 queries, two waves per SIMD: while one wave runs the
-//    softmax on the vector ALUs the other keeps the matrix cores busy (one wave per
-//    SIMD cannot overlap the two); each wave owns 32 queries inside one 64-token Q
+//  * workgroup = 4 waves = 128 queries; each wave owns 32 queries inside one 64-token Q
 //    block (wave-uniform Q scale) and walks 64-key tiles (one K block: uniform K scale);
-//  * K^ and V^ tiles stream HBM -> LDS with direct-to-LDS 16-byte loads, double
-//    buffered, the same number of loads per thread per tile (so explicit vmcnt waits
-//    are exact), XOR-swizzled so every 16-byte operand read is bank-conflict free;
+//  * the vector ALU, not the matrix core, bounds this kernel: per score the softmax
+//    issues about six vector instructions, two of them (exp2, the FP8 pack) at a
+//    quarter of the full rate, against about half as many cycles of MFMA.  A wave on
+//    its own issues vector instructions at about a quarter of the rate the ALU
+//    sustains with four ready waves, so the schedule is kept simple and small (no
+//    score double buffer: 158 VGPRs at head dim 128) to fit three waves per SIMD (four
+//    at head dim 64), which keep the ALU fed while others wait on the matrix core,
+//    LDS or the barrier;
+//  * K^ and V^ tiles stream HBM -> LDS with direct-to-LDS 16-byte loads, two tiles
+//    ahead (three LDS stages; one ahead for FP16 P.V at head dim 128, whose 24 KB
+//    stages fit only twice per workgroup), the same number of loads per thread per tile (so
+//    explicit vmcnt waits are exact), XOR-swizzled so every 16-byte operand read is
+//    bank-conflict free;
 //  * S^T = K^ Q^T on v_mfma_i32_32x32x32_i8 (keys on the M side): each lane holds one
 //    query column, so row max / row sum are lane-local plus one exchange between the
 //    two lane halves;
@@ -26,11 +34,11 @@
 //    exactly the register order the P.V MFMA wants for its B operand: P never leaves
 //    registers; V^ tiles are stored channel-major so the A operand is contiguous;
 //  * P.V on v_mfma_scale_f32_32x32x64_f8f6f4 (FP8, unit scales) or
-//    v_mfma_f32_32x32x16_f16 (FP16), output O^T accumulated in fp32 registers;
-//  * software pipelined per wave: the QK^T MFMAs of tile j+1 are issued before the
-//    softmax of tile j, so the matrix core works while the vector ALUs do.
+//    v_mfma_f32_32x32x16_f16 (FP16), output O^T accumulated in fp32 registers.
 #include "common.hpp"
 #include "internal.hpp"
+
+#include <type_traits>
 
 namespace sage {
 
@@ -74,7 +82,15 @@ struct Cfg {
     static constexpr int ROUNDS = (KCHUNKS + VCHUNKS) / THREADS;
     static constexpr int STAGE = ROUNDS * THREADS * 16;
     static_assert(KCHUNKS % THREADS == 0 && VCHUNKS % THREADS == 0, "each load round lies in one region");
-    static constexpr int NST = 3;  // LDS pipeline depth (tiles resident or in flight)
+    // Per wave, QK^T, softmax, rescale and P.V of a tile run in turn, with no score
+    // double buffer, so a wave fits in 168 VGPRs (128 at head dim 64) and three (four)
+    // waves share each SIMD.  The vector ALU is the binding unit -- the softmax costs
+    // about twice the MFMA time -- and one wave can issue a vector instruction only
+    // every other slot, so the ALU needs several ready waves per SIMD to stay busy.
+    static constexpr int OCC = DP == 64 ? 4 : 3;  // waves per SIMD
+    // LDS stages: three (two tiles stream in while one is used) when OCC workgroups of
+    // three fit in the 160 KB of a CU, else two
+    static constexpr int NST = OCC * 3 * STAGE <= 160 * 1024 ? 3 : 2;
     static constexpr int KS = DP / 32;  // MFMA k-steps of QK^T
     static constexpr int DT = DP / 32;  // 32-channel tiles of O^T
     // XOR swizzles: bit c of the chunk flip is parity(row & mask_c); each is
@@ -197,57 +213,109 @@ __device__ __forceinline__ float halves_sum(float v) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Online softmax step for one tile: updates m, l; returns alpha; fills P (FP8: p*448).
-// Reductions are balanced trees (short dependency chains).  Masked keys get INT32_MIN
+// P in the B-operand registers of the P.V MFMAs: FP8 e4m3 codes of p * 448 (one
+// 64-key MFMA), or fp16 (four 16-key MFMAs).
+template <bool FP8>
+struct PPack;
+template <>
+struct PPack<true> {
+    v8i b;
+};
+template <>
+struct PPack<false> {
+    v8h b[4];
+};
+
+// Online softmax step for one tile: updates m, l, returns alpha and writes P straight
+// into the P.V operand registers (FP8: e4m3 of p * 448; FP16: fp16 of p), four values
+// at a time, so no array of fp32 probabilities is ever live.  Masked keys get INT32_MIN
 // and p = 0.  t = S32 * c - m is formed with one rounding (fma), keeping P's rounding
 // to FP16 / e4m3 close to a correctly rounded evaluation.
 template <bool FP8, bool MASK, bool CAUSAL>
-__device__ __forceinline__ float softmax_tile(v16i (&S)[2], float (&P)[2][16], float c, float& m, float& l, int g,
+__device__ __forceinline__ float softmax_tile(v16i (&S)[2], PPack<FP8>& pk, float c, float& m, float& l, int g,
                                               int key0, int qidx, int Nkv) {
     if constexpr (MASK) {
-        // keep the key base opaque: otherwise the compiler proves it loop-invariant on the
-        // tail tile and hoists all 32 visibility masks (64 SGPRs) out of the tile loop
-        int kb = key0;
-        asm volatile("" : "+v"(kb));
+        // key key0 + key_of_reg(kt, g, r) is visible iff it is below min(Nkv, qidx + 1)
+        // (causal) or Nkv; key_of_reg(kt, g, r) = key_of_reg(kt, 0, r) + (32 | 8) * g,
+        // so one per-lane threshold against compile-time offsets decides every
+        // register.  The threshold is kept opaque: otherwise the compiler proves it
+        // loop-invariant on the tail tile and hoists 32 masks out of the tile loop.
+        int lim = Nkv;
+        if constexpr (CAUSAL) lim = min(lim, qidx + 1);
+        int t = lim - key0 - (FP8 ? 32 : 8) * g;
+        asm volatile("" : "+v"(t));
 #pragma unroll
         for (int kt = 0; kt < 2; kt++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int key = kb + key_of_reg<FP8>(kt, g, r);
-                const bool vis = key < Nkv && (!CAUSAL || key <= qidx);
-                if (!vis) S[kt][r] = INT32_MIN;
-            }
+            for (int r = 0; r < 16; r++)
+                if (!(key_of_reg<FP8>(kt, 0, r) < t)) S[kt][r] = INT32_MIN;
     }
-    int mx[16];
+    // row max: two chains of three-input maxima (v_max3), one per score tile
+    int mxk[2];
 #pragma unroll
-    for (int r = 0; r < 16; r++) mx[r] = max(S[0][r], S[1][r]);
+    for (int kt = 0; kt < 2; kt++) {
+        int a = max(max(S[kt][0], S[kt][1]), S[kt][2]);
 #pragma unroll
-    for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-        for (int r = 0; r < w; r++) mx[r] = max(mx[r], mx[r + w]);
-    float tmax = (MASK && mx[0] == INT32_MIN) ? -1e30f : float(mx[0]) * c;
+        for (int r = 3; r + 1 < 16; r += 2) a = max(max(a, S[kt][r]), S[kt][r + 1]);
+        mxk[kt] = max(a, S[kt][15]);
+    }
+    const int mx = max(mxk[0], mxk[1]);
+    float tmax = (MASK && mx == INT32_MIN) ? -1e30f : float(mx) * c;
     tmax = halves_max(tmax);
     const float mnew = fmaxf(m, tmax);
     const float alpha = __builtin_amdgcn_exp2f(m - mnew);
     m = mnew;
     const float negm = FP8 ? kLog2_448 - mnew : -mnew;
+    float acc[4];
 #pragma unroll
-    for (int kt = 0; kt < 2; kt++)
+    for (int w = 0; w < 8; w++) {
+        const int kt = w >> 2, r0 = 4 * (w & 3);
+        float q[4];
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(float(S[kt][r]), c, negm));
-            if constexpr (MASK) pv = S[kt][r] == INT32_MIN ? 0.0f : pv;
-            P[kt][r] = pv;
+        for (int e = 0; e < 4; e++) {
+            q[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(float(S[kt][r0 + e]), c, negm));
+            if constexpr (MASK) q[e] = S[kt][r0 + e] == INT32_MIN ? 0.0f : q[e];
+            acc[e] = w == 0 ? q[e] : acc[e] + q[e];
         }
-    float ps[16];
+        if constexpr (FP8) {
+            // the low half is written first; the register's previous contents are don't-care,
+            // so it reuses q[1]'s (dead after this point) instead of a zeroed one
+            const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], __float_as_int(q[1]), false);
+            pk.b[w] = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], lo, true);
+        } else {
 #pragma unroll
-    for (int r = 0; r < 16; r++) ps[r] = P[0][r] + P[1][r];
-#pragma unroll
-    for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-        for (int r = 0; r < w; r++) ps[r] = ps[r] + ps[r + w];
-    l = __builtin_fmaf(l, alpha, ps[0]);
+            for (int e = 0; e < 4; e++) pk.b[2 * kt + (r0 >> 3)][(r0 & 7) + e] = (_Float16)q[e];
+        }
+    }
+    l = __builtin_fmaf(l, alpha, (acc[0] + acc[1]) + (acc[2] + acc[3]));
     return alpha;
+}
+
+// O^T += V^T P^T for one tile; vst = the V^ region of the tile's LDS stage.
+template <class C, bool FP8>
+__device__ __forceinline__ void pv_tile(const uint8_t* __restrict__ vst, const PPack<FP8>& pk, v16f (&O)[C::DT],
+                                        int lane) {
+    const int i = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; dt++) {
+        const int d = 32 * dt + i;
+        const int sw = vswz<C>(d);
+        const uint8_t* rb = vst + d * C::VROW;
+        if constexpr (FP8) {
+            const v4i a0 = lds_read_16(rb + 16 * ((2 * g) ^ sw));
+            const v4i a1 = lds_read_16(rb + 16 * ((2 * g + 1) ^ sw));
+            const v8i a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+            O[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pk.b, O[dt], 0, 0, 0, 127, 0, 127);
+        } else {
+#pragma unroll
+            for (int mm = 0; mm < 4; mm++) {
+                const v4i araw = lds_read_16(rb + 16 * ((2 * mm + g) ^ sw));
+                v8h a;
+                __builtin_memcpy(&a, &araw, 16);
+                O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pk.b[mm], O[dt], 0, 0, 0);
+            }
+        }
+    }
 }
 
 struct KParams {
@@ -264,7 +332,7 @@ struct KParams {
 };
 
 template <int DP, bool FP8, bool CAUSAL, bool OBF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(KParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8>::OCC, Cfg<DP, FP8>::OCC))) void attn_fwd_kernel(KParams p) {
     using C = Cfg<DP, FP8>;
     // NST LDS stages: tile j lives in stage j % NST while tiles j+1 .. j+NST-1 stream in.
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::NST * C::STAGE];
@@ -324,102 +392,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int dt = 0; dt < C::DT; dt++) O[dt] = v16f{};
     float m = -1e30f, l = 0.0f;
 
-    // softmax of tile j from its scores S, then P.V with the V^ part of LDS stage st
-    auto softmax_pv = [&](v16i (&S)[2], const uint8_t* __restrict__ st, int j, float ksj) {
-        const float c = sq * ksj * p.cscale;
-        const bool need_mask = (CAUSAL && j == qb) || (ktail && j == p.NBk - 1);
-        float P[2][16];  // probabilities (FP8: p * 448)
-        float alpha;
-        if (need_mask) alpha = softmax_tile<FP8, true, CAUSAL>(S, P, c, m, l, g, j * kBlk, qidx, p.Nkv);
-        else alpha = softmax_tile<FP8, false, CAUSAL>(S, P, c, m, l, g, j * kBlk, qidx, p.Nkv);
-        // rescale the accumulator only when some row max of this wave moved
+    const DmaPlan<C> dma = make_dma_plan<C>(tid);
+    // LDS byte address of this wave's slot in stage 0 (wave-uniform)
+    const uint32_t lds_w0 = __builtin_amdgcn_readfirstlane(lds_addr(smem) + uint32_t(wave * kWave * 16));
+    auto issue_tile = [&](int t) {
+        issue_stage<C>(lds_w0 + uint32_t((t % C::NST) * C::STAGE), kbase + int64_t(t) * kBlk * DP,
+                       vbase + int64_t(t) * C::VBYTES, dma);
+    };
+    // tiles [0, jm) need no mask for this wave; [jm, jend) do.  The split is per wave,
+    // but every wave runs the same sequence of iterations (and barriers).
+    int jm = ktail ? p.NBk - 1 : p.NBk;
+    if constexpr (CAUSAL) jm = min(jm, qb);
+    jm = min(jm, jend);
+
+    // Tile j lives in stage j % NST; the next NST-1 tiles stream in meanwhile.  Every
+    // wave runs every iteration (a fully masked causal tile leaves m, l and O
+    // unchanged: p = 0 and all V^ codes, padding included, are finite).
+    constexpr int AHEAD = C::NST - 1;  // tiles in flight beyond the current one
+    static_assert(AHEAD == 1 || AHEAD == 2, "two or three stages");
+#pragma unroll
+    for (int t = 0; t < AHEAD; t++)
+        if (t < jend) issue_tile(t);
+    float ks_next = scalar_load_f32(ks_row);
+    auto step = [&](auto masked, int j) {
+        constexpr bool MASK = decltype(masked)::value;
+        // tile j landed for this wave (later tiles may still stream); the barrier
+        // publishes it for all waves and certifies that iteration j-1, the last
+        // reader of the stage refilled below, is over everywhere
+        if (AHEAD == 2 && j + 1 < jend) wait_vmcnt<C::ROUNDS>();  // tile j+1 may stream on
+        else wait_vmcnt<0>();
+        block_barrier();
+        if (j + AHEAD < jend) issue_tile(j + AHEAD);
+        const float c = sq * ks_next * p.cscale;
+        ks_next = scalar_load_f32(ks_row + min(j + 1, p.NBk - 1));
+        const uint8_t* st = smem + (j % C::NST) * C::STAGE;
+        v16i S[2];
+        qk_tile<C, FP8>(st, qf, S, lane);
+        PPack<FP8> pk;
+        const float alpha = softmax_tile<FP8, MASK, CAUSAL>(S, pk, c, m, l, g, j * kBlk, qidx, p.Nkv);
         if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
             for (int dt = 0; dt < C::DT; dt++) O[dt] *= alpha;
         }
-        const uint8_t* vst = st + C::KBYTES;
-        if constexpr (FP8) {
-            v8i pb;
-#pragma unroll
-            for (int w = 0; w < 8; w++) {
-                const float* pp = &P[w >> 2][4 * (w & 3)];
-                const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(pp[0], pp[1], 0, false);
-                pb[w] = __builtin_amdgcn_cvt_pk_fp8_f32(pp[2], pp[3], lo, true);
-            }
-#pragma unroll
-            for (int dt = 0; dt < C::DT; dt++) {
-                const int d = 32 * dt + i;
-                const int sw = vswz<C>(d);
-                const uint8_t* rb = vst + d * C::VROW;
-                const v4i a0 = lds_read_16(rb + 16 * ((2 * g) ^ sw));
-                const v4i a1 = lds_read_16(rb + 16 * ((2 * g + 1) ^ sw));
-                const v8i a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-                O[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, O[dt], 0, 0, 0, 127, 0, 127);
-            }
-        } else {
-            v8h ph[4];
-#pragma unroll
-            for (int mm = 0; mm < 4; mm++)
-#pragma unroll
-                for (int e = 0; e < 8; e++) ph[mm][e] = (_Float16)P[mm >> 1][8 * (mm & 1) + e];
-#pragma unroll
-            for (int dt = 0; dt < C::DT; dt++) {
-                const int d = 32 * dt + i;
-                const int sw = vswz<C>(d);
-                const uint8_t* rb = vst + d * C::VROW;
-#pragma unroll
-                for (int mm = 0; mm < 4; mm++) {
-                    const v4i araw = lds_read_16(rb + 16 * ((2 * mm + g) ^ sw));
-                    v8h a;
-                    __builtin_memcpy(&a, &araw, 16);
-                    O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, ph[mm], O[dt], 0, 0, 0);
-                }
-            }
-        }
+        pv_tile<C, FP8>(st + C::KBYTES, pk, O, lane);
     };
-    // does this wave compute tile t?
-    auto wants = [&](int t) { return active && t < jend && (!CAUSAL || t <= qb); };
-
-    // ---- main loop.  Tile j lives in LDS stage j % NST.  Iteration j: wait for the
-    // direct-to-LDS loads of tile j+1 (the only ones outstanding), one bare barrier
-    // publishes it and certifies that every wave has finished iteration j-1 (whose
-    // stage, (j + 2) % 3, is refilled with tile j+2 right after); then the QK^T MFMAs of
-    // tile j+1 are issued ahead of the softmax and P.V of tile j, whose scores were
-    // computed one iteration earlier.  S0 / S1 alternate between current and next.
-    static_assert(C::NST == 3, "the stage rotation below assumes three stages");
-    const DmaPlan<C> dma = make_dma_plan<C>(tid);
-    // LDS byte address of this wave's slot in stage 0 (wave-uniform)
-    const uint32_t lds_w0 = __builtin_amdgcn_readfirstlane(lds_addr(smem) + uint32_t(wave * kWave * 16));
-    issue_stage<C>(lds_w0, kbase, vbase, dma);
-    if (jend > 1) {
-        issue_stage<C>(lds_w0 + C::STAGE, kbase + int64_t(kBlk) * DP, vbase + C::VBYTES, dma);
-        wait_vmcnt<C::ROUNDS>();
-    } else {
-        wait_vmcnt<0>();
-    }
-    block_barrier();
-    v16i S0[2], S1[2];
-    if (wants(0)) qk_tile<C, FP8>(smem, qf, S0, lane);
-    int stage = 0;  // j % 3
-    auto iter = [&](int j, v16i (&Scur)[2], v16i (&Snext)[2]) {
-        const int st1 = stage == 2 ? 0 : stage + 1;  // (j + 1) % 3
-        const int st2 = st1 == 2 ? 0 : st1 + 1;      // (j + 2) % 3
-        if (j + 1 < jend) {
-            wait_vmcnt<0>();
-            block_barrier();
-            if (j + 2 < jend)
-                issue_stage<C>(lds_w0 + uint32_t(st2 * C::STAGE), kbase + int64_t(j + 2) * kBlk * DP,
-                               vbase + int64_t(j + 2) * C::VBYTES, dma);
-        }
-        if (wants(j + 1)) qk_tile<C, FP8>(smem + st1 * C::STAGE, qf, Snext, lane);
-        if (wants(j)) softmax_pv(Scur, smem + stage * C::STAGE, j, scalar_load_f32(ks_row + j));
-        stage = st1;
-    };
-    for (int j = 0; j < jend; j += 2) {
-        iter(j, S0, S1);
-        if (j + 1 >= jend) break;
-        iter(j + 1, S1, S0);
-    }
+    int j = 0;
+    for (; j < jm; j++) step(std::false_type{}, j);
+    for (; j < jend; j++) step(std::true_type{}, j);
+    // Matrix instructions must run with every lane enabled: without these empty uses the
+    // compiler sinks the last P.V MFMAs into the epilogue, below the per-lane exit of
+    // padding queries, and the operand rows held by the exited lanes are lost.
+#pragma unroll
+    for (int dt = 0; dt < C::DT; dt++) asm volatile("" : "+v"(O[dt]));
 
     // ---- epilogue: O^T / l (x v_scale in FP8 mode) -> out dtype, input layout
     if (!active) return;

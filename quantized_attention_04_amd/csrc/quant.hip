@@ -30,32 +30,50 @@ __host__ __device__ inline Strides make_strides(int layout_nhd, int H, int N, in
 
 // ------------------------------------------------------------------------------------------
 // K mean, pass 1: part[b][h][j][c] = sum of K[b,h,t,c] over the tokens t of block j,
-// ascending, in fp64.  grid (NB, H, B), block 128 threads, thread = channel.
-template <bool BF16>
-__global__ __launch_bounds__(128) void k_mean_partial_kernel(const uint16_t* __restrict__ k, Strides st, int N,
+// ascending, in fp64.  grid (NB, H, B), 256 threads: the block's 64 x D tile is read
+// with coalesced 16-byte loads into LDS, then thread c < D walks its channel.
+template <bool BF16, int DP, bool VEC8>
+__global__ __launch_bounds__(256) void k_mean_partial_kernel(const uint16_t* __restrict__ k, Strides st, int N,
                                                              int D, int NB, double* __restrict__ part) {
-    const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, c = threadIdx.x;
+    constexpr int CH = DP / 8, RSTEP = 256 / CH;  // RSTEP token rows per pass
+    __shared__ __attribute__((aligned(16))) uint16_t tile[kBlk][DP];
+    const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int ch = threadIdx.x % CH, r0 = threadIdx.x / CH, c0 = ch * 8;
+    const uint16_t* base = k + b * st.b + h * st.h;
+#pragma unroll
+    for (int p = 0; p < kBlk / RSTEP; p++) {
+        const int tl = p * RSTEP + r0, t = j * kBlk + tl;
+        v8u16 r = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (t < N && c0 < D) {
+            const uint16_t* src = base + int64_t(t) * st.t + c0;
+            if constexpr (VEC8) {
+                r = *(const v8u16*)src;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; e++) r[e] = (c0 + e < D) ? src[e] : (unsigned short)0;
+            }
+        }
+        *(v8u16*)&tile[tl][c0] = r;
+    }
+    __syncthreads();
+    const int c = threadIdx.x;
     if (c >= D) return;
-    const uint16_t* base = k + b * st.b + h * st.h + c;
-    const int t0 = j * kBlk, t1 = min(N, t0 + kBlk);
-    uint16_t raw[kBlk];
-#pragma unroll
-    for (int i = 0; i < kBlk; i++) raw[i] = (t0 + i < t1) ? base[int64_t(t0 + i) * st.t] : 0;
+    const int nt = min(kBlk, N - j * kBlk);
     double s = 0.0;
-#pragma unroll
-    for (int i = 0; i < kBlk; i++)
-        if (t0 + i < t1) s += double(in_to_f32<BF16>(raw[i]));
+    for (int t = 0; t < nt; t++) s += double(in_to_f32<BF16>(tile[t][c]));
     part[((int64_t(b) * gridDim.y + h) * NB + j) * D + c] = s;
 }
 
-// K mean, pass 2: mean = fp32((sum over blocks, ascending, of part) / N).
-__global__ __launch_bounds__(256) void k_mean_final_kernel(const double* __restrict__ part, int total, int NB, int D,
-                                                           int N, float* __restrict__ mean) {
+// K mean, pass 2: mean = fp32((sum over blocks, ascending, of part) / N).  One thread
+// per (b, h, channel) in 64-thread workgroups (enough of them to spread over the CUs).
+__global__ __launch_bounds__(64) void k_mean_final_kernel(const double* __restrict__ part, int total, int NB, int D,
+                                                          int N, float* __restrict__ mean) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= total) return;
     const int bh = i / D, c = i % D;
     const double* p = part + int64_t(bh) * NB * D + c;
     double s = 0.0;
+#pragma unroll 8
     for (int j = 0; j < NB; j++) s += p[int64_t(j) * D];
     mean[i] = float(s / double(N));
 }
@@ -188,8 +206,12 @@ __global__ __launch_bounds__(256) void v_amax_kernel(const uint16_t* __restrict_
     }
 }
 
-// V operand pass 2 (both modes): one workgroup per 64-token block; convert, transpose
-// through LDS, write the block channel-major ([Dp][64]) with 16-byte stores.
+// V operand pass 2 (both modes): one workgroup per 64-token block.  Thread (q, ch)
+// reads channels 8ch .. 8ch+7 of the four tokens 4q .. 4q+3 and writes, per channel,
+// the four codes as one 4-byte (FP8) or 8-byte (FP16) word into a channel-major LDS
+// tile, which then leaves in 16-byte stores ([Dp][64] per block).  Channel c's row
+// sits at LDS row c ^ ((c >> 3) & 3) (FP8) or c ^ ((c >> 3) & 1) (FP16): the four
+// (two) channel groups a wave writes at once then hit disjoint LDS banks.
 //   FP16: v^ = fp16(clamp(v, +-65504)) (round half even).
 //   FP8:  v^ = e4m3(clamp(fp32(v * inv[c]), +-448)), inv = fp32(448 / amax[c]);
 //         the block-0 workgroup also writes v_scale[c] = fp32(amax[c] / 448).
@@ -198,12 +220,14 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
                                                       int NB, const uint32_t* __restrict__ amax_bits,
                                                       void* __restrict__ vhat, float* __restrict__ vscale) {
     constexpr int ELT = FP8 ? 1 : 2;
-    constexpr int CH = DP / 8, RSTEP = 256 / CH;  // RSTEP token rows per pass
-    constexpr int ROWB = kBlk * ELT + 16;         // padded LDS row (bytes) per channel
+    constexpr int CH = DP / 8;               // 8-channel chunks per token row
+    constexpr int THREADS = CH * (kBlk / 4);  // one thread per (token quad, chunk)
+    constexpr int ROWB = kBlk * ELT;          // bytes per channel row of the tile
+    constexpr int RMASK = FP8 ? 3 : 1;
     __shared__ __attribute__((aligned(16))) uint8_t tile[DP * ROWB];
     const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int64_t bh = int64_t(b) * gridDim.y + h;
-    const int ch = threadIdx.x % CH, r0 = threadIdx.x / CH, c0 = ch * 8;
+    const int q = threadIdx.x % (kBlk / 4), ch = threadIdx.x / (kBlk / 4), c0 = ch * 8;
     const uint16_t* base = v + b * st.b + h * st.h;
 
     float inv[8];
@@ -218,40 +242,46 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
             vscale[bh * DP + threadIdx.x] = a / 448.0f;
         }
     }
+    v8u16 r[4];
 #pragma unroll
-    for (int p = 0; p < kBlk / RSTEP; p++) {
-        const int tl = p * RSTEP + r0, t = j * kBlk + tl;
-        v8u16 r = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int u = 0; u < 4; u++) {
+        const int t = j * kBlk + 4 * q + u;
+        r[u] = v8u16{0, 0, 0, 0, 0, 0, 0, 0};
         if (t < N && c0 < D) {
             const uint16_t* src = base + int64_t(t) * st.t + c0;
             if constexpr (VEC8) {
-                r = *(const v8u16*)src;
+                r[u] = *(const v8u16*)src;
             } else {
 #pragma unroll
-                for (int e = 0; e < 8; e++) r[e] = (c0 + e < D) ? src[e] : (unsigned short)0;
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-            const float x = in_to_f32<BF16>(r[e]);  // padding elements are +0
-            if constexpr (FP8) {
-                float y = x * inv[e];
-                y = fminf(fmaxf(y, -448.0f), 448.0f);
-                const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false);
-                tile[(c0 + e) * ROWB + tl] = uint8_t(pk & 0xff);
-            } else {
-                const float y = fminf(fmaxf(x, -65504.0f), 65504.0f);
-                *(uint16_t*)&tile[(c0 + e) * ROWB + 2 * tl] = f32_to_f16_bits(y);
+                for (int e = 0; e < 8; e++) r[u][e] = (c0 + e < D) ? src[e] : (unsigned short)0;
             }
         }
     }
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        const int c = c0 + e;
+        uint8_t* row = tile + (c ^ ((c >> 3) & RMASK)) * ROWB;
+        float y[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const float x = in_to_f32<BF16>(r[u][e]);  // padding elements are +0
+            y[u] = FP8 ? fminf(fmaxf(x * inv[e], -448.0f), 448.0f) : fminf(fmaxf(x, -65504.0f), 65504.0f);
+        }
+        if constexpr (FP8) {
+            const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+            *(int*)(row + 4 * q) = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+        } else {
+            *(uint2*)(row + 8 * q) = make_uint2(uint32_t(f32_to_f16_bits(y[0])) | (uint32_t(f32_to_f16_bits(y[1])) << 16),
+                                                uint32_t(f32_to_f16_bits(y[2])) | (uint32_t(f32_to_f16_bits(y[3])) << 16));
+        }
+    }
     __syncthreads();
-    constexpr int CHUNKS_PER_ROW = kBlk * ELT / 16;
-    constexpr int TOTAL = DP * CHUNKS_PER_ROW;
-    uint8_t* dst = (uint8_t*)vhat + (bh * NB + j) * int64_t(DP * kBlk * ELT);
-    for (int i = threadIdx.x; i < TOTAL; i += 256) {
-        const int c = i / CHUNKS_PER_ROW, q = i % CHUNKS_PER_ROW;
-        *(uint4*)(dst + int64_t(i) * 16) = *(const uint4*)&tile[c * ROWB + q * 16];
+    constexpr int CPR = ROWB / 16;  // 16-byte chunks per row
+    uint8_t* dst = (uint8_t*)vhat + (bh * NB + j) * int64_t(DP * ROWB);
+    for (int i = threadIdx.x; i < DP * CPR; i += THREADS) {
+        const int pr = i / CPR, k = i % CPR;
+        const int c = pr ^ ((pr >> 3) & RMASK);
+        *(uint4*)(dst + c * ROWB + 16 * k) = *(const uint4*)(tile + pr * ROWB + 16 * k);
     }
 }
 
@@ -263,11 +293,10 @@ hipError_t launch_qk_t(const QuantQKArgs& a, hipStream_t s) {
     const Strides sq = make_strides(a.layout_nhd, a.Hq, a.Nq, a.D);
     const Strides sk = make_strides(a.layout_nhd, a.Hkv, a.Nkv, a.D);
     const int nbq = (a.Nq + kBlk - 1) / kBlk, nbk = (a.Nkv + kBlk - 1) / kBlk;
-    k_mean_partial_kernel<BF16><<<dim3(nbk, a.Hkv, a.B), 128, 0, s>>>((const uint16_t*)a.k, sk, a.Nkv, a.D, nbk,
-                                                                        (double*)a.workspace);
+    k_mean_partial_kernel<BF16, DP, VEC8><<<dim3(nbk, a.Hkv, a.B), 256, 0, s>>>((const uint16_t*)a.k, sk, a.Nkv,
+                                                                                a.D, nbk, (double*)a.workspace);
     const int tot = a.B * a.Hkv * a.D;
-    k_mean_final_kernel<<<(tot + 255) / 256, 256, 0, s>>>((const double*)a.workspace, tot, nbk, a.D, a.Nkv,
-                                                          a.k_mean);
+    k_mean_final_kernel<<<(tot + 63) / 64, 64, 0, s>>>((const double*)a.workspace, tot, nbk, a.D, a.Nkv, a.k_mean);
     const int64_t qblocks = int64_t(a.B) * a.Hq * nbq, kblocks = int64_t(a.B) * a.Hkv * nbk;
     quant_blocks_kernel<BF16, DP, VEC8><<<unsigned((qblocks + 3) / 4), 256, 0, s>>>(
         (const uint16_t*)a.q, sq, a.B, a.Hq, a.Nq, a.D, nbq, nullptr, a.q_i8, a.q_scale);
@@ -286,10 +315,10 @@ hipError_t launch_v_t(const QuantVArgs& a, hipStream_t s) {
         fill_zero_kernel<<<(n + 255) / 256, 256, 0, s>>>(amax, n);
         v_amax_kernel<BF16, DP, VEC8><<<dim3((a.Nkv + 255) / 256, a.Hkv, a.B), 256, 0, s>>>(
             (const uint16_t*)a.v, sv, a.Nkv, a.D, amax);
-        quant_v_kernel<BF16, DP, VEC8, true><<<dim3(nb, a.Hkv, a.B), 256, 0, s>>>(
+        quant_v_kernel<BF16, DP, VEC8, true><<<dim3(nb, a.Hkv, a.B), DP * 2, 0, s>>>(
             (const uint16_t*)a.v, sv, a.Nkv, a.D, nb, amax, a.v_hat, a.v_scale);
     } else {
-        quant_v_kernel<BF16, DP, VEC8, false><<<dim3(nb, a.Hkv, a.B), 256, 0, s>>>(
+        quant_v_kernel<BF16, DP, VEC8, false><<<dim3(nb, a.Hkv, a.B), DP * 2, 0, s>>>(
             (const uint16_t*)a.v, sv, a.Nkv, a.D, nb, nullptr, a.v_hat, nullptr);
     }
     return hipGetLastError();

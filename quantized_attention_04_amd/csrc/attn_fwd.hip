@@ -34,7 +34,10 @@
 //    exactly the register order the P.V MFMA wants for its B operand: P never leaves
 //    registers; V^ tiles are stored channel-major so the A operand is contiguous;
 //  * P.V on v_mfma_scale_f32_32x32x64_f8f6f4 (FP8, unit scales) or
-//    v_mfma_f32_32x32x16_f16 (FP16), output O^T accumulated in fp32 registers.
+//    v_mfma_f32_32x32x16_f16 (FP16), output O^T accumulated in fp32 registers;
+//  * consecutive workgroups on one XCD take the query tiles of one (b, kv head), so
+//    the K^/V^ tiles they all stream come from that XCD's L2 (causal: heaviest tiles
+//    of the head first, for load balance).
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -343,23 +346,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
     // ---- workgroup -> (b, h, q tile)
     int b, h, qt;
     {
-        int L;
-        if constexpr (CAUSAL) {
-            L = blockIdx.x;  // heaviest (last) query tiles first
-            const int per = p.B * p.Hq;
-            qt = p.QT - 1 - L / per;
-            L = L % per;
-            const int hg = L % p.G, bhk = L / p.G;
-            b = bhk / p.Hkv;
-            h = (bhk % p.Hkv) * p.G + hg;
-        } else {
-            L = xcd_remap(blockIdx.x, gridDim.x);  // one (b, kv head) per XCD run
-            const int hg = L % p.G;
-            qt = (L / p.G) % p.QT;
-            const int bhk = L / (p.G * p.QT);
-            b = bhk / p.Hkv;
-            h = (bhk % p.Hkv) * p.G + hg;
-        }
+        // consecutive workgroups on one XCD share a (b, kv head), so its K^/V^ tiles are
+        // reused from that XCD's L2; causal: the heaviest query tiles of a head first
+        const int L = xcd_remap(blockIdx.x, gridDim.x);
+        const int hg = L % p.G;
+        qt = (L / p.G) % p.QT;
+        if constexpr (CAUSAL) qt = p.QT - 1 - qt;
+        const int bhk = L / (p.G * p.QT);
+        b = bhk / p.Hkv;
+        h = (bhk % p.Hkv) * p.G + hg;
     }
     const int hk = h / p.G;
     const int q0 = qt * C::BM + wave * C::QW;  // this wave's first query

@@ -420,7 +420,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
         if (j + AHEAD < jend) issue_tile(j + AHEAD);
         const float c = sq * ks_next * p.cscale;
         ks_next = scalar_load_f32(ks_row + min(j + 1, p.NBk - 1));
-        const uint8_t* st = smem + (j % C::NST) * C::STAGE;
+        // stage base as one wave-uniform value, so each LDS address costs a single add
+        const uint8_t* st = smem + __builtin_amdgcn_readfirstlane((j % C::NST) * C::STAGE);
         v16i S[2];
         qk_tile<C, FP8>(st, qf, S, lane);
         PPack<FP8> pk;

@@ -5,6 +5,11 @@ may import this module.  It shares no code with the HIP path; its arithmetic
 lives in ``oracle.c`` (see the header there for the passages each step
 follows), and this wrapper only marshals numpy arrays.
 
+Variable-length batches (``*_varlen``): the tokens of B sequences packed along one
+axis, delimited by prefix sums cu_seqlens; the batch is, by definition here, the
+dense scheme applied to every sequence on its own (its own K mean, block scales and
+V scales; causal aligned per sequence).
+
 Two modes:
   * ``attn_emulate``: the quantisation scheme replayed step by step (K mean
     smoothing, per-64-token INT8 Q/K, exact int32 scores, online exp2 softmax,
@@ -212,3 +217,68 @@ def attn_exact(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, sm_sca
                          np.ascontiguousarray(v, np.float32), B, Hq, Hkv, Nq, Nkv, D, int(bool(causal)),
                          float(sm_scale), rows, rows.shape[0], out)
     return out
+
+
+# ----------------------------------------------------------------------------- variable-length batches
+# sageattn_varlen (SageAttention project README, "Available APIs" and "Project Updates"):
+# several sequences of different lengths in one call.  Inputs are packed THD arrays
+# (total_tokens, H, D) with int prefix sums cu (cu[0] = 0, cu[B] = total).
+
+def _seq(x: np.ndarray, cu, b: int) -> np.ndarray:
+    """Sequence b of a packed (total, H, D) array as a (1, H, n, D) float32 array."""
+    return np.ascontiguousarray(x[int(cu[b]):int(cu[b + 1])].transpose(1, 0, 2)[None], dtype=np.float32)
+
+
+def quantize_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q, cu_k, pv_fp8: bool):
+    """Per-sequence Quantized (None where the sequence has no key)."""
+    out = []
+    for b in range(len(cu_q) - 1):
+        if int(cu_k[b + 1]) == int(cu_k[b]):
+            out.append(None)
+            continue
+        out.append(quantize(_seq(q, cu_q, b), _seq(k, cu_k, b), _seq(v, cu_k, b), pv_fp8))
+    return out
+
+
+def _per_sequence(rows: np.ndarray, D: int, fn):
+    """rows (b, h, i) with i local to sequence b; fn(b, local_rows) -> [n, D] (or None = zeros)."""
+    rows = np.asarray(rows, np.int64).reshape(-1, 3)
+    out = np.zeros((rows.shape[0], D), np.float64)
+    for b in np.unique(rows[:, 0]):
+        sel = np.nonzero(rows[:, 0] == b)[0]
+        local = rows[sel].copy()
+        local[:, 0] = 0
+        res = fn(int(b), np.ascontiguousarray(local))
+        if res is not None:
+            out[sel] = res
+    return out
+
+
+def attn_emulate_varlen(Qs, causal: bool, sm_scale: float, rows: np.ndarray, D: int, with_ambiguity: bool = False):
+    """Emulation rows of a varlen batch; a sequence without keys outputs zeros."""
+    amb_parts = {}
+
+    def fn(b, local):
+        if Qs[b] is None:
+            return None
+        o, a = attn_emulate(Qs[b], causal, sm_scale, local, with_ambiguity=True)
+        amb_parts[b] = a
+        return o
+
+    out = _per_sequence(rows, D, fn)
+    if not with_ambiguity:
+        return out
+    amb = _per_sequence(rows, D, lambda b, local: amb_parts.get(b))
+    return out, amb
+
+
+def attn_exact_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q, cu_k, causal: bool, sm_scale: float,
+                      rows: np.ndarray) -> np.ndarray:
+    D = q.shape[2]
+
+    def fn(b, local):
+        if int(cu_k[b + 1]) == int(cu_k[b]):
+            return None
+        return attn_exact(_seq(q, cu_q, b), _seq(k, cu_k, b), _seq(v, cu_k, b), causal, sm_scale, local)
+
+    return _per_sequence(rows, D, fn)

@@ -14,7 +14,10 @@
  * quantising QK^T and compensating the error):
  *
  *   exact mode      O = softmax(sm_scale * Q K^T + M) V in fp64, M = 0 or -inf
- *                   (causal: key j visible to query i iff j <= i);
+ *                   (causal: key j visible to query i iff j <= i + Nkv - Nq, the
+ *                   diagonal aligned to the bottom-right corner, so that with
+ *                   Nq < Nkv the queries are the last Nq positions of the keys'
+ *                   sequence; a row that sees no key at all outputs zeros);
  *   emulation mode  the quantisation scheme step by step:
  *                   K mean smoothing -> INT8 Q / K per 64-token block ->
  *                   exact int32 scores -> dequant -> online exp2 softmax over
@@ -251,12 +254,13 @@ void orc_scores_i32(const int8_t* q8, const int8_t* k8, long B, long Hq, long Hk
  *   p    = fp32( 2^fp32(S2 - m) )                               (correctly rounded)
  *   p^   = fp16(p)  or  e4m3(fp32(p * 448))                     (RNE, saturating)
  * and everything else in fp64.  For each row, for each 64-key block in ascending
- * order (blocks whose keys all lie beyond i are skipped when causal):
- *   masked keys (causal j > i) take no part;
+ * order (blocks whose keys all lie beyond i + Nkv - Nq are skipped when causal):
+ *   masked keys (causal j > i + Nkv - Nq) take no part;
  *   alpha = 2^(m_old - m_new)   (0 when the row was empty)
  *   l     = alpha * l + sum_j p_j                     (unrounded p, fp64 sum)
  *   acc   = alpha * acc + sum_j p^_j * vhat_j         (fp64)
- * Finally o = acc / l, times vscale[c] / 448 in FP8 mode.
+ * Finally o = acc / l, times vscale[c] / 448 in FP8 mode; o = 0 for a row with no
+ * visible key (l = 0).
  * Both PV accumulation modes (single-level fp32 and two-level) are modelled by the
  * same fp64 accumulation: they differ only in how the hardware rounds.
  *
@@ -296,6 +300,7 @@ void orc_attn_emulate(const int8_t* q8, const float* sq, const int8_t* k8, const
     const int fmt = pv_fp8 ? ORC_E4M3 : ORC_FP16;
     long group = Hq / Hkv;
     long nqb = (Nq + BLK - 1) / BLK, nkb = (Nkv + BLK - 1) / BLK;
+    const long off = Nkv - Nq; /* causal: key j visible to query i iff j <= i + off */
     (void)B;
 #pragma omp parallel for schedule(dynamic, 4)
     for (long r = 0; r < R; r++) {
@@ -312,12 +317,12 @@ void orc_attn_emulate(const int8_t* q8, const float* sq, const int8_t* k8, const
         double l = 0.0;
         for (long kb = 0; kb < nkb; kb++) {
             long j0 = kb * BLK;
-            if (causal && j0 > i) break;
+            if (causal && j0 > i + off) break;
             long j1 = j0 + BLK < Nkv ? j0 + BLK : Nkv;
             float c = (sqi * sk[(b * Hkv + hk) * nkb + kb]) * scale2;
             float bmax = -INFINITY;
             for (long j = j0; j < j1; j++) {
-                vis[j - j0] = !(causal && j > i);
+                vis[j - j0] = !(causal && j > i + off);
                 if (!vis[j - j0]) continue;
                 const int8_t* krow = k8 + ((b * Hkv + hk) * Nkv + j) * D;
                 int64_t s32 = 0;
@@ -354,7 +359,7 @@ void orc_attn_emulate(const int8_t* q8, const float* sq, const int8_t* k8, const
             m = mnew;
         }
         for (long d = 0; d < D; d++) {
-            double o = acc[d] / l, ao = aacc[d] / l;
+            double o = l > 0.0 ? acc[d] / l : 0.0, ao = l > 0.0 ? aacc[d] / l : 0.0;
             if (pv_fp8) {
                 o *= (double)vscale[(b * Hkv + hk) * D + d] / 448.0;
                 ao *= (double)vscale[(b * Hkv + hk) * D + d] / 448.0;
@@ -370,12 +375,13 @@ void orc_attn_emulate(const int8_t* q8, const float* sq, const int8_t* k8, const
 /* ---------------------------------------------------------------------------
  * Exact attention for selected rows, in fp64 from the exactly upcast inputs:
  *   s_j = sm_scale * sum_c q_c k_jc  (-inf where masked),  w_j = exp(s_j - max s),
- *   o   = sum_j w_j v_j / sum_j w_j.
+ *   o   = sum_j w_j v_j / sum_j w_j   (0 for a row with no visible key).
  * ------------------------------------------------------------------------- */
 void orc_attn_exact(const float* q, const float* k, const float* v, long B, long Hq, long Hkv, long Nq,
                     long Nkv, long D, int causal, double sm_scale, const int64_t* rows, long R,
                     double* out) {
     long group = Hq / Hkv;
+    const long off = Nkv - Nq; /* causal: key j visible to query i iff j <= i + off */
     (void)B;
 #pragma omp parallel for schedule(dynamic, 4)
     for (long r = 0; r < R; r++) {
@@ -385,7 +391,7 @@ void orc_attn_exact(const float* q, const float* k, const float* v, long B, long
         double* s = (double*)malloc((size_t)Nkv * sizeof(double));
         double smax = -INFINITY;
         for (long j = 0; j < Nkv; j++) {
-            if (causal && j > i) {
+            if (causal && j > i + off) {
                 s[j] = -INFINITY;
                 continue;
             }
@@ -404,7 +410,7 @@ void orc_attn_exact(const float* q, const float* k, const float* v, long B, long
             const float* vrow = v + ((b * Hkv + hk) * Nkv + j) * D;
             for (long c = 0; c < D; c++) out[r * D + c] += w * (double)vrow[c];
         }
-        for (long c = 0; c < D; c++) out[r * D + c] /= wsum;
+        for (long c = 0; c < D; c++) out[r * D + c] = wsum > 0.0 ? out[r * D + c] / wsum : 0.0;
         free(s);
     }
 }

@@ -523,3 +523,81 @@ def test_emulation_error_bound_on_scores():
     eq, ek = sq * (0.5 + 2 ** -15), sk * (0.5 + 2 ** -15)
     bound = np.abs(qq).sum(1)[:, None] * ek + np.abs(kt).sum(1)[None, :] * eq + 32 * eq * ek
     assert (np.abs(emul - exact) <= bound).all()
+
+
+# ----------------------------------------------------------------------------- causal with Nq != Nkv, varlen
+
+@pytest.mark.parametrize("nq,nkv", [(5, 9), (9, 5), (64, 130), (70, 70)])
+def test_exact_causal_bottom_right_vs_sdpa_mask(nq, nkv):
+    """Causal with Nq != Nkv: key j visible to query i iff j <= i + Nkv - Nq.  Checked
+    against torch SDPA (fp64) given that boolean mask explicitly; rows that see no key
+    are zeros in the oracle (SDPA leaves them undefined)."""
+    q = _bf16_vals((1, 2, nq, 16), seed=60)
+    k = _bf16_vals((1, 2, nkv, 16), seed=61)
+    v = _bf16_vals((1, 2, nkv, 16), seed=62)
+    sc = 0.25
+    got = oracle.attn_exact(q, k, v, True, sc, oracle.all_rows(1, 2, nq)).reshape(1, 2, nq, 16)
+    mask = torch.ones(nq, nkv, dtype=torch.bool).tril(diagonal=nkv - nq)
+    t = lambda a: torch.from_numpy(a.astype(np.float64))
+    ref = F.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=mask, scale=sc).numpy()
+    seen = mask.any(dim=1).numpy()
+    np.testing.assert_allclose(got[:, :, seen], ref[:, :, seen], rtol=0, atol=1e-12)
+    assert (got[:, :, ~seen] == 0).all()
+
+
+def test_emulate_causal_offset_is_the_tail_of_the_square_problem():
+    """With Nkv - Nq a multiple of 64 the short query set's 64-token blocks coincide
+    with the last blocks of the full one, so its causal (bottom-right) emulation must
+    equal, bit for bit, the last Nq rows of the square causal problem."""
+    n, nq = 200, 72  # offset 128
+    q = _bf16_vals((1, 2, n, 32), seed=63)
+    k = _bf16_vals((1, 2, n, 32), seed=64) + 0.5
+    v = _bf16_vals((1, 2, n, 32), seed=65)
+    for pv_fp8 in (False, True):
+        full = oracle.quantize(q, k, v, pv_fp8)
+        short = oracle.quantize(np.ascontiguousarray(q[:, :, n - nq:]), k, v, pv_fp8)
+        np.testing.assert_array_equal(short.q_i8, full.q_i8[:, :, n - nq:])
+        rows_full = np.array([(0, h, n - nq + i) for h in range(2) for i in range(nq)], np.int64)
+        rows_short = np.array([(0, h, i) for h in range(2) for i in range(nq)], np.int64)
+        a = oracle.attn_emulate(full, True, 0.2, rows_full)
+        b = oracle.attn_emulate(short, True, 0.2, rows_short)
+        np.testing.assert_array_equal(a, b)
+
+
+def test_rows_without_visible_keys_are_zero():
+    q = _bf16_vals((1, 1, 10, 8), seed=66)
+    k = _bf16_vals((1, 1, 4, 8), seed=67)
+    v = _bf16_vals((1, 1, 4, 8), seed=68)
+    rows = oracle.all_rows(1, 1, 10)
+    Q = oracle.quantize(q, k, v, False)
+    em = oracle.attn_emulate(Q, True, 0.3, rows)
+    ex = oracle.attn_exact(q, k, v, True, 0.3, rows)
+    # offset 4 - 10 = -6: queries 0..5 see no key, query 6 sees key 0 only
+    assert (em[:6] == 0).all() and (ex[:6] == 0).all()
+    np.testing.assert_allclose(ex[6], v[0, 0, 0], rtol=1e-15)
+    assert np.abs(em[6:]).sum() > 0
+
+
+def test_varlen_oracle_is_the_dense_oracle_per_sequence():
+    """The packed (total, H, D) helpers slice each sequence back to (1, H, n, D) and
+    call the dense functions: check the slicing against dense calls made directly."""
+    lens_q, lens_k = [3, 70, 1], [5, 66, 2]
+    cu_q, cu_k = np.cumsum([0] + lens_q), np.cumsum([0] + lens_k)
+    H, D = 2, 16
+    q = _bf16_vals((cu_q[-1], H, D), seed=69)
+    k = _bf16_vals((cu_k[-1], H, D), seed=70)
+    v = _bf16_vals((cu_k[-1], H, D), seed=71)
+    Qs = oracle.quantize_varlen(q, k, v, cu_q, cu_k, True)
+    rows = np.array([(b, h, i) for b in range(3) for h in range(H) for i in range(lens_q[b])], np.int64)
+    got = oracle.attn_emulate_varlen(Qs, True, 0.25, rows, D)
+    ex = oracle.attn_exact_varlen(q, k, v, cu_q, cu_k, True, 0.25, rows)
+    for b in range(3):
+        qs = q[cu_q[b]:cu_q[b + 1]].transpose(1, 0, 2)[None].copy()
+        ks = k[cu_k[b]:cu_k[b + 1]].transpose(1, 0, 2)[None].copy()
+        vs = v[cu_k[b]:cu_k[b + 1]].transpose(1, 0, 2)[None].copy()
+        Qd = oracle.quantize(qs, ks, vs, True)
+        np.testing.assert_array_equal(Qd.k_i8, Qs[b].k_i8)
+        r = oracle.all_rows(1, H, lens_q[b])
+        sel = rows[:, 0] == b
+        np.testing.assert_array_equal(got[sel], oracle.attn_emulate(Qd, True, 0.25, r))
+        np.testing.assert_array_equal(ex[sel], oracle.attn_exact(qs, ks, vs, True, 0.25, r))

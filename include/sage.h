@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SAGE_ABI_VERSION 1
+#define SAGE_ABI_VERSION 2
 
 typedef enum sage_status {
     SAGE_OK = 0,
@@ -132,7 +132,11 @@ sage_status sage_quant_v(const void* v, sage_dtype dtype, sage_layout layout, in
  *   above (v_scale only in FP8 mode, may be NULL otherwise).
  *   out: [B,H_qo,Nq,D] (HND) or [B,Nq,H_qo,D] (NHD) in out_dtype; every element
  *   is written.
- *   is_causal: key j is visible to query i iff j <= i; requires Nq == Nkv.
+ *   is_causal: key j is visible to query i iff j <= i + Nkv - Nq (the diagonal
+ *   aligned to the bottom-right corner: with Nq < Nkv the queries are the last Nq
+ *   positions of the keys' sequence; README "Project Updates" allows q and k/v of
+ *   different lengths).  A query that sees no key (Nq > Nkv, i < Nq - Nkv) gets an
+ *   output row of zeros.
  *   sm_scale: finite and > 0 (callers pass 1/sqrt(D) for SDPA semantics).
  *   accum: SAGE_ACC_FP32 or SAGE_ACC_FP16_FP32.
  */
@@ -150,6 +154,61 @@ sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t
  */
 sage_status sage_debug_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int B, int H_qo, int H_kv, int Nq, int Nkv,
                                 int D, sage_pv pv, const int32_t* tiles, int T, int32_t* out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Variable-length batches (README "Available APIs": sageattn_varlen, several
+ * sequences of different lengths in one call; "Project Updates": q and k/v of
+ * different lengths).  The tokens of the B sequences are packed along one axis:
+ *   q [total_q][H_qo][D], k and v [total_kv][H_kv][D], out [total_q][H_qo][D],
+ *   all contiguous; cu_seqlens_q / cu_seqlens_kv are DEVICE int32 [B + 1] prefix
+ *   sums (cu[0] = 0, non-decreasing, cu[B] = total): sequence b holds tokens
+ *   cu[b] .. cu[b+1]-1.  max_seqlen_q / max_seqlen_kv (host) bound every sequence's
+ *   length and size the launch grids.
+ * The batch is the dense operation above applied to every sequence on its own:
+ * its own K mean, block scales and V scales, causal aligned per sequence; a
+ * sequence without keys gives zeros.  The kernels clamp what they read from
+ * cu_seqlens into [0, total] and to max_seqlen, so inconsistent prefix sums give
+ * wrong numbers but no access outside the buffers.
+ * Layouts of the quantised intermediates: per (kv) head, sage_varlen_rows(total, B)
+ * = total + 64*B rows of Dp elements and sage_varlen_slots(total, B) =
+ * ceil(rows / 64) block slots; sequence b's 64-token block j occupies rows
+ * R_b + 64*j .. R_b + 64*j + 63, R_b = cu[b] + 64*b (rows past the sequence's end
+ * written with zero), and slot floor(R_b / 64) + j:
+ *   q_i8     int8   [H_qo][rows(total_q)][Dp]     q_scale  float [H_qo][slots(total_q)]
+ *   k_i8     int8   [H_kv][rows(total_kv)][Dp]    k_scale  float [H_kv][slots(total_kv)]
+ *   k_mean   float  [B][H_kv][D]
+ *   v_hat    fp16 or e4m3 [H_kv][slots(total_kv)][Dp][64] (blocks channel-major)
+ *   v_scale  float  [B][H_kv][Dp]                  (FP8 mode only)
+ * Rows and slots between two sequences' blocks are not written.
+ */
+int64_t sage_varlen_rows(int total, int B);
+int64_t sage_varlen_slots(int total, int B);
+
+/* Workspace of sage_quant_qk_varlen: H_kv * slots(total_kv, B) * D * 8 bytes (fp64
+ * block partial sums of K).  sage_quant_v_varlen takes sage_quant_v_workspace_bytes. */
+size_t sage_quant_qk_varlen_workspace_bytes(int B, int H_kv, int total_kv, int D);
+
+/* sage_quant_qk on a packed batch: per sequence, the K mean over its own tokens and
+ * the 64-token blocks counted from its first token (arithmetic as sage_quant_qk). */
+sage_status sage_quant_qk_varlen(const void* q, const void* k, sage_dtype dtype, const int32_t* cu_seqlens_q,
+                                 const int32_t* cu_seqlens_kv, int B, int H_qo, int H_kv, int total_q, int total_kv,
+                                 int max_seqlen_q, int max_seqlen_kv, int D, int8_t* q_i8, float* q_scale,
+                                 int8_t* k_i8, float* k_scale, float* k_mean, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/* sage_quant_v on a packed batch: in FP8 mode the per-channel scale of each sequence
+ * comes from that sequence's tokens alone. */
+sage_status sage_quant_v_varlen(const void* v, sage_dtype dtype, const int32_t* cu_seqlens_kv, int B, int H_kv,
+                                int total_kv, int max_seqlen_kv, int D, sage_pv pv, void* v_hat, float* v_scale,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* sage_attn_fwd on a packed batch (causal per sequence as in sage_attn_fwd);
+ * out [total_q][H_qo][D] in out_dtype, every element written. */
+sage_status sage_attn_fwd_varlen(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                                 const void* v_hat, const float* v_scale, void* out, sage_dtype out_dtype,
+                                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int B, int H_qo, int H_kv,
+                                 int total_q, int total_kv, int max_seqlen_q, int max_seqlen_kv, int D, int is_causal,
+                                 float sm_scale, sage_pv pv, sage_accum accum, void* stream);
 
 #ifdef __cplusplus
 }

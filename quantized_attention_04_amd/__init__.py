@@ -13,6 +13,10 @@ Tensor level:
     debug_qk_int32(qk, tiles, pv) -> int32 [T, 64, 64]
     sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None,
              pv="fp8", accum="fp32")   -- the composition of the three calls
+Packed variable-length batches (q (total_q, H, D), cu_seqlens prefix sums):
+    quant_qk_varlen, quant_v_varlen, attn_fwd_varlen,
+    sageattn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                    is_causal=False, sm_scale=None, pv="fp16", accum="fp32")
 """
 from __future__ import annotations
 
@@ -26,7 +30,8 @@ import torch
 
 __all__ = [
     "SageError", "lib", "library_path", "QKQuant", "VQuant", "quant_qk", "quant_v", "attn_fwd", "debug_qk_int32",
-    "sageattn", "padded_dim", "num_blocks", "SAGE_OK", "SAGE_ERR_INVALID_ARG", "SAGE_ERR_UNSUPPORTED",
+    "sageattn", "QKQuantVarlen", "VQuantVarlen", "quant_qk_varlen", "quant_v_varlen", "attn_fwd_varlen",
+    "sageattn_varlen", "varlen_rows", "varlen_slots", "padded_dim", "num_blocks", "SAGE_OK", "SAGE_ERR_INVALID_ARG", "SAGE_ERR_UNSUPPORTED",
     "SAGE_ERR_WORKSPACE", "SAGE_ERR_DEVICE", "SAGE_ERR_HIP",
 ]
 
@@ -56,6 +61,15 @@ _EXPORTS = {
                       + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "sage_debug_qk_int32": (ctypes.c_int, [ctypes.c_void_p] * 2 + [ctypes.c_int] * 7
                             + [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]),
+    "sage_varlen_rows": (ctypes.c_int64, [ctypes.c_int] * 2),
+    "sage_varlen_slots": (ctypes.c_int64, [ctypes.c_int] * 2),
+    "sage_quant_qk_varlen_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
+    "sage_quant_qk_varlen": (ctypes.c_int, [ctypes.c_void_p] * 2 + [ctypes.c_int] + [ctypes.c_void_p] * 2
+                             + [ctypes.c_int] * 8 + [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "sage_quant_v_varlen": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p] + [ctypes.c_int] * 6
+                            + [ctypes.c_void_p] * 3 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "sage_attn_fwd_varlen": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] + [ctypes.c_void_p] * 2
+                             + [ctypes.c_int] * 9 + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
 }
 
 _lib = None
@@ -84,7 +98,7 @@ def lib() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.restype = res
         fn.argtypes = args
-    if L.sage_abi_version() != 1:
+    if L.sage_abi_version() != 2:
         raise ImportError("libsage ABI version mismatch")
     _lib = L
     return L
@@ -260,3 +274,152 @@ def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: s
     qk = quant_qk(q, k, tensor_layout)
     vq = quant_v(v, tensor_layout, pv)
     return attn_fwd(qk, vq, q.dtype, tensor_layout, is_causal, sm_scale, accum)
+
+
+# ----------------------------------------------------------------------------- variable-length batches
+# sageattn_varlen (SageAttention project README, "Available APIs"): the tokens of B
+# sequences packed along one axis, q (total_q, Hq, D) and k, v (total_kv, Hkv, D),
+# delimited by int32 prefix sums cu_seqlens [B + 1] on the GPU.
+
+def varlen_rows(total: int, B: int) -> int:
+    return int(lib().sage_varlen_rows(total, B))
+
+
+def varlen_slots(total: int, B: int) -> int:
+    return int(lib().sage_varlen_slots(total, B))
+
+
+@dataclasses.dataclass
+class QKQuantVarlen:
+    q_i8: torch.Tensor      # int8 [Hq, rows(total_q), Dp]
+    q_scale: torch.Tensor   # f32  [Hq, slots(total_q)]
+    k_i8: torch.Tensor      # int8 [Hkv, rows(total_kv), Dp]
+    k_scale: torch.Tensor   # f32  [Hkv, slots(total_kv)]
+    k_mean: torch.Tensor    # f32  [B, Hkv, D]
+    cu_q: torch.Tensor
+    cu_k: torch.Tensor
+    B: int
+    Hq: int
+    Hkv: int
+    total_q: int
+    total_kv: int
+    max_q: int
+    max_k: int
+    D: int
+
+
+@dataclasses.dataclass
+class VQuantVarlen:
+    v_hat: torch.Tensor               # uint8 [Hkv, slots(total_kv), Dp, 64*elt]
+    v_scale: Optional[torch.Tensor]   # f32 [B, Hkv, Dp] (FP8 only)
+    pv: str
+
+
+def _packed_dims(x: torch.Tensor, name: str):
+    if x.dim() != 3:
+        raise ValueError(f"{name}: expected a packed (total_tokens, heads, head_dim) tensor, got {tuple(x.shape)}")
+    return x.shape
+
+
+def _cu(cu: torch.Tensor, dev: torch.device, name: str) -> torch.Tensor:
+    if cu.dim() != 1 or cu.numel() < 2:
+        raise ValueError(f"{name}: expected a 1-D tensor of B + 1 prefix sums")
+    if cu.device != dev:
+        raise ValueError(f"{name}: must live on {dev}")
+    return cu.to(torch.int32).contiguous()
+
+
+def quant_qk_varlen(q: torch.Tensor, k: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
+                    max_seqlen_q: int, max_seqlen_k: int, workspace: Optional[torch.Tensor] = None,
+                    out: Optional[QKQuantVarlen] = None) -> QKQuantVarlen:
+    _check_input(q, "q")
+    _check_input(k, "k")
+    if q.dtype != k.dtype or q.device != k.device:
+        raise ValueError("q and k must share dtype and device")
+    total_q, Hq, D = _packed_dims(q, "q")
+    total_k, Hkv, Dk = _packed_dims(k, "k")
+    if Dk != D:
+        raise ValueError("q and k disagree on head_dim")
+    dev = q.device
+    cq, ck = _cu(cu_seqlens_q, dev, "cu_seqlens_q"), _cu(cu_seqlens_k, dev, "cu_seqlens_k")
+    if cq.numel() != ck.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must describe the same number of sequences")
+    B = cq.numel() - 1
+    L = lib()
+    Dp = padded_dim(D)
+    if out is None:
+        rq, sq, rk, sk = varlen_rows(total_q, B), varlen_slots(total_q, B), varlen_rows(total_k, B), varlen_slots(total_k, B)
+        out = QKQuantVarlen(torch.empty(Hq, rq, max(Dp, 1), dtype=torch.int8, device=dev),
+                            torch.empty(Hq, sq, dtype=torch.float32, device=dev),
+                            torch.empty(Hkv, rk, max(Dp, 1), dtype=torch.int8, device=dev),
+                            torch.empty(Hkv, sk, dtype=torch.float32, device=dev),
+                            torch.empty(B, Hkv, D, dtype=torch.float32, device=dev), cq, ck, B, Hq, Hkv, total_q,
+                            total_k, int(max_seqlen_q), int(max_seqlen_k), D)
+    need = L.sage_quant_qk_varlen_workspace_bytes(B, Hkv, total_k, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=dev)
+    _check(L.sage_quant_qk_varlen(q.data_ptr(), k.data_ptr(), _DT[q.dtype], cq.data_ptr(), ck.data_ptr(), B, Hq, Hkv,
+                                  total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), D, out.q_i8.data_ptr(),
+                                  out.q_scale.data_ptr(), out.k_i8.data_ptr(), out.k_scale.data_ptr(),
+                                  out.k_mean.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(dev)))
+    return out
+
+
+def quant_v_varlen(v: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_k: int, pv: str = "fp16",
+                   workspace: Optional[torch.Tensor] = None, out: Optional[VQuantVarlen] = None) -> VQuantVarlen:
+    _check_input(v, "v")
+    if pv not in _PV:
+        raise ValueError(f"pv must be 'fp16' or 'fp8', got {pv!r}")
+    total_k, Hkv, D = _packed_dims(v, "v")
+    dev = v.device
+    ck = _cu(cu_seqlens_k, dev, "cu_seqlens_k")
+    B = ck.numel() - 1
+    L = lib()
+    Dp = padded_dim(D)
+    elt = 1 if pv == "fp8" else 2
+    if out is None:
+        out = VQuantVarlen(torch.empty(Hkv, varlen_slots(total_k, B), max(Dp, 1), 64 * elt, dtype=torch.uint8,
+                                       device=dev),
+                           torch.empty(B, Hkv, max(Dp, 1), dtype=torch.float32, device=dev) if pv == "fp8" else None,
+                           pv)
+    need = L.sage_quant_v_workspace_bytes(B, Hkv, D, _PV[pv])
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(L.sage_quant_v_varlen(v.data_ptr(), _DT[v.dtype], ck.data_ptr(), B, Hkv, total_k, int(max_seqlen_k), D,
+                                 _PV[pv], out.v_hat.data_ptr(), _ptr(out.v_scale), _ptr(workspace),
+                                 0 if workspace is None else workspace.numel(), _stream(dev)))
+    return out
+
+
+def attn_fwd_varlen(qk: QKQuantVarlen, vq: VQuantVarlen, out_dtype: torch.dtype, is_causal: bool = False,
+                    sm_scale: Optional[float] = None, accum: str = "fp32",
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    if out_dtype not in _DT:
+        raise ValueError("out_dtype must be float16 or bfloat16")
+    if accum not in _ACC:
+        raise ValueError(f"accum must be one of {sorted(_ACC)}, got {accum!r}")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(qk.D)
+    dev = qk.q_i8.device
+    if out is None:
+        out = torch.empty(qk.total_q, qk.Hq, qk.D, dtype=out_dtype, device=dev)
+    _check(lib().sage_attn_fwd_varlen(qk.q_i8.data_ptr(), qk.q_scale.data_ptr(), qk.k_i8.data_ptr(),
+                                      qk.k_scale.data_ptr(), vq.v_hat.data_ptr(), _ptr(vq.v_scale), out.data_ptr(),
+                                      _DT[out_dtype], qk.cu_q.data_ptr(), qk.cu_k.data_ptr(), qk.B, qk.Hq, qk.Hkv,
+                                      qk.total_q, qk.total_kv, qk.max_q, qk.max_k, qk.D, int(bool(is_causal)),
+                                      float(sm_scale), _PV[vq.pv], _ACC[accum], _stream(dev)))
+    return out
+
+
+def sageattn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                    cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, is_causal: bool = False,
+                    sm_scale: Optional[float] = None, pv: str = "fp16", accum: str = "fp32") -> torch.Tensor:
+    """Attention over a packed batch of sequences of different lengths (each sequence
+    attends only to its own keys); returns q's dtype, shape (total_q, Hq, D)."""
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _check_input(x, name)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must share a dtype")
+    qk = quant_qk_varlen(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    vq = quant_v_varlen(v, qk.cu_k, max_seqlen_k, pv)
+    return attn_fwd_varlen(qk, vq, q.dtype, is_causal, sm_scale, accum)

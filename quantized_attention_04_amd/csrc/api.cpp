@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <climits>
 #include <cmath>
 
 #include "../../include/sage.h"
@@ -81,6 +82,50 @@ sage_status check_shape(int B, int Hq, int Hkv, int Nq, int Nkv, int D) {
 int padded_dim(int D) { return D <= 0 || D > 128 ? 0 : (D <= 64 ? 64 : 128); }
 int nblocks(int N) { return N <= 0 ? 0 : (N + 63) / 64; }
 
+// Packed (variable-length) batches: rows and block slots per head.
+int64_t varlen_rows(int total, int B) { return int64_t(total) + 64 * int64_t(B); }
+int64_t varlen_slots(int total, int B) { return (varlen_rows(total, B) + 63) / 64; }
+
+sage_status check_varlen(const int32_t* cu_q, const int32_t* cu_k, int B, int Hq, int Hkv, int total_q, int total_kv,
+                         int max_q, int max_kv, int D) {
+    if (!cu_q || !cu_k) return fail(SAGE_ERR_INVALID_ARG, "cu_seqlens pointers must not be null");
+    if (!aligned(cu_q, 4) || !aligned(cu_k, 4)) return fail(SAGE_ERR_INVALID_ARG, "cu_seqlens must be 4-byte aligned");
+    if (total_q <= 0 || total_kv <= 0)
+        return fail(SAGE_ERR_INVALID_ARG, "total token counts must be positive (total_q=%d total_kv=%d)", total_q,
+                    total_kv);
+    sage_status s = check_shape(B, Hq, Hkv, max_q, max_kv, D);
+    if (s != SAGE_OK) return s;
+    if (varlen_rows(total_q, B) > INT32_MAX || varlen_rows(total_kv, B) > INT32_MAX)
+        return fail(SAGE_ERR_UNSUPPORTED, "total tokens + 64 * batch above 2^31");
+    return SAGE_OK;
+}
+
+
+// Checks shared by the dense and the packed attention calls (not the shapes).
+sage_status check_attn_args(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                            const void* v_hat, const float* v_scale, void* out, sage_dtype out_dtype, int is_causal,
+                            float sm_scale, sage_pv pv, sage_accum accum, int D, const char* what) {
+    if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v_hat || !out)
+        return fail(SAGE_ERR_INVALID_ARG, "%s: null tensor pointer", what);
+    if (out_dtype != SAGE_FP16 && out_dtype != SAGE_BF16)
+        return fail(SAGE_ERR_INVALID_ARG, "bad out dtype %d", int(out_dtype));
+    if (pv != SAGE_PV_FP16 && pv != SAGE_PV_FP8) return fail(SAGE_ERR_INVALID_ARG, "bad pv mode %d", int(pv));
+    if (accum != SAGE_ACC_FP32 && accum != SAGE_ACC_FP16_FP32 && accum != SAGE_ACC_FP16)
+        return fail(SAGE_ERR_INVALID_ARG, "bad accum mode %d", int(accum));
+    if (is_causal != 0 && is_causal != 1) return fail(SAGE_ERR_INVALID_ARG, "is_causal must be 0 or 1");
+    if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
+        return fail(SAGE_ERR_INVALID_ARG, "sm_scale must be finite and > 0 (got %g)", double(sm_scale));
+    if (accum == SAGE_ACC_FP16)
+        return fail(SAGE_ERR_UNSUPPORTED, "single-level fp16 PV accumulation is not offered: gfx950 matrix cores "
+                                          "accumulate FP16/FP8 products in fp32");
+    if (pv == SAGE_PV_FP8 && (!v_scale || !aligned(v_scale, 4)))
+        return fail(SAGE_ERR_INVALID_ARG, "%s: FP8 mode needs v_scale", what);
+    if (!aligned(q_i8, 16) || !aligned(k_i8, 16) || !aligned(v_hat, 16) || !aligned(q_scale, 4) ||
+        !aligned(k_scale, 4) || !aligned(out, (D % 4) == 0 ? 8 : 2))
+        return fail(SAGE_ERR_INVALID_ARG, "%s: misaligned tensor", what);
+    return SAGE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -133,8 +178,14 @@ sage_status sage_quant_qk(const void* q, const void* k, sage_dtype dtype, sage_l
                     need, workspace ? workspace_bytes : size_t(0));
     s = check_device();
     if (s != SAGE_OK) return s;
-    sage::QuantQKArgs a{q, k, dtype == SAGE_BF16, layout == SAGE_NHD, B, H_qo, H_kv, Nq, Nkv, D,
-                        q_i8, q_scale, k_i8, k_scale, k_mean, workspace};
+    sage::QuantQKArgs a{};
+    a.q = q;
+    a.k = k;
+    a.bf16 = dtype == SAGE_BF16;
+    a.layout_nhd = layout == SAGE_NHD;
+    a.B = B, a.Hq = H_qo, a.Hkv = H_kv, a.Nq = Nq, a.Nkv = Nkv, a.D = D;
+    a.q_i8 = q_i8, a.q_scale = q_scale, a.k_i8 = k_i8, a.k_scale = k_scale, a.k_mean = k_mean;
+    a.workspace = workspace;
     return launch_status(sage::launch_quant_qk(a, (hipStream_t)stream), "sage_quant_qk");
 }
 
@@ -157,8 +208,13 @@ sage_status sage_quant_v(const void* v, sage_dtype dtype, sage_layout layout, in
     }
     s = check_device();
     if (s != SAGE_OK) return s;
-    sage::QuantVArgs a{v, dtype == SAGE_BF16, layout == SAGE_NHD, B, H_kv, Nkv, D, pv == SAGE_PV_FP8,
-                       v_hat, v_scale, workspace};
+    sage::QuantVArgs a{};
+    a.v = v;
+    a.bf16 = dtype == SAGE_BF16;
+    a.layout_nhd = layout == SAGE_NHD;
+    a.B = B, a.Hkv = H_kv, a.Nkv = Nkv, a.D = D;
+    a.fp8 = pv == SAGE_PV_FP8;
+    a.v_hat = v_hat, a.v_scale = v_scale, a.workspace = workspace;
     return launch_status(sage::launch_quant_v(a, (hipStream_t)stream), "sage_quant_v");
 }
 
@@ -166,34 +222,25 @@ sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t
                           const void* v_hat, const float* v_scale, void* out, sage_dtype out_dtype,
                           sage_layout out_layout, int B, int H_qo, int H_kv, int Nq, int Nkv, int D, int is_causal,
                           float sm_scale, sage_pv pv, sage_accum accum, void* stream) {
-    if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v_hat || !out)
-        return fail(SAGE_ERR_INVALID_ARG, "sage_attn_fwd: null tensor pointer");
-    if (out_dtype != SAGE_FP16 && out_dtype != SAGE_BF16)
-        return fail(SAGE_ERR_INVALID_ARG, "bad out dtype %d", int(out_dtype));
+    sage_status s = check_attn_args(q_i8, q_scale, k_i8, k_scale, v_hat, v_scale, out, out_dtype, is_causal, sm_scale,
+                                    pv, accum, D, "sage_attn_fwd");
+    if (s != SAGE_OK) return s;
     if (out_layout != SAGE_HND && out_layout != SAGE_NHD)
         return fail(SAGE_ERR_INVALID_ARG, "bad layout %d", int(out_layout));
-    if (pv != SAGE_PV_FP16 && pv != SAGE_PV_FP8) return fail(SAGE_ERR_INVALID_ARG, "bad pv mode %d", int(pv));
-    if (accum != SAGE_ACC_FP32 && accum != SAGE_ACC_FP16_FP32 && accum != SAGE_ACC_FP16)
-        return fail(SAGE_ERR_INVALID_ARG, "bad accum mode %d", int(accum));
-    if (is_causal != 0 && is_causal != 1) return fail(SAGE_ERR_INVALID_ARG, "is_causal must be 0 or 1");
-    if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
-        return fail(SAGE_ERR_INVALID_ARG, "sm_scale must be finite and > 0 (got %g)", double(sm_scale));
-    sage_status s = check_shape(B, H_qo, H_kv, Nq, Nkv, D);
+    s = check_shape(B, H_qo, H_kv, Nq, Nkv, D);
     if (s != SAGE_OK) return s;
-    if (accum == SAGE_ACC_FP16)
-        return fail(SAGE_ERR_UNSUPPORTED, "single-level fp16 PV accumulation is not offered: gfx950 matrix cores "
-                                          "accumulate FP16/FP8 products in fp32");
-    if (is_causal && Nq != Nkv) return fail(SAGE_ERR_UNSUPPORTED, "causal attention requires Nq == Nkv");
-    if (pv == SAGE_PV_FP8 && (!v_scale || !aligned(v_scale, 4)))
-        return fail(SAGE_ERR_INVALID_ARG, "sage_attn_fwd: FP8 mode needs v_scale");
-    if (!aligned(q_i8, 16) || !aligned(k_i8, 16) || !aligned(v_hat, 16) || !aligned(q_scale, 4) ||
-        !aligned(k_scale, 4) || !aligned(out, (D % 4) == 0 ? 8 : 2))
-        return fail(SAGE_ERR_INVALID_ARG, "sage_attn_fwd: misaligned tensor");
     s = check_device();
     if (s != SAGE_OK) return s;
-    sage::AttnArgs a{q_i8, q_scale, k_i8, k_scale, v_hat, v_scale, out, out_dtype == SAGE_BF16,
-                     out_layout == SAGE_NHD, B, H_qo, H_kv, Nq, Nkv, D, is_causal, sm_scale, pv == SAGE_PV_FP8,
-                     accum == SAGE_ACC_FP16_FP32};
+    sage::AttnArgs a{};
+    a.q_i8 = q_i8, a.q_scale = q_scale, a.k_i8 = k_i8, a.k_scale = k_scale, a.v_hat = v_hat, a.v_scale = v_scale;
+    a.out = out;
+    a.out_bf16 = out_dtype == SAGE_BF16;
+    a.out_nhd = out_layout == SAGE_NHD;
+    a.B = B, a.Hq = H_qo, a.Hkv = H_kv, a.Nq = Nq, a.Nkv = Nkv, a.D = D;
+    a.causal = is_causal;
+    a.sm_scale = sm_scale;
+    a.fp8 = pv == SAGE_PV_FP8;
+    a.two_level = accum == SAGE_ACC_FP16_FP32;
     return launch_status(sage::launch_attn_fwd(a, (hipStream_t)stream), "sage_attn_fwd");
 }
 
@@ -210,6 +257,101 @@ sage_status sage_debug_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int B, i
     if (s != SAGE_OK) return s;
     sage::DebugQKArgs a{q_i8, k_i8, B, H_qo, H_kv, Nq, Nkv, D, pv == SAGE_PV_FP8, tiles, T, out};
     return launch_status(sage::launch_debug_qk(a, (hipStream_t)stream), "sage_debug_qk_int32");
+}
+
+int64_t sage_varlen_rows(int total, int B) { return total <= 0 || B <= 0 ? 0 : varlen_rows(total, B); }
+int64_t sage_varlen_slots(int total, int B) { return total <= 0 || B <= 0 ? 0 : varlen_slots(total, B); }
+
+size_t sage_quant_qk_varlen_workspace_bytes(int B, int H_kv, int total_kv, int D) {
+    if (B <= 0 || H_kv <= 0 || total_kv <= 0 || D <= 0 || D > 128) return 0;
+    return size_t(H_kv) * size_t(varlen_slots(total_kv, B)) * size_t(D) * sizeof(double);
+}
+
+sage_status sage_quant_qk_varlen(const void* q, const void* k, sage_dtype dtype, const int32_t* cu_seqlens_q,
+                                 const int32_t* cu_seqlens_kv, int B, int H_qo, int H_kv, int total_q, int total_kv,
+                                 int max_seqlen_q, int max_seqlen_kv, int D, int8_t* q_i8, float* q_scale,
+                                 int8_t* k_i8, float* k_scale, float* k_mean, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    if (!q || !k || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean)
+        return fail(SAGE_ERR_INVALID_ARG, "sage_quant_qk_varlen: null tensor pointer");
+    if (dtype != SAGE_FP16 && dtype != SAGE_BF16) return fail(SAGE_ERR_INVALID_ARG, "bad dtype %d", int(dtype));
+    sage_status s = check_varlen(cu_seqlens_q, cu_seqlens_kv, B, H_qo, H_kv, total_q, total_kv, max_seqlen_q,
+                                 max_seqlen_kv, D);
+    if (s != SAGE_OK) return s;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_i8, 16) || !aligned(k_i8, 16) || !aligned(q_scale, 4) ||
+        !aligned(k_scale, 4) || !aligned(k_mean, 4))
+        return fail(SAGE_ERR_INVALID_ARG, "sage_quant_qk_varlen: tensors must be 16-byte aligned (scales 4-byte)");
+    const size_t need = sage_quant_qk_varlen_workspace_bytes(B, H_kv, total_kv, D);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 8))
+        return fail(SAGE_ERR_WORKSPACE, "sage_quant_qk_varlen: workspace of %zu bytes (8-byte aligned) required, got %zu",
+                    need, workspace ? workspace_bytes : size_t(0));
+    s = check_device();
+    if (s != SAGE_OK) return s;
+    sage::QuantQKArgs a{};
+    a.q = q;
+    a.k = k;
+    a.bf16 = dtype == SAGE_BF16;
+    a.B = B, a.Hq = H_qo, a.Hkv = H_kv, a.Nq = max_seqlen_q, a.Nkv = max_seqlen_kv, a.D = D;
+    a.cu_q = cu_seqlens_q, a.cu_k = cu_seqlens_kv, a.total_q = total_q, a.total_k = total_kv;
+    a.q_i8 = q_i8, a.q_scale = q_scale, a.k_i8 = k_i8, a.k_scale = k_scale, a.k_mean = k_mean;
+    a.workspace = workspace;
+    return launch_status(sage::launch_quant_qk(a, (hipStream_t)stream), "sage_quant_qk_varlen");
+}
+
+sage_status sage_quant_v_varlen(const void* v, sage_dtype dtype, const int32_t* cu_seqlens_kv, int B, int H_kv,
+                                int total_kv, int max_seqlen_kv, int D, sage_pv pv, void* v_hat, float* v_scale,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    if (!v || !v_hat) return fail(SAGE_ERR_INVALID_ARG, "sage_quant_v_varlen: null tensor pointer");
+    if (dtype != SAGE_FP16 && dtype != SAGE_BF16) return fail(SAGE_ERR_INVALID_ARG, "bad dtype %d", int(dtype));
+    if (pv != SAGE_PV_FP16 && pv != SAGE_PV_FP8) return fail(SAGE_ERR_INVALID_ARG, "bad pv mode %d", int(pv));
+    sage_status s = check_varlen(cu_seqlens_kv, cu_seqlens_kv, B, H_kv, H_kv, total_kv, total_kv, max_seqlen_kv,
+                                 max_seqlen_kv, D);
+    if (s != SAGE_OK) return s;
+    if (!aligned(v, 16) || !aligned(v_hat, 16))
+        return fail(SAGE_ERR_INVALID_ARG, "sage_quant_v_varlen: tensors must be 16-byte aligned");
+    if (pv == SAGE_PV_FP8) {
+        if (!v_scale || !aligned(v_scale, 4))
+            return fail(SAGE_ERR_INVALID_ARG, "sage_quant_v_varlen: FP8 mode needs v_scale");
+        const size_t need = sage_quant_v_workspace_bytes(B, H_kv, D, pv);
+        if (!workspace || workspace_bytes < need || !aligned(workspace, 4))
+            return fail(SAGE_ERR_WORKSPACE, "sage_quant_v_varlen: workspace of %zu bytes required, got %zu", need,
+                        workspace ? workspace_bytes : size_t(0));
+    }
+    s = check_device();
+    if (s != SAGE_OK) return s;
+    sage::QuantVArgs a{};
+    a.v = v;
+    a.bf16 = dtype == SAGE_BF16;
+    a.B = B, a.Hkv = H_kv, a.Nkv = max_seqlen_kv, a.D = D;
+    a.cu_k = cu_seqlens_kv, a.total_k = total_kv;
+    a.fp8 = pv == SAGE_PV_FP8;
+    a.v_hat = v_hat, a.v_scale = v_scale, a.workspace = workspace;
+    return launch_status(sage::launch_quant_v(a, (hipStream_t)stream), "sage_quant_v_varlen");
+}
+
+sage_status sage_attn_fwd_varlen(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                                 const void* v_hat, const float* v_scale, void* out, sage_dtype out_dtype,
+                                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int B, int H_qo, int H_kv,
+                                 int total_q, int total_kv, int max_seqlen_q, int max_seqlen_kv, int D, int is_causal,
+                                 float sm_scale, sage_pv pv, sage_accum accum, void* stream) {
+    sage_status s = check_attn_args(q_i8, q_scale, k_i8, k_scale, v_hat, v_scale, out, out_dtype, is_causal, sm_scale,
+                                    pv, accum, D, "sage_attn_fwd_varlen");
+    if (s != SAGE_OK) return s;
+    s = check_varlen(cu_seqlens_q, cu_seqlens_kv, B, H_qo, H_kv, total_q, total_kv, max_seqlen_q, max_seqlen_kv, D);
+    if (s != SAGE_OK) return s;
+    s = check_device();
+    if (s != SAGE_OK) return s;
+    sage::AttnArgs a{};
+    a.q_i8 = q_i8, a.q_scale = q_scale, a.k_i8 = k_i8, a.k_scale = k_scale, a.v_hat = v_hat, a.v_scale = v_scale;
+    a.out = out;
+    a.out_bf16 = out_dtype == SAGE_BF16;
+    a.B = B, a.Hq = H_qo, a.Hkv = H_kv, a.Nq = max_seqlen_q, a.Nkv = max_seqlen_kv, a.D = D;
+    a.causal = is_causal;
+    a.sm_scale = sm_scale;
+    a.fp8 = pv == SAGE_PV_FP8;
+    a.two_level = accum == SAGE_ACC_FP16_FP32;
+    a.cu_q = cu_seqlens_q, a.cu_k = cu_seqlens_kv, a.total_q = total_q, a.total_k = total_kv;
+    return launch_status(sage::launch_attn_fwd(a, (hipStream_t)stream), "sage_attn_fwd_varlen");
 }
 
 }  // extern "C"

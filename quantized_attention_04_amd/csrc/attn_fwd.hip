@@ -234,17 +234,18 @@ struct PPack<false> {
 // at a time, so no array of fp32 probabilities is ever live.  Masked keys get INT32_MIN
 // and p = 0.  t = S32 * c - m is formed with one rounding (fma), keeping P's rounding
 // to FP16 / e4m3 close to a correctly rounded evaluation.
+// kmax: the last key this lane's query may see when causal.
 template <bool FP8, bool MASK, bool CAUSAL>
 __device__ __forceinline__ float softmax_tile(v16i (&S)[2], PPack<FP8>& pk, float c, float& m, float& l, int g,
-                                              int key0, int qidx, int Nkv) {
+                                              int key0, int kmax, int Nkv) {
     if constexpr (MASK) {
-        // key key0 + key_of_reg(kt, g, r) is visible iff it is below min(Nkv, qidx + 1)
+        // key key0 + key_of_reg(kt, g, r) is visible iff it is below min(Nkv, kmax + 1)
         // (causal) or Nkv; key_of_reg(kt, g, r) = key_of_reg(kt, 0, r) + (32 | 8) * g,
         // so one per-lane threshold against compile-time offsets decides every
         // register.  The threshold is kept opaque: otherwise the compiler proves it
         // loop-invariant on the tail tile and hoists 32 masks out of the tile loop.
         int lim = Nkv;
-        if constexpr (CAUSAL) lim = min(lim, qidx + 1);
+        if constexpr (CAUSAL) lim = min(lim, kmax + 1);
         int t = lim - key0 - (FP8 ? 32 : 8) * g;
         asm volatile("" : "+v"(t));
 #pragma unroll
@@ -329,8 +330,9 @@ struct KParams {
     const uint8_t* v_hat;
     const float* v_scale;
     void* out;
-    int64_t osb, osh, osq;  // output element strides (batch, head, token)
-    int B, Hq, Hkv, G, Nq, Nkv, D, NBq, NBk, QT;
+    SeqMap qm, km;          // query and key/value sequences (dense or packed batch)
+    int64_t osb, osh, osq;  // output element strides (batch, head, token); packed: token = Hq*D, head = D
+    int B, Hq, Hkv, G, D, QT;
     float cscale;  // sm_scale * log2(e)
 };
 
@@ -357,30 +359,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
         h = (bhk % p.Hkv) * p.G + hg;
     }
     const int hk = h / p.G;
+    const SeqView qv = seq_view(p.qm, b, h), kv = seq_view(p.km, b, hk);
+    const int Nq = qv.n, Nkv = kv.n, NBk = (Nkv + kBlk - 1) / kBlk;
+    if (qt * C::BM >= Nq) return;  // the whole workgroup: past this sequence's queries
+    // causal: key j is visible to query i iff j <= i + off (diagonal aligned to the
+    // bottom-right corner, so with Nq < Nkv the queries are the sequence's last ones)
+    const int off = Nkv - Nq;
     const int q0 = qt * C::BM + wave * C::QW;  // this wave's first query
-    const bool active = q0 < p.Nq;
+    const bool active = q0 < Nq;
     const int qb = q0 / kBlk;
     const int qidx = q0 + i;  // this lane's query
 
-    const int64_t bhk = int64_t(b) * p.Hkv + hk;
-    const int8_t* kbase = p.k_i8 + bhk * int64_t(p.NBk) * kBlk * DP;
-    const uint8_t* vbase = p.v_hat + bhk * int64_t(p.NBk) * C::VBYTES;
+    const int8_t* kbase = p.k_i8 + kv.row0 * DP;
+    const uint8_t* vbase = p.v_hat + kv.slot0 * C::VBYTES;
 
-    int jend = p.NBk;
-    if constexpr (CAUSAL) jend = min(p.NBk, (min(qt * C::BM + C::BM, p.Nq) - 1) / kBlk + 1);
-    const bool ktail = (p.Nkv % kBlk) != 0;
+    int jend = NBk;
+    if constexpr (CAUSAL) {
+        const int kmax = min(qt * C::BM + C::BM, Nq) - 1 + off;  // last key the workgroup sees
+        jend = kmax < 0 ? 0 : min(NBk, kmax / kBlk + 1);
+    }
+    const bool ktail = (Nkv % kBlk) != 0;
 
     // ---- per-wave state
     v4i qf[C::KS];
     float sq = 0.0f;
     if (active) {
-        load_q_frags<C>(qf, p.q_i8 + ((int64_t(b) * p.Hq + h) * p.NBq * kBlk + q0) * DP, lane);
-        sq = scalar_load_f32(p.q_scale + (int64_t(b) * p.Hq + h) * p.NBq + qb);
+        load_q_frags<C>(qf, p.q_i8 + (qv.row0 + q0) * DP, lane);
+        sq = scalar_load_f32(p.q_scale + qv.slot0 + qb);
     } else {
 #pragma unroll
         for (int s = 0; s < C::KS; s++) qf[s] = v4i{0, 0, 0, 0};
     }
-    const float* ks_row = p.k_scale + bhk * p.NBk;
+    const float* ks_row = p.k_scale + kv.slot0;
     wait_vmcnt<0>();  // Q fragments resident before the tile pipeline starts
     v16f O[C::DT];
 #pragma unroll
@@ -396,8 +406,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
     };
     // tiles [0, jm) need no mask for this wave; [jm, jend) do.  The split is per wave,
     // but every wave runs the same sequence of iterations (and barriers).
-    int jm = ktail ? p.NBk - 1 : p.NBk;
-    if constexpr (CAUSAL) jm = min(jm, qb);
+    int jm = ktail ? NBk - 1 : NBk;
+    if constexpr (CAUSAL) {
+        const int seen = q0 + off + 1;  // keys visible to the wave's first query
+        jm = min(jm, seen > 0 ? seen / kBlk : 0);
+    }
     jm = min(jm, jend);
 
     // Tile j lives in stage j % NST; the next NST-1 tiles stream in meanwhile.  Every
@@ -408,7 +421,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
 #pragma unroll
     for (int t = 0; t < AHEAD; t++)
         if (t < jend) issue_tile(t);
-    float ks_next = scalar_load_f32(ks_row);
+    float ks_next = jend > 0 ? scalar_load_f32(ks_row) : 0.0f;
     auto step = [&](auto masked, int j) {
         constexpr bool MASK = decltype(masked)::value;
         // tile j landed for this wave (later tiles may still stream); the barrier
@@ -419,13 +432,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
         block_barrier();
         if (j + AHEAD < jend) issue_tile(j + AHEAD);
         const float c = sq * ks_next * p.cscale;
-        ks_next = scalar_load_f32(ks_row + min(j + 1, p.NBk - 1));
+        ks_next = scalar_load_f32(ks_row + min(j + 1, NBk - 1));
         // stage base as one wave-uniform value, so each LDS address costs a single add
         const uint8_t* st = smem + __builtin_amdgcn_readfirstlane((j % C::NST) * C::STAGE);
         v16i S[2];
         qk_tile<C, FP8>(st, qf, S, lane);
         PPack<FP8> pk;
-        const float alpha = softmax_tile<FP8, MASK, CAUSAL>(S, pk, c, m, l, g, j * kBlk, qidx, p.Nkv);
+        const float alpha = softmax_tile<FP8, MASK, CAUSAL>(S, pk, c, m, l, g, j * kBlk, qidx + off, Nkv);
         if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
             for (int dt = 0; dt < C::DT; dt++) O[dt] *= alpha;
@@ -444,11 +457,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
     // ---- epilogue: O^T / l (x v_scale in FP8 mode) -> out dtype, input layout
     if (!active) return;
     const float ltot = halves_sum(l);
-    const float inv = 1.0f / ltot;
-    if (qidx >= p.Nq) return;
-    const float* vsc = FP8 ? p.v_scale + bhk * DP : nullptr;
+    const bool empty = !(ltot > 0.0f);  // a query that sees no key: zeros
+    const float inv = empty ? 0.0f : 1.0f / ltot;
+    if (qidx >= Nq) return;
+    const float* vsc = FP8 ? p.v_scale + (int64_t(b) * p.Hkv + hk) * DP : nullptr;
     const bool vec4 = (p.D & 3) == 0;
-    uint16_t* orow = (uint16_t*)p.out + b * p.osb + h * p.osh + qidx * p.osq;
+    const int64_t obase = p.qm.cu != nullptr ? qv.start * p.osq : b * p.osb;
+    uint16_t* orow = (uint16_t*)p.out + obase + h * p.osh + qidx * p.osq;
 #pragma unroll
     for (int dt = 0; dt < C::DT; dt++)
 #pragma unroll
@@ -459,7 +474,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 float o = O[dt][4 * a4 + e] * inv;
-                if constexpr (FP8) o *= vsc[d0 + e];
+                if constexpr (FP8) o = empty ? 0.0f : o * vsc[d0 + e];
                 hv[e] = OBF16 ? f32_to_bf16_bits(o) : f32_to_f16_bits(o);
             }
             if (vec4) {
@@ -553,16 +568,19 @@ hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s) {
     p.Hq = a.Hq;
     p.Hkv = a.Hkv;
     p.G = a.Hq / a.Hkv;
-    p.Nq = a.Nq;
-    p.Nkv = a.Nkv;
     p.D = a.D;
-    p.NBq = (a.Nq + kBlk - 1) / kBlk;
-    p.NBk = (a.Nkv + kBlk - 1) / kBlk;
+    // the quantised operands' rows and slots (their input layout plays no part here)
+    p.qm = make_seq_map(0, a.cu_q, a.B, a.Hq, a.Nq, a.total_q, a.D);
+    p.km = make_seq_map(0, a.cu_k, a.B, a.Hkv, a.Nkv, a.total_k, a.D);
     constexpr int BM = Cfg<128, true>::BM;
     static_assert(Cfg<64, false>::BM == BM && Cfg<64, true>::BM == BM && Cfg<128, false>::BM == BM, "uniform BM");
     p.QT = (a.Nq + BM - 1) / BM;
     p.cscale = a.sm_scale * kLog2e;
-    if (a.out_nhd) {
+    if (a.cu_q != nullptr) {  // packed (total, H_qo, D)
+        p.osb = 0;
+        p.osh = a.D;
+        p.osq = int64_t(a.Hq) * a.D;
+    } else if (a.out_nhd) {
         p.osb = int64_t(a.Nq) * a.Hq * a.D;
         p.osh = a.D;
         p.osq = int64_t(a.Hq) * a.D;

@@ -18,6 +18,89 @@ typedef unsigned short v8u16 __attribute__((ext_vector_type(8)));
 constexpr int kBlk = 64;  // tokens per quantisation block and per KV tile
 constexpr int kWave = 64;
 
+// ---- where the tokens of one (batch entry, head) live -------------------------------
+struct Strides {
+    int64_t b, h, t;  // element strides of batch, head, token (channel stride is 1)
+};
+
+__host__ __device__ inline Strides make_strides(int layout_nhd, int H, int N, int D) {
+    Strides s;
+    if (layout_nhd) {
+        s.b = int64_t(N) * H * D;
+        s.h = D;
+        s.t = int64_t(H) * D;
+    } else {
+        s.b = int64_t(H) * N * D;
+        s.h = int64_t(N) * D;
+        s.t = D;
+    }
+    return s;
+}
+
+// A batch of sequences, either dense (every sequence N tokens, input strides st) or
+// packed (sequence b = tokens cu[b] .. cu[b+1]-1 of one axis of a (total, H, D)
+// tensor).  Quantised rows and per-block slots: dense, (b, h) owns rows
+// (b*H + h)*NB*64 .. and slots (b*H + h)*NB ..; packed, head h owns `rows` rows and
+// `slots` slots and sequence b starts at row R_b = cu[b] + 64*b (slot floor(R_b/64)),
+// which keeps every sequence's blocks disjoint without a prefix scan over the batch.
+struct SeqMap {
+    const int32_t* cu;   // packed: device prefix sums [B + 1]; dense: null
+    Strides st;          // input strides (packed: t = H*D, h = D)
+    int H, N, NB;        // heads; dense: tokens and 64-token blocks per sequence
+    int total, maxlen;   // packed: tokens in all, bound on one sequence's length
+    int64_t rows, slots; // packed: quantised rows and block slots per head
+};
+struct SeqView {
+    int64_t start;   // first token on the input's token axis (packed), else 0
+    int64_t in_off;  // element offset of (token 0, channel 0) of this (b, h) in the input
+    int n;           // tokens
+    int64_t row0;    // quantised row of token 0
+    int64_t slot0;   // slot of block 0
+};
+// The map of a dense batch (cu == null: B sequences of `n` tokens, input layout HND
+// or NHD) or of a packed one (cu != null: `n` bounds every sequence, `total` tokens in
+// all, input (total, H, D)).  N and NB then give the grid extents.
+inline SeqMap make_seq_map(int layout_nhd, const int32_t* cu, int B, int H, int n, int total, int D) {
+    SeqMap m{};
+    m.cu = cu;
+    m.H = H;
+    m.N = n;
+    m.NB = (n + kBlk - 1) / kBlk;
+    if (cu == nullptr) {
+        m.st = make_strides(layout_nhd, H, n, D);
+    } else {
+        m.st = Strides{0, int64_t(D), int64_t(H) * D};
+        m.total = total;
+        m.maxlen = n;
+        m.rows = int64_t(total) + int64_t(kBlk) * B;
+        m.slots = (m.rows + kBlk - 1) / kBlk;
+    }
+    return m;
+}
+
+// Packed offsets are clamped into [0, total] and to maxlen, so inconsistent prefix
+// sums give wrong numbers but never an access outside the tensors.
+__device__ __forceinline__ SeqView seq_view(const SeqMap& m, int b, int h) {
+    SeqView v;
+    if (m.cu == nullptr) {
+        v.start = 0;
+        v.in_off = b * m.st.b + h * m.st.h;
+        v.n = m.N;
+        v.row0 = (int64_t(b) * m.H + h) * m.NB * kBlk;
+        v.slot0 = (int64_t(b) * m.H + h) * m.NB;
+    } else {
+        const int s = min(max(m.cu[b], 0), m.total);
+        const int e = min(max(m.cu[b + 1], s), m.total);
+        v.n = min(e - s, m.maxlen);
+        const int64_t R = int64_t(s) + int64_t(kBlk) * b;
+        v.start = s;
+        v.in_off = int64_t(s) * m.st.t + h * m.st.h;
+        v.row0 = h * m.rows + R;
+        v.slot0 = h * m.slots + R / kBlk;
+    }
+    return v;
+}
+
 // ---- element conversions -------------------------------------------------------
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {

@@ -5,11 +5,16 @@
 
 namespace sage {
 
+// Batches are dense (cu_* null: B sequences of Nq / Nkv tokens) or packed (cu_* =
+// device prefix sums, Nq / Nkv bound every sequence, total_* tokens in all).
 struct QuantQKArgs {
     const void* q;
     const void* k;
     int bf16, layout_nhd;
     int B, Hq, Hkv, Nq, Nkv, D;
+    const int32_t* cu_q;
+    const int32_t* cu_k;
+    int total_q, total_k;
     int8_t* q_i8;
     float* q_scale;
     int8_t* k_i8;
@@ -22,6 +27,8 @@ struct QuantVArgs {
     const void* v;
     int bf16, layout_nhd;
     int B, Hkv, Nkv, D;
+    const int32_t* cu_k;
+    int total_k;
     int fp8;
     void* v_hat;
     float* v_scale;
@@ -41,6 +48,9 @@ struct AttnArgs {
     int causal;
     float sm_scale;
     int fp8, two_level;
+    const int32_t* cu_q;
+    const int32_t* cu_k;
+    int total_q, total_k;
 };
 
 struct DebugQKArgs {

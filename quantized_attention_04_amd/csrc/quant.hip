@@ -4,42 +4,32 @@
 // fp64 sum over blocks; INT8 block quantisation of Q and smoothed K; the P.V operand
 // V^ in FP16 or FP8-e4m3 with per-channel scales.  The arithmetic of each step is the
 // one stated in include/sage.h (SageAttention project README, "Current Features":
-// INT8 quantization and smoothing for QK^T, FP8 quantization for PV).
+// INT8 quantization and smoothing for QK^T, FP8 quantization for PV).  Every kernel
+// walks a batch of sequences through a SeqMap, dense or packed (the variable-length
+// form of the README's "Available APIs": sageattn_varlen); grids span the longest
+// sequence and blocks past a sequence's end return at once.
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace sage {
 
-struct Strides {
-    int64_t b, h, t;  // element strides of batch, head, token (channel stride is 1)
-};
-
-__host__ __device__ inline Strides make_strides(int layout_nhd, int H, int N, int D) {
-    Strides s;
-    if (layout_nhd) {
-        s.b = int64_t(N) * H * D;
-        s.h = D;
-        s.t = int64_t(H) * D;
-    } else {
-        s.b = int64_t(H) * N * D;
-        s.h = int64_t(N) * D;
-        s.t = D;
-    }
-    return s;
-}
-
 // ------------------------------------------------------------------------------------------
-// K mean, pass 1: part[b][h][j][c] = sum of K[b,h,t,c] over the tokens t of block j,
-// ascending, in fp64.  grid (NB, H, B), 256 threads: the block's 64 x D tile is read
-// with coalesced 16-byte loads into LDS, then thread c < D walks its channel.
+// K mean, pass 1: part[slot of block j][c] = sum of K[b,h,t,c] over the tokens t of
+// block j, ascending, in fp64.  grid (max blocks, H, B), 256 threads: the block's
+// 64 x D tile is read with coalesced 16-byte loads into LDS, then thread c < D walks
+// its channel.
 template <bool BF16, int DP, bool VEC8>
-__global__ __launch_bounds__(256) void k_mean_partial_kernel(const uint16_t* __restrict__ k, Strides st, int N,
-                                                             int D, int NB, double* __restrict__ part) {
+__global__ __launch_bounds__(256) void k_mean_partial_kernel(const uint16_t* __restrict__ k, SeqMap m, int D,
+                                                             double* __restrict__ part) {
     constexpr int CH = DP / 8, RSTEP = 256 / CH;  // RSTEP token rows per pass
     __shared__ __attribute__((aligned(16))) uint16_t tile[kBlk][DP];
     const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const SeqView sv = seq_view(m, b, h);
+    if (j * kBlk >= sv.n) return;  // the whole workgroup: past this sequence's end
+    const int N = sv.n;
+    const Strides st = m.st;
     const int ch = threadIdx.x % CH, r0 = threadIdx.x / CH, c0 = ch * 8;
-    const uint16_t* base = k + b * st.b + h * st.h;
+    const uint16_t* base = k + sv.in_off;
 #pragma unroll
     for (int p = 0; p < kBlk / RSTEP; p++) {
         const int tl = p * RSTEP + r0, t = j * kBlk + tl;
@@ -61,46 +51,50 @@ __global__ __launch_bounds__(256) void k_mean_partial_kernel(const uint16_t* __r
     const int nt = min(kBlk, N - j * kBlk);
     double s = 0.0;
     for (int t = 0; t < nt; t++) s += double(in_to_f32<BF16>(tile[t][c]));
-    part[((int64_t(b) * gridDim.y + h) * NB + j) * D + c] = s;
+    part[(sv.slot0 + j) * D + c] = s;
 }
 
-// K mean, pass 2: mean = fp32((sum over blocks, ascending, of part) / N).  One thread
-// per (b, h, channel) in 64-thread workgroups (enough of them to spread over the CUs).
-__global__ __launch_bounds__(64) void k_mean_final_kernel(const double* __restrict__ part, int total, int NB, int D,
-                                                          int N, float* __restrict__ mean) {
+// K mean, pass 2: mean = fp32((sum over blocks, ascending, of part) / N); 0 for a
+// sequence without tokens.  One thread per (b, h, channel) in 64-thread workgroups
+// (enough of them to spread over the CUs).
+__global__ __launch_bounds__(64) void k_mean_final_kernel(const double* __restrict__ part, SeqMap m, int total,
+                                                          int D, float* __restrict__ mean) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= total) return;
-    const int bh = i / D, c = i % D;
-    const double* p = part + int64_t(bh) * NB * D + c;
+    const int c = i % D, h = (i / D) % m.H, b = i / (D * m.H);
+    const SeqView sv = seq_view(m, b, h);
+    const int nb = (sv.n + kBlk - 1) / kBlk;
+    const double* p = part + sv.slot0 * D + c;
     double s = 0.0;
 #pragma unroll 8
-    for (int j = 0; j < NB; j++) s += p[int64_t(j) * D];
-    mean[i] = float(s / double(N));
+    for (int j = 0; j < nb; j++) s += p[int64_t(j) * D];
+    mean[i] = sv.n > 0 ? float(s / double(sv.n)) : 0.0f;
 }
 
 // ------------------------------------------------------------------------------------------
-// INT8 block quantisation.  One wave per 64-token block of one (b, head); 4 waves per
-// workgroup.  Lane l covers 8 consecutive channels (chunk l % CH, CH = Dp / 8) of the
-// token rows l / CH + p * (64 / CH), p = 0 .. CH-1.
+// INT8 block quantisation.  One wave per 64-token block of one (b, head): grid
+// (ceil(max blocks / 4), H, B), 4 waves per workgroup.  Lane l covers 8 consecutive
+// channels (chunk l % CH, CH = Dp / 8) of the token rows l / CH + p * (64 / CH),
+// p = 0 .. CH-1.
 //   y = x (Q) or fp32(x - mean[c]) (K); amax = max |y|; scale = amax / 127;
 //   inv = 127 / amax; code = clamp(rne(y * inv), -127, 127).
 template <bool BF16, int DP, bool VEC8>
-__global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __restrict__ x, Strides st, int B, int H,
-                                                           int N, int D, int NB, const float* __restrict__ mean,
-                                                           int8_t* __restrict__ xq, float* __restrict__ scale) {
+__global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __restrict__ x, SeqMap m, int D,
+                                                           const float* __restrict__ mean, int8_t* __restrict__ xq,
+                                                           float* __restrict__ scale) {
     constexpr int CH = DP / 8;        // 8-channel chunks per row
     constexpr int RPP = kWave / CH;   // rows per pass
     constexpr int PASSES = kBlk / RPP;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int64_t blk = int64_t(blockIdx.x) * 4 + wave;
-    const int64_t total = int64_t(B) * H * NB;
-    if (blk >= total) return;
-    const int j = int(blk % NB);
-    const int64_t bh = blk / NB;
-    const int h = int(bh % H), b = int(bh / H);
+    const int j = blockIdx.x * 4 + wave, h = blockIdx.y, b = blockIdx.z;
+    const SeqView sv = seq_view(m, b, h);
+    if (j * kBlk >= sv.n) return;  // this wave: past the sequence's end
+    const int N = sv.n;
+    const Strides st = m.st;
+    const int64_t bh = int64_t(b) * m.H + h;
     const int ch = lane % CH, r0 = lane / CH;
     const int c0 = ch * 8;
-    const uint16_t* base = x + b * st.b + h * st.h;
+    const uint16_t* base = x + sv.in_off;
 
     float mu[8];
 #pragma unroll
@@ -139,8 +133,7 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __res
     const bool zero = !(amax > 0.0f);
     const float sc = zero ? 0.0f : amax / 127.0f;
     const float inv = zero ? 0.0f : 127.0f / amax;
-    if (lane == 0) scale[int64_t(bh) * NB + j] = sc;
-    const int64_t npad = int64_t(NB) * kBlk;
+    if (lane == 0) scale[sv.slot0 + j] = sc;
 #pragma unroll
     for (int p = 0; p < PASSES; p++) {
         const int t = j * kBlk + p * RPP + r0;
@@ -156,7 +149,7 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __res
             }
             w[e / 4] |= uint32_t(code & 0xff) << (8 * (e % 4));
         }
-        int8_t* dst = xq + (bh * npad + j * kBlk + p * RPP + r0) * DP + c0;
+        int8_t* dst = xq + (sv.row0 + j * kBlk + p * RPP + r0) * DP + c0;
         *(uint2*)dst = make_uint2(w[0], w[1]);
     }
 }
@@ -169,17 +162,22 @@ __global__ void fill_zero_kernel(uint32_t* __restrict__ p, int n) {
     if (i < n) p[i] = 0u;
 }
 
-// FP8 pass 1: per-channel amax over all tokens.  grid (ceil(N/256), H, B), 256 threads;
-// thread covers 8 channels of every (256 / CH)-th token of its 256-token slab.  The
-// non-negative float maxima are combined with an integer atomic max on their bits.
+// FP8 pass 1: per-channel amax over all tokens of a sequence.  grid (ceil(max N/256),
+// H, B), 256 threads; thread covers 8 channels of every (256 / CH)-th token of its
+// 256-token slab.  The non-negative float maxima are combined with an integer atomic
+// max on their bits.
 template <bool BF16, int DP, bool VEC8>
-__global__ __launch_bounds__(256) void v_amax_kernel(const uint16_t* __restrict__ v, Strides st, int N, int D,
+__global__ __launch_bounds__(256) void v_amax_kernel(const uint16_t* __restrict__ v, SeqMap sm, int D,
                                                      uint32_t* __restrict__ amax_bits) {
     constexpr int CH = DP / 8, RSTEP = 256 / CH;
     __shared__ float red[RSTEP][DP];
     const int h = blockIdx.y, b = blockIdx.z;
+    const SeqView sv = seq_view(sm, b, h);
+    if (int(blockIdx.x) * 256 >= sv.n) return;  // the whole workgroup
+    const int N = sv.n;
+    const Strides st = sm.st;
     const int ch = threadIdx.x % CH, r0 = threadIdx.x / CH, c0 = ch * 8;
-    const uint16_t* base = v + b * st.b + h * st.h;
+    const uint16_t* base = v + sv.in_off;
     float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     const int t_end = min(N, int(blockIdx.x + 1) * 256);
     if (c0 < D) {
@@ -202,7 +200,7 @@ __global__ __launch_bounds__(256) void v_amax_kernel(const uint16_t* __restrict_
     for (int c = threadIdx.x; c < D; c += 256) {
         float mx = 0.0f;
         for (int r = 0; r < RSTEP; r++) mx = fmaxf(mx, red[r][c]);
-        atomicMax(amax_bits + (int64_t(b) * gridDim.y + h) * DP + c, __float_as_uint(mx));
+        atomicMax(amax_bits + (int64_t(b) * sm.H + h) * DP + c, __float_as_uint(mx));
     }
 }
 
@@ -216,8 +214,8 @@ __global__ __launch_bounds__(256) void v_amax_kernel(const uint16_t* __restrict_
 //   FP8:  v^ = e4m3(clamp(fp32(v * inv[c]), +-448)), inv = fp32(448 / amax[c]);
 //         the block-0 workgroup also writes v_scale[c] = fp32(amax[c] / 448).
 template <bool BF16, int DP, bool VEC8, bool FP8>
-__global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict__ v, Strides st, int N, int D,
-                                                      int NB, const uint32_t* __restrict__ amax_bits,
+__global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict__ v, SeqMap m, int D,
+                                                      const uint32_t* __restrict__ amax_bits,
                                                       void* __restrict__ vhat, float* __restrict__ vscale) {
     constexpr int ELT = FP8 ? 1 : 2;
     constexpr int CH = DP / 8;               // 8-channel chunks per token row
@@ -226,9 +224,13 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
     constexpr int RMASK = FP8 ? 3 : 1;
     __shared__ __attribute__((aligned(16))) uint8_t tile[DP * ROWB];
     const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int64_t bh = int64_t(b) * gridDim.y + h;
+    const SeqView sv = seq_view(m, b, h);
+    if (j * kBlk >= sv.n) return;  // the whole workgroup: past this sequence's end
+    const int N = sv.n;
+    const Strides st = m.st;
+    const int64_t bh = int64_t(b) * m.H + h;
     const int q = threadIdx.x % (kBlk / 4), ch = threadIdx.x / (kBlk / 4), c0 = ch * 8;
-    const uint16_t* base = v + b * st.b + h * st.h;
+    const uint16_t* base = v + sv.in_off;
 
     float inv[8];
     if constexpr (FP8) {
@@ -277,7 +279,7 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
     }
     __syncthreads();
     constexpr int CPR = ROWB / 16;  // 16-byte chunks per row
-    uint8_t* dst = (uint8_t*)vhat + (bh * NB + j) * int64_t(DP * ROWB);
+    uint8_t* dst = (uint8_t*)vhat + (sv.slot0 + j) * int64_t(DP * ROWB);
     for (int i = threadIdx.x; i < DP * CPR; i += THREADS) {
         const int pr = i / CPR, k = i % CPR;
         const int c = pr ^ ((pr >> 3) & RMASK);
@@ -290,36 +292,33 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
 namespace {
 template <bool BF16, int DP, bool VEC8>
 hipError_t launch_qk_t(const QuantQKArgs& a, hipStream_t s) {
-    const Strides sq = make_strides(a.layout_nhd, a.Hq, a.Nq, a.D);
-    const Strides sk = make_strides(a.layout_nhd, a.Hkv, a.Nkv, a.D);
-    const int nbq = (a.Nq + kBlk - 1) / kBlk, nbk = (a.Nkv + kBlk - 1) / kBlk;
-    k_mean_partial_kernel<BF16, DP, VEC8><<<dim3(nbk, a.Hkv, a.B), 256, 0, s>>>((const uint16_t*)a.k, sk, a.Nkv,
-                                                                                a.D, nbk, (double*)a.workspace);
+    const SeqMap mq = make_seq_map(a.layout_nhd, a.cu_q, a.B, a.Hq, a.Nq, a.total_q, a.D);
+    const SeqMap mk = make_seq_map(a.layout_nhd, a.cu_k, a.B, a.Hkv, a.Nkv, a.total_k, a.D);
+    k_mean_partial_kernel<BF16, DP, VEC8><<<dim3(mk.NB, a.Hkv, a.B), 256, 0, s>>>((const uint16_t*)a.k, mk, a.D,
+                                                                                (double*)a.workspace);
     const int tot = a.B * a.Hkv * a.D;
-    k_mean_final_kernel<<<(tot + 63) / 64, 64, 0, s>>>((const double*)a.workspace, tot, nbk, a.D, a.Nkv, a.k_mean);
-    const int64_t qblocks = int64_t(a.B) * a.Hq * nbq, kblocks = int64_t(a.B) * a.Hkv * nbk;
-    quant_blocks_kernel<BF16, DP, VEC8><<<unsigned((qblocks + 3) / 4), 256, 0, s>>>(
-        (const uint16_t*)a.q, sq, a.B, a.Hq, a.Nq, a.D, nbq, nullptr, a.q_i8, a.q_scale);
-    quant_blocks_kernel<BF16, DP, VEC8><<<unsigned((kblocks + 3) / 4), 256, 0, s>>>(
-        (const uint16_t*)a.k, sk, a.B, a.Hkv, a.Nkv, a.D, nbk, a.k_mean, a.k_i8, a.k_scale);
+    k_mean_final_kernel<<<(tot + 63) / 64, 64, 0, s>>>((const double*)a.workspace, mk, tot, a.D, a.k_mean);
+    quant_blocks_kernel<BF16, DP, VEC8><<<dim3((mq.NB + 3) / 4, a.Hq, a.B), 256, 0, s>>>(
+        (const uint16_t*)a.q, mq, a.D, nullptr, a.q_i8, a.q_scale);
+    quant_blocks_kernel<BF16, DP, VEC8><<<dim3((mk.NB + 3) / 4, a.Hkv, a.B), 256, 0, s>>>(
+        (const uint16_t*)a.k, mk, a.D, a.k_mean, a.k_i8, a.k_scale);
     return hipGetLastError();
 }
 
 template <bool BF16, int DP, bool VEC8>
 hipError_t launch_v_t(const QuantVArgs& a, hipStream_t s) {
-    const Strides sv = make_strides(a.layout_nhd, a.Hkv, a.Nkv, a.D);
-    const int nb = (a.Nkv + kBlk - 1) / kBlk;
+    const SeqMap mv = make_seq_map(a.layout_nhd, a.cu_k, a.B, a.Hkv, a.Nkv, a.total_k, a.D);
     if (a.fp8) {
         const int n = a.B * a.Hkv * DP;
         uint32_t* amax = (uint32_t*)a.workspace;
         fill_zero_kernel<<<(n + 255) / 256, 256, 0, s>>>(amax, n);
-        v_amax_kernel<BF16, DP, VEC8><<<dim3((a.Nkv + 255) / 256, a.Hkv, a.B), 256, 0, s>>>(
-            (const uint16_t*)a.v, sv, a.Nkv, a.D, amax);
-        quant_v_kernel<BF16, DP, VEC8, true><<<dim3(nb, a.Hkv, a.B), DP * 2, 0, s>>>(
-            (const uint16_t*)a.v, sv, a.Nkv, a.D, nb, amax, a.v_hat, a.v_scale);
+        v_amax_kernel<BF16, DP, VEC8><<<dim3((mv.N + 255) / 256, a.Hkv, a.B), 256, 0, s>>>((const uint16_t*)a.v, mv,
+                                                                                         a.D, amax);
+        quant_v_kernel<BF16, DP, VEC8, true><<<dim3(mv.NB, a.Hkv, a.B), DP * 2, 0, s>>>(
+            (const uint16_t*)a.v, mv, a.D, amax, a.v_hat, a.v_scale);
     } else {
-        quant_v_kernel<BF16, DP, VEC8, false><<<dim3(nb, a.Hkv, a.B), DP * 2, 0, s>>>(
-            (const uint16_t*)a.v, sv, a.Nkv, a.D, nb, nullptr, a.v_hat, nullptr);
+        quant_v_kernel<BF16, DP, VEC8, false><<<dim3(mv.NB, a.Hkv, a.B), DP * 2, 0, s>>>(
+            (const uint16_t*)a.v, mv, a.D, nullptr, a.v_hat, nullptr);
     }
     return hipGetLastError();
 }

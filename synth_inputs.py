@@ -21,6 +21,7 @@ head dim 128, and a grouped-query case with an odd head dim.
 from __future__ import annotations
 
 import dataclasses
+import itertools
 from typing import List, Optional, Tuple
 
 import torch
@@ -98,3 +99,58 @@ def make_qkv(w: Workload, seed: Optional[int] = None) -> Tuple[torch.Tensor, tor
         k += off[None, :, None, :]
     dt = w.torch_dtype
     return (_to_layout(q.to(dt), w.layout), _to_layout(k.to(dt), w.layout), _to_layout(v.to(dt), w.layout))
+
+
+# ----------------------------------------------------------------------------- packed variable-length batches
+
+@dataclasses.dataclass(frozen=True)
+class VarlenWorkload:
+    """Sequences of different lengths packed along one token axis (sageattn_varlen)."""
+    name: str
+    lens_q: Tuple[int, ...]
+    lens_k: Tuple[int, ...]
+    Hq: int
+    Hkv: int
+    D: int
+    dtype: str = "bf16"
+    causal: bool = False
+    pv: str = "fp16"
+    accum: str = "fp32"
+    seed: int = 0
+    k_offset_sigma: Optional[float] = None
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float16
+
+    @property
+    def B(self) -> int:
+        return len(self.lens_q)
+
+    def ops(self) -> float:
+        """4 * H * sum_b(visible query-key pairs) * D."""
+        total = 0.0
+        for nq, nk in zip(self.lens_q, self.lens_k):
+            if self.causal:
+                off = nk - nq
+                total += sum(max(0, min(nk, i + off + 1)) for i in range(nq))
+            else:
+                total += nq * nk
+        return 4.0 * self.Hq * total * self.D
+
+
+def make_varlen(w: VarlenWorkload):
+    """CPU tensors q (total_q, Hq, D), k, v (total_k, Hkv, D) and int32 prefix sums
+    cu_q, cu_k: randn in fp32 from one seeded generator (q, k, v, then the key offset,
+    one per (head, channel), shared by every token), cast to the workload dtype."""
+    g = torch.Generator().manual_seed(w.seed)
+    tq, tk = sum(w.lens_q), sum(w.lens_k)
+    q = torch.randn(tq, w.Hq, w.D, generator=g, dtype=torch.float32)
+    k = torch.randn(tk, w.Hkv, w.D, generator=g, dtype=torch.float32)
+    v = torch.randn(tk, w.Hkv, w.D, generator=g, dtype=torch.float32)
+    if w.k_offset_sigma is not None:
+        k += torch.randn(w.Hkv, w.D, generator=g, dtype=torch.float32)[None] * w.k_offset_sigma
+    cu_q = torch.tensor([0] + list(itertools.accumulate(w.lens_q)), dtype=torch.int32)
+    cu_k = torch.tensor([0] + list(itertools.accumulate(w.lens_k)), dtype=torch.int32)
+    dt = w.torch_dtype
+    return q.to(dt), k.to(dt), v.to(dt), cu_q, cu_k

@@ -112,16 +112,14 @@ def metrics(a: np.ndarray, b: np.ndarray) -> Dict[str, float]:
     }
 
 
-def check_output(case: Case, out: torch.Tensor, rows: np.ndarray, causal: Optional[bool] = None,
-                 exact: bool = True) -> Dict[str, Dict[str, float]]:
-    w = case.w
-    c = w.causal if causal is None else causal
-    got = gather_rows(out, rows, w.layout)
+def compare_rows(got: np.ndarray, em_raw: np.ndarray, amb: np.ndarray, ex: Optional[np.ndarray], fmt: int,
+                 pv: str) -> Dict[str, Dict[str, float]]:
+    """The output acceptance test on gathered rows [R, D]: against the emulation,
+    max-abs <= 1e-2 (one output ulp where that is wider) plus the ambiguity allowance
+    and cosine >= 0.9999; against exact attention (if given) cosine >= 0.999 and
+    relative L1 <= 3e-2 (FP16 P.V) / 5e-2 (FP8 P.V)."""
     assert np.isfinite(got).all()
-    note(f"[oracle] emulate {len(rows)} rows")
-    fmt = oracle.BF16 if w.dtype == "bf16" else oracle.FP16
     # the emulation's output is its fp64 result rounded to the output dtype
-    em_raw, amb = oracle.attn_emulate(case.oq, c, sm_scale_of(w.D), rows, with_ambiguity=True)
     em = oracle.round_to(em_raw, fmt)
     res = {"emulate": metrics(got, em)}
     res["emulate"]["ambiguity_max"] = float(amb.max())
@@ -131,14 +129,28 @@ def check_output(case: Case, out: torch.Tensor, rows: np.ndarray, causal: Option
     ulp = np.ldexp(1.0, np.floor(np.log2(np.maximum(np.abs(em), 1e-30))).astype(int) - (7 if fmt == oracle.BF16 else 10))
     res["emulate"]["worst_excess"] = float((np.abs(got - em) - np.maximum(1e-2, ulp) - amb).max())
     assert res["emulate"]["worst_excess"] <= 0 and res["emulate"]["cos"] >= 0.9999, res
-    if exact:
-        note(f"[oracle] exact {len(rows)} rows")
-        ex = oracle.attn_exact(case.qf, case.kf, case.vf, c, sm_scale_of(w.D), rows)
+    if ex is not None:
         res["exact"] = metrics(got, ex)
-        bound = FP8_REL_L1 if w.pv == "fp8" else FP16_REL_L1
+        bound = FP8_REL_L1 if pv == "fp8" else FP16_REL_L1
         assert res["exact"]["cos"] >= 0.999 and res["exact"]["rel_l1"] <= bound, res
     note(f"[metrics] {res}")
     return res
+
+
+def check_output(case: Case, out: torch.Tensor, rows: np.ndarray, causal: Optional[bool] = None,
+                 exact: bool = True) -> Dict[str, Dict[str, float]]:
+    w = case.w
+    c = w.causal if causal is None else causal
+    got = gather_rows(out, rows, w.layout)
+    assert np.isfinite(got).all()
+    note(f"[oracle] emulate {len(rows)} rows")
+    fmt = oracle.BF16 if w.dtype == "bf16" else oracle.FP16
+    em_raw, amb = oracle.attn_emulate(case.oq, c, sm_scale_of(w.D), rows, with_ambiguity=True)
+    ex = None
+    if exact:
+        note(f"[oracle] exact {len(rows)} rows")
+        ex = oracle.attn_exact(case.qf, case.kf, case.vf, c, sm_scale_of(w.D), rows)
+    return compare_rows(got, em_raw, amb, ex, fmt, w.pv)
 
 
 def tile_sample(w: si.Workload, per_head_random: int = 8, heads: int = 4, seed: int = 0) -> np.ndarray:

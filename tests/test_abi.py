@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_strings():
     L = qa.lib()
-    assert L.sage_abi_version() == 1
+    assert L.sage_abi_version() == 2
     for s in range(6):
         assert L.sage_status_string(s).decode().startswith("SAGE_")
     assert qa.padded_dim(1) == 64 and qa.padded_dim(64) == 64 and qa.padded_dim(65) == 128
@@ -124,7 +124,6 @@ def test_quant_v_rejects(kw, code):
     ({"acc": 3}, qa.SAGE_ERR_INVALID_ARG),
     ({"causal": 2}, qa.SAGE_ERR_INVALID_ARG),
     ({"acc": qa.SAGE_ACC_FP16}, qa.SAGE_ERR_UNSUPPORTED),
-    ({"causal": 1, "Nkv": 256}, qa.SAGE_ERR_UNSUPPORTED),
     ({"v_scale": None}, qa.SAGE_ERR_INVALID_ARG),
     ({"Hq": 32, "Hkv": 6}, qa.SAGE_ERR_INVALID_ARG),
     ({"out": FAKE + 2}, qa.SAGE_ERR_INVALID_ARG),
@@ -149,6 +148,10 @@ def test_valid_arguments_reach_the_device_check_only():
     assert _qk() == qa.SAGE_ERR_DEVICE
     assert _attn() == qa.SAGE_ERR_DEVICE
     assert _v() == qa.SAGE_ERR_DEVICE
+    assert _attn(causal=1, Nkv=256) == qa.SAGE_ERR_DEVICE  # causal with Nq != Nkv is accepted
+    assert _qkv() == qa.SAGE_ERR_DEVICE
+    assert _vv() == qa.SAGE_ERR_DEVICE
+    assert _attnv() == qa.SAGE_ERR_DEVICE
 
 
 def test_python_layer_rejects_fp32_and_cpu_tensors():
@@ -158,3 +161,90 @@ def test_python_layer_rejects_fp32_and_cpu_tensors():
     h = x.half()
     with pytest.raises(ValueError, match="GPU"):
         qa.sageattn(h, h, h)
+
+
+# ----------------------------------------------------------------------------- packed (varlen) batches
+
+def test_varlen_sizes():
+    L = qa.lib()
+    assert L.sage_varlen_rows(1000, 3) == 1000 + 192
+    assert L.sage_varlen_slots(1000, 3) == (1192 + 63) // 64
+    assert L.sage_varlen_rows(0, 3) == 0 and L.sage_varlen_slots(10, 0) == 0
+    assert L.sage_quant_qk_varlen_workspace_bytes(3, 2, 1000, 96) == 2 * ((1192 + 63) // 64) * 96 * 8
+    assert L.sage_quant_qk_varlen_workspace_bytes(3, 2, 1000, 129) == 0
+
+
+def _qkv(**kw):
+    a = dict(q=FAKE, k=FAKE, dtype=0, cuq=FAKE, cuk=FAKE, B=3, Hq=2, Hkv=2, tq=300, tk=400, mq=200, mk=200, D=64,
+             q_i8=FAKE, q_scale=FAKE, k_i8=FAKE, k_scale=FAKE, k_mean=FAKE, ws=FAKE, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return qa.lib().sage_quant_qk_varlen(a["q"], a["k"], a["dtype"], a["cuq"], a["cuk"], a["B"], a["Hq"], a["Hkv"],
+                                         a["tq"], a["tk"], a["mq"], a["mk"], a["D"], a["q_i8"], a["q_scale"],
+                                         a["k_i8"], a["k_scale"], a["k_mean"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def _vv(**kw):
+    a = dict(v=FAKE, dtype=1, cuk=FAKE, B=3, Hkv=2, tk=400, mk=200, D=128, pv=1, v_hat=FAKE, v_scale=FAKE, ws=FAKE,
+             ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return qa.lib().sage_quant_v_varlen(a["v"], a["dtype"], a["cuk"], a["B"], a["Hkv"], a["tk"], a["mk"], a["D"],
+                                        a["pv"], a["v_hat"], a["v_scale"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def _attnv(**kw):
+    a = dict(q_i8=FAKE, q_scale=FAKE, k_i8=FAKE, k_scale=FAKE, v_hat=FAKE, v_scale=FAKE, out=FAKE, odt=1, cuq=FAKE,
+             cuk=FAKE, B=3, Hq=4, Hkv=2, tq=300, tk=400, mq=200, mk=200, D=128, causal=1, sm=0.1, pv=1, acc=0,
+             stream=None)
+    a.update(kw)
+    return qa.lib().sage_attn_fwd_varlen(a["q_i8"], a["q_scale"], a["k_i8"], a["k_scale"], a["v_hat"], a["v_scale"],
+                                         a["out"], a["odt"], a["cuq"], a["cuk"], a["B"], a["Hq"], a["Hkv"], a["tq"],
+                                         a["tk"], a["mq"], a["mk"], a["D"], a["causal"], a["sm"], a["pv"], a["acc"],
+                                         a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"cuq": None}, qa.SAGE_ERR_INVALID_ARG),
+    ({"cuk": FAKE + 2}, qa.SAGE_ERR_INVALID_ARG),
+    ({"tq": 0}, qa.SAGE_ERR_INVALID_ARG),
+    ({"mk": 0}, qa.SAGE_ERR_INVALID_ARG),
+    ({"B": 0}, qa.SAGE_ERR_INVALID_ARG),
+    ({"Hq": 3}, qa.SAGE_ERR_INVALID_ARG),
+    ({"D": 160}, qa.SAGE_ERR_UNSUPPORTED),
+    ({"tq": 2 ** 31 - 100}, qa.SAGE_ERR_UNSUPPORTED),
+    ({"ws_bytes": 16}, qa.SAGE_ERR_WORKSPACE),
+    ({"q_i8": FAKE + 4}, qa.SAGE_ERR_INVALID_ARG),
+])
+def test_quant_qk_varlen_rejects(kw, code):
+    assert _qkv(**kw) == code
+    assert _detail()
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"cuk": None}, qa.SAGE_ERR_INVALID_ARG),
+    ({"pv": 3}, qa.SAGE_ERR_INVALID_ARG),
+    ({"v_scale": None}, qa.SAGE_ERR_INVALID_ARG),
+    ({"ws": None}, qa.SAGE_ERR_WORKSPACE),
+    ({"tk": -1}, qa.SAGE_ERR_INVALID_ARG),
+])
+def test_quant_v_varlen_rejects(kw, code):
+    assert _vv(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"cuq": None}, qa.SAGE_ERR_INVALID_ARG),
+    ({"out": None}, qa.SAGE_ERR_INVALID_ARG),
+    ({"sm": float("nan")}, qa.SAGE_ERR_INVALID_ARG),
+    ({"acc": qa.SAGE_ACC_FP16}, qa.SAGE_ERR_UNSUPPORTED),
+    ({"Hq": 5}, qa.SAGE_ERR_INVALID_ARG),
+    ({"mq": -3}, qa.SAGE_ERR_INVALID_ARG),
+])
+def test_attn_fwd_varlen_rejects(kw, code):
+    assert _attnv(**kw) == code
+    assert _detail()
+
+
+def test_python_varlen_layer_rejects_bad_shapes():
+    x = torch.zeros(2, 1, 64, 64, dtype=torch.float16)
+    cu = torch.tensor([0, 64], dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        qa.sageattn_varlen(x, x, x, cu, cu, 64, 64)

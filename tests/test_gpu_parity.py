@@ -85,6 +85,11 @@ OUT_CASES = [
     ("d100_fp8", W("seq_sweep", B=1, Hq=2, Hkv=2, Nq=300, Nkv=300, D=100, seed=14), "all"),
     ("one_key", W("tiny", Nq=130, Nkv=1, seed=16), "all"),
     ("one_query", W("llm_prefill", Nq=1, Nkv=500, seed=17), "all"),
+    # causal with Nq != Nkv: the diagonal aligned to the bottom-right corner
+    ("causal_nq_lt_nkv_fp8", W("seq_sweep", B=2, Hq=4, Hkv=2, Nq=130, Nkv=333, causal=True, seed=18), "all"),
+    ("causal_nq_gt_nkv_fp16", W("llm_prefill", Hq=4, Hkv=2, Nq=300, Nkv=100, causal=True, seed=19), "all"),
+    ("causal_decode_d64_fp8", W("video_dit", Hq=2, Hkv=2, Nq=1, Nkv=1000, causal=True, seed=20), "all"),
+    ("causal_chunk_d96", W("gqa", B=1, Nq=200, Nkv=1500, D=96, causal=True, seed=21), "all"),
 ]
 
 

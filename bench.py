@@ -40,8 +40,9 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    # defaults sized past the ~100 ms over which the shader clock ramps up under load
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--n", type=int, default=8192, help="sequence length of the headline point")
     p.add_argument("--causal", action="store_true", help="headline point causal")
     p.add_argument("--no-sweep", action="store_true")
@@ -242,11 +243,63 @@ def main():
                 torch.cuda.empty_cache()
         result["sweep"] = sweep
 
+    # ---------------------------------------------------------------- packed variable-length batch
+    if not args.no_sweep:
+        result["varlen"] = varlen_point(qa, torch, np, si, dev, args.sweep_steps)
+
     # ---------------------------------------------------------------- CPU baseline (the oracle, untuned)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, full, np, torch)
 
     print(json.dumps(result), flush=True)
+
+
+def varlen_point(qa, torch, np, si, dev, steps):
+    """sageattn_varlen on a packed batch: 16 causal prefill sequences of seeded mixed
+    lengths (256 .. 8192 tokens), GQA 32/8, D=128, bf16, INT8 QK + FP16 P.V (the
+    README's varlen kernel).  Inputs drawn on the GPU."""
+    rng = np.random.default_rng(41)
+    lens = tuple(int(x) for x in rng.integers(256, 8193, size=16))
+    w = si.VarlenWorkload("varlen_prefill", lens, lens, 32, 8, 128, causal=True, pv="fp16", seed=41)
+    g = torch.Generator(device=dev).manual_seed(w.seed)
+    tq = sum(lens)
+    q = torch.randn(tq, w.Hq, w.D, generator=g, device=dev).to(torch.bfloat16)
+    k = torch.randn(tq, w.Hkv, w.D, generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn(tq, w.Hkv, w.D, generator=g, device=dev).to(torch.bfloat16)
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device=dev)
+    mx = max(lens)
+    qk = qa.quant_qk_varlen(q, k, cu, cu, mx, mx)
+    vq = qa.quant_v_varlen(v, cu, mx, w.pv)
+    out = qa.attn_fwd_varlen(qk, vq, torch.bfloat16, True)
+
+    def quant():
+        qa.quant_qk_varlen(q, k, cu, cu, mx, mx, out=qk)
+        qa.quant_v_varlen(v, cu, mx, w.pv, out=vq)
+
+    def attn():
+        qa.attn_fwd_varlen(qk, vq, torch.bfloat16, True, out=out)
+
+    for _ in range(3):
+        quant()
+        attn()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for a, b, c in ev:
+        a.record()
+        quant()
+        b.record()
+        attn()
+        c.record()
+    torch.cuda.synchronize()
+    at = sum(b.elapsed_time(c) for a, b, c in ev) / steps
+    st = sum(a.elapsed_time(c) for a, b, c in ev) / steps
+    ops = w.ops()
+    res = {"workload": f"{w.name}: 16 causal sequences, {tq} tokens (lengths {min(lens)}..{max(lens)}), "
+                       f"H{w.Hq}/{w.Hkv} D{w.D} bf16 INT8-QK FP16-PV",
+           "attn_tops": round(ops / (at * 1e-3) / 1e12, 1), "attn_ms": round(at, 4),
+           "step_tops": round(ops / (st * 1e-3) / 1e12, 1), "step_ms": round(st, 4)}
+    log(f"[bench] varlen: attn {at:.3f} ms = {res['attn_tops']} TOPS, step {res['step_tops']} TOPS")
+    return res
 
 
 def cpu_baseline(w, full, np, torch):

@@ -238,6 +238,7 @@ struct PPack<false> {
 template <bool FP8, bool MASK, bool CAUSAL>
 __device__ __forceinline__ float softmax_tile(v16i (&S)[2], PPack<FP8>& pk, float c, float& m, float& l, int g,
                                               int key0, int kmax, int Nkv) {
+    int tvis = 0;  // MASK: register r of tile kt is visible iff key_of_reg(kt, 0, r) < tvis
     if constexpr (MASK) {
         // key key0 + key_of_reg(kt, g, r) is visible iff it is below min(Nkv, kmax + 1)
         // (causal) or Nkv; key_of_reg(kt, g, r) = key_of_reg(kt, 0, r) + (32 | 8) * g,
@@ -253,6 +254,7 @@ __device__ __forceinline__ float softmax_tile(v16i (&S)[2], PPack<FP8>& pk, floa
 #pragma unroll
             for (int r = 0; r < 16; r++)
                 if (!(key_of_reg<FP8>(kt, 0, r) < t)) S[kt][r] = INT32_MIN;
+        tvis = t;
     }
     // row max: two chains of three-input maxima (v_max3), one per score tile
     int mxk[2];
@@ -278,7 +280,8 @@ __device__ __forceinline__ float softmax_tile(v16i (&S)[2], PPack<FP8>& pk, floa
 #pragma unroll
         for (int e = 0; e < 4; e++) {
             q[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(float(S[kt][r0 + e]), c, negm));
-            if constexpr (MASK) q[e] = S[kt][r0 + e] == INT32_MIN ? 0.0f : q[e];
+            // the same predicate as above (compiled to a scalar-mask select, not VCC)
+            if constexpr (MASK) q[e] = key_of_reg<FP8>(kt, 0, r0 + e) < tvis ? q[e] : 0.0f;
             acc[e] = w == 0 ? q[e] : acc[e] + q[e];
         }
         if constexpr (FP8) {
@@ -433,6 +436,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
         if (j + AHEAD < jend) issue_tile(j + AHEAD);
         const float c = sq * ks_next * p.cscale;
         ks_next = scalar_load_f32(ks_row + min(j + 1, NBk - 1));
+        // a tile no query of this wave may see (causal: beyond the wave's last query's
+        // horizon) leaves m, l and O unchanged: take part in the pipeline only
+        if constexpr (MASK && CAUSAL)
+            if (j * kBlk > q0 + C::QW - 1 + off) return;
         // stage base as one wave-uniform value, so each LDS address costs a single add
         const uint8_t* st = smem + __builtin_amdgcn_readfirstlane((j % C::NST) * C::STAGE);
         v16i S[2];

@@ -18,7 +18,7 @@
  * (batch, seq, heads, dim), is_causal, sm_scale (SDPA semantics, default
  * 1/sqrt(head_dim) -- qwbw.cn one-line integration article), grouped-query
  * attention with num_qo_heads a multiple of num_kv_heads (same article), and head
- * dims other than 64/128 zero-padded (same article, pad_qkv paragraph).
+ * dims other than 64/128/256 zero-padded (same article, pad_qkv paragraph).
  *
  * Conventions for every call:
  *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
@@ -29,7 +29,7 @@
  *  - Arguments are validated before any HIP call: on error nothing is written and
  *    no kernel is launched; sage_last_error_detail() explains the failure.
  *  - Shapes: B batch, H_qo query heads, H_kv kv heads, Nq / Nkv sequence lengths,
- *    D true head dim (1..128).  Dp = 64 if D <= 64 else 128 (the padded head dim),
+ *    D true head dim (1..256).  Dp = 64, 128 or 256: the smallest of them >= D,
  *    NB(N) = ceil(N / 64), N_pad(N) = 64 * NB(N).  Query head h reads kv head
  *    h / (H_qo / H_kv).
  *  - Every padding element of an output buffer (tokens >= N, channels >= D) is
@@ -60,7 +60,7 @@ extern "C" {
 typedef enum sage_status {
     SAGE_OK = 0,
     SAGE_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad enum, H_qo % H_kv != 0, bad sm_scale */
-    SAGE_ERR_UNSUPPORTED = 2, /* D > 128, SAGE_ACC_FP16, causal with Nq != Nkv, size overflow */
+    SAGE_ERR_UNSUPPORTED = 2, /* D > 256, SAGE_ACC_FP16, size overflow */
     SAGE_ERR_WORKSPACE = 3,   /* workspace pointer NULL or smaller than required */
     SAGE_ERR_DEVICE = 4,      /* no HIP device, or the current device is not gfx950 */
     SAGE_ERR_HIP = 5          /* a kernel launch failed (hipGetLastError) */
@@ -80,7 +80,7 @@ const char* sage_status_string(sage_status s);
 /* Thread-local text describing the last failure of a call made on this thread. */
 const char* sage_last_error_detail(void);
 
-/* Dp for a head dim (64 or 128), 0 when D is outside 1..128. */
+/* Dp for a head dim (64, 128 or 256), 0 when D is outside 1..256. */
 int sage_padded_dim(int D);
 /* NB(N) = ceil(N / 64). */
 int sage_num_blocks(int N);

@@ -71,7 +71,7 @@ sage_status check_shape(int B, int Hq, int Hkv, int Nq, int Nkv, int D) {
                     Hkv, Nq, Nkv, D);
     if (Hq % Hkv != 0)
         return fail(SAGE_ERR_INVALID_ARG, "num_qo_heads (%d) must be a multiple of num_kv_heads (%d)", Hq, Hkv);
-    if (D > 128) return fail(SAGE_ERR_UNSUPPORTED, "head_dim %d > 128 is not supported", D);
+    if (D > 256) return fail(SAGE_ERR_UNSUPPORTED, "head_dim %d > 256 is not supported", D);
     if (Nq > kMaxN || Nkv > kMaxN) return fail(SAGE_ERR_UNSUPPORTED, "sequence length above %d", kMaxN);
     if (B > kMaxGridYZ || Hq > kMaxGridYZ) return fail(SAGE_ERR_UNSUPPORTED, "batch or head count above %d", kMaxGridYZ);
     const double elems = double(B) * Hq * double(Nq > Nkv ? Nq : Nkv) * 128.0;
@@ -79,7 +79,7 @@ sage_status check_shape(int B, int Hq, int Hkv, int Nq, int Nkv, int D) {
     return SAGE_OK;
 }
 
-int padded_dim(int D) { return D <= 0 || D > 128 ? 0 : (D <= 64 ? 64 : 128); }
+int padded_dim(int D) { return D <= 0 || D > 256 ? 0 : (D <= 64 ? 64 : (D <= 128 ? 128 : 256)); }
 int nblocks(int N) { return N <= 0 ? 0 : (N + 63) / 64; }
 
 // Packed (variable-length) batches: rows and block slots per head.
@@ -150,12 +150,12 @@ int sage_padded_dim(int D) { return padded_dim(D); }
 int sage_num_blocks(int N) { return nblocks(N); }
 
 size_t sage_quant_qk_workspace_bytes(int B, int H_kv, int Nkv, int D) {
-    if (B <= 0 || H_kv <= 0 || Nkv <= 0 || D <= 0 || D > 128) return 0;
+    if (B <= 0 || H_kv <= 0 || Nkv <= 0 || D <= 0 || D > 256) return 0;
     return size_t(B) * size_t(H_kv) * size_t(nblocks(Nkv)) * size_t(D) * sizeof(double);
 }
 
 size_t sage_quant_v_workspace_bytes(int B, int H_kv, int D, sage_pv pv) {
-    if (B <= 0 || H_kv <= 0 || D <= 0 || D > 128) return 0;
+    if (B <= 0 || H_kv <= 0 || D <= 0 || D > 256) return 0;
     if (pv != SAGE_PV_FP8) return 0;
     return size_t(B) * size_t(H_kv) * size_t(padded_dim(D)) * sizeof(uint32_t);
 }
@@ -263,7 +263,7 @@ int64_t sage_varlen_rows(int total, int B) { return total <= 0 || B <= 0 ? 0 : v
 int64_t sage_varlen_slots(int total, int B) { return total <= 0 || B <= 0 ? 0 : varlen_slots(total, B); }
 
 size_t sage_quant_qk_varlen_workspace_bytes(int B, int H_kv, int total_kv, int D) {
-    if (B <= 0 || H_kv <= 0 || total_kv <= 0 || D <= 0 || D > 128) return 0;
+    if (B <= 0 || H_kv <= 0 || total_kv <= 0 || D <= 0 || D > 256) return 0;
     return size_t(H_kv) * size_t(varlen_slots(total_kv, B)) * size_t(D) * sizeof(double);
 }
 

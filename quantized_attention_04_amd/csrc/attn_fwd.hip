@@ -66,7 +66,7 @@ __device__ __forceinline__ void block_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Mode constants.  DP = padded head dim (64 | 128); FP8 = P.V in e4m3 (else fp16).
+// Mode constants.  DP = padded head dim (64 | 128 | 256); FP8 = P.V in e4m3 (else fp16).
 template <int DP, bool FP8>
 struct Cfg {
     static constexpr int WAVES = 4;  // one wave per SIMD; two workgroups share a CU
@@ -90,7 +90,8 @@ struct Cfg {
     // waves share each SIMD.  The vector ALU is the binding unit -- the softmax costs
     // about twice the MFMA time -- and one wave can issue a vector instruction only
     // every other slot, so the ALU needs several ready waves per SIMD to stay busy.
-    static constexpr int OCC = DP == 64 ? 4 : 3;  // waves per SIMD
+    // (head dim 256: 128 accumulator VGPRs alone, two waves)
+    static constexpr int OCC = DP == 64 ? 4 : (DP == 128 ? 3 : 2);  // waves per SIMD
     // LDS stages: three (two tiles stream in while one is used) when OCC workgroups of
     // three fit in the 160 KB of a CU, else two
     static constexpr int NST = OCC * 3 * STAGE <= 160 * 1024 ? 3 : 2;
@@ -109,7 +110,14 @@ struct Cfg {
 
 template <class C>
 __device__ __forceinline__ int kswz(int row) {
-    return parity(row & C::KM0) | (parity(row & C::KM1) << 1) | (parity(row & C::KM2) << 2);
+    if constexpr (C::KROW == 256) {
+        // 16 chunks per row and every row on the same banks: the 16 lanes served per
+        // LDS cycle read 16 different rows (bits 0-2 and 5 of the row for FP8's key
+        // order, bits 0-3 for FP16's), which this XOR maps onto 16 distinct chunks
+        return C::VELT == 1 ? ((row & 7) | (((row >> 5) & 1) << 3)) : (row & 15);
+    } else {
+        return parity(row & C::KM0) | (parity(row & C::KM1) << 1) | (parity(row & C::KM2) << 2);
+    }
 }
 template <class C>
 __device__ __forceinline__ int vswz(int row) {
@@ -580,7 +588,9 @@ hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s) {
     p.qm = make_seq_map(0, a.cu_q, a.B, a.Hq, a.Nq, a.total_q, a.D);
     p.km = make_seq_map(0, a.cu_k, a.B, a.Hkv, a.Nkv, a.total_k, a.D);
     constexpr int BM = Cfg<128, true>::BM;
-    static_assert(Cfg<64, false>::BM == BM && Cfg<64, true>::BM == BM && Cfg<128, false>::BM == BM, "uniform BM");
+    static_assert(Cfg<64, false>::BM == BM && Cfg<64, true>::BM == BM && Cfg<128, false>::BM == BM &&
+                      Cfg<256, true>::BM == BM && Cfg<256, false>::BM == BM,
+                  "uniform BM");
     p.QT = (a.Nq + BM - 1) / BM;
     p.cscale = a.sm_scale * kLog2e;
     if (a.cu_q != nullptr) {  // packed (total, H_qo, D)
@@ -598,13 +608,15 @@ hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s) {
     }
     const int nwg = a.B * a.Hq * p.QT;
     if (a.D <= 64) return a.fp8 ? dispatch_rest<64, true>(a, p, nwg, s) : dispatch_rest<64, false>(a, p, nwg, s);
-    return a.fp8 ? dispatch_rest<128, true>(a, p, nwg, s) : dispatch_rest<128, false>(a, p, nwg, s);
+    if (a.D <= 128) return a.fp8 ? dispatch_rest<128, true>(a, p, nwg, s) : dispatch_rest<128, false>(a, p, nwg, s);
+    return a.fp8 ? dispatch_rest<256, true>(a, p, nwg, s) : dispatch_rest<256, false>(a, p, nwg, s);
 }
 
 hipError_t launch_debug_qk(const DebugQKArgs& a, hipStream_t s) {
     const int NBq = (a.Nq + kBlk - 1) / kBlk, NBk = (a.Nkv + kBlk - 1) / kBlk;
     if (a.D <= 64) return a.fp8 ? launch_debug_t<64, true>(a, NBq, NBk, s) : launch_debug_t<64, false>(a, NBq, NBk, s);
-    return a.fp8 ? launch_debug_t<128, true>(a, NBq, NBk, s) : launch_debug_t<128, false>(a, NBq, NBk, s);
+    if (a.D <= 128) return a.fp8 ? launch_debug_t<128, true>(a, NBq, NBk, s) : launch_debug_t<128, false>(a, NBq, NBk, s);
+    return a.fp8 ? launch_debug_t<256, true>(a, NBq, NBk, s) : launch_debug_t<256, false>(a, NBq, NBk, s);
 }
 
 }  // namespace sage

@@ -214,7 +214,7 @@ __global__ __launch_bounds__(256) void v_amax_kernel(const uint16_t* __restrict_
 //   FP8:  v^ = e4m3(clamp(fp32(v * inv[c]), +-448)), inv = fp32(448 / amax[c]);
 //         the block-0 workgroup also writes v_scale[c] = fp32(amax[c] / 448).
 template <bool BF16, int DP, bool VEC8, bool FP8>
-__global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict__ v, SeqMap m, int D,
+__global__ __launch_bounds__(2 * DP) void quant_v_kernel(const uint16_t* __restrict__ v, SeqMap m, int D,
                                                       const uint32_t* __restrict__ amax_bits,
                                                       void* __restrict__ vhat, float* __restrict__ vscale) {
     constexpr int ELT = FP8 ? 1 : 2;
@@ -325,26 +325,28 @@ hipError_t launch_v_t(const QuantVArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_quant_qk(const QuantQKArgs& a, hipStream_t s) {
+template <bool BF16>
+hipError_t launch_qk_dp(const QuantQKArgs& a, hipStream_t s) {
     const bool vec = (a.D % 8) == 0;
-    const int dp = a.D <= 64 ? 64 : 128;
-    if (a.bf16) {
-        if (dp == 64) return vec ? launch_qk_t<true, 64, true>(a, s) : launch_qk_t<true, 64, false>(a, s);
-        return vec ? launch_qk_t<true, 128, true>(a, s) : launch_qk_t<true, 128, false>(a, s);
-    }
-    if (dp == 64) return vec ? launch_qk_t<false, 64, true>(a, s) : launch_qk_t<false, 64, false>(a, s);
-    return vec ? launch_qk_t<false, 128, true>(a, s) : launch_qk_t<false, 128, false>(a, s);
+    if (a.D <= 64) return vec ? launch_qk_t<BF16, 64, true>(a, s) : launch_qk_t<BF16, 64, false>(a, s);
+    if (a.D <= 128) return vec ? launch_qk_t<BF16, 128, true>(a, s) : launch_qk_t<BF16, 128, false>(a, s);
+    return vec ? launch_qk_t<BF16, 256, true>(a, s) : launch_qk_t<BF16, 256, false>(a, s);
+}
+
+hipError_t launch_quant_qk(const QuantQKArgs& a, hipStream_t s) {
+    return a.bf16 ? launch_qk_dp<true>(a, s) : launch_qk_dp<false>(a, s);
+}
+
+template <bool BF16>
+hipError_t launch_v_dp(const QuantVArgs& a, hipStream_t s) {
+    const bool vec = (a.D % 8) == 0;
+    if (a.D <= 64) return vec ? launch_v_t<BF16, 64, true>(a, s) : launch_v_t<BF16, 64, false>(a, s);
+    if (a.D <= 128) return vec ? launch_v_t<BF16, 128, true>(a, s) : launch_v_t<BF16, 128, false>(a, s);
+    return vec ? launch_v_t<BF16, 256, true>(a, s) : launch_v_t<BF16, 256, false>(a, s);
 }
 
 hipError_t launch_quant_v(const QuantVArgs& a, hipStream_t s) {
-    const bool vec = (a.D % 8) == 0;
-    const int dp = a.D <= 64 ? 64 : 128;
-    if (a.bf16) {
-        if (dp == 64) return vec ? launch_v_t<true, 64, true>(a, s) : launch_v_t<true, 64, false>(a, s);
-        return vec ? launch_v_t<true, 128, true>(a, s) : launch_v_t<true, 128, false>(a, s);
-    }
-    if (dp == 64) return vec ? launch_v_t<false, 64, true>(a, s) : launch_v_t<false, 64, false>(a, s);
-    return vec ? launch_v_t<false, 128, true>(a, s) : launch_v_t<false, 128, false>(a, s);
+    return a.bf16 ? launch_v_dp<true>(a, s) : launch_v_dp<false>(a, s);
 }
 
 }  // namespace sage

@@ -39,7 +39,8 @@ def test_abi_version_and_strings():
     for s in range(6):
         assert L.sage_status_string(s).decode().startswith("SAGE_")
     assert qa.padded_dim(1) == 64 and qa.padded_dim(64) == 64 and qa.padded_dim(65) == 128
-    assert qa.padded_dim(128) == 128 and qa.padded_dim(129) == 0 and qa.padded_dim(0) == 0
+    assert qa.padded_dim(128) == 128 and qa.padded_dim(129) == 256 and qa.padded_dim(256) == 256
+    assert qa.padded_dim(257) == 0 and qa.padded_dim(0) == 0
     assert qa.num_blocks(1) == 1 and qa.num_blocks(64) == 1 and qa.num_blocks(65) == 2 and qa.num_blocks(17776) == 278
 
 
@@ -47,7 +48,8 @@ def test_workspace_sizes():
     L = qa.lib()
     assert L.sage_quant_qk_workspace_bytes(2, 8, 8192, 128) == 2 * 8 * 128 * 128 * 8
     assert L.sage_quant_qk_workspace_bytes(1, 1, 100, 96) == 2 * 96 * 8
-    assert L.sage_quant_qk_workspace_bytes(1, 1, 100, 129) == 0
+    assert L.sage_quant_qk_workspace_bytes(1, 1, 100, 129) == 2 * 129 * 8
+    assert L.sage_quant_qk_workspace_bytes(1, 1, 100, 257) == 0
     assert L.sage_quant_v_workspace_bytes(2, 8, 96, qa.SAGE_PV_FP8) == 2 * 8 * 128 * 4
     assert L.sage_quant_v_workspace_bytes(2, 8, 96, qa.SAGE_PV_FP16) == 0
 
@@ -90,8 +92,8 @@ def _detail():
     ({"B": 0}, qa.SAGE_ERR_INVALID_ARG),
     ({"Nkv": -1}, qa.SAGE_ERR_INVALID_ARG),
     ({"Hq": 6, "Hkv": 4}, qa.SAGE_ERR_INVALID_ARG),
-    ({"D": 129}, qa.SAGE_ERR_UNSUPPORTED),
-    ({"D": 256}, qa.SAGE_ERR_UNSUPPORTED),
+    ({"D": 257}, qa.SAGE_ERR_UNSUPPORTED),
+    ({"D": 512}, qa.SAGE_ERR_UNSUPPORTED),
     ({"q": FAKE + 2}, qa.SAGE_ERR_INVALID_ARG),
     ({"ws": None}, qa.SAGE_ERR_WORKSPACE),
     ({"ws_bytes": 2 * 64 * 8 - 1}, qa.SAGE_ERR_WORKSPACE),
@@ -107,7 +109,7 @@ def test_quant_qk_rejects(kw, code):
     ({"v_scale": None}, qa.SAGE_ERR_INVALID_ARG),
     ({"ws": None}, qa.SAGE_ERR_WORKSPACE),
     ({"ws_bytes": 2 * 128 * 4 - 4}, qa.SAGE_ERR_WORKSPACE),
-    ({"D": 200}, qa.SAGE_ERR_UNSUPPORTED),
+    ({"D": 300}, qa.SAGE_ERR_UNSUPPORTED),
     ({"v_hat": FAKE + 8}, qa.SAGE_ERR_INVALID_ARG),
 ])
 def test_quant_v_rejects(kw, code):
@@ -171,7 +173,7 @@ def test_varlen_sizes():
     assert L.sage_varlen_slots(1000, 3) == (1192 + 63) // 64
     assert L.sage_varlen_rows(0, 3) == 0 and L.sage_varlen_slots(10, 0) == 0
     assert L.sage_quant_qk_varlen_workspace_bytes(3, 2, 1000, 96) == 2 * ((1192 + 63) // 64) * 96 * 8
-    assert L.sage_quant_qk_varlen_workspace_bytes(3, 2, 1000, 129) == 0
+    assert L.sage_quant_qk_varlen_workspace_bytes(3, 2, 1000, 257) == 0
 
 
 def _qkv(**kw):
@@ -209,7 +211,7 @@ def _attnv(**kw):
     ({"mk": 0}, qa.SAGE_ERR_INVALID_ARG),
     ({"B": 0}, qa.SAGE_ERR_INVALID_ARG),
     ({"Hq": 3}, qa.SAGE_ERR_INVALID_ARG),
-    ({"D": 160}, qa.SAGE_ERR_UNSUPPORTED),
+    ({"D": 260}, qa.SAGE_ERR_UNSUPPORTED),
     ({"tq": 2 ** 31 - 100}, qa.SAGE_ERR_UNSUPPORTED),
     ({"ws_bytes": 16}, qa.SAGE_ERR_WORKSPACE),
     ({"q_i8": FAKE + 4}, qa.SAGE_ERR_INVALID_ARG),

@@ -31,6 +31,8 @@ QUANT_CASES = [
     ("ragged_bf16_nhd_d72_fp8", W("video_dit", B=2, Hq=4, Hkv=2, Nq=70, Nkv=200, D=72, seed=12)),
     ("one_token_d8", W("tiny", Nq=1, Nkv=1, D=8, seed=13)),
     ("d100_fp8", W("seq_sweep", B=1, Hq=2, Hkv=2, Nq=300, Nkv=300, D=100, seed=14)),
+    ("d256_fp8", W("seq_sweep", B=1, Hq=4, Hkv=2, Nq=300, Nkv=300, D=256, seed=22)),
+    ("d200_fp16_nhd", W("gqa", B=1, Hq=4, Hkv=2, Nq=200, Nkv=250, D=200, seed=23)),
 ]
 
 
@@ -53,6 +55,8 @@ TILE_CASES = [
     ("video_dit_small", W("video_dit", Nq=1000, Nkv=1000, Hq=2, Hkv=2)),
     ("gqa_d96", W("gqa", Nq=700, Nkv=700, B=1)),
     ("ragged_d40", W("tiny", B=2, Hq=4, Hkv=2, Nq=100, Nkv=150, D=40, seed=11)),
+    ("d256", W("seq_sweep", B=1, Hq=2, Hkv=2, Nq=200, Nkv=200, D=256, seed=22)),
+    ("d200", W("gqa", B=1, Hq=4, Hkv=2, Nq=130, Nkv=190, D=200, seed=23)),
 ]
 
 
@@ -90,6 +94,11 @@ OUT_CASES = [
     ("causal_nq_gt_nkv_fp16", W("llm_prefill", Hq=4, Hkv=2, Nq=300, Nkv=100, causal=True, seed=19), "all"),
     ("causal_decode_d64_fp8", W("video_dit", Hq=2, Hkv=2, Nq=1, Nkv=1000, causal=True, seed=20), "all"),
     ("causal_chunk_d96", W("gqa", B=1, Nq=200, Nkv=1500, D=96, causal=True, seed=21), "all"),
+    # head dims above 128: Dp = 256
+    ("d256_fp8", W("seq_sweep", B=1, Hq=4, Hkv=2, Nq=300, Nkv=300, D=256, seed=22), "all"),
+    ("d256_causal_fp16", W("llm_prefill", Hq=2, Hkv=2, Nq=300, Nkv=300, D=256, causal=True, seed=24), "all"),
+    ("d200_gqa_nhd", W("gqa", B=1, Hq=8, Hkv=2, Nq=500, Nkv=500, D=200, seed=25), "all"),
+    ("d256_4k", W("seq_sweep", B=1, Hq=8, Hkv=8, Nq=4096, Nkv=4096, D=256, seed=26), 16),
 ]
 
 

@@ -25,6 +25,7 @@ CASES = [
     VW("q_ne_k_causal_d96", (10, 300, 64, 5), (100, 300, 30, 64), 4, 4, 96, dtype="fp16", causal=True, seed=32),
     VW("q_ne_k_fp8_d64_offset", (70, 3, 129), (200, 65, 129), 2, 1, 64, pv="fp8", seed=33, k_offset_sigma=2.0),
     VW("empty_sequences", (0, 50, 20, 7), (10, 0, 80, 7), 2, 2, 64, pv="fp8", causal=True, seed=34),
+    VW("d256_fp8_causal", (100, 300, 65), (100, 300, 130), 4, 2, 256, pv="fp8", causal=True, seed=37),
 ]
 
 

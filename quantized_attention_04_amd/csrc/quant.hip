@@ -78,7 +78,7 @@ __global__ __launch_bounds__(64) void k_mean_final_kernel(const double* __restri
 // p = 0 .. CH-1.
 //   y = x (Q) or fp32(x - mean[c]) (K); amax = max |y|; scale = amax / 127;
 //   inv = 127 / amax; code = clamp(rne(y * inv), -127, 127).
-template <bool BF16, int DP, bool VEC8>
+template <bool BF16, int DP, bool VEC8, bool SMOOTH>
 __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __restrict__ x, SeqMap m, int D,
                                                            const float* __restrict__ mean, int8_t* __restrict__ xq,
                                                            float* __restrict__ scale) {
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __res
 
     float mu[8];
 #pragma unroll
-    for (int e = 0; e < 8; e++) mu[e] = (mean != nullptr && c0 + e < D) ? mean[int64_t(bh) * D + c0 + e] : 0.0f;
+    for (int e = 0; e < 8; e++) mu[e] = (SMOOTH && c0 + e < D) ? mean[int64_t(bh) * D + c0 + e] : 0.0f;
 
     v8u16 raw[PASSES];
 #pragma unroll
@@ -116,16 +116,28 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __res
         }
         raw[p] = r;
     }
-    // amax over the block's real elements
+    // amax over the block's real elements (a full block of whole chunks needs no
+    // per-element test: channel padding holds y = 0)
+    const bool full = VEC8 && (j + 1) * kBlk <= N;
     float amax = 0.0f;
+    if (full) {
 #pragma unroll
-    for (int p = 0; p < PASSES; p++) {
-        const int t = j * kBlk + p * RPP + r0;
+        for (int p = 0; p < PASSES; p++)
 #pragma unroll
-        for (int e = 0; e < 8; e++) {
-            if (t < N && c0 + e < D) {
-                const float y = in_to_f32<BF16>(raw[p][e]) - mu[e];
+            for (int e = 0; e < 8; e++) {
+                const float y = SMOOTH ? in_to_f32<BF16>(raw[p][e]) - mu[e] : in_to_f32<BF16>(raw[p][e]);
                 amax = fmaxf(amax, fabsf(y));
+            }
+    } else {
+#pragma unroll
+        for (int p = 0; p < PASSES; p++) {
+            const int t = j * kBlk + p * RPP + r0;
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                if (t < N && c0 + e < D) {
+                    const float y = SMOOTH ? in_to_f32<BF16>(raw[p][e]) - mu[e] : in_to_f32<BF16>(raw[p][e]);
+                    amax = fmaxf(amax, fabsf(y));
+                }
             }
         }
     }
@@ -134,6 +146,33 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __res
     const float sc = zero ? 0.0f : amax / 127.0f;
     const float inv = zero ? 0.0f : 127.0f / amax;
     if (lane == 0) scale[sv.slot0 + j] = sc;
+    if (full && amax <= 3.4e38f && inv <= 3.4e38f) {
+        // Full block, whole 8-channel chunks, finite amax and inv (wave-uniform): every
+        // element of the tile is real, channel padding reads as x = 0 with mean 0, so
+        // y = 0 there.  |fp32(y * inv)| <= 127 (1 + 2^-23) by construction, so the
+        // clamp is inert, and adding 1.5 * 2^23 rounds the product to an integer (ties
+        // to even) held in the low mantissa bits: its low byte is the two's-complement
+        // code.  Same codes as the general path below, at a quarter of the instructions.
+        constexpr float kRound = 12582912.0f;
+#pragma unroll
+        for (int p = 0; p < PASSES; p++) {
+            uint32_t r[8];
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const float y = SMOOTH ? in_to_f32<BF16>(raw[p][e]) - mu[e] : in_to_f32<BF16>(raw[p][e]);
+                const float t = y * inv;
+                r[e] = __float_as_uint(t + kRound);
+            }
+            // bytes 0 of r[0..3] and r[4..7] into one word each
+            const uint32_t w0 = __builtin_amdgcn_perm(r[1], r[0], 0x0c0c0400u) |
+                                __builtin_amdgcn_perm(r[3], r[2], 0x04000c0cu);
+            const uint32_t w1 = __builtin_amdgcn_perm(r[5], r[4], 0x0c0c0400u) |
+                                __builtin_amdgcn_perm(r[7], r[6], 0x04000c0cu);
+            int8_t* dst = xq + (sv.row0 + j * kBlk + p * RPP + r0) * DP + c0;
+            *(uint2*)dst = make_uint2(w0, w1);
+        }
+        return;
+    }
 #pragma unroll
     for (int p = 0; p < PASSES; p++) {
         const int t = j * kBlk + p * RPP + r0;
@@ -142,9 +181,11 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __res
         for (int e = 0; e < 8; e++) {
             int code = 0;
             if (!zero && t < N && c0 + e < D) {
-                const float y = in_to_f32<BF16>(raw[p][e]) - mu[e];
+                const float y = SMOOTH ? in_to_f32<BF16>(raw[p][e]) - mu[e] : in_to_f32<BF16>(raw[p][e]);
                 float r = rintf(y * inv);
-                r = fminf(fmaxf(r, -127.0f), 127.0f);
+                // comparisons, not fminf/fmaxf: a NaN product stays NaN and converts to 0
+                r = r > 127.0f ? 127.0f : r;
+                r = r < -127.0f ? -127.0f : r;
                 code = int(r);
             }
             w[e / 4] |= uint32_t(code & 0xff) << (8 * (e % 4));
@@ -181,17 +222,30 @@ __global__ __launch_bounds__(256) void v_amax_kernel(const uint16_t* __restrict_
     float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     const int t_end = min(N, int(blockIdx.x + 1) * 256);
     if (c0 < D) {
-        for (int t = blockIdx.x * 256 + r0; t < t_end; t += RSTEP) {
-            const uint16_t* src = base + int64_t(t) * st.t + c0;
-            v8u16 r;
-            if constexpr (VEC8) {
-                r = *(const v8u16*)src;
-            } else {
+        // all loads of a round in flight at once; rows past the end read as 0, which
+        // leaves a maximum of absolute values unchanged
+        constexpr int ITER = 256 / RSTEP, ROUND = ITER < 16 ? ITER : 16;
 #pragma unroll
-                for (int e = 0; e < 8; e++) r[e] = (c0 + e < D) ? src[e] : (unsigned short)0;
+        for (int i0 = 0; i0 < ITER; i0 += ROUND) {
+            v8u16 r[ROUND];
+#pragma unroll
+            for (int u = 0; u < ROUND; u++) {
+                const int t = blockIdx.x * 256 + r0 + (i0 + u) * RSTEP;
+                r[u] = v8u16{0, 0, 0, 0, 0, 0, 0, 0};
+                if (t < t_end) {
+                    const uint16_t* src = base + int64_t(t) * st.t + c0;
+                    if constexpr (VEC8) {
+                        r[u] = *(const v8u16*)src;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; e++) r[u][e] = (c0 + e < D) ? src[e] : (unsigned short)0;
+                    }
+                }
             }
 #pragma unroll
-            for (int e = 0; e < 8; e++) m[e] = fmaxf(m[e], fabsf(in_to_f32<BF16>(r[e])));
+            for (int u = 0; u < ROUND; u++)
+#pragma unroll
+                for (int e = 0; e < 8; e++) m[e] = fmaxf(m[e], fabsf(in_to_f32<BF16>(r[u][e])));
         }
     }
 #pragma unroll
@@ -298,9 +352,9 @@ hipError_t launch_qk_t(const QuantQKArgs& a, hipStream_t s) {
                                                                                 (double*)a.workspace);
     const int tot = a.B * a.Hkv * a.D;
     k_mean_final_kernel<<<(tot + 63) / 64, 64, 0, s>>>((const double*)a.workspace, mk, tot, a.D, a.k_mean);
-    quant_blocks_kernel<BF16, DP, VEC8><<<dim3((mq.NB + 3) / 4, a.Hq, a.B), 256, 0, s>>>(
+    quant_blocks_kernel<BF16, DP, VEC8, false><<<dim3((mq.NB + 3) / 4, a.Hq, a.B), 256, 0, s>>>(
         (const uint16_t*)a.q, mq, a.D, nullptr, a.q_i8, a.q_scale);
-    quant_blocks_kernel<BF16, DP, VEC8><<<dim3((mk.NB + 3) / 4, a.Hkv, a.B), 256, 0, s>>>(
+    quant_blocks_kernel<BF16, DP, VEC8, true><<<dim3((mk.NB + 3) / 4, a.Hkv, a.B), 256, 0, s>>>(
         (const uint16_t*)a.k, mk, a.D, a.k_mean, a.k_i8, a.k_scale);
     return hipGetLastError();
 }

@@ -2,7 +2,7 @@
 """Benchmark: SageAttention-style quantized attention forward on one MI355X.
 
 One step = the whole hot path over one batch resident in HBM:
-    sage_quant_qk (K mean + INT8 Q/K)  ->  sage_quant_v (V operand)  ->  sage_attn_fwd.
+    sage_quant_qkv (K mean, INT8 Q/K, V operand in one call)  ->  sage_attn_fwd.
 Metric (the kernel-throughput sweep of the SageAttention pages): effective TOPS =
 4*B*H*Nq*Nkv*D / t, halved when causal.  `value` uses the whole step time; the
 attention-kernel-only rate (the pages' convention, quantisation excluded) is reported
@@ -69,18 +69,14 @@ class Runner:
         self.q, self.k, self.v = q, k, v
         dev = q.device
         L = qa.lib()
-        self.ws_qk = torch.empty(max(8, L.sage_quant_qk_workspace_bytes(w.B, w.Hkv, w.Nkv, w.D)), dtype=torch.uint8,
-                                 device=dev)
-        nv = L.sage_quant_v_workspace_bytes(w.B, w.Hkv, w.D, 1 if w.pv == "fp8" else 0)
-        self.ws_v = torch.empty(max(nv, 8), dtype=torch.uint8, device=dev)
-        self.qk = qa.quant_qk(q, k, w.layout, workspace=self.ws_qk)
-        self.vq = qa.quant_v(v, w.layout, w.pv, workspace=self.ws_v)
+        nws = L.sage_quant_qkv_workspace_bytes(w.B, w.Hkv, w.Nkv, w.D, 1 if w.pv == "fp8" else 0)
+        self.ws = torch.empty(max(8, nws), dtype=torch.uint8, device=dev)
+        self.qk, self.vq = qa.quant_qkv(q, k, v, w.layout, w.pv, workspace=self.ws)
         self.out = qa.attn_fwd(self.qk, self.vq, w.torch_dtype, w.layout, w.causal, None, w.accum)
 
     def quant(self):
         qa, w = self.qa, self.w
-        qa.quant_qk(self.q, self.k, w.layout, workspace=self.ws_qk, out=self.qk)
-        qa.quant_v(self.v, w.layout, w.pv, workspace=self.ws_v, out=self.vq)
+        qa.quant_qkv(self.q, self.k, self.v, w.layout, w.pv, workspace=self.ws, out_qk=self.qk, out_v=self.vq)
 
     def attn(self):
         qa, w = self.qa, self.w
@@ -268,13 +264,13 @@ def varlen_point(qa, torch, np, si, dev, steps):
     v = torch.randn(tq, w.Hkv, w.D, generator=g, device=dev).to(torch.bfloat16)
     cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device=dev)
     mx = max(lens)
-    qk = qa.quant_qk_varlen(q, k, cu, cu, mx, mx)
-    vq = qa.quant_v_varlen(v, cu, mx, w.pv)
+    qk, vq = qa.quant_qkv_varlen(q, k, v, cu, cu, mx, mx, w.pv)
+    ws = torch.empty(max(8, qa.lib().sage_quant_qkv_varlen_workspace_bytes(16, w.Hkv, tq, w.D, 0)), dtype=torch.uint8,
+                     device=dev)
     out = qa.attn_fwd_varlen(qk, vq, torch.bfloat16, True)
 
     def quant():
-        qa.quant_qk_varlen(q, k, cu, cu, mx, mx, out=qk)
-        qa.quant_v_varlen(v, cu, mx, w.pv, out=vq)
+        qa.quant_qkv_varlen(q, k, v, cu, cu, mx, mx, w.pv, workspace=ws, out_qk=qk, out_v=vq)
 
     def attn():
         qa.attn_fwd_varlen(qk, vq, torch.bfloat16, True, out=out)

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SAGE_ABI_VERSION 2
+#define SAGE_ABI_VERSION 3
 
 typedef enum sage_status {
     SAGE_OK = 0,
@@ -125,6 +125,27 @@ size_t sage_quant_v_workspace_bytes(int B, int H_kv, int D, sage_pv pv);
 sage_status sage_quant_v(const void* v, sage_dtype dtype, sage_layout layout, int B, int H_kv, int Nkv, int D,
                          sage_pv pv, void* v_hat, float* v_scale, void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/* Workspace of sage_quant_qkv: the fp64 K block sums of sage_quant_qk
+ * (B * H_kv * NB(Nkv) * D * 8 bytes), plus in FP8 mode per-block V channel maxima
+ * (B * H_kv * NB(Nkv) * Dp * 4) and per-channel V maxima (B * H_kv * Dp * 4).
+ * 0 for invalid sizes or pv. */
+size_t sage_quant_qkv_workspace_bytes(int B, int H_kv, int Nkv, int D, sage_pv pv);
+
+/*
+ * sage_quant_qk and sage_quant_v in one call: the same outputs, bit for bit, in four
+ * kernel launches instead of six or seven (Q quantisation and the K/V statistics
+ * stream in one grid; then the K means and V maxima; then K and V quantisation).
+ *   q, k, v, dtype, layout, shapes: as sage_quant_qk and sage_quant_v.
+ *   Outputs: q_i8, q_scale, k_i8, k_scale, k_mean, v_hat, v_scale (v_scale only in
+ *   FP8 mode, may be NULL otherwise).
+ *   workspace: at least sage_quant_qkv_workspace_bytes(...) bytes, 8-byte aligned,
+ *   contents on entry ignored and on exit unspecified.
+ */
+sage_status sage_quant_qkv(const void* q, const void* k, const void* v, sage_dtype dtype, sage_layout layout, int B,
+                           int H_qo, int H_kv, int Nq, int Nkv, int D, sage_pv pv, int8_t* q_i8, float* q_scale,
+                           int8_t* k_i8, float* k_scale, float* k_mean, void* v_hat, float* v_scale, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /*
  * Attention on the quantised operands (step 3-4 above).
@@ -201,6 +222,18 @@ sage_status sage_quant_qk_varlen(const void* q, const void* k, sage_dtype dtype,
 sage_status sage_quant_v_varlen(const void* v, sage_dtype dtype, const int32_t* cu_seqlens_kv, int B, int H_kv,
                                 int total_kv, int max_seqlen_kv, int D, sage_pv pv, void* v_hat, float* v_scale,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace of sage_quant_qkv_varlen: as sage_quant_qkv_workspace_bytes with
+ * H_kv * slots(total_kv, B) block slots in place of B * H_kv * NB(Nkv). */
+size_t sage_quant_qkv_varlen_workspace_bytes(int B, int H_kv, int total_kv, int D, sage_pv pv);
+
+/* sage_quant_qk_varlen and sage_quant_v_varlen in one call (outputs bit for bit the
+ * same; the fused launch sequence of sage_quant_qkv). */
+sage_status sage_quant_qkv_varlen(const void* q, const void* k, const void* v, sage_dtype dtype,
+                                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int B, int H_qo, int H_kv,
+                                  int total_q, int total_kv, int max_seqlen_q, int max_seqlen_kv, int D, sage_pv pv,
+                                  int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
+                                  void* v_hat, float* v_scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /* sage_attn_fwd on a packed batch (causal per sequence as in sage_attn_fwd);
  * out [total_q][H_qo][D] in out_dtype, every element written. */

@@ -30,7 +30,8 @@ import torch
 
 __all__ = [
     "SageError", "lib", "library_path", "QKQuant", "VQuant", "quant_qk", "quant_v", "attn_fwd", "debug_qk_int32",
-    "sageattn", "QKQuantVarlen", "VQuantVarlen", "quant_qk_varlen", "quant_v_varlen", "attn_fwd_varlen",
+    "quant_qkv", "sageattn", "QKQuantVarlen", "VQuantVarlen", "quant_qk_varlen", "quant_v_varlen",
+    "quant_qkv_varlen", "attn_fwd_varlen",
     "sageattn_varlen", "varlen_rows", "varlen_slots", "padded_dim", "num_blocks", "SAGE_OK", "SAGE_ERR_INVALID_ARG", "SAGE_ERR_UNSUPPORTED",
     "SAGE_ERR_WORKSPACE", "SAGE_ERR_DEVICE", "SAGE_ERR_HIP",
 ]
@@ -70,6 +71,12 @@ _EXPORTS = {
                             + [ctypes.c_void_p] * 3 + [ctypes.c_size_t, ctypes.c_void_p]),
     "sage_attn_fwd_varlen": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] + [ctypes.c_void_p] * 2
                              + [ctypes.c_int] * 9 + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+    "sage_quant_qkv_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 5),
+    "sage_quant_qkv": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 2 + [ctypes.c_int] * 7
+                       + [ctypes.c_void_p] * 8 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "sage_quant_qkv_varlen_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 5),
+    "sage_quant_qkv_varlen": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] + [ctypes.c_void_p] * 2
+                              + [ctypes.c_int] * 9 + [ctypes.c_void_p] * 8 + [ctypes.c_size_t, ctypes.c_void_p]),
 }
 
 _lib = None
@@ -98,7 +105,7 @@ def lib() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.restype = res
         fn.argtypes = args
-    if L.sage_abi_version() != 2:
+    if L.sage_abi_version() != 3:
         raise ImportError("libsage ABI version mismatch")
     _lib = L
     return L
@@ -264,15 +271,48 @@ def debug_qk_int32(qk: QKQuant, tiles: torch.Tensor, pv: str = "fp8") -> torch.T
     return out
 
 
+def quant_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: str = "HND", pv: str = "fp8",
+              workspace: Optional[torch.Tensor] = None, out_qk: Optional[QKQuant] = None,
+              out_v: Optional[VQuant] = None):
+    """quant_qk and quant_v in one library call (same outputs, fewer kernel launches)."""
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _check_input(x, name)
+    if not (q.dtype == k.dtype == v.dtype) or not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must share dtype and device")
+    if pv not in _PV:
+        raise ValueError(f"pv must be 'fp16' or 'fp8', got {pv!r}")
+    B, Hq, Nq, D = _dims(q, layout)
+    Bk, Hkv, Nkv, Dk = _dims(k, layout)
+    if Bk != B or Dk != D or _dims(v, layout) != (B, Hkv, Nkv, D):
+        raise ValueError("q, k and v disagree on batch, heads, length or head_dim")
+    L = lib()
+    Dp, nbq, nbk = padded_dim(D), num_blocks(Nq), num_blocks(Nkv)
+    dev = q.device
+    if out_qk is None:
+        out_qk = QKQuant(torch.empty(B, Hq, nbq * 64, max(Dp, 1), dtype=torch.int8, device=dev),
+                         torch.empty(B, Hq, nbq, dtype=torch.float32, device=dev),
+                         torch.empty(B, Hkv, nbk * 64, max(Dp, 1), dtype=torch.int8, device=dev),
+                         torch.empty(B, Hkv, nbk, dtype=torch.float32, device=dev),
+                         torch.empty(B, Hkv, D, dtype=torch.float32, device=dev), B, Hq, Hkv, Nq, Nkv, D)
+    if out_v is None:
+        elt = 1 if pv == "fp8" else 2
+        out_v = VQuant(torch.empty(B, Hkv, nbk, max(Dp, 1), 64 * elt, dtype=torch.uint8, device=dev),
+                       torch.empty(B, Hkv, max(Dp, 1), dtype=torch.float32, device=dev) if pv == "fp8" else None, pv)
+    need = L.sage_quant_qkv_workspace_bytes(B, Hkv, Nkv, D, _PV[pv])
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=dev)
+    _check(L.sage_quant_qkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), _DT[q.dtype], _LAYOUT[layout], B, Hq, Hkv, Nq,
+                            Nkv, D, _PV[pv], out_qk.q_i8.data_ptr(), out_qk.q_scale.data_ptr(),
+                            out_qk.k_i8.data_ptr(), out_qk.k_scale.data_ptr(), out_qk.k_mean.data_ptr(),
+                            out_v.v_hat.data_ptr(), _ptr(out_v.v_scale), workspace.data_ptr(), workspace.numel(),
+                            _stream(dev)))
+    return out_qk, out_v
+
+
 def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: str = "HND", is_causal: bool = False,
              sm_scale: Optional[float] = None, pv: str = "fp8", accum: str = "fp32") -> torch.Tensor:
     """softmax(sm_scale * q k^T [causal]) v with INT8 QK^T and FP8/FP16 PV; returns q's dtype and layout."""
-    for name, x in (("q", q), ("k", k), ("v", v)):
-        _check_input(x, name)
-    if not (q.dtype == k.dtype == v.dtype):
-        raise ValueError("q, k and v must share a dtype")
-    qk = quant_qk(q, k, tensor_layout)
-    vq = quant_v(v, tensor_layout, pv)
+    qk, vq = quant_qkv(q, k, v, tensor_layout, pv)
     return attn_fwd(qk, vq, q.dtype, tensor_layout, is_causal, sm_scale, accum)
 
 
@@ -391,6 +431,54 @@ def quant_v_varlen(v: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_k: in
     return out
 
 
+def quant_qkv_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                     cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, pv: str = "fp16",
+                     workspace: Optional[torch.Tensor] = None, out_qk: Optional[QKQuantVarlen] = None,
+                     out_v: Optional[VQuantVarlen] = None):
+    """quant_qk_varlen and quant_v_varlen in one library call (same outputs)."""
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _check_input(x, name)
+    if not (q.dtype == k.dtype == v.dtype) or not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must share dtype and device")
+    if pv not in _PV:
+        raise ValueError(f"pv must be 'fp16' or 'fp8', got {pv!r}")
+    total_q, Hq, D = _packed_dims(q, "q")
+    total_k, Hkv, Dk = _packed_dims(k, "k")
+    if Dk != D or tuple(v.shape) != (total_k, Hkv, D):
+        raise ValueError("q, k and v disagree on heads, tokens or head_dim")
+    dev = q.device
+    cq, ck = _cu(cu_seqlens_q, dev, "cu_seqlens_q"), _cu(cu_seqlens_k, dev, "cu_seqlens_k")
+    if cq.numel() != ck.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must describe the same number of sequences")
+    B = cq.numel() - 1
+    L = lib()
+    Dp = padded_dim(D)
+    rq, sq, rk, sk = varlen_rows(total_q, B), varlen_slots(total_q, B), varlen_rows(total_k, B), varlen_slots(total_k, B)
+    qk = out_qk
+    if qk is None:
+        qk = QKQuantVarlen(torch.empty(Hq, rq, max(Dp, 1), dtype=torch.int8, device=dev),
+                           torch.empty(Hq, sq, dtype=torch.float32, device=dev),
+                           torch.empty(Hkv, rk, max(Dp, 1), dtype=torch.int8, device=dev),
+                           torch.empty(Hkv, sk, dtype=torch.float32, device=dev),
+                           torch.empty(B, Hkv, D, dtype=torch.float32, device=dev), cq, ck, B, Hq, Hkv, total_q,
+                           total_k, int(max_seqlen_q), int(max_seqlen_k), D)
+    vq = out_v
+    if vq is None:
+        elt = 1 if pv == "fp8" else 2
+        vq = VQuantVarlen(torch.empty(Hkv, sk, max(Dp, 1), 64 * elt, dtype=torch.uint8, device=dev),
+                          torch.empty(B, Hkv, max(Dp, 1), dtype=torch.float32, device=dev) if pv == "fp8" else None,
+                          pv)
+    need = L.sage_quant_qkv_varlen_workspace_bytes(B, Hkv, total_k, D, _PV[pv])
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=dev)
+    _check(L.sage_quant_qkv_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), _DT[q.dtype], cq.data_ptr(),
+                                   ck.data_ptr(), B, Hq, Hkv, total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), D,
+                                   _PV[pv], qk.q_i8.data_ptr(), qk.q_scale.data_ptr(), qk.k_i8.data_ptr(),
+                                   qk.k_scale.data_ptr(), qk.k_mean.data_ptr(), vq.v_hat.data_ptr(),
+                                   _ptr(vq.v_scale), workspace.data_ptr(), workspace.numel(), _stream(dev)))
+    return qk, vq
+
+
 def attn_fwd_varlen(qk: QKQuantVarlen, vq: VQuantVarlen, out_dtype: torch.dtype, is_causal: bool = False,
                     sm_scale: Optional[float] = None, accum: str = "fp32",
                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -416,10 +504,5 @@ def sageattn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
                     sm_scale: Optional[float] = None, pv: str = "fp16", accum: str = "fp32") -> torch.Tensor:
     """Attention over a packed batch of sequences of different lengths (each sequence
     attends only to its own keys); returns q's dtype, shape (total_q, Hq, D)."""
-    for name, x in (("q", q), ("k", k), ("v", v)):
-        _check_input(x, name)
-    if not (q.dtype == k.dtype == v.dtype):
-        raise ValueError("q, k and v must share a dtype")
-    qk = quant_qk_varlen(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
-    vq = quant_v_varlen(v, qk.cu_k, max_seqlen_k, pv)
+    qk, vq = quant_qkv_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, pv)
     return attn_fwd_varlen(qk, vq, q.dtype, is_causal, sm_scale, accum)

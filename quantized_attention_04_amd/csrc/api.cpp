@@ -126,6 +126,22 @@ sage_status check_attn_args(const int8_t* q_i8, const float* q_scale, const int8
     return SAGE_OK;
 }
 
+// Pointer, dtype and pv checks of the fused Q/K/V quantisation.
+sage_status check_qkv_args(const void* q, const void* k, const void* v, sage_dtype dtype, sage_pv pv,
+                           const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                           const float* k_mean, const void* v_hat, const float* v_scale, const char* what) {
+    if (!q || !k || !v || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean || !v_hat)
+        return fail(SAGE_ERR_INVALID_ARG, "%s: null tensor pointer", what);
+    if (dtype != SAGE_FP16 && dtype != SAGE_BF16) return fail(SAGE_ERR_INVALID_ARG, "bad dtype %d", int(dtype));
+    if (pv != SAGE_PV_FP16 && pv != SAGE_PV_FP8) return fail(SAGE_ERR_INVALID_ARG, "bad pv mode %d", int(pv));
+    if (pv == SAGE_PV_FP8 && (!v_scale || !aligned(v_scale, 4)))
+        return fail(SAGE_ERR_INVALID_ARG, "%s: FP8 mode needs v_scale", what);
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(q_i8, 16) || !aligned(k_i8, 16) ||
+        !aligned(v_hat, 16) || !aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(k_mean, 4))
+        return fail(SAGE_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned (scales 4-byte)", what);
+    return SAGE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -216,6 +232,42 @@ sage_status sage_quant_v(const void* v, sage_dtype dtype, sage_layout layout, in
     a.fp8 = pv == SAGE_PV_FP8;
     a.v_hat = v_hat, a.v_scale = v_scale, a.workspace = workspace;
     return launch_status(sage::launch_quant_v(a, (hipStream_t)stream), "sage_quant_v");
+}
+
+size_t sage_quant_qkv_workspace_bytes(int B, int H_kv, int Nkv, int D, sage_pv pv) {
+    if (B <= 0 || H_kv <= 0 || Nkv <= 0 || D <= 0 || D > 256) return 0;
+    if (pv != SAGE_PV_FP16 && pv != SAGE_PV_FP8) return 0;
+    return sage::qkv_workspace(B, H_kv, Nkv, D, false, 0, pv == SAGE_PV_FP8).bytes;
+}
+
+sage_status sage_quant_qkv(const void* q, const void* k, const void* v, sage_dtype dtype, sage_layout layout, int B,
+                           int H_qo, int H_kv, int Nq, int Nkv, int D, sage_pv pv, int8_t* q_i8, float* q_scale,
+                           int8_t* k_i8, float* k_scale, float* k_mean, void* v_hat, float* v_scale, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    sage_status s = check_qkv_args(q, k, v, dtype, pv, q_i8, q_scale, k_i8, k_scale, k_mean, v_hat, v_scale,
+                                   "sage_quant_qkv");
+    if (s != SAGE_OK) return s;
+    if (layout != SAGE_HND && layout != SAGE_NHD) return fail(SAGE_ERR_INVALID_ARG, "bad layout %d", int(layout));
+    s = check_shape(B, H_qo, H_kv, Nq, Nkv, D);
+    if (s != SAGE_OK) return s;
+    const size_t need = sage_quant_qkv_workspace_bytes(B, H_kv, Nkv, D, pv);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 8))
+        return fail(SAGE_ERR_WORKSPACE, "sage_quant_qkv: workspace of %zu bytes (8-byte aligned) required, got %zu",
+                    need, workspace ? workspace_bytes : size_t(0));
+    s = check_device();
+    if (s != SAGE_OK) return s;
+    sage::QuantQKArgs a{};
+    a.q = q, a.k = k;
+    a.bf16 = dtype == SAGE_BF16;
+    a.layout_nhd = layout == SAGE_NHD;
+    a.B = B, a.Hq = H_qo, a.Hkv = H_kv, a.Nq = Nq, a.Nkv = Nkv, a.D = D;
+    a.q_i8 = q_i8, a.q_scale = q_scale, a.k_i8 = k_i8, a.k_scale = k_scale, a.k_mean = k_mean;
+    a.workspace = workspace;
+    sage::QuantVArgs va{};
+    va.v = v;
+    va.fp8 = pv == SAGE_PV_FP8;
+    va.v_hat = v_hat, va.v_scale = v_scale;
+    return launch_status(sage::launch_quant_qkv(a, va, (hipStream_t)stream), "sage_quant_qkv");
 }
 
 sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
@@ -327,6 +379,43 @@ sage_status sage_quant_v_varlen(const void* v, sage_dtype dtype, const int32_t* 
     a.fp8 = pv == SAGE_PV_FP8;
     a.v_hat = v_hat, a.v_scale = v_scale, a.workspace = workspace;
     return launch_status(sage::launch_quant_v(a, (hipStream_t)stream), "sage_quant_v_varlen");
+}
+
+size_t sage_quant_qkv_varlen_workspace_bytes(int B, int H_kv, int total_kv, int D, sage_pv pv) {
+    if (B <= 0 || H_kv <= 0 || total_kv <= 0 || D <= 0 || D > 256) return 0;
+    if (pv != SAGE_PV_FP16 && pv != SAGE_PV_FP8) return 0;
+    return sage::qkv_workspace(B, H_kv, 0, D, true, total_kv, pv == SAGE_PV_FP8).bytes;
+}
+
+sage_status sage_quant_qkv_varlen(const void* q, const void* k, const void* v, sage_dtype dtype,
+                                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int B, int H_qo, int H_kv,
+                                  int total_q, int total_kv, int max_seqlen_q, int max_seqlen_kv, int D, sage_pv pv,
+                                  int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
+                                  void* v_hat, float* v_scale, void* workspace, size_t workspace_bytes, void* stream) {
+    sage_status s = check_qkv_args(q, k, v, dtype, pv, q_i8, q_scale, k_i8, k_scale, k_mean, v_hat, v_scale,
+                                   "sage_quant_qkv_varlen");
+    if (s != SAGE_OK) return s;
+    s = check_varlen(cu_seqlens_q, cu_seqlens_kv, B, H_qo, H_kv, total_q, total_kv, max_seqlen_q, max_seqlen_kv, D);
+    if (s != SAGE_OK) return s;
+    const size_t need = sage_quant_qkv_varlen_workspace_bytes(B, H_kv, total_kv, D, pv);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 8))
+        return fail(SAGE_ERR_WORKSPACE,
+                    "sage_quant_qkv_varlen: workspace of %zu bytes (8-byte aligned) required, got %zu", need,
+                    workspace ? workspace_bytes : size_t(0));
+    s = check_device();
+    if (s != SAGE_OK) return s;
+    sage::QuantQKArgs a{};
+    a.q = q, a.k = k;
+    a.bf16 = dtype == SAGE_BF16;
+    a.B = B, a.Hq = H_qo, a.Hkv = H_kv, a.Nq = max_seqlen_q, a.Nkv = max_seqlen_kv, a.D = D;
+    a.cu_q = cu_seqlens_q, a.cu_k = cu_seqlens_kv, a.total_q = total_q, a.total_k = total_kv;
+    a.q_i8 = q_i8, a.q_scale = q_scale, a.k_i8 = k_i8, a.k_scale = k_scale, a.k_mean = k_mean;
+    a.workspace = workspace;
+    sage::QuantVArgs va{};
+    va.v = v;
+    va.fp8 = pv == SAGE_PV_FP8;
+    va.v_hat = v_hat, va.v_scale = v_scale;
+    return launch_status(sage::launch_quant_qkv(a, va, (hipStream_t)stream), "sage_quant_qkv_varlen");
 }
 
 sage_status sage_attn_fwd_varlen(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,

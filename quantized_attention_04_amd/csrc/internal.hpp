@@ -63,7 +63,27 @@ struct DebugQKArgs {
     int32_t* out;
 };
 
+// Workspace of the fused Q/K/V quantisation (byte offsets; total = bytes):
+// fp64 K block channel sums [slots][D], then (FP8) fp32 V block channel maxima
+// [slots][Dp] and the V channel maxima as float bits [B * H_kv][Dp].  slots = block
+// slots of K: B * H_kv * ceil(Nkv / 64) dense, H_kv * ceil((total + 64 B) / 64) packed.
+struct QKVWorkspace {
+    size_t kpart, vpart, amax, bytes;
+};
+inline QKVWorkspace qkv_workspace(int B, int Hkv, int Nkv, int D, bool packed, int total_kv, bool fp8) {
+    const size_t dp = D <= 64 ? 64 : (D <= 128 ? 128 : 256);
+    const size_t slots = packed ? size_t(Hkv) * size_t((int64_t(total_kv) + 64 * int64_t(B) + 63) / 64)
+                                : size_t(B) * size_t(Hkv) * size_t((Nkv + 63) / 64);
+    QKVWorkspace w;
+    w.kpart = 0;
+    w.vpart = slots * size_t(D) * sizeof(double);
+    w.amax = w.vpart + (fp8 ? slots * dp * sizeof(float) : 0);
+    w.bytes = w.amax + (fp8 ? size_t(B) * size_t(Hkv) * dp * sizeof(uint32_t) : 0);
+    return w;
+}
+
 hipError_t launch_quant_qk(const QuantQKArgs& a, hipStream_t s);
+hipError_t launch_quant_qkv(const QuantQKArgs& a, const QuantVArgs& v, hipStream_t s);
 hipError_t launch_quant_v(const QuantVArgs& a, hipStream_t s);
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s);
 hipError_t launch_debug_qk(const DebugQKArgs& a, hipStream_t s);

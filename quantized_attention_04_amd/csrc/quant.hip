@@ -19,11 +19,10 @@ namespace sage {
 // 64 x D tile is read with coalesced 16-byte loads into LDS, then thread c < D walks
 // its channel.
 template <bool BF16, int DP, bool VEC8>
-__global__ __launch_bounds__(256) void k_mean_partial_kernel(const uint16_t* __restrict__ k, SeqMap m, int D,
-                                                             double* __restrict__ part) {
+__device__ __forceinline__ void k_partial_block(const uint16_t* __restrict__ k, const SeqMap& m, int D,
+                                                double* __restrict__ part, int j, int h, int b,
+                                                uint16_t (*tile)[DP]) {
     constexpr int CH = DP / 8, RSTEP = 256 / CH;  // RSTEP token rows per pass
-    __shared__ __attribute__((aligned(16))) uint16_t tile[kBlk][DP];
-    const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const SeqView sv = seq_view(m, b, h);
     if (j * kBlk >= sv.n) return;  // the whole workgroup: past this sequence's end
     const int N = sv.n;
@@ -53,6 +52,12 @@ __global__ __launch_bounds__(256) void k_mean_partial_kernel(const uint16_t* __r
     for (int t = 0; t < nt; t++) s += double(in_to_f32<BF16>(tile[t][c]));
     part[(sv.slot0 + j) * D + c] = s;
 }
+template <bool BF16, int DP, bool VEC8>
+__global__ __launch_bounds__(256) void k_mean_partial_kernel(const uint16_t* __restrict__ k, SeqMap m, int D,
+                                                             double* __restrict__ part) {
+    __shared__ __attribute__((aligned(16))) uint16_t tile[kBlk][DP];
+    k_partial_block<BF16, DP, VEC8>(k, m, D, part, blockIdx.x, blockIdx.y, blockIdx.z, tile);
+}
 
 // K mean, pass 2: mean = fp32((sum over blocks, ascending, of part) / N); 0 for a
 // sequence without tokens.  One thread per (b, h, channel) in 64-thread workgroups
@@ -79,14 +84,12 @@ __global__ __launch_bounds__(64) void k_mean_final_kernel(const double* __restri
 //   y = x (Q) or fp32(x - mean[c]) (K); amax = max |y|; scale = amax / 127;
 //   inv = 127 / amax; code = clamp(rne(y * inv), -127, 127).
 template <bool BF16, int DP, bool VEC8, bool SMOOTH>
-__global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __restrict__ x, SeqMap m, int D,
-                                                           const float* __restrict__ mean, int8_t* __restrict__ xq,
-                                                           float* __restrict__ scale) {
+__device__ __forceinline__ void quant_block_wave(const uint16_t* __restrict__ x, const SeqMap& m, int D,
+                                                 const float* __restrict__ mean, int8_t* __restrict__ xq,
+                                                 float* __restrict__ scale, int j, int h, int b, int lane) {
     constexpr int CH = DP / 8;        // 8-channel chunks per row
     constexpr int RPP = kWave / CH;   // rows per pass
     constexpr int PASSES = kBlk / RPP;
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int j = blockIdx.x * 4 + wave, h = blockIdx.y, b = blockIdx.z;
     const SeqView sv = seq_view(m, b, h);
     if (j * kBlk >= sv.n) return;  // this wave: past the sequence's end
     const int N = sv.n;
@@ -194,6 +197,14 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __res
         *(uint2*)dst = make_uint2(w[0], w[1]);
     }
 }
+template <bool BF16, int DP, bool VEC8, bool SMOOTH>
+__global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __restrict__ x, SeqMap m, int D,
+                                                           const float* __restrict__ mean, int8_t* __restrict__ xq,
+                                                           float* __restrict__ scale) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    quant_block_wave<BF16, DP, VEC8, SMOOTH>(x, m, D, mean, xq, scale, blockIdx.x * 4 + wave, blockIdx.y, blockIdx.z,
+                                             lane);
+}
 
 // ------------------------------------------------------------------------------------------
 // V operand, FP8 mode, pass 0: clear the per-channel amax buffer (a fill kernel rather
@@ -255,6 +266,132 @@ __global__ __launch_bounds__(256) void v_amax_kernel(const uint16_t* __restrict_
         float mx = 0.0f;
         for (int r = 0; r < RSTEP; r++) mx = fmaxf(mx, red[r][c]);
         atomicMax(amax_bits + (int64_t(b) * sm.H + h) * DP + c, __float_as_uint(mx));
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Q, K and V together (sage_quant_qkv): the same results as the two-call path in four
+// launches.  Pass 1 streams Q (block quantisation), K (block channel sums) and, in FP8
+// mode, V (block channel maxima) side by side in one grid; pass 2 forms the K means
+// and V maxima; pass 3 quantises K and V with the kernels above.  The per-block V
+// maxima replace the integer atomics of v_amax_kernel (same maximum: max is exact in
+// any order).
+
+// One 64-token K/V block of one (b, kv head): K channel sums as k_partial_block (fp64,
+// ascending tokens) and, with VMAX, the per-channel maximum of |v| -> vpart[slot][c],
+// c < DP (channel padding and rows past the end read as 0).  256 threads; the K tile
+// goes to LDS and the V rows to registers with all loads in flight together.
+template <bool BF16, int DP, bool VEC8, bool VMAX>
+__device__ __forceinline__ void kv_stats_block(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                               const SeqMap& m, int D, double* __restrict__ kpart,
+                                               float* __restrict__ vpart, int j, int h, int b, uint16_t (*tile)[DP],
+                                               float (*red)[DP]) {
+    constexpr int CH = DP / 8, RSTEP = 256 / CH, ROWS = kBlk / RSTEP;
+    const SeqView sv = seq_view(m, b, h);
+    if (j * kBlk >= sv.n) return;  // the whole workgroup: past this sequence's end
+    const int N = sv.n;
+    const int ch = threadIdx.x % CH, r0 = threadIdx.x / CH, c0 = ch * 8;
+    auto load8 = [&](const uint16_t* base, int t) {
+        v8u16 r = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (t < N && c0 < D) {
+            const uint16_t* src = base + int64_t(t) * m.st.t + c0;
+            if constexpr (VEC8) {
+                r = *(const v8u16*)src;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; e++) r[e] = (c0 + e < D) ? src[e] : (unsigned short)0;
+            }
+        }
+        return r;
+    };
+    v8u16 kr[ROWS], vr[VMAX ? ROWS : 1];
+#pragma unroll
+    for (int u = 0; u < ROWS; u++) {
+        const int t = j * kBlk + r0 + u * RSTEP;
+        kr[u] = load8(k + sv.in_off, t);
+        if constexpr (VMAX) vr[u] = load8(v + sv.in_off, t);
+    }
+#pragma unroll
+    for (int u = 0; u < ROWS; u++) *(v8u16*)&tile[r0 + u * RSTEP][c0] = kr[u];
+    if constexpr (VMAX) {
+        float mx[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int u = 0; u < ROWS; u++)
+#pragma unroll
+            for (int e = 0; e < 8; e++) mx[e] = fmaxf(mx[e], fabsf(in_to_f32<BF16>(vr[u][e])));
+#pragma unroll
+        for (int e = 0; e < 8; e++) red[r0][c0 + e] = mx[e];
+    }
+    __syncthreads();
+    const int c = threadIdx.x;
+    if (c < D) {
+        const int nt = min(kBlk, N - j * kBlk);
+        double s = 0.0;
+        for (int t = 0; t < nt; t++) s += double(in_to_f32<BF16>(tile[t][c]));
+        kpart[(sv.slot0 + j) * D + c] = s;
+    }
+    if constexpr (VMAX) {
+        for (int cc = c; cc < DP; cc += 256) {
+            float a = 0.0f;
+#pragma unroll
+            for (int q = 0; q < RSTEP; q++) a = fmaxf(a, red[q][cc]);
+            vpart[(sv.slot0 + j) * DP + cc] = a;
+        }
+    }
+}
+
+// Pass 1.  nq workgroups quantise four Q blocks each (number x of a (head, batch): x
+// + nq4 * (h + Hq * b)); nkv take one K/V block each (j + NB * (h + H_kv * b)).  The
+// two kinds are spread evenly over the grid, so Q's read-write stream and the K/V
+// read streams run side by side.
+template <bool BF16, int DP, bool VEC8, bool VMAX>
+__global__ __launch_bounds__(256) void qkv_pass1_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                        const uint16_t* __restrict__ v, SeqMap mq, SeqMap mk, int D,
+                                                        int nq, int nkv, int8_t* __restrict__ q_i8,
+                                                        float* __restrict__ q_scale, double* __restrict__ kpart,
+                                                        float* __restrict__ vpart) {
+    __shared__ __attribute__((aligned(16))) uint16_t tile[kBlk][DP];
+    __shared__ float red[VMAX ? 256 / (DP / 8) : 1][DP];
+    const int64_t wg = blockIdx.x, T = int64_t(nq) + nkv;
+    const int a0 = int(wg * nq / T), a1 = int((wg + 1) * nq / T);  // Q workgroups before wg, before wg + 1
+    if (a1 > a0) {
+        const int nq4 = (mq.NB + 3) / 4;
+        const int x = a0 % nq4, h = (a0 / nq4) % mq.H, b = a0 / (nq4 * mq.H);
+        const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+        quant_block_wave<BF16, DP, VEC8, false>(q, mq, D, nullptr, q_i8, q_scale, x * 4 + wave, h, b, lane);
+    } else {
+        const int r = int(wg) - a1;
+        const int j = r % mk.NB, h = (r / mk.NB) % mk.H, b = r / (mk.NB * mk.H);
+        kv_stats_block<BF16, DP, VEC8, VMAX>(k, v, mk, D, kpart, vpart, j, h, b, tile, red);
+    }
+}
+
+// Pass 2: per (b, kv head, channel): the K mean as k_mean_final_kernel (c < D) and, with
+// VMAX, the V channel maximum over the sequence's blocks as float bits (c < DP), the
+// form quant_v_kernel reads.  One thread per (b, kv head, c < DP).
+template <int DP, bool VMAX>
+__global__ __launch_bounds__(64) void qkv_pass2_kernel(const double* __restrict__ kpart,
+                                                       const float* __restrict__ vpart, SeqMap m, int B, int D,
+                                                       float* __restrict__ mean, uint32_t* __restrict__ amax_bits) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    const int c = i % DP, bh = i / DP;
+    if (bh >= B * m.H) return;
+    const int h = bh % m.H, b = bh / m.H;
+    const SeqView sv = seq_view(m, b, h);
+    const int nb = (sv.n + kBlk - 1) / kBlk;
+    if (c < D) {
+        const double* p = kpart + sv.slot0 * D + c;
+        double s = 0.0;
+#pragma unroll 32
+        for (int j = 0; j < nb; j++) s += p[int64_t(j) * D];  // ascending block order
+        mean[int64_t(bh) * D + c] = sv.n > 0 ? float(s / double(sv.n)) : 0.0f;
+    }
+    if constexpr (VMAX) {
+        const float* p = vpart + sv.slot0 * DP + c;
+        float a = 0.0f;
+#pragma unroll 32
+        for (int j = 0; j < nb; j++) a = fmaxf(a, p[int64_t(j) * DP]);
+        amax_bits[int64_t(bh) * DP + c] = __float_as_uint(a);
     }
 }
 
@@ -379,6 +516,41 @@ hipError_t launch_v_t(const QuantVArgs& a, hipStream_t s) {
 
 }  // namespace
 
+template <bool BF16, int DP, bool VEC8>
+hipError_t launch_qkv_t(const QuantQKArgs& a, const QuantVArgs& va, hipStream_t s) {
+    const SeqMap mq = make_seq_map(a.layout_nhd, a.cu_q, a.B, a.Hq, a.Nq, a.total_q, a.D);
+    const SeqMap mk = make_seq_map(a.layout_nhd, a.cu_k, a.B, a.Hkv, a.Nkv, a.total_k, a.D);
+    const QKVWorkspace w = qkv_workspace(a.B, a.Hkv, a.Nkv, a.D, a.cu_k != nullptr, a.total_k, va.fp8);
+    char* ws = (char*)a.workspace;
+    double* kpart = (double*)(ws + w.kpart);
+    float* vpart = (float*)(ws + w.vpart);
+    uint32_t* amax = (uint32_t*)(ws + w.amax);
+    const int nq = ((mq.NB + 3) / 4) * a.Hq * a.B;
+    const int nkv = mk.NB * a.Hkv * a.B;
+    if (va.fp8) {
+        qkv_pass1_kernel<BF16, DP, VEC8, true><<<nq + nkv, 256, 0, s>>>(
+            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)va.v, mq, mk, a.D, nq, nkv, a.q_i8,
+            a.q_scale, kpart, vpart);
+        qkv_pass2_kernel<DP, true><<<(a.B * a.Hkv * DP + 63) / 64, 64, 0, s>>>(kpart, vpart, mk, a.B, a.D, a.k_mean,
+                                                                             amax);
+    } else {
+        qkv_pass1_kernel<BF16, DP, VEC8, false><<<nq + nkv, 256, 0, s>>>(
+            (const uint16_t*)a.q, (const uint16_t*)a.k, nullptr, mq, mk, a.D, nq, nkv, a.q_i8, a.q_scale, kpart,
+            nullptr);
+        qkv_pass2_kernel<DP, false><<<(a.B * a.Hkv * DP + 63) / 64, 64, 0, s>>>(kpart, nullptr, mk, a.B, a.D,
+                                                                              a.k_mean, nullptr);
+    }
+    quant_blocks_kernel<BF16, DP, VEC8, true><<<dim3((mk.NB + 3) / 4, a.Hkv, a.B), 256, 0, s>>>(
+        (const uint16_t*)a.k, mk, a.D, a.k_mean, a.k_i8, a.k_scale);
+    if (va.fp8)
+        quant_v_kernel<BF16, DP, VEC8, true><<<dim3(mk.NB, a.Hkv, a.B), DP * 2, 0, s>>>(
+            (const uint16_t*)va.v, mk, a.D, amax, va.v_hat, va.v_scale);
+    else
+        quant_v_kernel<BF16, DP, VEC8, false><<<dim3(mk.NB, a.Hkv, a.B), DP * 2, 0, s>>>(
+            (const uint16_t*)va.v, mk, a.D, nullptr, va.v_hat, nullptr);
+    return hipGetLastError();
+}
+
 template <bool BF16>
 hipError_t launch_qk_dp(const QuantQKArgs& a, hipStream_t s) {
     const bool vec = (a.D % 8) == 0;
@@ -401,6 +573,18 @@ hipError_t launch_v_dp(const QuantVArgs& a, hipStream_t s) {
 
 hipError_t launch_quant_v(const QuantVArgs& a, hipStream_t s) {
     return a.bf16 ? launch_v_dp<true>(a, s) : launch_v_dp<false>(a, s);
+}
+
+template <bool BF16>
+hipError_t launch_qkv_dp(const QuantQKArgs& a, const QuantVArgs& v, hipStream_t s) {
+    const bool vec = (a.D % 8) == 0;
+    if (a.D <= 64) return vec ? launch_qkv_t<BF16, 64, true>(a, v, s) : launch_qkv_t<BF16, 64, false>(a, v, s);
+    if (a.D <= 128) return vec ? launch_qkv_t<BF16, 128, true>(a, v, s) : launch_qkv_t<BF16, 128, false>(a, v, s);
+    return vec ? launch_qkv_t<BF16, 256, true>(a, v, s) : launch_qkv_t<BF16, 256, false>(a, v, s);
+}
+
+hipError_t launch_quant_qkv(const QuantQKArgs& a, const QuantVArgs& v, hipStream_t s) {
+    return a.bf16 ? launch_qkv_dp<true>(a, v, s) : launch_qkv_dp<false>(a, v, s);
 }
 
 }  // namespace sage

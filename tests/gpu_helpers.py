@@ -50,11 +50,14 @@ class Case:
             self._oq = oracle.quantize(self.qf, self.kf, self.vf, self.w.pv == "fp8")
         return self._oq
 
-    def gpu_quant(self):
-        note(f"[gpu] quant_qk/quant_v {self.w.name} B{self.w.B} Hq{self.w.Hq} Hkv{self.w.Hkv} "
-             f"Nq{self.w.Nq} Nkv{self.w.Nkv} D{self.w.D} {self.w.layout} pv={self.w.pv}")
-        qk = qa.quant_qk(self.dq, self.dk, self.w.layout)
-        vq = qa.quant_v(self.dv, self.w.layout, self.w.pv)
+    def gpu_quant(self, fused: bool = False):
+        note(f"[gpu] {'quant_qkv' if fused else 'quant_qk/quant_v'} {self.w.name} B{self.w.B} Hq{self.w.Hq} "
+             f"Hkv{self.w.Hkv} Nq{self.w.Nq} Nkv{self.w.Nkv} D{self.w.D} {self.w.layout} pv={self.w.pv}")
+        if fused:
+            qk, vq = qa.quant_qkv(self.dq, self.dk, self.dv, self.w.layout, self.w.pv)
+        else:
+            qk = qa.quant_qk(self.dq, self.dk, self.w.layout)
+            vq = qa.quant_v(self.dv, self.w.layout, self.w.pv)
         torch.cuda.synchronize()
         return qk, vq
 

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_strings():
     L = qa.lib()
-    assert L.sage_abi_version() == 2
+    assert L.sage_abi_version() == 3
     for s in range(6):
         assert L.sage_status_string(s).decode().startswith("SAGE_")
     assert qa.padded_dim(1) == 64 and qa.padded_dim(64) == 64 and qa.padded_dim(65) == 128
@@ -82,6 +82,59 @@ def _v(**kw):
 
 def _detail():
     return qa.lib().sage_last_error_detail().decode()
+
+
+def _fused(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, layout=0, B=1, Hq=4, Hkv=2, Nq=128, Nkv=100, D=96, pv=1, q_i8=FAKE,
+             q_scale=FAKE, k_i8=FAKE, k_scale=FAKE, k_mean=FAKE, v_hat=FAKE, v_scale=FAKE, ws=FAKE, ws_bytes=1 << 20,
+             stream=None)
+    a.update(kw)
+    return qa.lib().sage_quant_qkv(a["q"], a["k"], a["v"], a["dtype"], a["layout"], a["B"], a["Hq"], a["Hkv"],
+                                   a["Nq"], a["Nkv"], a["D"], a["pv"], a["q_i8"], a["q_scale"], a["k_i8"],
+                                   a["k_scale"], a["k_mean"], a["v_hat"], a["v_scale"], a["ws"], a["ws_bytes"],
+                                   a["stream"])
+
+
+def test_fused_quant_workspace_sizes():
+    L = qa.lib()
+    fp8, fp16 = qa.SAGE_PV_FP8, qa.SAGE_PV_FP16
+    slots = 2 * 8 * 128  # B * H_kv * NB(8192)
+    assert L.sage_quant_qkv_workspace_bytes(2, 8, 8192, 128, fp16) == slots * 128 * 8
+    assert L.sage_quant_qkv_workspace_bytes(2, 8, 8192, 128, fp8) == slots * 128 * 8 + slots * 128 * 4 + 2 * 8 * 128 * 4
+    # D = 96: K sums over the 96 real channels, V maxima over Dp = 128
+    assert L.sage_quant_qkv_workspace_bytes(1, 2, 100, 96, fp8) == 4 * 96 * 8 + 4 * 128 * 4 + 2 * 128 * 4
+    assert L.sage_quant_qkv_workspace_bytes(1, 2, 100, 257, fp8) == 0
+    assert L.sage_quant_qkv_workspace_bytes(1, 2, 100, 96, 3) == 0
+    # packed: H_kv * ceil((total + 64 B) / 64) slots
+    s = 2 * ((1000 + 64 * 3 + 63) // 64)
+    assert L.sage_quant_qkv_varlen_workspace_bytes(3, 2, 1000, 96, fp16) == s * 96 * 8
+    assert L.sage_quant_qkv_varlen_workspace_bytes(3, 2, 1000, 96, fp8) == s * 96 * 8 + s * 128 * 4 + 3 * 2 * 128 * 4
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"v": None}, qa.SAGE_ERR_INVALID_ARG),
+    ({"k_mean": None}, qa.SAGE_ERR_INVALID_ARG),
+    ({"pv": 2}, qa.SAGE_ERR_INVALID_ARG),
+    ({"v_scale": None}, qa.SAGE_ERR_INVALID_ARG),
+    ({"dtype": 3}, qa.SAGE_ERR_INVALID_ARG),
+    ({"layout": 2}, qa.SAGE_ERR_INVALID_ARG),
+    ({"Hq": 3}, qa.SAGE_ERR_INVALID_ARG),
+    ({"D": 257}, qa.SAGE_ERR_UNSUPPORTED),
+    ({"v": FAKE + 4}, qa.SAGE_ERR_INVALID_ARG),
+    ({"ws": None}, qa.SAGE_ERR_WORKSPACE),
+    ({"ws_bytes": 4 * 96 * 8 + 4 * 128 * 4 + 2 * 128 * 4 - 1}, qa.SAGE_ERR_WORKSPACE),
+    ({"ws": FAKE + 4}, qa.SAGE_ERR_WORKSPACE),
+])
+def test_fused_quant_rejects(kw, code):
+    assert _fused(**kw) == code
+    assert _detail()
+
+
+def test_fused_quant_fp16_takes_no_scale():
+    if torch.cuda.is_available():
+        pytest.skip("would launch kernels on fake pointers")
+    assert _fused(pv=0, v_scale=None, ws_bytes=4 * 96 * 8) == qa.SAGE_ERR_DEVICE
+    assert _fused() == qa.SAGE_ERR_DEVICE
 
 
 @pytest.mark.parametrize("kw,code", [

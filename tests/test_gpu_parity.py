@@ -49,6 +49,17 @@ def test_quantization_bit_exact(cid, w):
     check_quant_bit_exact(case2, qk, vq2)
 
 
+@pytest.mark.parametrize("cid,w", QUANT_CASES, ids=[c[0] for c in QUANT_CASES])
+def test_fused_quantization_bit_exact(cid, w):
+    """sage_quant_qkv (one call, four launches) against the oracle, in both P.V modes."""
+    case = Case(w)
+    qk, vq = case.gpu_quant(fused=True)
+    check_quant_bit_exact(case, qk, vq)
+    case2 = case.with_pv("fp16" if w.pv == "fp8" else "fp8")
+    qk2, vq2 = case2.gpu_quant(fused=True)
+    check_quant_bit_exact(case2, qk2, vq2)
+
+
 TILE_CASES = [
     ("tiny", W("tiny")),
     ("llm_prefill", W("llm_prefill")),

@@ -38,12 +38,15 @@ class VCase:
         self.cq, self.ck = self.cu_q.numpy().astype(np.int64), self.cu_k.numpy().astype(np.int64)
         self.Qs = oracle.quantize_varlen(self.qf, self.kf, self.vf, self.cq, self.ck, w.pv == "fp8")
 
-    def gpu(self, accum=None):
+    def gpu(self, accum=None, fused=False):
         w, dev = self.w, "cuda:0"
-        note(f"[gpu] varlen {w.name} B{w.B} Hq{w.Hq} Hkv{w.Hkv} D{w.D} pv={w.pv} causal={w.causal}")
+        note(f"[gpu] varlen {w.name} B{w.B} Hq{w.Hq} Hkv{w.Hkv} D{w.D} pv={w.pv} causal={w.causal} fused={fused}")
         q, k, v, cq, ck = (x.to(dev) for x in (self.q, self.k, self.v, self.cu_q, self.cu_k))
-        qk = qa.quant_qk_varlen(q, k, cq, ck, max(w.lens_q + (1,)), max(w.lens_k + (1,)))
-        vq = qa.quant_v_varlen(v, ck, max(w.lens_k + (1,)), w.pv)
+        if fused:
+            qk, vq = qa.quant_qkv_varlen(q, k, v, cq, ck, max(w.lens_q + (1,)), max(w.lens_k + (1,)), w.pv)
+        else:
+            qk = qa.quant_qk_varlen(q, k, cq, ck, max(w.lens_q + (1,)), max(w.lens_k + (1,)))
+            vq = qa.quant_v_varlen(v, ck, max(w.lens_k + (1,)), w.pv)
         out = qa.attn_fwd_varlen(qk, vq, w.torch_dtype, w.causal, sm_scale_of(w.D), accum or w.accum)
         torch.cuda.synchronize()
         return qk, vq, out
@@ -54,10 +57,11 @@ def _rows_slots(cu, b):
     return R, R // 64
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "fused"])
 @pytest.mark.parametrize("w", CASES, ids=[c.name for c in CASES])
-def test_varlen_quantization_bit_exact(w):
+def test_varlen_quantization_bit_exact(w, fused):
     c = VCase(w)
-    qk, vq, _ = c.gpu()
+    qk, vq, _ = c.gpu(fused=fused)
     Dp = qa.padded_dim(w.D)
     q8, qs = qk.q_i8.cpu().numpy(), qk.q_scale.cpu().numpy()
     k8, ks, km = qk.k_i8.cpu().numpy(), qk.k_scale.cpu().numpy(), qk.k_mean.cpu().numpy()

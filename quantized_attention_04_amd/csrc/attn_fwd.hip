@@ -90,8 +90,9 @@ struct Cfg {
     // waves share each SIMD.  The vector ALU is the binding unit -- the softmax costs
     // about twice the MFMA time -- and one wave can issue a vector instruction only
     // every other slot, so the ALU needs several ready waves per SIMD to stay busy.
-    // (head dim 256: 128 accumulator VGPRs alone, two waves)
-    static constexpr int OCC = DP == 64 ? 4 : (DP == 128 ? 3 : 2);  // waves per SIMD
+    // (head dim 256: 128 accumulator VGPRs alone, two waves; one with FP16 P.V, whose
+    // operand registers take it past 256 VGPRs)
+    static constexpr int OCC = DP == 64 ? 4 : (DP == 128 ? 3 : (FP8 ? 2 : 1));  // waves per SIMD
     // LDS stages: three (two tiles stream in while one is used) when OCC workgroups of
     // three fit in the 160 KB of a CU, else two
     static constexpr int NST = OCC * 3 * STAGE <= 160 * 1024 ? 3 : 2;

@@ -148,10 +148,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 // compiler from guarding every later LDS read with a wait for ALL outstanding loads
 // (it cannot tell a prefetch into one LDS stage from reads of the other).  Callers
 // order it with explicit vmcnt waits and barriers.  Loads complete in issue order.
+// The LDS base travels in M0 as a register operand of the statement (constraint
+// "{m0}"), so the compiler loads M0 itself and knows the statement reads it.
 __device__ __forceinline__ void load_lds_16(const void* gptr, void* lds_base) {
     const uint32_t lds =
         __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base);
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds) : "memory");
 }
 
 // Same copy with the global address split into a wave-uniform 64-bit base (SGPR pair)
@@ -160,9 +162,8 @@ __device__ __forceinline__ void load_lds_16(const void* gptr, void* lds_base) {
 // and a single live SGPR for the LDS side.
 template <int LDS_OFF>
 __device__ __forceinline__ void load_lds_16_s(const void* sbase, uint32_t voff, uint32_t lds_wave_base) {
-    asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
-                 "s"(lds_wave_base), "i"(LDS_OFF)
-                 : "memory", "m0", "scc");
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_wave_base + uint32_t(LDS_OFF))
+                 : "memory");
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;

@@ -57,10 +57,13 @@ def lib() -> ctypes.CDLL:
     L.orc_round_array.argtypes = [_f64p, _L, ctypes.c_int, ctypes.c_int, _f64p]
     L.orc_k_mean.argtypes = [_f32p, _L, _L, _L, _L, _f32p]
     L.orc_quant_blocks.argtypes = [_f32p, ctypes.c_void_p, _L, _L, _L, _L, _i8p, _f32p]
+    L.orc_quant_groups.argtypes = [_f32p, ctypes.c_void_p, _L, _L, _L, _L, _L, _i8p, _f32p]
     L.orc_quant_v.argtypes = [_f32p, _L, _L, _L, _L, ctypes.c_int, _f32p, _f32p]
     L.orc_scores_i32.argtypes = [_i8p, _i8p, _L, _L, _L, _L, _L, _L, _i64p, _L, _i32p]
     L.orc_attn_emulate.argtypes = [_i8p, _f32p, _i8p, _f32p, _f32p, _f32p, ctypes.c_int, _L, _L, _L, _L, _L,
                                    _L, ctypes.c_int, ctypes.c_double, _i64p, _L, _f64p, ctypes.c_void_p]
+    L.orc_attn_emulate_g.argtypes = [_i8p, _f32p, _i8p, _f32p, _f32p, _f32p, ctypes.c_int, _L, _L, _L, _L, _L,
+                                     _L, _L, _L, ctypes.c_int, ctypes.c_double, _i64p, _L, _f64p, ctypes.c_void_p]
     L.orc_attn_exact.argtypes = [_f32p, _f32p, _f32p, _L, _L, _L, _L, _L, _L, ctypes.c_int, ctypes.c_double,
                                  _i64p, _L, _f64p]
     _lib = L
@@ -139,6 +142,28 @@ def quant_blocks(x: np.ndarray, mean: Optional[np.ndarray] = None):
     return xq, sc
 
 
+def quant_groups(x: np.ndarray, G: int, mean: Optional[np.ndarray] = None):
+    """INT8 quantisation with one scale per G consecutive tokens (G = 64: quant_blocks);
+    returns (int8 [B,H,N,D], scale [B,H,ceil(N/G)])."""
+    B, H, N, D = x.shape
+    ng = (N + G - 1) // G
+    xq = np.empty((B, H, N, D), np.int8)
+    sc = np.empty((B, H, ng), np.float32)
+    mp = None
+    if mean is not None:
+        mean = np.ascontiguousarray(mean, np.float32)
+        assert mean.shape == (B, H, D)
+        mp = mean.ctypes.data_as(ctypes.c_void_p)
+    lib().orc_quant_groups(np.ascontiguousarray(x, np.float32), mp, B, H, N, D, int(G), xq, sc)
+    return xq, sc
+
+
+# Quantisation granularities: tokens per Q scale and per K scale.  "thread" is the
+# gfx950 reading of the README's per-thread quantisation (one scale per query row,
+# one per 32 keys: the groups one lane / one half-wave owns in the score MFMA).
+GRANULARITY = {"block": (64, 64), "thread": (1, 32)}
+
+
 def quant_v(v: np.ndarray, pv_fp8: bool):
     """V operand: (values float32 [B,H,N,D], vscale float32 [B,H,D] or None)."""
     B, H, N, D = v.shape
@@ -160,15 +185,18 @@ class Quantized:
     pv_fp8: bool
     Hq: int
     Hkv: int
+    qg: int = 64   # tokens per Q scale
+    kg: int = 64   # tokens per K scale
 
 
-def quantize(q: np.ndarray, k: np.ndarray, v: np.ndarray, pv_fp8: bool) -> Quantized:
+def quantize(q: np.ndarray, k: np.ndarray, v: np.ndarray, pv_fp8: bool, gran: str = "block") -> Quantized:
     """q, k, v: float32 (B, H, N, D) arrays holding the exact fp16/bf16 inputs."""
+    qg, kg = GRANULARITY[gran]
     mu = k_mean(k)
-    q8, sq = quant_blocks(q)
-    k8, sk = quant_blocks(k, mu)
+    q8, sq = quant_groups(q, qg)
+    k8, sk = quant_groups(k, kg, mu)
     vh, vs = quant_v(v, pv_fp8)
-    return Quantized(q8, sq, k8, sk, mu, vh, vs, bool(pv_fp8), q.shape[1], k.shape[1])
+    return Quantized(q8, sq, k8, sk, mu, vh, vs, bool(pv_fp8), q.shape[1], k.shape[1], qg, kg)
 
 
 def v_hat_bits(vals: np.ndarray, pv_fp8: bool) -> np.ndarray:
@@ -201,9 +229,9 @@ def attn_emulate(Q: Quantized, causal: bool, sm_scale: float, rows: np.ndarray, 
     out = np.empty((rows.shape[0], D), np.float64)
     amb = np.empty((rows.shape[0], D), np.float64) if with_ambiguity else None
     vs = Q.v_scale if Q.v_scale is not None else np.zeros((B, Q.Hkv, D), np.float32)
-    lib().orc_attn_emulate(Q.q_i8, Q.q_scale, Q.k_i8, Q.k_scale, Q.v_hat, vs, int(Q.pv_fp8), B, Hq, Q.Hkv, Nq,
-                           Nkv, D, int(bool(causal)), float(sm_scale), rows, rows.shape[0], out,
-                           None if amb is None else amb.ctypes.data_as(ctypes.c_void_p))
+    lib().orc_attn_emulate_g(Q.q_i8, Q.q_scale, Q.k_i8, Q.k_scale, Q.v_hat, vs, int(Q.pv_fp8), B, Hq, Q.Hkv, Nq,
+                             Nkv, D, int(Q.qg), int(Q.kg), int(bool(causal)), float(sm_scale), rows, rows.shape[0],
+                             out, None if amb is None else amb.ctypes.data_as(ctypes.c_void_p))
     return (out, amb) if with_ambiguity else out
 
 
@@ -229,14 +257,14 @@ def _seq(x: np.ndarray, cu, b: int) -> np.ndarray:
     return np.ascontiguousarray(x[int(cu[b]):int(cu[b + 1])].transpose(1, 0, 2)[None], dtype=np.float32)
 
 
-def quantize_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q, cu_k, pv_fp8: bool):
+def quantize_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q, cu_k, pv_fp8: bool, gran: str = "block"):
     """Per-sequence Quantized (None where the sequence has no key)."""
     out = []
     for b in range(len(cu_q) - 1):
         if int(cu_k[b + 1]) == int(cu_k[b]):
             out.append(None)
             continue
-        out.append(quantize(_seq(q, cu_q, b), _seq(k, cu_k, b), _seq(v, cu_k, b), pv_fp8))
+        out.append(quantize(_seq(q, cu_q, b), _seq(k, cu_k, b), _seq(v, cu_k, b), pv_fp8, gran))
     return out
 
 

@@ -42,7 +42,7 @@
 
 #define BLK 64 /* token block: one quantisation scale per 64 consecutive tokens */
 
-int orc_version(void) { return 1; }
+int orc_version(void) { return 2; }
 
 int orc_threads(void) {
 #ifdef _OPENMP
@@ -136,9 +136,24 @@ void orc_k_mean(const float* k, long B, long H, long N, long D, float* mean) {
  *   q     = clamp(rne(fp32(y * inv)), -127, 127);
  *   amax == 0  ->  scale = 0 and q = 0.
  * ------------------------------------------------------------------------- */
+void orc_quant_groups(const float* x, const float* mean, long B, long H, long N, long D, long G,
+                      int8_t* xq, float* scale);
+
 void orc_quant_blocks(const float* x, const float* mean, long B, long H, long N, long D,
                       int8_t* xq, float* scale) {
-    long nblk = (N + BLK - 1) / BLK;
+    orc_quant_groups(x, mean, B, H, N, D, BLK, xq, scale);
+}
+
+/* The same arithmetic with one scale per G consecutive tokens (G = 64: the blocks
+ * above).  Finer groups are the "per-thread" granularity of the SageAttention
+ * project README ("Project Updates", v2.0.1: finer quantisation groups that keep
+ * the matrix-core path efficient; "Current Features": varying granularities).  On
+ * gfx950 that reading is G = 1 for Q (one query column per lane of the score MFMA)
+ * and G = 32 for K (the 32 keys one half-wave of lanes holds), so every lane still
+ * dequantises a tile with a single factor.  scale: [B][H][ceil(N / G)]. */
+void orc_quant_groups(const float* x, const float* mean, long B, long H, long N, long D, long G,
+                      int8_t* xq, float* scale) {
+    long nblk = (N + G - 1) / G;
 #pragma omp parallel for collapse(3) schedule(static)
     for (long b = 0; b < B; b++)
         for (long h = 0; h < H; h++)
@@ -146,7 +161,7 @@ void orc_quant_blocks(const float* x, const float* mean, long B, long H, long N,
                 const float* xb = x + (b * H + h) * N * D;
                 const float* mu = mean ? mean + (b * H + h) * D : NULL;
                 int8_t* qb = xq + (b * H + h) * N * D;
-                long t0 = j * BLK, t1 = (j + 1) * BLK < N ? (j + 1) * BLK : N;
+                long t0 = j * G, t1 = (j + 1) * G < N ? (j + 1) * G : N;
                 float amax = 0.0f;
                 for (long t = t0; t < t1; t++)
                     for (long c = 0; c < D; c++) {
@@ -292,14 +307,30 @@ static double tie_flip(double x, int fmt) {
     return fabs(x - mid) <= AMB_REL * x ? q : 0.0;
 }
 
+void orc_attn_emulate_g(const int8_t* q8, const float* sq, const int8_t* k8, const float* sk,
+                        const float* vhat, const float* vscale, int pv_fp8, long B, long Hq, long Hkv,
+                        long Nq, long Nkv, long D, long qg, long kg, int causal, double sm_scale,
+                        const int64_t* rows, long R, double* out, double* amb);
+
 void orc_attn_emulate(const int8_t* q8, const float* sq, const int8_t* k8, const float* sk,
                       const float* vhat, const float* vscale, int pv_fp8, long B, long Hq, long Hkv,
                       long Nq, long Nkv, long D, int causal, double sm_scale, const int64_t* rows,
                       long R, double* out, double* amb) {
+    orc_attn_emulate_g(q8, sq, k8, sk, vhat, vscale, pv_fp8, B, Hq, Hkv, Nq, Nkv, D, BLK, BLK, causal, sm_scale,
+                       rows, R, out, amb);
+}
+
+/* The same with Q scales per qg tokens and K scales per kg keys (orc_quant_groups):
+ * the dequantisation factor c of a score takes the scale of its query's group and
+ * of its key's group.  The online softmax still advances in 64-key blocks. */
+void orc_attn_emulate_g(const int8_t* q8, const float* sq, const int8_t* k8, const float* sk,
+                        const float* vhat, const float* vscale, int pv_fp8, long B, long Hq, long Hkv,
+                        long Nq, long Nkv, long D, long qg, long kg, int causal, double sm_scale,
+                        const int64_t* rows, long R, double* out, double* amb) {
     const float scale2 = (float)sm_scale * 1.44269504088896341f; /* fp32(sm_scale * log2 e) */
     const int fmt = pv_fp8 ? ORC_E4M3 : ORC_FP16;
     long group = Hq / Hkv;
-    long nqb = (Nq + BLK - 1) / BLK, nkb = (Nkv + BLK - 1) / BLK;
+    long nqg = (Nq + qg - 1) / qg, nkg = (Nkv + kg - 1) / kg, nkb = (Nkv + BLK - 1) / BLK;
     const long off = Nkv - Nq; /* causal: key j visible to query i iff j <= i + off */
     (void)B;
 #pragma omp parallel for schedule(dynamic, 4)
@@ -307,7 +338,7 @@ void orc_attn_emulate(const int8_t* q8, const float* sq, const int8_t* k8, const
         long b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
         long hk = h / group;
         const int8_t* qrow = q8 + ((b * Hq + h) * Nq + i) * D;
-        float sqi = sq[(b * Hq + h) * nqb + i / BLK];
+        float sqi = sq[(b * Hq + h) * nqg + i / qg];
         double* acc = (double*)calloc((size_t)D, sizeof(double));
         double* aacc = (double*)calloc((size_t)D, sizeof(double));
         float s2[BLK];
@@ -319,11 +350,11 @@ void orc_attn_emulate(const int8_t* q8, const float* sq, const int8_t* k8, const
             long j0 = kb * BLK;
             if (causal && j0 > i + off) break;
             long j1 = j0 + BLK < Nkv ? j0 + BLK : Nkv;
-            float c = (sqi * sk[(b * Hkv + hk) * nkb + kb]) * scale2;
             float bmax = -INFINITY;
             for (long j = j0; j < j1; j++) {
                 vis[j - j0] = !(causal && j > i + off);
                 if (!vis[j - j0]) continue;
+                const float c = (sqi * sk[(b * Hkv + hk) * nkg + j / kg]) * scale2;
                 const int8_t* krow = k8 + ((b * Hkv + hk) * Nkv + j) * D;
                 int64_t s32 = 0;
                 for (long d = 0; d < D; d++) s32 += (int64_t)qrow[d] * (int64_t)krow[d];

@@ -601,3 +601,128 @@ def test_varlen_oracle_is_the_dense_oracle_per_sequence():
         sel = rows[:, 0] == b
         np.testing.assert_array_equal(got[sel], oracle.attn_emulate(Qd, True, 0.25, r))
         np.testing.assert_array_equal(ex[sel], oracle.attn_exact(qs, ks, vs, True, 0.25, r))
+
+
+# ----------------------------------------------------------------------------- finer granularity
+# "per-thread" quantisation (SageAttention project README, "Project Updates" v2.0.1 and
+# "Current Features"): one Q scale per token, one K scale per 32 keys.
+
+def _equal_amax(shape, A, seed, group_axis_len):
+    """bf16 values in (-A, A) with |x| = A reached once in every group of
+    `group_axis_len` tokens (every token when 1): every group has amax A."""
+    x = np.clip(_bf16_vals(shape, scale=0.3 * A, seed=seed), -0.9 * A, 0.9 * A)
+    B, H, N, D = shape
+    g = torch.Generator().manual_seed(seed + 1)
+    for t0 in range(0, N, group_axis_len):
+        t = t0 + int(torch.randint(0, min(group_axis_len, N - t0), (1,), generator=g))
+        c = int(torch.randint(0, D, (1,), generator=g))
+        x[:, :, t, c] = A if (t + c) % 2 else -A
+    return np.ascontiguousarray(x.astype(np.float32))
+
+
+def test_quant_groups_of_64_are_the_blocks():
+    x = _bf16_vals((2, 2, 150, 40), seed=60)
+    for mean in (None, oracle.k_mean(x)):
+        a = oracle.quant_blocks(x, mean)
+        b = oracle.quant_groups(x, 64, mean)
+        np.testing.assert_array_equal(a[0], b[0])
+        np.testing.assert_array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("G", [1, 32])
+def test_quant_groups_equal_amax_reduce_to_blocks(G):
+    """When every group of G tokens has the block's amax, the group scales equal the
+    block scale and the codes equal the block codes (ragged tail included)."""
+    x = _equal_amax((1, 2, 150, 24), 3.0, 61, G)
+    qb, sb = oracle.quant_blocks(x)
+    qg, sg = oracle.quant_groups(x, G)
+    np.testing.assert_array_equal(qg, qb)
+    assert sg.shape == (1, 2, (150 + G - 1) // G)
+    assert (sg == sb[0, 0, 0]).all()
+
+
+@pytest.mark.parametrize("G", [1, 32])
+def test_quant_groups_invariants(G):
+    """Per group: max|code| = 127 where the group is non-zero, scale = amax / 127 and
+    |y - code * scale| <= scale / 2 (plus the inv rounding), zeros for a zero group."""
+    x = _bf16_vals((1, 2, 100, 48), seed=62) * np.exp(_bf16_vals((1, 2, 100, 1), scale=1.5, seed=63))
+    x = np.ascontiguousarray(x.astype(np.float32))
+    x[0, 1, 40:72] = 0.0
+    mu = oracle.k_mean(x)
+    for mean in (None, mu):
+        q, s = oracle.quant_groups(x, G, mean)
+        y = x - (mean[:, :, None, :] if mean is not None else 0)
+        for h in range(2):
+            for j in range(s.shape[2]):
+                blk = y[0, h, G * j:G * j + G].astype(np.float64)
+                qb = q[0, h, G * j:G * j + G].astype(np.float64)
+                amax, sc = np.abs(blk).max(), float(s[0, h, j])
+                if amax == 0:
+                    assert sc == 0 and (qb == 0).all()
+                    continue
+                assert abs(sc * 127 - amax) <= amax * 2 ** -23
+                assert np.abs(qb).max() == 127
+                assert (np.abs(blk - qb * sc) <= sc * (0.5 + 2 ** -15)).all()
+
+
+def test_per_token_q_scales_shrink_error_on_outlier_tokens():
+    """Tokens 50x larger than their neighbours: per-token scales keep the small
+    tokens' relative error at the INT8 level, one scale per 64 tokens does not."""
+    x = _bf16_vals((1, 1, 128, 64), seed=64).astype(np.float32)
+    x[0, 0, ::16] *= 50.0
+    small = np.ones(128, bool)
+    small[::16] = False
+    errs = {}
+    for G in (64, 1):
+        q, s = oracle.quant_groups(np.ascontiguousarray(x), G)
+        sc = np.repeat(s[0, 0], G)[:128][:, None]
+        deq = q[0, 0].astype(np.float64) * sc
+        errs[G] = np.abs(deq - x[0, 0])[small].mean() / np.abs(x[0, 0])[small].mean()
+    assert errs[1] < 0.01 and errs[64] > 5 * errs[1], errs
+
+
+@pytest.mark.parametrize("pv_fp8", [False, True])
+def test_emulate_thread_granularity_equal_scales_is_block(pv_fp8):
+    """With every Q token and every 32-key group at the block amax (and K's mean 0:
+    each channel holds +x and -x), the finer scales equal the block scales and the
+    emulation gives the block result exactly."""
+    q = _equal_amax((1, 2, 100, 32), 2.0, 65, 1)
+    kh = _equal_amax((1, 2, 75, 32), 1.5, 66, 32)
+    k = np.ascontiguousarray(np.concatenate([kh, -kh], axis=2))  # channel sums exactly 0
+    v = _bf16_vals((1, 2, 150, 32), seed=67)
+    Qb = oracle.quantize(q, k, v, pv_fp8, "block")
+    Qt = oracle.quantize(q, k, v, pv_fp8, "thread")
+    assert (Qt.k_mean == 0).all()
+    np.testing.assert_array_equal(Qb.q_i8, Qt.q_i8)
+    np.testing.assert_array_equal(Qb.k_i8, Qt.k_i8)
+    rows = oracle.all_rows(1, 2, 100)
+    for causal in (False, True):
+        np.testing.assert_array_equal(oracle.attn_emulate(Qb, causal, 0.2, rows),
+                                      oracle.attn_emulate(Qt, causal, 0.2, rows))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_emulate_thread_granularity_is_softmax_of_dequantised_scores(causal):
+    """FP16 P.V: the emulation equals fp64 softmax(sm_scale * Qd Kd^T) V^ with Qd, Kd
+    the codes times their own token / 32-key scales (V^ = fp16(v)), up to the fp16
+    rounding of P.  Scales spread over 100x between groups, so a score dequantised
+    with another group's scale would be far off."""
+    q = _bf16_vals((1, 2, 70, 32), seed=68) * np.exp(_bf16_vals((1, 2, 70, 1), scale=1.2, seed=69))
+    k = _bf16_vals((1, 2, 150, 32), seed=70) * np.exp(_bf16_vals((1, 2, 150, 1), scale=1.2, seed=71)) + 0.3
+    v = _bf16_vals((1, 2, 150, 32), seed=72)
+    q, k = (np.ascontiguousarray(a.astype(np.float32)) for a in (q, k))
+    Q = oracle.quantize(q, k, v, False, "thread")
+    assert Q.q_scale.shape == (1, 2, 70) and Q.k_scale.shape == (1, 2, 5)
+    sm = 0.25
+    rows = oracle.all_rows(1, 2, 70)
+    got = oracle.attn_emulate(Q, causal, sm, rows)
+    for h in range(2):
+        qd = Q.q_i8[0, h].astype(np.float64) * Q.q_scale[0, h][:, None].astype(np.float64)
+        kd = Q.k_i8[0, h].astype(np.float64) * np.repeat(Q.k_scale[0, h], 32)[:150, None].astype(np.float64)
+        s = sm * qd @ kd.T
+        if causal:
+            s = np.where(np.arange(150)[None, :] <= np.arange(70)[:, None] + 80, s, -np.inf)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        ref = p @ Q.v_hat[0, h].astype(np.float64) / p.sum(axis=1, keepdims=True)
+        err = np.abs(got[h * 70:(h + 1) * 70] - ref).max()
+        assert err <= 2e-3 * np.abs(ref).max(), err

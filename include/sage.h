@@ -74,6 +74,16 @@ typedef enum sage_pv { SAGE_PV_FP16 = 0, SAGE_PV_FP8 = 1 } sage_pv;
  * fp16 inner accumulator is an fp32 one on gfx950 matrix cores); fp16 single level
  * is not offered (the gfx950 FP16/FP8 matrix instructions accumulate in fp32). */
 typedef enum sage_accum { SAGE_ACC_FP32 = 0, SAGE_ACC_FP16_FP32 = 1, SAGE_ACC_FP16 = 2 } sage_accum;
+/* Q/K quantisation granularity (README "Current Features": varying granularities).
+ * SAGE_GRAN_BLOCK: one scale per 64 tokens for Q and for K (the layouts above).
+ * SAGE_GRAN_THREAD: the finer "per-thread" quantisation of README "Project Updates"
+ * (v2.0.1), read for gfx950 as the groups each lane owns in the score MFMA: one Q
+ * scale per token, one K scale per 32 keys.  Scale layouts then:
+ *   q_scale  float [B][H_qo][N_pad(Nq)]        (per token, padding rows 0)
+ *   k_scale  float [B][H_kv][NB(Nkv)][2]       (keys 64j .. 64j+31, 64j+32 .. 64j+63)
+ * and for packed batches q_scale [H_qo][rows(total_q)], k_scale [H_kv][slots(total_kv)][2].
+ * The codes are still per element (x * inv rounded), every other step unchanged. */
+typedef enum sage_qk_gran { SAGE_GRAN_BLOCK = 0, SAGE_GRAN_THREAD = 1 } sage_qk_gran;
 
 int sage_abi_version(void);
 const char* sage_status_string(sage_status s);
@@ -139,13 +149,16 @@ size_t sage_quant_qkv_workspace_bytes(int B, int H_kv, int Nkv, int D, sage_pv p
  *   q, k, v, dtype, layout, shapes: as sage_quant_qk and sage_quant_v.
  *   Outputs: q_i8, q_scale, k_i8, k_scale, k_mean, v_hat, v_scale (v_scale only in
  *   FP8 mode, may be NULL otherwise).
+ *   gran: SAGE_GRAN_BLOCK (the outputs of the two calls) or SAGE_GRAN_THREAD (per-token
+ *   Q scales and per-32-key K scales, layouts at sage_qk_gran; attention then goes
+ *   through sage_attn_fwd_g with the same gran).
  *   workspace: at least sage_quant_qkv_workspace_bytes(...) bytes, 8-byte aligned,
  *   contents on entry ignored and on exit unspecified.
  */
 sage_status sage_quant_qkv(const void* q, const void* k, const void* v, sage_dtype dtype, sage_layout layout, int B,
-                           int H_qo, int H_kv, int Nq, int Nkv, int D, sage_pv pv, int8_t* q_i8, float* q_scale,
-                           int8_t* k_i8, float* k_scale, float* k_mean, void* v_hat, float* v_scale, void* workspace,
-                           size_t workspace_bytes, void* stream);
+                           int H_qo, int H_kv, int Nq, int Nkv, int D, sage_pv pv, sage_qk_gran gran, int8_t* q_i8,
+                           float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean, void* v_hat, float* v_scale,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Attention on the quantised operands (step 3-4 above).
@@ -165,6 +178,14 @@ sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t
                           const void* v_hat, const float* v_scale, void* out, sage_dtype out_dtype,
                           sage_layout out_layout, int B, int H_qo, int H_kv, int Nq, int Nkv, int D, int is_causal,
                           float sm_scale, sage_pv pv, sage_accum accum, void* stream);
+
+/* sage_attn_fwd on operands quantised with granularity `gran` (sage_quant_qkv):
+ * each score is dequantised with its query's and its key's own scale.
+ * sage_attn_fwd(...) is sage_attn_fwd_g(..., SAGE_GRAN_BLOCK, stream). */
+sage_status sage_attn_fwd_g(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                            const void* v_hat, const float* v_scale, void* out, sage_dtype out_dtype,
+                            sage_layout out_layout, int B, int H_qo, int H_kv, int Nq, int Nkv, int D, int is_causal,
+                            float sm_scale, sage_pv pv, sage_accum accum, sage_qk_gran gran, void* stream);
 
 /*
  * Debug dump of INT32 score tiles through the attention kernel's own operand
@@ -232,8 +253,9 @@ size_t sage_quant_qkv_varlen_workspace_bytes(int B, int H_kv, int total_kv, int 
 sage_status sage_quant_qkv_varlen(const void* q, const void* k, const void* v, sage_dtype dtype,
                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int B, int H_qo, int H_kv,
                                   int total_q, int total_kv, int max_seqlen_q, int max_seqlen_kv, int D, sage_pv pv,
-                                  int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
-                                  void* v_hat, float* v_scale, void* workspace, size_t workspace_bytes, void* stream);
+                                  sage_qk_gran gran, int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
+                                  float* k_mean, void* v_hat, float* v_scale, void* workspace, size_t workspace_bytes,
+                                  void* stream);
 
 /* sage_attn_fwd on a packed batch (causal per sequence as in sage_attn_fwd);
  * out [total_q][H_qo][D] in out_dtype, every element written. */
@@ -242,6 +264,14 @@ sage_status sage_attn_fwd_varlen(const int8_t* q_i8, const float* q_scale, const
                                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int B, int H_qo, int H_kv,
                                  int total_q, int total_kv, int max_seqlen_q, int max_seqlen_kv, int D, int is_causal,
                                  float sm_scale, sage_pv pv, sage_accum accum, void* stream);
+
+/* sage_attn_fwd_varlen with a quantisation granularity (as sage_attn_fwd_g). */
+sage_status sage_attn_fwd_varlen_g(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                                   const void* v_hat, const float* v_scale, void* out, sage_dtype out_dtype,
+                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int B, int H_qo,
+                                   int H_kv, int total_q, int total_kv, int max_seqlen_q, int max_seqlen_kv, int D,
+                                   int is_causal, float sm_scale, sage_pv pv, sage_accum accum, sage_qk_gran gran,
+                                   void* stream);
 
 #ifdef __cplusplus
 }

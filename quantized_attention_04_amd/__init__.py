@@ -44,6 +44,7 @@ SAGE_FP16, SAGE_BF16 = 0, 1
 SAGE_HND, SAGE_NHD = 0, 1
 SAGE_PV_FP16, SAGE_PV_FP8 = 0, 1
 SAGE_ACC_FP32, SAGE_ACC_FP16_FP32, SAGE_ACC_FP16 = 0, 1, 2
+SAGE_GRAN_BLOCK, SAGE_GRAN_THREAD = 0, 1
 
 _EXPORTS = {
     # name: (restype, argtypes)
@@ -72,11 +73,16 @@ _EXPORTS = {
     "sage_attn_fwd_varlen": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] + [ctypes.c_void_p] * 2
                              + [ctypes.c_int] * 9 + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "sage_quant_qkv_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 5),
-    "sage_quant_qkv": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 2 + [ctypes.c_int] * 7
+    "sage_quant_qkv": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 2 + [ctypes.c_int] * 8
                        + [ctypes.c_void_p] * 8 + [ctypes.c_size_t, ctypes.c_void_p]),
     "sage_quant_qkv_varlen_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 5),
     "sage_quant_qkv_varlen": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] + [ctypes.c_void_p] * 2
-                              + [ctypes.c_int] * 9 + [ctypes.c_void_p] * 8 + [ctypes.c_size_t, ctypes.c_void_p]),
+                              + [ctypes.c_int] * 10 + [ctypes.c_void_p] * 8 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "sage_attn_fwd_g": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int, ctypes.c_int] + [ctypes.c_int] * 7
+                        + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+    "sage_attn_fwd_varlen_g": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] + [ctypes.c_void_p] * 2
+                               + [ctypes.c_int] * 9 + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                       ctypes.c_void_p]),
 }
 
 _lib = None
@@ -134,6 +140,7 @@ def num_blocks(N: int) -> int:
 # ----------------------------------------------------------------------------- tensor helpers
 
 _DT = {torch.float16: SAGE_FP16, torch.bfloat16: SAGE_BF16}
+_GRAN = {"block": SAGE_GRAN_BLOCK, "thread": SAGE_GRAN_THREAD}
 _LAYOUT = {"HND": SAGE_HND, "NHD": SAGE_NHD}
 _PV = {"fp16": SAGE_PV_FP16, "fp8": SAGE_PV_FP8}
 _ACC = {"fp32": SAGE_ACC_FP32, "fp16+fp32": SAGE_ACC_FP16_FP32, "fp32+fp16": SAGE_ACC_FP16_FP32,
@@ -182,6 +189,7 @@ class QKQuant:
     Nq: int
     Nkv: int
     D: int
+    gran: str = "block"     # "thread": q_scale [B, Hq, N_pad(Nq)] per token, k_scale [B, Hkv, NB(Nkv), 2]
 
 
 @dataclasses.dataclass
@@ -254,10 +262,13 @@ def attn_fwd(qk: QKQuant, vq: VQuant, out_dtype: torch.dtype, layout: str = "HND
     if out is None:
         shape = (B, Hq, Nq, D) if layout == "HND" else (B, Nq, Hq, D)
         out = torch.empty(shape, dtype=out_dtype, device=dev)
-    _check(lib().sage_attn_fwd(qk.q_i8.data_ptr(), qk.q_scale.data_ptr(), qk.k_i8.data_ptr(), qk.k_scale.data_ptr(),
-                               vq.v_hat.data_ptr(), _ptr(vq.v_scale), out.data_ptr(), _DT[out_dtype], _LAYOUT[layout],
-                               B, Hq, Hkv, Nq, Nkv, D, int(bool(is_causal)), float(sm_scale), _PV[vq.pv], _ACC[accum],
-                               _stream(dev)))
+    args = (qk.q_i8.data_ptr(), qk.q_scale.data_ptr(), qk.k_i8.data_ptr(), qk.k_scale.data_ptr(), vq.v_hat.data_ptr(),
+            _ptr(vq.v_scale), out.data_ptr(), _DT[out_dtype], _LAYOUT[layout], B, Hq, Hkv, Nq, Nkv, D,
+            int(bool(is_causal)), float(sm_scale), _PV[vq.pv], _ACC[accum])
+    if qk.gran == "block":
+        _check(lib().sage_attn_fwd(*args, _stream(dev)))
+    else:
+        _check(lib().sage_attn_fwd_g(*args, _GRAN[qk.gran], _stream(dev)))
     return out
 
 
@@ -273,8 +284,11 @@ def debug_qk_int32(qk: QKQuant, tiles: torch.Tensor, pv: str = "fp8") -> torch.T
 
 def quant_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: str = "HND", pv: str = "fp8",
               workspace: Optional[torch.Tensor] = None, out_qk: Optional[QKQuant] = None,
-              out_v: Optional[VQuant] = None):
-    """quant_qk and quant_v in one library call (same outputs, fewer kernel launches)."""
+              out_v: Optional[VQuant] = None, gran: str = "block"):
+    """quant_qk and quant_v in one library call (same outputs, fewer kernel launches).
+    gran="thread": one Q scale per token and one K scale per 32 keys."""
+    if gran not in _GRAN:
+        raise ValueError(f"gran must be 'block' or 'thread', got {gran!r}")
     for name, x in (("q", q), ("k", k), ("v", v)):
         _check_input(x, name)
     if not (q.dtype == k.dtype == v.dtype) or not (q.device == k.device == v.device):
@@ -289,11 +303,14 @@ def quant_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: str = "
     Dp, nbq, nbk = padded_dim(D), num_blocks(Nq), num_blocks(Nkv)
     dev = q.device
     if out_qk is None:
+        thr = gran == "thread"
         out_qk = QKQuant(torch.empty(B, Hq, nbq * 64, max(Dp, 1), dtype=torch.int8, device=dev),
-                         torch.empty(B, Hq, nbq, dtype=torch.float32, device=dev),
+                         torch.empty(B, Hq, nbq * 64 if thr else nbq, dtype=torch.float32, device=dev),
                          torch.empty(B, Hkv, nbk * 64, max(Dp, 1), dtype=torch.int8, device=dev),
-                         torch.empty(B, Hkv, nbk, dtype=torch.float32, device=dev),
-                         torch.empty(B, Hkv, D, dtype=torch.float32, device=dev), B, Hq, Hkv, Nq, Nkv, D)
+                         torch.empty((B, Hkv, nbk, 2) if thr else (B, Hkv, nbk), dtype=torch.float32, device=dev),
+                         torch.empty(B, Hkv, D, dtype=torch.float32, device=dev), B, Hq, Hkv, Nq, Nkv, D, gran)
+    elif out_qk.gran != gran:
+        raise ValueError("out_qk was allocated for another granularity")
     if out_v is None:
         elt = 1 if pv == "fp8" else 2
         out_v = VQuant(torch.empty(B, Hkv, nbk, max(Dp, 1), 64 * elt, dtype=torch.uint8, device=dev),
@@ -302,7 +319,7 @@ def quant_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: str = "
     if workspace is None:
         workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=dev)
     _check(L.sage_quant_qkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), _DT[q.dtype], _LAYOUT[layout], B, Hq, Hkv, Nq,
-                            Nkv, D, _PV[pv], out_qk.q_i8.data_ptr(), out_qk.q_scale.data_ptr(),
+                            Nkv, D, _PV[pv], _GRAN[gran], out_qk.q_i8.data_ptr(), out_qk.q_scale.data_ptr(),
                             out_qk.k_i8.data_ptr(), out_qk.k_scale.data_ptr(), out_qk.k_mean.data_ptr(),
                             out_v.v_hat.data_ptr(), _ptr(out_v.v_scale), workspace.data_ptr(), workspace.numel(),
                             _stream(dev)))
@@ -310,9 +327,11 @@ def quant_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: str = "
 
 
 def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: str = "HND", is_causal: bool = False,
-             sm_scale: Optional[float] = None, pv: str = "fp8", accum: str = "fp32") -> torch.Tensor:
-    """softmax(sm_scale * q k^T [causal]) v with INT8 QK^T and FP8/FP16 PV; returns q's dtype and layout."""
-    qk, vq = quant_qkv(q, k, v, tensor_layout, pv)
+             sm_scale: Optional[float] = None, pv: str = "fp8", accum: str = "fp32",
+             qk_gran: str = "block") -> torch.Tensor:
+    """softmax(sm_scale * q k^T [causal]) v with INT8 QK^T and FP8/FP16 PV; returns q's dtype and layout.
+    qk_gran: "block" (one scale per 64 tokens) or "thread" (per query token, per 32 keys)."""
+    qk, vq = quant_qkv(q, k, v, tensor_layout, pv, gran=qk_gran)
     return attn_fwd(qk, vq, q.dtype, tensor_layout, is_causal, sm_scale, accum)
 
 
@@ -346,6 +365,7 @@ class QKQuantVarlen:
     max_q: int
     max_k: int
     D: int
+    gran: str = "block"     # "thread": q_scale [Hq, rows(total_q)], k_scale [Hkv, slots(total_kv), 2]
 
 
 @dataclasses.dataclass
@@ -434,8 +454,10 @@ def quant_v_varlen(v: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_k: in
 def quant_qkv_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
                      cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, pv: str = "fp16",
                      workspace: Optional[torch.Tensor] = None, out_qk: Optional[QKQuantVarlen] = None,
-                     out_v: Optional[VQuantVarlen] = None):
+                     out_v: Optional[VQuantVarlen] = None, gran: str = "block"):
     """quant_qk_varlen and quant_v_varlen in one library call (same outputs)."""
+    if gran not in _GRAN:
+        raise ValueError(f"gran must be 'block' or 'thread', got {gran!r}")
     for name, x in (("q", q), ("k", k), ("v", v)):
         _check_input(x, name)
     if not (q.dtype == k.dtype == v.dtype) or not (q.device == k.device == v.device):
@@ -456,12 +478,15 @@ def quant_qkv_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqle
     rq, sq, rk, sk = varlen_rows(total_q, B), varlen_slots(total_q, B), varlen_rows(total_k, B), varlen_slots(total_k, B)
     qk = out_qk
     if qk is None:
+        thr = gran == "thread"
         qk = QKQuantVarlen(torch.empty(Hq, rq, max(Dp, 1), dtype=torch.int8, device=dev),
-                           torch.empty(Hq, sq, dtype=torch.float32, device=dev),
+                           torch.empty(Hq, rq if thr else sq, dtype=torch.float32, device=dev),
                            torch.empty(Hkv, rk, max(Dp, 1), dtype=torch.int8, device=dev),
-                           torch.empty(Hkv, sk, dtype=torch.float32, device=dev),
+                           torch.empty((Hkv, sk, 2) if thr else (Hkv, sk), dtype=torch.float32, device=dev),
                            torch.empty(B, Hkv, D, dtype=torch.float32, device=dev), cq, ck, B, Hq, Hkv, total_q,
-                           total_k, int(max_seqlen_q), int(max_seqlen_k), D)
+                           total_k, int(max_seqlen_q), int(max_seqlen_k), D, gran)
+    elif qk.gran != gran:
+        raise ValueError("out_qk was allocated for another granularity")
     vq = out_v
     if vq is None:
         elt = 1 if pv == "fp8" else 2
@@ -473,7 +498,7 @@ def quant_qkv_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqle
         workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=dev)
     _check(L.sage_quant_qkv_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), _DT[q.dtype], cq.data_ptr(),
                                    ck.data_ptr(), B, Hq, Hkv, total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), D,
-                                   _PV[pv], qk.q_i8.data_ptr(), qk.q_scale.data_ptr(), qk.k_i8.data_ptr(),
+                                   _PV[pv], _GRAN[gran], qk.q_i8.data_ptr(), qk.q_scale.data_ptr(), qk.k_i8.data_ptr(),
                                    qk.k_scale.data_ptr(), qk.k_mean.data_ptr(), vq.v_hat.data_ptr(),
                                    _ptr(vq.v_scale), workspace.data_ptr(), workspace.numel(), _stream(dev)))
     return qk, vq
@@ -491,18 +516,22 @@ def attn_fwd_varlen(qk: QKQuantVarlen, vq: VQuantVarlen, out_dtype: torch.dtype,
     dev = qk.q_i8.device
     if out is None:
         out = torch.empty(qk.total_q, qk.Hq, qk.D, dtype=out_dtype, device=dev)
-    _check(lib().sage_attn_fwd_varlen(qk.q_i8.data_ptr(), qk.q_scale.data_ptr(), qk.k_i8.data_ptr(),
-                                      qk.k_scale.data_ptr(), vq.v_hat.data_ptr(), _ptr(vq.v_scale), out.data_ptr(),
-                                      _DT[out_dtype], qk.cu_q.data_ptr(), qk.cu_k.data_ptr(), qk.B, qk.Hq, qk.Hkv,
-                                      qk.total_q, qk.total_kv, qk.max_q, qk.max_k, qk.D, int(bool(is_causal)),
-                                      float(sm_scale), _PV[vq.pv], _ACC[accum], _stream(dev)))
+    args = (qk.q_i8.data_ptr(), qk.q_scale.data_ptr(), qk.k_i8.data_ptr(), qk.k_scale.data_ptr(), vq.v_hat.data_ptr(),
+            _ptr(vq.v_scale), out.data_ptr(), _DT[out_dtype], qk.cu_q.data_ptr(), qk.cu_k.data_ptr(), qk.B, qk.Hq,
+            qk.Hkv, qk.total_q, qk.total_kv, qk.max_q, qk.max_k, qk.D, int(bool(is_causal)), float(sm_scale),
+            _PV[vq.pv], _ACC[accum])
+    if qk.gran == "block":
+        _check(lib().sage_attn_fwd_varlen(*args, _stream(dev)))
+    else:
+        _check(lib().sage_attn_fwd_varlen_g(*args, _GRAN[qk.gran], _stream(dev)))
     return out
 
 
 def sageattn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
                     cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, is_causal: bool = False,
-                    sm_scale: Optional[float] = None, pv: str = "fp16", accum: str = "fp32") -> torch.Tensor:
+                    sm_scale: Optional[float] = None, pv: str = "fp16", accum: str = "fp32",
+                    qk_gran: str = "block") -> torch.Tensor:
     """Attention over a packed batch of sequences of different lengths (each sequence
     attends only to its own keys); returns q's dtype, shape (total_q, Hq, D)."""
-    qk, vq = quant_qkv_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, pv)
+    qk, vq = quant_qkv_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, pv, gran=qk_gran)
     return attn_fwd_varlen(qk, vq, q.dtype, is_causal, sm_scale, accum)

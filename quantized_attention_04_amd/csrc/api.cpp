@@ -241,9 +241,11 @@ size_t sage_quant_qkv_workspace_bytes(int B, int H_kv, int Nkv, int D, sage_pv p
 }
 
 sage_status sage_quant_qkv(const void* q, const void* k, const void* v, sage_dtype dtype, sage_layout layout, int B,
-                           int H_qo, int H_kv, int Nq, int Nkv, int D, sage_pv pv, int8_t* q_i8, float* q_scale,
-                           int8_t* k_i8, float* k_scale, float* k_mean, void* v_hat, float* v_scale, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+                           int H_qo, int H_kv, int Nq, int Nkv, int D, sage_pv pv, sage_qk_gran gran, int8_t* q_i8,
+                           float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean, void* v_hat, float* v_scale,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    if (gran != SAGE_GRAN_BLOCK && gran != SAGE_GRAN_THREAD)
+        return fail(SAGE_ERR_INVALID_ARG, "bad quantisation granularity %d", int(gran));
     sage_status s = check_qkv_args(q, k, v, dtype, pv, q_i8, q_scale, k_i8, k_scale, k_mean, v_hat, v_scale,
                                    "sage_quant_qkv");
     if (s != SAGE_OK) return s;
@@ -263,6 +265,7 @@ sage_status sage_quant_qkv(const void* q, const void* k, const void* v, sage_dty
     a.B = B, a.Hq = H_qo, a.Hkv = H_kv, a.Nq = Nq, a.Nkv = Nkv, a.D = D;
     a.q_i8 = q_i8, a.q_scale = q_scale, a.k_i8 = k_i8, a.k_scale = k_scale, a.k_mean = k_mean;
     a.workspace = workspace;
+    a.thread_gran = gran == SAGE_GRAN_THREAD;
     sage::QuantVArgs va{};
     va.v = v;
     va.fp8 = pv == SAGE_PV_FP8;
@@ -274,6 +277,16 @@ sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t
                           const void* v_hat, const float* v_scale, void* out, sage_dtype out_dtype,
                           sage_layout out_layout, int B, int H_qo, int H_kv, int Nq, int Nkv, int D, int is_causal,
                           float sm_scale, sage_pv pv, sage_accum accum, void* stream) {
+    return sage_attn_fwd_g(q_i8, q_scale, k_i8, k_scale, v_hat, v_scale, out, out_dtype, out_layout, B, H_qo, H_kv,
+                           Nq, Nkv, D, is_causal, sm_scale, pv, accum, SAGE_GRAN_BLOCK, stream);
+}
+
+sage_status sage_attn_fwd_g(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                            const void* v_hat, const float* v_scale, void* out, sage_dtype out_dtype,
+                            sage_layout out_layout, int B, int H_qo, int H_kv, int Nq, int Nkv, int D, int is_causal,
+                            float sm_scale, sage_pv pv, sage_accum accum, sage_qk_gran gran, void* stream) {
+    if (gran != SAGE_GRAN_BLOCK && gran != SAGE_GRAN_THREAD)
+        return fail(SAGE_ERR_INVALID_ARG, "bad quantisation granularity %d", int(gran));
     sage_status s = check_attn_args(q_i8, q_scale, k_i8, k_scale, v_hat, v_scale, out, out_dtype, is_causal, sm_scale,
                                     pv, accum, D, "sage_attn_fwd");
     if (s != SAGE_OK) return s;
@@ -293,6 +306,7 @@ sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t
     a.sm_scale = sm_scale;
     a.fp8 = pv == SAGE_PV_FP8;
     a.two_level = accum == SAGE_ACC_FP16_FP32;
+    a.thread_gran = gran == SAGE_GRAN_THREAD;
     return launch_status(sage::launch_attn_fwd(a, (hipStream_t)stream), "sage_attn_fwd");
 }
 
@@ -390,8 +404,11 @@ size_t sage_quant_qkv_varlen_workspace_bytes(int B, int H_kv, int total_kv, int 
 sage_status sage_quant_qkv_varlen(const void* q, const void* k, const void* v, sage_dtype dtype,
                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int B, int H_qo, int H_kv,
                                   int total_q, int total_kv, int max_seqlen_q, int max_seqlen_kv, int D, sage_pv pv,
-                                  int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
-                                  void* v_hat, float* v_scale, void* workspace, size_t workspace_bytes, void* stream) {
+                                  sage_qk_gran gran, int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
+                                  float* k_mean, void* v_hat, float* v_scale, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+    if (gran != SAGE_GRAN_BLOCK && gran != SAGE_GRAN_THREAD)
+        return fail(SAGE_ERR_INVALID_ARG, "bad quantisation granularity %d", int(gran));
     sage_status s = check_qkv_args(q, k, v, dtype, pv, q_i8, q_scale, k_i8, k_scale, k_mean, v_hat, v_scale,
                                    "sage_quant_qkv_varlen");
     if (s != SAGE_OK) return s;
@@ -411,6 +428,7 @@ sage_status sage_quant_qkv_varlen(const void* q, const void* k, const void* v, s
     a.cu_q = cu_seqlens_q, a.cu_k = cu_seqlens_kv, a.total_q = total_q, a.total_k = total_kv;
     a.q_i8 = q_i8, a.q_scale = q_scale, a.k_i8 = k_i8, a.k_scale = k_scale, a.k_mean = k_mean;
     a.workspace = workspace;
+    a.thread_gran = gran == SAGE_GRAN_THREAD;
     sage::QuantVArgs va{};
     va.v = v;
     va.fp8 = pv == SAGE_PV_FP8;
@@ -423,6 +441,19 @@ sage_status sage_attn_fwd_varlen(const int8_t* q_i8, const float* q_scale, const
                                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int B, int H_qo, int H_kv,
                                  int total_q, int total_kv, int max_seqlen_q, int max_seqlen_kv, int D, int is_causal,
                                  float sm_scale, sage_pv pv, sage_accum accum, void* stream) {
+    return sage_attn_fwd_varlen_g(q_i8, q_scale, k_i8, k_scale, v_hat, v_scale, out, out_dtype, cu_seqlens_q,
+                                  cu_seqlens_kv, B, H_qo, H_kv, total_q, total_kv, max_seqlen_q, max_seqlen_kv, D,
+                                  is_causal, sm_scale, pv, accum, SAGE_GRAN_BLOCK, stream);
+}
+
+sage_status sage_attn_fwd_varlen_g(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                                   const void* v_hat, const float* v_scale, void* out, sage_dtype out_dtype,
+                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int B, int H_qo,
+                                   int H_kv, int total_q, int total_kv, int max_seqlen_q, int max_seqlen_kv, int D,
+                                   int is_causal, float sm_scale, sage_pv pv, sage_accum accum, sage_qk_gran gran,
+                                   void* stream) {
+    if (gran != SAGE_GRAN_BLOCK && gran != SAGE_GRAN_THREAD)
+        return fail(SAGE_ERR_INVALID_ARG, "bad quantisation granularity %d", int(gran));
     sage_status s = check_attn_args(q_i8, q_scale, k_i8, k_scale, v_hat, v_scale, out, out_dtype, is_causal, sm_scale,
                                     pv, accum, D, "sage_attn_fwd_varlen");
     if (s != SAGE_OK) return s;
@@ -440,6 +471,7 @@ sage_status sage_attn_fwd_varlen(const int8_t* q_i8, const float* q_scale, const
     a.fp8 = pv == SAGE_PV_FP8;
     a.two_level = accum == SAGE_ACC_FP16_FP32;
     a.cu_q = cu_seqlens_q, a.cu_k = cu_seqlens_kv, a.total_q = total_q, a.total_k = total_kv;
+    a.thread_gran = gran == SAGE_GRAN_THREAD;
     return launch_status(sage::launch_attn_fwd(a, (hipStream_t)stream), "sage_attn_fwd_varlen");
 }
 

@@ -244,9 +244,11 @@ struct PPack<false> {
 // and p = 0.  t = S32 * c - m is formed with one rounding (fma), keeping P's rounding
 // to FP16 / e4m3 close to a correctly rounded evaluation.
 // kmax: the last key this lane's query may see when causal.
-template <bool FP8, bool MASK, bool CAUSAL>
-__device__ __forceinline__ float softmax_tile(v16i (&S)[2], PPack<FP8>& pk, float c, float& m, float& l, int g,
-                                              int key0, int kmax, int Nkv) {
+// c0, c1: dequantisation factors of score tiles 0 and 1 (equal unless K carries one
+// scale per 32 keys with FP16 P.V, whose tile kt holds keys 32 kt .. 32 kt + 31).
+template <bool FP8, bool MASK, bool CAUSAL, bool C2 = false>
+__device__ __forceinline__ float softmax_tile(v16i (&S)[2], PPack<FP8>& pk, float c0, float c1, float& m, float& l,
+                                              int g, int key0, int kmax, int Nkv) {
     int tvis = 0;  // MASK: register r of tile kt is visible iff key_of_reg(kt, 0, r) < tvis
     if constexpr (MASK) {
         // key key0 + key_of_reg(kt, g, r) is visible iff it is below min(Nkv, kmax + 1)
@@ -274,8 +276,16 @@ __device__ __forceinline__ float softmax_tile(v16i (&S)[2], PPack<FP8>& pk, floa
         for (int r = 3; r + 1 < 16; r += 2) a = max(max(a, S[kt][r]), S[kt][r + 1]);
         mxk[kt] = max(a, S[kt][15]);
     }
-    const int mx = max(mxk[0], mxk[1]);
-    float tmax = (MASK && mx == INT32_MIN) ? -1e30f : float(mx) * c;
+    float tmax;
+    if constexpr (C2) {
+        // each tile's maximum with its own factor (float(S) * c is monotone in S)
+        const float t0 = (MASK && mxk[0] == INT32_MIN) ? -1e30f : float(mxk[0]) * c0;
+        const float t1 = (MASK && mxk[1] == INT32_MIN) ? -1e30f : float(mxk[1]) * c1;
+        tmax = fmaxf(t0, t1);
+    } else {
+        const int mx = max(mxk[0], mxk[1]);
+        tmax = (MASK && mx == INT32_MIN) ? -1e30f : float(mx) * c0;
+    }
     tmax = halves_max(tmax);
     const float mnew = fmaxf(m, tmax);
     const float alpha = __builtin_amdgcn_exp2f(m - mnew);
@@ -288,7 +298,7 @@ __device__ __forceinline__ float softmax_tile(v16i (&S)[2], PPack<FP8>& pk, floa
         float q[4];
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-            q[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(float(S[kt][r0 + e]), c, negm));
+            q[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(float(S[kt][r0 + e]), kt ? c1 : c0, negm));
             // the same predicate as above (compiled to a scalar-mask select, not VCC)
             if constexpr (MASK) q[e] = key_of_reg<FP8>(kt, 0, r0 + e) < tvis ? q[e] : 0.0f;
             acc[e] = w == 0 ? q[e] : acc[e] + q[e];
@@ -348,7 +358,10 @@ struct KParams {
     float cscale;  // sm_scale * log2(e)
 };
 
-template <int DP, bool FP8, bool CAUSAL, bool OBF16>
+// TG: the per-thread scales of sage_quant_qkv -- q_scale per token (indexed like the
+// rows of q_i8), k_scale per 32 keys ([slot][2]) -- so the dequantisation factor is
+// per lane: the lane's query, and its lane half's keys (FP8) or the tile's keys (FP16).
+template <int DP, bool FP8, bool CAUSAL, bool OBF16, bool TG = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8>::OCC, Cfg<DP, FP8>::OCC))) void attn_fwd_kernel(KParams p) {
     using C = Cfg<DP, FP8>;
     // NST LDS stages: tile j lives in stage j % NST while tiles j+1 .. j+NST-1 stream in.
@@ -397,7 +410,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
     float sq = 0.0f;
     if (active) {
         load_q_frags<C>(qf, p.q_i8 + (qv.row0 + q0) * DP, lane);
-        sq = scalar_load_f32(p.q_scale + qv.slot0 + qb);
+        if constexpr (TG) sq = p.q_scale[qv.row0 + qidx];  // 0 for padding rows
+        else sq = scalar_load_f32(p.q_scale + qv.slot0 + qb);
     } else {
 #pragma unroll
         for (int s = 0; s < C::KS; s++) qf[s] = v4i{0, 0, 0, 0};
@@ -433,7 +447,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
 #pragma unroll
     for (int t = 0; t < AHEAD; t++)
         if (t < jend) issue_tile(t);
-    float ks_next = jend > 0 ? scalar_load_f32(ks_row) : 0.0f;
+    // K scale(s) of the next tile, loaded one tile ahead (TG: the two 32-key halves)
+    float ks_next = 0.0f, ks_next1 = 0.0f;
+    if (jend > 0) {
+        if constexpr (TG) {
+            ks_next = scalar_load_f32(p.k_scale + 2 * kv.slot0);
+            ks_next1 = scalar_load_f32(p.k_scale + 2 * kv.slot0 + 1);
+        } else {
+            ks_next = scalar_load_f32(ks_row);
+        }
+    }
     auto step = [&](auto masked, int j) {
         constexpr bool MASK = decltype(masked)::value;
         // tile j landed for this wave (later tiles may still stream); the barrier
@@ -443,8 +466,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
         else wait_vmcnt<0>();
         block_barrier();
         if (j + AHEAD < jend) issue_tile(j + AHEAD);
-        const float c = sq * ks_next * p.cscale;
-        ks_next = scalar_load_f32(ks_row + min(j + 1, NBk - 1));
+        float c0, c1;
+        if constexpr (TG) {
+            const float a0 = sq * ks_next * p.cscale, a1 = sq * ks_next1 * p.cscale;
+            // FP8: lane half g holds keys 32 g .. 32 g + 31; FP16: tile kt holds 32 kt ..
+            c0 = FP8 ? (g ? a1 : a0) : a0;
+            c1 = FP8 ? c0 : a1;
+            const int jn = min(j + 1, NBk - 1);
+            ks_next = scalar_load_f32(p.k_scale + 2 * (kv.slot0 + jn));
+            ks_next1 = scalar_load_f32(p.k_scale + 2 * (kv.slot0 + jn) + 1);
+        } else {
+            c0 = c1 = sq * ks_next * p.cscale;
+            ks_next = scalar_load_f32(ks_row + min(j + 1, NBk - 1));
+        }
         // a tile no query of this wave may see (causal: beyond the wave's last query's
         // horizon) leaves m, l and O unchanged: take part in the pipeline only
         if constexpr (MASK && CAUSAL)
@@ -454,7 +488,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
         v16i S[2];
         qk_tile<C, FP8>(st, qf, S, lane);
         PPack<FP8> pk;
-        const float alpha = softmax_tile<FP8, MASK, CAUSAL>(S, pk, c, m, l, g, j * kBlk, qidx + off, Nkv);
+        const float alpha =
+            softmax_tile<FP8, MASK, CAUSAL, TG && !FP8>(S, pk, c0, c1, m, l, g, j * kBlk, qidx + off, Nkv);
         if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
             for (int dt = 0; dt < C::DT; dt++) O[dt] *= alpha;
@@ -540,10 +575,10 @@ __global__ __launch_bounds__(256) void debug_qk_kernel(const int8_t* __restrict_
         for (int r = 0; r < 16; r++) o[(wave * C::QW + i) * kBlk + key_of_reg<FP8>(kt, g, r)] = S[kt][r];
 }
 
-template <int DP, bool FP8, bool CAUSAL, bool OBF16>
+template <int DP, bool FP8, bool CAUSAL, bool OBF16, bool TG>
 hipError_t launch_attn_t(const KParams& p, int nwg, hipStream_t s) {
     using C = Cfg<DP, FP8>;
-    auto kern = attn_fwd_kernel<DP, FP8, CAUSAL, OBF16>;
+    auto kern = attn_fwd_kernel<DP, FP8, CAUSAL, OBF16, TG>;
     hipLaunchKernelGGL(kern, dim3(nwg), dim3(C::THREADS), 0, s, p);
     return hipGetLastError();
 }
@@ -551,12 +586,16 @@ hipError_t launch_attn_t(const KParams& p, int nwg, hipStream_t s) {
 template <int DP, bool FP8>
 hipError_t dispatch_rest(const AttnArgs& a, const KParams& p, int nwg, hipStream_t s) {
     // both accumulation modes use the MFMA-chained fp32 accumulation (see the header)
-    const int key = (a.causal ? 2 : 0) | (a.out_bf16 ? 1 : 0);
+    const int key = (a.thread_gran ? 4 : 0) | (a.causal ? 2 : 0) | (a.out_bf16 ? 1 : 0);
     switch (key) {
-    case 0: return launch_attn_t<DP, FP8, false, false>(p, nwg, s);
-    case 1: return launch_attn_t<DP, FP8, false, true>(p, nwg, s);
-    case 2: return launch_attn_t<DP, FP8, true, false>(p, nwg, s);
-    default: return launch_attn_t<DP, FP8, true, true>(p, nwg, s);
+    case 0: return launch_attn_t<DP, FP8, false, false, false>(p, nwg, s);
+    case 1: return launch_attn_t<DP, FP8, false, true, false>(p, nwg, s);
+    case 2: return launch_attn_t<DP, FP8, true, false, false>(p, nwg, s);
+    case 3: return launch_attn_t<DP, FP8, true, true, false>(p, nwg, s);
+    case 4: return launch_attn_t<DP, FP8, false, false, true>(p, nwg, s);
+    case 5: return launch_attn_t<DP, FP8, false, true, true>(p, nwg, s);
+    case 6: return launch_attn_t<DP, FP8, true, false, true>(p, nwg, s);
+    default: return launch_attn_t<DP, FP8, true, true, true>(p, nwg, s);
     }
 }
 

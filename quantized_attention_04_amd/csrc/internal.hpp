@@ -21,6 +21,7 @@ struct QuantQKArgs {
     float* k_scale;
     float* k_mean;
     void* workspace;
+    int thread_gran;  // 1: one Q scale per token and one K scale per 32 keys (else per 64)
 };
 
 struct QuantVArgs {
@@ -51,6 +52,7 @@ struct AttnArgs {
     const int32_t* cu_q;
     const int32_t* cu_k;
     int total_q, total_k;
+    int thread_gran;  // scales of sage_quant_qkv's per-thread granularity
 };
 
 struct DebugQKArgs {

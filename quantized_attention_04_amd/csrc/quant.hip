@@ -80,16 +80,21 @@ __global__ __launch_bounds__(64) void k_mean_final_kernel(const double* __restri
 // INT8 block quantisation.  One wave per 64-token block of one (b, head): grid
 // (ceil(max blocks / 4), H, B), 4 waves per workgroup.  Lane l covers 8 consecutive
 // channels (chunk l % CH, CH = Dp / 8) of the token rows l / CH + p * (64 / CH),
-// p = 0 .. CH-1.
-//   y = x (Q) or fp32(x - mean[c]) (K); amax = max |y|; scale = amax / 127;
-//   inv = 127 / amax; code = clamp(rne(y * inv), -127, 127).
-template <bool BF16, int DP, bool VEC8, bool SMOOTH>
+// p = 0 .. CH-1.  One scale per group of G tokens of the block:
+//   y = x (Q) or fp32(x - mean[c]) (K); amax = max |y| over the group; scale =
+//   amax / 127; inv = 127 / amax; code = clamp(rne(y * inv), -127, 127).
+// G = 64: scale[slot]; G = 32: scale[2 slot + half]; G = 1: scale[row] (one per
+// token: the rows of xq, padding rows 0).  G = 1 and 32 are the finer "per-thread"
+// groups (SageAttention project README, "Project Updates" v2.0.1): a query column
+// of the score MFMA per lane, the 32 keys of a half-wave.
+template <bool BF16, int DP, bool VEC8, bool SMOOTH, int G = 64>
 __device__ __forceinline__ void quant_block_wave(const uint16_t* __restrict__ x, const SeqMap& m, int D,
                                                  const float* __restrict__ mean, int8_t* __restrict__ xq,
                                                  float* __restrict__ scale, int j, int h, int b, int lane) {
     constexpr int CH = DP / 8;        // 8-channel chunks per row
     constexpr int RPP = kWave / CH;   // rows per pass
     constexpr int PASSES = kBlk / RPP;
+    static_assert(G == 64 || G == 32 || G == 1, "token groups of 64, 32 or 1");
     const SeqView sv = seq_view(m, b, h);
     if (j * kBlk >= sv.n) return;  // this wave: past the sequence's end
     const int N = sv.n;
@@ -119,51 +124,102 @@ __device__ __forceinline__ void quant_block_wave(const uint16_t* __restrict__ x,
         }
         raw[p] = r;
     }
-    // amax over the block's real elements (a full block of whole chunks needs no
+    auto yval = [&](int p, int e) {
+        return SMOOTH ? in_to_f32<BF16>(raw[p][e]) - mu[e] : in_to_f32<BF16>(raw[p][e]);
+    };
+    // per-pass amax of this lane's real elements (a full block of whole chunks needs no
     // per-element test: channel padding holds y = 0)
     const bool full = VEC8 && (j + 1) * kBlk <= N;
-    float amax = 0.0f;
+    float am[PASSES];
     if (full) {
 #pragma unroll
-        for (int p = 0; p < PASSES; p++)
+        for (int p = 0; p < PASSES; p++) {
+            am[p] = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 8; e++) {
-                const float y = SMOOTH ? in_to_f32<BF16>(raw[p][e]) - mu[e] : in_to_f32<BF16>(raw[p][e]);
-                amax = fmaxf(amax, fabsf(y));
-            }
+            for (int e = 0; e < 8; e++) am[p] = fmaxf(am[p], fabsf(yval(p, e)));
+        }
     } else {
 #pragma unroll
         for (int p = 0; p < PASSES; p++) {
             const int t = j * kBlk + p * RPP + r0;
+            am[p] = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 8; e++) {
-                if (t < N && c0 + e < D) {
-                    const float y = SMOOTH ? in_to_f32<BF16>(raw[p][e]) - mu[e] : in_to_f32<BF16>(raw[p][e]);
-                    amax = fmaxf(amax, fabsf(y));
-                }
-            }
+            for (int e = 0; e < 8; e++)
+                if (t < N && c0 + e < D) am[p] = fmaxf(am[p], fabsf(yval(p, e)));
         }
     }
-    amax = wave_max(amax);
-    const bool zero = !(amax > 0.0f);
-    const float sc = zero ? 0.0f : amax / 127.0f;
-    const float inv = zero ? 0.0f : 127.0f / amax;
-    if (lane == 0) scale[sv.slot0 + j] = sc;
-    if (full && amax <= 3.4e38f && inv <= 3.4e38f) {
-        // Full block, whole 8-channel chunks, finite amax and inv (wave-uniform): every
-        // element of the tile is real, channel padding reads as x = 0 with mean 0, so
-        // y = 0 there.  |fp32(y * inv)| <= 127 (1 + 2^-23) by construction, so the
-        // clamp is inert, and adding 1.5 * 2^23 rounds the product to an integer (ties
-        // to even) held in the low mantissa bits: its low byte is the two's-complement
-        // code.  Same codes as the general path below, at a quarter of the instructions.
+    // the amax of each pass's group
+    if constexpr (G == 64) {
+        float a = 0.0f;
+#pragma unroll
+        for (int p = 0; p < PASSES; p++) a = fmaxf(a, am[p]);
+        a = wave_max(a);
+#pragma unroll
+        for (int p = 0; p < PASSES; p++) am[p] = a;
+    } else if constexpr (G == 32) {
+        float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+        for (int p = 0; p < PASSES; p++) {
+            if (p * RPP < 32) a0 = fmaxf(a0, am[p]);
+            else a1 = fmaxf(a1, am[p]);
+        }
+        a0 = wave_max(a0);
+        a1 = wave_max(a1);
+#pragma unroll
+        for (int p = 0; p < PASSES; p++) am[p] = p * RPP < 32 ? a0 : a1;
+    } else {
+        // one row = CH consecutive lanes
+#pragma unroll
+        for (int p = 0; p < PASSES; p++)
+#pragma unroll
+            for (int o = CH / 2; o >= 1; o >>= 1) am[p] = fmaxf(am[p], __shfl_xor(am[p], o, 64));
+    }
+    // scale and inv once per group (the divisions are IEEE, so not cheap)
+    float inv[PASSES];
+    bool finite = true;
+    auto group_scale = [&](float a, float& iv) {
+        const bool zero = !(a > 0.0f);
+        iv = zero ? 0.0f : 127.0f / a;
+        finite = finite && a <= 3.4e38f && iv <= 3.4e38f;
+        return zero ? 0.0f : a / 127.0f;
+    };
+    if constexpr (G == 1) {
+#pragma unroll
+        for (int p = 0; p < PASSES; p++) {
+            const float sc = group_scale(am[p], inv[p]);
+            if (ch == 0) scale[sv.row0 + j * kBlk + p * RPP + r0] = sc;
+        }
+    } else if constexpr (G == 32) {
+        float i0, i1;
+        const float s0 = group_scale(am[0], i0), s1 = group_scale(am[PASSES - 1], i1);
+        if (lane == 0) {
+            scale[(sv.slot0 + j) * 2] = s0;
+            scale[(sv.slot0 + j) * 2 + 1] = s1;
+        }
+#pragma unroll
+        for (int p = 0; p < PASSES; p++) inv[p] = p * RPP < 32 ? i0 : i1;
+    } else {
+        float i0;
+        const float s0 = group_scale(am[0], i0);
+        if (lane == 0) scale[sv.slot0 + j] = s0;
+#pragma unroll
+        for (int p = 0; p < PASSES; p++) inv[p] = i0;
+    }
+    if (full && __builtin_amdgcn_ballot_w64(!finite) == 0) {
+        // Full block, whole 8-channel chunks, finite amax and inv everywhere (a
+        // wave-uniform test): every element of the tile is real, channel padding reads
+        // as x = 0 with mean 0, so y = 0 there.  |fp32(y * inv)| <= 127 (1 + 2^-23) by
+        // construction, so the clamp is inert, and adding 1.5 * 2^23 rounds the product
+        // to an integer (ties to even) held in the low mantissa bits: its low byte is
+        // the two's-complement code.  Same codes as the general path below, at a
+        // quarter of the instructions.
         constexpr float kRound = 12582912.0f;
 #pragma unroll
         for (int p = 0; p < PASSES; p++) {
             uint32_t r[8];
 #pragma unroll
             for (int e = 0; e < 8; e++) {
-                const float y = SMOOTH ? in_to_f32<BF16>(raw[p][e]) - mu[e] : in_to_f32<BF16>(raw[p][e]);
-                const float t = y * inv;
+                const float t = yval(p, e) * inv[p];
                 r[e] = __float_as_uint(t + kRound);
             }
             // bytes 0 of r[0..3] and r[4..7] into one word each
@@ -183,9 +239,8 @@ __device__ __forceinline__ void quant_block_wave(const uint16_t* __restrict__ x,
 #pragma unroll
         for (int e = 0; e < 8; e++) {
             int code = 0;
-            if (!zero && t < N && c0 + e < D) {
-                const float y = SMOOTH ? in_to_f32<BF16>(raw[p][e]) - mu[e] : in_to_f32<BF16>(raw[p][e]);
-                float r = rintf(y * inv);
+            if (am[p] > 0.0f && t < N && c0 + e < D) {
+                float r = rintf(yval(p, e) * inv[p]);
                 // comparisons, not fminf/fmaxf: a NaN product stays NaN and converts to 0
                 r = r > 127.0f ? 127.0f : r;
                 r = r < -127.0f ? -127.0f : r;
@@ -197,13 +252,13 @@ __device__ __forceinline__ void quant_block_wave(const uint16_t* __restrict__ x,
         *(uint2*)dst = make_uint2(w[0], w[1]);
     }
 }
-template <bool BF16, int DP, bool VEC8, bool SMOOTH>
+template <bool BF16, int DP, bool VEC8, bool SMOOTH, int G = 64>
 __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __restrict__ x, SeqMap m, int D,
                                                            const float* __restrict__ mean, int8_t* __restrict__ xq,
                                                            float* __restrict__ scale) {
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    quant_block_wave<BF16, DP, VEC8, SMOOTH>(x, m, D, mean, xq, scale, blockIdx.x * 4 + wave, blockIdx.y, blockIdx.z,
-                                             lane);
+    quant_block_wave<BF16, DP, VEC8, SMOOTH, G>(x, m, D, mean, xq, scale, blockIdx.x * 4 + wave, blockIdx.y,
+                                                blockIdx.z, lane);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -344,7 +399,7 @@ __device__ __forceinline__ void kv_stats_block(const uint16_t* __restrict__ k, c
 // + nq4 * (h + Hq * b)); nkv take one K/V block each (j + NB * (h + H_kv * b)).  The
 // two kinds are spread evenly over the grid, so Q's read-write stream and the K/V
 // read streams run side by side.
-template <bool BF16, int DP, bool VEC8, bool VMAX>
+template <bool BF16, int DP, bool VEC8, bool VMAX, int QG>
 __global__ __launch_bounds__(256) void qkv_pass1_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                         const uint16_t* __restrict__ v, SeqMap mq, SeqMap mk, int D,
                                                         int nq, int nkv, int8_t* __restrict__ q_i8,
@@ -358,7 +413,7 @@ __global__ __launch_bounds__(256) void qkv_pass1_kernel(const uint16_t* __restri
         const int nq4 = (mq.NB + 3) / 4;
         const int x = a0 % nq4, h = (a0 / nq4) % mq.H, b = a0 / (nq4 * mq.H);
         const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-        quant_block_wave<BF16, DP, VEC8, false>(q, mq, D, nullptr, q_i8, q_scale, x * 4 + wave, h, b, lane);
+        quant_block_wave<BF16, DP, VEC8, false, QG>(q, mq, D, nullptr, q_i8, q_scale, x * 4 + wave, h, b, lane);
     } else {
         const int r = int(wg) - a1;
         const int j = r % mk.NB, h = (r / mk.NB) % mk.H, b = r / (mk.NB * mk.H);
@@ -516,7 +571,7 @@ hipError_t launch_v_t(const QuantVArgs& a, hipStream_t s) {
 
 }  // namespace
 
-template <bool BF16, int DP, bool VEC8>
+template <bool BF16, int DP, bool VEC8, int QG, int KG>
 hipError_t launch_qkv_t(const QuantQKArgs& a, const QuantVArgs& va, hipStream_t s) {
     const SeqMap mq = make_seq_map(a.layout_nhd, a.cu_q, a.B, a.Hq, a.Nq, a.total_q, a.D);
     const SeqMap mk = make_seq_map(a.layout_nhd, a.cu_k, a.B, a.Hkv, a.Nkv, a.total_k, a.D);
@@ -528,19 +583,19 @@ hipError_t launch_qkv_t(const QuantQKArgs& a, const QuantVArgs& va, hipStream_t 
     const int nq = ((mq.NB + 3) / 4) * a.Hq * a.B;
     const int nkv = mk.NB * a.Hkv * a.B;
     if (va.fp8) {
-        qkv_pass1_kernel<BF16, DP, VEC8, true><<<nq + nkv, 256, 0, s>>>(
+        qkv_pass1_kernel<BF16, DP, VEC8, true, QG><<<nq + nkv, 256, 0, s>>>(
             (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)va.v, mq, mk, a.D, nq, nkv, a.q_i8,
             a.q_scale, kpart, vpart);
         qkv_pass2_kernel<DP, true><<<(a.B * a.Hkv * DP + 63) / 64, 64, 0, s>>>(kpart, vpart, mk, a.B, a.D, a.k_mean,
                                                                              amax);
     } else {
-        qkv_pass1_kernel<BF16, DP, VEC8, false><<<nq + nkv, 256, 0, s>>>(
+        qkv_pass1_kernel<BF16, DP, VEC8, false, QG><<<nq + nkv, 256, 0, s>>>(
             (const uint16_t*)a.q, (const uint16_t*)a.k, nullptr, mq, mk, a.D, nq, nkv, a.q_i8, a.q_scale, kpart,
             nullptr);
         qkv_pass2_kernel<DP, false><<<(a.B * a.Hkv * DP + 63) / 64, 64, 0, s>>>(kpart, nullptr, mk, a.B, a.D,
                                                                               a.k_mean, nullptr);
     }
-    quant_blocks_kernel<BF16, DP, VEC8, true><<<dim3((mk.NB + 3) / 4, a.Hkv, a.B), 256, 0, s>>>(
+    quant_blocks_kernel<BF16, DP, VEC8, true, KG><<<dim3((mk.NB + 3) / 4, a.Hkv, a.B), 256, 0, s>>>(
         (const uint16_t*)a.k, mk, a.D, a.k_mean, a.k_i8, a.k_scale);
     if (va.fp8)
         quant_v_kernel<BF16, DP, VEC8, true><<<dim3(mk.NB, a.Hkv, a.B), DP * 2, 0, s>>>(
@@ -575,12 +630,19 @@ hipError_t launch_quant_v(const QuantVArgs& a, hipStream_t s) {
     return a.bf16 ? launch_v_dp<true>(a, s) : launch_v_dp<false>(a, s);
 }
 
+template <bool BF16, int QG, int KG>
+hipError_t launch_qkv_g(const QuantQKArgs& a, const QuantVArgs& v, hipStream_t s) {
+    const bool vec = (a.D % 8) == 0;
+    if (a.D <= 64)
+        return vec ? launch_qkv_t<BF16, 64, true, QG, KG>(a, v, s) : launch_qkv_t<BF16, 64, false, QG, KG>(a, v, s);
+    if (a.D <= 128)
+        return vec ? launch_qkv_t<BF16, 128, true, QG, KG>(a, v, s) : launch_qkv_t<BF16, 128, false, QG, KG>(a, v, s);
+    return vec ? launch_qkv_t<BF16, 256, true, QG, KG>(a, v, s) : launch_qkv_t<BF16, 256, false, QG, KG>(a, v, s);
+}
 template <bool BF16>
 hipError_t launch_qkv_dp(const QuantQKArgs& a, const QuantVArgs& v, hipStream_t s) {
-    const bool vec = (a.D % 8) == 0;
-    if (a.D <= 64) return vec ? launch_qkv_t<BF16, 64, true>(a, v, s) : launch_qkv_t<BF16, 64, false>(a, v, s);
-    if (a.D <= 128) return vec ? launch_qkv_t<BF16, 128, true>(a, v, s) : launch_qkv_t<BF16, 128, false>(a, v, s);
-    return vec ? launch_qkv_t<BF16, 256, true>(a, v, s) : launch_qkv_t<BF16, 256, false>(a, v, s);
+    // per-thread granularity: one Q scale per token, one K scale per 32 keys
+    return a.thread_gran ? launch_qkv_g<BF16, 1, 32>(a, v, s) : launch_qkv_g<BF16, 64, 64>(a, v, s);
 }
 
 hipError_t launch_quant_qkv(const QuantQKArgs& a, const QuantVArgs& v, hipStream_t s) {

@@ -28,9 +28,10 @@ def sm_scale_of(D: int) -> float:
 class Case:
     """Inputs (host + device), the GPU quantisation and the oracle quantisation."""
 
-    def __init__(self, w: si.Workload, dev: str = "cuda:0"):
+    def __init__(self, w: si.Workload, dev: str = "cuda:0", gran: str = "block"):
         self.w = w
-        note(f"[case] {w}")
+        self.gran = gran
+        note(f"[case] {w} gran={gran}")
         self.q, self.k, self.v = si.make_qkv(w)
         self.dq, self.dk, self.dv = (t.to(dev) for t in (self.q, self.k, self.v))
         self.qf, self.kf, self.vf = (oracle.to_hnd_f32(t, w.layout) for t in (self.q, self.k, self.v))
@@ -47,14 +48,14 @@ class Case:
     @property
     def oq(self) -> oracle.Quantized:
         if self._oq is None:
-            self._oq = oracle.quantize(self.qf, self.kf, self.vf, self.w.pv == "fp8")
+            self._oq = oracle.quantize(self.qf, self.kf, self.vf, self.w.pv == "fp8", self.gran)
         return self._oq
 
     def gpu_quant(self, fused: bool = False):
         note(f"[gpu] {'quant_qkv' if fused else 'quant_qk/quant_v'} {self.w.name} B{self.w.B} Hq{self.w.Hq} "
              f"Hkv{self.w.Hkv} Nq{self.w.Nq} Nkv{self.w.Nkv} D{self.w.D} {self.w.layout} pv={self.w.pv}")
-        if fused:
-            qk, vq = qa.quant_qkv(self.dq, self.dk, self.dv, self.w.layout, self.w.pv)
+        if fused or self.gran != "block":
+            qk, vq = qa.quant_qkv(self.dq, self.dk, self.dv, self.w.layout, self.w.pv, gran=self.gran)
         else:
             qk = qa.quant_qk(self.dq, self.dk, self.w.layout)
             vq = qa.quant_v(self.dv, self.w.layout, self.w.pv)
@@ -78,8 +79,18 @@ def check_quant_bit_exact(case: Case, qk, vq) -> None:
         g = g.cpu().numpy()
         np.testing.assert_array_equal(g[:, :, :N, :w.D], ref, err_msg=f"{name}_i8")
         assert not g[:, :, N:, :].any() and not g[:, :, :, w.D:].any(), f"{name}_i8 padding not zero"
-    np.testing.assert_array_equal(qk.q_scale.cpu().numpy(), o.q_scale, err_msg="q_scale")
-    np.testing.assert_array_equal(qk.k_scale.cpu().numpy(), o.k_scale, err_msg="k_scale")
+    if case.gran == "block":
+        np.testing.assert_array_equal(qk.q_scale.cpu().numpy(), o.q_scale, err_msg="q_scale")
+        np.testing.assert_array_equal(qk.k_scale.cpu().numpy(), o.k_scale, err_msg="k_scale")
+    else:
+        # per token [B, Hq, N_pad] (padding rows 0); per 32 keys [B, Hkv, NB, 2]
+        qs = qk.q_scale.cpu().numpy()
+        np.testing.assert_array_equal(qs[:, :, :w.Nq], o.q_scale, err_msg="q_scale (per token)")
+        assert not qs[:, :, w.Nq:].any()
+        ks = qk.k_scale.cpu().numpy().reshape(w.B, w.Hkv, -1)
+        ng = o.k_scale.shape[2]
+        np.testing.assert_array_equal(ks[:, :, :ng], o.k_scale, err_msg="k_scale (per 32 keys)")
+        assert not ks[:, :, ng:].any()
     # V^: [B, H, NB, Dp, 64] channel-major blocks -> [B, H, N_pad, Dp]
     B, H, NB = w.B, w.Hkv, qa.num_blocks(w.Nkv)
     raw = vq.v_hat.cpu()

@@ -85,12 +85,12 @@ def _detail():
 
 
 def _fused(**kw):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, layout=0, B=1, Hq=4, Hkv=2, Nq=128, Nkv=100, D=96, pv=1, q_i8=FAKE,
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, layout=0, B=1, Hq=4, Hkv=2, Nq=128, Nkv=100, D=96, pv=1, gran=0, q_i8=FAKE,
              q_scale=FAKE, k_i8=FAKE, k_scale=FAKE, k_mean=FAKE, v_hat=FAKE, v_scale=FAKE, ws=FAKE, ws_bytes=1 << 20,
              stream=None)
     a.update(kw)
     return qa.lib().sage_quant_qkv(a["q"], a["k"], a["v"], a["dtype"], a["layout"], a["B"], a["Hq"], a["Hkv"],
-                                   a["Nq"], a["Nkv"], a["D"], a["pv"], a["q_i8"], a["q_scale"], a["k_i8"],
+                                   a["Nq"], a["Nkv"], a["D"], a["pv"], a["gran"], a["q_i8"], a["q_scale"], a["k_i8"],
                                    a["k_scale"], a["k_mean"], a["v_hat"], a["v_scale"], a["ws"], a["ws_bytes"],
                                    a["stream"])
 
@@ -124,6 +124,7 @@ def test_fused_quant_workspace_sizes():
     ({"ws": None}, qa.SAGE_ERR_WORKSPACE),
     ({"ws_bytes": 4 * 96 * 8 + 4 * 128 * 4 + 2 * 128 * 4 - 1}, qa.SAGE_ERR_WORKSPACE),
     ({"ws": FAKE + 4}, qa.SAGE_ERR_WORKSPACE),
+    ({"gran": 2}, qa.SAGE_ERR_INVALID_ARG),
 ])
 def test_fused_quant_rejects(kw, code):
     assert _fused(**kw) == code
@@ -135,6 +136,18 @@ def test_fused_quant_fp16_takes_no_scale():
         pytest.skip("would launch kernels on fake pointers")
     assert _fused(pv=0, v_scale=None, ws_bytes=4 * 96 * 8) == qa.SAGE_ERR_DEVICE
     assert _fused() == qa.SAGE_ERR_DEVICE
+    assert _fused(gran=1) == qa.SAGE_ERR_DEVICE
+
+
+def test_attn_fwd_g_checks_granularity_first():
+    L = qa.lib()
+    args = [FAKE] * 7 + [0, 0, 1, 2, 2, 128, 128, 64, 0, 0.125, 1, 0]
+    assert L.sage_attn_fwd_g(*args, 5, None) == qa.SAGE_ERR_INVALID_ARG and "granularity" in _detail()
+    assert L.sage_attn_fwd_g(*args[:6], None, *args[7:], 1, None) == qa.SAGE_ERR_INVALID_ARG
+    if not torch.cuda.is_available():
+        assert L.sage_attn_fwd_g(*args, 1, None) == qa.SAGE_ERR_DEVICE
+    vargs = [FAKE] * 7 + [0, FAKE, FAKE, 2, 2, 2, 100, 100, 60, 60, 64, 0, 0.125, 1, 0]
+    assert L.sage_attn_fwd_varlen_g(*vargs, -1, None) == qa.SAGE_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("kw,code", [

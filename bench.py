@@ -64,19 +64,20 @@ def kernel_source_hash() -> str:
 class Runner:
     """Preallocated buffers for one workload; step() enqueues the three C-ABI calls."""
 
-    def __init__(self, qa, torch, q, k, v, w):
-        self.qa, self.torch, self.w = qa, torch, w
+    def __init__(self, qa, torch, q, k, v, w, gran: str = "block"):
+        self.qa, self.torch, self.w, self.gran = qa, torch, w, gran
         self.q, self.k, self.v = q, k, v
         dev = q.device
         L = qa.lib()
         nws = L.sage_quant_qkv_workspace_bytes(w.B, w.Hkv, w.Nkv, w.D, 1 if w.pv == "fp8" else 0)
         self.ws = torch.empty(max(8, nws), dtype=torch.uint8, device=dev)
-        self.qk, self.vq = qa.quant_qkv(q, k, v, w.layout, w.pv, workspace=self.ws)
+        self.qk, self.vq = qa.quant_qkv(q, k, v, w.layout, w.pv, workspace=self.ws, gran=gran)
         self.out = qa.attn_fwd(self.qk, self.vq, w.torch_dtype, w.layout, w.causal, None, w.accum)
 
     def quant(self):
         qa, w = self.qa, self.w
-        qa.quant_qkv(self.q, self.k, self.v, w.layout, w.pv, workspace=self.ws, out_qk=self.qk, out_v=self.vq)
+        qa.quant_qkv(self.q, self.k, self.v, w.layout, w.pv, workspace=self.ws, out_qk=self.qk, out_v=self.vq,
+                     gran=self.gran)
 
     def attn(self):
         qa, w = self.qa, self.w
@@ -218,6 +219,19 @@ def main():
     log(f"[bench] step {ms_step:.3f} ms  attn {ms_attn:.3f} ms ({attn_tops:.0f} TOPS, "
         f"{100 * achieved / PEAK_TOPS:.1f}% of peak)  quant {ms_quant:.3f} ms")
     del r
+
+    # ---------------------------------------------------------------- per-thread granularity
+    # the same workload with one Q scale per token and one K scale per 32 keys
+    if not args.no_sweep:
+        rt = Runner(qa, torch, q, k, v, w, gran="thread")
+        st, at, qt, _ = rt.time(args.sweep_steps, 3)
+        result["thread_gran"] = {"workload": "the headline workload with per-token Q and per-32-key K scales",
+                                 "step_tops": round(ops / (st * 1e-3) / 1e12, 1),
+                                 "attn_tops": round(ops / (at * 1e-3) / 1e12, 1),
+                                 "attn_ms": round(at, 4), "quant_ms": round(qt, 4)}
+        log(f"[bench] thread granularity: attn {at:.3f} ms = {result['thread_gran']['attn_tops']} TOPS, "
+            f"quant {qt:.3f} ms")
+        del rt
 
     # ---------------------------------------------------------------- sweep
     if not args.no_sweep:

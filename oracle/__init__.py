@@ -30,13 +30,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-FP16, BF16, E4M3 = 0, 1, 2
+FP16, BF16, E4M3, E2M1 = 0, 1, 2, 3
 BLK = 64
 
 _f32p = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
 _f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
 _i8p = np.ctypeslib.ndpointer(np.int8, flags="C_CONTIGUOUS")
 _i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
+_u8p = np.ctypeslib.ndpointer(np.uint8, flags="C_CONTIGUOUS")
 _i64p = np.ctypeslib.ndpointer(np.int64, flags="C_CONTIGUOUS")
 _L = ctypes.c_long
 
@@ -66,6 +67,16 @@ def lib() -> ctypes.CDLL:
                                      _L, _L, _L, ctypes.c_int, ctypes.c_double, _i64p, _L, _f64p, ctypes.c_void_p]
     L.orc_attn_exact.argtypes = [_f32p, _f32p, _f32p, _L, _L, _L, _L, _L, _L, ctypes.c_int, ctypes.c_double,
                                  _i64p, _L, _f64p]
+    L.orc_mx_exp.restype = ctypes.c_int
+    L.orc_mx_exp.argtypes = [ctypes.c_double]
+    L.orc_e2m1_value.restype = ctypes.c_double
+    L.orc_e2m1_value.argtypes = [ctypes.c_int]
+    L.orc_e2m1_code.restype = ctypes.c_int
+    L.orc_e2m1_code.argtypes = [ctypes.c_double]
+    L.orc_quant_mxfp4_rows.argtypes = [_f32p, ctypes.c_void_p, _L, _L, _L, _L, _u8p, _i32p]
+    L.orc_quant_mxfp4_tokens.argtypes = [_f32p, _L, _L, _L, _L, _u8p, _i32p]
+    L.orc_attn_emulate_mxfp4.argtypes = [_u8p, _i32p, _u8p, _i32p, _u8p, _i32p, _L, _L, _L, _L, _L, _L,
+                                         ctypes.c_int, ctypes.c_double, _i64p, _L, _f64p, ctypes.c_void_p]
     _lib = L
     return L
 
@@ -310,3 +321,90 @@ def attn_exact_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q, cu_k, c
         return attn_exact(_seq(q, cu_q, b), _seq(k, cu_k, b), _seq(v, cu_k, b), causal, sm_scale, local)
 
     return _per_sequence(rows, D, fn)
+
+
+# ----------------------------------------------------------------------------- microscaling FP4
+
+MX_BLOCK = 32
+E2M1_VALUES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def mx_exp(amax: float) -> int:
+    """Shared exponent of an MX block: floor(log2 amax) - 2, held to [-126, 127]."""
+    return int(lib().orc_mx_exp(float(amax)))
+
+
+def e2m1_decode(code) -> np.ndarray:
+    """Values of 4-bit E2M1 codes (sign bit 8)."""
+    c = np.asarray(code, np.int64)
+    mag = np.asarray(E2M1_VALUES)[c & 7]
+    return np.where(c & 8, -mag, mag)
+
+
+def quant_mxfp4_rows(x: np.ndarray, mean: Optional[np.ndarray] = None):
+    """Q or K (B, H, N, D) -> (codes uint8 [B,H,N,D], exponents int32 [B,H,N,ceil(D/32)]),
+    blocks of 32 channels per token; ``mean`` (B, H, D) is subtracted first (fp32)."""
+    B, H, N, D = x.shape
+    code = np.empty((B, H, N, D), np.uint8)
+    E = np.empty((B, H, N, (D + 31) // 32), np.int32)
+    mp = None
+    if mean is not None:
+        mean = np.ascontiguousarray(mean, np.float32)
+        assert mean.shape == (B, H, D)
+        mp = mean.ctypes.data_as(ctypes.c_void_p)
+    lib().orc_quant_mxfp4_rows(np.ascontiguousarray(x, np.float32), mp, B, H, N, D, code, E)
+    return code, E
+
+
+def quant_mxfp4_tokens(v: np.ndarray):
+    """V (B, H, N, D) -> (codes uint8 [B,H,D,N] channel-major, exponents int32
+    [B,H,D,ceil(N/32)]), blocks of 32 tokens per channel."""
+    B, H, N, D = v.shape
+    code = np.empty((B, H, D, N), np.uint8)
+    E = np.empty((B, H, D, (N + 31) // 32), np.int32)
+    lib().orc_quant_mxfp4_tokens(np.ascontiguousarray(v, np.float32), B, H, N, D, code, E)
+    return code, E
+
+
+def mx_dequant(code: np.ndarray, E: np.ndarray) -> np.ndarray:
+    """Dequantised values (float64) of codes whose last axis is blocked by 32."""
+    n = code.shape[-1]
+    scale = np.repeat(np.ldexp(1.0, E.astype(np.int64)), MX_BLOCK, axis=-1)[..., :n]
+    return e2m1_decode(code) * scale
+
+
+@dataclasses.dataclass
+class MXQuantized:
+    q_code: np.ndarray   # [B, Hq, Nq, D]
+    q_exp: np.ndarray    # [B, Hq, Nq, ceil(D/32)]
+    k_code: np.ndarray   # [B, Hkv, Nkv, D] (smoothed K)
+    k_exp: np.ndarray
+    k_mean: np.ndarray   # [B, Hkv, D]
+    v_code: np.ndarray   # [B, Hkv, D, Nkv]
+    v_exp: np.ndarray    # [B, Hkv, D, ceil(Nkv/32)]
+    Hq: int
+    Hkv: int
+
+
+def quantize_mxfp4(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> MXQuantized:
+    """q, k, v: float32 (B, H, N, D) arrays holding the exact fp16/bf16 inputs."""
+    mu = k_mean(k)
+    qc, qe = quant_mxfp4_rows(q)
+    kc, ke = quant_mxfp4_rows(k, mu)
+    vc, ve = quant_mxfp4_tokens(v)
+    return MXQuantized(qc, qe, kc, ke, mu, vc, ve, q.shape[1], k.shape[1])
+
+
+def attn_emulate_mxfp4(Q: MXQuantized, causal: bool, sm_scale: float, rows: np.ndarray,
+                       with_ambiguity: bool = False):
+    """Emulation of the microscaling FP4 scheme for rows (b, h, i); [R, D] float64
+    (and the per-element ambiguity allowance when asked)."""
+    B, Hq, Nq, D = Q.q_code.shape
+    Nkv = Q.k_code.shape[2]
+    rows = np.ascontiguousarray(rows, np.int64)
+    out = np.empty((len(rows), D), np.float64)
+    amb = np.empty((len(rows), D), np.float64) if with_ambiguity else None
+    lib().orc_attn_emulate_mxfp4(Q.q_code, Q.q_exp, Q.k_code, Q.k_exp, Q.v_code, Q.v_exp, B, Hq, Q.Hkv, Nq, Nkv, D,
+                                 int(bool(causal)), float(sm_scale), rows, len(rows), out,
+                                 amb.ctypes.data_as(ctypes.c_void_p) if amb is not None else None)
+    return (out, amb) if with_ambiguity else out

@@ -42,7 +42,7 @@
 
 #define BLK 64 /* token block: one quantisation scale per 64 consecutive tokens */
 
-int orc_version(void) { return 2; }
+int orc_version(void) { return 3; }
 
 int orc_threads(void) {
 #ifdef _OPENMP
@@ -59,15 +59,17 @@ int orc_threads(void) {
  *   fp16      p=11 emin=-14  max 65504
  *   bf16      p=8  emin=-126 max (2 - 2^-7) * 2^127
  *   e4m3fn    p=4  emin=-6   max 448 (OCP FP8 E4M3, no infinities)
+ *   e2m1      p=2  emin=0    max 6   (OCP FP4 E2M1: +-{0, .5, 1, 1.5, 2, 3, 4, 6})
  * With sat != 0 results beyond maxv clamp to +-maxv; otherwise they become
  * +-inf (fp16/bf16) or NaN (e4m3fn has no infinity).
  * ------------------------------------------------------------------------- */
-enum { ORC_FP16 = 0, ORC_BF16 = 1, ORC_E4M3 = 2 };
+enum { ORC_FP16 = 0, ORC_BF16 = 1, ORC_E4M3 = 2, ORC_E2M1 = 3 };
 
 static void fmt_params(int fmt, int* p, int* emin, double* maxv) {
     switch (fmt) {
     case ORC_FP16: *p = 11; *emin = -14; *maxv = 65504.0; break;
     case ORC_BF16: *p = 8; *emin = -126; *maxv = ldexp(2.0 - ldexp(1.0, -7), 127); break;
+    case ORC_E2M1: *p = 2; *emin = 0; *maxv = 6.0; break;
     default: *p = 4; *emin = -6; *maxv = 448.0; break;
     }
 }
@@ -443,5 +445,228 @@ void orc_attn_exact(const float* q, const float* k, const float* v, long B, long
         }
         for (long c = 0; c < D; c++) out[r * D + c] = wsum > 0.0 ? out[r * D + c] / wsum : 0.0;
         free(s);
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Microscaling FP4.  The SageAttention README (gittoolsai.com tool page, "Project
+ * Updates" and the citation list) names a microscaling FP4 attention for inference
+ * (SageAttention3) and gives nothing past that title.  Reading: the OCP Microscaling
+ * Formats (MX) v1.0 MXFP4 format, which is what gfx950's scaled matrix instructions
+ * consume, applied to both products of the scheme above:
+ *   block    32 consecutive elements along the contraction axis share one scale:
+ *            Q and the smoothed K per token along the channels, V per channel along
+ *            the tokens, P per query along 32 consecutive keys of a 64-key block;
+ *   scale    X = 2^E with E = floor(log2 amax) - 2 (2 is the largest E2M1 exponent),
+ *            held to [-126, 127]; a block with amax = 0 takes E = -126 and codes of
+ *            zero (with the sign of each zero);
+ *   element  e2m1(x / X): round to nearest, ties to even, saturating at 6 (so a block's
+ *            largest element may clip from [6, 8) X to 6 X); the sign is kept, also
+ *            for values that round to zero;
+ *   code     4 bits, sign bit 8 | index of the magnitude in {0, .5, 1, 1.5, 2, 3, 4, 6}.
+ * The attention itself is the scheme above with S = sum of dequantised Q * K products,
+ * P quantised per 32-key half block after the online-softmax step, and
+ * P.V = sum of dequantised P * V products.
+ * ------------------------------------------------------------------------- */
+static const double E2M1_MAG[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+int orc_mx_exp(double amax) {
+    if (!(amax > 0.0)) return -126;
+    int e2;
+    frexp(amax, &e2); /* amax = f * 2^e2, f in [0.5, 1): floor(log2 amax) = e2 - 1 */
+    int E = e2 - 1 - 2;
+    if (E < -126) E = -126;
+    if (E > 127) E = 127;
+    return E;
+}
+
+double orc_e2m1_value(int code) { return (code & 8 ? -1.0 : 1.0) * E2M1_MAG[code & 7]; }
+
+/* code of an E2M1 value (already rounded); the sign bit follows the sign of v, -0 included */
+int orc_e2m1_code(double v) {
+    double a = fabs(v);
+    int idx = 0;
+    for (int i = 0; i < 8; i++)
+        if (E2M1_MAG[i] == a) idx = i;
+    return (signbit(v) ? 8 : 0) | idx;
+}
+
+/* one block of n (<= 32) values: exponent and codes */
+static int mx_block(const double* x, long n, uint8_t* code) {
+    double amax = 0.0;
+    for (long i = 0; i < n; i++)
+        if (fabs(x[i]) > amax) amax = fabs(x[i]);
+    int E = orc_mx_exp(amax);
+    for (long i = 0; i < n; i++) {
+        double y = amax > 0.0 ? ldexp(x[i], -E) : x[i]; /* exact: a power-of-two scaling */
+        code[i] = (uint8_t)orc_e2m1_code(orc_round(y, ORC_E2M1, 1));
+    }
+    return E;
+}
+
+/* Q or K (B, H, N, D): blocks of 32 channels of each token; mean (B, H, D) or NULL is
+ * subtracted first in fp32.  code [B, H, N, D], E [B, H, N, ceil(D/32)]. */
+void orc_quant_mxfp4_rows(const float* x, const float* mean, long B, long H, long N, long D, uint8_t* code,
+                          int32_t* E) {
+    long nb = (D + 31) / 32;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (long b = 0; b < B; b++)
+        for (long h = 0; h < H; h++) {
+            double buf[32];
+            for (long t = 0; t < N; t++) {
+                const float* row = x + ((b * H + h) * N + t) * D;
+                for (long c0 = 0; c0 < D; c0 += 32) {
+                    long n = D - c0 < 32 ? D - c0 : 32;
+                    for (long i = 0; i < n; i++) {
+                        float v = row[c0 + i];
+                        if (mean) v = v - mean[(b * H + h) * D + c0 + i]; /* fp32 subtract */
+                        buf[i] = (double)v;
+                    }
+                    E[((b * H + h) * N + t) * nb + c0 / 32] =
+                        mx_block(buf, n, code + ((b * H + h) * N + t) * D + c0);
+                }
+            }
+        }
+}
+
+/* V (B, H, N, D): blocks of 32 tokens of each channel.  code [B, H, D, N] (channel
+ * major), E [B, H, D, ceil(N/32)]. */
+void orc_quant_mxfp4_tokens(const float* v, long B, long H, long N, long D, uint8_t* code, int32_t* E) {
+    long nb = (N + 31) / 32;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (long b = 0; b < B; b++)
+        for (long h = 0; h < H; h++) {
+            double buf[32];
+            for (long c = 0; c < D; c++)
+                for (long t0 = 0; t0 < N; t0 += 32) {
+                    long n = N - t0 < 32 ? N - t0 : 32;
+                    for (long i = 0; i < n; i++) buf[i] = (double)v[((b * H + h) * N + t0 + i) * D + c];
+                    E[((b * H + h) * D + c) * nb + t0 / 32] = mx_block(buf, n, code + ((b * H + h) * D + c) * N + t0);
+                }
+        }
+}
+
+/* P of one half block (n <= 32 values p = 2^t >= 0): the dequantised values ph, and
+ * for the ambiguity: per element the change that a different rounding decision would
+ * make when p / X sits within 2^-14 of a tie, or when the block maximum sits within
+ * 2^-14 of a power of two without being one exactly (a kernel computing p with a few
+ * ulps of error may then pick the neighbouring exponent), the change the other
+ * exponent makes.  A maximum from an integer t (the row maximum itself, t = 0) is
+ * exact on both sides. */
+static void mx_p_block(const double* p, const float* t, const int* vis, long n, double* ph, double* flip) {
+    double pmax = 0.0;
+    float tmax = -INFINITY;
+    for (long i = 0; i < n; i++) {
+        if (vis[i] && p[i] > pmax) pmax = p[i];
+        if (vis[i] && t[i] > tmax) tmax = t[i];
+    }
+    int E = orc_mx_exp(pmax);
+    int Ealt = E;
+    if (pmax > 0.0 && tmax != floorf(tmax)) {
+        int e2;
+        double f = frexp(pmax, &e2); /* f in [0.5, 1) */
+        if (f - 0.5 <= AMB_REL * pmax / ldexp(1.0, e2)) Ealt = E - 1;       /* just above 2^(e2-1) */
+        else if (1.0 - f <= AMB_REL) Ealt = E + 1;                         /* just below 2^e2 */
+        if (Ealt < -126 || Ealt > 127) Ealt = E;
+    }
+    for (long i = 0; i < n; i++) {
+        ph[i] = 0.0;
+        flip[i] = 0.0;
+        if (!vis[i] || pmax == 0.0) continue;
+        double y = ldexp(p[i], -E);
+        ph[i] = ldexp(orc_round(y, ORC_E2M1, 1), E);
+        flip[i] = ldexp(tie_flip(y, ORC_E2M1), E);
+        if (Ealt != E) {
+            double alt = ldexp(orc_round(ldexp(p[i], -Ealt), ORC_E2M1, 1), Ealt);
+            flip[i] += fabs(alt - ph[i]);
+        }
+    }
+}
+
+/* Emulation of the microscaling FP4 scheme for selected rows (b, h, i).
+ *   qc, kc: codes [B, H, N, D] with exponents qE, kE [B, H, N, ceil(D/32)];
+ *   vc: codes [B, Hkv, D, Nkv] with vE [B, Hkv, D, ceil(Nkv/32)].
+ * Scores: S = sum_d q * k over the dequantised values (fp64, exact for these
+ * operands), then, as for INT8, s2 = fp32(S) * fp32(sm_scale * log2 e) in fp32, the
+ * running max over 64-key blocks, p = fp32(2^(s2 - m)), l += p (unquantised),
+ * p quantised per 32-key half block, acc = alpha * acc + sum ph * v (fp64). */
+void orc_attn_emulate_mxfp4(const uint8_t* qc, const int32_t* qE, const uint8_t* kc, const int32_t* kE,
+                            const uint8_t* vc, const int32_t* vE, long B, long Hq, long Hkv, long Nq, long Nkv,
+                            long D, int causal, double sm_scale, const int64_t* rows, long R, double* out,
+                            double* amb) {
+    const float scale2 = (float)sm_scale * 1.44269504088896341f;
+    long group = Hq / Hkv, nbd = (D + 31) / 32, nbt = (Nkv + 31) / 32, nkb = (Nkv + BLK - 1) / BLK;
+    const long off = Nkv - Nq;
+    (void)B;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (long r = 0; r < R; r++) {
+        long b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+        long hk = h / group;
+        double* qd = (double*)malloc((size_t)D * sizeof(double));
+        double* acc = (double*)calloc((size_t)D, sizeof(double));
+        double* aacc = (double*)calloc((size_t)D, sizeof(double));
+        for (long d = 0; d < D; d++)
+            qd[d] = ldexp(orc_e2m1_value(qc[((b * Hq + h) * Nq + i) * D + d]), qE[((b * Hq + h) * Nq + i) * nbd + d / 32]);
+        float s2[BLK];
+        int vis[BLK];
+        double pj[BLK], ph[BLK], flip[BLK];
+        float tj[BLK];
+        float m = -INFINITY;
+        double l = 0.0;
+        for (long kb = 0; kb < nkb; kb++) {
+            long j0 = kb * BLK;
+            if (causal && j0 > i + off) break;
+            long j1 = j0 + BLK < Nkv ? j0 + BLK : Nkv;
+            float bmax = -INFINITY;
+            for (long j = j0; j < j1; j++) {
+                vis[j - j0] = !(causal && j > i + off);
+                if (!vis[j - j0]) continue;
+                const uint8_t* krow = kc + ((b * Hkv + hk) * Nkv + j) * D;
+                const int32_t* ke = kE + ((b * Hkv + hk) * Nkv + j) * nbd;
+                double S = 0.0;
+                for (long d = 0; d < D; d++) S += qd[d] * ldexp(orc_e2m1_value(krow[d]), ke[d / 32]);
+                float v = (float)S * scale2;
+                s2[j - j0] = v;
+                if (v > bmax) bmax = v;
+            }
+            float mnew = m > bmax ? m : bmax;
+            double alpha = (m == -INFINITY) ? 0.0 : exp2((double)m - (double)mnew);
+            double psum = 0.0;
+            for (long j = j0; j < j1; j++) {
+                pj[j - j0] = 0.0;
+                tj[j - j0] = -INFINITY;
+                if (!vis[j - j0]) continue;
+                float t = s2[j - j0] - mnew;
+                float p = (float)exp2((double)t);
+                psum += (double)p;
+                pj[j - j0] = (double)p;
+                tj[j - j0] = t;
+            }
+            for (long h0 = j0; h0 < j1; h0 += 32) {
+                long n = j1 - h0 < 32 ? j1 - h0 : 32;
+                mx_p_block(pj + (h0 - j0), tj + (h0 - j0), vis + (h0 - j0), n, ph + (h0 - j0), flip + (h0 - j0));
+            }
+            l = alpha * l + psum;
+            for (long d = 0; d < D; d++) {
+                const uint8_t* vrow = vc + ((b * Hkv + hk) * D + d) * Nkv;
+                const int32_t* ve = vE + ((b * Hkv + hk) * D + d) * nbt;
+                double a = 0.0, fa = 0.0;
+                for (long j = j0; j < j1; j++) {
+                    double vv = ldexp(orc_e2m1_value(vrow[j]), ve[j / 32]);
+                    a += ph[j - j0] * vv;
+                    fa += flip[j - j0] * fabs(vv);
+                }
+                acc[d] = alpha * acc[d] + a;
+                aacc[d] = alpha * aacc[d] + fa;
+            }
+            m = mnew;
+        }
+        for (long d = 0; d < D; d++) {
+            out[r * D + d] = l > 0.0 ? acc[d] / l : 0.0;
+            if (amb) amb[r * D + d] = l > 0.0 ? aacc[d] / l : 0.0;
+        }
+        free(qd);
+        free(acc);
+        free(aacc);
     }
 }

@@ -257,6 +257,10 @@ def main():
     if not args.no_sweep:
         result["varlen"] = varlen_point(qa, torch, np, si, dev, args.sweep_steps)
 
+    # ---------------------------------------------------------------- microscaling FP4 variant
+    if not args.no_sweep:
+        result["mxfp4"] = mxfp4_points(qa, torch, q, k, v, w, args.sweep_steps)
+
     # ---------------------------------------------------------------- CPU baseline (the oracle, untuned)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, full, np, torch)
@@ -309,6 +313,52 @@ def varlen_point(qa, torch, np, si, dev, steps):
            "attn_tops": round(ops / (at * 1e-3) / 1e12, 1), "attn_ms": round(at, 4),
            "step_tops": round(ops / (st * 1e-3) / 1e12, 1), "step_ms": round(st, 4)}
     log(f"[bench] varlen: attn {at:.3f} ms = {res['attn_tops']} TOPS, step {res['step_tops']} TOPS")
+    return res
+
+
+MXFP4_PEAK_TOPS = 10100.0  # dense FP4 matrix-core peak of MI355X
+
+
+def mxfp4_points(qa, torch, q, k, v, w, steps):
+    """The microscaling FP4 variant (quant_mxfp4 + attn_fwd_mxfp4, preallocated) on the
+    headline workload, non-causal and causal; HIP events on the launch stream."""
+    L = qa.lib()
+    ws = torch.empty(max(8, L.sage_quant_mxfp4_workspace_bytes(w.B, w.Hkv, w.Nkv, w.D)), dtype=torch.uint8,
+                     device=q.device)
+    mq = qa.quant_mxfp4(q, k, v, w.layout, workspace=ws)
+    out = torch.empty_like(q)
+    res = {"workload": f"B{w.B} H{w.Hq} N{w.Nq} D{w.D} bf16 HND, MXFP4 Q/K/V/P (blocks of 32, E8M0 scales)",
+           "peak_tops_fp4": MXFP4_PEAK_TOPS, "points": []}
+    for causal in (False, True):
+        wc = w.with_(causal=causal)
+
+        def quant():
+            qa.quant_mxfp4(q, k, v, w.layout, workspace=ws, out=mq)
+
+        def attn():
+            qa.attn_fwd_mxfp4(mq, w.torch_dtype, w.layout, causal, None, out=out)
+
+        for _ in range(3):
+            quant()
+            attn()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for a, b, c in ev:
+            a.record()
+            quant()
+            b.record()
+            attn()
+            c.record()
+        torch.cuda.synchronize()
+        at = sum(b.elapsed_time(c) for a, b, c in ev) / steps
+        qt = sum(a.elapsed_time(b) for a, b, c in ev) / steps
+        o = wc.ops()
+        res["points"].append({"causal": causal, "attn_ms": round(at, 4), "quant_ms": round(qt, 4),
+                              "attn_tops": round(o / (at * 1e-3) / 1e12, 1),
+                              "step_tops": round(o / ((at + qt) * 1e-3) / 1e12, 1),
+                              "attn_frac_of_fp4_peak": round(o / (at * 1e-3) / 1e12 / MXFP4_PEAK_TOPS, 4)})
+        log(f"[bench] mxfp4 causal={causal}: attn {at:.3f} ms = {res['points'][-1]['attn_tops']} TOPS, "
+            f"quant {qt:.3f} ms")
     return res
 
 

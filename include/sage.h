@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SAGE_ABI_VERSION 3
+#define SAGE_ABI_VERSION 4
 
 typedef enum sage_status {
     SAGE_OK = 0,
@@ -272,6 +272,56 @@ sage_status sage_attn_fwd_varlen_g(const int8_t* q_i8, const float* q_scale, con
                                    int H_kv, int total_q, int total_kv, int max_seqlen_q, int max_seqlen_kv, int D,
                                    int is_causal, float sm_scale, sage_pv pv, sage_accum accum, sage_qk_gran gran,
                                    void* stream);
+
+/* ---- Microscaling FP4 (MXFP4) variant ---------------------------------------------
+ * The SageAttention README names a microscaling FP4 attention for inference
+ * ("SageAttention3: Microscaling FP4 Attention", project updates and citations) and
+ * gives only that title.  These calls take the OCP Microscaling (MX) v1.0 MXFP4 format
+ * that gfx950's scaled matrix instructions read, on both products of the scheme above
+ * (K smoothing and the online base-2 softmax over 64-key blocks unchanged):
+ *   - a block of 32 consecutive elements along a contraction axis shares the scale
+ *     X = 2^E, E = floor(log2 amax) - 2 held to [-126, 127] (an all-zero block: -126),
+ *     stored as the E8M0 byte E + 127;
+ *   - each element is e2m1(x / X): round to nearest even, saturating at 6, sign kept;
+ *     a 4-bit code (sign bit 8 | index in {0, .5, 1, 1.5, 2, 3, 4, 6}); two per byte,
+ *     element 2t in the low nibble of byte t;
+ *   - Q and smoothed K are blocked along the channels of each token, V along the
+ *     tokens of each channel, P along 32 consecutive keys (after the softmax step, with
+ *     p = 2^(s2 - m) and the row sum l over unquantised p).
+ * Scores: S = sum of dequantised Q * K products (scales applied inside the matrix
+ * instruction, fp32), s2 = fp32(S * fp32(sm_scale * log2 e)), t = s2 - m in fp32, so
+ * the row maximum has p = 1 exactly.  Supported head dims: D <= 128 (Dp = 64 or 128);
+ * dense batches.  Layouts (row-major, innermost last):
+ *   q4      uint8 [B][H_qo][N_pad(Nq)][Dp/2]      q4_exp  uint8 [B][H_qo][N_pad(Nq)][Dp/32]
+ *   k4      uint8 [B][H_kv][N_pad(Nkv)][Dp/2]     k4_exp  uint8 [B][H_kv][N_pad(Nkv)][Dp/32]
+ *   k_mean  float [B][H_kv][D]
+ *   v4      uint8 [B][H_kv][NB(Nkv)][Dp][32]      (per 64-token block, channel-major:
+ *                                                   byte t of channel c = tokens 2t, 2t+1)
+ *   v4_exp  uint8 [B][H_kv][NB(Nkv)][2][32][Dp/32] (block j, token half g, channel
+ *                                                   32 u + i at [g][i][u])
+ * Padding (tokens >= N, channels >= D) holds zero codes and the exponent byte 1. */
+
+/* Workspace of sage_quant_mxfp4: B * H_kv * NB(Nkv) * D * 8 bytes (fp64 K block
+ * channel sums); 0 for invalid sizes. */
+size_t sage_quant_mxfp4_workspace_bytes(int B, int H_kv, int Nkv, int D);
+
+/* K mean, then MXFP4 codes and exponents of Q, smoothed K and V (layouts above).
+ * q, k, v: fp16/bf16 in `layout` (as sage_quant_qk / sage_quant_v).  Code buffers
+ * 16-byte aligned; workspace at least sage_quant_mxfp4_workspace_bytes(...) bytes,
+ * 8-byte aligned, overwritten.  D > 128: SAGE_ERR_UNSUPPORTED. */
+sage_status sage_quant_mxfp4(const void* q, const void* k, const void* v, sage_dtype dtype, sage_layout layout, int B,
+                             int H_qo, int H_kv, int Nq, int Nkv, int D, uint8_t* q4, uint8_t* q4_exp, uint8_t* k4,
+                             uint8_t* k4_exp, float* k_mean, uint8_t* v4, uint8_t* v4_exp, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Attention forward on the outputs of sage_quant_mxfp4: out in out_dtype and
+ * out_layout ([B][H_qo][Nq][D] or [B][Nq][H_qo][D]), every element written; causal
+ * aligned to the bottom-right corner as in sage_attn_fwd; a query that sees no key
+ * gives zeros.  sm_scale finite and > 0.  D > 128: SAGE_ERR_UNSUPPORTED. */
+sage_status sage_attn_fwd_mxfp4(const uint8_t* q4, const uint8_t* q4_exp, const uint8_t* k4, const uint8_t* k4_exp,
+                                const uint8_t* v4, const uint8_t* v4_exp, void* out, sage_dtype out_dtype,
+                                sage_layout out_layout, int B, int H_qo, int H_kv, int Nq, int Nkv, int D,
+                                int is_causal, float sm_scale, void* stream);
 
 #ifdef __cplusplus
 }

@@ -13,6 +13,10 @@ Tensor level:
     debug_qk_int32(qk, tiles, pv) -> int32 [T, 64, 64]
     sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None,
              pv="fp8", accum="fp32")   -- the composition of the three calls
+Microscaling FP4 (OCP MXFP4 blocks of 32 on both products, head dim <= 128):
+    quant_mxfp4(q, k, v, layout) -> MXQuant
+    attn_fwd_mxfp4(mq, out_dtype, layout, is_causal, sm_scale) -> out
+    sageattn_mxfp4(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None)
 Packed variable-length batches (q (total_q, H, D), cu_seqlens prefix sums):
     quant_qk_varlen, quant_v_varlen, attn_fwd_varlen,
     sageattn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
@@ -31,7 +35,7 @@ import torch
 __all__ = [
     "SageError", "lib", "library_path", "QKQuant", "VQuant", "quant_qk", "quant_v", "attn_fwd", "debug_qk_int32",
     "quant_qkv", "sageattn", "QKQuantVarlen", "VQuantVarlen", "quant_qk_varlen", "quant_v_varlen",
-    "quant_qkv_varlen", "attn_fwd_varlen",
+    "quant_qkv_varlen", "attn_fwd_varlen", "MXQuant", "quant_mxfp4", "attn_fwd_mxfp4", "sageattn_mxfp4",
     "sageattn_varlen", "varlen_rows", "varlen_slots", "padded_dim", "num_blocks", "SAGE_OK", "SAGE_ERR_INVALID_ARG", "SAGE_ERR_UNSUPPORTED",
     "SAGE_ERR_WORKSPACE", "SAGE_ERR_DEVICE", "SAGE_ERR_HIP",
 ]
@@ -80,6 +84,11 @@ _EXPORTS = {
                               + [ctypes.c_int] * 10 + [ctypes.c_void_p] * 8 + [ctypes.c_size_t, ctypes.c_void_p]),
     "sage_attn_fwd_g": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int, ctypes.c_int] + [ctypes.c_int] * 7
                         + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+    "sage_quant_mxfp4_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
+    "sage_quant_mxfp4": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 2 + [ctypes.c_int] * 6
+                         + [ctypes.c_void_p] * 7 + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "sage_attn_fwd_mxfp4": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] * 2 + [ctypes.c_int] * 7
+                            + [ctypes.c_float, ctypes.c_void_p]),
     "sage_attn_fwd_varlen_g": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] + [ctypes.c_void_p] * 2
                                + [ctypes.c_int] * 9 + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                        ctypes.c_void_p]),
@@ -111,7 +120,7 @@ def lib() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.restype = res
         fn.argtypes = args
-    if L.sage_abi_version() != 3:
+    if L.sage_abi_version() != 4:
         raise ImportError("libsage ABI version mismatch")
     _lib = L
     return L
@@ -324,6 +333,83 @@ def quant_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: str = "
                             out_v.v_hat.data_ptr(), _ptr(out_v.v_scale), workspace.data_ptr(), workspace.numel(),
                             _stream(dev)))
     return out_qk, out_v
+
+
+@dataclasses.dataclass
+class MXQuant:
+    """Outputs of sage_quant_mxfp4 (layouts in include/sage.h, "Microscaling FP4")."""
+    q4: torch.Tensor       # uint8 [B, Hq, N_pad(Nq), Dp/2]   E2M1 codes, two per byte
+    q4_exp: torch.Tensor   # uint8 [B, Hq, N_pad(Nq), Dp/32]  E8M0 block exponents
+    k4: torch.Tensor       # uint8 [B, Hkv, N_pad(Nkv), Dp/2] (smoothed K)
+    k4_exp: torch.Tensor   # uint8 [B, Hkv, N_pad(Nkv), Dp/32]
+    k_mean: torch.Tensor   # f32   [B, Hkv, D]
+    v4: torch.Tensor       # uint8 [B, Hkv, NB(Nkv), Dp, 32]
+    v4_exp: torch.Tensor   # uint8 [B, Hkv, NB(Nkv), 2, 32, Dp/32]
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nkv: int
+    D: int
+
+
+def quant_mxfp4(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: str = "HND",
+                workspace: Optional[torch.Tensor] = None, out: Optional[MXQuant] = None) -> MXQuant:
+    """K mean, then MXFP4 codes and block exponents of Q, smoothed K and V in one call."""
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _check_input(x, name)
+    if not (q.dtype == k.dtype == v.dtype) or not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must share dtype and device")
+    B, Hq, Nq, D = _dims(q, layout)
+    Bk, Hkv, Nkv, Dk = _dims(k, layout)
+    if Bk != B or Dk != D or _dims(v, layout) != (B, Hkv, Nkv, D):
+        raise ValueError("q, k and v disagree on batch, heads, length or head_dim")
+    L = lib()
+    Dp, nbq, nbk = padded_dim(D), num_blocks(Nq), num_blocks(Nkv)
+    Dp = max(Dp, 64)
+    dev = q.device
+    if out is None:
+        u8 = dict(dtype=torch.uint8, device=dev)
+        out = MXQuant(torch.empty(B, Hq, nbq * 64, Dp // 2, **u8), torch.empty(B, Hq, nbq * 64, Dp // 32, **u8),
+                      torch.empty(B, Hkv, nbk * 64, Dp // 2, **u8), torch.empty(B, Hkv, nbk * 64, Dp // 32, **u8),
+                      torch.empty(B, Hkv, D, dtype=torch.float32, device=dev),
+                      torch.empty(B, Hkv, nbk, Dp, 32, **u8), torch.empty(B, Hkv, nbk, 2, 32, Dp // 32, **u8),
+                      B, Hq, Hkv, Nq, Nkv, D)
+    need = L.sage_quant_mxfp4_workspace_bytes(B, Hkv, Nkv, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=dev)
+    _check(L.sage_quant_mxfp4(q.data_ptr(), k.data_ptr(), v.data_ptr(), _DT[q.dtype], _LAYOUT[layout], B, Hq, Hkv, Nq,
+                              Nkv, D, out.q4.data_ptr(), out.q4_exp.data_ptr(), out.k4.data_ptr(),
+                              out.k4_exp.data_ptr(), out.k_mean.data_ptr(), out.v4.data_ptr(), out.v4_exp.data_ptr(),
+                              workspace.data_ptr(), workspace.numel(), _stream(dev)))
+    return out
+
+
+def attn_fwd_mxfp4(mq: MXQuant, out_dtype: torch.dtype, layout: str = "HND", is_causal: bool = False,
+                   sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    if out_dtype not in _DT:
+        raise ValueError("out_dtype must be float16 or bfloat16")
+    if layout not in _LAYOUT:
+        raise ValueError(f"layout must be 'HND' or 'NHD', got {layout!r}")
+    B, Hq, Hkv, Nq, Nkv, D = mq.B, mq.Hq, mq.Hkv, mq.Nq, mq.Nkv, mq.D
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    dev = mq.q4.device
+    if out is None:
+        shape = (B, Hq, Nq, D) if layout == "HND" else (B, Nq, Hq, D)
+        out = torch.empty(shape, dtype=out_dtype, device=dev)
+    _check(lib().sage_attn_fwd_mxfp4(mq.q4.data_ptr(), mq.q4_exp.data_ptr(), mq.k4.data_ptr(), mq.k4_exp.data_ptr(),
+                                     mq.v4.data_ptr(), mq.v4_exp.data_ptr(), out.data_ptr(), _DT[out_dtype],
+                                     _LAYOUT[layout], B, Hq, Hkv, Nq, Nkv, D, int(bool(is_causal)), float(sm_scale),
+                                     _stream(dev)))
+    return out
+
+
+def sageattn_mxfp4(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: str = "HND",
+                   is_causal: bool = False, sm_scale: Optional[float] = None) -> torch.Tensor:
+    """The microscaling FP4 variant: quant_mxfp4 then attn_fwd_mxfp4 (output in q's dtype and layout)."""
+    mq = quant_mxfp4(q, k, v, tensor_layout)
+    return attn_fwd_mxfp4(mq, q.dtype, tensor_layout, is_causal, sm_scale)
 
 
 def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: str = "HND", is_causal: bool = False,

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsage.so")
-SOURCES = ["api.cpp", "quant.hip", "attn_fwd.hip"]
+SOURCES = ["api.cpp", "quant.hip", "attn_fwd.hip", "attn_mx.hip"]
 ARCH = "gfx950"
 
 

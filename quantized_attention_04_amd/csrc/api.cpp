@@ -475,4 +475,75 @@ sage_status sage_attn_fwd_varlen_g(const int8_t* q_i8, const float* q_scale, con
     return launch_status(sage::launch_attn_fwd(a, (hipStream_t)stream), "sage_attn_fwd_varlen");
 }
 
+
+// ---- microscaling FP4 ---------------------------------------------------------------
+
+size_t sage_quant_mxfp4_workspace_bytes(int B, int H_kv, int Nkv, int D) {
+    if (B <= 0 || H_kv <= 0 || Nkv <= 0 || D <= 0 || D > 128) return 0;
+    return size_t(B) * size_t(H_kv) * size_t(nblocks(Nkv)) * size_t(D) * sizeof(double);
+}
+
+sage_status sage_quant_mxfp4(const void* q, const void* k, const void* v, sage_dtype dtype, sage_layout layout, int B,
+                             int H_qo, int H_kv, int Nq, int Nkv, int D, uint8_t* q4, uint8_t* q4_exp, uint8_t* k4,
+                             uint8_t* k4_exp, float* k_mean, uint8_t* v4, uint8_t* v4_exp, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !q4 || !q4_exp || !k4 || !k4_exp || !k_mean || !v4 || !v4_exp)
+        return fail(SAGE_ERR_INVALID_ARG, "sage_quant_mxfp4: null tensor pointer");
+    if (dtype != SAGE_FP16 && dtype != SAGE_BF16) return fail(SAGE_ERR_INVALID_ARG, "bad dtype %d", int(dtype));
+    if (layout != SAGE_HND && layout != SAGE_NHD) return fail(SAGE_ERR_INVALID_ARG, "bad layout %d", int(layout));
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(q4, 16) || !aligned(k4, 16) ||
+        !aligned(v4, 16) || !aligned(k_mean, 4))
+        return fail(SAGE_ERR_INVALID_ARG, "sage_quant_mxfp4: misaligned tensor");
+    sage_status s = check_shape(B, H_qo, H_kv, Nq, Nkv, D);
+    if (s != SAGE_OK) return s;
+    if (D > 128) return fail(SAGE_ERR_UNSUPPORTED, "sage_quant_mxfp4: head_dim %d > 128 is not supported", D);
+    const size_t need = sage_quant_mxfp4_workspace_bytes(B, H_kv, Nkv, D);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 8))
+        return fail(SAGE_ERR_WORKSPACE, "sage_quant_mxfp4: workspace of %zu bytes (8-byte aligned) required, got %zu",
+                    need, workspace ? workspace_bytes : size_t(0));
+    s = check_device();
+    if (s != SAGE_OK) return s;
+    sage::QuantMXArgs a{};
+    a.q = q, a.k = k, a.v = v;
+    a.bf16 = dtype == SAGE_BF16;
+    a.layout_nhd = layout == SAGE_NHD;
+    a.B = B, a.Hq = H_qo, a.Hkv = H_kv, a.Nq = Nq, a.Nkv = Nkv, a.D = D;
+    a.q4 = q4, a.q4_exp = q4_exp, a.k4 = k4, a.k4_exp = k4_exp, a.k_mean = k_mean, a.v4 = v4, a.v4_exp = v4_exp;
+    a.workspace = workspace;
+    return launch_status(sage::launch_quant_mxfp4(a, (hipStream_t)stream), "sage_quant_mxfp4");
+}
+
+sage_status sage_attn_fwd_mxfp4(const uint8_t* q4, const uint8_t* q4_exp, const uint8_t* k4, const uint8_t* k4_exp,
+                                const uint8_t* v4, const uint8_t* v4_exp, void* out, sage_dtype out_dtype,
+                                sage_layout out_layout, int B, int H_qo, int H_kv, int Nq, int Nkv, int D,
+                                int is_causal, float sm_scale, void* stream) {
+    if (!q4 || !q4_exp || !k4 || !k4_exp || !v4 || !v4_exp || !out)
+        return fail(SAGE_ERR_INVALID_ARG, "sage_attn_fwd_mxfp4: null tensor pointer");
+    if (out_dtype != SAGE_FP16 && out_dtype != SAGE_BF16)
+        return fail(SAGE_ERR_INVALID_ARG, "bad out dtype %d", int(out_dtype));
+    if (out_layout != SAGE_HND && out_layout != SAGE_NHD)
+        return fail(SAGE_ERR_INVALID_ARG, "bad layout %d", int(out_layout));
+    if (is_causal != 0 && is_causal != 1) return fail(SAGE_ERR_INVALID_ARG, "is_causal must be 0 or 1");
+    if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
+        return fail(SAGE_ERR_INVALID_ARG, "sm_scale must be finite and > 0 (got %g)", double(sm_scale));
+    if (!aligned(q4, 16) || !aligned(k4, 16) || !aligned(v4, 16) || !aligned(out, (D % 4) == 0 ? 8 : 2))
+        return fail(SAGE_ERR_INVALID_ARG, "sage_attn_fwd_mxfp4: misaligned tensor");
+    sage_status s = check_shape(B, H_qo, H_kv, Nq, Nkv, D);
+    if (s != SAGE_OK) return s;
+    if (D > 128) return fail(SAGE_ERR_UNSUPPORTED, "sage_attn_fwd_mxfp4: head_dim %d > 128 is not supported", D);
+    const int64_t grid = int64_t((Nq + 127) / 128) * H_qo * B;
+    if (grid > INT32_MAX) return fail(SAGE_ERR_UNSUPPORTED, "sage_attn_fwd_mxfp4: grid too large");
+    s = check_device();
+    if (s != SAGE_OK) return s;
+    sage::AttnMXArgs a{};
+    a.q4 = q4, a.q4_exp = q4_exp, a.k4 = k4, a.k4_exp = k4_exp, a.v4 = v4, a.v4_exp = v4_exp;
+    a.out = out;
+    a.out_bf16 = out_dtype == SAGE_BF16;
+    a.out_nhd = out_layout == SAGE_NHD;
+    a.B = B, a.Hq = H_qo, a.Hkv = H_kv, a.Nq = Nq, a.Nkv = Nkv, a.D = D;
+    a.causal = is_causal;
+    a.sm_scale = sm_scale;
+    return launch_status(sage::launch_attn_mxfp4(a, (hipStream_t)stream), "sage_attn_fwd_mxfp4");
+}
+
 }  // extern "C"

@@ -54,18 +54,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLog2_448 = 8.807354f;
 
 
-__device__ __forceinline__ int parity(uint32_t x) { return __builtin_popcount(x) & 1; }
-
-// Workgroup barrier without the memory fence of __syncthreads(): the fence would make
-// the compiler wait for every outstanding global load, including the prefetch of the
-// next tile.  LDS visibility is ensured by the explicit vmcnt waits before it; the
-// signal fences keep the compiler from moving memory accesses across it.
-__device__ __forceinline__ void block_barrier() {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 // Mode constants.  DP = padded head dim (64 | 128 | 256); FP8 = P.V in e4m3 (else fp16).
 template <int DP, bool FP8>
 struct Cfg {
@@ -212,17 +200,6 @@ __device__ __forceinline__ void load_q_frags(v4i (&qf)[C::KS], const int8_t* qro
     const int i = lane & 31, g = lane >> 5;
 #pragma unroll
     for (int s = 0; s < C::KS; s++) qf[s] = *(const v4i*)(qrows + i * C::KROW + 32 * s + 16 * g);
-}
-
-// Combine a value with the one held by the lane 32 positions away (the other half of
-// the same query column): v_permlane32_swap returns the two halves side by side.
-__device__ __forceinline__ float halves_max(float v) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float halves_sum(float v) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // P in the B-operand registers of the P.V MFMAs: FP8 e4m3 codes of p * 448 (one

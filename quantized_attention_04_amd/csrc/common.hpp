@@ -133,6 +133,29 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+__device__ __forceinline__ int parity(uint32_t x) { return __builtin_popcount(x) & 1; }
+
+// Workgroup barrier without the memory fence of __syncthreads(): the fence would make
+// the compiler wait for every outstanding global load, including the prefetch of the
+// next tile.  LDS visibility is ensured by the explicit vmcnt waits before it; the
+// signal fences keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void block_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Combine a value with the one held by the lane 32 positions away (the other half of
+// the same query column): v_permlane32_swap returns the two halves side by side.
+__device__ __forceinline__ float halves_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ---- waits --------------------------------------------------------------------------
 // s_waitcnt vmcnt(n) with the other counters left at their maximum (gfx9 encoding:
 // vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).

@@ -55,6 +55,38 @@ struct AttnArgs {
     int thread_gran;  // scales of sage_quant_qkv's per-thread granularity
 };
 
+// Microscaling FP4 (dense batches): codes and E8M0 exponent bytes of Q, smoothed K and V
+// in the layouts of include/sage.h; workspace = the fp64 K block channel sums.
+struct QuantMXArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    int bf16, layout_nhd;
+    int B, Hq, Hkv, Nq, Nkv, D;
+    uint8_t* q4;
+    uint8_t* q4_exp;
+    uint8_t* k4;
+    uint8_t* k4_exp;
+    float* k_mean;
+    uint8_t* v4;
+    uint8_t* v4_exp;
+    void* workspace;
+};
+
+struct AttnMXArgs {
+    const uint8_t* q4;
+    const uint8_t* q4_exp;
+    const uint8_t* k4;
+    const uint8_t* k4_exp;
+    const uint8_t* v4;
+    const uint8_t* v4_exp;
+    void* out;
+    int out_bf16, out_nhd;
+    int B, Hq, Hkv, Nq, Nkv, D;
+    int causal;
+    float sm_scale;
+};
+
 struct DebugQKArgs {
     const int8_t* q_i8;
     const int8_t* k_i8;
@@ -89,5 +121,7 @@ hipError_t launch_quant_qkv(const QuantQKArgs& a, const QuantVArgs& v, hipStream
 hipError_t launch_quant_v(const QuantVArgs& a, hipStream_t s);
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s);
 hipError_t launch_debug_qk(const DebugQKArgs& a, hipStream_t s);
+hipError_t launch_quant_mxfp4(const QuantMXArgs& a, hipStream_t s);
+hipError_t launch_attn_mxfp4(const AttnMXArgs& a, hipStream_t s);
 
 }  // namespace sage

@@ -649,4 +649,168 @@ hipError_t launch_quant_qkv(const QuantQKArgs& a, const QuantVArgs& v, hipStream
     return a.bf16 ? launch_qkv_dp<true>(a, v, s) : launch_qkv_dp<false>(a, v, s);
 }
 
+
+// ------------------------------------------------------------------------------------------
+// Microscaling FP4 (the README's "SageAttention3: Microscaling FP4 Attention", taken as
+// the OCP MX v1.0 MXFP4 format that gfx950's scaled matrix instructions read): every
+// 32 consecutive elements along a contraction axis share the power-of-two scale
+// X = 2^E, E = floor(log2 amax) - 2 held to [-126, 127] (an all-zero block: -126),
+// stored as the E8M0 byte E + 127; elements are e2m1(x / X), round to nearest even,
+// saturating at 6, as 4-bit codes (element 2t in the low nibble of byte t).
+//   Q, smoothed K: per token, blocks of 32 channels -> codes [row][Dp/2], exponents
+//                  [row][Dp/32] (rows and block slots as for INT8);
+//   V:             per channel, blocks of 32 tokens; per 64-token slot the codes
+//                  [Dp][32] (channel-major) and the exponents in the order
+//                  [token half g][channel % 32][channel / 32], so that the lane of the
+//                  P.V matrix instruction holding channel 32 t + i, half g finds its
+//                  Dp / 32 exponents in one word.
+
+__device__ __forceinline__ int mx_exp(float amax) {  // amax >= 0 (a zero or subnormal amax gives -126)
+    return max(int((__float_as_uint(amax) >> 23) & 0xffu) - 129, -126);
+}
+__device__ __forceinline__ float mx_scale_f32(int E) { return __uint_as_float(uint32_t(E + 127) << 23); }
+
+// Q or K: one wave per 64-token block; lane l covers 8 channels (chunk l % CH) of the
+// token rows l / CH + p * (64 / CH); the four lanes of a 32-channel block (aligned
+// groups of four lanes) combine their maxima with two lane exchanges.
+template <bool BF16, int DP, bool VEC8, bool SMOOTH>
+__global__ __launch_bounds__(256) void mx_rows_kernel(const uint16_t* __restrict__ x, SeqMap m, int D,
+                                                      const float* __restrict__ mean, uint8_t* __restrict__ xq,
+                                                      uint8_t* __restrict__ xe) {
+    constexpr int CH = DP / 8, RPP = kWave / CH, PASSES = kBlk / RPP;
+    const int lane = threadIdx.x % kWave;
+    const int j = blockIdx.x * 4 + int(threadIdx.x / kWave), h = blockIdx.y, b = blockIdx.z;
+    const SeqView sv = seq_view(m, b, h);
+    if (j * kBlk >= sv.n) return;  // this wave: past the sequence's end
+    const int N = sv.n;
+    const Strides st = m.st;
+    const int64_t bh = int64_t(b) * m.H + h;
+    const int ch = lane % CH, r0 = lane / CH, c0 = ch * 8;
+    const uint16_t* base = x + sv.in_off;
+    float mu[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) mu[e] = (SMOOTH && c0 + e < D) ? mean[bh * D + c0 + e] : 0.0f;
+#pragma unroll 4
+    for (int p = 0; p < PASSES; p++) {
+        const int t = j * kBlk + p * RPP + r0;
+        v8u16 r = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (t < N && c0 < D) {
+            const uint16_t* src = base + int64_t(t) * st.t + c0;
+            if constexpr (VEC8) {
+                r = *(const v8u16*)src;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; e++) r[e] = (c0 + e < D) ? src[e] : (unsigned short)0;
+            }
+        }
+        float y[8], am = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            const bool real = t < N && c0 + e < D;  // padding tokens and channels: +0
+            y[e] = real ? in_to_f32<BF16>(r[e]) - mu[e] : 0.0f;
+            am = fmaxf(am, fabsf(y[e]));
+        }
+        am = fmaxf(am, __shfl_xor(am, 1));
+        am = fmaxf(am, __shfl_xor(am, 2));
+        const int E = mx_exp(am);
+        const float X = mx_scale_f32(E);
+        int w = 0;
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], X, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], X, 1);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], X, 2);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], X, 3);
+        const int64_t row = sv.row0 + t;
+        *(int*)(xq + row * (DP / 2) + 4 * ch) = w;
+        if ((ch & 3) == 0) xe[row * (DP / 32) + ch / 4] = uint8_t(E + 127);
+    }
+}
+
+// V: one workgroup of 2 Dp threads per 64-token block; the block's 64 x Dp tile is
+// read with 16-byte loads into LDS, then thread 2 d + g quantises channel d over the
+// tokens 32 g .. 32 g + 31 and writes its 16 code bytes (consecutive threads,
+// consecutive bytes) and its exponent.
+template <bool BF16, int DP, bool VEC8>
+__global__ __launch_bounds__(2 * DP) void mx_v_kernel(const uint16_t* __restrict__ v, SeqMap m, int D,
+                                                      uint8_t* __restrict__ vq, uint8_t* __restrict__ ve) {
+    constexpr int CH = DP / 8, THREADS = 2 * DP, RPP = THREADS / CH;  // RPP token rows per pass
+    constexpr int LD = DP + 8;                                        // LDS row pitch (elements)
+    __shared__ __attribute__((aligned(16))) uint16_t tile[kBlk * LD];
+    const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const SeqView sv = seq_view(m, b, h);
+    if (j * kBlk >= sv.n) return;  // the whole workgroup: past this sequence's end
+    const int N = sv.n;
+    const Strides st = m.st;
+    const uint16_t* base = v + sv.in_off;
+    {
+        const int ch = threadIdx.x % CH, r0 = threadIdx.x / CH, c0 = ch * 8;
+#pragma unroll
+        for (int p = 0; p < kBlk / RPP; p++) {
+            const int tl = p * RPP + r0, t = j * kBlk + tl;
+            v8u16 r = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (t < N && c0 < D) {
+                const uint16_t* src = base + int64_t(t) * st.t + c0;
+                if constexpr (VEC8) {
+                    r = *(const v8u16*)src;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; e++) r[e] = (c0 + e < D) ? src[e] : (unsigned short)0;
+                }
+            }
+            *(v8u16*)&tile[tl * LD + c0] = r;
+        }
+    }
+    __syncthreads();
+    const int d = threadIdx.x >> 1, g = threadIdx.x & 1;
+    float y[32], am = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 32; u++) {
+        y[u] = in_to_f32<BF16>(tile[(32 * g + u) * LD + d]);  // padding: +0
+        am = fmaxf(am, fabsf(y[u]));
+    }
+    const int E = mx_exp(am);
+    const float X = mx_scale_f32(E);
+    int w[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        int x = 0;
+        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, y[8 * k + 0], y[8 * k + 1], X, 0);
+        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, y[8 * k + 2], y[8 * k + 3], X, 1);
+        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, y[8 * k + 4], y[8 * k + 5], X, 2);
+        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, y[8 * k + 6], y[8 * k + 7], X, 3);
+        w[k] = x;
+    }
+    const int64_t slot = sv.slot0 + j;
+    *(int4*)(vq + (slot * DP + d) * 32 + 16 * g) = make_int4(w[0], w[1], w[2], w[3]);
+    ve[slot * DP * 2 + (g * 32 + (d & 31)) * (DP / 32) + (d >> 5)] = uint8_t(E + 127);
+}
+
+namespace {
+template <bool BF16, int DP, bool VEC8>
+hipError_t launch_mx_t(const QuantMXArgs& a, hipStream_t s) {
+    const SeqMap mq = make_seq_map(a.layout_nhd, nullptr, a.B, a.Hq, a.Nq, 0, a.D);
+    const SeqMap mk = make_seq_map(a.layout_nhd, nullptr, a.B, a.Hkv, a.Nkv, 0, a.D);
+    k_mean_partial_kernel<BF16, DP, VEC8><<<dim3(mk.NB, a.Hkv, a.B), 256, 0, s>>>((const uint16_t*)a.k, mk, a.D,
+                                                                                (double*)a.workspace);
+    const int tot = a.B * a.Hkv * a.D;
+    k_mean_final_kernel<<<(tot + 63) / 64, 64, 0, s>>>((const double*)a.workspace, mk, tot, a.D, a.k_mean);
+    mx_rows_kernel<BF16, DP, VEC8, false><<<dim3((mq.NB + 3) / 4, a.Hq, a.B), 256, 0, s>>>(
+        (const uint16_t*)a.q, mq, a.D, nullptr, a.q4, a.q4_exp);
+    mx_rows_kernel<BF16, DP, VEC8, true><<<dim3((mk.NB + 3) / 4, a.Hkv, a.B), 256, 0, s>>>(
+        (const uint16_t*)a.k, mk, a.D, a.k_mean, a.k4, a.k4_exp);
+    mx_v_kernel<BF16, DP, VEC8><<<dim3(mk.NB, a.Hkv, a.B), 2 * DP, 0, s>>>((const uint16_t*)a.v, mk, a.D, a.v4,
+                                                                          a.v4_exp);
+    return hipGetLastError();
+}
+template <bool BF16>
+hipError_t launch_mx_dp(const QuantMXArgs& a, hipStream_t s) {
+    const bool vec = (a.D % 8) == 0;
+    if (a.D <= 64) return vec ? launch_mx_t<BF16, 64, true>(a, s) : launch_mx_t<BF16, 64, false>(a, s);
+    return vec ? launch_mx_t<BF16, 128, true>(a, s) : launch_mx_t<BF16, 128, false>(a, s);
+}
+}  // namespace
+
+hipError_t launch_quant_mxfp4(const QuantMXArgs& a, hipStream_t s) {
+    return a.bf16 ? launch_mx_dp<true>(a, s) : launch_mx_dp<false>(a, s);
+}
+
 }  // namespace sage

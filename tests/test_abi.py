@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_strings():
     L = qa.lib()
-    assert L.sage_abi_version() == 3
+    assert L.sage_abi_version() == 4
     for s in range(6):
         assert L.sage_status_string(s).decode().startswith("SAGE_")
     assert qa.padded_dim(1) == 64 and qa.padded_dim(64) == 64 and qa.padded_dim(65) == 128
@@ -316,3 +316,62 @@ def test_python_varlen_layer_rejects_bad_shapes():
     cu = torch.tensor([0, 64], dtype=torch.int32)
     with pytest.raises(ValueError, match="GPU"):
         qa.sageattn_varlen(x, x, x, cu, cu, 64, 64)
+
+
+# ---- microscaling FP4 entry points
+
+def _mxq(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, layout=0, B=1, Hq=2, Hkv=2, Nq=128, Nkv=128, D=64, q4=FAKE, q4e=FAKE,
+             k4=FAKE, k4e=FAKE, km=FAKE, v4=FAKE, v4e=FAKE, ws=FAKE, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return qa.lib().sage_quant_mxfp4(a["q"], a["k"], a["v"], a["dtype"], a["layout"], a["B"], a["Hq"], a["Hkv"],
+                                     a["Nq"], a["Nkv"], a["D"], a["q4"], a["q4e"], a["k4"], a["k4e"], a["km"], a["v4"],
+                                     a["v4e"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def _mxa(**kw):
+    a = dict(q4=FAKE, q4e=FAKE, k4=FAKE, k4e=FAKE, v4=FAKE, v4e=FAKE, out=FAKE, odt=1, olay=0, B=1, Hq=2, Hkv=2,
+             Nq=128, Nkv=128, D=64, causal=0, sm=0.125, stream=None)
+    a.update(kw)
+    return qa.lib().sage_attn_fwd_mxfp4(a["q4"], a["q4e"], a["k4"], a["k4e"], a["v4"], a["v4e"], a["out"], a["odt"],
+                                        a["olay"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nkv"], a["D"], a["causal"],
+                                        a["sm"], a["stream"])
+
+
+def test_mxfp4_workspace_sizes():
+    L = qa.lib()
+    assert L.sage_quant_mxfp4_workspace_bytes(4, 32, 8192, 128) == 4 * 32 * 128 * 128 * 8
+    assert L.sage_quant_mxfp4_workspace_bytes(1, 1, 100, 72) == 2 * 72 * 8
+    assert L.sage_quant_mxfp4_workspace_bytes(1, 1, 100, 129) == 0
+    assert L.sage_quant_mxfp4_workspace_bytes(0, 1, 100, 64) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), qa.SAGE_ERR_INVALID_ARG), (dict(v4e=None), qa.SAGE_ERR_INVALID_ARG),
+    (dict(km=None), qa.SAGE_ERR_INVALID_ARG), (dict(dtype=2), qa.SAGE_ERR_INVALID_ARG),
+    (dict(layout=2), qa.SAGE_ERR_INVALID_ARG), (dict(q4=FAKE + 8), qa.SAGE_ERR_INVALID_ARG),
+    (dict(Hq=3), qa.SAGE_ERR_INVALID_ARG), (dict(Nkv=0), qa.SAGE_ERR_INVALID_ARG),
+    (dict(D=160), qa.SAGE_ERR_UNSUPPORTED), (dict(ws=None), qa.SAGE_ERR_WORKSPACE),
+    (dict(ws_bytes=2 * 64 * 8 - 1), qa.SAGE_ERR_WORKSPACE), (dict(ws=FAKE + 4), qa.SAGE_ERR_WORKSPACE),
+])
+def test_quant_mxfp4_rejects(kw, code):
+    assert _mxq(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q4=None), qa.SAGE_ERR_INVALID_ARG), (dict(out=None), qa.SAGE_ERR_INVALID_ARG),
+    (dict(odt=5), qa.SAGE_ERR_INVALID_ARG), (dict(olay=3), qa.SAGE_ERR_INVALID_ARG),
+    (dict(causal=2), qa.SAGE_ERR_INVALID_ARG), (dict(sm=0.0), qa.SAGE_ERR_INVALID_ARG),
+    (dict(sm=float("nan")), qa.SAGE_ERR_INVALID_ARG), (dict(k4=FAKE + 1), qa.SAGE_ERR_INVALID_ARG),
+    (dict(Hkv=4), qa.SAGE_ERR_INVALID_ARG), (dict(D=129), qa.SAGE_ERR_UNSUPPORTED),
+    (dict(D=0), qa.SAGE_ERR_INVALID_ARG),
+])
+def test_attn_fwd_mxfp4_rejects(kw, code):
+    assert _mxa(**kw) == code
+
+
+def test_mxfp4_valid_arguments_reach_the_device_check_only():
+    if torch.cuda.is_available():
+        pytest.skip("would launch kernels on fake pointers")
+    assert _mxq() == qa.SAGE_ERR_DEVICE
+    assert _mxa() == qa.SAGE_ERR_DEVICE

@@ -1,0 +1,186 @@
+"""GPU parity of the microscaling FP4 variant (sage_quant_mxfp4 / sage_attn_fwd_mxfp4)
+through the C ABI, against the CPU oracle's MXFP4 reading.
+
+Bit-exact: the K mean, every E2M1 code and every E8M0 block exponent of Q, smoothed
+K and V, padding included.  Output: against the emulation, max-abs <= 1e-2 (one
+output ulp where wider) plus the ambiguity allowance (P values within 2^-14 of a
+rounding tie, P blocks whose maximum sits within 2^-14 of a power of two) and
+cosine >= 0.9999; against exact attention, the envelope of the FP4 scheme itself
+(relative L1 <= 0.35, cosine >= 0.94; the oracle's own emulation measures about
+0.25 / 0.97 on these inputs).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_attention_04_amd as qa
+import synth_inputs as si
+from gpu_helpers import gather_rows, metrics, note, sm_scale_of
+
+pytestmark = pytest.mark.gpu
+
+W = si.workload
+
+CASES = [
+    ("tiny_fp16", W("tiny"), "all"),
+    ("tiny_causal", W("tiny", causal=True), "all"),
+    ("ragged_fp16_d40", W("tiny", B=2, Hq=3, Hkv=3, Nq=100, Nkv=100, D=40, seed=11), "all"),
+    ("gqa_nhd_d72_causal_nq_lt_nkv", W("video_dit", B=2, Hq=4, Hkv=2, Nq=70, Nkv=200, D=72, causal=True, seed=12),
+     "all"),
+    ("d128_causal_1000", W("seq_sweep", B=1, Hq=4, Hkv=2, Nq=1000, Nkv=1000, causal=True, seed=40), 48),
+    ("d96_gqa_nhd", W("gqa", B=1, Hq=8, Hkv=2, Nq=500, Nkv=500, D=96, causal=False, seed=41), 48),
+    ("one_key", W("tiny", Nq=130, Nkv=1, seed=16), "all"),
+    ("one_query", W("llm_prefill", Nq=1, Nkv=500, seed=17), "all"),
+    ("offset_keys_d64", W("video_dit", B=1, Hq=2, Hkv=2, Nq=333, Nkv=333, seed=42), 64),
+]
+
+
+class MXCase:
+    def __init__(self, w: si.Workload):
+        self.w = w
+        note(f"[mx case] {w}")
+        self.q, self.k, self.v = si.make_qkv(w)
+        self.qf, self.kf, self.vf = (oracle.to_hnd_f32(t, w.layout) for t in (self.q, self.k, self.v))
+        self._o = None
+
+    @property
+    def o(self) -> oracle.MXQuantized:
+        if self._o is None:
+            self._o = oracle.quantize_mxfp4(self.qf, self.kf, self.vf)
+        return self._o
+
+    def gpu(self, causal=None, layout=None):
+        w = self.w
+        lay = layout or w.layout
+        c = w.causal if causal is None else causal
+        note(f"[gpu] mxfp4 {w.name} B{w.B} Hq{w.Hq} Hkv{w.Hkv} Nq{w.Nq} Nkv{w.Nkv} D{w.D} {lay} causal={c}")
+        q, k, v = self.q, self.k, self.v
+        if lay != w.layout:  # the same logical tensors in the other layout
+            q, k, v = (x.transpose(1, 2).contiguous() for x in (q, k, v))
+        mq = qa.quant_mxfp4(q.cuda(), k.cuda(), v.cuda(), lay)
+        out = qa.attn_fwd_mxfp4(mq, w.torch_dtype, lay, c, sm_scale_of(w.D))
+        torch.cuda.synchronize()
+        return mq, out
+
+
+def _nibbles(b: np.ndarray) -> np.ndarray:
+    """uint8 [..., n] -> codes [..., 2n] (element 2t in the low nibble of byte t)"""
+    return np.stack([b & 15, b >> 4], axis=-1).reshape(*b.shape[:-1], 2 * b.shape[-1])
+
+
+def check_mx_bit_exact(c: MXCase, mq) -> None:
+    w, o = c.w, c.o
+    Dp = qa.padded_dim(w.D)
+    nbd = (w.D + 31) // 32
+    np.testing.assert_array_equal(mq.k_mean.cpu().numpy(), o.k_mean, err_msg="k_mean")
+    for name, codes, exps, rc, re, N in (("q", mq.q4, mq.q4_exp, o.q_code, o.q_exp, w.Nq),
+                                          ("k", mq.k4, mq.k4_exp, o.k_code, o.k_exp, w.Nkv)):
+        g = _nibbles(codes.cpu().numpy())
+        np.testing.assert_array_equal(g[:, :, :N, :w.D], rc, err_msg=f"{name}4 codes")
+        assert not g[:, :, N:].any() and not g[:, :, :, w.D:].any(), f"{name}4 padding"
+        e = exps.cpu().numpy().astype(np.int64)
+        np.testing.assert_array_equal(e[:, :, :N, :nbd], re + 127, err_msg=f"{name}4 exponents")
+        assert (e[:, :, N:] == 1).all() and (e[:, :, :, nbd:] == 1).all(), f"{name}4 padding exponents"
+    B, H, NB = w.B, w.Hkv, qa.num_blocks(w.Nkv)
+    v4 = _nibbles(mq.v4.cpu().numpy())                        # [B, H, NB, Dp, 64]
+    vt = v4.transpose(0, 1, 3, 2, 4).reshape(B, H, Dp, NB * 64)
+    np.testing.assert_array_equal(vt[:, :, :w.D, :w.Nkv], o.v_code, err_msg="v4 codes")
+    assert not vt[:, :, w.D:].any() and not vt[:, :, :, w.Nkv:].any(), "v4 padding"
+    ve = mq.v4_exp.cpu().numpy().astype(np.int64)             # [B, H, NB, 2, 32, Dp/32]: channel 32 u + i at [g][i][u]
+    ve = ve.transpose(0, 1, 5, 4, 2, 3).reshape(B, H, Dp, NB * 2)  # [B, H, channel, 32-token block]
+    nbt = (w.Nkv + 31) // 32
+    np.testing.assert_array_equal(ve[:, :, :w.D, :nbt], o.v_exp + 127, err_msg="v4 exponents")
+    assert (ve[:, :, w.D:] == 1).all() and (ve[:, :, :, nbt:] == 1).all(), "v4 padding exponents"
+
+
+def check_mx_output(c: MXCase, out: torch.Tensor, rows: np.ndarray, causal: bool, layout=None) -> None:
+    w = c.w
+    got = gather_rows(out, rows, layout or w.layout)
+    assert np.isfinite(got).all()
+    sm = sm_scale_of(w.D)
+    note(f"[oracle] mxfp4 emulate {len(rows)} rows")
+    em_raw, amb = oracle.attn_emulate_mxfp4(c.o, causal, sm, rows, with_ambiguity=True)
+    fmt = oracle.BF16 if w.dtype == "bf16" else oracle.FP16
+    em = oracle.round_to(em_raw, fmt)
+    ulp = np.ldexp(1.0, np.floor(np.log2(np.maximum(np.abs(em), 1e-30))).astype(int) - (7 if fmt == oracle.BF16 else 10))
+    res = {"emulate": metrics(got, em)}
+    res["emulate"]["worst_excess"] = float((np.abs(got - em) - np.maximum(1e-2, ulp) - amb).max())
+    ex = oracle.attn_exact(c.qf, c.kf, c.vf, causal, sm, rows)
+    res["exact"] = metrics(got, ex)
+    note(f"[metrics] {res}")
+    assert res["emulate"]["worst_excess"] <= 0 and res["emulate"]["cos"] >= 0.9999, res
+    assert res["exact"]["rel_l1"] <= 0.35 and res["exact"]["cos"] >= 0.94, res
+
+
+def _rows(w, rows):
+    return oracle.all_rows(w.B, w.Hq, w.Nq) if rows == "all" else oracle.sample_rows(w.B, w.Hq, w.Nq, rows, seed=3)
+
+
+@pytest.mark.parametrize("cid,w,rows", CASES, ids=[c[0] for c in CASES])
+def test_mxfp4_quantization_bit_exact(cid, w, rows):
+    c = MXCase(w)
+    mq, _ = c.gpu()
+    check_mx_bit_exact(c, mq)
+
+
+@pytest.mark.parametrize("cid,w,rows", CASES, ids=[c[0] for c in CASES])
+def test_mxfp4_output_matches_oracle(cid, w, rows):
+    c = MXCase(w)
+    _, out = c.gpu()
+    check_mx_output(c, out, _rows(w, rows), w.causal)
+
+
+def test_mxfp4_full_size_sampled_rows():
+    """B4 H32 N8192 D128 bf16 HND non-causal: the size the benchmark times, in its
+    launch configuration; quantisation bit-exact on the full tensors."""
+    w = W("seq_sweep")
+    c = MXCase(w)
+    mq, out = c.gpu()
+    check_mx_bit_exact(c, mq)
+    rows = oracle.sample_rows(w.B, w.Hq, w.Nq, 8, seed=5)
+    check_mx_output(c, out, rows, False)
+
+
+def test_mxfp4_layouts_give_identical_outputs():
+    w = W("tiny", B=2, Hq=4, Hkv=2, Nq=150, Nkv=150, D=64, seed=43)
+    c = MXCase(w)
+    _, a = c.gpu(layout="HND")
+    _, b = c.gpu(layout="NHD")
+    assert torch.equal(a, b.transpose(1, 2))
+
+
+def test_mxfp4_gqa_equals_repeated_kv_heads():
+    w = W("gqa", B=1, Hq=8, Hkv=2, Nq=300, Nkv=300, D=128, causal=True, seed=44)
+    c = MXCase(w)
+    _, a = c.gpu()
+    q, k, v = (x.cuda() for x in (c.q, c.k, c.v))
+    kr, vr = (x.repeat_interleave(4, dim=2).contiguous() for x in (k, v))  # NHD: heads on dim 2
+    mq = qa.quant_mxfp4(q, kr, vr, "NHD")
+    b = qa.attn_fwd_mxfp4(mq, w.torch_dtype, "NHD", True, sm_scale_of(w.D))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_mxfp4_deterministic_and_sageattn_composition():
+    w = W("llm_prefill", Hq=4, Hkv=4, Nq=700, Nkv=700, causal=True, seed=45)
+    c = MXCase(w)
+    _, a = c.gpu()
+    q, k, v = (x.cuda() for x in (c.q, c.k, c.v))
+    b = qa.sageattn_mxfp4(q, k, v, w.layout, True, sm_scale_of(w.D))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_mxfp4_negative_zeros_and_zero_blocks():
+    """All-zero blocks take exponent byte 1; -0.0 inputs keep their sign bit (code 8)."""
+    w = W("tiny", B=1, Hq=2, Hkv=2, Nq=64, Nkv=64, D=64, seed=46)
+    c = MXCase(w)
+    c.q[0, 0, 3, :32] = -0.0
+    c.q[0, 1, 5, :] = 0.0
+    c.v[0, 1, :, 7] = -0.0
+    c.qf, c.kf, c.vf = (oracle.to_hnd_f32(t, w.layout) for t in (c.q, c.k, c.v))
+    c._o = None
+    mq, out = c.gpu()
+    check_mx_bit_exact(c, mq)
+    check_mx_output(c, out, _rows(w, "all"), False)

@@ -48,6 +48,7 @@ def parse():
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--sweep-steps", type=int, default=10)
+    p.add_argument("--mxfp4", action="store_true", help="time the MXFP4 variant also with --no-sweep")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (HBM counter calibration)")
     return p.parse_args()
@@ -258,7 +259,7 @@ def main():
         result["varlen"] = varlen_point(qa, torch, np, si, dev, args.sweep_steps)
 
     # ---------------------------------------------------------------- microscaling FP4 variant
-    if not args.no_sweep:
+    if not args.no_sweep or args.mxfp4:
         result["mxfp4"] = mxfp4_points(qa, torch, q, k, v, w, args.sweep_steps)
 
     # ---------------------------------------------------------------- CPU baseline (the oracle, untuned)

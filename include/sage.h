@@ -290,8 +290,8 @@ sage_status sage_attn_fwd_varlen_g(const int8_t* q_i8, const float* q_scale, con
  *     p = 2^(s2 - m) and the row sum l over unquantised p).
  * Scores: S = sum of dequantised Q * K products (scales applied inside the matrix
  * instruction, fp32), s2 = fp32(S * fp32(sm_scale * log2 e)), t = s2 - m in fp32, so
- * the row maximum has p = 1 exactly.  Supported head dims: D <= 128 (Dp = 64 or 128);
- * dense batches.  Layouts (row-major, innermost last):
+ * the row maximum has p = 1 exactly.  Head dims up to 256 (Dp = 64, 128 or 256, as
+ * above); dense batches.  Layouts (row-major, innermost last):
  *   q4      uint8 [B][H_qo][N_pad(Nq)][Dp/2]      q4_exp  uint8 [B][H_qo][N_pad(Nq)][Dp/32]
  *   k4      uint8 [B][H_kv][N_pad(Nkv)][Dp/2]     k4_exp  uint8 [B][H_kv][N_pad(Nkv)][Dp/32]
  *   k_mean  float [B][H_kv][D]
@@ -308,7 +308,7 @@ size_t sage_quant_mxfp4_workspace_bytes(int B, int H_kv, int Nkv, int D);
 /* K mean, then MXFP4 codes and exponents of Q, smoothed K and V (layouts above).
  * q, k, v: fp16/bf16 in `layout` (as sage_quant_qk / sage_quant_v).  Code buffers
  * 16-byte aligned; workspace at least sage_quant_mxfp4_workspace_bytes(...) bytes,
- * 8-byte aligned, overwritten.  D > 128: SAGE_ERR_UNSUPPORTED. */
+ * 8-byte aligned, overwritten.  D > 256: SAGE_ERR_UNSUPPORTED. */
 sage_status sage_quant_mxfp4(const void* q, const void* k, const void* v, sage_dtype dtype, sage_layout layout, int B,
                              int H_qo, int H_kv, int Nq, int Nkv, int D, uint8_t* q4, uint8_t* q4_exp, uint8_t* k4,
                              uint8_t* k4_exp, float* k_mean, uint8_t* v4, uint8_t* v4_exp, void* workspace,
@@ -317,7 +317,7 @@ sage_status sage_quant_mxfp4(const void* q, const void* k, const void* v, sage_d
 /* Attention forward on the outputs of sage_quant_mxfp4: out in out_dtype and
  * out_layout ([B][H_qo][Nq][D] or [B][Nq][H_qo][D]), every element written; causal
  * aligned to the bottom-right corner as in sage_attn_fwd; a query that sees no key
- * gives zeros.  sm_scale finite and > 0.  D > 128: SAGE_ERR_UNSUPPORTED. */
+ * gives zeros.  sm_scale finite and > 0.  D > 256: SAGE_ERR_UNSUPPORTED. */
 sage_status sage_attn_fwd_mxfp4(const uint8_t* q4, const uint8_t* q4_exp, const uint8_t* k4, const uint8_t* k4_exp,
                                 const uint8_t* v4, const uint8_t* v4_exp, void* out, sage_dtype out_dtype,
                                 sage_layout out_layout, int B, int H_qo, int H_kv, int Nq, int Nkv, int D,

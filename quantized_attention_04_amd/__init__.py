@@ -13,7 +13,7 @@ Tensor level:
     debug_qk_int32(qk, tiles, pv) -> int32 [T, 64, 64]
     sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None,
              pv="fp8", accum="fp32")   -- the composition of the three calls
-Microscaling FP4 (OCP MXFP4 blocks of 32 on both products, head dim <= 128):
+Microscaling FP4 (OCP MXFP4 blocks of 32 on both products, head dim <= 256):
     quant_mxfp4(q, k, v, layout) -> MXQuant
     attn_fwd_mxfp4(mq, out_dtype, layout, is_causal, sm_scale) -> out
     sageattn_mxfp4(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None)

@@ -479,7 +479,7 @@ sage_status sage_attn_fwd_varlen_g(const int8_t* q_i8, const float* q_scale, con
 // ---- microscaling FP4 ---------------------------------------------------------------
 
 size_t sage_quant_mxfp4_workspace_bytes(int B, int H_kv, int Nkv, int D) {
-    if (B <= 0 || H_kv <= 0 || Nkv <= 0 || D <= 0 || D > 128) return 0;
+    if (B <= 0 || H_kv <= 0 || Nkv <= 0 || D <= 0 || D > 256) return 0;
     return size_t(B) * size_t(H_kv) * size_t(nblocks(Nkv)) * size_t(D) * sizeof(double);
 }
 
@@ -496,7 +496,6 @@ sage_status sage_quant_mxfp4(const void* q, const void* k, const void* v, sage_d
         return fail(SAGE_ERR_INVALID_ARG, "sage_quant_mxfp4: misaligned tensor");
     sage_status s = check_shape(B, H_qo, H_kv, Nq, Nkv, D);
     if (s != SAGE_OK) return s;
-    if (D > 128) return fail(SAGE_ERR_UNSUPPORTED, "sage_quant_mxfp4: head_dim %d > 128 is not supported", D);
     const size_t need = sage_quant_mxfp4_workspace_bytes(B, H_kv, Nkv, D);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 8))
         return fail(SAGE_ERR_WORKSPACE, "sage_quant_mxfp4: workspace of %zu bytes (8-byte aligned) required, got %zu",
@@ -530,7 +529,6 @@ sage_status sage_attn_fwd_mxfp4(const uint8_t* q4, const uint8_t* q4_exp, const 
         return fail(SAGE_ERR_INVALID_ARG, "sage_attn_fwd_mxfp4: misaligned tensor");
     sage_status s = check_shape(B, H_qo, H_kv, Nq, Nkv, D);
     if (s != SAGE_OK) return s;
-    if (D > 128) return fail(SAGE_ERR_UNSUPPORTED, "sage_attn_fwd_mxfp4: head_dim %d > 128 is not supported", D);
     const int64_t grid = int64_t((Nq + 127) / 128) * H_qo * B;
     if (grid > INT32_MAX) return fail(SAGE_ERR_UNSUPPORTED, "sage_attn_fwd_mxfp4: grid too large");
     s = check_device();

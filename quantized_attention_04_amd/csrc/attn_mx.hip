@@ -48,7 +48,7 @@ struct MXCfg {
     static constexpr int STAGE = KBYTES + VBYTES + EXB;
     static constexpr int KS = DP / 64;          // QK^T instructions per score tile
     static constexpr int DT = DP / 32;          // 32-channel tiles of O^T
-    static constexpr int OCC = DP == 64 ? 4 : 3;
+    static constexpr int OCC = DP == 64 ? 4 : (DP == 128 ? 3 : 2);  // head dim 256: 128 accumulator VGPRs
     static constexpr int NST = 3;
     static_assert((KBYTES + VBYTES) % (THREADS * 16) == 0 && KBYTES % (kWave * 16) == 0,
                   "every wave's 1 KB of a code round lies in one region");
@@ -57,11 +57,13 @@ struct MXCfg {
 
 // XOR swizzles of the 16-byte chunks of a row, chosen so that the operand reads (8 lanes
 // x 128 B or 16 lanes x 256 B served per LDS cycle) hit distinct banks:
-//  K^ (head dim 128: 4 chunks per key; 64: 2), read at keys key_of_row(kt, i):
+//  K^ (head dim 256: 8 chunks per key; 128: 4; 64: 2), read at keys key_of_row(kt, i)
+//  -- the 8 (16) lanes of a cycle read keys that differ in bits 0, 1, 5 (1, 2, 5);
 //  V^ (2 chunks per channel), read at channels 32 t + i.
 template <int DP>
 __device__ __forceinline__ int mx_kswz(int row) {
-    if constexpr (DP == 128) return (((row >> 1) ^ (row >> 2)) & 1) | (((row >> 5) & 1) << 1);
+    if constexpr (DP == 256) return ((row ^ (row >> 2)) & 1) | (row & 2) | (((row >> 5) & 1) << 2);
+    else if constexpr (DP == 128) return (((row >> 1) ^ (row >> 2)) & 1) | (((row >> 5) & 1) << 1);
     else return (row >> 5) & 1;
 }
 __device__ __forceinline__ int mx_vswz(int row) { return ((row >> 2) ^ (row >> 3)) & 1; }
@@ -390,7 +392,8 @@ hipError_t launch_mx_attn_dp(const AttnMXArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attn_mxfp4(const AttnMXArgs& a, hipStream_t s) {
-    return a.D <= 64 ? launch_mx_attn_dp<64>(a, s) : launch_mx_attn_dp<128>(a, s);
+    if (a.D <= 64) return launch_mx_attn_dp<64>(a, s);
+    return a.D <= 128 ? launch_mx_attn_dp<128>(a, s) : launch_mx_attn_dp<256>(a, s);
 }
 
 }  // namespace sage

@@ -805,7 +805,8 @@ template <bool BF16>
 hipError_t launch_mx_dp(const QuantMXArgs& a, hipStream_t s) {
     const bool vec = (a.D % 8) == 0;
     if (a.D <= 64) return vec ? launch_mx_t<BF16, 64, true>(a, s) : launch_mx_t<BF16, 64, false>(a, s);
-    return vec ? launch_mx_t<BF16, 128, true>(a, s) : launch_mx_t<BF16, 128, false>(a, s);
+    if (a.D <= 128) return vec ? launch_mx_t<BF16, 128, true>(a, s) : launch_mx_t<BF16, 128, false>(a, s);
+    return vec ? launch_mx_t<BF16, 256, true>(a, s) : launch_mx_t<BF16, 256, false>(a, s);
 }
 }  // namespace
 

@@ -342,7 +342,8 @@ def test_mxfp4_workspace_sizes():
     L = qa.lib()
     assert L.sage_quant_mxfp4_workspace_bytes(4, 32, 8192, 128) == 4 * 32 * 128 * 128 * 8
     assert L.sage_quant_mxfp4_workspace_bytes(1, 1, 100, 72) == 2 * 72 * 8
-    assert L.sage_quant_mxfp4_workspace_bytes(1, 1, 100, 129) == 0
+    assert L.sage_quant_mxfp4_workspace_bytes(1, 1, 100, 200) == 2 * 200 * 8
+    assert L.sage_quant_mxfp4_workspace_bytes(1, 1, 100, 257) == 0
     assert L.sage_quant_mxfp4_workspace_bytes(0, 1, 100, 64) == 0
 
 
@@ -351,7 +352,7 @@ def test_mxfp4_workspace_sizes():
     (dict(km=None), qa.SAGE_ERR_INVALID_ARG), (dict(dtype=2), qa.SAGE_ERR_INVALID_ARG),
     (dict(layout=2), qa.SAGE_ERR_INVALID_ARG), (dict(q4=FAKE + 8), qa.SAGE_ERR_INVALID_ARG),
     (dict(Hq=3), qa.SAGE_ERR_INVALID_ARG), (dict(Nkv=0), qa.SAGE_ERR_INVALID_ARG),
-    (dict(D=160), qa.SAGE_ERR_UNSUPPORTED), (dict(ws=None), qa.SAGE_ERR_WORKSPACE),
+    (dict(D=300), qa.SAGE_ERR_UNSUPPORTED), (dict(ws=None), qa.SAGE_ERR_WORKSPACE),
     (dict(ws_bytes=2 * 64 * 8 - 1), qa.SAGE_ERR_WORKSPACE), (dict(ws=FAKE + 4), qa.SAGE_ERR_WORKSPACE),
 ])
 def test_quant_mxfp4_rejects(kw, code):
@@ -363,7 +364,7 @@ def test_quant_mxfp4_rejects(kw, code):
     (dict(odt=5), qa.SAGE_ERR_INVALID_ARG), (dict(olay=3), qa.SAGE_ERR_INVALID_ARG),
     (dict(causal=2), qa.SAGE_ERR_INVALID_ARG), (dict(sm=0.0), qa.SAGE_ERR_INVALID_ARG),
     (dict(sm=float("nan")), qa.SAGE_ERR_INVALID_ARG), (dict(k4=FAKE + 1), qa.SAGE_ERR_INVALID_ARG),
-    (dict(Hkv=4), qa.SAGE_ERR_INVALID_ARG), (dict(D=129), qa.SAGE_ERR_UNSUPPORTED),
+    (dict(Hkv=4), qa.SAGE_ERR_INVALID_ARG), (dict(D=257), qa.SAGE_ERR_UNSUPPORTED),
     (dict(D=0), qa.SAGE_ERR_INVALID_ARG),
 ])
 def test_attn_fwd_mxfp4_rejects(kw, code):

@@ -9,8 +9,10 @@
 //         each query and of each (smoothed) key, on v_mfma_scale_f32_32x32x64_f8f6f4
 //         in FP4 mode -- the scales are applied inside the matrix instruction, so the
 //         scores arrive in fp32;
-//   s2  = fp32(S * c), c = sm_scale * log2(e); running max m over 64-key tiles;
-//         t = s2 - m (so the row maximum has t = 0 and p = 1 exactly);
+//   t   = fma(S, c, -m), c = sm_scale * log2(e), m the running max of S c over 64-key
+//         tiles rounded toward -inf, so that the row maximum has 0 <= t < one ulp of m
+//         and p = 1 (to 2^-20, never below 1: a p of the maximum just below 1 would
+//         give its P block the next lower exponent and clip it from 8 X to 6 X);
 //         p = 2^t; l = alpha * l + sum p (unquantised);
 //   P^  = e2m1(p / X) per 32 keys (one lane's keys), X = 2^(floor(log2 pmax) - 2);
 //   O   = alpha * O + P^ V^ on the same instruction with P's and V's scales.
@@ -116,6 +118,13 @@ struct MXParams {
     int B, Hq, Hkv, G, D, QT;
     float cscale;  // sm_scale * log2(e)
 };
+
+// three-input maximum of scores straight from the matrix instruction: the
+// NaN-propagating maximum needs no quieting of its inputs (fmaxf would add one
+// instruction per pair)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
 
 __device__ __forceinline__ int mx_exp_dev(float amax) {  // floor(log2 amax) - 2, at least -126
     return max(int((__float_as_uint(amax) >> 23) & 0xffu) - 129, -126);
@@ -262,26 +271,24 @@ attn_mx_kernel(MXParams p) {
             for (int kt = 0; kt < 2; kt++)
 #pragma unroll
                 for (int r = 0; r < 16; r++)
-                    S[kt][r] = (16 * kt + r < t) ? S[kt][r] * c : -INFINITY;
-        } else {
-#pragma unroll
-            for (int kt = 0; kt < 2; kt++)
-#pragma unroll
-                for (int r = 0; r < 16; r++) S[kt][r] *= c;
+                    if (!(16 * kt + r < t)) S[kt][r] = -INFINITY;
         }
 #pragma unroll
         for (int kt = 0; kt < 2; kt++) {
-            float a = fmaxf(fmaxf(S[kt][0], S[kt][1]), S[kt][2]);
+            float a = max3f(S[kt][0], S[kt][1], S[kt][2]);
 #pragma unroll
-            for (int r = 3; r + 1 < 16; r += 2) a = fmaxf(fmaxf(a, S[kt][r]), S[kt][r + 1]);
-            mx = fmaxf(mx, fmaxf(a, S[kt][15]));
+            for (int r = 3; r + 1 < 16; r += 2) a = max3f(a, S[kt][r], S[kt][r + 1]);
+            mx = max3f(mx, a, S[kt][15]);
         }
-        const float mnew = fmaxf(m, halves_max(mx));
+        // the tile's row maximum in log2 units, rounded toward -inf, so that the fma
+        // t = S c - m of the maximum is >= 0 and below one ulp of m: its p is 1
+        const float tr = halves_max(mx);
+        float mt = tr * c;
+        if (__builtin_fmaf(tr, c, -mt) < 0.0f) mt = __uint_as_float(__float_as_uint(mt) + (mt > 0.0f ? -1 : 1));
+        const float mnew = fmaxf(m, mt);
         const float alpha = __builtin_amdgcn_exp2f(m - mnew);
         m = mnew;
-        // this lane's P block: its largest p is 2^(mx - m) (the same subtraction as that
-        // element's), so the block exponent is known before any p is formed
-        const int E = mx_exp_dev(__builtin_amdgcn_exp2f(mx - mnew));
+        const int E = mx_exp_dev(__builtin_amdgcn_exp2f(__builtin_fmaf(mx, c, -mnew)));
         const float X = __uint_as_float(uint32_t(E + 127) << 23);
         v4i pk;
         float acc[4];
@@ -291,7 +298,7 @@ attn_mx_kernel(MXParams p) {
             float q[8];
 #pragma unroll
             for (int e = 0; e < 8; e++) {
-                q[e] = __builtin_amdgcn_exp2f(S[kt][r0 + e] - mnew);
+                q[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kt][r0 + e], c, -mnew));
                 acc[e & 3] = (w == 0 && e < 4) ? q[e] : acc[e & 3] + q[e];
             }
             int x = 0;

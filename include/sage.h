@@ -291,7 +291,7 @@ sage_status sage_attn_fwd_varlen_g(const int8_t* q_i8, const float* q_scale, con
  * Scores: S = sum of dequantised Q * K products (scales applied inside the matrix
  * instruction, fp32), s2 = fp32(S * fp32(sm_scale * log2 e)), t = s2 - m in fp32, so
  * the row maximum has p = 1 exactly.  Head dims up to 256 (Dp = 64, 128 or 256, as
- * above); dense batches.  Layouts (row-major, innermost last):
+ * above); dense batches here, packed ones below.  Layouts (row-major, innermost last):
  *   q4      uint8 [B][H_qo][N_pad(Nq)][Dp/2]      q4_exp  uint8 [B][H_qo][N_pad(Nq)][Dp/32]
  *   k4      uint8 [B][H_kv][N_pad(Nkv)][Dp/2]     k4_exp  uint8 [B][H_kv][N_pad(Nkv)][Dp/32]
  *   k_mean  float [B][H_kv][D]
@@ -322,6 +322,27 @@ sage_status sage_attn_fwd_mxfp4(const uint8_t* q4, const uint8_t* q4_exp, const 
                                 const uint8_t* v4, const uint8_t* v4_exp, void* out, sage_dtype out_dtype,
                                 sage_layout out_layout, int B, int H_qo, int H_kv, int Nq, int Nkv, int D,
                                 int is_causal, float sm_scale, void* stream);
+
+/* The MXFP4 calls on a packed batch (README "Available APIs", sageattn_varlen; the dense
+ * scheme per sequence, as for the INT8 calls): q (total_q, H_qo, D), k and v
+ * (total_kv, H_kv, D), cu_seqlens as for sage_quant_qk_varlen.  Rows and slots per head
+ * as there: q4 [H_qo][rows(total_q)][Dp/2], q4_exp [H_qo][rows(total_q)][Dp/32],
+ * k4 / k4_exp likewise over H_kv and total_kv, v4 [H_kv][slots(total_kv)][Dp][32],
+ * v4_exp [H_kv][slots(total_kv)][2][32][Dp/32], k_mean [B][H_kv][D]; out
+ * [total_q][H_qo][D].  Workspace: H_kv * slots(total_kv) * D * 8 bytes. */
+size_t sage_quant_mxfp4_varlen_workspace_bytes(int B, int H_kv, int total_kv, int D);
+sage_status sage_quant_mxfp4_varlen(const void* q, const void* k, const void* v, sage_dtype dtype,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int B, int H_qo,
+                                    int H_kv, int total_q, int total_kv, int max_seqlen_q, int max_seqlen_kv, int D,
+                                    uint8_t* q4, uint8_t* q4_exp, uint8_t* k4, uint8_t* k4_exp, float* k_mean,
+                                    uint8_t* v4, uint8_t* v4_exp, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+sage_status sage_attn_fwd_mxfp4_varlen(const uint8_t* q4, const uint8_t* q4_exp, const uint8_t* k4,
+                                       const uint8_t* k4_exp, const uint8_t* v4, const uint8_t* v4_exp, void* out,
+                                       sage_dtype out_dtype, const int32_t* cu_seqlens_q,
+                                       const int32_t* cu_seqlens_kv, int B, int H_qo, int H_kv, int total_q,
+                                       int total_kv, int max_seqlen_q, int max_seqlen_kv, int D, int is_causal,
+                                       float sm_scale, void* stream);
 
 #ifdef __cplusplus
 }

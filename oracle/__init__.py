@@ -408,3 +408,33 @@ def attn_emulate_mxfp4(Q: MXQuantized, causal: bool, sm_scale: float, rows: np.n
                                  int(bool(causal)), float(sm_scale), rows, len(rows), out,
                                  amb.ctypes.data_as(ctypes.c_void_p) if amb is not None else None)
     return (out, amb) if with_ambiguity else out
+
+
+def quantize_mxfp4_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q, cu_k):
+    """Per-sequence MXQuantized of a packed batch (None where the sequence has no key)."""
+    out = []
+    for b in range(len(cu_q) - 1):
+        if int(cu_k[b + 1]) == int(cu_k[b]):
+            out.append(None)
+            continue
+        out.append(quantize_mxfp4(_seq(q, cu_q, b), _seq(k, cu_k, b), _seq(v, cu_k, b)))
+    return out
+
+
+def attn_emulate_mxfp4_varlen(Qs, causal: bool, sm_scale: float, rows: np.ndarray, D: int,
+                              with_ambiguity: bool = False):
+    """MXFP4 emulation rows of a packed batch; a sequence without keys outputs zeros."""
+    amb_parts = {}
+
+    def fn(b, local):
+        if Qs[b] is None:
+            return None
+        o, a = attn_emulate_mxfp4(Qs[b], causal, sm_scale, local, with_ambiguity=True)
+        amb_parts[b] = a
+        return o
+
+    out = _per_sequence(rows, D, fn)
+    if not with_ambiguity:
+        return out
+    amb = _per_sequence(rows, D, lambda b, local: amb_parts.get(b))
+    return out, amb

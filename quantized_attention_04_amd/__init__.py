@@ -17,6 +17,7 @@ Microscaling FP4 (OCP MXFP4 blocks of 32 on both products, head dim <= 256):
     quant_mxfp4(q, k, v, layout) -> MXQuant
     attn_fwd_mxfp4(mq, out_dtype, layout, is_causal, sm_scale) -> out
     sageattn_mxfp4(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None)
+    quant_mxfp4_varlen, attn_fwd_mxfp4_varlen, sageattn_mxfp4_varlen (packed batches)
 Packed variable-length batches (q (total_q, H, D), cu_seqlens prefix sums):
     quant_qk_varlen, quant_v_varlen, attn_fwd_varlen,
     sageattn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
@@ -36,6 +37,7 @@ __all__ = [
     "SageError", "lib", "library_path", "QKQuant", "VQuant", "quant_qk", "quant_v", "attn_fwd", "debug_qk_int32",
     "quant_qkv", "sageattn", "QKQuantVarlen", "VQuantVarlen", "quant_qk_varlen", "quant_v_varlen",
     "quant_qkv_varlen", "attn_fwd_varlen", "MXQuant", "quant_mxfp4", "attn_fwd_mxfp4", "sageattn_mxfp4",
+    "MXQuantVarlen", "quant_mxfp4_varlen", "attn_fwd_mxfp4_varlen", "sageattn_mxfp4_varlen",
     "sageattn_varlen", "varlen_rows", "varlen_slots", "padded_dim", "num_blocks", "SAGE_OK", "SAGE_ERR_INVALID_ARG", "SAGE_ERR_UNSUPPORTED",
     "SAGE_ERR_WORKSPACE", "SAGE_ERR_DEVICE", "SAGE_ERR_HIP",
 ]
@@ -89,6 +91,12 @@ _EXPORTS = {
                          + [ctypes.c_void_p] * 7 + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "sage_attn_fwd_mxfp4": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] * 2 + [ctypes.c_int] * 7
                             + [ctypes.c_float, ctypes.c_void_p]),
+    "sage_quant_mxfp4_varlen_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
+    "sage_quant_mxfp4_varlen": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] + [ctypes.c_void_p] * 2
+                                + [ctypes.c_int] * 8 + [ctypes.c_void_p] * 7 + [ctypes.c_void_p, ctypes.c_size_t,
+                                                                                ctypes.c_void_p]),
+    "sage_attn_fwd_mxfp4_varlen": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] + [ctypes.c_void_p] * 2
+                                   + [ctypes.c_int] * 9 + [ctypes.c_float, ctypes.c_void_p]),
     "sage_attn_fwd_varlen_g": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] + [ctypes.c_void_p] * 2
                                + [ctypes.c_int] * 9 + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                        ctypes.c_void_p]),
@@ -621,3 +629,89 @@ def sageattn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
     attends only to its own keys); returns q's dtype, shape (total_q, Hq, D)."""
     qk, vq = quant_qkv_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, pv, gran=qk_gran)
     return attn_fwd_varlen(qk, vq, q.dtype, is_causal, sm_scale, accum)
+
+
+@dataclasses.dataclass
+class MXQuantVarlen:
+    """Outputs of sage_quant_mxfp4_varlen (packed rows and slots per head)."""
+    q4: torch.Tensor       # uint8 [Hq, rows(total_q), Dp/2]
+    q4_exp: torch.Tensor   # uint8 [Hq, rows(total_q), Dp/32]
+    k4: torch.Tensor       # uint8 [Hkv, rows(total_kv), Dp/2]
+    k4_exp: torch.Tensor   # uint8 [Hkv, rows(total_kv), Dp/32]
+    k_mean: torch.Tensor   # f32   [B, Hkv, D]
+    v4: torch.Tensor       # uint8 [Hkv, slots(total_kv), Dp, 32]
+    v4_exp: torch.Tensor   # uint8 [Hkv, slots(total_kv), 2, 32, Dp/32]
+    cu_q: torch.Tensor
+    cu_k: torch.Tensor
+    B: int
+    Hq: int
+    Hkv: int
+    total_q: int
+    total_k: int
+    max_q: int
+    max_k: int
+    D: int
+
+
+def quant_mxfp4_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                       cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+                       workspace: Optional[torch.Tensor] = None, out: Optional[MXQuantVarlen] = None) -> MXQuantVarlen:
+    """quant_mxfp4 on a packed batch: each sequence quantised on its own."""
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _check_input(x, name)
+    if not (q.dtype == k.dtype == v.dtype) or not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must share dtype and device")
+    total_q, Hq, D = _packed_dims(q, "q")
+    total_k, Hkv, Dk = _packed_dims(k, "k")
+    if Dk != D or tuple(v.shape) != (total_k, Hkv, D):
+        raise ValueError("q, k and v disagree on heads, tokens or head_dim")
+    dev = q.device
+    cq, ck = _cu(cu_seqlens_q, dev, "cu_seqlens_q"), _cu(cu_seqlens_k, dev, "cu_seqlens_k")
+    if cq.numel() != ck.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must describe the same number of sequences")
+    B = cq.numel() - 1
+    L = lib()
+    Dp = max(padded_dim(D), 64)
+    rq, rk, sk = varlen_rows(total_q, B), varlen_rows(total_k, B), varlen_slots(total_k, B)
+    if out is None:
+        u8 = dict(dtype=torch.uint8, device=dev)
+        out = MXQuantVarlen(torch.empty(Hq, rq, Dp // 2, **u8), torch.empty(Hq, rq, Dp // 32, **u8),
+                            torch.empty(Hkv, rk, Dp // 2, **u8), torch.empty(Hkv, rk, Dp // 32, **u8),
+                            torch.empty(B, Hkv, D, dtype=torch.float32, device=dev),
+                            torch.empty(Hkv, sk, Dp, 32, **u8), torch.empty(Hkv, sk, 2, 32, Dp // 32, **u8),
+                            cq, ck, B, Hq, Hkv, total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), D)
+    need = L.sage_quant_mxfp4_varlen_workspace_bytes(B, Hkv, total_k, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=dev)
+    _check(L.sage_quant_mxfp4_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), _DT[q.dtype], cq.data_ptr(),
+                                     ck.data_ptr(), B, Hq, Hkv, total_q, total_k, int(max_seqlen_q),
+                                     int(max_seqlen_k), D, out.q4.data_ptr(), out.q4_exp.data_ptr(),
+                                     out.k4.data_ptr(), out.k4_exp.data_ptr(), out.k_mean.data_ptr(),
+                                     out.v4.data_ptr(), out.v4_exp.data_ptr(), workspace.data_ptr(),
+                                     workspace.numel(), _stream(dev)))
+    return out
+
+
+def attn_fwd_mxfp4_varlen(mq: MXQuantVarlen, out_dtype: torch.dtype, is_causal: bool = False,
+                          sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    if out_dtype not in _DT:
+        raise ValueError("out_dtype must be float16 or bfloat16")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(mq.D)
+    dev = mq.q4.device
+    if out is None:
+        out = torch.empty(mq.total_q, mq.Hq, mq.D, dtype=out_dtype, device=dev)
+    _check(lib().sage_attn_fwd_mxfp4_varlen(mq.q4.data_ptr(), mq.q4_exp.data_ptr(), mq.k4.data_ptr(),
+                                            mq.k4_exp.data_ptr(), mq.v4.data_ptr(), mq.v4_exp.data_ptr(),
+                                            out.data_ptr(), _DT[out_dtype], mq.cu_q.data_ptr(), mq.cu_k.data_ptr(),
+                                            mq.B, mq.Hq, mq.Hkv, mq.total_q, mq.total_k, mq.max_q, mq.max_k, mq.D,
+                                            int(bool(is_causal)), float(sm_scale), _stream(dev)))
+    return out
+
+
+def sageattn_mxfp4_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                          cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, is_causal: bool = False,
+                          sm_scale: Optional[float] = None) -> torch.Tensor:
+    """The microscaling FP4 variant on a packed batch (output (total_q, H_qo, D) in q's dtype)."""
+    mq = quant_mxfp4_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    return attn_fwd_mxfp4_varlen(mq, q.dtype, is_causal, sm_scale)

@@ -512,6 +512,76 @@ sage_status sage_quant_mxfp4(const void* q, const void* k, const void* v, sage_d
     return launch_status(sage::launch_quant_mxfp4(a, (hipStream_t)stream), "sage_quant_mxfp4");
 }
 
+size_t sage_quant_mxfp4_varlen_workspace_bytes(int B, int H_kv, int total_kv, int D) {
+    if (B <= 0 || H_kv <= 0 || total_kv <= 0 || D <= 0 || D > 256) return 0;
+    return size_t(H_kv) * size_t(varlen_slots(total_kv, B)) * size_t(D) * sizeof(double);
+}
+
+sage_status sage_quant_mxfp4_varlen(const void* q, const void* k, const void* v, sage_dtype dtype,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int B, int H_qo,
+                                    int H_kv, int total_q, int total_kv, int max_seqlen_q, int max_seqlen_kv, int D,
+                                    uint8_t* q4, uint8_t* q4_exp, uint8_t* k4, uint8_t* k4_exp, float* k_mean,
+                                    uint8_t* v4, uint8_t* v4_exp, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+    if (!q || !k || !v || !q4 || !q4_exp || !k4 || !k4_exp || !k_mean || !v4 || !v4_exp)
+        return fail(SAGE_ERR_INVALID_ARG, "sage_quant_mxfp4_varlen: null tensor pointer");
+    if (dtype != SAGE_FP16 && dtype != SAGE_BF16) return fail(SAGE_ERR_INVALID_ARG, "bad dtype %d", int(dtype));
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(q4, 16) || !aligned(k4, 16) ||
+        !aligned(v4, 16) || !aligned(k_mean, 4))
+        return fail(SAGE_ERR_INVALID_ARG, "sage_quant_mxfp4_varlen: misaligned tensor");
+    sage_status s =
+        check_varlen(cu_seqlens_q, cu_seqlens_kv, B, H_qo, H_kv, total_q, total_kv, max_seqlen_q, max_seqlen_kv, D);
+    if (s != SAGE_OK) return s;
+    const size_t need = sage_quant_mxfp4_varlen_workspace_bytes(B, H_kv, total_kv, D);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 8))
+        return fail(SAGE_ERR_WORKSPACE,
+                    "sage_quant_mxfp4_varlen: workspace of %zu bytes (8-byte aligned) required, got %zu", need,
+                    workspace ? workspace_bytes : size_t(0));
+    s = check_device();
+    if (s != SAGE_OK) return s;
+    sage::QuantMXArgs a{};
+    a.q = q, a.k = k, a.v = v;
+    a.bf16 = dtype == SAGE_BF16;
+    a.B = B, a.Hq = H_qo, a.Hkv = H_kv, a.Nq = max_seqlen_q, a.Nkv = max_seqlen_kv, a.D = D;
+    a.cu_q = cu_seqlens_q, a.cu_k = cu_seqlens_kv, a.total_q = total_q, a.total_k = total_kv;
+    a.q4 = q4, a.q4_exp = q4_exp, a.k4 = k4, a.k4_exp = k4_exp, a.k_mean = k_mean, a.v4 = v4, a.v4_exp = v4_exp;
+    a.workspace = workspace;
+    return launch_status(sage::launch_quant_mxfp4(a, (hipStream_t)stream), "sage_quant_mxfp4_varlen");
+}
+
+sage_status sage_attn_fwd_mxfp4_varlen(const uint8_t* q4, const uint8_t* q4_exp, const uint8_t* k4,
+                                       const uint8_t* k4_exp, const uint8_t* v4, const uint8_t* v4_exp, void* out,
+                                       sage_dtype out_dtype, const int32_t* cu_seqlens_q,
+                                       const int32_t* cu_seqlens_kv, int B, int H_qo, int H_kv, int total_q,
+                                       int total_kv, int max_seqlen_q, int max_seqlen_kv, int D, int is_causal,
+                                       float sm_scale, void* stream) {
+    if (!q4 || !q4_exp || !k4 || !k4_exp || !v4 || !v4_exp || !out)
+        return fail(SAGE_ERR_INVALID_ARG, "sage_attn_fwd_mxfp4_varlen: null tensor pointer");
+    if (out_dtype != SAGE_FP16 && out_dtype != SAGE_BF16)
+        return fail(SAGE_ERR_INVALID_ARG, "bad out dtype %d", int(out_dtype));
+    if (is_causal != 0 && is_causal != 1) return fail(SAGE_ERR_INVALID_ARG, "is_causal must be 0 or 1");
+    if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
+        return fail(SAGE_ERR_INVALID_ARG, "sm_scale must be finite and > 0 (got %g)", double(sm_scale));
+    if (!aligned(q4, 16) || !aligned(k4, 16) || !aligned(v4, 16) || !aligned(out, (D % 4) == 0 ? 8 : 2))
+        return fail(SAGE_ERR_INVALID_ARG, "sage_attn_fwd_mxfp4_varlen: misaligned tensor");
+    sage_status s =
+        check_varlen(cu_seqlens_q, cu_seqlens_kv, B, H_qo, H_kv, total_q, total_kv, max_seqlen_q, max_seqlen_kv, D);
+    if (s != SAGE_OK) return s;
+    const int64_t grid = int64_t((max_seqlen_q + 127) / 128) * H_qo * B;
+    if (grid > INT32_MAX) return fail(SAGE_ERR_UNSUPPORTED, "sage_attn_fwd_mxfp4_varlen: grid too large");
+    s = check_device();
+    if (s != SAGE_OK) return s;
+    sage::AttnMXArgs a{};
+    a.q4 = q4, a.q4_exp = q4_exp, a.k4 = k4, a.k4_exp = k4_exp, a.v4 = v4, a.v4_exp = v4_exp;
+    a.out = out;
+    a.out_bf16 = out_dtype == SAGE_BF16;
+    a.B = B, a.Hq = H_qo, a.Hkv = H_kv, a.Nq = max_seqlen_q, a.Nkv = max_seqlen_kv, a.D = D;
+    a.causal = is_causal;
+    a.sm_scale = sm_scale;
+    a.cu_q = cu_seqlens_q, a.cu_k = cu_seqlens_kv, a.total_q = total_q, a.total_k = total_kv;
+    return launch_status(sage::launch_attn_mxfp4(a, (hipStream_t)stream), "sage_attn_fwd_mxfp4_varlen");
+}
+
 sage_status sage_attn_fwd_mxfp4(const uint8_t* q4, const uint8_t* q4_exp, const uint8_t* k4, const uint8_t* k4_exp,
                                 const uint8_t* v4, const uint8_t* v4_exp, void* out, sage_dtype out_dtype,
                                 sage_layout out_layout, int B, int H_qo, int H_kv, int Nq, int Nkv, int D,

@@ -338,7 +338,8 @@ attn_mx_kernel(MXParams p) {
     const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;  // a query that sees no key: zeros
     if (qidx >= Nq) return;
     const bool vec4 = (p.D & 3) == 0;
-    uint16_t* orow = (uint16_t*)p.out + b * p.osb + h * p.osh + qidx * p.osq;
+    const int64_t obase = p.qm.cu != nullptr ? qv.start * p.osq : b * p.osb;
+    uint16_t* orow = (uint16_t*)p.out + obase + h * p.osh + qidx * p.osq;
 #pragma unroll
     for (int dt = 0; dt < C::DT; dt++)
 #pragma unroll
@@ -373,11 +374,13 @@ hipError_t launch_mx_attn_t(const AttnMXArgs& a, hipStream_t s) {
     p.v4 = a.v4;
     p.v4_exp = a.v4_exp;
     p.out = a.out;
-    p.qm = make_seq_map(0, nullptr, a.B, a.Hq, a.Nq, 0, a.D);
-    p.km = make_seq_map(0, nullptr, a.B, a.Hkv, a.Nkv, 0, a.D);
-    p.osb = a.out_nhd ? int64_t(a.Nq) * a.Hq * a.D : int64_t(a.Hq) * a.Nq * a.D;
-    p.osh = a.out_nhd ? int64_t(a.D) : int64_t(a.Nq) * a.D;
-    p.osq = a.out_nhd ? int64_t(a.Hq) * a.D : int64_t(a.D);
+    // the quantised operands' rows and slots (dense or packed)
+    p.qm = make_seq_map(0, a.cu_q, a.B, a.Hq, a.Nq, a.total_q, a.D);
+    p.km = make_seq_map(0, a.cu_k, a.B, a.Hkv, a.Nkv, a.total_k, a.D);
+    const bool tok_major = a.out_nhd || a.cu_q != nullptr;  // (.., token, head, dim) output
+    p.osb = a.cu_q != nullptr ? 0 : (a.out_nhd ? int64_t(a.Nq) * a.Hq * a.D : int64_t(a.Hq) * a.Nq * a.D);
+    p.osh = tok_major ? int64_t(a.D) : int64_t(a.Nq) * a.D;
+    p.osq = tok_major ? int64_t(a.Hq) * a.D : int64_t(a.D);
     p.B = a.B;
     p.Hq = a.Hq;
     p.Hkv = a.Hkv;

@@ -55,14 +55,18 @@ struct AttnArgs {
     int thread_gran;  // scales of sage_quant_qkv's per-thread granularity
 };
 
-// Microscaling FP4 (dense batches): codes and E8M0 exponent bytes of Q, smoothed K and V
-// in the layouts of include/sage.h; workspace = the fp64 K block channel sums.
+// Microscaling FP4: codes and E8M0 exponent bytes of Q, smoothed K and V in the layouts
+// of include/sage.h; workspace = the fp64 K block channel sums.  Dense or packed batches
+// as for the INT8 path (cu_* null: dense).
 struct QuantMXArgs {
     const void* q;
     const void* k;
     const void* v;
     int bf16, layout_nhd;
     int B, Hq, Hkv, Nq, Nkv, D;
+    const int32_t* cu_q;
+    const int32_t* cu_k;
+    int total_q, total_k;
     uint8_t* q4;
     uint8_t* q4_exp;
     uint8_t* k4;
@@ -85,6 +89,9 @@ struct AttnMXArgs {
     int B, Hq, Hkv, Nq, Nkv, D;
     int causal;
     float sm_scale;
+    const int32_t* cu_q;
+    const int32_t* cu_k;
+    int total_q, total_k;
 };
 
 struct DebugQKArgs {

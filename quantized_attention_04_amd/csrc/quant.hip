@@ -787,8 +787,8 @@ __global__ __launch_bounds__(2 * DP) void mx_v_kernel(const uint16_t* __restrict
 namespace {
 template <bool BF16, int DP, bool VEC8>
 hipError_t launch_mx_t(const QuantMXArgs& a, hipStream_t s) {
-    const SeqMap mq = make_seq_map(a.layout_nhd, nullptr, a.B, a.Hq, a.Nq, 0, a.D);
-    const SeqMap mk = make_seq_map(a.layout_nhd, nullptr, a.B, a.Hkv, a.Nkv, 0, a.D);
+    const SeqMap mq = make_seq_map(a.layout_nhd, a.cu_q, a.B, a.Hq, a.Nq, a.total_q, a.D);
+    const SeqMap mk = make_seq_map(a.layout_nhd, a.cu_k, a.B, a.Hkv, a.Nkv, a.total_k, a.D);
     k_mean_partial_kernel<BF16, DP, VEC8><<<dim3(mk.NB, a.Hkv, a.B), 256, 0, s>>>((const uint16_t*)a.k, mk, a.D,
                                                                                 (double*)a.workspace);
     const int tot = a.B * a.Hkv * a.D;

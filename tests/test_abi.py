@@ -376,3 +376,56 @@ def test_mxfp4_valid_arguments_reach_the_device_check_only():
         pytest.skip("would launch kernels on fake pointers")
     assert _mxq() == qa.SAGE_ERR_DEVICE
     assert _mxa() == qa.SAGE_ERR_DEVICE
+
+
+def _mxqv(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, cq=FAKE, ck=FAKE, B=2, Hq=2, Hkv=2, tq=100, tk=100, mq=64, mk=64, D=64,
+             q4=FAKE, q4e=FAKE, k4=FAKE, k4e=FAKE, km=FAKE, v4=FAKE, v4e=FAKE, ws=FAKE, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return qa.lib().sage_quant_mxfp4_varlen(a["q"], a["k"], a["v"], a["dtype"], a["cq"], a["ck"], a["B"], a["Hq"],
+                                            a["Hkv"], a["tq"], a["tk"], a["mq"], a["mk"], a["D"], a["q4"], a["q4e"],
+                                            a["k4"], a["k4e"], a["km"], a["v4"], a["v4e"], a["ws"], a["ws_bytes"],
+                                            a["stream"])
+
+
+def _mxav(**kw):
+    a = dict(q4=FAKE, q4e=FAKE, k4=FAKE, k4e=FAKE, v4=FAKE, v4e=FAKE, out=FAKE, odt=1, cq=FAKE, ck=FAKE, B=2, Hq=2,
+             Hkv=2, tq=100, tk=100, mq=64, mk=64, D=64, causal=0, sm=0.125, stream=None)
+    a.update(kw)
+    return qa.lib().sage_attn_fwd_mxfp4_varlen(a["q4"], a["q4e"], a["k4"], a["k4e"], a["v4"], a["v4e"], a["out"],
+                                               a["odt"], a["cq"], a["ck"], a["B"], a["Hq"], a["Hkv"], a["tq"], a["tk"],
+                                               a["mq"], a["mk"], a["D"], a["causal"], a["sm"], a["stream"])
+
+
+def test_mxfp4_varlen_workspace_sizes():
+    L = qa.lib()
+    assert L.sage_quant_mxfp4_varlen_workspace_bytes(3, 2, 500, 64) == 2 * qa.varlen_slots(500, 3) * 64 * 8
+    assert L.sage_quant_mxfp4_varlen_workspace_bytes(3, 2, 500, 257) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(v=None), qa.SAGE_ERR_INVALID_ARG), (dict(cq=None), qa.SAGE_ERR_INVALID_ARG),
+    (dict(ck=FAKE + 2), qa.SAGE_ERR_INVALID_ARG), (dict(dtype=7), qa.SAGE_ERR_INVALID_ARG),
+    (dict(tq=0), qa.SAGE_ERR_INVALID_ARG), (dict(Hq=3), qa.SAGE_ERR_INVALID_ARG),
+    (dict(D=300), qa.SAGE_ERR_UNSUPPORTED), (dict(ws=None), qa.SAGE_ERR_WORKSPACE),
+    (dict(ws_bytes=8), qa.SAGE_ERR_WORKSPACE),
+])
+def test_quant_mxfp4_varlen_rejects(kw, code):
+    assert _mxqv(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(out=None), qa.SAGE_ERR_INVALID_ARG), (dict(cq=None), qa.SAGE_ERR_INVALID_ARG),
+    (dict(odt=3), qa.SAGE_ERR_INVALID_ARG), (dict(causal=5), qa.SAGE_ERR_INVALID_ARG),
+    (dict(sm=-1.0), qa.SAGE_ERR_INVALID_ARG), (dict(tk=0), qa.SAGE_ERR_INVALID_ARG),
+    (dict(D=300), qa.SAGE_ERR_UNSUPPORTED),
+])
+def test_attn_fwd_mxfp4_varlen_rejects(kw, code):
+    assert _mxav(**kw) == code
+
+
+def test_mxfp4_varlen_valid_arguments_reach_the_device_check_only():
+    if torch.cuda.is_available():
+        pytest.skip("would launch kernels on fake pointers")
+    assert _mxqv() == qa.SAGE_ERR_DEVICE
+    assert _mxav() == qa.SAGE_ERR_DEVICE

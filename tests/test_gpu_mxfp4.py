@@ -187,3 +187,104 @@ def test_mxfp4_negative_zeros_and_zero_blocks():
     mq, out = c.gpu()
     check_mx_bit_exact(c, mq)
     check_mx_output(c, out, _rows(w, "all"), False)
+
+
+# ----------------------------------------------------------------------------- packed batches
+
+VW = si.VarlenWorkload
+VCASES = [
+    VW("mx_mixed", (1, 64, 100, 1000, 257), (1, 64, 100, 1000, 257), 4, 2, 128, seed=50),
+    VW("mx_q_ne_k_causal_d96", (10, 300, 64, 5), (100, 300, 30, 64), 4, 4, 96, dtype="fp16", causal=True, seed=51),
+    VW("mx_empty_sequences_d64", (0, 50, 20, 7), (10, 0, 80, 7), 2, 2, 64, causal=True, seed=52),
+    VW("mx_d256_causal", (100, 300, 65), (100, 300, 130), 4, 2, 256, causal=True, seed=53),
+]
+
+
+class MXVCase:
+    def __init__(self, w):
+        self.w = w
+        note(f"[mx varlen case] {w}")
+        self.q, self.k, self.v, self.cu_q, self.cu_k = si.make_varlen(w)
+        self.qf, self.kf, self.vf = (x.float().numpy() for x in (self.q, self.k, self.v))
+        self.cq, self.ck = self.cu_q.numpy().astype(np.int64), self.cu_k.numpy().astype(np.int64)
+        self.Qs = oracle.quantize_mxfp4_varlen(self.qf, self.kf, self.vf, self.cq, self.ck)
+
+    def gpu(self):
+        w, dev = self.w, "cuda:0"
+        note(f"[gpu] mxfp4 varlen {w.name} B{w.B} Hq{w.Hq} Hkv{w.Hkv} D{w.D} causal={w.causal}")
+        q, k, v, cq, ck = (x.to(dev) for x in (self.q, self.k, self.v, self.cu_q, self.cu_k))
+        mq = qa.quant_mxfp4_varlen(q, k, v, cq, ck, max(w.lens_q + (1,)), max(w.lens_k + (1,)))
+        out = qa.attn_fwd_mxfp4_varlen(mq, w.torch_dtype, w.causal, sm_scale_of(w.D))
+        torch.cuda.synchronize()
+        return mq, out
+
+
+@pytest.mark.parametrize("w", VCASES, ids=[c.name for c in VCASES])
+def test_mxfp4_varlen_quantization_bit_exact(w):
+    c = MXVCase(w)
+    mq, _ = c.gpu()
+    Dp = qa.padded_dim(w.D)
+    nbd = (w.D + 31) // 32
+    q4, q4e = _nibbles(mq.q4.cpu().numpy()), mq.q4_exp.cpu().numpy().astype(np.int64)
+    k4, k4e = _nibbles(mq.k4.cpu().numpy()), mq.k4_exp.cpu().numpy().astype(np.int64)
+    v4 = _nibbles(mq.v4.cpu().numpy())                         # [Hkv, slots, Dp, 64]
+    ve = mq.v4_exp.cpu().numpy().astype(np.int64)              # [Hkv, slots, 2, 32, Dp/32]
+    km = mq.k_mean.cpu().numpy()
+    for b in range(w.B):
+        nq, nk = w.lens_q[b], w.lens_k[b]
+        if nq:
+            R = int(c.cq[b]) + 64 * b
+            qc, qe = oracle.quant_mxfp4_rows(oracle._seq(c.qf, c.cq, b))
+            np.testing.assert_array_equal(q4[:, R:R + nq, :w.D], qc[0], err_msg=f"q4 seq {b}")
+            np.testing.assert_array_equal(q4e[:, R:R + nq, :nbd], qe[0] + 127, err_msg=f"q4_exp seq {b}")
+            nb = qa.num_blocks(nq)
+            assert not q4[:, R + nq:R + 64 * nb].any() and (q4e[:, R + nq:R + 64 * nb] == 1).all()
+        if nk:
+            o = c.Qs[b]
+            R = int(c.ck[b]) + 64 * b
+            S, nb = R // 64, qa.num_blocks(nk)
+            np.testing.assert_array_equal(km[b], o.k_mean[0], err_msg=f"k_mean seq {b}")
+            np.testing.assert_array_equal(k4[:, R:R + nk, :w.D], o.k_code[0], err_msg=f"k4 seq {b}")
+            np.testing.assert_array_equal(k4e[:, R:R + nk, :nbd], o.k_exp[0] + 127, err_msg=f"k4_exp seq {b}")
+            vt = v4[:, S:S + nb].transpose(0, 2, 1, 3).reshape(w.Hkv, Dp, nb * 64)
+            np.testing.assert_array_equal(vt[:, :w.D, :nk], o.v_code[0], err_msg=f"v4 seq {b}")
+            assert not vt[:, :, nk:].any() and not vt[:, w.D:].any()
+            e = ve[:, S:S + nb].transpose(0, 4, 3, 1, 2).reshape(w.Hkv, Dp, nb * 2)
+            nbt = (nk + 31) // 32
+            np.testing.assert_array_equal(e[:, :w.D, :nbt], o.v_exp[0] + 127, err_msg=f"v4_exp seq {b}")
+            assert (e[:, :, nbt:] == 1).all() and (e[:, w.D:] == 1).all()
+
+
+@pytest.mark.parametrize("w", VCASES, ids=[c.name for c in VCASES])
+def test_mxfp4_varlen_output_matches_oracle(w):
+    c = MXVCase(w)
+    _, out = c.gpu()
+    rows = np.array([(b, h, i) for b in range(w.B) for h in range(w.Hq) for i in range(w.lens_q[b])], np.int64)
+    sm = sm_scale_of(w.D)
+    em_raw, amb = oracle.attn_emulate_mxfp4_varlen(c.Qs, w.causal, sm, rows, w.D, with_ambiguity=True)
+    fmt = oracle.BF16 if w.dtype == "bf16" else oracle.FP16
+    em = oracle.round_to(em_raw, fmt)
+    o = out.float().cpu().numpy()
+    got = o[c.cq[rows[:, 0]] + rows[:, 2], rows[:, 1]].astype(np.float64)
+    ulp = np.ldexp(1.0, np.floor(np.log2(np.maximum(np.abs(em), 1e-30))).astype(int) - (7 if fmt == oracle.BF16 else 10))
+    excess = float((np.abs(got - em) - np.maximum(1e-2, ulp) - amb).max())
+    m = metrics(got, em)
+    note(f"[metrics] varlen {w.name} {m} worst_excess {excess}")
+    assert excess <= 0 and m["cos"] >= 0.9999, (m, excess)
+    for b in range(w.B):  # sequences without keys: zeros
+        if w.lens_k[b] == 0 and w.lens_q[b]:
+            assert not out[int(c.cq[b]):int(c.cq[b + 1])].any()
+
+
+def test_mxfp4_varlen_equals_dense_per_sequence():
+    """A packed batch and per-sequence dense calls run the same arithmetic on the same
+    tiles: bit-identical outputs."""
+    w = VW("mx_dense_equiv", (300, 64, 1000), (300, 64, 1000), 4, 2, 128, causal=True, seed=54)
+    c = MXVCase(w)
+    _, out = c.gpu()
+    for b in range(w.B):
+        q = c.q[c.cq[b]:c.cq[b + 1]][None].to("cuda:0")
+        k = c.k[c.ck[b]:c.ck[b + 1]][None].to("cuda:0")
+        v = c.v[c.ck[b]:c.ck[b + 1]][None].to("cuda:0")
+        dense = qa.sageattn_mxfp4(q, k, v, "NHD", True, sm_scale_of(w.D))
+        assert torch.equal(dense[0], out[int(c.cq[b]):int(c.cq[b + 1])]), f"sequence {b}"

@@ -29,10 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "effective attention TOPS at D=128 vs N (1K–32K); % of INT8/FP8 MFMA peak"
 PEAK_TOPS = 5000.0        # MI355X dense INT8 / FP8 matrix-core peak (TOPS)
-PEAK_HBM_GBS = 8000.0
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "attn_fwd_traffic.json")
-
-
+OPS_PER_CLK = 256 * 8192  # dense INT8 / FP8 matrix-core operations per shader clock (256 CUs)
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -176,6 +173,7 @@ def main():
     alg_ops = 4.0 * w.B * w.Hq * w.Nq * w.Nkv * Dp / (2 if w.causal else 1)
     achieved = alg_ops / (ms_attn * 1e-3) / 1e12
     traffic = None
+    sclk = None  # GHz of the attention launches, from the profiled GRBM cycle counters
     src_hash = kernel_source_hash()
     if os.path.exists(PROFILE_TRAFFIC):
         try:
@@ -184,6 +182,7 @@ def main():
             key = f"B{w.B}_H{w.Hq}_N{w.Nq}_D{w.D}_{'causal' if w.causal else 'noncausal'}"
             if pt.get("kernel_source_sha256_16") == src_hash and key in pt.get("workloads", {}):
                 traffic = pt["workloads"][key]
+                sclk = pt.get("sclk_ghz", {}).get(key)
         except (OSError, ValueError):
             traffic = None
     # quantisation kernels: HBM-bound; algorithmic bytes = one read of q, k, v (bf16)
@@ -215,7 +214,13 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_TOPS, 4), "traffic": traffic,
                      "kernel": "attn_fwd_kernel<128, fp8, noncausal, two-level, bf16>",
-                     "alg_ops_per_launch": alg_ops, "kernel_source_sha256_16": src_hash},
+                     "alg_ops_per_launch": alg_ops, "kernel_source_sha256_16": src_hash,
+                     # the same fraction against 256 CUs x 8192 ops/clk at the shader clock the
+                     # attention launches ran at: GRBM cycles per XCD / launch duration, from the
+                     # profiled run of this kernel source (profiles/attn_fwd_traffic.json)
+                     "sclk_ghz_profiled": sclk,
+                     "frac_at_profiled_sclk": (round(achieved / (OPS_PER_CLK * sclk * 1e9 / 1e12), 4)
+                                               if sclk else None)},
     }
     log(f"[bench] step {ms_step:.3f} ms  attn {ms_attn:.3f} ms ({attn_tops:.0f} TOPS, "
         f"{100 * achieved / PEAK_TOPS:.1f}% of peak)  quant {ms_quant:.3f} ms")

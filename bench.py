@@ -119,7 +119,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU: the path has no multi-GPU code "
-                                   f"(asked for --gpus {args.gpus}); see DESIGN.md for how it would shard"}))
+                                   f"(asked for --gpus {args.gpus}); one GPU's share of a sharded run is the same "
+                                   "kernels on fewer heads or sequences"}))
         sys.exit(2)
 
     import numpy as np

@@ -15,11 +15,11 @@
 //  * workgroup = 4 waves = 128 queries; each wave owns 32 queries inside one 64-token Q
 //    block (wave-uniform Q scale) and walks 64-key tiles (one K block: uniform K scale);
 //  * the vector ALU, not the matrix core, bounds this kernel: per score the softmax
-//    issues about six vector instructions, two of them (exp2, the FP8 pack) at a
+//    issues about five vector instructions, two of them (exp2, the FP8 pack) at a
 //    quarter of the full rate, against about half as many cycles of MFMA.  A wave on
 //    its own issues vector instructions at about a quarter of the rate the ALU
 //    sustains with four ready waves, so the schedule is kept simple and small (no
-//    score double buffer: 158 VGPRs at head dim 128) to fit three waves per SIMD (four
+//    score double buffer: 164 VGPRs at head dim 128) to fit three waves per SIMD (four
 //    at head dim 64), which keep the ALU fed while others wait on the matrix core,
 //    LDS or the barrier;
 //  * K^ and V^ tiles stream HBM -> LDS with direct-to-LDS 16-byte loads, two tiles
@@ -64,7 +64,7 @@ constexpr float kLog2_448 = 8.807354f;
 // Mode constants.  DP = padded head dim (64 | 128 | 256); FP8 = P.V in e4m3 (else fp16).
 template <int DP, bool FP8>
 struct Cfg {
-    static constexpr int WAVES = 4;  // one wave per SIMD; two workgroups share a CU
+    static constexpr int WAVES = 4;  // one wave per SIMD; OCC workgroups share a CU
     static constexpr int THREADS = WAVES * kWave;
     static constexpr int QW = 32;            // queries per wave
     static constexpr int BM = WAVES * QW;    // queries per workgroup

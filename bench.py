@@ -18,6 +18,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -56,10 +57,14 @@ def parse():
 
 
 def kernel_source_hash() -> str:
+    """Hash of the attention kernel's source with comments and blank lines removed, so
+    that profiled counters stay attached to the code they were taken on."""
     h = hashlib.sha256()
     for f in ("attn_fwd.hip", "common.hpp"):
-        with open(os.path.join(ROOT, "quantized_attention_04_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "quantized_attention_04_amd", "csrc", f)) as fh:
+            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
+        h.update("\n".join(ln for ln in lines if ln).encode())
     return h.hexdigest()[:16]
 
 

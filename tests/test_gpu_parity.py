@@ -187,3 +187,27 @@ def test_zero_query_block_gives_mean_of_values():
     assert float(qk.q_scale[0, 0, 0]) == 0.0
     out = c.gpu_attn(qk, vq)
     check_output(c, out, oracle.all_rows(w.B, w.Hq, w.Nq))
+
+
+@pytest.mark.parametrize("D,pv", [(128, "fp8"), (128, "fp16"), (64, "fp8"), (120, "fp8")])
+def test_extreme_scores(D, pv):
+    """Every INT8 score at its extreme, +-D * 127^2 (2064512 at D = 128): Q constant (codes
+    127, or -127 in the second head) against K rows of alternating sign per token (channel
+    mean 0, codes +-127).  Half the keys then score about +16 in log2 units and half about
+    -16; the output is the mean of the V^ rows of the winning keys."""
+    w = W("tiny", B=1, Hq=2, Hkv=2, Nq=128, Nkv=192, D=D, pv=pv, seed=31)
+    c = Case(w)
+    sign = torch.tensor([1.0, -1.0], dtype=torch.float32).view(1, 2, 1, 1)
+    q = (torch.ones(1, 2, w.Nq, D) * sign).to(c.q.dtype)
+    tok = torch.where(torch.arange(w.Nkv) % 2 == 0, 1.0, -1.0).view(1, 1, w.Nkv, 1)
+    k = (torch.ones(1, 2, w.Nkv, D) * tok).to(c.k.dtype)
+    c.q, c.k = q, k
+    c.dq, c.dk = q.to(c.dq.device), k.to(c.dk.device)
+    c.qf, c.kf = (oracle.to_hnd_f32(t, w.layout) for t in (q, k))
+    qk, vq = c.gpu_quant()
+    check_quant_bit_exact(c, qk, vq)
+    assert int(qk.q_i8[0, 0, 0, 0]) == 127 and int(qk.q_i8[0, 1, 0, 0]) == -127
+    assert int(qk.k_i8[0, 0, 0, 0]) == 127 and int(qk.k_i8[0, 0, 1, 0]) == -127
+    for causal in (False, True):
+        out = c.gpu_attn(qk, vq, causal=causal)
+        check_output(c, out, oracle.all_rows(w.B, w.Hq, w.Nq), causal=causal)

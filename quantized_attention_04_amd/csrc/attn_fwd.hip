@@ -371,28 +371,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
 
     // ---- workgroup -> (b, h, q tile)
     int b, h, qt;
-    {
-        // consecutive workgroups on one XCD share a (b, kv head), so its K^/V^ tiles are
-        // reused from that XCD's L2.  Causal: the query tiles of a group of grp kv heads
-        // run together in decreasing order of work (longest first), which shortens the
-        // tail of each group while its K^/V^ still fit in L2 and MALL.
-        const int L = xcd_remap(blockIdx.x, gridDim.x);
-        int bhk, hg;
-        if constexpr (CAUSAL) {
-            const int per = p.grp * p.G * p.QT, nkv = p.B * p.Hkv;
-            const int grp = L / per, r = L % per;
-            const int gsz = min(p.grp, nkv - grp * p.grp);  // the last group may be smaller
-            hg = r % p.G;
-            qt = p.QT - 1 - r / (p.G * gsz);
-            bhk = grp * p.grp + (r / p.G) % gsz;
-        } else {
-            hg = L % p.G;
-            qt = (L / p.G) % p.QT;
-            bhk = L / (p.G * p.QT);
-        }
-        b = bhk / p.Hkv;
-        h = (bhk % p.Hkv) * p.G + hg;
-    }
+    block_tile<CAUSAL>(p.B, p.Hkv, p.G, p.QT, p.grp, b, h, qt);
     const int hk = h / p.G;
     const SeqView qv = seq_view(p.qm, b, h), kv = seq_view(p.km, b, hk);
     const int Nq = qv.n, Nkv = kv.n, NBk = (Nkv + kBlk - 1) / kBlk;
@@ -643,12 +622,8 @@ hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s) {
                   "uniform BM");
     p.QT = (a.Nq + BM - 1) / BM;
     {
-        // causal head groups: as many kv heads (up to 4) as have K^ + V^ within 8 MiB
-        // together (an XCD's 4 MB L2 plus its share of the MALL); measured at 1K-32K
-        const int dp = a.D <= 64 ? 64 : (a.D <= 128 ? 128 : 256);
-        const int64_t head = int64_t((a.Nkv + kBlk - 1) / kBlk) * kBlk * dp * (a.fp8 ? 2 : 3);
-        const int64_t budget = int64_t(8) << 20;
-        p.grp = 4 * head <= budget ? 4 : (2 * head <= budget ? 2 : 1);
+        const int dp = a.D <= 64 ? 64 : (a.D <= 128 ? 128 : 256);  // K^ int8 + V^ fp8 | fp16
+        p.grp = causal_head_group(int64_t((a.Nkv + kBlk - 1) / kBlk) * kBlk * dp * (a.fp8 ? 2 : 3));
     }
     p.cscale = a.sm_scale * kLog2e;
     if (a.cu_q != nullptr) {  // packed (total, H_qo, D)

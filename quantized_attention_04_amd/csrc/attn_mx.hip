@@ -116,6 +116,7 @@ struct MXParams {
     SeqMap qm, km;
     int64_t osb, osh, osq;
     int B, Hq, Hkv, G, D, QT;
+    int grp;       // causal: kv heads whose query tiles are interleaved (1, 2 or 4)
     float cscale;  // sm_scale * log2(e)
 };
 
@@ -140,15 +141,7 @@ attn_mx_kernel(MXParams p) {
     const int g = lane >> 5, i = lane & 31;
 
     int b, h, qt;
-    {
-        const int L = xcd_remap(blockIdx.x, gridDim.x);
-        const int hg = L % p.G;
-        qt = (L / p.G) % p.QT;
-        if constexpr (CAUSAL) qt = p.QT - 1 - qt;
-        const int bhk = L / (p.G * p.QT);
-        b = bhk / p.Hkv;
-        h = (bhk % p.Hkv) * p.G + hg;
-    }
+    block_tile<CAUSAL>(p.B, p.Hkv, p.G, p.QT, p.grp, b, h, qt);
     const int hk = h / p.G;
     const SeqView qv = seq_view(p.qm, b, h), kv = seq_view(p.km, b, hk);
     const int Nq = qv.n, Nkv = kv.n, NBk = (Nkv + kBlk - 1) / kBlk;
@@ -387,6 +380,8 @@ hipError_t launch_mx_attn_t(const AttnMXArgs& a, hipStream_t s) {
     p.G = a.Hq / a.Hkv;
     p.D = a.D;
     p.QT = (a.Nq + C::BM - 1) / C::BM;
+    // K4 and V4 of one kv head: codes (DP / 2 bytes per token each) and exponents
+    p.grp = causal_head_group(int64_t((a.Nkv + kBlk - 1) / kBlk) * kBlk * (DP + DP / 16));
     p.cscale = a.sm_scale * 1.4426950408889634f;
     const int64_t grid = int64_t(p.QT) * a.Hq * a.B;
     attn_mx_kernel<DP, CAUSAL, OBF16><<<dim3(unsigned(grid)), C::THREADS, 0, s>>>(p);

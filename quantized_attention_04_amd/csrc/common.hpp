@@ -214,4 +214,37 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
     return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
 }
 
+// Workgroup -> (batch b, query head h, query tile qt) of a grid of B * Hkv * G * QT
+// attention workgroups.  Consecutive logical ids on one XCD share a (b, kv head), so the
+// K/V tiles they all stream come from that XCD's L2.  Causal: the query tiles of a group
+// of grp kv heads run together in decreasing order of work (longest first), which
+// shortens each group's tail while its K/V still fit in L2 and MALL; grp = 1 is plain
+// head-by-head order.
+template <bool CAUSAL>
+__device__ __forceinline__ void block_tile(int B, int Hkv, int G, int QT, int grp, int& b, int& h, int& qt) {
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    int bhk, hg;
+    if constexpr (CAUSAL) {
+        const int per = grp * G * QT, nkv = B * Hkv;
+        const int gi = L / per, r = L % per;
+        const int gsz = min(grp, nkv - gi * grp);  // the last group may be smaller
+        hg = r % G;
+        qt = QT - 1 - r / (G * gsz);
+        bhk = gi * grp + (r / G) % gsz;
+    } else {
+        hg = L % G;
+        qt = (L / G) % QT;
+        bhk = L / (G * QT);
+    }
+    b = bhk / Hkv;
+    h = (bhk % Hkv) * G + hg;
+}
+
+// Host: kv heads per causal group -- as many (up to four) as have their K and V operands
+// (head_bytes each) within 8 MiB together: an XCD's 4 MB L2 plus its share of the MALL.
+inline int causal_head_group(int64_t head_bytes) {
+    const int64_t budget = int64_t(8) << 20;
+    return 4 * head_bytes <= budget ? 4 : (2 * head_bytes <= budget ? 2 : 1);
+}
+
 }  // namespace sage

@@ -119,6 +119,32 @@ class Runner:
         quant = [a.elapsed_time(b) for a, b, c in ev]
         return total / steps, sum(attn) / steps, sum(quant) / steps, sorted(attn)[len(attn) // 2]
 
+    def time_graph(self, steps: int, warmup: int) -> float:
+        """ms per step with the step (same kernels, same buffers) captured once into a HIP
+        graph and replayed: the launch rate no longer depends on the Python wrappers."""
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.step()
+        for _ in range(warmup):
+            graph.replay()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(steps):
+            graph.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        del graph
+        return t0.elapsed_time(t1) / steps
+
 
 def main():
     args = parse()
@@ -174,6 +200,7 @@ def main():
     r = Runner(qa, torch, q, k, v, w)
     log(f"[bench] headline {w}")
     ms_step, ms_attn, ms_quant, ms_attn_med = r.time(args.steps, args.warmup)
+    ms_graph = r.time_graph(args.steps, 5)
     ops = w.ops()
     value = ops / (ms_step * 1e-3) / 1e12
     attn_tops = ops / (ms_attn * 1e-3) / 1e12
@@ -216,6 +243,9 @@ def main():
                                f"{'causal' if w.causal else 'non-causal'} INT8-QK FP8-PV fp16+fp32-accum",
                    "B": w.B, "H": w.Hq, "N": w.Nq, "D": w.D, "causal": w.causal, "layout": w.layout,
                    "pv": w.pv, "accum": w.accum},
+        # the same step replayed from a captured HIP graph (no Python between launches)
+        "graph_ms_per_step": round(ms_graph, 4),
+        "graph_step_tops": round(ops / (ms_graph * 1e-3) / 1e12, 2),
         "attn_kernel_tops": round(attn_tops, 2),
         "attn_kernel_ms": round(ms_attn, 4),
         "attn_kernel_ms_median": round(ms_attn_med, 4),
@@ -258,8 +288,10 @@ def main():
                 qs, ks, vs = inputs_for(n)
                 rs = Runner(qa, torch, qs, ks, vs, ws)
                 st, at, qt, _ = rs.time(args.sweep_steps, 3)
+                gt = rs.time_graph(args.sweep_steps, 3)
                 o = ws.ops()
                 sweep.append({"N": n, "causal": causal, "step_tops": round(o / (st * 1e-3) / 1e12, 1),
+                              "graph_step_tops": round(o / (gt * 1e-3) / 1e12, 1),
                               "attn_tops": round(o / (at * 1e-3) / 1e12, 1),
                               "attn_frac_of_peak": round(o / (at * 1e-3) / 1e12 / PEAK_TOPS, 4),
                               "attn_ms": round(at, 4), "quant_ms": round(qt, 4)})

@@ -87,7 +87,9 @@ __global__ __launch_bounds__(64) void k_mean_final_kernel(const double* __restri
 // token: the rows of xq, padding rows 0).  G = 1 and 32 are the finer "per-thread"
 // groups (SageAttention project README, "Project Updates" v2.0.1): a query column
 // of the score MFMA per lane, the 32 keys of a half-wave.
-template <bool BF16, int DP, bool VEC8, bool SMOOTH, int G = 64>
+// ROWMEAN: mean points at the (b, h) row of D means (for example in LDS), not at the
+// [B][H][D] array.
+template <bool BF16, int DP, bool VEC8, bool SMOOTH, int G = 64, bool ROWMEAN = false>
 __device__ __forceinline__ void quant_block_wave(const uint16_t* __restrict__ x, const SeqMap& m, int D,
                                                  const float* __restrict__ mean, int8_t* __restrict__ xq,
                                                  float* __restrict__ scale, int j, int h, int b, int lane) {
@@ -106,7 +108,8 @@ __device__ __forceinline__ void quant_block_wave(const uint16_t* __restrict__ x,
 
     float mu[8];
 #pragma unroll
-    for (int e = 0; e < 8; e++) mu[e] = (SMOOTH && c0 + e < D) ? mean[int64_t(bh) * D + c0 + e] : 0.0f;
+    for (int e = 0; e < 8; e++)
+        mu[e] = (SMOOTH && c0 + e < D) ? mean[(ROWMEAN ? 0 : int64_t(bh) * D) + c0 + e] : 0.0f;
 
     v8u16 raw[PASSES];
 #pragma unroll
@@ -459,10 +462,13 @@ __global__ __launch_bounds__(64) void qkv_pass2_kernel(const double* __restrict_
 //   FP16: v^ = fp16(clamp(v, +-65504)) (round half even).
 //   FP8:  v^ = e4m3(clamp(fp32(v * inv[c]), +-448)), inv = fp32(448 / amax[c]);
 //         the block-0 workgroup also writes v_scale[c] = fp32(amax[c] / 448).
-template <bool BF16, int DP, bool VEC8, bool FP8>
+// FOLD (FP8, short sequences): amax[c] is reduced here from the per-block channel maxima
+// vpart of qkv_pass1_kernel, as qkv_pass2_kernel would (amax_bits is then unused).
+template <bool BF16, int DP, bool VEC8, bool FP8, bool FOLD = false>
 __global__ __launch_bounds__(2 * DP) void quant_v_kernel(const uint16_t* __restrict__ v, SeqMap m, int D,
                                                       const uint32_t* __restrict__ amax_bits,
-                                                      void* __restrict__ vhat, float* __restrict__ vscale) {
+                                                      void* __restrict__ vhat, float* __restrict__ vscale,
+                                                      const float* __restrict__ vpart = nullptr) {
     constexpr int ELT = FP8 ? 1 : 2;
     constexpr int CH = DP / 8;               // 8-channel chunks per token row
     constexpr int THREADS = CH * (kBlk / 4);  // one thread per (token quad, chunk)
@@ -480,15 +486,25 @@ __global__ __launch_bounds__(2 * DP) void quant_v_kernel(const uint16_t* __restr
 
     float inv[8];
     if constexpr (FP8) {
+        __shared__ float samax[FOLD ? DP : 1];
+        if constexpr (FOLD) {
+            if (threadIdx.x < DP) {
+                const int nb = (N + kBlk - 1) / kBlk;
+                const float* pp = vpart + sv.slot0 * DP + threadIdx.x;
+                float a = 0.0f;
+#pragma unroll 16
+                for (int i = 0; i < nb; i++) a = fmaxf(a, pp[int64_t(i) * DP]);  // ascending blocks
+                samax[threadIdx.x] = a;
+            }
+            __syncthreads();
+        }
+        auto amax_of = [&](int c) { return FOLD ? samax[c] : __uint_as_float(amax_bits[bh * DP + c]); };
 #pragma unroll
         for (int e = 0; e < 8; e++) {
-            const float a = __uint_as_float(amax_bits[bh * DP + c0 + e]);
+            const float a = amax_of(c0 + e);
             inv[e] = a > 0.0f ? 448.0f / a : 0.0f;
         }
-        if (j == 0 && threadIdx.x < DP) {
-            const float a = __uint_as_float(amax_bits[bh * DP + threadIdx.x]);
-            vscale[bh * DP + threadIdx.x] = a / 448.0f;
-        }
+        if (j == 0 && threadIdx.x < DP) vscale[bh * DP + threadIdx.x] = amax_of(threadIdx.x) / 448.0f;
     }
     v8u16 r[4];
 #pragma unroll
@@ -531,6 +547,35 @@ __global__ __launch_bounds__(2 * DP) void quant_v_kernel(const uint16_t* __restr
         const int c = pr ^ ((pr >> 3) & RMASK);
         *(uint4*)(dst + c * ROWB + 16 * k) = *(const uint4*)(tile + pr * ROWB + 16 * k);
     }
+}
+
+// K operand of sage_quant_qkv for short sequences (at most kFoldBlocks blocks): each
+// workgroup reduces its (b, kv head)'s K mean from the fp64 block sums of
+// qkv_pass1_kernel itself, in qkv_pass2_kernel's order (ascending blocks), instead of a
+// separate pass-2 launch; the x == 0 workgroup writes k_mean.  Then as
+// quant_blocks_kernel.
+constexpr int kFoldBlocks = 32;
+template <bool BF16, int DP, bool VEC8, int G>
+__global__ __launch_bounds__(256) void quant_k_fold_kernel(const uint16_t* __restrict__ k, SeqMap m, int D,
+                                                           const double* __restrict__ kpart,
+                                                           float* __restrict__ mean, int8_t* __restrict__ xq,
+                                                           float* __restrict__ scale) {
+    __shared__ float smean[DP];
+    const int h = blockIdx.y, b = blockIdx.z, c = threadIdx.x;
+    const SeqView sv = seq_view(m, b, h);
+    if (c < D) {
+        const int nb = (sv.n + kBlk - 1) / kBlk;
+        const double* pp = kpart + sv.slot0 * D + c;
+        double sum = 0.0;
+#pragma unroll 16
+        for (int i = 0; i < nb; i++) sum += pp[int64_t(i) * D];
+        const float mu = sv.n > 0 ? float(sum / double(sv.n)) : 0.0f;
+        smean[c] = mu;
+        if (blockIdx.x == 0) mean[(int64_t(b) * m.H + h) * D + c] = mu;
+    }
+    __syncthreads();
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    quant_block_wave<BF16, DP, VEC8, true, G, true>(k, m, D, smean, xq, scale, blockIdx.x * 4 + wave, h, b, lane);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -582,6 +627,26 @@ hipError_t launch_qkv_t(const QuantQKArgs& a, const QuantVArgs& va, hipStream_t 
     uint32_t* amax = (uint32_t*)(ws + w.amax);
     const int nq = ((mq.NB + 3) / 4) * a.Hq * a.B;
     const int nkv = mk.NB * a.Hkv * a.B;
+    if (mk.NB <= kFoldBlocks) {
+        // short sequences: pass 2 folded into the K and V launches (three launches)
+        if (va.fp8)
+            qkv_pass1_kernel<BF16, DP, VEC8, true, QG><<<nq + nkv, 256, 0, s>>>(
+                (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)va.v, mq, mk, a.D, nq, nkv, a.q_i8,
+                a.q_scale, kpart, vpart);
+        else
+            qkv_pass1_kernel<BF16, DP, VEC8, false, QG><<<nq + nkv, 256, 0, s>>>(
+                (const uint16_t*)a.q, (const uint16_t*)a.k, nullptr, mq, mk, a.D, nq, nkv, a.q_i8, a.q_scale, kpart,
+                nullptr);
+        quant_k_fold_kernel<BF16, DP, VEC8, KG><<<dim3((mk.NB + 3) / 4, a.Hkv, a.B), 256, 0, s>>>(
+            (const uint16_t*)a.k, mk, a.D, kpart, a.k_mean, a.k_i8, a.k_scale);
+        if (va.fp8)
+            quant_v_kernel<BF16, DP, VEC8, true, true><<<dim3(mk.NB, a.Hkv, a.B), DP * 2, 0, s>>>(
+                (const uint16_t*)va.v, mk, a.D, nullptr, va.v_hat, va.v_scale, vpart);
+        else
+            quant_v_kernel<BF16, DP, VEC8, false><<<dim3(mk.NB, a.Hkv, a.B), DP * 2, 0, s>>>(
+                (const uint16_t*)va.v, mk, a.D, nullptr, va.v_hat, nullptr);
+        return hipGetLastError();
+    }
     if (va.fp8) {
         qkv_pass1_kernel<BF16, DP, VEC8, true, QG><<<nq + nkv, 256, 0, s>>>(
             (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)va.v, mq, mk, a.D, nq, nkv, a.q_i8,

@@ -51,7 +51,7 @@ def test_quantization_bit_exact(cid, w):
 
 @pytest.mark.parametrize("cid,w", QUANT_CASES, ids=[c[0] for c in QUANT_CASES])
 def test_fused_quantization_bit_exact(cid, w):
-    """sage_quant_qkv (one call, four launches) against the oracle, in both P.V modes."""
+    """sage_quant_qkv (one call, three or four launches) against the oracle, in both P.V modes."""
     case = Case(w)
     qk, vq = case.gpu_quant(fused=True)
     check_quant_bit_exact(case, qk, vq)

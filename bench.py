@@ -94,9 +94,18 @@ class Runner:
         self.quant()
         self.attn()
 
-    def time(self, steps: int, warmup: int):
-        """(ms per step, ms per attention launch, ms per quant pair), HIP events on the launch stream."""
+    def time(self, steps: int, warmup: int, ramp_s: float = 0.0):
+        """(ms per step, ms per attention launch, ms per quant pair), HIP events on the launch stream.
+        ramp_s: before the warmup steps, untimed steps for at least this long (at most 500 steps),
+        so that the shader clock has left its idle level whatever the warmup count."""
         torch = self.torch
+        if ramp_s > 0:
+            t_end = time.perf_counter() + ramp_s
+            for _ in range(500):
+                self.step()
+                torch.cuda.synchronize()
+                if time.perf_counter() >= t_end:
+                    break
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
@@ -199,7 +208,8 @@ def main():
     q, k, v = inputs_for(args.n)
     r = Runner(qa, torch, q, k, v, w)
     log(f"[bench] headline {w}")
-    ms_step, ms_attn, ms_quant, ms_attn_med = r.time(args.steps, args.warmup)
+    # the shader clock ramps up over the first ~100 ms of load: 0.3 s of untimed steps first
+    ms_step, ms_attn, ms_quant, ms_attn_med = r.time(args.steps, args.warmup, ramp_s=0.3)
     ms_graph = r.time_graph(args.steps, 5)
     ops = w.ops()
     value = ops / (ms_step * 1e-3) / 1e12

@@ -34,6 +34,8 @@ CASES = [
     ("one_query", W("llm_prefill", Nq=1, Nkv=500, seed=17), "all"),
     ("offset_keys_d64", W("video_dit", B=1, Hq=2, Hkv=2, Nq=333, Nkv=333, seed=42), 64),
     ("d256_causal", W("seq_sweep", B=1, Hq=4, Hkv=2, Nq=300, Nkv=300, D=256, causal=True, seed=47), "all"),
+    # six kv heads in causal groups of four: a full group, then a partial one
+    ("causal_head_groups_4_2", W("seq_sweep", B=3, Hq=4, Hkv=2, Nq=260, Nkv=260, causal=True, seed=55), "all"),
     ("d200_gqa_nhd", W("gqa", B=1, Hq=4, Hkv=2, Nq=200, Nkv=250, D=200, causal=False, seed=48), "all"),
     ("d256_2k", W("seq_sweep", B=1, Hq=4, Hkv=4, Nq=2048, Nkv=2048, D=256, seed=49), 16),
 ]

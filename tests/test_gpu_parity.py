@@ -105,6 +105,8 @@ OUT_CASES = [
     ("causal_nq_gt_nkv_fp16", W("llm_prefill", Hq=4, Hkv=2, Nq=300, Nkv=100, causal=True, seed=19), "all"),
     ("causal_decode_d64_fp8", W("video_dit", Hq=2, Hkv=2, Nq=1, Nkv=1000, causal=True, seed=20), "all"),
     ("causal_chunk_d96", W("gqa", B=1, Nq=200, Nkv=1500, D=96, causal=True, seed=21), "all"),
+    # six kv heads in causal groups of four: a full group, then a partial one
+    ("causal_head_groups_4_2", W("seq_sweep", B=3, Hq=4, Hkv=2, Nq=260, Nkv=260, causal=True, seed=27), "all"),
     # head dims above 128: Dp = 256
     ("d256_fp8", W("seq_sweep", B=1, Hq=4, Hkv=2, Nq=300, Nkv=300, D=256, seed=22), "all"),
     ("d256_causal_fp16", W("llm_prefill", Hq=2, Hkv=2, Nq=300, Nkv=300, D=256, causal=True, seed=24), "all"),

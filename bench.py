@@ -126,6 +126,7 @@ class Runner:
         total = t0.elapsed_time(t1)
         attn = [b.elapsed_time(c) for a, b, c in ev]
         quant = [a.elapsed_time(b) for a, b, c in ev]
+        self.attn_min = min(attn)
         return total / steps, sum(attn) / steps, sum(quant) / steps, sorted(attn)[len(attn) // 2]
 
     def time_graph(self, steps: int, warmup: int) -> float:
@@ -259,6 +260,7 @@ def main():
         "attn_kernel_tops": round(attn_tops, 2),
         "attn_kernel_ms": round(ms_attn, 4),
         "attn_kernel_ms_median": round(ms_attn_med, 4),
+        "attn_kernel_ms_min": round(r.attn_min, 4),
         "quant_ms": round(ms_quant, 4),
         "quant_GBps": round(quant_bytes / (ms_quant * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TOPS, "unit": "TFLOP/s",
@@ -451,7 +453,19 @@ def cpu_baseline(w, full, np, torch):
             "sample": f"emulation-mode oracle: full quantisation ({t_quant:.2f}s) + {len(rows)} of {total_rows} "
                       f"query rows ({t_rows:.2f}s), extrapolated linearly in rows to one whole step "
                       f"({t_full:.1f}s)",
-            "seconds_measured": round(t_quant + t_rows, 2)}
+            "seconds_measured": round(t_quant + t_rows, 2), "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), for the oracle baseline."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 if __name__ == "__main__":

@@ -136,6 +136,16 @@ def test_sweep_32k_sampled_rows():
     check_output(case, out, rows, exact=True)
 
 
+def test_sweep_16k_causal_sampled_rows():
+    """Causal at 16K, where the launch interleaves the query tiles of kv-head pairs."""
+    w = W("seq_sweep", Nq=16384, Nkv=16384, causal=True)
+    case = Case(w)
+    qk, vq = case.gpu_quant()
+    out = case.gpu_attn(qk, vq)
+    rows = oracle.sample_rows(w.B, w.Hq, w.Nq, per_head=4, seed=6)
+    check_output(case, out, rows, exact=True)
+
+
 def test_layouts_give_identical_outputs():
     w = W("gqa", B=1, Nq=500, Nkv=500, D=96)
     a = Case(w.with_(layout="HND"))

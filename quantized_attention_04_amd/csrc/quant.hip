@@ -333,7 +333,9 @@ __global__ __launch_bounds__(256) void v_amax_kernel(const uint16_t* __restrict_
 // mode, V (block channel maxima) side by side in one grid; pass 2 forms the K means
 // and V maxima; pass 3 quantises K and V with the kernels above.  The per-block V
 // maxima replace the integer atomics of v_amax_kernel (same maximum: max is exact in
-// any order).
+// any order).  Sequences of at most kFoldBlocks blocks skip pass 2: the K and V
+// launches reduce the partials of their own (b, kv head) in the same order (three
+// launches in all).
 
 // One 64-token K/V block of one (b, kv head): K channel sums as k_partial_block (fp64,
 // ascending tokens) and, with VMAX, the per-channel maximum of |v| -> vpart[slot][c],

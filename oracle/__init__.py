@@ -61,10 +61,15 @@ def lib() -> ctypes.CDLL:
     L.orc_quant_groups.argtypes = [_f32p, ctypes.c_void_p, _L, _L, _L, _L, _L, _i8p, _f32p]
     L.orc_quant_v.argtypes = [_f32p, _L, _L, _L, _L, ctypes.c_int, _f32p, _f32p]
     L.orc_scores_i32.argtypes = [_i8p, _i8p, _L, _L, _L, _L, _L, _L, _i64p, _L, _i32p]
+    L.orc_attn_emulate.restype = _L
     L.orc_attn_emulate.argtypes = [_i8p, _f32p, _i8p, _f32p, _f32p, _f32p, ctypes.c_int, _L, _L, _L, _L, _L,
                                    _L, ctypes.c_int, ctypes.c_double, _i64p, _L, _f64p, ctypes.c_void_p]
+    L.orc_attn_emulate_g.restype = _L
     L.orc_attn_emulate_g.argtypes = [_i8p, _f32p, _i8p, _f32p, _f32p, _f32p, ctypes.c_int, _L, _L, _L, _L, _L,
                                      _L, _L, _L, ctypes.c_int, ctypes.c_double, _i64p, _L, _f64p, ctypes.c_void_p]
+    L.orc_tie_flip.restype = ctypes.c_double
+    L.orc_tie_flip.argtypes = [ctypes.c_double, ctypes.c_int]
+    L.orc_mx_p_block.argtypes = [_f64p, _f32p, _i32p, _L, _f64p, _f64p]
     L.orc_attn_exact.argtypes = [_f32p, _f32p, _f32p, _L, _L, _L, _L, _L, _L, ctypes.c_int, ctypes.c_double,
                                  _i64p, _L, _f64p]
     L.orc_mx_exp.restype = ctypes.c_int
@@ -75,6 +80,7 @@ def lib() -> ctypes.CDLL:
     L.orc_e2m1_code.argtypes = [ctypes.c_double]
     L.orc_quant_mxfp4_rows.argtypes = [_f32p, ctypes.c_void_p, _L, _L, _L, _L, _u8p, _i32p]
     L.orc_quant_mxfp4_tokens.argtypes = [_f32p, _L, _L, _L, _L, _u8p, _i32p]
+    L.orc_attn_emulate_mxfp4.restype = _L
     L.orc_attn_emulate_mxfp4.argtypes = [_u8p, _i32p, _u8p, _i32p, _u8p, _i32p, _L, _L, _L, _L, _L, _L,
                                          ctypes.c_int, ctypes.c_double, _i64p, _L, _f64p, ctypes.c_void_p]
     _lib = L
@@ -231,18 +237,42 @@ def scores_i32(Q: Quantized, tiles: Sequence[Sequence[int]]) -> np.ndarray:
     return out
 
 
+AMB_REL = 2.0 ** -14    # relative distance from a rounding tie within which either code is correct
+SCORE_RANGE = 1024.0    # |S2| below which that margin covers every fp32 evaluation of p
+
+
+class ScoreRangeError(ValueError):
+    """The tie margin was asked for on rows whose scores leave the range in which it holds."""
+
+
+def _range_check(bad: int, with_ambiguity: bool) -> None:
+    if with_ambiguity and bad:
+        raise ScoreRangeError(f"{bad} row(s) have a score or running max with |S2| >= {SCORE_RANGE:g} (log2 "
+                              f"units) where p can still round to a nonzero code: the 2^-14 tie margin is not "
+                              f"defined there")
+
+
+def tie_flip(x: float, fmt: int) -> float:
+    """|code_hi - code_lo| when x (> 0) lies within a relative 2^-14 of a rounding tie of
+    format fmt, else 0 (the per-P term of the ambiguity allowance)."""
+    return float(lib().orc_tie_flip(float(x), int(fmt)))
+
+
 def attn_emulate(Q: Quantized, causal: bool, sm_scale: float, rows: np.ndarray, with_ambiguity: bool = False):
     """Emulation-mode rows [R, D] (fp64).  With with_ambiguity, also the per-element
-    effect of flipping the P roundings that lie within 2^-14 (relative) of a tie."""
+    effect of flipping the P roundings that lie within 2^-14 (relative) of a tie; that
+    margin holds while the scores that matter stay below 2^10 in magnitude, and
+    ScoreRangeError is raised for rows beyond it."""
     B, Hq, Nq, D = Q.q_i8.shape
     Nkv = Q.k_i8.shape[2]
     rows = np.ascontiguousarray(rows, np.int64).reshape(-1, 3)
     out = np.empty((rows.shape[0], D), np.float64)
     amb = np.empty((rows.shape[0], D), np.float64) if with_ambiguity else None
     vs = Q.v_scale if Q.v_scale is not None else np.zeros((B, Q.Hkv, D), np.float32)
-    lib().orc_attn_emulate_g(Q.q_i8, Q.q_scale, Q.k_i8, Q.k_scale, Q.v_hat, vs, int(Q.pv_fp8), B, Hq, Q.Hkv, Nq,
-                             Nkv, D, int(Q.qg), int(Q.kg), int(bool(causal)), float(sm_scale), rows, rows.shape[0],
-                             out, None if amb is None else amb.ctypes.data_as(ctypes.c_void_p))
+    bad = lib().orc_attn_emulate_g(Q.q_i8, Q.q_scale, Q.k_i8, Q.k_scale, Q.v_hat, vs, int(Q.pv_fp8), B, Hq, Q.Hkv,
+                                   Nq, Nkv, D, int(Q.qg), int(Q.kg), int(bool(causal)), float(sm_scale), rows,
+                                   rows.shape[0], out, None if amb is None else amb.ctypes.data_as(ctypes.c_void_p))
+    _range_check(bad, with_ambiguity)
     return (out, amb) if with_ambiguity else out
 
 
@@ -404,10 +434,23 @@ def attn_emulate_mxfp4(Q: MXQuantized, causal: bool, sm_scale: float, rows: np.n
     rows = np.ascontiguousarray(rows, np.int64)
     out = np.empty((len(rows), D), np.float64)
     amb = np.empty((len(rows), D), np.float64) if with_ambiguity else None
-    lib().orc_attn_emulate_mxfp4(Q.q_code, Q.q_exp, Q.k_code, Q.k_exp, Q.v_code, Q.v_exp, B, Hq, Q.Hkv, Nq, Nkv, D,
-                                 int(bool(causal)), float(sm_scale), rows, len(rows), out,
-                                 amb.ctypes.data_as(ctypes.c_void_p) if amb is not None else None)
+    bad = lib().orc_attn_emulate_mxfp4(Q.q_code, Q.q_exp, Q.k_code, Q.k_exp, Q.v_code, Q.v_exp, B, Hq, Q.Hkv, Nq,
+                                       Nkv, D, int(bool(causal)), float(sm_scale), rows, len(rows), out,
+                                       amb.ctypes.data_as(ctypes.c_void_p) if amb is not None else None)
+    _range_check(bad, with_ambiguity)
     return (out, amb) if with_ambiguity else out
+
+
+def mx_p_block(p: np.ndarray, t: np.ndarray, vis: Optional[np.ndarray] = None):
+    """One 32-key block of P in the microscaling scheme: (dequantised values, ambiguity
+    per element) for p = 2^t (float64 p, float32 t)."""
+    p = np.ascontiguousarray(p, np.float64)
+    t = np.ascontiguousarray(t, np.float32)
+    vis = np.ones(p.shape, np.int32) if vis is None else np.ascontiguousarray(vis, np.int32)
+    ph = np.empty_like(p)
+    flip = np.empty_like(p)
+    lib().orc_mx_p_block(p, t, vis, p.size, ph, flip)
+    return ph, flip
 
 
 def quantize_mxfp4_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q, cu_k):

@@ -42,7 +42,7 @@
 
 #define BLK 64 /* token block: one quantisation scale per 64 consecutive tokens */
 
-int orc_version(void) { return 3; }
+int orc_version(void) { return 4; }
 
 int orc_threads(void) {
 #ifdef _OPENMP
@@ -263,8 +263,12 @@ void orc_scores_i32(const int8_t* q8, const int8_t* k8, long B, long Hq, long Hk
  * Emulation-mode attention for selected query rows.  rows holds R triples
  * (b, h, i); out is [R, D] in fp64 (before the cast to the output dtype).
  *
- * The rounding of P to FP16 / e4m3 is a decision taken in floating point, and the
- * pages fix no precision for it, so P is formed in fp32 (the kernel's precision):
+ * Precision of the softmax.  The pages name fp32 as the precision of the scheme's
+ * floating-point side (SageAttention README, "Available APIs": pv_accum_dtype
+ * "fp32"; the qwbw.cn integration article calls the fp32 accumulation the most
+ * stable setting) and fix no other; the block scales the quantiser produces are
+ * fp32 numbers.  The dequantised scores and the online softmax are therefore
+ * evaluated in fp32, each operation rounded once (round to nearest even):
  *   c    = fp32( fp32(sq * sk) * fp32(sm_scale * log2(e)) )     dequant factor
  *   S2   = fp32( S32 * c )                                       (S32 exact in fp32)
  *   m    = running max of S2 over the row (fp32), -inf while empty
@@ -281,28 +285,23 @@ void orc_scores_i32(const int8_t* q8, const int8_t* k8, long B, long Hq, long Hk
  * Both PV accumulation modes (single-level fp32 and two-level) are modelled by the
  * same fp64 accumulation: they differ only in how the hardware rounds.
  *
- * amb (optional, [R, D]): for every P whose pre-rounding value x lies within a
- * relative 2^-14 of a rounding tie (where a kernel computing p with a few ulps of
- * difference may round the other way), the output change that flipping that single
- * decision would cause, |code_hi - code_lo| * |vhat| / l (rescaled like acc), summed.
- * A kernel may also form t from the score read as the fp32 value K0 + S32 * 2^-26,
- * K0 = fp32(1/(2 pi)) (an integer accumulator started at K0's bits, so no int-to-float
- * conversion is needed), as fma(value, c 2^26, fp32(nm - K0 c 2^26)) with nm = -m (or
- * log2 448 - m for FP8): the bias's one rounding moves t by up to half an ulp of
- * |nm - K0 c 2^26|, which moves p by ln 2 times that, relatively; the margin of the
- * INT8 scheme adds that amount to 2^-14.
+ * amb (optional, [R, D]): a rounding of p to FP16 / e4m3 is an integer-like decision
+ * taken on an fp32 value.  Another fp32 evaluation of the same formula (t formed with
+ * one rounding instead of two, a faithfully rounded exp2, 448 folded into the
+ * exponent) lands within a relative 2^-14 of this p whenever every score that can
+ * still produce a nonzero code has |S2| < 2^10: the difference is then at most one
+ * half ulp of 2^10 (2^-15) in t plus a few fp32 ulps, i.e. below 0.4 * 2^-14 in p.
+ * So a p within a relative 2^-14 of a rounding tie may legitimately round either way;
+ * for each such p, amb adds the output change that flipping that single decision
+ * causes, |code_hi - code_lo| * |vhat| / l (rescaled like acc).  The margin is a fixed
+ * constant and depends on nothing but the formula above.  A row in which a score with
+ * t > -32 (p > 2^-32, the only ones that can round to a nonzero code) or the running
+ * max reaches |S2| >= 2^10 lies outside the range where the margin holds: the return
+ * value counts such rows, and the caller treats a nonzero count as an error when it
+ * asked for amb.
  * ------------------------------------------------------------------------- */
 static const double AMB_REL = 1.0 / 16384.0;
-static const double K0_INV2PI_F32 = 0x1.45f306p-3; /* fp32(1/(2 pi)) */
-
-/* relative margin for a P of the INT8 scheme with dequantisation factor c and running max m */
-static double int8_margin(float c, float m, int pv_fp8) {
-    double nm = (pv_fp8 ? 8.807354922057604 : 0.0) - (double)m;
-    double mag = fabs(nm - K0_INV2PI_F32 * (double)c * 67108864.0);
-    int e2;
-    frexp(mag, &e2); /* mag in [2^(e2-1), 2^e2): fp32 ulp there is 2^(e2-24) */
-    return AMB_REL + 0.6931471805599453 * ldexp(1.0, e2 - 25) * 1.001;
-}
+static const float SCORE_RANGE = 1024.0f; /* |S2| below which AMB_REL covers every fp32 evaluation */
 
 /* quantum of the format at x (> 0): spacing of representable values around x */
 static double fmt_quantum(double x, int fmt) {
@@ -316,33 +315,40 @@ static double fmt_quantum(double x, int fmt) {
     return ldexp(1.0, ex - (p - 1));
 }
 
-/* |code_hi - code_lo| when x (> 0) lies within rel * x of the midpoint, else 0 */
-static double tie_flip_rel(double x, int fmt, double rel) {
+/* |code_hi - code_lo| when x (> 0) lies within AMB_REL * x of a rounding tie
+ * (the midpoint of two neighbouring codes), else 0 */
+double orc_tie_flip(double x, int fmt) {
     if (!(x > 0.0)) return 0.0;
     double q = fmt_quantum(x, fmt);
     double lo = floor(x / q) * q;
     double mid = lo + 0.5 * q;
-    return fabs(x - mid) <= rel * x ? q : 0.0;
+    return fabs(x - mid) <= AMB_REL * x ? q : 0.0;
 }
-static double tie_flip(double x, int fmt) { return tie_flip_rel(x, fmt, AMB_REL); }
+static double tie_flip(double x, int fmt) { return orc_tie_flip(x, fmt); }
 
-void orc_attn_emulate_g(const int8_t* q8, const float* sq, const int8_t* k8, const float* sk,
+/* 1 when a score s2 (with running max m, t = s2 - m) can produce a nonzero code and
+ * lies outside the range where AMB_REL covers every fp32 evaluation */
+static int out_of_range(float s2, float m, float t) {
+    return t > -32.0f && (fabsf(s2) >= SCORE_RANGE || fabsf(m) >= SCORE_RANGE);
+}
+
+long orc_attn_emulate_g(const int8_t* q8, const float* sq, const int8_t* k8, const float* sk,
                         const float* vhat, const float* vscale, int pv_fp8, long B, long Hq, long Hkv,
                         long Nq, long Nkv, long D, long qg, long kg, int causal, double sm_scale,
                         const int64_t* rows, long R, double* out, double* amb);
 
-void orc_attn_emulate(const int8_t* q8, const float* sq, const int8_t* k8, const float* sk,
+long orc_attn_emulate(const int8_t* q8, const float* sq, const int8_t* k8, const float* sk,
                       const float* vhat, const float* vscale, int pv_fp8, long B, long Hq, long Hkv,
                       long Nq, long Nkv, long D, int causal, double sm_scale, const int64_t* rows,
                       long R, double* out, double* amb) {
-    orc_attn_emulate_g(q8, sq, k8, sk, vhat, vscale, pv_fp8, B, Hq, Hkv, Nq, Nkv, D, BLK, BLK, causal, sm_scale,
+    return orc_attn_emulate_g(q8, sq, k8, sk, vhat, vscale, pv_fp8, B, Hq, Hkv, Nq, Nkv, D, BLK, BLK, causal, sm_scale,
                        rows, R, out, amb);
 }
 
 /* The same with Q scales per qg tokens and K scales per kg keys (orc_quant_groups):
  * the dequantisation factor c of a score takes the scale of its query's group and
  * of its key's group.  The online softmax still advances in 64-key blocks. */
-void orc_attn_emulate_g(const int8_t* q8, const float* sq, const int8_t* k8, const float* sk,
+long orc_attn_emulate_g(const int8_t* q8, const float* sq, const int8_t* k8, const float* sk,
                         const float* vhat, const float* vscale, int pv_fp8, long B, long Hq, long Hkv,
                         long Nq, long Nkv, long D, long qg, long kg, int causal, double sm_scale,
                         const int64_t* rows, long R, double* out, double* amb) {
@@ -351,8 +357,9 @@ void orc_attn_emulate_g(const int8_t* q8, const float* sq, const int8_t* k8, con
     long group = Hq / Hkv;
     long nqg = (Nq + qg - 1) / qg, nkg = (Nkv + kg - 1) / kg, nkb = (Nkv + BLK - 1) / BLK;
     const long off = Nkv - Nq; /* causal: key j visible to query i iff j <= i + off */
+    long bad_rows = 0;
     (void)B;
-#pragma omp parallel for schedule(dynamic, 4)
+#pragma omp parallel for schedule(dynamic, 4) reduction(+ : bad_rows)
     for (long r = 0; r < R; r++) {
         long b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
         long hk = h / group;
@@ -360,7 +367,8 @@ void orc_attn_emulate_g(const int8_t* q8, const float* sq, const int8_t* k8, con
         float sqi = sq[(b * Hq + h) * nqg + i / qg];
         double* acc = (double*)calloc((size_t)D, sizeof(double));
         double* aacc = (double*)calloc((size_t)D, sizeof(double));
-        float s2[BLK], cj[BLK];
+        int bad = 0;
+        float s2[BLK];
         int vis[BLK];
         double pj[BLK], flip[BLK];
         float m = -INFINITY;
@@ -379,7 +387,6 @@ void orc_attn_emulate_g(const int8_t* q8, const float* sq, const int8_t* k8, con
                 for (long d = 0; d < D; d++) s32 += (int64_t)qrow[d] * (int64_t)krow[d];
                 float v = (float)s32 * c;
                 s2[j - j0] = v;
-                cj[j - j0] = c;
                 if (v > bmax) bmax = v;
             }
             float mnew = m > bmax ? m : bmax;
@@ -394,7 +401,8 @@ void orc_attn_emulate_g(const int8_t* q8, const float* sq, const int8_t* k8, con
                 psum += (double)p;
                 double x = pv_fp8 ? (double)(p * 448.0f) : (double)p;
                 pj[j - j0] = orc_round(x, fmt, 1);
-                flip[j - j0] = tie_flip_rel(x, fmt, int8_margin(cj[j - j0], mnew, pv_fp8));
+                flip[j - j0] = tie_flip(x, fmt);
+                bad |= out_of_range(s2[j - j0], mnew, t);
             }
             l = alpha * l + psum;
             for (long d = 0; d < D; d++) {
@@ -420,7 +428,9 @@ void orc_attn_emulate_g(const int8_t* q8, const float* sq, const int8_t* k8, con
         }
         free(acc);
         free(aacc);
+        bad_rows += bad;
     }
+    return bad_rows;
 }
 
 /* ---------------------------------------------------------------------------
@@ -567,11 +577,11 @@ void orc_quant_mxfp4_tokens(const float* v, long B, long H, long N, long D, uint
 /* P of one half block (n <= 32 values p = 2^t >= 0): the dequantised values ph, and
  * for the ambiguity: per element the change that a different rounding decision would
  * make when p / X sits within 2^-14 of a tie, or when the block maximum sits within
- * 2^-14 of a power of two without being one exactly (a kernel computing p with a few
- * ulps of error may then pick the neighbouring exponent), the change the other
- * exponent makes.  A maximum from an integer t (the row maximum itself, t = 0) is
- * exact on both sides. */
-static void mx_p_block(const double* p, const float* t, const int* vis, long n, double* ph, double* flip) {
+ * 2^-14 of a power of two without being one exactly (another fp32 evaluation of p,
+ * within 2^-14 of this one, may then pick the neighbouring exponent), the change the
+ * other exponent makes.  A maximum from an integer t (the row maximum itself, t = 0)
+ * is an exact power of two in any faithful evaluation of 2^t. */
+void orc_mx_p_block(const double* p, const float* t, const int* vis, long n, double* ph, double* flip) {
     double pmax = 0.0;
     float tmax = -INFINITY;
     for (long i = 0; i < n; i++) {
@@ -608,16 +618,18 @@ static void mx_p_block(const double* p, const float* t, const int* vis, long n, 
  * operands), then, as for INT8, s2 = fp32(S) * fp32(sm_scale * log2 e) in fp32, the
  * running max over 64-key blocks, p = fp32(2^(s2 - m)), l += p (unquantised),
  * p quantised per 32-key half block, acc = alpha * acc + sum ph * v (fp64). */
-void orc_attn_emulate_mxfp4(const uint8_t* qc, const int32_t* qE, const uint8_t* kc, const int32_t* kE,
+long orc_attn_emulate_mxfp4(const uint8_t* qc, const int32_t* qE, const uint8_t* kc, const int32_t* kE,
                             const uint8_t* vc, const int32_t* vE, long B, long Hq, long Hkv, long Nq, long Nkv,
                             long D, int causal, double sm_scale, const int64_t* rows, long R, double* out,
                             double* amb) {
     const float scale2 = (float)sm_scale * 1.44269504088896341f;
     long group = Hq / Hkv, nbd = (D + 31) / 32, nbt = (Nkv + 31) / 32, nkb = (Nkv + BLK - 1) / BLK;
     const long off = Nkv - Nq;
+    long bad_rows = 0;
     (void)B;
-#pragma omp parallel for schedule(dynamic, 4)
+#pragma omp parallel for schedule(dynamic, 4) reduction(+ : bad_rows)
     for (long r = 0; r < R; r++) {
+        int bad = 0;
         long b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
         long hk = h / group;
         double* qd = (double*)malloc((size_t)D * sizeof(double));
@@ -659,10 +671,11 @@ void orc_attn_emulate_mxfp4(const uint8_t* qc, const int32_t* qE, const uint8_t*
                 psum += (double)p;
                 pj[j - j0] = (double)p;
                 tj[j - j0] = t;
+                bad |= out_of_range(s2[j - j0], mnew, t);
             }
             for (long h0 = j0; h0 < j1; h0 += 32) {
                 long n = j1 - h0 < 32 ? j1 - h0 : 32;
-                mx_p_block(pj + (h0 - j0), tj + (h0 - j0), vis + (h0 - j0), n, ph + (h0 - j0), flip + (h0 - j0));
+                orc_mx_p_block(pj + (h0 - j0), tj + (h0 - j0), vis + (h0 - j0), n, ph + (h0 - j0), flip + (h0 - j0));
             }
             l = alpha * l + psum;
             for (long d = 0; d < D; d++) {
@@ -686,5 +699,7 @@ void orc_attn_emulate_mxfp4(const uint8_t* qc, const int32_t* qE, const uint8_t*
         free(qd);
         free(acc);
         free(aacc);
+        bad_rows += bad;
     }
+    return bad_rows;
 }

@@ -13,8 +13,9 @@ import oracle
 import quantized_attention_04_amd as qa
 import synth_inputs as si
 
-FP8_REL_L1 = 5e-2   # exact-mode bound with FP8 P.V (the scheme itself sits near 4e-2)
+FP8_REL_L1 = 5e-2   # exact-mode bound with FP8 P.V (the scheme itself sits near 4e-2, above the 3e-2 target)
 FP16_REL_L1 = 3e-2
+AMB_CAP = 1e-2      # per-element cap on the tie allowance added to the emulation tolerance
 
 
 def note(msg: str) -> None:
@@ -139,9 +140,14 @@ def compare_rows(got: np.ndarray, em_raw: np.ndarray, amb: np.ndarray, ex: Optio
     res["emulate"]["ambiguity_max"] = float(amb.max())
     # max-abs <= 1e-2, except where one output ulp is wider than that (bf16 |o| >= 2):
     # both sides round independently computed values, so one ulp apart is allowed there;
-    # plus the effect of P roundings that sit within 2^-14 of a tie (either side is right)
+    # plus the effect of P roundings that sit within 2^-14 of a tie (either side is right),
+    # capped per element so that the allowance can never carry a large error
     ulp = np.ldexp(1.0, np.floor(np.log2(np.maximum(np.abs(em), 1e-30))).astype(int) - (7 if fmt == oracle.BF16 else 10))
-    res["emulate"]["worst_excess"] = float((np.abs(got - em) - np.maximum(1e-2, ulp) - amb).max())
+    base = np.maximum(1e-2, ulp)
+    err = np.abs(got - em)
+    res["emulate"]["worst_excess"] = float((err - base - np.minimum(amb, AMB_CAP)).max())
+    res["emulate"]["needed_allowance"] = int((err > base).sum())   # elements inside only because of it
+    res["emulate"]["elements"] = int(err.size)
     assert res["emulate"]["worst_excess"] <= 0 and res["emulate"]["cos"] >= 0.9999, res
     if ex is not None:
         res["exact"] = metrics(got, ex)

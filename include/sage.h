@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SAGE_ABI_VERSION 4
+#define SAGE_ABI_VERSION 5
 
 typedef enum sage_status {
     SAGE_OK = 0,
@@ -69,11 +69,30 @@ typedef enum sage_status {
 typedef enum sage_dtype { SAGE_FP16 = 0, SAGE_BF16 = 1 } sage_dtype;
 typedef enum sage_layout { SAGE_HND = 0, SAGE_NHD = 1 } sage_layout;
 typedef enum sage_pv { SAGE_PV_FP16 = 0, SAGE_PV_FP8 = 1 } sage_pv;
-/* PV accumulation: fp32 single level; two-level (per-64-key-block fp32 partial sums
- * added into the fp32 output accumulator -- the pages' "fp32+fp16" mode, whose
- * fp16 inner accumulator is an fp32 one on gfx950 matrix cores); fp16 single level
- * is not offered (the gfx950 FP16/FP8 matrix instructions accumulate in fp32). */
-typedef enum sage_accum { SAGE_ACC_FP32 = 0, SAGE_ACC_FP16_FP32 = 1, SAGE_ACC_FP16 = 2 } sage_accum;
+/* PV accumulation (README "Available APIs", pv_accum_dtype; "Current Features":
+ * two-level accumulation for FP8 P.V):
+ *   SAGE_ACC_FP32        fp32 single level: the matrix instruction adds each tile's
+ *                        products to the fp32 output accumulator;
+ *   SAGE_ACC_FP16_FP32   the pages' "fp32+fp16" two-level mode, an ALIAS of SAGE_ACC_FP32
+ *                        on gfx950: the two-level strategy keeps a reduced-precision inner
+ *                        accumulator of the tensor cores from losing bits by adding short
+ *                        runs into fp32; the gfx950 FP8/FP16 matrix instructions accumulate
+ *                        straight into an fp32 operand, so single-level fp32 already gives
+ *                        every level fp32 precision;
+ *   SAGE_ACC_FP16        fp16 single level: not offered (SAGE_ERR_UNSUPPORTED; the gfx950
+ *                        FP16/FP8 matrix instructions accumulate in fp32);
+ *   SAGE_ACC_FP16_FP32_SPLIT  the literal two-level form: each 64-key tile's products in fresh
+ *                        fp32 accumulators, folded into the output accumulator with vector
+ *                        adds (64 more vector instructions per tile; block granularity only).
+ *                        Its fp32 accumulator rounds differently from SAGE_ACC_FP32's, so
+ *                        outputs may differ from it by one output ulp.
+ */
+typedef enum sage_accum {
+    SAGE_ACC_FP32 = 0,
+    SAGE_ACC_FP16_FP32 = 1,
+    SAGE_ACC_FP16 = 2,
+    SAGE_ACC_FP16_FP32_SPLIT = 3
+} sage_accum;
 /* Q/K quantisation granularity (README "Current Features": varying granularities).
  * SAGE_GRAN_BLOCK: one scale per 64 tokens for Q and for K (the layouts above).
  * SAGE_GRAN_THREAD: the finer "per-thread" quantisation of README "Project Updates"
@@ -172,7 +191,7 @@ sage_status sage_quant_qkv(const void* q, const void* k, const void* v, sage_dty
  *   different lengths).  A query that sees no key (Nq > Nkv, i < Nq - Nkv) gets an
  *   output row of zeros.
  *   sm_scale: finite and > 0 (callers pass 1/sqrt(D) for SDPA semantics).
- *   accum: SAGE_ACC_FP32 or SAGE_ACC_FP16_FP32.
+ *   accum: SAGE_ACC_FP32, SAGE_ACC_FP16_FP32 or SAGE_ACC_FP16_FP32_SPLIT.
  */
 sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
                           const void* v_hat, const float* v_scale, void* out, sage_dtype out_dtype,
@@ -189,7 +208,10 @@ sage_status sage_attn_fwd_g(const int8_t* q_i8, const float* q_scale, const int8
 
 /*
  * Debug dump of INT32 score tiles through the attention kernel's own operand
- * path (LDS staging, MFMA operand order of the given PV mode).
+ * path: the K^ tile arrives by the same direct-to-LDS loads and swizzle, and the
+ * scores come from the same matrix-instruction sequence and accumulator form (at
+ * head dims up to 128 the accumulators start at a fixed bias, taken off again as an
+ * integer before the write), in the MFMA operand order of the given PV mode.
  *   tiles: device int32 [T][4] = (b, h_qo, q_block, k_block), each in range.
  *   out:   device int32 [T][64][64]; out[t][i][j] = sum_c q_i8[b,h,64*qb+i,c] *
  *          k_i8[b,h_kv,64*kb+j,c] (padding rows/columns give 0).

@@ -49,7 +49,7 @@ SAGE_OK, SAGE_ERR_INVALID_ARG, SAGE_ERR_UNSUPPORTED, SAGE_ERR_WORKSPACE, SAGE_ER
 SAGE_FP16, SAGE_BF16 = 0, 1
 SAGE_HND, SAGE_NHD = 0, 1
 SAGE_PV_FP16, SAGE_PV_FP8 = 0, 1
-SAGE_ACC_FP32, SAGE_ACC_FP16_FP32, SAGE_ACC_FP16 = 0, 1, 2
+SAGE_ACC_FP32, SAGE_ACC_FP16_FP32, SAGE_ACC_FP16, SAGE_ACC_FP16_FP32_SPLIT = 0, 1, 2, 3
 SAGE_GRAN_BLOCK, SAGE_GRAN_THREAD = 0, 1
 
 _EXPORTS = {
@@ -128,7 +128,7 @@ def lib() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.restype = res
         fn.argtypes = args
-    if L.sage_abi_version() != 4:
+    if L.sage_abi_version() != 5:
         raise ImportError("libsage ABI version mismatch")
     _lib = L
     return L
@@ -160,8 +160,11 @@ _DT = {torch.float16: SAGE_FP16, torch.bfloat16: SAGE_BF16}
 _GRAN = {"block": SAGE_GRAN_BLOCK, "thread": SAGE_GRAN_THREAD}
 _LAYOUT = {"HND": SAGE_HND, "NHD": SAGE_NHD}
 _PV = {"fp16": SAGE_PV_FP16, "fp8": SAGE_PV_FP8}
+# "fp16+fp32" runs the fp32 single-level accumulation (gfx950 matrix cores accumulate in fp32);
+# "fp16+fp32-split": the literal two-level form (a fresh fp32 partial per 64-key tile plus a
+# vector add), within one output ulp of it
 _ACC = {"fp32": SAGE_ACC_FP32, "fp16+fp32": SAGE_ACC_FP16_FP32, "fp32+fp16": SAGE_ACC_FP16_FP32,
-        "fp16": SAGE_ACC_FP16}
+        "fp16": SAGE_ACC_FP16, "fp16+fp32-split": SAGE_ACC_FP16_FP32_SPLIT}
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:

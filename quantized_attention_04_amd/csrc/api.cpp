@@ -110,7 +110,8 @@ sage_status check_attn_args(const int8_t* q_i8, const float* q_scale, const int8
     if (out_dtype != SAGE_FP16 && out_dtype != SAGE_BF16)
         return fail(SAGE_ERR_INVALID_ARG, "bad out dtype %d", int(out_dtype));
     if (pv != SAGE_PV_FP16 && pv != SAGE_PV_FP8) return fail(SAGE_ERR_INVALID_ARG, "bad pv mode %d", int(pv));
-    if (accum != SAGE_ACC_FP32 && accum != SAGE_ACC_FP16_FP32 && accum != SAGE_ACC_FP16)
+    if (accum != SAGE_ACC_FP32 && accum != SAGE_ACC_FP16_FP32 && accum != SAGE_ACC_FP16 &&
+        accum != SAGE_ACC_FP16_FP32_SPLIT)
         return fail(SAGE_ERR_INVALID_ARG, "bad accum mode %d", int(accum));
     if (is_causal != 0 && is_causal != 1) return fail(SAGE_ERR_INVALID_ARG, "is_causal must be 0 or 1");
     if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
@@ -287,6 +288,8 @@ sage_status sage_attn_fwd_g(const int8_t* q_i8, const float* q_scale, const int8
                             float sm_scale, sage_pv pv, sage_accum accum, sage_qk_gran gran, void* stream) {
     if (gran != SAGE_GRAN_BLOCK && gran != SAGE_GRAN_THREAD)
         return fail(SAGE_ERR_INVALID_ARG, "bad quantisation granularity %d", int(gran));
+    if (gran == SAGE_GRAN_THREAD && accum == SAGE_ACC_FP16_FP32_SPLIT)
+        return fail(SAGE_ERR_UNSUPPORTED, "SAGE_ACC_FP16_FP32_SPLIT is offered with SAGE_GRAN_BLOCK only");
     sage_status s = check_attn_args(q_i8, q_scale, k_i8, k_scale, v_hat, v_scale, out, out_dtype, is_causal, sm_scale,
                                     pv, accum, D, "sage_attn_fwd");
     if (s != SAGE_OK) return s;
@@ -305,7 +308,7 @@ sage_status sage_attn_fwd_g(const int8_t* q_i8, const float* q_scale, const int8
     a.causal = is_causal;
     a.sm_scale = sm_scale;
     a.fp8 = pv == SAGE_PV_FP8;
-    a.two_level = accum == SAGE_ACC_FP16_FP32;
+    a.split_partials = accum == SAGE_ACC_FP16_FP32_SPLIT;
     a.thread_gran = gran == SAGE_GRAN_THREAD;
     return launch_status(sage::launch_attn_fwd(a, (hipStream_t)stream), "sage_attn_fwd");
 }
@@ -454,6 +457,8 @@ sage_status sage_attn_fwd_varlen_g(const int8_t* q_i8, const float* q_scale, con
                                    void* stream) {
     if (gran != SAGE_GRAN_BLOCK && gran != SAGE_GRAN_THREAD)
         return fail(SAGE_ERR_INVALID_ARG, "bad quantisation granularity %d", int(gran));
+    if (gran == SAGE_GRAN_THREAD && accum == SAGE_ACC_FP16_FP32_SPLIT)
+        return fail(SAGE_ERR_UNSUPPORTED, "SAGE_ACC_FP16_FP32_SPLIT is offered with SAGE_GRAN_BLOCK only");
     sage_status s = check_attn_args(q_i8, q_scale, k_i8, k_scale, v_hat, v_scale, out, out_dtype, is_causal, sm_scale,
                                     pv, accum, D, "sage_attn_fwd_varlen");
     if (s != SAGE_OK) return s;
@@ -469,7 +474,7 @@ sage_status sage_attn_fwd_varlen_g(const int8_t* q_i8, const float* q_scale, con
     a.causal = is_causal;
     a.sm_scale = sm_scale;
     a.fp8 = pv == SAGE_PV_FP8;
-    a.two_level = accum == SAGE_ACC_FP16_FP32;
+    a.split_partials = accum == SAGE_ACC_FP16_FP32_SPLIT;
     a.cu_q = cu_seqlens_q, a.cu_k = cu_seqlens_kv, a.total_q = total_q, a.total_k = total_kv;
     a.thread_gran = gran == SAGE_GRAN_THREAD;
     return launch_status(sage::launch_attn_fwd(a, (hipStream_t)stream), "sage_attn_fwd_varlen");

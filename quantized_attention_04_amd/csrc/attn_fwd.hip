@@ -5,11 +5,12 @@
 // matrix-core products, are dequantised with the per-64-token block scales of Q and
 // K, and feed an online base-2 softmax (running row max m, running row sum l); P is
 // rounded to FP16 or FP8-e4m3 and multiplied with V^ on the matrix cores with fp32
-// accumulation.  The README's two-level accumulation (short low-precision sums added
-// into fp32) is what the gfx950 matrix core does by construction: each MFMA sums its
-// 64 products internally and adds the result to the fp32 accumulator operand; a fresh
-// per-tile partial added with a vector-ALU add measures bit-for-bit the same error
-// over 256 chained FP8 MFMAs, so both accumulation modes share this code.
+// accumulation.  The README's two-level accumulation (short sums in a reduced-precision
+// tensor-core accumulator, added into fp32) guards against an inner accumulator that
+// gfx950 does not have: its FP8/FP16 matrix instructions add their products straight
+// into an fp32 operand.  The two-level mode name therefore runs the single-level fp32
+// accumulation; the literal form (a fresh fp32 partial per tile plus a vector add) is
+// kept as its own mode (pv_tile's TL) and rounds the accumulator slightly differently.
 //
 // gfx950 design:
 //  * workgroup = 4 waves = 128 queries; each wave owns 32 queries inside one 64-token Q
@@ -137,12 +138,6 @@ __device__ __forceinline__ int key_of_reg(int kt, int g, int r) {
     return key_of_row<FP8>(kt, 8 * (r >> 2) + 4 * g + (r & 3));
 }
 
-// Global address of K^ chunk ci (LDS chunk (row, c) holds global chunk (row, c ^ swz)).
-template <class C>
-__device__ __forceinline__ const int8_t* k_chunk_src(int ci, const int8_t* ktile) {
-    const int row = ci / (C::KROW / 16), cpos = ci % (C::KROW / 16);
-    return ktile + row * C::KROW + 16 * (cpos ^ kswz<C>(row));
-}
 // Per-thread source offsets of the direct-to-LDS loads, computed once: round u of
 // every thread covers LDS chunk u * THREADS + tid, which lies wholly in the K^ region
 // (rounds < KROUNDS) or the V^ region, so each round has a single uniform base.
@@ -167,14 +162,15 @@ __device__ __forceinline__ DmaPlan<C> make_dma_plan(int tid) {
     }
     return d;
 }
-// lds_wave_base: LDS byte address of the stage plus this wave's 1 KB slot of round 0
-template <class C, int U = 0>
+// lds_wave_base: LDS byte address of the stage plus this wave's 1 KB slot of round 0;
+// rounds U .. END-1 (END = KROUNDS: the K^ region alone)
+template <class C, int U = 0, int END = C::ROUNDS>
 __device__ __forceinline__ void issue_stage(uint32_t lds_wave_base, const int8_t* ktile, const uint8_t* vtile,
                                             const DmaPlan<C>& d) {
-    if constexpr (U < C::ROUNDS) {
+    if constexpr (U < END) {
         const void* base = U < C::KROUNDS ? (const void*)ktile : (const void*)vtile;
         load_lds_16_s<U * C::THREADS * 16>(base, d.off[U], lds_wave_base);
-        issue_stage<C, U + 1>(lds_wave_base, ktile, vtile, d);
+        issue_stage<C, U + 1, END>(lds_wave_base, ktile, vtile, d);
     }
 }
 
@@ -226,12 +222,14 @@ struct PPack<false> {
 // Online softmax step for one tile: updates m, l, returns alpha and writes P straight
 // into the P.V operand registers (FP8: e4m3 of p * 448; FP16: fp16 of p), four values
 // at a time, so no array of fp32 probabilities is ever live.  Masked keys get INT32_MIN
-// and p = 0.  t = S32 * c - m is formed with one rounding (fma), keeping P's rounding
-// to FP16 / e4m3 close to a correctly rounded evaluation.  OFS (offset scores, head dims
-// up to 128): S holds the bits of K0 + S32 2^-26; the row max is taken on those bits
-// (same order), m = fp32((value - K0) c 2^26) is exactly fp32(S32 c), and t = fma(value,
-// c 2^26, fp32(negm - K0 c 2^26)): the bias, rounded once per tile, moves t by at most
-// half an ulp of |negm - K0 c 2^26| (about c / 2, half a unit of S32).
+// and p = 0.  The running max m = fp32(S32max c) is the scheme's fp32 score maximum, and
+// t = S32 c - m is formed with one rounding (fma) from the exact score, so p differs from
+// the two-rounding fp32 evaluation fp32(2^fp32(fp32(S32 c) - m)) by at most half an ulp
+// of the score (plus half an ulp of m - log2 448 with FP8), a few 1e-5 relative at
+// |S2| < 2^10.  OFS (offset scores, head dims up to 128): S holds the bits of K0 + S32
+// 2^-26, so the row max is taken on those bits (same order) and value - K0 = S32 2^-26
+// exactly (one binade), which times c 2^26 is S32 c: the score needs one subtraction
+// of an inline constant instead of an integer-to-float conversion.
 // kmax: the last key this lane's query may see when causal.
 // c0, c1: dequantisation factors of score tiles 0 and 1 (equal unless K carries one
 // scale per 32 keys with FP16 P.V, whose tile kt holds keys 32 kt .. 32 kt + 31).
@@ -284,10 +282,14 @@ __device__ __forceinline__ float softmax_tile(v16i (&S)[2], PPack<FP8>& pk, floa
     const float mnew = fmaxf(m, tmax);
     const float alpha = __builtin_amdgcn_exp2f(m - mnew);
     m = mnew;
-    const float negm = FP8 ? kLog2_448 - mnew : -mnew;
-    // OFS: t = value * c 2^26 + (negm - K0 c 2^26), the bias rounded once per tile
-    const float nb0 = OFS ? __builtin_fmaf(-K0, c0s, negm) : negm;
-    const float nb1 = OFS ? __builtin_fmaf(-K0, c1s, negm) : negm;
+    float negm = FP8 ? kLog2_448 - mnew : -mnew;
+    if constexpr (FP8) {
+        // 448 p of the maximum exceeds 448 by at most the roundings of m and of negm
+        // (1.5 ulp of m: 2^-11 relative at |m| < 2^12, far inside the [448, 464) that
+        // e4m3's round-to-nearest maps to 448); from |m| = 2^12 on the bias backs off by
+        // 8 ulps of m, so that 2^(t + log2 448) stays at or below 448 by construction
+        negm = fabsf(mnew) >= 4096.0f ? __builtin_fmaf(fabsf(mnew), -0x1p-20f, negm) : negm;
+    }
     float acc[4];
 #pragma unroll
     for (int w = 0; w < 8; w++) {
@@ -295,8 +297,7 @@ __device__ __forceinline__ float softmax_tile(v16i (&S)[2], PPack<FP8>& pk, floa
         float q[4];
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-            const float sv = OFS ? __int_as_float(S[kt][r0 + e]) : float(S[kt][r0 + e]);
-            q[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, kt ? c1s : c0s, kt ? nb1 : nb0));
+            q[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sf(S[kt][r0 + e]), kt ? c1s : c0s, negm));
             // the same predicate as above (compiled to a scalar-mask select, not VCC)
             if constexpr (MASK) q[e] = key_of_reg<FP8>(kt, 0, r0 + e) < tvis ? q[e] : 0.0f;
             acc[e] = w == 0 ? q[e] : acc[e] + q[e];
@@ -316,7 +317,11 @@ __device__ __forceinline__ float softmax_tile(v16i (&S)[2], PPack<FP8>& pk, floa
 }
 
 // O^T += V^T P^T for one tile; vst = the V^ region of the tile's LDS stage.
-template <class C, bool FP8>
+// TL = false: the products accumulate straight into O (the matrix instruction adds its
+// sum to the fp32 accumulator operand).  TL = true: the explicit two-level form of the
+// README's two-level accumulation -- each tile's products go into a fresh fp32 partial,
+// which one vector add then folds into O.
+template <class C, bool FP8, bool TL = false>
 __device__ __forceinline__ void pv_tile(const uint8_t* __restrict__ vst, const PPack<FP8>& pk, v16f (&O)[C::DT],
                                         int lane) {
     const int i = lane & 31, g = lane >> 5;
@@ -325,20 +330,23 @@ __device__ __forceinline__ void pv_tile(const uint8_t* __restrict__ vst, const P
         const int d = 32 * dt + i;
         const int sw = vswz<C>(d);
         const uint8_t* rb = vst + d * C::VROW;
+        v16f acc = TL ? v16f{} : O[dt];
         if constexpr (FP8) {
             const v4i a0 = lds_read_16(rb + 16 * ((2 * g) ^ sw));
             const v4i a1 = lds_read_16(rb + 16 * ((2 * g + 1) ^ sw));
             const v8i a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-            O[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pk.b, O[dt], 0, 0, 0, 127, 0, 127);
+            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pk.b, acc, 0, 0, 0, 127, 0, 127);
         } else {
 #pragma unroll
             for (int mm = 0; mm < 4; mm++) {
                 const v4i araw = lds_read_16(rb + 16 * ((2 * mm + g) ^ sw));
                 v8h a;
                 __builtin_memcpy(&a, &araw, 16);
-                O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pk.b[mm], O[dt], 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pk.b[mm], acc, 0, 0, 0);
             }
         }
+        if constexpr (TL) O[dt] += acc;
+        else O[dt] = acc;
     }
 }
 
@@ -360,7 +368,8 @@ struct KParams {
 // TG: the per-thread scales of sage_quant_qkv -- q_scale per token (indexed like the
 // rows of q_i8), k_scale per 32 keys ([slot][2]) -- so the dequantisation factor is
 // per lane: the lane's query, and its lane half's keys (FP8) or the tile's keys (FP16).
-template <int DP, bool FP8, bool CAUSAL, bool OBF16, bool TG = false>
+// TL: the explicit two-level P.V accumulation (pv_tile).
+template <int DP, bool FP8, bool CAUSAL, bool OBF16, bool TG = false, bool TL = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8>::OCC, Cfg<DP, FP8>::OCC))) void attn_fwd_kernel(KParams p) {
     using C = Cfg<DP, FP8>;
     // NST LDS stages: tile j lives in stage j % NST while tiles j+1 .. j+NST-1 stream in.
@@ -483,7 +492,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
 #pragma unroll
             for (int dt = 0; dt < C::DT; dt++) O[dt] *= alpha;
         }
-        pv_tile<C, FP8>(st + C::KBYTES, pk, O, lane);
+        pv_tile<C, FP8, TL>(st + C::KBYTES, pk, O, lane);
     };
     int j = 0;
     for (; j < jm; j++) step(std::false_type{}, j);
@@ -529,8 +538,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
 }
 
 // ---- debug dump of INT32 score tiles through the same loader / operand path ----------
-// One workgroup per tile: the K^ tile is staged with the same swizzle as in the
-// attention kernel; waves 0 and 1 compute the two 32-query halves with qk_tile.
+// One workgroup per tile: the K^ tile arrives through the attention kernel's own
+// direct-to-LDS plan (its K^ rounds: same per-thread offsets, swizzle, waits and
+// barrier); waves 0 and 1 compute the two 32-query halves with qk_tile in the
+// accumulator form the attention kernel uses (offset scores at head dims up to 128,
+// whose bias is taken off as an integer before the write).
 template <int DP, bool FP8>
 __global__ __launch_bounds__(256) void debug_qk_kernel(const int8_t* __restrict__ q_i8,
                                                        const int8_t* __restrict__ k_i8, int B, int Hq, int Hkv,
@@ -547,34 +559,49 @@ __global__ __launch_bounds__(256) void debug_qk_kernel(const int8_t* __restrict_
         for (int e = tid; e < kBlk * kBlk; e += C::THREADS) o[e] = INT32_MIN;
         return;
     }
+    constexpr bool OFS = DP <= 128;
     const int hk = h / (Hq / Hkv);
     const int8_t* ktile = k_i8 + ((int64_t(b) * Hkv + hk) * NBk + kb) * kBlk * DP;
-    for (int ci = tid; ci < C::KCHUNKS; ci += C::THREADS)
-        *(uint4*)(smem + ci * 16) = *(const uint4*)k_chunk_src<C>(ci, ktile);
-    __syncthreads();
+    const DmaPlan<C> dma = make_dma_plan<C>(tid);
+    const uint32_t lds_w0 = __builtin_amdgcn_readfirstlane(lds_addr(smem) + uint32_t(wave * kWave * 16));
+    issue_stage<C, 0, C::KROUNDS>(lds_w0, ktile, nullptr, dma);
+    wait_vmcnt<0>();
+    block_barrier();
     if (wave >= 2) return;
     v4i qf[C::KS];
     load_q_frags<C>(qf, q_i8 + (((int64_t(b) * Hq + h) * NBq + qb) * kBlk + wave * C::QW) * DP, lane);
     v16i S[2];
-    qk_tile<C, FP8>(smem, qf, S, lane);
+    qk_tile<C, FP8, OFS>(smem, qf, S, lane);
     const int g = lane >> 5, i = lane & 31;
 #pragma unroll
     for (int kt = 0; kt < 2; kt++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) o[(wave * C::QW + i) * kBlk + key_of_reg<FP8>(kt, g, r)] = S[kt][r];
+        for (int r = 0; r < 16; r++)
+            o[(wave * C::QW + i) * kBlk + key_of_reg<FP8>(kt, g, r)] = OFS ? S[kt][r] - kScoreBias : S[kt][r];
 }
 
-template <int DP, bool FP8, bool CAUSAL, bool OBF16, bool TG>
+template <int DP, bool FP8, bool CAUSAL, bool OBF16, bool TG, bool TL = false>
 hipError_t launch_attn_t(const KParams& p, int nwg, hipStream_t s) {
     using C = Cfg<DP, FP8>;
-    auto kern = attn_fwd_kernel<DP, FP8, CAUSAL, OBF16, TG>;
+    auto kern = attn_fwd_kernel<DP, FP8, CAUSAL, OBF16, TG, TL>;
     hipLaunchKernelGGL(kern, dim3(nwg), dim3(C::THREADS), 0, s, p);
     return hipGetLastError();
 }
 
 template <int DP, bool FP8>
 hipError_t dispatch_rest(const AttnArgs& a, const KParams& p, int nwg, hipStream_t s) {
-    // both accumulation modes use the MFMA-chained fp32 accumulation (see the header)
+    // SAGE_ACC_FP32 and SAGE_ACC_FP16_FP32 both run the accumulation straight into O
+    // (fp32 at every level already); the literal two-level form runs for
+    // SAGE_ACC_FP16_FP32_SPLIT
+    if (a.split_partials) {
+        const int k2 = (a.causal ? 2 : 0) | (a.out_bf16 ? 1 : 0);
+        switch (k2) {
+        case 0: return launch_attn_t<DP, FP8, false, false, false, true>(p, nwg, s);
+        case 1: return launch_attn_t<DP, FP8, false, true, false, true>(p, nwg, s);
+        case 2: return launch_attn_t<DP, FP8, true, false, false, true>(p, nwg, s);
+        default: return launch_attn_t<DP, FP8, true, true, false, true>(p, nwg, s);
+        }
+    }
     const int key = (a.thread_gran ? 4 : 0) | (a.causal ? 2 : 0) | (a.out_bf16 ? 1 : 0);
     switch (key) {
     case 0: return launch_attn_t<DP, FP8, false, false, false>(p, nwg, s);

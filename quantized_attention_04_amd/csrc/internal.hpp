@@ -48,7 +48,8 @@ struct AttnArgs {
     int B, Hq, Hkv, Nq, Nkv, D;
     int causal;
     float sm_scale;
-    int fp8, two_level;
+    int fp8;
+    int split_partials;  // the explicit two-level P.V form (fresh fp32 partial per tile + vector add)
     const int32_t* cu_q;
     const int32_t* cu_k;
     int total_q, total_k;

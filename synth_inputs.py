@@ -10,6 +10,12 @@ Recipe (one workload = one seed):
   * video-DiT workload only: then draw a per-(head, channel) offset ~ N(0, sigma=2)
     and add it to every token of k (the K outlier pattern that mean smoothing is
     meant to remove);
+  * large-magnitude variants only (``qk_scale``, ``outliers``): q and k are multiplied
+    by qk_scale; with outliers = (f_chan, f_tok), 4 channels of every head (drawn with
+    torch.randperm from the same generator) are multiplied by f_chan in q and k, and 1%
+    of the tokens of every head (likewise drawn) by f_tok -- the outlier channels and
+    tokens of real activations, which drive the block scales, and with them the
+    dequantisation factor of the scores, up by one to two orders of magnitude;
   * cast to fp16 / bf16 with round-to-nearest-even (torch's ``.to``);
   * NHD layout = the same logical tensor stored as (B, N, H, D), contiguous.
 
@@ -45,6 +51,8 @@ class Workload:
     accum: str          # "fp32" | "fp16+fp32"
     seed: int
     k_offset_sigma: Optional[float] = None
+    qk_scale: float = 1.0
+    outliers: Optional[Tuple[float, float]] = None   # (channel factor, token factor)
 
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -97,6 +105,16 @@ def make_qkv(w: Workload, seed: Optional[int] = None) -> Tuple[torch.Tensor, tor
     if w.k_offset_sigma is not None:
         off = torch.randn(w.Hkv, w.D, generator=g, dtype=torch.float32) * w.k_offset_sigma
         k += off[None, :, None, :]
+    if w.qk_scale != 1.0:
+        q *= w.qk_scale
+        k *= w.qk_scale
+    if w.outliers is not None:
+        fc, ft = w.outliers
+        for x in (q, k):
+            for h in range(x.shape[1]):
+                x[:, h, :, torch.randperm(w.D, generator=g)[:4]] *= fc
+                n = x.shape[2]
+                x[:, h, torch.randperm(n, generator=g)[:max(1, n // 100)], :] *= ft
     dt = w.torch_dtype
     return (_to_layout(q.to(dt), w.layout), _to_layout(k.to(dt), w.layout), _to_layout(v.to(dt), w.layout))
 

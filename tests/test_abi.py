@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_strings():
     L = qa.lib()
-    assert L.sage_abi_version() == 4
+    assert L.sage_abi_version() == 5
     for s in range(6):
         assert L.sage_status_string(s).decode().startswith("SAGE_")
     assert qa.padded_dim(1) == 64 and qa.padded_dim(64) == 64 and qa.padded_dim(65) == 128
@@ -148,6 +148,12 @@ def test_attn_fwd_g_checks_granularity_first():
         assert L.sage_attn_fwd_g(*args, 1, None) == qa.SAGE_ERR_DEVICE
     vargs = [FAKE] * 7 + [0, FAKE, FAKE, 2, 2, 2, 100, 100, 60, 60, 64, 0, 0.125, 1, 0]
     assert L.sage_attn_fwd_varlen_g(*vargs, -1, None) == qa.SAGE_ERR_INVALID_ARG
+    # the explicit two-level accumulation is offered with block granularity only
+    split = args[:-1] + [qa.SAGE_ACC_FP16_FP32_SPLIT]
+    assert L.sage_attn_fwd_g(*split, 1, None) == qa.SAGE_ERR_UNSUPPORTED and "SPLIT" in _detail()
+    assert L.sage_attn_fwd_varlen_g(*(vargs[:-1] + [qa.SAGE_ACC_FP16_FP32_SPLIT]), 1, None) == qa.SAGE_ERR_UNSUPPORTED
+    if not torch.cuda.is_available():
+        assert L.sage_attn_fwd_g(*split, 0, None) == qa.SAGE_ERR_DEVICE
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -189,7 +195,7 @@ def test_quant_v_rejects(kw, code):
     ({"sm": float("inf")}, qa.SAGE_ERR_INVALID_ARG),
     ({"sm": float("nan")}, qa.SAGE_ERR_INVALID_ARG),
     ({"pv": 2}, qa.SAGE_ERR_INVALID_ARG),
-    ({"acc": 3}, qa.SAGE_ERR_INVALID_ARG),
+    ({"acc": 4}, qa.SAGE_ERR_INVALID_ARG),
     ({"causal": 2}, qa.SAGE_ERR_INVALID_ARG),
     ({"acc": qa.SAGE_ACC_FP16}, qa.SAGE_ERR_UNSUPPORTED),
     ({"v_scale": None}, qa.SAGE_ERR_INVALID_ARG),

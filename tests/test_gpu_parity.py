@@ -146,6 +146,28 @@ def test_sweep_16k_causal_sampled_rows():
     check_output(case, out, rows, exact=True)
 
 
+# The rest of the sequence sweep (1K and 8K are in OUT_CASES, 32K non-causal and 16K causal
+# above), in the launch configuration the benchmark times.  At 32K causal each kv head's
+# K^ + V^ take 8 MiB, so the causal order runs one head at a time (group of one).
+SWEEP_CASES = [
+    ("sweep_2k", W("seq_sweep", Nq=2048, Nkv=2048), 8),
+    ("sweep_2k_causal", W("seq_sweep", Nq=2048, Nkv=2048, causal=True), 8),
+    ("sweep_4k", W("seq_sweep", Nq=4096, Nkv=4096), 8),
+    ("sweep_4k_causal", W("seq_sweep", Nq=4096, Nkv=4096, causal=True), 8),
+    ("sweep_16k", W("seq_sweep", Nq=16384, Nkv=16384), 4),
+    ("sweep_32k_causal", W("seq_sweep", Nq=32768, Nkv=32768, causal=True), 4),
+]
+
+
+@pytest.mark.parametrize("cid,w,per_head", SWEEP_CASES, ids=[c[0] for c in SWEEP_CASES])
+def test_sweep_points_sampled_rows(cid, w, per_head):
+    case = Case(w)
+    qk, vq = case.gpu_quant(fused=True)
+    out = case.gpu_attn(qk, vq)
+    rows = oracle.sample_rows(w.B, w.Hq, w.Nq, per_head=per_head, seed=7)
+    check_output(case, out, rows, exact=True)
+
+
 def test_layouts_give_identical_outputs():
     w = W("gqa", B=1, Nq=500, Nkv=500, D=96)
     a = Case(w.with_(layout="HND"))

@@ -180,6 +180,26 @@ sage_status sage_quant_qkv(const void* q, const void* k, const void* v, sage_dty
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * sage_quant_qkv for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same arguments
+ * and outputs, bit for bit, without the workspace -- its kernels use a static device
+ * array of sage_quant_qkv_noalloc_max_bytes() bytes (32 MiB) that each GPU the library
+ * runs on holds until the process ends.  The call allocates and frees nothing.
+ *   Limit: sizes whose sage_quant_qkv_workspace_bytes(...) exceeds that maximum return
+ *   SAGE_ERR_UNSUPPORTED before any HIP call (for example B=4, H_kv=32, D=128 FP8
+ *   fits up to Nkv = 10880; larger problems use sage_quant_qkv).
+ *   Concurrency: every call on one GPU shares that GPU's array.  Calls that may overlap
+ *   on one GPU (different streams, or threads without ordering) race and give wrong
+ *   outputs; calls ordered on one stream are safe.  Nothing in the array has to start
+ *   at zero, and a call leaves the previous call's contents overwritten.
+ */
+size_t sage_quant_qkv_noalloc_max_bytes(void);
+sage_status sage_quant_qkv_noalloc(const void* q, const void* k, const void* v, sage_dtype dtype, sage_layout layout,
+                                   int B, int H_qo, int H_kv, int Nq, int Nkv, int D, sage_pv pv, sage_qk_gran gran,
+                                   int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
+                                   void* v_hat, float* v_scale, void* stream);
+
+/*
  * Attention on the quantised operands (step 3-4 above).
  *   Reads q_i8/q_scale/k_i8/k_scale/v_hat/v_scale as produced by the two calls
  *   above (v_scale only in FP8 mode, may be NULL otherwise).

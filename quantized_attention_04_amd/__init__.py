@@ -97,6 +97,9 @@ _EXPORTS = {
                                                                                 ctypes.c_void_p]),
     "sage_attn_fwd_mxfp4_varlen": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] + [ctypes.c_void_p] * 2
                                    + [ctypes.c_int] * 9 + [ctypes.c_float, ctypes.c_void_p]),
+    "sage_quant_qkv_noalloc_max_bytes": (ctypes.c_size_t, []),
+    "sage_quant_qkv_noalloc": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 10
+                               + [ctypes.c_void_p] * 8),
     "sage_attn_fwd_varlen_g": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] + [ctypes.c_void_p] * 2
                                + [ctypes.c_int] * 9 + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                        ctypes.c_void_p]),
@@ -304,9 +307,11 @@ def debug_qk_int32(qk: QKQuant, tiles: torch.Tensor, pv: str = "fp8") -> torch.T
 
 def quant_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: str = "HND", pv: str = "fp8",
               workspace: Optional[torch.Tensor] = None, out_qk: Optional[QKQuant] = None,
-              out_v: Optional[VQuant] = None, gran: str = "block"):
+              out_v: Optional[VQuant] = None, gran: str = "block", noalloc: bool = False):
     """quant_qk and quant_v in one library call (same outputs, fewer kernel launches).
-    gran="thread": one Q scale per token and one K scale per 32 keys."""
+    gran="thread": one Q scale per token and one K scale per 32 keys.
+    noalloc=True: sage_quant_qkv_noalloc, whose workspace is the library's static device
+    scratch (nothing is allocated for the call once out_qk and out_v are given)."""
     if gran not in _GRAN:
         raise ValueError(f"gran must be 'block' or 'thread', got {gran!r}")
     for name, x in (("q", q), ("k", k), ("v", v)):
@@ -335,6 +340,15 @@ def quant_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: str = "
         elt = 1 if pv == "fp8" else 2
         out_v = VQuant(torch.empty(B, Hkv, nbk, max(Dp, 1), 64 * elt, dtype=torch.uint8, device=dev),
                        torch.empty(B, Hkv, max(Dp, 1), dtype=torch.float32, device=dev) if pv == "fp8" else None, pv)
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc takes no workspace")
+        _check(L.sage_quant_qkv_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), _DT[q.dtype], _LAYOUT[layout], B,
+                                        Hq, Hkv, Nq, Nkv, D, _PV[pv], _GRAN[gran], out_qk.q_i8.data_ptr(),
+                                        out_qk.q_scale.data_ptr(), out_qk.k_i8.data_ptr(), out_qk.k_scale.data_ptr(),
+                                        out_qk.k_mean.data_ptr(), out_v.v_hat.data_ptr(), _ptr(out_v.v_scale),
+                                        _stream(dev)))
+        return out_qk, out_v
     need = L.sage_quant_qkv_workspace_bytes(B, Hkv, Nkv, D, _PV[pv])
     if workspace is None:
         workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=dev)

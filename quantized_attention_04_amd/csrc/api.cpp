@@ -274,6 +274,48 @@ sage_status sage_quant_qkv(const void* q, const void* k, const void* v, sage_dty
     return launch_status(sage::launch_quant_qkv(a, va, (hipStream_t)stream), "sage_quant_qkv");
 }
 
+size_t sage_quant_qkv_noalloc_max_bytes(void) { return sage::kNoAllocScratchBytes; }
+
+sage_status sage_quant_qkv_noalloc(const void* q, const void* k, const void* v, sage_dtype dtype, sage_layout layout,
+                                   int B, int H_qo, int H_kv, int Nq, int Nkv, int D, sage_pv pv, sage_qk_gran gran,
+                                   int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
+                                   void* v_hat, float* v_scale, void* stream) {
+    if (gran != SAGE_GRAN_BLOCK && gran != SAGE_GRAN_THREAD)
+        return fail(SAGE_ERR_INVALID_ARG, "bad quantisation granularity %d", int(gran));
+    sage_status s = check_qkv_args(q, k, v, dtype, pv, q_i8, q_scale, k_i8, k_scale, k_mean, v_hat, v_scale,
+                                   "sage_quant_qkv_noalloc");
+    if (s != SAGE_OK) return s;
+    if (layout != SAGE_HND && layout != SAGE_NHD) return fail(SAGE_ERR_INVALID_ARG, "bad layout %d", int(layout));
+    s = check_shape(B, H_qo, H_kv, Nq, Nkv, D);
+    if (s != SAGE_OK) return s;
+    const size_t need = sage_quant_qkv_workspace_bytes(B, H_kv, Nkv, D, pv);
+    if (need > sage::kNoAllocScratchBytes)
+        return fail(SAGE_ERR_UNSUPPORTED,
+                    "sage_quant_qkv_noalloc: these sizes need %zu bytes of workspace, the static scratch holds %zu "
+                    "(use sage_quant_qkv with a caller-supplied workspace)",
+                    need, sage::kNoAllocScratchBytes);
+    s = check_device();
+    if (s != SAGE_OK) return s;
+    void* ws = nullptr;
+    const hipError_t e = sage::noalloc_scratch(&ws);
+    if (e != hipSuccess)
+        return fail(SAGE_ERR_HIP, "sage_quant_qkv_noalloc: no device address for the static scratch: %s",
+                    hipGetErrorString(e));
+    sage::QuantQKArgs a{};
+    a.q = q, a.k = k;
+    a.bf16 = dtype == SAGE_BF16;
+    a.layout_nhd = layout == SAGE_NHD;
+    a.B = B, a.Hq = H_qo, a.Hkv = H_kv, a.Nq = Nq, a.Nkv = Nkv, a.D = D;
+    a.q_i8 = q_i8, a.q_scale = q_scale, a.k_i8 = k_i8, a.k_scale = k_scale, a.k_mean = k_mean;
+    a.workspace = ws;
+    a.thread_gran = gran == SAGE_GRAN_THREAD;
+    sage::QuantVArgs va{};
+    va.v = v;
+    va.fp8 = pv == SAGE_PV_FP8;
+    va.v_hat = v_hat, va.v_scale = v_scale;
+    return launch_status(sage::launch_quant_qkv(a, va, (hipStream_t)stream), "sage_quant_qkv_noalloc");
+}
+
 sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
                           const void* v_hat, const float* v_scale, void* out, sage_dtype out_dtype,
                           sage_layout out_layout, int B, int H_qo, int H_kv, int Nq, int Nkv, int D, int is_causal,

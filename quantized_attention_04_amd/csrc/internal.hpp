@@ -124,6 +124,11 @@ inline QKVWorkspace qkv_workspace(int B, int Hkv, int Nkv, int D, bool packed, i
     return w;
 }
 
+// Static workspace of sage_quant_qkv_noalloc (quant.hip): its size, and its device
+// address on the current device (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 hipError_t launch_quant_qk(const QuantQKArgs& a, hipStream_t s);
 hipError_t launch_quant_qkv(const QuantQKArgs& a, const QuantVArgs& v, hipStream_t s);
 hipError_t launch_quant_v(const QuantVArgs& a, hipStream_t s);

@@ -8,6 +8,8 @@
 // walks a batch of sequences through a SeqMap, dense or packed (the variable-length
 // form of the README's "Available APIs": sageattn_varlen); grids span the longest
 // sequence and blocks past a sequence's end return at once.
+#include <atomic>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -714,6 +716,38 @@ hipError_t launch_qkv_dp(const QuantQKArgs& a, const QuantVArgs& v, hipStream_t 
 
 hipError_t launch_quant_qkv(const QuantQKArgs& a, const QuantVArgs& v, hipStream_t s) {
     return a.bf16 ? launch_qkv_dp<true>(a, v, s) : launch_qkv_dp<false>(a, v, s);
+}
+
+// ---- the fused quantisation's workspace in static device memory --------------------
+// For callers that cannot allocate (sage_quant_qkv_noalloc).  Every device the library
+// runs on holds one copy for the life of the process.  In host code the array's name
+// stands for a host-side shadow, not for the device copy, so kernels only ever receive
+// the device address that hipGetSymbolAddress reports, fetched once per device (with
+// that device current) on its first use.  The fused launch sequence writes every part
+// of the workspace it reads, so nothing in it has to start at zero.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::atomic<uintptr_t> g_scratch_ptr[kMaxScratchDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    uintptr_t p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == 0) {
+        void* d = nullptr;
+        e = hipGetSymbolAddress(&d, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (d == nullptr) return hipErrorInvalidSymbol;
+        p = reinterpret_cast<uintptr_t>(d);
+        g_scratch_ptr[dev].store(p, std::memory_order_release);  // same value if two threads race here
+    }
+    *ptr = reinterpret_cast<void*>(p);
+    return hipSuccess;
 }
 
 

@@ -139,6 +139,28 @@ def test_fused_quant_fp16_takes_no_scale():
     assert _fused(gran=1) == qa.SAGE_ERR_DEVICE
 
 
+def test_quant_qkv_noalloc_limits():
+    """The allocation-free fused quantisation refuses sizes whose workspace exceeds its
+    static scratch before any HIP call, and otherwise validates like sage_quant_qkv."""
+    L = qa.lib()
+    cap = L.sage_quant_qkv_noalloc_max_bytes()
+    assert cap == 32 << 20
+
+    def call(B, Hkv, N, D, pv=1, **kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, layout=0, B=B, Hq=Hkv, Hkv=Hkv, Nq=N, Nkv=N, D=D, pv=pv, gran=0)
+        a.update(kw)
+        return L.sage_quant_qkv_noalloc(a["q"], a["k"], a["v"], a["dtype"], a["layout"], a["B"], a["Hq"], a["Hkv"],
+                                        a["Nq"], a["Nkv"], a["D"], a["pv"], a["gran"], *([FAKE] * 7), None)
+    assert L.sage_quant_qkv_workspace_bytes(4, 32, 10880, 128, 1) <= cap < L.sage_quant_qkv_workspace_bytes(
+        4, 32, 10944, 128, 1)
+    assert call(4, 32, 10944, 128) == qa.SAGE_ERR_UNSUPPORTED and "static scratch" in _detail()
+    assert call(1, 2, 100, 64, gran=5) == qa.SAGE_ERR_INVALID_ARG
+    assert call(1, 2, 100, 64, q=None) == qa.SAGE_ERR_INVALID_ARG
+    assert call(1, 2, 100, 300) == qa.SAGE_ERR_UNSUPPORTED
+    if not torch.cuda.is_available():
+        assert call(4, 32, 10880, 128) == qa.SAGE_ERR_DEVICE
+
+
 def test_attn_fwd_g_checks_granularity_first():
     L = qa.lib()
     args = [FAKE] * 7 + [0, 0, 1, 2, 2, 128, 128, 64, 0, 0.125, 1, 0]

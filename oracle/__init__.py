@@ -67,6 +67,9 @@ def lib() -> ctypes.CDLL:
     L.orc_attn_emulate_g.restype = _L
     L.orc_attn_emulate_g.argtypes = [_i8p, _f32p, _i8p, _f32p, _f32p, _f32p, ctypes.c_int, _L, _L, _L, _L, _L,
                                      _L, _L, _L, ctypes.c_int, ctypes.c_double, _i64p, _L, _f64p, ctypes.c_void_p]
+    L.orc_attn_breakdown.argtypes = [_f32p, _f32p, _f32p, _i8p, _f32p, _i8p, _f32p, _f32p, _f32p, ctypes.c_int, _L,
+                                     _L, _L, _L, _L, _L, ctypes.c_int, ctypes.c_double, _i64p, _L, ctypes.c_int,
+                                     _f64p]
     L.orc_tie_flip.restype = ctypes.c_double
     L.orc_tie_flip.argtypes = [ctypes.c_double, ctypes.c_int]
     L.orc_mx_p_block.argtypes = [_f64p, _f32p, _i32p, _L, _f64p, _f64p]
@@ -274,6 +277,27 @@ def attn_emulate(Q: Quantized, causal: bool, sm_scale: float, rows: np.ndarray, 
                                    rows.shape[0], out, None if amb is None else amb.ctypes.data_as(ctypes.c_void_p))
     _range_check(bad, with_ambiguity)
     return (out, amb) if with_ambiguity else out
+
+
+# approximations of the scheme that attn_breakdown can switch on one at a time
+PART_QK, PART_P, PART_V = 1, 2, 4
+
+
+def attn_breakdown(q: np.ndarray, k: np.ndarray, v: np.ndarray, Q: Quantized, causal: bool, sm_scale: float,
+                   rows: np.ndarray, parts: int) -> np.ndarray:
+    """Rows [R, D] (fp64) of attention with the chosen approximations of the scheme on
+    (PART_QK: INT8 scores, PART_P: P rounded to its P.V format, PART_V: V quantised) and
+    the others exact; parts = 0 is exact attention.  Block granularity."""
+    B, Hq, Nq, D = q.shape
+    Hkv, Nkv = k.shape[1], k.shape[2]
+    rows = np.ascontiguousarray(rows, np.int64).reshape(-1, 3)
+    out = np.empty((rows.shape[0], D), np.float64)
+    vs = Q.v_scale if Q.v_scale is not None else np.zeros((B, Hkv, D), np.float32)
+    lib().orc_attn_breakdown(np.ascontiguousarray(q, np.float32), np.ascontiguousarray(k, np.float32),
+                             np.ascontiguousarray(v, np.float32), Q.q_i8, Q.q_scale, Q.k_i8, Q.k_scale, Q.v_hat, vs,
+                             int(Q.pv_fp8), B, Hq, Hkv, Nq, Nkv, D, int(bool(causal)), float(sm_scale), rows,
+                             rows.shape[0], int(parts), out)
+    return out
 
 
 def attn_exact(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, sm_scale: float,

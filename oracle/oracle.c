@@ -703,3 +703,93 @@ long orc_attn_emulate_mxfp4(const uint8_t* qc, const int32_t* qE, const uint8_t*
     }
     return bad_rows;
 }
+
+/* ---------------------------------------------------------------------------
+ * Error breakdown of the scheme: the attention of selected rows with each of its
+ * three approximations switched on or off independently (parts, a bit set):
+ *   bit 0  scores from the INT8 codes and block scales, S2 = S32 sq sk sm_scale log2 e
+ *          (else exact scores sm_scale log2 e q.k from the unquantised q and k);
+ *   bit 1  P rounded to its P.V format: fp16(p), or e4m3(448 p) / 448
+ *          (else the unrounded p);
+ *   bit 2  V as the quantised operand: fp16(v), or the e4m3 code times v_scale
+ *          (v_scale = amax / 448) (else the exact v).
+ * Everything is fp64; the online softmax walks 64-key blocks in ascending order with
+ * the running maximum (so P is rounded relative to it, as in the emulation), and l sums
+ * the unrounded p.  parts = 0 is exact attention; parts = 7 is the emulation's
+ * arithmetic with its fp32 score and softmax steps taken in fp64 instead.
+ * q, k, v: the exact inputs (B, H, N, D); q8/sq/k8/sk/vhat/vscale: as orc_attn_emulate.
+ * ------------------------------------------------------------------------- */
+void orc_attn_breakdown(const float* q, const float* k, const float* v, const int8_t* q8, const float* sq,
+                        const int8_t* k8, const float* sk, const float* vhat, const float* vscale, int pv_fp8, long B,
+                        long Hq, long Hkv, long Nq, long Nkv, long D, int causal, double sm_scale,
+                        const int64_t* rows, long R, int parts, double* out) {
+    const double LOG2E = 1.4426950408889634074;
+    const int fmt = pv_fp8 ? ORC_E4M3 : ORC_FP16;
+    long group = Hq / Hkv;
+    long nqb = (Nq + BLK - 1) / BLK, nkb = (Nkv + BLK - 1) / BLK;
+    const long off = Nkv - Nq;
+    (void)B;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (long r = 0; r < R; r++) {
+        long b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+        long hk = h / group;
+        double* acc = (double*)calloc((size_t)D, sizeof(double));
+        double s2[BLK], pj[BLK];
+        int vis[BLK];
+        double m = -INFINITY, l = 0.0;
+        for (long kb = 0; kb < nkb; kb++) {
+            long j0 = kb * BLK;
+            if (causal && j0 > i + off) break;
+            long j1 = j0 + BLK < Nkv ? j0 + BLK : Nkv;
+            double bmax = -INFINITY;
+            for (long j = j0; j < j1; j++) {
+                vis[j - j0] = !(causal && j > i + off);
+                if (!vis[j - j0]) continue;
+                double sc = 0.0;
+                if (parts & 1) {
+                    const int8_t* qr = q8 + ((b * Hq + h) * Nq + i) * D;
+                    const int8_t* kr = k8 + ((b * Hkv + hk) * Nkv + j) * D;
+                    int64_t s32 = 0;
+                    for (long d = 0; d < D; d++) s32 += (int64_t)qr[d] * (int64_t)kr[d];
+                    sc = (double)s32 * (double)sq[(b * Hq + h) * nqb + i / BLK] *
+                         (double)sk[(b * Hkv + hk) * nkb + kb] * sm_scale * LOG2E;
+                } else {
+                    const float* qr = q + ((b * Hq + h) * Nq + i) * D;
+                    const float* kr = k + ((b * Hkv + hk) * Nkv + j) * D;
+                    for (long d = 0; d < D; d++) sc += (double)qr[d] * (double)kr[d];
+                    sc *= sm_scale * LOG2E;
+                }
+                s2[j - j0] = sc;
+                if (sc > bmax) bmax = sc;
+            }
+            double mnew = m > bmax ? m : bmax;
+            double alpha = (m == -INFINITY) ? 0.0 : exp2(m - mnew);
+            double psum = 0.0;
+            for (long j = j0; j < j1; j++) {
+                pj[j - j0] = 0.0;
+                if (!vis[j - j0]) continue;
+                double p = exp2(s2[j - j0] - mnew);
+                psum += p;
+                pj[j - j0] = (parts & 2) ? (pv_fp8 ? orc_round(p * 448.0, fmt, 1) / 448.0 : orc_round(p, fmt, 1)) : p;
+            }
+            l = alpha * l + psum;
+            for (long d = 0; d < D; d++) {
+                double a = 0.0;
+                for (long j = j0; j < j1; j++) {
+                    double vv;
+                    if (parts & 4) {
+                        vv = (double)vhat[((b * Hkv + hk) * Nkv + j) * D + d];
+                        if (pv_fp8) vv *= (double)vscale[(b * Hkv + hk) * D + d]; /* v = code * amax / 448 */
+                    } else {
+                        vv = (double)v[((b * Hkv + hk) * Nkv + j) * D + d];
+                    }
+                    a += pj[j - j0] * vv;
+                }
+                acc[d] = alpha * acc[d] + a;
+            }
+            m = mnew;
+        }
+        for (long d = 0; d < D; d++) out[r * D + d] = l > 0.0 ? acc[d] / l : 0.0;
+        free(acc);
+    }
+}

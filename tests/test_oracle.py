@@ -733,3 +733,50 @@ def test_emulate_thread_granularity_is_softmax_of_dequantised_scores(causal):
         ref = p @ Q.v_hat[0, h].astype(np.float64) / p.sum(axis=1, keepdims=True)
         err = np.abs(got[h * 70:(h + 1) * 70] - ref).max()
         assert err <= 2e-3 * np.abs(ref).max(), err
+
+
+# ----------------------------------------------------------------------------- error breakdown
+
+@pytest.mark.parametrize("pv_fp8,causal", [(False, False), (True, True)])
+def test_breakdown_extremes(pv_fp8, causal):
+    """No approximation on: exact attention.  All on: the emulation (whose fp32 softmax
+    steps move p by ~1e-7; P roundings within 2^-14 of a tie may differ, as amb says)."""
+    q = _bf16_vals((1, 2, 150, 48), seed=60)
+    k = _bf16_vals((1, 2, 150, 48), seed=61) + 0.7
+    v = _bf16_vals((1, 2, 150, 48), seed=62)
+    Q = oracle.quantize(q, k, v, pv_fp8)
+    rows = oracle.all_rows(1, 2, 150)
+    ex = oracle.attn_exact(q, k, v, causal, 0.2, rows)
+    np.testing.assert_allclose(oracle.attn_breakdown(q, k, v, Q, causal, 0.2, rows, 0), ex, rtol=0, atol=1e-12)
+    em, amb = oracle.attn_emulate(Q, causal, 0.2, rows, with_ambiguity=True)
+    full = oracle.attn_breakdown(q, k, v, Q, causal, 0.2, rows, 7)
+    # fp32 against fp64 p: relative ~1e-7 on each weight, so absolute 1e-6 of the output scale
+    assert (np.abs(full - em) <= 1e-6 * np.abs(em).max() + amb).all()
+
+
+def test_breakdown_single_parts_closed_forms():
+    """Each approximation alone, against its closed form on one key block (one-shot
+    base-2 softmax): INT8 scores -> softmax of the dequantised code products; P only ->
+    fp16-rounded weights over the unrounded sum; V only -> the exact weights on the
+    fp16 V (fp16 inputs: V unchanged, so equal to exact attention)."""
+    q = _fp16_vals((1, 1, 40, 32), seed=63)
+    k = _fp16_vals((1, 1, 60, 32), seed=64)
+    v = _fp16_vals((1, 1, 60, 32), seed=65)
+    Q = oracle.quantize(q, k, v, pv_fp8=False)
+    rows = oracle.all_rows(1, 1, 40)
+    sc = 0.3
+    s_ex = q[0, 0].astype(np.float64) @ k[0, 0].astype(np.float64).T * sc * LOG2E
+    s_q = (Q.q_i8[0, 0].astype(np.int64) @ Q.k_i8[0, 0].astype(np.int64).T) * \
+        Q.q_scale[0, 0, 0].astype(np.float64) * Q.k_scale[0, 0, 0].astype(np.float64) * sc * LOG2E
+    V = v[0, 0].astype(np.float64)
+
+    def soft(s, rnd=False):
+        p = np.exp2(s - s.max(1, keepdims=True))
+        w = p.astype(np.float16).astype(np.float64) if rnd else p
+        return w @ V / p.sum(1, keepdims=True)
+    np.testing.assert_allclose(oracle.attn_breakdown(q, k, v, Q, False, sc, rows, oracle.PART_QK), soft(s_q),
+                               rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(oracle.attn_breakdown(q, k, v, Q, False, sc, rows, oracle.PART_P), soft(s_ex, True),
+                               rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(oracle.attn_breakdown(q, k, v, Q, False, sc, rows, oracle.PART_V), soft(s_ex),
+                               rtol=1e-12, atol=1e-14)

@@ -227,6 +227,36 @@ sage_status sage_attn_fwd_g(const int8_t* q_i8, const float* q_scale, const int8
                             float sm_scale, sage_pv pv, sage_accum accum, sage_qk_gran gran, void* stream);
 
 /*
+ * Key-range splits for launches that leave the chip idle (few heads and short query
+ * ranges: B=1 H=8 N=2048 gives 128 workgroups for 256 CUs).  The key tiles of every
+ * 128-query tile are split into num_splits ranges of equal tile count; each range runs
+ * the online softmax of sage_attn_fwd on its own (its own running maximum, from -inf)
+ * and leaves its own output o_s = O_s / l_s (fp16: |o_s| is bounded by the largest
+ * |v^|, an fp16 value), running maximum m_s and row sum l_s (fp32) in the workspace; a
+ * second kernel combines them, o = sum_s w_s o_s / sum_s w_s with w_s = 2^(m_s - M) l_s
+ * and M = max_s m_s, and writes out as sage_attn_fwd does.  This is the same
+ * attention with the softmax state merged once more (the merge the online softmax
+ * already does between key tiles); P's roundings are then taken relative to each
+ * range's running maximum, which moves FP16 P by at most one fp16 rounding (the output
+ * stays within the parity bar), but would move FP8 P codes by up to a binade, so the
+ * splits are offered with SAGE_PV_FP16 only (SAGE_ERR_UNSUPPORTED otherwise).
+ *   Arguments: those of sage_attn_fwd (block granularity), plus num_splits (1 = plain
+ *   sage_attn_fwd, workspace ignored; at most 64) and a device workspace of at least
+ *   sage_attn_fwd_split_workspace_bytes(B, H_qo, Nq, D, num_splits) bytes, 16-byte
+ *   aligned, contents on entry ignored and on exit unspecified.
+ *   sage_attn_fwd_split_choice gives the library's pick for a shape: 1 (no split) unless
+ *   pv is SAGE_PV_FP16 and the unsplit launch has fewer than 384 workgroups; then enough
+ *   splits for about two workgroups per CU, each of at least four key tiles.
+ */
+int sage_attn_fwd_split_choice(int B, int H_qo, int Nq, int Nkv, int D, int is_causal, sage_pv pv);
+size_t sage_attn_fwd_split_workspace_bytes(int B, int H_qo, int Nq, int D, int num_splits);
+sage_status sage_attn_fwd_split(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                                const void* v_hat, const float* v_scale, void* out, sage_dtype out_dtype,
+                                sage_layout out_layout, int B, int H_qo, int H_kv, int Nq, int Nkv, int D,
+                                int is_causal, float sm_scale, sage_pv pv, sage_accum accum, int num_splits,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Debug dump of INT32 score tiles through the attention kernel's own operand
  * path: the K^ tile arrives by the same direct-to-LDS loads and swizzle, and the
  * scores come from the same matrix-instruction sequence and accumulator form (at

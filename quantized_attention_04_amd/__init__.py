@@ -97,6 +97,11 @@ _EXPORTS = {
                                                                                 ctypes.c_void_p]),
     "sage_attn_fwd_mxfp4_varlen": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] + [ctypes.c_void_p] * 2
                                    + [ctypes.c_int] * 9 + [ctypes.c_float, ctypes.c_void_p]),
+    "sage_attn_fwd_split_choice": (ctypes.c_int, [ctypes.c_int] * 6 + [ctypes.c_int]),
+    "sage_attn_fwd_split_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 5),
+    "sage_attn_fwd_split": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] * 9
+                            + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                               ctypes.c_size_t, ctypes.c_void_p]),
     "sage_quant_qkv_noalloc_max_bytes": (ctypes.c_size_t, []),
     "sage_quant_qkv_noalloc": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 10
                                + [ctypes.c_void_p] * 8),
@@ -272,8 +277,21 @@ def quant_v(v: torch.Tensor, layout: str = "HND", pv: str = "fp8", workspace: Op
     return out
 
 
+def split_choice(qk: QKQuant, pv: str, is_causal: bool = False) -> int:
+    """The library's key-range split count for this launch (1: no split)."""
+    return int(lib().sage_attn_fwd_split_choice(qk.B, qk.Hq, qk.Nq, qk.Nkv, qk.D, int(bool(is_causal)), _PV[pv]))
+
+
+def split_workspace_bytes(qk: QKQuant, splits: int) -> int:
+    return int(lib().sage_attn_fwd_split_workspace_bytes(qk.B, qk.Hq, qk.Nq, qk.D, int(splits)))
+
+
 def attn_fwd(qk: QKQuant, vq: VQuant, out_dtype: torch.dtype, layout: str = "HND", is_causal: bool = False,
-             sm_scale: Optional[float] = None, accum: str = "fp32", out: Optional[torch.Tensor] = None) -> torch.Tensor:
+             sm_scale: Optional[float] = None, accum: str = "fp32", out: Optional[torch.Tensor] = None,
+             splits=1, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """sage_attn_fwd (or sage_attn_fwd_g).  splits: key-range splits of every query tile
+    (sage_attn_fwd_split; FP16 P.V, block granularity), an int or "auto" for the
+    library's choice; workspace: the splits' fp32 state (allocated here if None)."""
     if out_dtype not in _DT:
         raise ValueError("out_dtype must be float16 or bfloat16")
     if accum not in _ACC:
@@ -288,7 +306,15 @@ def attn_fwd(qk: QKQuant, vq: VQuant, out_dtype: torch.dtype, layout: str = "HND
     args = (qk.q_i8.data_ptr(), qk.q_scale.data_ptr(), qk.k_i8.data_ptr(), qk.k_scale.data_ptr(), vq.v_hat.data_ptr(),
             _ptr(vq.v_scale), out.data_ptr(), _DT[out_dtype], _LAYOUT[layout], B, Hq, Hkv, Nq, Nkv, D,
             int(bool(is_causal)), float(sm_scale), _PV[vq.pv], _ACC[accum])
-    if qk.gran == "block":
+    if splits == "auto":
+        splits = split_choice(qk, vq.pv, is_causal) if qk.gran == "block" and accum != "fp16+fp32-split" else 1
+    splits = int(splits)
+    if splits > 1:
+        need = split_workspace_bytes(qk, splits)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        _check(lib().sage_attn_fwd_split(*args, splits, workspace.data_ptr(), workspace.numel(), _stream(dev)))
+    elif qk.gran == "block":
         _check(lib().sage_attn_fwd(*args, _stream(dev)))
     else:
         _check(lib().sage_attn_fwd_g(*args, _GRAN[qk.gran], _stream(dev)))
@@ -441,9 +467,10 @@ def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: s
              sm_scale: Optional[float] = None, pv: str = "fp8", accum: str = "fp32",
              qk_gran: str = "block") -> torch.Tensor:
     """softmax(sm_scale * q k^T [causal]) v with INT8 QK^T and FP8/FP16 PV; returns q's dtype and layout.
-    qk_gran: "block" (one scale per 64 tokens) or "thread" (per query token, per 32 keys)."""
+    qk_gran: "block" (one scale per 64 tokens) or "thread" (per query token, per 32 keys).
+    Launches too small to fill the GPU take the library's key-range splits (FP16 P.V)."""
     qk, vq = quant_qkv(q, k, v, tensor_layout, pv, gran=qk_gran)
-    return attn_fwd(qk, vq, q.dtype, tensor_layout, is_causal, sm_scale, accum)
+    return attn_fwd(qk, vq, q.dtype, tensor_layout, is_causal, sm_scale, accum, splits="auto")
 
 
 # ----------------------------------------------------------------------------- variable-length batches

@@ -62,6 +62,7 @@ sage_status launch_status(hipError_t e, const char* what) {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 constexpr int kMaxN = 1 << 28;     // tokens per sequence
+constexpr int kMaxSplits = 64;     // key-range splits of one query tile
 constexpr int kMaxGridYZ = 65535;  // batch and head grid dimensions
 
 // Shared shape checks.  Returns SAGE_OK or the failing status (with detail set).
@@ -353,6 +354,69 @@ sage_status sage_attn_fwd_g(const int8_t* q_i8, const float* q_scale, const int8
     a.split_partials = accum == SAGE_ACC_FP16_FP32_SPLIT;
     a.thread_gran = gran == SAGE_GRAN_THREAD;
     return launch_status(sage::launch_attn_fwd(a, (hipStream_t)stream), "sage_attn_fwd");
+}
+
+int sage_attn_fwd_split_choice(int B, int H_qo, int Nq, int Nkv, int D, int is_causal, sage_pv pv) {
+    (void)is_causal;
+    if (B <= 0 || H_qo <= 0 || Nq <= 0 || Nkv <= 0 || D <= 0 || D > 256 || pv != SAGE_PV_FP16) return 1;
+    // workgroups of the unsplit launch (128 queries each); a split pays when they leave
+    // CUs idle: aim at two workgroups per CU (256 CUs), every split >= 4 key tiles
+    const int64_t nwg = int64_t(B) * H_qo * ((Nq + 127) / 128);
+    const int nbk = nblocks(Nkv);
+    if (nwg >= 384 || nbk < 8) return 1;
+    int S = int((512 + nwg - 1) / nwg);
+    S = S < nbk / 4 ? S : nbk / 4;
+    S = S < 16 ? S : 16;
+    if (S <= 1) return 1;
+    const int tps = (nbk + S - 1) / S;
+    return (nbk + tps - 1) / tps;
+}
+
+size_t sage_attn_fwd_split_workspace_bytes(int B, int H_qo, int Nq, int D, int num_splits) {
+    if (B <= 0 || H_qo <= 0 || Nq <= 0 || D <= 0 || D > 256 || num_splits <= 1 || num_splits > kMaxSplits) return 0;
+    return sage::attn_split_workspace(B, H_qo, Nq, D, num_splits).bytes;
+}
+
+sage_status sage_attn_fwd_split(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                                const void* v_hat, const float* v_scale, void* out, sage_dtype out_dtype,
+                                sage_layout out_layout, int B, int H_qo, int H_kv, int Nq, int Nkv, int D,
+                                int is_causal, float sm_scale, sage_pv pv, sage_accum accum, int num_splits,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    if (num_splits < 1 || num_splits > kMaxSplits)
+        return fail(SAGE_ERR_INVALID_ARG, "num_splits must be in 1..%d (got %d)", kMaxSplits, num_splits);
+    if (num_splits == 1)
+        return sage_attn_fwd_g(q_i8, q_scale, k_i8, k_scale, v_hat, v_scale, out, out_dtype, out_layout, B, H_qo,
+                               H_kv, Nq, Nkv, D, is_causal, sm_scale, pv, accum, SAGE_GRAN_BLOCK, stream);
+    sage_status s = check_attn_args(q_i8, q_scale, k_i8, k_scale, v_hat, v_scale, out, out_dtype, is_causal, sm_scale,
+                                    pv, accum, D, "sage_attn_fwd_split");
+    if (s != SAGE_OK) return s;
+    if (out_layout != SAGE_HND && out_layout != SAGE_NHD)
+        return fail(SAGE_ERR_INVALID_ARG, "bad layout %d", int(out_layout));
+    s = check_shape(B, H_qo, H_kv, Nq, Nkv, D);
+    if (s != SAGE_OK) return s;
+    if (pv != SAGE_PV_FP16)
+        return fail(SAGE_ERR_UNSUPPORTED, "sage_attn_fwd_split: key-range splits are offered with FP16 P.V only (each "
+                                          "split's own running maximum would move FP8 P codes)");
+    if (accum == SAGE_ACC_FP16_FP32_SPLIT)
+        return fail(SAGE_ERR_UNSUPPORTED, "sage_attn_fwd_split: SAGE_ACC_FP16_FP32_SPLIT is not offered with splits");
+    const size_t need = sage_attn_fwd_split_workspace_bytes(B, H_qo, Nq, D, num_splits);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16))
+        return fail(SAGE_ERR_WORKSPACE, "sage_attn_fwd_split: workspace of %zu bytes (16-byte aligned) required, got %zu",
+                    need, workspace ? workspace_bytes : size_t(0));
+    s = check_device();
+    if (s != SAGE_OK) return s;
+    sage::AttnArgs a{};
+    a.q_i8 = q_i8, a.q_scale = q_scale, a.k_i8 = k_i8, a.k_scale = k_scale, a.v_hat = v_hat, a.v_scale = v_scale;
+    a.out = out;
+    a.out_bf16 = out_dtype == SAGE_BF16;
+    a.out_nhd = out_layout == SAGE_NHD;
+    a.B = B, a.Hq = H_qo, a.Hkv = H_kv, a.Nq = Nq, a.Nkv = Nkv, a.D = D;
+    a.causal = is_causal;
+    a.sm_scale = sm_scale;
+    a.fp8 = 0;
+    a.splits = num_splits;
+    a.workspace = workspace;
+    return launch_status(sage::launch_attn_fwd(a, (hipStream_t)stream), "sage_attn_fwd_split");
 }
 
 sage_status sage_debug_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int B, int H_qo, int H_kv, int Nq, int Nkv,

@@ -363,13 +363,22 @@ struct KParams {
     int B, Hq, Hkv, G, D, QT;
     int grp;       // causal: kv heads whose query tiles are interleaved (1, 2 or 4)
     float cscale;  // sm_scale * log2(e)
+    // key-range splits (SPLIT kernels): split s of a query tile walks key tiles
+    // [s * tps, (s + 1) * tps) and leaves its own output O_s / l_s in fp16 in part_o
+    // [B*Hq][Nq][splits][Dp] and its running max and row sum in fp32 in part_ml
+    // [B*Hq][Nq][splits][2] (Nq = qm.N)
+    int splits, tps;
+    _Float16* part_o;
+    float* part_ml;
 };
 
 // TG: the per-thread scales of sage_quant_qkv -- q_scale per token (indexed like the
 // rows of q_i8), k_scale per 32 keys ([slot][2]) -- so the dequantisation factor is
 // per lane: the lane's query, and its lane half's keys (FP8) or the tile's keys (FP16).
 // TL: the explicit two-level P.V accumulation (pv_tile).
-template <int DP, bool FP8, bool CAUSAL, bool OBF16, bool TG = false, bool TL = false>
+// SPLIT: one key range of a query tile (KParams::splits); the fp32 partial state goes to
+// the workspace and split_merge_kernel combines the splits.
+template <int DP, bool FP8, bool CAUSAL, bool OBF16, bool TG = false, bool TL = false, bool SPLIT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8>::OCC, Cfg<DP, FP8>::OCC))) void attn_fwd_kernel(KParams p) {
     using C = Cfg<DP, FP8>;
     // NST LDS stages: tile j lives in stage j % NST while tiles j+1 .. j+NST-1 stream in.
@@ -379,8 +388,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
     const int g = lane >> 5, i = lane & 31;
 
     // ---- workgroup -> (b, h, q tile)
-    int b, h, qt;
-    block_tile<CAUSAL>(p.B, p.Hkv, p.G, p.QT, p.grp, b, h, qt);
+    int b, h, qt, sidx = 0;
+    block_tile<CAUSAL>(p.B, p.Hkv, p.G, p.QT, p.grp, b, h, qt, SPLIT ? p.splits : 1, &sidx);
     const int hk = h / p.G;
     const SeqView qv = seq_view(p.qm, b, h), kv = seq_view(p.km, b, hk);
     const int Nq = qv.n, Nkv = kv.n, NBk = (Nkv + kBlk - 1) / kBlk;
@@ -400,6 +409,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
     if constexpr (CAUSAL) {
         const int kmax = min(qt * C::BM + C::BM, Nq) - 1 + off;  // last key the workgroup sees
         jend = kmax < 0 ? 0 : min(NBk, kmax / kBlk + 1);
+    }
+    // the key tiles this workgroup walks: [jbeg, jend) (all of them unless SPLIT)
+    int jbeg = 0;
+    if constexpr (SPLIT) {
+        jbeg = sidx * p.tps;
+        jend = min(jend, jbeg + p.tps);
+        jbeg = min(jbeg, jend);  // an empty range leaves m = -1e30, l = 0, O = 0
     }
     const bool ktail = (Nkv % kBlk) != 0;
 
@@ -435,7 +451,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
         const int seen = q0 + off + 1;  // keys visible to the wave's first query
         jm = min(jm, seen > 0 ? seen / kBlk : 0);
     }
-    jm = min(jm, jend);
+    jm = max(min(jm, jend), jbeg);
 
     // Tile j lives in stage j % NST; the next NST-1 tiles stream in meanwhile.  Every
     // wave runs every iteration (a fully masked causal tile leaves m, l and O
@@ -444,15 +460,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
     static_assert(AHEAD == 1 || AHEAD == 2, "two or three stages");
 #pragma unroll
     for (int t = 0; t < AHEAD; t++)
-        if (t < jend) issue_tile(t);
+        if (jbeg + t < jend) issue_tile(jbeg + t);
     // K scale(s) of the next tile, loaded one tile ahead (TG: the two 32-key halves)
     float ks_next = 0.0f, ks_next1 = 0.0f;
-    if (jend > 0) {
+    if (jend > jbeg) {
         if constexpr (TG) {
-            ks_next = scalar_load_f32(p.k_scale + 2 * kv.slot0);
-            ks_next1 = scalar_load_f32(p.k_scale + 2 * kv.slot0 + 1);
+            ks_next = scalar_load_f32(p.k_scale + 2 * (kv.slot0 + jbeg));
+            ks_next1 = scalar_load_f32(p.k_scale + 2 * (kv.slot0 + jbeg) + 1);
         } else {
-            ks_next = scalar_load_f32(ks_row);
+            ks_next = scalar_load_f32(ks_row + jbeg);
         }
     }
     auto step = [&](auto masked, int j) {
@@ -494,7 +510,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
         }
         pv_tile<C, FP8, TL>(st + C::KBYTES, pk, O, lane);
     };
-    int j = 0;
+    int j = jbeg;
     for (; j < jm; j++) step(std::false_type{}, j);
     for (; j < jend; j++) step(std::true_type{}, j);
     // Matrix instructions must run with every lane enabled: without these empty uses the
@@ -506,6 +522,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
     // ---- epilogue: O^T / l (x v_scale in FP8 mode) -> out dtype, input layout
     if (!active) return;
     const float ltot = halves_sum(l);
+    if constexpr (SPLIT) {
+        // this split's own output O / l in fp16 (all Dp channels; padding ones are 0; zeros
+        // for an empty range), its running max and row sum in fp32.  |O / l| is bounded by
+        // the largest |v^|, an fp16 value, so the fp16 store cannot overflow.
+        if (qidx >= Nq) return;
+        const int64_t row = ((int64_t(b) * p.Hq + h) * p.qm.N + qidx) * p.splits + sidx;
+        const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+        _Float16* po = p.part_o + row * DP;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; dt++)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; a4++) {
+                const int k0 = 4 * a4;
+                *(uint2*)(po + 32 * dt + 8 * a4 + 4 * g) =
+                    make_uint2(uint32_t(f32_to_f16_bits(O[dt][k0] * inv)) |
+                                   (uint32_t(f32_to_f16_bits(O[dt][k0 + 1] * inv)) << 16),
+                               uint32_t(f32_to_f16_bits(O[dt][k0 + 2] * inv)) |
+                                   (uint32_t(f32_to_f16_bits(O[dt][k0 + 3] * inv)) << 16));
+            }
+        if (g == 0) *(v2f*)(p.part_ml + row * 2) = v2f{m, ltot};
+        return;
+    }
     const bool empty = !(ltot > 0.0f);  // a query that sees no key: zeros
     const float inv = empty ? 0.0f : 1.0f / ltot;
     if (qidx >= Nq) return;
@@ -535,6 +573,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
                     if (d0 + e < p.D) orow[d0 + e] = hv[e];
             }
         }
+}
+
+// ---- combining key-range splits ----------------------------------------------------
+// One thread per (b, h, query, 4 channels): the splits' states (o_s = O_s / l_s, m_s, l_s)
+// combine as o = sum_s w_s o_s / sum_s w_s with w_s = 2^(m_s - M) l_s and M = max_s m_s
+// (fp32), times v_scale / 448 in FP8 mode, then the output dtype and layout of the
+// unsplit kernel.  A query with no visible key (every l_s = 0) gets zeros.
+template <int DP, bool FP8, bool OBF16>
+__global__ __launch_bounds__(256) void split_merge_kernel(KParams p) {
+    constexpr int G4 = DP / 4;
+    const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t r = t / G4;
+    const int d0 = int(t % G4) * 4;
+    const int NqM = p.qm.N;
+    if (r >= int64_t(p.B) * p.Hq * NqM || d0 >= p.D) return;
+    const int q = int(r % NqM), bh = int(r / NqM), b = bh / p.Hq, h = bh % p.Hq;
+    const SeqView qv = seq_view(p.qm, b, h);
+    if (q >= qv.n) return;
+    const float* ml = p.part_ml + r * p.splits * 2;
+    float M = -1e30f;
+    for (int s = 0; s < p.splits; s++) M = fmaxf(M, ml[2 * s]);
+    float L = 0.0f;
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < p.splits; s++) {
+        const float w = __builtin_amdgcn_exp2f(ml[2 * s] - M) * ml[2 * s + 1];  // 0 for an empty split
+        L += w;
+        const uint2 raw = *(const uint2*)(p.part_o + (r * p.splits + s) * DP + d0);
+        const uint32_t wd[2] = {raw.x, raw.y};
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+            acc[e] = __builtin_fmaf(w, f16_bits_to_f32(uint16_t(wd[e >> 1] >> (16 * (e & 1)))), acc[e]);
+    }
+    const bool empty = !(L > 0.0f);
+    const float inv = empty ? 0.0f : 1.0f / L;
+    const int hk = h / p.G;
+    const int64_t obase = p.qm.cu != nullptr ? qv.start * p.osq : b * p.osb;
+    uint16_t* orow = (uint16_t*)p.out + obase + h * p.osh + q * p.osq;
+    uint16_t hv[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        float o = acc[e] * inv;
+        if constexpr (FP8) o = empty ? 0.0f : o * p.v_scale[(int64_t(b) * p.Hkv + hk) * DP + d0 + e];
+        hv[e] = OBF16 ? f32_to_bf16_bits(o) : f32_to_f16_bits(o);
+    }
+    if ((p.D & 3) == 0) {
+        *(uint2*)(orow + d0) = make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16),
+                                          uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+            if (d0 + e < p.D) orow[d0 + e] = hv[e];
+    }
 }
 
 // ---- debug dump of INT32 score tiles through the same loader / operand path ----------
@@ -585,6 +675,27 @@ hipError_t launch_attn_t(const KParams& p, int nwg, hipStream_t s) {
     using C = Cfg<DP, FP8>;
     auto kern = attn_fwd_kernel<DP, FP8, CAUSAL, OBF16, TG, TL>;
     hipLaunchKernelGGL(kern, dim3(nwg), dim3(C::THREADS), 0, s, p);
+    return hipGetLastError();
+}
+
+// key-range splits (FP16 P.V, block granularity): the split kernel, then the merge
+template <int DP>
+hipError_t dispatch_split(const AttnArgs& a, const KParams& p, int nwg, hipStream_t s) {
+    using C = Cfg<DP, false>;
+    if (a.causal)
+        hipLaunchKernelGGL((attn_fwd_kernel<DP, false, true, false, false, false, true>), dim3(nwg), dim3(C::THREADS),
+                           0, s, p);
+    else
+        hipLaunchKernelGGL((attn_fwd_kernel<DP, false, false, false, false, false, true>), dim3(nwg),
+                           dim3(C::THREADS), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t threads = int64_t(p.B) * p.Hq * p.qm.N * (DP / 4);
+    const dim3 grid(unsigned((threads + 255) / 256));
+    if (a.out_bf16)
+        hipLaunchKernelGGL((split_merge_kernel<DP, false, true>), grid, dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((split_merge_kernel<DP, false, false>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
@@ -667,6 +778,26 @@ hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s) {
         p.osq = a.D;
     }
     const int nwg = a.B * a.Hq * p.QT;
+    p.splits = 1;
+    p.tps = 0;
+    p.part_o = nullptr;
+    p.part_ml = nullptr;
+    if (a.splits > 1) {
+        // balanced ranges: tps key tiles each, as few splits as cover every key tile
+        const int NBk = (a.Nkv + kBlk - 1) / kBlk;
+        p.tps = (NBk + a.splits - 1) / a.splits;
+        p.splits = (NBk + p.tps - 1) / p.tps;
+        const SplitWorkspace ws = attn_split_workspace(a.B, a.Hq, a.Nq, a.D, a.splits);
+        p.part_o = (_Float16*)a.workspace;
+        p.part_ml = (float*)((char*)a.workspace + ws.ml);
+        if (p.splits > 1) {
+            const int n = nwg * p.splits;
+            if (a.D <= 64) return dispatch_split<64>(a, p, n, s);
+            if (a.D <= 128) return dispatch_split<128>(a, p, n, s);
+            return dispatch_split<256>(a, p, n, s);
+        }
+        p.splits = 1;
+    }
     if (a.D <= 64) return a.fp8 ? dispatch_rest<64, true>(a, p, nwg, s) : dispatch_rest<64, false>(a, p, nwg, s);
     if (a.D <= 128) return a.fp8 ? dispatch_rest<128, true>(a, p, nwg, s) : dispatch_rest<128, false>(a, p, nwg, s);
     return a.fp8 ? dispatch_rest<256, true>(a, p, nwg, s) : dispatch_rest<256, false>(a, p, nwg, s);

@@ -220,9 +220,17 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
 // of grp kv heads run together in decreasing order of work (longest first), which
 // shortens each group's tail while its K/V still fit in L2 and MALL; grp = 1 is plain
 // head-by-head order.
+// splits > 1 (key-range splits of one query tile): the splits of a query tile are
+// consecutive logical ids, so they share the tile's Q rows and the head's K/V on one XCD;
+// s returns the split index.
 template <bool CAUSAL>
-__device__ __forceinline__ void block_tile(int B, int Hkv, int G, int QT, int grp, int& b, int& h, int& qt) {
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
+__device__ __forceinline__ void block_tile(int B, int Hkv, int G, int QT, int grp, int& b, int& h, int& qt,
+                                           int splits = 1, int* s = nullptr) {
+    int L = xcd_remap(blockIdx.x, gridDim.x);
+    if (splits > 1) {
+        *s = L % splits;
+        L /= splits;
+    }
     int bhk, hg;
     if constexpr (CAUSAL) {
         const int per = grp * G * QT, nkv = B * Hkv;

@@ -54,7 +54,20 @@ struct AttnArgs {
     const int32_t* cu_k;
     int total_q, total_k;
     int thread_gran;  // scales of sage_quant_qkv's per-thread granularity
+    int splits;       // > 1: key-range splits (FP16 P.V, block granularity) into workspace
+    void* workspace;  // splits > 1: part_o fp16 [B*Hq][Nq][splits][Dp], then part_ml fp32 [..][2]
 };
+
+// Workspace of the key-range split attention: fp16 per-split outputs [rows][Dp] at byte
+// 0, then fp32 (running max, row sum) pairs [rows][2] at byte ml; rows = B*Hq*Nq*splits.
+struct SplitWorkspace {
+    size_t ml, bytes;
+};
+inline SplitWorkspace attn_split_workspace(int B, int Hq, int Nq, int D, int splits) {
+    const size_t dp = D <= 64 ? 64 : (D <= 128 ? 128 : 256);
+    const size_t rows = size_t(B) * size_t(Hq) * size_t(Nq) * size_t(splits);
+    return SplitWorkspace{rows * dp * 2, rows * (dp * 2 + 2 * sizeof(float))};
+}
 
 // Microscaling FP4: codes and E8M0 exponent bytes of Q, smoothed K and V in the layouts
 // of include/sage.h; workspace = the fp64 K block channel sums.  Dense or packed batches

@@ -161,6 +161,42 @@ def test_quant_qkv_noalloc_limits():
         assert call(4, 32, 10880, 128) == qa.SAGE_ERR_DEVICE
 
 
+def test_attn_fwd_split_limits():
+    """Key-range splits: FP16 P.V only, a workspace of the stated size, 1..64 splits; the
+    library's choice splits only under-filled FP16 P.V launches."""
+    L = qa.lib()
+    ws = L.sage_attn_fwd_split_workspace_bytes(1, 8, 2048, 128, 6)
+    assert ws == 8 * 2048 * 6 * (128 * 2 + 8)
+    assert L.sage_attn_fwd_split_workspace_bytes(1, 8, 2048, 128, 1) == 0
+    assert L.sage_attn_fwd_split_workspace_bytes(1, 8, 2048, 300, 4) == 0
+    assert L.sage_attn_fwd_split_choice(1, 8, 2048, 2048, 128, 0, 0) > 1          # LLM prefill, FP16 P.V
+    assert L.sage_attn_fwd_split_choice(1, 8, 2048, 2048, 128, 0, 1) == 1         # FP8 P.V: never
+    assert L.sage_attn_fwd_split_choice(4, 32, 8192, 8192, 128, 0, 0) == 1        # fills the GPU
+    assert L.sage_attn_fwd_split_choice(1, 8, 2048, 256, 128, 0, 0) == 1          # too few key tiles
+    for B, H, N in ((1, 8, 2048), (1, 2, 256), (2, 3, 700)):
+        S = L.sage_attn_fwd_split_choice(B, H, N, N, 64, 1, 0)
+        if S > 1:  # balanced ranges of at least four tiles
+            tps = -(-qa.num_blocks(N) // S)
+            assert tps >= 4 and -(-qa.num_blocks(N) // tps) == S
+    ws = L.sage_attn_fwd_split_workspace_bytes(1, 8, 2048, 128, 4)
+
+    def call(**kw):
+        a = dict(pv=0, acc=0, splits=4, ws=FAKE, wsb=ws, D=128)
+        a.update(kw)
+        return L.sage_attn_fwd_split(*([FAKE] * 7), 0, 0, 1, 8, 8, 2048, 2048, a["D"], 0, 0.088, a["pv"], a["acc"],
+                                     a["splits"], a["ws"], a["wsb"], None)
+    assert call(pv=1) == qa.SAGE_ERR_UNSUPPORTED and "FP16" in _detail()
+    assert call(acc=qa.SAGE_ACC_FP16_FP32_SPLIT) == qa.SAGE_ERR_UNSUPPORTED
+    assert call(splits=0) == qa.SAGE_ERR_INVALID_ARG
+    assert call(splits=65) == qa.SAGE_ERR_INVALID_ARG
+    assert call(wsb=ws - 1) == qa.SAGE_ERR_WORKSPACE
+    assert call(ws=None) == qa.SAGE_ERR_WORKSPACE
+    assert call(ws=FAKE + 8) == qa.SAGE_ERR_WORKSPACE
+    if not torch.cuda.is_available():
+        assert call() == qa.SAGE_ERR_DEVICE
+        assert call(splits=1, ws=None) == qa.SAGE_ERR_DEVICE  # one split: plain sage_attn_fwd
+
+
 def test_attn_fwd_g_checks_granularity_first():
     L = qa.lib()
     args = [FAKE] * 7 + [0, 0, 1, 2, 2, 128, 128, 64, 0, 0.125, 1, 0]

@@ -30,7 +30,6 @@ sys.path.insert(0, ROOT)
 
 METRIC = "effective attention TOPS at D=128 vs N (1K–32K); % of INT8/FP8 MFMA peak"
 PEAK_TOPS = 5000.0        # MI355X dense INT8 / FP8 matrix-core peak (TOPS)
-OPS_PER_CLK = 256 * 8192  # dense INT8 / FP8 matrix-core operations per shader clock (256 CUs)
 PEAK_HBM_GBS = 8000.0
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "attn_fwd_traffic.json")
 
@@ -53,6 +52,9 @@ def parse():
     p.add_argument("--mxfp4", action="store_true", help="time the MXFP4 variant also with --no-sweep")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (HBM counter calibration)")
+    p.add_argument("--no-configs", action="store_true", help="skip the per-workload points")
+    p.add_argument("--cpu-full", action="store_true",
+                   help="CPU baselines of the per-workload points on every query row (minutes)")
     return p.parse_args()
 
 
@@ -129,6 +131,13 @@ class Runner:
         self.attn_min = min(attn)
         return total / steps, sum(attn) / steps, sum(quant) / steps, sorted(attn)[len(attn) // 2]
 
+    def graph_times(self, reps: int = 10, replays: int = 5):
+        """(attention ms, quantisation ms, step ms) per call, each from a HIP graph of
+        `reps` back-to-back calls replayed `replays` times: GPU time with no host gaps
+        between launches (short kernels otherwise wait on the Python wrappers)."""
+        return (graph_ms(self.torch, self.attn, reps, replays), graph_ms(self.torch, self.quant, reps, replays),
+                graph_ms(self.torch, self.step, reps, replays))
+
     def time_graph(self, steps: int, warmup: int) -> float:
         """ms per step with the step (same kernels, same buffers) captured once into a HIP
         graph and replayed: the launch rate no longer depends on the Python wrappers."""
@@ -154,6 +163,35 @@ class Runner:
         torch.cuda.synchronize()
         del graph
         return t0.elapsed_time(t1) / steps
+
+
+def graph_ms(torch, fn, reps: int = 10, replays: int = 5) -> float:
+    """ms per call of fn, from a captured HIP graph of `reps` calls (median of `replays`
+    timed replays after two warm-up replays)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(reps):
+            fn()
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(replays):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        graph.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        ts.append(t0.elapsed_time(t1) / reps)
+    del graph
+    return sorted(ts)[len(ts) // 2]
 
 
 def main():
@@ -221,7 +259,6 @@ def main():
     alg_ops = 4.0 * w.B * w.Hq * w.Nq * w.Nkv * Dp / (2 if w.causal else 1)
     achieved = alg_ops / (ms_attn * 1e-3) / 1e12
     traffic = None
-    sclk = None  # GHz of the attention launches, from the profiled GRBM cycle counters
     src_hash = kernel_source_hash()
     if os.path.exists(PROFILE_TRAFFIC):
         try:
@@ -230,7 +267,6 @@ def main():
             key = f"B{w.B}_H{w.Hq}_N{w.Nq}_D{w.D}_{'causal' if w.causal else 'noncausal'}"
             if pt.get("kernel_source_sha256_16") == src_hash and key in pt.get("workloads", {}):
                 traffic = pt["workloads"][key]
-                sclk = pt.get("sclk_ghz", {}).get(key)
         except (OSError, ValueError):
             traffic = None
     # quantisation kernels: HBM-bound; algorithmic bytes = one read of q, k, v (bf16)
@@ -263,16 +299,11 @@ def main():
         "attn_kernel_ms_min": round(r.attn_min, 4),
         "quant_ms": round(ms_quant, 4),
         "quant_GBps": round(quant_bytes / (ms_quant * 1e-3) / 1e9, 1),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TOPS, "unit": "TFLOP/s",
+        # dense INT8 (QK^T) + FP8 (P.V) matrix-core operations: tera-operations per second
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TOPS, "unit": "TOP/s",
                      "frac": round(achieved / PEAK_TOPS, 4), "traffic": traffic,
-                     "kernel": "attn_fwd_kernel<128, fp8, noncausal, two-level, bf16>",
-                     "alg_ops_per_launch": alg_ops, "kernel_source_sha256_16": src_hash,
-                     # the same fraction against 256 CUs x 8192 ops/clk at the shader clock the
-                     # attention launches ran at: GRBM cycles per XCD / launch duration, from the
-                     # profiled run of this kernel source (profiles/attn_fwd_traffic.json)
-                     "sclk_ghz_profiled": sclk,
-                     "frac_at_profiled_sclk": (round(achieved / (OPS_PER_CLK * sclk * 1e9 / 1e12), 4)
-                                               if sclk else None)},
+                     "kernel": "attn_fwd_kernel<128, fp8, noncausal, bf16 out>",
+                     "alg_ops_per_launch": alg_ops, "kernel_source_sha256_16": src_hash},
     }
     log(f"[bench] step {ms_step:.3f} ms  attn {ms_attn:.3f} ms ({attn_tops:.0f} TOPS, "
         f"{100 * achieved / PEAK_TOPS:.1f}% of peak)  quant {ms_quant:.3f} ms")
@@ -299,16 +330,16 @@ def main():
                 ws = base.with_(Nq=n, Nkv=n, causal=causal)
                 qs, ks, vs = inputs_for(n)
                 rs = Runner(qa, torch, qs, ks, vs, ws)
-                st, at, qt, _ = rs.time(args.sweep_steps, 3)
-                gt = rs.time_graph(args.sweep_steps, 3)
+                st, _, _, _ = rs.time(args.sweep_steps, 3)  # eager steps (host wrappers between launches)
+                at, qt, gt = rs.graph_times()
                 o = ws.ops()
-                sweep.append({"N": n, "causal": causal, "step_tops": round(o / (st * 1e-3) / 1e12, 1),
-                              "graph_step_tops": round(o / (gt * 1e-3) / 1e12, 1),
+                sweep.append({"N": n, "causal": causal, "step_tops": round(o / (gt * 1e-3) / 1e12, 1),
+                              "eager_step_tops": round(o / (st * 1e-3) / 1e12, 1),
                               "attn_tops": round(o / (at * 1e-3) / 1e12, 1),
                               "attn_frac_of_peak": round(o / (at * 1e-3) / 1e12 / PEAK_TOPS, 4),
-                              "attn_ms": round(at, 4), "quant_ms": round(qt, 4)})
+                              "attn_ms": round(at, 4), "quant_ms": round(qt, 4), "step_ms": round(gt, 4)})
                 log(f"[bench] sweep N={n} causal={causal}: attn {at:.3f} ms = {sweep[-1]['attn_tops']} TOPS, "
-                    f"step {sweep[-1]['step_tops']} TOPS")
+                    f"step {sweep[-1]['step_tops']} TOPS (graph), eager step {sweep[-1]['eager_step_tops']}")
                 del rs, qs, ks, vs
                 torch.cuda.empty_cache()
         result["sweep"] = sweep
@@ -324,6 +355,12 @@ def main():
     # ---------------------------------------------------------------- CPU baseline (the oracle, untuned)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, full, np, torch)
+    del full, q, k, v
+    torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- every workload family
+    if not args.no_configs:
+        result["configs"] = config_points(qa, torch, np, si, dev, args)
 
     print(json.dumps(result), flush=True)
 
@@ -454,6 +491,114 @@ def cpu_baseline(w, full, np, torch):
                       f"query rows ({t_rows:.2f}s), extrapolated linearly in rows to one whole step "
                       f"({t_full:.1f}s)",
             "seconds_measured": round(t_quant + t_rows, 2), "cpu_model": cpu_model()}
+
+
+# The other workloads the benchmark sweep stands beside (seeded host inputs, the same
+# bytes the parity tests use).  Ceiling in effective TOPS: with FP16 P.V the P.V half
+# runs at the FP16 matrix rate (half the INT8/FP8 rate), so at most 2/3 of the 5.0 POPS
+# peak; a padded head dim (96 -> 128) spends uncounted work on the padding.
+CONFIGS = [
+    ("tiny B1 H2 N256 D64 fp16 HND non-causal FP16-PV", "tiny", {}, 2 / 3),
+    ("llm_prefill B1 H8 N2048 D128 fp16 HND non-causal FP16-PV", "llm_prefill", {}, 2 / 3),
+    ("llm_prefill B1 H8 N2048 D128 fp16 HND causal FP16-PV", "llm_prefill", {"causal": True}, 2 / 3),
+    ("video_dit B1 H24 N17776 D64 bf16 NHD non-causal FP8-PV (K channel offset)", "video_dit", {}, 1.0),
+    ("gqa B2 H32/8 N8192 D128 bf16 NHD causal FP16-PV", "gqa", {}, 2 / 3),
+    ("gqa B2 H32/8 N8192 D96 (padded to 128) bf16 NHD causal FP16-PV", "gqa", {"D": 96}, 0.5),
+]
+
+
+def config_points(qa, torch, np, si, dev, args):
+    """Per workload: attention (with the library's key-range split choice, as sageattn
+    does), quantisation and the whole step timed from HIP graphs of back-to-back calls,
+    effective TOPS,
+    fraction of the 5.0 POPS peak and of the P.V mode's ceiling, quantisation GB/s, and
+    the CPU oracle on the machine's host (every row for the small workloads, a bounded
+    sample extrapolated in rows for the large ones)."""
+    import oracle
+    out = []
+    for label, fam, kw, ceil in CONFIGS:
+        w = si.workload(fam, **kw)
+        q, k, v = si.make_qkv(w)
+        dq, dk, dv = (t.to(dev) for t in (q, k, v))
+        L = qa.lib()
+        ws = torch.empty(max(8, L.sage_quant_qkv_workspace_bytes(w.B, w.Hkv, w.Nkv, w.D, 1 if w.pv == "fp8" else 0)),
+                         dtype=torch.uint8, device=dev)
+        qk, vq = qa.quant_qkv(dq, dk, dv, w.layout, w.pv, workspace=ws)
+        splits = qa.split_choice(qk, w.pv, w.causal)
+        aws = torch.empty(max(16, qa.split_workspace_bytes(qk, splits)), dtype=torch.uint8, device=dev)
+        o = qa.attn_fwd(qk, vq, w.torch_dtype, w.layout, w.causal, None, w.accum, splits=splits, workspace=aws)
+
+        def quant():
+            qa.quant_qkv(dq, dk, dv, w.layout, w.pv, workspace=ws, out_qk=qk, out_v=vq)
+
+        def attn():
+            qa.attn_fwd(qk, vq, w.torch_dtype, w.layout, w.causal, None, w.accum, out=o, splits=splits, workspace=aws)
+
+        def step():
+            quant()
+            attn()
+
+        t_end = time.perf_counter() + 0.2
+        while time.perf_counter() < t_end:
+            step()
+            torch.cuda.synchronize()
+        # GPU time per call from HIP graphs of back-to-back calls (these launches are short
+        # enough that host wrappers between eager launches would show in the timings)
+        at = graph_ms(torch, attn)
+        qt = graph_ms(torch, quant)
+        stp = graph_ms(torch, step)
+        ops = w.ops()
+        Dp = qa.padded_dim(w.D)
+        elems_q, elems_kv = w.B * w.Hq * w.Nq * w.D, w.B * w.Hkv * w.Nkv * w.D
+        qbytes = (elems_q + 2 * elems_kv) * 2 + elems_q + elems_kv + elems_kv * (1 if w.pv == "fp8" else 2) + 4 * (
+            w.B * w.Hq * math.ceil(w.Nq / 64) + w.B * w.Hkv * math.ceil(w.Nkv / 64) + w.B * w.Hkv * (Dp + w.D))
+        tops = ops / (at * 1e-3) / 1e12
+        pt = {"workload": label, "attn_ms_median": round(at, 4), "attn_tops": round(tops, 1),
+              "attn_frac_of_peak": round(tops / PEAK_TOPS, 4), "mode_ceiling_frac": round(ceil, 4),
+              "attn_frac_of_mode_ceiling": round(tops / (PEAK_TOPS * ceil), 4),
+              "key_range_splits": splits, "quant_ms_median": round(qt, 4),
+              "quant_GBps": round(qbytes / (qt * 1e-3) / 1e9, 1),
+              "step_ms": round(stp, 4), "step_tops": round(ops / (stp * 1e-3) / 1e12, 1)}
+        log(f"[bench] {label}: attn {at * 1e3:.1f} us = {tops:.1f} TOPS ({100 * tops / PEAK_TOPS:.1f}% of peak, "
+            f"{100 * pt['attn_frac_of_mode_ceiling']:.1f}% of the mode ceiling), splits {splits}, "
+            f"quant {qt * 1e3:.1f} us = {pt['quant_GBps']} GB/s")
+        del dq, dk, dv, qk, vq, o, ws, aws
+        torch.cuda.empty_cache()
+        if not args.no_cpu:
+            pt["cpu_baseline"] = config_cpu_baseline(oracle, np, w, q, k, v, full=args.cpu_full)
+        out.append(pt)
+    return out
+
+
+def config_cpu_baseline(oracle, np, w, q, k, v, full: bool):
+    """The emulation-mode oracle on the host: full quantisation, then attention on every
+    query row when that is at most ~2e10 multiply-adds (or --cpu-full), else on a seeded
+    sample sized to ~3 s and extrapolated linearly in rows."""
+    t = time.perf_counter()
+    qf, kf, vf = (oracle.to_hnd_f32(x, w.layout) for x in (q, k, v))
+    Q = oracle.quantize(qf, kf, vf, w.pv == "fp8")
+    t_quant = time.perf_counter() - t
+    sm = float(np.float32(1 / math.sqrt(w.D)))
+    total_rows = w.B * w.Hq * w.Nq
+    macs = 2.0 * total_rows * w.Nkv * w.D / (2 if w.causal else 1)
+    if full or macs <= 2e10:
+        rows = oracle.all_rows(w.B, w.Hq, w.Nq)
+        kind = "every query row"
+    else:
+        probe = oracle.sample_rows(w.B, w.Hq, w.Nq, per_head=2, seed=7)
+        t = time.perf_counter()
+        oracle.attn_emulate(Q, w.causal, sm, probe)
+        per_row = (time.perf_counter() - t) / len(probe)
+        per_head = int(max(4, min(w.Nq, 3.0 / max(per_row, 1e-9) / (w.B * w.Hq))))
+        rows = oracle.sample_rows(w.B, w.Hq, w.Nq, per_head=per_head, seed=8)
+        kind = "sampled rows, extrapolated"
+    t = time.perf_counter()
+    oracle.attn_emulate(Q, w.causal, sm, rows)
+    t_rows = time.perf_counter() - t
+    t_full = t_quant + t_rows * total_rows / len(rows)
+    return {"value": round(w.ops() / t_full / 1e12, 6), "unit": "TOPS", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{kind}: quantisation {t_quant:.2f}s + {len(rows)} of {total_rows} rows {t_rows:.2f}s "
+                      f"-> one whole pass {t_full:.1f}s", "cpu_model": cpu_model()}
 
 
 def cpu_model() -> str:

@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (HBM counter calibration)")
     p.add_argument("--no-configs", action="store_true", help="skip the per-workload points")
+    p.add_argument("--configs-only", action="store_true",
+                   help="only the per-workload points (one JSON line with them; for profiling)")
     p.add_argument("--cpu-full", action="store_true",
                    help="CPU baselines of the per-workload points on every query row (minutes)")
     return p.parse_args()
@@ -214,6 +216,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     qa.lib()
+    if args.configs_only:
+        print(json.dumps({"configs": config_points(qa, torch, np, si, dev, args)}), flush=True)
+        return
 
     nmax = max([args.n] + ([] if args.no_sweep else list(si.SWEEP_N)))
     base = si.workload("seq_sweep", Nq=nmax, Nkv=nmax)

@@ -576,53 +576,74 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
 }
 
 // ---- combining key-range splits ----------------------------------------------------
-// One thread per (b, h, query, 4 channels): the splits' states (o_s = O_s / l_s, m_s, l_s)
+// One thread per (b, h, query, 8 channels): the splits' states (o_s = O_s / l_s, m_s, l_s)
 // combine as o = sum_s w_s o_s / sum_s w_s with w_s = 2^(m_s - M) l_s and M = max_s m_s
 // (fp32), times v_scale / 448 in FP8 mode, then the output dtype and layout of the
-// unsplit kernel.  A query with no visible key (every l_s = 0) gets zeros.
+// unsplit kernel.  The splits are taken four at a time, all loads of a group issued
+// before any use; a later group with a larger maximum rescales what the earlier ones
+// summed (with at most four splits, one group: M is the maximum over all of them).  A
+// query with no visible key (every l_s = 0) gets zeros.
 template <int DP, bool FP8, bool OBF16>
 __global__ __launch_bounds__(256) void split_merge_kernel(KParams p) {
-    constexpr int G4 = DP / 4;
+    constexpr int G8 = DP / 8;
     const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    const int64_t r = t / G4;
-    const int d0 = int(t % G4) * 4;
+    const int64_t r = t / G8;
+    const int d0 = int(t % G8) * 8;
     const int NqM = p.qm.N;
     if (r >= int64_t(p.B) * p.Hq * NqM || d0 >= p.D) return;
     const int q = int(r % NqM), bh = int(r / NqM), b = bh / p.Hq, h = bh % p.Hq;
     const SeqView qv = seq_view(p.qm, b, h);
     if (q >= qv.n) return;
     const float* ml = p.part_ml + r * p.splits * 2;
-    float M = -1e30f;
-    for (int s = 0; s < p.splits; s++) M = fmaxf(M, ml[2 * s]);
-    float L = 0.0f;
-    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int s = 0; s < p.splits; s++) {
-        const float w = __builtin_amdgcn_exp2f(ml[2 * s] - M) * ml[2 * s + 1];  // 0 for an empty split
-        L += w;
-        const uint2 raw = *(const uint2*)(p.part_o + (r * p.splits + s) * DP + d0);
-        const uint32_t wd[2] = {raw.x, raw.y};
+    const _Float16* po = p.part_o + r * p.splits * DP + d0;
+    float M = -1e30f, L = 0.0f;
+    float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s0 = 0; s0 < p.splits; s0 += 4) {
+        v2f st[4];
+        uint4 ov[4];
 #pragma unroll
-        for (int e = 0; e < 4; e++)
-            acc[e] = __builtin_fmaf(w, f16_bits_to_f32(uint16_t(wd[e >> 1] >> (16 * (e & 1)))), acc[e]);
+        for (int u = 0; u < 4; u++) {
+            const bool in = s0 + u < p.splits;
+            st[u] = in ? *(const v2f*)(ml + 2 * (s0 + u)) : v2f{-1e30f, 0.0f};
+            ov[u] = in ? *(const uint4*)(po + (s0 + u) * DP) : make_uint4(0, 0, 0, 0);
+        }
+        const float Mn = fmaxf(fmaxf(fmaxf(M, st[0].x), fmaxf(st[1].x, st[2].x)), st[3].x);
+        const float sc = __builtin_amdgcn_exp2f(M - Mn);  // 0 on the first group
+        L *= sc;
+#pragma unroll
+        for (int e = 0; e < 8; e++) acc[e] *= sc;
+        M = Mn;
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const float w = __builtin_amdgcn_exp2f(st[u].x - M) * st[u].y;  // 0 for an empty or absent split
+            L += w;
+            const uint32_t wd[4] = {ov[u].x, ov[u].y, ov[u].z, ov[u].w};
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                acc[e] = __builtin_fmaf(w, f16_bits_to_f32(uint16_t(wd[e >> 1] >> (16 * (e & 1)))), acc[e]);
+        }
     }
     const bool empty = !(L > 0.0f);
     const float inv = empty ? 0.0f : 1.0f / L;
     const int hk = h / p.G;
     const int64_t obase = p.qm.cu != nullptr ? qv.start * p.osq : b * p.osb;
     uint16_t* orow = (uint16_t*)p.out + obase + h * p.osh + q * p.osq;
-    uint16_t hv[4];
+    uint16_t hv[8];
 #pragma unroll
-    for (int e = 0; e < 4; e++) {
+    for (int e = 0; e < 8; e++) {
         float o = acc[e] * inv;
         if constexpr (FP8) o = empty ? 0.0f : o * p.v_scale[(int64_t(b) * p.Hkv + hk) * DP + d0 + e];
         hv[e] = OBF16 ? f32_to_bf16_bits(o) : f32_to_f16_bits(o);
     }
-    if ((p.D & 3) == 0) {
-        *(uint2*)(orow + d0) = make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16),
-                                          uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
+    auto pack = [&](int e) { return uint32_t(hv[e]) | (uint32_t(hv[e + 1]) << 16); };
+    if ((p.D & 7) == 0) {
+        *(uint4*)(orow + d0) = make_uint4(pack(0), pack(2), pack(4), pack(6));
+    } else if ((p.D & 3) == 0) {
+        *(uint2*)(orow + d0) = make_uint2(pack(0), pack(2));
+        if (d0 + 4 < p.D) *(uint2*)(orow + d0 + 4) = make_uint2(pack(4), pack(6));
     } else {
 #pragma unroll
-        for (int e = 0; e < 4; e++)
+        for (int e = 0; e < 8; e++)
             if (d0 + e < p.D) orow[d0 + e] = hv[e];
     }
 }
@@ -690,7 +711,7 @@ hipError_t dispatch_split(const AttnArgs& a, const KParams& p, int nwg, hipStrea
                            dim3(C::THREADS), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t threads = int64_t(p.B) * p.Hq * p.qm.N * (DP / 4);
+    const int64_t threads = int64_t(p.B) * p.Hq * p.qm.N * (DP / 8);
     const dim3 grid(unsigned((threads + 255) / 256));
     if (a.out_bf16)
         hipLaunchKernelGGL((split_merge_kernel<DP, false, true>), grid, dim3(256), 0, s, p);

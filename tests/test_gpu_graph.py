@@ -30,7 +30,7 @@ def _step_fn(kind, q, k, v, causal):
             qa.quant_mxfp4(q, k, v, workspace=ws, out=mq)
             qa.attn_fwd_mxfp4(mq, torch.bfloat16, "HND", causal, out=out)
         return step, out
-    pv = "fp16" if kind == "int8_fp16" else "fp8"
+    pv = "fp16" if kind in ("int8_fp16", "int8_fp16_split") else "fp8"
     if kind == "int8_separate":  # sage_quant_qk + sage_quant_v (its FP8 path clears a buffer with a kernel)
         wk = torch.empty(max(8, L.sage_quant_qk_workspace_bytes(B, HKV, N, D)), dtype=torch.uint8, device=dev)
         wv = torch.empty(max(8, L.sage_quant_v_workspace_bytes(B, HKV, D, 1)), dtype=torch.uint8, device=dev)
@@ -47,16 +47,20 @@ def _step_fn(kind, q, k, v, causal):
 
         def quant():
             qa.quant_qkv(q, k, v, "HND", pv, workspace=ws, out_qk=qk, out_v=vq)
-    out = qa.attn_fwd(qk, vq, torch.bfloat16, "HND", causal)
+    # key-range splits (split kernel, then the merge): one workspace for every call
+    splits = 3 if kind == "int8_fp16_split" else 1
+    aws = torch.empty(max(16, qa.split_workspace_bytes(qk, splits)), dtype=torch.uint8, device=dev) \
+        if splits > 1 else None
+    out = qa.attn_fwd(qk, vq, torch.bfloat16, "HND", causal, splits=splits, workspace=aws)
 
     def step():
         quant()
-        qa.attn_fwd(qk, vq, torch.bfloat16, "HND", causal, out=out)
+        qa.attn_fwd(qk, vq, torch.bfloat16, "HND", causal, out=out, splits=splits, workspace=aws)
     return step, out
 
 
 @pytest.mark.parametrize("kind,causal", [("int8_fp8", False), ("int8_fp16", True), ("int8_separate", True),
-                                         ("mxfp4", True)])
+                                         ("mxfp4", True), ("int8_fp16_split", False), ("int8_fp16_split", True)])
 def test_graph_replays_equal_eager_steps(kind, causal):
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev)

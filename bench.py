@@ -264,16 +264,18 @@ def main():
     alg_ops = 4.0 * w.B * w.Hq * w.Nq * w.Nkv * Dp / (2 if w.causal else 1)
     achieved = alg_ops / (ms_attn * 1e-3) / 1e12
     traffic = None
+    cycles = None
     src_hash = kernel_source_hash()
     if os.path.exists(PROFILE_TRAFFIC):
         try:
             with open(PROFILE_TRAFFIC) as fh:
                 pt = json.load(fh)
             key = f"B{w.B}_H{w.Hq}_N{w.Nq}_D{w.D}_{'causal' if w.causal else 'noncausal'}"
-            if pt.get("kernel_source_sha256_16") == src_hash and key in pt.get("workloads", {}):
-                traffic = pt["workloads"][key]
+            if pt.get("kernel_source_sha256_16") == src_hash:
+                traffic = pt.get("workloads", {}).get(key)
+                cycles = pt.get("shader_cycles_per_launch", {}).get(key)
         except (OSError, ValueError):
-            traffic = None
+            traffic = cycles = None
     # quantisation kernels: HBM-bound; algorithmic bytes = one read of q, k, v (bf16)
     # + one write of the int8 / fp8 codes and the scales
     elems = w.B * w.Hq * w.Nq * w.D
@@ -310,6 +312,14 @@ def main():
                      "kernel": "attn_fwd_kernel<128, fp8, noncausal, bf16 out>",
                      "alg_ops_per_launch": alg_ops, "kernel_source_sha256_16": src_hash},
     }
+    if cycles:
+        # the same fraction against 256 CUs x 8192 ops per clock at the clock the launch ran
+        # at: the launch's shader cycles come from the counters (GRBM_GUI_ACTIVE / 8 XCDs,
+        # hash-checked like traffic) and are a property of the compute-bound kernel, so the
+        # time cancels; the clock this box's launches ran at is then cycles / time
+        result["roofline"]["frac_per_clock"] = round(alg_ops / (cycles * 256 * 8192), 4)
+        result["roofline"]["shader_cycles_per_launch"] = cycles
+        result["roofline"]["implied_sclk_ghz"] = round(cycles / (ms_attn * 1e-3) / 1e9, 3)
     log(f"[bench] step {ms_step:.3f} ms  attn {ms_attn:.3f} ms ({attn_tops:.0f} TOPS, "
         f"{100 * achieved / PEAK_TOPS:.1f}% of peak)  quant {ms_quant:.3f} ms")
     del r

@@ -8,11 +8,13 @@ Metric (the kernel-throughput sweep of the SageAttention pages): effective TOPS 
 attention-kernel-only rate (the pages' convention, quantisation excluded) is reported
 beside it, with a roofline against the dense INT8/FP8 matrix-core peak.
 
-Workload: B=4, H=32, D=128, bf16 q/k/v ~ N(0,1), HND, INT8 QK^T + FP8-e4m3 P.V with
-two-level accumulation, non-causal, N=8192 (the sweep covers N = 1K..32K, causal
-and non-causal).  Prints ONE JSON line on stdout.
+Workload: B=4, H=32, D=128, bf16 q/k/v ~ N(0,1), HND, INT8 QK^T + FP8-e4m3 P.V with the
+"fp16+fp32" accumulation name (on gfx950 the P.V products chain through the fp32
+accumulator), non-causal, N=8192 (the sweep covers N = 1K..32K, causal and
+non-causal).  Every other workload (tiny, LLM prefill, video DiT, GQA at D128 / D96) is
+timed after it, each with its own CPU-oracle baseline.  Prints ONE JSON line on stdout.
 
-    python bench.py [--steps K] [--warmup W] [--n 8192] [--no-sweep] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--n 8192] [--no-sweep] [--no-cpu] [--no-configs]
 """
 from __future__ import annotations
 

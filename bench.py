@@ -142,6 +142,27 @@ class Runner:
         return (graph_ms(self.torch, self.attn, reps, replays), graph_ms(self.torch, self.quant, reps, replays),
                 graph_ms(self.torch, self.step, reps, replays))
 
+    def fused_q_graph_times(self, reps: int = 10, replays: int = 5):
+        """(attention ms, quantisation ms, step ms) of the schedule with Q quantised in the
+        attention prologue: sage_quant_kv, then sage_attn_fwd_fused_q (the same codes and
+        the same output as the step above), each from a HIP graph as graph_times."""
+        qa, w = self.qa, self.w
+        if not hasattr(self, "kq"):
+            self.kq, self.vq2 = qa.quant_kv(self.k, self.v, w.layout, w.pv, workspace=self.ws)
+            self.out2 = qa.attn_fwd_fused_q(self.q, self.kq, self.vq2, w.layout, w.causal, None, w.accum)
+
+        def quant():
+            qa.quant_kv(self.k, self.v, w.layout, w.pv, workspace=self.ws, out_k=self.kq, out_v=self.vq2)
+
+        def attn():
+            qa.attn_fwd_fused_q(self.q, self.kq, self.vq2, w.layout, w.causal, None, w.accum, out=self.out2)
+
+        def step():
+            quant()
+            attn()
+        return (graph_ms(self.torch, attn, reps, replays), graph_ms(self.torch, quant, reps, replays),
+                graph_ms(self.torch, step, reps, replays))
+
     def time_graph(self, steps: int, warmup: int) -> float:
         """ms per step with the step (same kernels, same buffers) captured once into a HIP
         graph and replayed: the launch rate no longer depends on the Python wrappers."""
@@ -349,14 +370,19 @@ def main():
                 rs = Runner(qa, torch, qs, ks, vs, ws)
                 st, _, _, _ = rs.time(args.sweep_steps, 3)  # eager steps (host wrappers between launches)
                 at, qt, gt = rs.graph_times()
+                fa, fq, fs = rs.fused_q_graph_times()
                 o = ws.ops()
                 sweep.append({"N": n, "causal": causal, "step_tops": round(o / (gt * 1e-3) / 1e12, 1),
                               "eager_step_tops": round(o / (st * 1e-3) / 1e12, 1),
                               "attn_tops": round(o / (at * 1e-3) / 1e12, 1),
                               "attn_frac_of_peak": round(o / (at * 1e-3) / 1e12 / PEAK_TOPS, 4),
-                              "attn_ms": round(at, 4), "quant_ms": round(qt, 4), "step_ms": round(gt, 4)})
+                              "attn_ms": round(at, 4), "quant_ms": round(qt, 4), "step_ms": round(gt, 4),
+                              # Q quantised in the attention prologue (sage_quant_kv + sage_attn_fwd_fused_q)
+                              "fused_q": {"step_tops": round(o / (fs * 1e-3) / 1e12, 1), "step_ms": round(fs, 4),
+                                          "attn_ms": round(fa, 4), "quant_ms": round(fq, 4)}})
                 log(f"[bench] sweep N={n} causal={causal}: attn {at:.3f} ms = {sweep[-1]['attn_tops']} TOPS, "
-                    f"step {sweep[-1]['step_tops']} TOPS (graph), eager step {sweep[-1]['eager_step_tops']}")
+                    f"step {sweep[-1]['step_tops']} TOPS (graph), eager step {sweep[-1]['eager_step_tops']}; "
+                    f"fused-Q step {sweep[-1]['fused_q']['step_tops']} TOPS (quant {fq:.3f} ms, attn {fa:.3f} ms)")
                 del rs, qs, ks, vs
                 torch.cuda.empty_cache()
         result["sweep"] = sweep

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SAGE_ABI_VERSION 5
+#define SAGE_ABI_VERSION 6
 
 typedef enum sage_status {
     SAGE_OK = 0,
@@ -200,6 +200,18 @@ sage_status sage_quant_qkv_noalloc(const void* q, const void* k, const void* v, 
                                    void* v_hat, float* v_scale, void* stream);
 
 /*
+ * The K and V part of sage_quant_qkv alone (K mean, INT8 codes and block scales of the
+ * smoothed K, V^ and v_scale; SageAttention README, "Current Features"), for use with
+ * sage_attn_fwd_fused_q, which quantises Q itself.  Block granularity, dense batches.
+ *   Arguments, layouts, workspace (sage_quant_qkv_workspace_bytes(B, H_kv, Nkv, D, pv)
+ *   bytes, 8-byte aligned, contents ignored) and errors as sage_quant_qkv, without the
+ *   Q tensors; results bit-identical to that call's K and V outputs.
+ */
+sage_status sage_quant_kv(const void* k, const void* v, sage_dtype dtype, sage_layout layout, int B, int H_kv, int Nkv,
+                          int D, sage_pv pv, int8_t* k_i8, float* k_scale, float* k_mean, void* v_hat, float* v_scale,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Attention on the quantised operands (step 3-4 above).
  *   Reads q_i8/q_scale/k_i8/k_scale/v_hat/v_scale as produced by the two calls
  *   above (v_scale only in FP8 mode, may be NULL otherwise).
@@ -255,6 +267,25 @@ sage_status sage_attn_fwd_split(const int8_t* q_i8, const float* q_scale, const 
                                 sage_layout out_layout, int B, int H_qo, int H_kv, int Nq, int Nkv, int D,
                                 int is_causal, float sm_scale, sage_pv pv, sage_accum accum, int num_splits,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Attention with the Q quantisation done in the attention kernel itself: the same
+ * scheme as sage_quant_qkv + sage_attn_fwd (block granularity; SageAttention README,
+ * "Current Features"), but each workgroup reads its 128 queries in fp16 / bf16 and
+ * quantises them per 64-token block in its prologue (the block quantiser's arithmetic,
+ * so the codes and scales are bit-identical to sage_quant_qkv's), so the INT8 Q codes
+ * never go through HBM.  The output is bit-identical to sage_attn_fwd's on those codes.
+ *   q: fp16 / bf16 (dtype), layout HND or NHD, dense, 16-byte aligned; the output takes
+ *   q's dtype and layout.  k_i8 / k_scale / v_hat / v_scale as from sage_quant_kv (or
+ *   sage_quant_qkv).  q_i8_out [B][H_qo][N_pad][Dp] (16-byte aligned) and q_scale_out
+ *   [B][H_qo][NB], both optional (null: not written), receive the codes and scales the
+ *   kernel formed.  accum SAGE_ACC_FP16_FP32_SPLIT: SAGE_ERR_UNSUPPORTED; other errors as
+ *   sage_attn_fwd.
+ */
+sage_status sage_attn_fwd_fused_q(const void* q, sage_dtype dtype, sage_layout layout, const int8_t* k_i8,
+                                  const float* k_scale, const void* v_hat, const float* v_scale, void* out, int B,
+                                  int H_qo, int H_kv, int Nq, int Nkv, int D, int is_causal, float sm_scale, sage_pv pv,
+                                  sage_accum accum, int8_t* q_i8_out, float* q_scale_out, void* stream);
 
 /*
  * Debug dump of INT32 score tiles through the attention kernel's own operand

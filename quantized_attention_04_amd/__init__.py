@@ -105,6 +105,11 @@ _EXPORTS = {
     "sage_quant_qkv_noalloc_max_bytes": (ctypes.c_size_t, []),
     "sage_quant_qkv_noalloc": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 10
                                + [ctypes.c_void_p] * 8),
+    "sage_quant_kv": (ctypes.c_int, [ctypes.c_void_p] * 2 + [ctypes.c_int] * 7 + [ctypes.c_void_p] * 6
+                      + [ctypes.c_size_t, ctypes.c_void_p]),
+    "sage_attn_fwd_fused_q": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 5
+                              + [ctypes.c_int] * 7 + [ctypes.c_float, ctypes.c_int, ctypes.c_int]
+                              + [ctypes.c_void_p] * 3),
     "sage_attn_fwd_varlen_g": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] + [ctypes.c_void_p] * 2
                                + [ctypes.c_int] * 9 + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                        ctypes.c_void_p]),
@@ -136,7 +141,7 @@ def lib() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.restype = res
         fn.argtypes = args
-    if L.sage_abi_version() != 5:
+    if L.sage_abi_version() != 6:
         raise ImportError("libsage ABI version mismatch")
     _lib = L
     return L
@@ -468,7 +473,19 @@ def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: s
              qk_gran: str = "block") -> torch.Tensor:
     """softmax(sm_scale * q k^T [causal]) v with INT8 QK^T and FP8/FP16 PV; returns q's dtype and layout.
     qk_gran: "block" (one scale per 64 tokens) or "thread" (per query token, per 32 keys).
-    Launches too small to fill the GPU take the library's key-range splits (FP16 P.V)."""
+    Launches too small to fill the GPU take the library's key-range splits (FP16 P.V);
+    otherwise, at block granularity, Q is quantised inside the attention kernel
+    (sage_quant_kv + sage_attn_fwd_fused_q: the same codes and output, no Q codes in HBM)."""
+    if pv not in _PV:
+        raise ValueError(f"pv must be 'fp16' or 'fp8', got {pv!r}")
+    B, Hq, Nq, D = _dims(q, tensor_layout)
+    _, _, Nkv, _ = _dims(k, tensor_layout)
+    if qk_gran == "block" and accum != "fp16+fp32-split" and \
+            lib().sage_attn_fwd_split_choice(B, Hq, Nq, Nkv, D, int(bool(is_causal)), _PV[pv]) == 1:
+        kq, vq = quant_kv(k, v, tensor_layout, pv)
+        if q.dtype != k.dtype or q.device != k.device:
+            raise ValueError("q, k and v must share dtype and device")
+        return attn_fwd_fused_q(q, kq, vq, tensor_layout, is_causal, sm_scale, accum)
     qk, vq = quant_qkv(q, k, v, tensor_layout, pv, gran=qk_gran)
     return attn_fwd(qk, vq, q.dtype, tensor_layout, is_causal, sm_scale, accum, splits="auto")
 
@@ -586,6 +603,76 @@ def quant_v_varlen(v: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_k: in
     _check(L.sage_quant_v_varlen(v.data_ptr(), _DT[v.dtype], ck.data_ptr(), B, Hkv, total_k, int(max_seqlen_k), D,
                                  _PV[pv], out.v_hat.data_ptr(), _ptr(out.v_scale), _ptr(workspace),
                                  0 if workspace is None else workspace.numel(), _stream(dev)))
+    return out
+
+
+@dataclasses.dataclass
+class KQuant:
+    k_i8: torch.Tensor      # int8 [B, Hkv, N_pad(Nkv), Dp]
+    k_scale: torch.Tensor   # f32  [B, Hkv, NB(Nkv)]
+    k_mean: torch.Tensor    # f32  [B, Hkv, D]
+    B: int
+    Hkv: int
+    Nkv: int
+    D: int
+
+
+def quant_kv(k: torch.Tensor, v: torch.Tensor, layout: str = "HND", pv: str = "fp8",
+             workspace: Optional[torch.Tensor] = None, out_k: Optional[KQuant] = None,
+             out_v: Optional[VQuant] = None):
+    """sage_quant_kv: the K and V part of quant_qkv (for attn_fwd_fused_q, which
+    quantises Q itself); block granularity."""
+    for name, x in (("k", k), ("v", v)):
+        _check_input(x, name)
+    if k.dtype != v.dtype or k.device != v.device:
+        raise ValueError("k and v must share dtype and device")
+    if pv not in _PV:
+        raise ValueError(f"pv must be 'fp16' or 'fp8', got {pv!r}")
+    B, Hkv, Nkv, D = _dims(k, layout)
+    if _dims(v, layout) != (B, Hkv, Nkv, D):
+        raise ValueError("k and v disagree on batch, heads, length or head_dim")
+    L = lib()
+    Dp, nbk = padded_dim(D), num_blocks(Nkv)
+    dev = k.device
+    if out_k is None:
+        out_k = KQuant(torch.empty(B, Hkv, nbk * 64, max(Dp, 1), dtype=torch.int8, device=dev),
+                       torch.empty(B, Hkv, nbk, dtype=torch.float32, device=dev),
+                       torch.empty(B, Hkv, D, dtype=torch.float32, device=dev), B, Hkv, Nkv, D)
+    if out_v is None:
+        elt = 1 if pv == "fp8" else 2
+        out_v = VQuant(torch.empty(B, Hkv, nbk, max(Dp, 1), 64 * elt, dtype=torch.uint8, device=dev),
+                       torch.empty(B, Hkv, max(Dp, 1), dtype=torch.float32, device=dev) if pv == "fp8" else None, pv)
+    need = L.sage_quant_qkv_workspace_bytes(B, Hkv, Nkv, D, _PV[pv])
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=dev)
+    _check(L.sage_quant_kv(k.data_ptr(), v.data_ptr(), _DT[k.dtype], _LAYOUT[layout], B, Hkv, Nkv, D, _PV[pv],
+                           out_k.k_i8.data_ptr(), out_k.k_scale.data_ptr(), out_k.k_mean.data_ptr(),
+                           out_v.v_hat.data_ptr(), _ptr(out_v.v_scale), workspace.data_ptr(), workspace.numel(),
+                           _stream(dev)))
+    return out_k, out_v
+
+
+def attn_fwd_fused_q(q: torch.Tensor, kq: KQuant, vq: VQuant, layout: str = "HND", is_causal: bool = False,
+                     sm_scale: Optional[float] = None, accum: str = "fp32", out: Optional[torch.Tensor] = None,
+                     q_codes: Optional[tuple] = None) -> torch.Tensor:
+    """sage_attn_fwd_fused_q: attention that quantises Q (fp16 / bf16, dense) in its own
+    prologue; output in q's dtype and layout.  q_codes: optional (q_i8, q_scale) tensors,
+    shaped as QKQuant's, that receive the codes and block scales the kernel formed."""
+    _check_input(q, "q")
+    if accum not in _ACC:
+        raise ValueError(f"accum must be one of {sorted(_ACC)}, got {accum!r}")
+    B, Hq, Nq, D = _dims(q, layout)
+    if (kq.B, kq.D) != (B, D):
+        raise ValueError("q and the K operand disagree on batch or head_dim")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    qi, qs = (None, None) if q_codes is None else q_codes
+    _check(lib().sage_attn_fwd_fused_q(q.data_ptr(), _DT[q.dtype], _LAYOUT[layout], kq.k_i8.data_ptr(),
+                                       kq.k_scale.data_ptr(), vq.v_hat.data_ptr(), _ptr(vq.v_scale), out.data_ptr(),
+                                       B, Hq, kq.Hkv, Nq, kq.Nkv, D, int(bool(is_causal)), float(sm_scale),
+                                       _PV[vq.pv], _ACC[accum], _ptr(qi), _ptr(qs), _stream(q.device)))
     return out
 
 

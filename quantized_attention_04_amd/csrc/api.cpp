@@ -275,6 +275,79 @@ sage_status sage_quant_qkv(const void* q, const void* k, const void* v, sage_dty
     return launch_status(sage::launch_quant_qkv(a, va, (hipStream_t)stream), "sage_quant_qkv");
 }
 
+sage_status sage_quant_kv(const void* k, const void* v, sage_dtype dtype, sage_layout layout, int B, int H_kv, int Nkv,
+                          int D, sage_pv pv, int8_t* k_i8, float* k_scale, float* k_mean, void* v_hat, float* v_scale,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    if (!k || !v || !k_i8 || !k_scale || !k_mean || !v_hat)
+        return fail(SAGE_ERR_INVALID_ARG, "sage_quant_kv: null tensor pointer");
+    if (dtype != SAGE_FP16 && dtype != SAGE_BF16) return fail(SAGE_ERR_INVALID_ARG, "bad dtype %d", int(dtype));
+    if (pv != SAGE_PV_FP16 && pv != SAGE_PV_FP8) return fail(SAGE_ERR_INVALID_ARG, "bad pv mode %d", int(pv));
+    if (pv == SAGE_PV_FP8 && (!v_scale || !aligned(v_scale, 4)))
+        return fail(SAGE_ERR_INVALID_ARG, "sage_quant_kv: FP8 mode needs v_scale");
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_i8, 16) || !aligned(v_hat, 16) || !aligned(k_scale, 4) ||
+        !aligned(k_mean, 4))
+        return fail(SAGE_ERR_INVALID_ARG, "sage_quant_kv: tensors must be 16-byte aligned (scales 4-byte)");
+    if (layout != SAGE_HND && layout != SAGE_NHD) return fail(SAGE_ERR_INVALID_ARG, "bad layout %d", int(layout));
+    sage_status s = check_shape(B, H_kv, H_kv, Nkv, Nkv, D);
+    if (s != SAGE_OK) return s;
+    const size_t need = sage_quant_qkv_workspace_bytes(B, H_kv, Nkv, D, pv);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 8))
+        return fail(SAGE_ERR_WORKSPACE, "sage_quant_kv: workspace of %zu bytes (8-byte aligned) required, got %zu", need,
+                    workspace ? workspace_bytes : size_t(0));
+    s = check_device();
+    if (s != SAGE_OK) return s;
+    sage::QuantQKArgs a{};
+    a.q = nullptr;  // no Q: the K/V part of sage_quant_qkv's schedule
+    a.k = k;
+    a.bf16 = dtype == SAGE_BF16;
+    a.layout_nhd = layout == SAGE_NHD;
+    a.B = B, a.Hq = H_kv, a.Hkv = H_kv, a.Nq = Nkv, a.Nkv = Nkv, a.D = D;
+    a.k_i8 = k_i8, a.k_scale = k_scale, a.k_mean = k_mean;
+    a.workspace = workspace;
+    sage::QuantVArgs va{};
+    va.v = v;
+    va.fp8 = pv == SAGE_PV_FP8;
+    va.v_hat = v_hat, va.v_scale = v_scale;
+    return launch_status(sage::launch_quant_qkv(a, va, (hipStream_t)stream), "sage_quant_kv");
+}
+
+sage_status sage_attn_fwd_fused_q(const void* q, sage_dtype dtype, sage_layout layout, const int8_t* k_i8,
+                                  const float* k_scale, const void* v_hat, const float* v_scale, void* out, int B,
+                                  int H_qo, int H_kv, int Nq, int Nkv, int D, int is_causal, float sm_scale, sage_pv pv,
+                                  sage_accum accum, int8_t* q_i8_out, float* q_scale_out, void* stream) {
+    if (!q) return fail(SAGE_ERR_INVALID_ARG, "sage_attn_fwd_fused_q: null q");
+    if (dtype != SAGE_FP16 && dtype != SAGE_BF16) return fail(SAGE_ERR_INVALID_ARG, "bad dtype %d", int(dtype));
+    // the Q operand checks of sage_attn_fwd stand on the K operand's pointers here (q_i8 and
+    // q_scale are not read); q itself is checked below
+    sage_status s = check_attn_args(k_i8, k_scale, k_i8, k_scale, v_hat, v_scale, out, dtype, is_causal, sm_scale, pv,
+                                    accum, D, "sage_attn_fwd_fused_q");
+    if (s != SAGE_OK) return s;
+    if (!aligned(q, 16) || (q_i8_out && !aligned(q_i8_out, 16)) || (q_scale_out && !aligned(q_scale_out, 4)))
+        return fail(SAGE_ERR_INVALID_ARG, "sage_attn_fwd_fused_q: q and q_i8_out must be 16-byte aligned");
+    if (accum == SAGE_ACC_FP16_FP32_SPLIT)
+        return fail(SAGE_ERR_UNSUPPORTED, "sage_attn_fwd_fused_q: SAGE_ACC_FP16_FP32_SPLIT is not offered here");
+    if (layout != SAGE_HND && layout != SAGE_NHD) return fail(SAGE_ERR_INVALID_ARG, "bad layout %d", int(layout));
+    s = check_shape(B, H_qo, H_kv, Nq, Nkv, D);
+    if (s != SAGE_OK) return s;
+    s = check_device();
+    if (s != SAGE_OK) return s;
+    sage::AttnArgs a{};
+    a.k_i8 = k_i8, a.k_scale = k_scale, a.v_hat = v_hat, a.v_scale = v_scale;
+    a.out = out;
+    a.out_bf16 = dtype == SAGE_BF16;
+    a.out_nhd = layout == SAGE_NHD;
+    a.B = B, a.Hq = H_qo, a.Hkv = H_kv, a.Nq = Nq, a.Nkv = Nkv, a.D = D;
+    a.causal = is_causal;
+    a.sm_scale = sm_scale;
+    a.fp8 = pv == SAGE_PV_FP8;
+    a.q16 = q;
+    a.q_bf16 = dtype == SAGE_BF16;
+    a.q_nhd = layout == SAGE_NHD;
+    a.q_i8_out = q_i8_out;
+    a.q_scale_out = q_scale_out;
+    return launch_status(sage::launch_attn_fwd(a, (hipStream_t)stream), "sage_attn_fwd_fused_q");
+}
+
 size_t sage_quant_qkv_noalloc_max_bytes(void) { return sage::kNoAllocScratchBytes; }
 
 sage_status sage_quant_qkv_noalloc(const void* q, const void* k, const void* v, sage_dtype dtype, sage_layout layout,

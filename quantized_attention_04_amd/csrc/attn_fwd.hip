@@ -370,7 +370,133 @@ struct KParams {
     int splits, tps;
     _Float16* part_o;
     float* part_ml;
+    // QF kernels: Q arrives in fp16 / bf16 (q_bf16) with element strides qst, dense batch,
+    // and each workgroup quantises its own queries in the prologue; the codes and block
+    // scales also go to q_i8_out / q_scale_out where those are non-null
+    const uint16_t* q16;
+    Strides qst;
+    int q_bf16;
+    int8_t* q_i8_out;
+    float* q_scale_out;
 };
+
+// Q quantisation inside the attention prologue (QF): lane (g, i) of a wave loads the
+// channels 32 s + 16 g .. + 15 (s < KS) of its query q0 + i -- exactly the bytes of the
+// Q operand fragments it holds -- and the two waves of a 64-token block combine their
+// maxima through LDS.  The arithmetic is the block quantiser's: amax = max |x| over the
+// block's real elements (NaNs ignored), scale = amax / 127, inv = 127 / amax, code =
+// clamp(rne(x inv), -127, 127) with a NaN product giving 0; all-zero block: scale 0,
+// codes 0.  Absent rows and padding channels load as +0, which changes no maximum and
+// gives code 0.
+//   The maximum is taken on the magnitude bits: fp16 and bf16 are sign-magnitude, so
+// |x| orders like bits & 0x7fff (two values per packed 16-bit maximum); a NaN's bits lie
+// above the infinity's, and a block holding one takes the per-element path instead.
+//   Codes: with a finite amax and inv, |fp32(x inv)| <= 127 (1 + 2^-23), so the clamp is
+// inert and adding 1.5 * 2^23 rounds the product to an integer (ties to even) whose low
+// byte is the code (a NaN's low byte is 0: fp16 / bf16 NaNs widen with zero low bits);
+// otherwise the clamping path.
+template <class C, bool BF16>
+__device__ __forceinline__ void quant_q_frags(const KParams& p, v4i (&qf)[C::KS], float& sq, float* blk_amax,
+                                              int b, int h, int q0, int Nq, int64_t row0, int64_t slot0,
+                                              int lane, int wave) {
+    constexpr int KS = C::KS;
+    typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+    const int i = lane & 31, g = lane >> 5;
+    const int t = q0 + i;
+    const bool row = t < Nq;
+    const uint16_t* src = p.q16 + b * p.qst.b + h * p.qst.h + int64_t(row ? t : 0) * p.qst.t;
+    v8u16 raw[KS][2];
+    const bool vec = (p.D & 7) == 0;
+#pragma unroll
+    for (int s = 0; s < KS; s++)
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            const int c = 32 * s + 16 * g + 8 * u;
+            v8u16 r = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (row && c < p.D) {
+                if (vec) {
+                    r = *(const v8u16*)(src + c);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; e++) r[e] = c + e < p.D ? src[c + e] : (unsigned short)0;
+                }
+            }
+            raw[s][u] = r;
+        }
+    auto word = [&](int s, int w) {  // elements 2w, 2w + 1 of fragment s as one 32-bit word
+        const v8u16& r = raw[s][w >> 2];
+        return uint32_t(r[2 * (w & 3)]) | (uint32_t(r[2 * (w & 3) + 1]) << 16);
+    };
+    auto val = [&](int s, int e) { return in_to_f32<BF16>(raw[s][e >> 3][e & 7]); };
+    v2u16 mx2 = {0, 0};
+#pragma unroll
+    for (int s = 0; s < KS; s++)
+#pragma unroll
+        for (int w = 0; w < 8; w++) {
+            const uint32_t m = word(s, w) & 0x7fff7fffu;
+            v2u16 mv;
+            __builtin_memcpy(&mv, &m, 4);
+            mx2 = __builtin_elementwise_max(mx2, mv);
+        }
+    const uint32_t mbits = mx2[0] > mx2[1] ? mx2[0] : mx2[1];
+    float a;
+    if (mbits > (BF16 ? 0x7f80u : 0x7c00u)) {  // a NaN in this lane's elements: fmaxf ignores it
+        a = 0.0f;
+#pragma unroll
+        for (int s = 0; s < KS; s++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) a = fmaxf(a, fabsf(val(s, e)));
+    } else {
+        a = in_to_f32<BF16>(uint16_t(mbits));
+    }
+    a = wave_max(a);
+    if (lane == 0) blk_amax[wave] = a;
+    __syncthreads();
+    a = fmaxf(a, blk_amax[wave ^ 1]);
+    const bool zero = !(a > 0.0f);
+    const float inv = zero ? 0.0f : 127.0f / a;
+    sq = zero ? 0.0f : a / 127.0f;
+    if (!zero && a <= 3.4e38f && inv <= 3.4e38f) {  // uniform over the two waves of the block
+        constexpr float kRound = 12582912.0f;
+#pragma unroll
+        for (int s = 0; s < KS; s++) {
+            uint32_t w[4];
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                uint32_t r[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++) r[e] = __float_as_uint(val(s, 4 * k + e) * inv + kRound);
+                w[k] = __builtin_amdgcn_perm(r[1], r[0], 0x0c0c0400u) | __builtin_amdgcn_perm(r[3], r[2], 0x04000c0cu);
+            }
+            qf[s] = v4i{int(w[0]), int(w[1]), int(w[2]), int(w[3])};
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < KS; s++) {
+            uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 16; e++) {
+                int code = 0;
+                if (!zero && row && 32 * s + 16 * g + e < p.D) {
+                    float r = rintf(val(s, e) * inv);
+                    r = r > 127.0f ? 127.0f : r;
+                    r = r < -127.0f ? -127.0f : r;
+                    code = int(r);
+                }
+                w[e / 4] |= uint32_t(code & 0xff) << (8 * (e % 4));
+            }
+            qf[s] = v4i{int(w[0]), int(w[1]), int(w[2]), int(w[3])};
+        }
+    }
+    // the codes and scale for callers that keep them (rows up to the padded block end)
+    const int npad = (Nq + kBlk - 1) / kBlk * kBlk;
+    if (p.q_i8_out != nullptr && t < npad) {
+#pragma unroll
+        for (int s = 0; s < KS; s++) *(v4i*)(p.q_i8_out + (row0 + t) * C::KROW + 32 * s + 16 * g) = qf[s];
+    }
+    if (p.q_scale_out != nullptr && lane == 0 && (wave & 1) == 0 && q0 < npad)
+        p.q_scale_out[slot0 + q0 / kBlk] = sq;
+}
 
 // TG: the per-thread scales of sage_quant_qkv -- q_scale per token (indexed like the
 // rows of q_i8), k_scale per 32 keys ([slot][2]) -- so the dequantisation factor is
@@ -378,7 +504,8 @@ struct KParams {
 // TL: the explicit two-level P.V accumulation (pv_tile).
 // SPLIT: one key range of a query tile (KParams::splits); the fp32 partial state goes to
 // the workspace and split_merge_kernel combines the splits.
-template <int DP, bool FP8, bool CAUSAL, bool OBF16, bool TG = false, bool TL = false, bool SPLIT = false>
+template <int DP, bool FP8, bool CAUSAL, bool OBF16, bool TG = false, bool TL = false, bool SPLIT = false,
+          bool QF = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8>::OCC, Cfg<DP, FP8>::OCC))) void attn_fwd_kernel(KParams p) {
     using C = Cfg<DP, FP8>;
     // NST LDS stages: tile j lives in stage j % NST while tiles j+1 .. j+NST-1 stream in.
@@ -422,7 +549,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
     // ---- per-wave state
     v4i qf[C::KS];
     float sq = 0.0f;
-    if (active) {
+    if constexpr (QF) {
+        // every wave takes part (the block maximum goes through LDS and a barrier)
+        __shared__ float blk_amax[C::WAVES];
+        if (p.q_bf16) quant_q_frags<C, true>(p, qf, sq, blk_amax, b, h, q0, Nq, qv.row0, qv.slot0, lane, wave);
+        else quant_q_frags<C, false>(p, qf, sq, blk_amax, b, h, q0, Nq, qv.row0, qv.slot0, lane, wave);
+    } else if (active) {
         load_q_frags<C>(qf, p.q_i8 + (qv.row0 + q0) * DP, lane);
         if constexpr (TG) sq = p.q_scale[qv.row0 + qidx];  // 0 for padding rows
         else sq = scalar_load_f32(p.q_scale + qv.slot0 + qb);
@@ -691,10 +823,10 @@ __global__ __launch_bounds__(256) void debug_qk_kernel(const int8_t* __restrict_
             o[(wave * C::QW + i) * kBlk + key_of_reg<FP8>(kt, g, r)] = OFS ? S[kt][r] - kScoreBias : S[kt][r];
 }
 
-template <int DP, bool FP8, bool CAUSAL, bool OBF16, bool TG, bool TL = false>
+template <int DP, bool FP8, bool CAUSAL, bool OBF16, bool TG, bool TL = false, bool QF = false>
 hipError_t launch_attn_t(const KParams& p, int nwg, hipStream_t s) {
     using C = Cfg<DP, FP8>;
-    auto kern = attn_fwd_kernel<DP, FP8, CAUSAL, OBF16, TG, TL>;
+    auto kern = attn_fwd_kernel<DP, FP8, CAUSAL, OBF16, TG, TL, false, QF>;
     hipLaunchKernelGGL(kern, dim3(nwg), dim3(C::THREADS), 0, s, p);
     return hipGetLastError();
 }
@@ -718,6 +850,18 @@ hipError_t dispatch_split(const AttnArgs& a, const KParams& p, int nwg, hipStrea
     else
         hipLaunchKernelGGL((split_merge_kernel<DP, false, false>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
+}
+
+// Q quantised in the attention prologue (block granularity, dense batches)
+template <int DP, bool FP8>
+hipError_t dispatch_qf(const AttnArgs& a, const KParams& p, int nwg, hipStream_t s) {
+    const int key = (a.causal ? 2 : 0) | (a.out_bf16 ? 1 : 0);
+    switch (key) {
+    case 0: return launch_attn_t<DP, FP8, false, false, false, false, true>(p, nwg, s);
+    case 1: return launch_attn_t<DP, FP8, false, true, false, false, true>(p, nwg, s);
+    case 2: return launch_attn_t<DP, FP8, true, false, false, false, true>(p, nwg, s);
+    default: return launch_attn_t<DP, FP8, true, true, false, false, true>(p, nwg, s);
+    }
 }
 
 template <int DP, bool FP8>
@@ -803,6 +947,16 @@ hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s) {
     p.tps = 0;
     p.part_o = nullptr;
     p.part_ml = nullptr;
+    p.q16 = (const uint16_t*)a.q16;
+    p.qst = make_strides(a.q_nhd, a.Hq, a.Nq, a.D);
+    p.q_bf16 = a.q_bf16;
+    p.q_i8_out = a.q_i8_out;
+    p.q_scale_out = a.q_scale_out;
+    if (a.q16 != nullptr) {
+        if (a.D <= 64) return a.fp8 ? dispatch_qf<64, true>(a, p, nwg, s) : dispatch_qf<64, false>(a, p, nwg, s);
+        if (a.D <= 128) return a.fp8 ? dispatch_qf<128, true>(a, p, nwg, s) : dispatch_qf<128, false>(a, p, nwg, s);
+        return a.fp8 ? dispatch_qf<256, true>(a, p, nwg, s) : dispatch_qf<256, false>(a, p, nwg, s);
+    }
     if (a.splits > 1) {
         // balanced ranges: tps key tiles each, as few splits as cover every key tile
         const int NBk = (a.Nkv + kBlk - 1) / kBlk;

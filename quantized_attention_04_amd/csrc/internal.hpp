@@ -56,6 +56,13 @@ struct AttnArgs {
     int thread_gran;  // scales of sage_quant_qkv's per-thread granularity
     int splits;       // > 1: key-range splits (FP16 P.V, block granularity) into workspace
     void* workspace;  // splits > 1: part_o fp16 [B*Hq][Nq][splits][Dp], then part_ml fp32 [..][2]
+    // non-null: Q in fp16 / bf16 (q_bf16), layout q_nhd, dense, quantised in the attention
+    // prologue (q_i8 / q_scale unused); the codes and scales also go to q_i8_out /
+    // q_scale_out where those are non-null
+    const void* q16;
+    int q_bf16, q_nhd;
+    int8_t* q_i8_out;
+    float* q_scale_out;
 };
 
 // Workspace of the key-range split attention: fp16 per-split outputs [rows][Dp] at byte

@@ -629,7 +629,7 @@ hipError_t launch_qkv_t(const QuantQKArgs& a, const QuantVArgs& va, hipStream_t 
     double* kpart = (double*)(ws + w.kpart);
     float* vpart = (float*)(ws + w.vpart);
     uint32_t* amax = (uint32_t*)(ws + w.amax);
-    const int nq = ((mq.NB + 3) / 4) * a.Hq * a.B;
+    const int nq = a.q != nullptr ? ((mq.NB + 3) / 4) * a.Hq * a.B : 0;  // sage_quant_kv: no Q
     const int nkv = mk.NB * a.Hkv * a.B;
     if (mk.NB <= kFoldBlocks) {
         // short sequences: pass 2 folded into the K and V launches (three launches)

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_strings():
     L = qa.lib()
-    assert L.sage_abi_version() == 5
+    assert L.sage_abi_version() == 6
     for s in range(6):
         assert L.sage_status_string(s).decode().startswith("SAGE_")
     assert qa.padded_dim(1) == 64 and qa.padded_dim(64) == 64 and qa.padded_dim(65) == 128
@@ -493,3 +493,44 @@ def test_mxfp4_varlen_valid_arguments_reach_the_device_check_only():
         pytest.skip("would launch kernels on fake pointers")
     assert _mxqv() == qa.SAGE_ERR_DEVICE
     assert _mxav() == qa.SAGE_ERR_DEVICE
+
+
+def test_fused_q_entry_points_validate_first():
+    """sage_quant_kv and sage_attn_fwd_fused_q: bad arguments are refused before any HIP
+    call (then, with no GPU, the device check fails)."""
+    L = qa.lib()
+    need = L.sage_quant_qkv_workspace_bytes(2, 4, 1000, 128, 1)
+
+    def kv(**kw):
+        a = dict(k=FAKE, dtype=1, layout=0, H=4, N=1000, D=128, pv=1, vs=FAKE, ws=FAKE, wsb=need)
+        a.update(kw)
+        return L.sage_quant_kv(a["k"], FAKE, a["dtype"], a["layout"], 2, a["H"], a["N"], a["D"], a["pv"], FAKE, FAKE,
+                               FAKE, FAKE, a["vs"], a["ws"], a["wsb"], None)
+    assert kv(k=None) == qa.SAGE_ERR_INVALID_ARG
+    assert kv(dtype=7) == qa.SAGE_ERR_INVALID_ARG
+    assert kv(vs=None) == qa.SAGE_ERR_INVALID_ARG and "v_scale" in _detail()
+    assert kv(layout=3) == qa.SAGE_ERR_INVALID_ARG
+    assert kv(D=300) == qa.SAGE_ERR_UNSUPPORTED
+    assert kv(wsb=need - 1) == qa.SAGE_ERR_WORKSPACE
+    assert kv(k=FAKE + 8) == qa.SAGE_ERR_INVALID_ARG  # misaligned
+    if not torch.cuda.is_available():
+        assert kv() == qa.SAGE_ERR_DEVICE
+        assert kv(pv=0, vs=None) == qa.SAGE_ERR_DEVICE  # FP16 V needs no v_scale
+
+    def fq(**kw):
+        a = dict(q=FAKE, dtype=1, layout=0, Hq=8, Hkv=2, acc=0, qi=None, causal=0, sm=0.088)
+        a.update(kw)
+        return L.sage_attn_fwd_fused_q(a["q"], a["dtype"], a["layout"], FAKE, FAKE, FAKE, FAKE, FAKE, 2, a["Hq"],
+                                       a["Hkv"], 1000, 1000, 128, a["causal"], a["sm"], 1, a["acc"], a["qi"], None,
+                                       None)
+    assert fq(q=None) == qa.SAGE_ERR_INVALID_ARG
+    assert fq(dtype=5) == qa.SAGE_ERR_INVALID_ARG
+    assert fq(q=FAKE + 2) == qa.SAGE_ERR_INVALID_ARG
+    assert fq(qi=FAKE + 4) == qa.SAGE_ERR_INVALID_ARG
+    assert fq(acc=qa.SAGE_ACC_FP16_FP32_SPLIT) == qa.SAGE_ERR_UNSUPPORTED
+    assert fq(acc=qa.SAGE_ACC_FP16) == qa.SAGE_ERR_UNSUPPORTED
+    assert fq(Hq=7) == qa.SAGE_ERR_INVALID_ARG  # not a multiple of H_kv
+    assert fq(causal=2) == qa.SAGE_ERR_INVALID_ARG
+    assert fq(sm=-1.0) == qa.SAGE_ERR_INVALID_ARG
+    if not torch.cuda.is_available():
+        assert fq() == qa.SAGE_ERR_DEVICE

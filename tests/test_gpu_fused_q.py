@@ -1,0 +1,88 @@
+"""Q quantised inside the attention kernel (sage_quant_kv + sage_attn_fwd_fused_q): the
+same codes, scales and outputs as sage_quant_qkv + sage_attn_fwd, bit for bit, through
+the C ABI.  Since sage_quant_qkv's codes are checked bit for bit against the oracle and
+its attention output against the oracle's emulation elsewhere, equality here carries
+both over; one case also checks the fused codes against the oracle directly."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_attention_04_amd as qa
+import synth_inputs as si
+from gpu_helpers import Case, check_output, note
+
+pytestmark = pytest.mark.gpu
+
+W = si.workload
+CASES = [
+    ("d128_fp8_bf16", W("seq_sweep", B=2, Hq=4, Hkv=4, Nq=1000, Nkv=1000)),
+    ("d128_fp8_bf16_causal", W("seq_sweep", B=1, Hq=4, Hkv=4, Nq=777, Nkv=777, causal=True)),
+    ("d128_fp16_fp16_nhd", W("llm_prefill", Hq=4, Hkv=4, Nq=900, Nkv=900, layout="NHD")),
+    ("d64_fp8_nhd_offset", W("video_dit", Hq=3, Hkv=3, Nq=1100, Nkv=1100)),
+    ("gqa_d96_causal", W("gqa", B=1, Hq=8, Hkv=2, Nq=640, Nkv=640, D=96)),
+    ("d100_scalar_loads", W("llm_prefill", Hq=2, Hkv=2, Nq=300, Nkv=300, D=100)),
+    ("d256_fp8", W("seq_sweep", B=1, Hq=2, Hkv=2, Nq=500, Nkv=500, D=256)),
+    ("d200_fp16_causal", W("llm_prefill", Hq=2, Hkv=1, Nq=450, Nkv=450, D=200, causal=True)),
+    ("causal_nq_lt_nkv", W("llm_prefill", Hq=4, Hkv=2, Nq=200, Nkv=1500, D=96, causal=True)),
+    ("decode_one_query", W("seq_sweep", B=2, Hq=4, Hkv=4, Nq=1, Nkv=700, causal=True)),
+    ("short_40", W("tiny", Hq=2, Hkv=2, Nq=40, Nkv=40, D=40)),
+]
+
+
+def _both(case: Case, accum=None):
+    w = case.w
+    qk, vq = case.gpu_quant(fused=True)
+    ref = qa.attn_fwd(qk, vq, w.torch_dtype, w.layout, w.causal, None, accum or w.accum)
+    note(f"[gpu] quant_kv + attn_fwd_fused_q {w.name} {w.layout} D{w.D} Nq{w.Nq} Nkv{w.Nkv}")
+    kq, vq2 = qa.quant_kv(case.dk, case.dv, w.layout, w.pv)
+    qi = torch.full_like(qk.q_i8, 0x55)
+    qs = torch.full_like(qk.q_scale, -1.0)
+    out = qa.attn_fwd_fused_q(case.dq, kq, vq2, w.layout, w.causal, None, accum or w.accum, q_codes=(qi, qs))
+    torch.cuda.synchronize()
+    # the K and V operands: bit for bit those of sage_quant_qkv
+    assert torch.equal(kq.k_i8, qk.k_i8) and torch.equal(kq.k_scale, qk.k_scale)
+    assert torch.equal(kq.k_mean, qk.k_mean) and torch.equal(vq2.v_hat, vq.v_hat)
+    if w.pv == "fp8":
+        assert torch.equal(vq2.v_scale, vq.v_scale)
+    return qk, ref, out, qi, qs
+
+
+@pytest.mark.parametrize("cid,w", CASES, ids=[c[0] for c in CASES])
+def test_fused_q_equals_separate_quantisation(cid, w):
+    case = Case(w)
+    qk, ref, out, qi, qs = _both(case)
+    assert torch.equal(qi, qk.q_i8), "Q codes (padding rows included)"
+    assert torch.equal(qs, qk.q_scale), "Q block scales"
+    assert torch.equal(out, ref), "output differs from sage_attn_fwd on the same codes"
+
+
+def test_fused_q_codes_against_the_oracle():
+    w = W("gqa", B=1, Hq=4, Hkv=2, Nq=333, Nkv=333, D=72)
+    case = Case(w)
+    _, _, out, qi, qs = _both(case)
+    o = case.oq
+    np.testing.assert_array_equal(qi.cpu().numpy()[:, :, :w.Nq, :w.D], o.q_i8)
+    np.testing.assert_array_equal(qs.cpu().numpy(), o.q_scale)
+    check_output(case, out, oracle.all_rows(w.B, w.Hq, w.Nq))
+
+
+def test_fused_q_full_size_headline():
+    """B4 H32 N8192 D128 bf16, FP8 P.V, non-causal: the launch the benchmark times."""
+    w = W("seq_sweep")
+    case = Case(w)
+    qk, ref, out, qi, qs = _both(case)
+    assert torch.equal(qs, qk.q_scale) and torch.equal(qi, qk.q_i8)
+    assert torch.equal(out, ref)
+
+
+def test_fused_q_without_code_outputs_and_accum_names():
+    w = W("seq_sweep", B=1, Hq=2, Hkv=2, Nq=640, Nkv=640)
+    case = Case(w)
+    qk, vq = case.gpu_quant(fused=True)
+    kq, vq2 = qa.quant_kv(case.dk, case.dv, w.layout, w.pv)
+    for acc in ("fp32", "fp16+fp32"):
+        ref = qa.attn_fwd(qk, vq, w.torch_dtype, w.layout, False, None, acc)
+        out = qa.attn_fwd_fused_q(case.dq, kq, vq2, w.layout, False, None, acc)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)

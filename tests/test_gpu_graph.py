@@ -31,6 +31,15 @@ def _step_fn(kind, q, k, v, causal):
             qa.attn_fwd_mxfp4(mq, torch.bfloat16, "HND", causal, out=out)
         return step, out
     pv = "fp16" if kind in ("int8_fp16", "int8_fp16_split") else "fp8"
+    if kind == "int8_fused_q":  # sage_quant_kv + sage_attn_fwd_fused_q (Q quantised in the attention prologue)
+        ws = torch.empty(max(8, L.sage_quant_qkv_workspace_bytes(B, HKV, N, D, 1)), dtype=torch.uint8, device=dev)
+        kq, vq = qa.quant_kv(k, v, "HND", pv, workspace=ws)
+        out = qa.attn_fwd_fused_q(q, kq, vq, "HND", causal)
+
+        def step():
+            qa.quant_kv(k, v, "HND", pv, workspace=ws, out_k=kq, out_v=vq)
+            qa.attn_fwd_fused_q(q, kq, vq, "HND", causal, out=out)
+        return step, out
     if kind == "int8_separate":  # sage_quant_qk + sage_quant_v (its FP8 path clears a buffer with a kernel)
         wk = torch.empty(max(8, L.sage_quant_qk_workspace_bytes(B, HKV, N, D)), dtype=torch.uint8, device=dev)
         wv = torch.empty(max(8, L.sage_quant_v_workspace_bytes(B, HKV, D, 1)), dtype=torch.uint8, device=dev)
@@ -60,7 +69,8 @@ def _step_fn(kind, q, k, v, causal):
 
 
 @pytest.mark.parametrize("kind,causal", [("int8_fp8", False), ("int8_fp16", True), ("int8_separate", True),
-                                         ("mxfp4", True), ("int8_fp16_split", False), ("int8_fp16_split", True)])
+                                         ("mxfp4", True), ("int8_fp16_split", False), ("int8_fp16_split", True),
+                                         ("int8_fused_q", True)])
 def test_graph_replays_equal_eager_steps(kind, causal):
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev)

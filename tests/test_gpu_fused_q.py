@@ -86,3 +86,28 @@ def test_fused_q_without_code_outputs_and_accum_names():
         out = qa.attn_fwd_fused_q(case.dq, kq, vq2, w.layout, False, None, acc)
         torch.cuda.synchronize()
         assert torch.equal(out, ref)
+
+
+def test_fused_q_nonfinite_and_zero_blocks():
+    """A NaN (ignored by the block maximum, code 0), an infinity (scale inf, codes 0), an
+    all-zero block and negative zeros: the fused codes, scales and outputs equal the
+    separate quantiser's bit for bit (outputs compared as bits, NaNs included)."""
+    w = W("seq_sweep", B=1, Hq=2, Hkv=2, Nq=320, Nkv=320, dtype="fp16")
+    case = Case(w)
+    for dq in (case.dq,):
+        dq[0, 0, 5, 7] = float("nan")      # block 0 of head 0
+        dq[0, 0, 70, 3] = float("inf")     # block 1 of head 0
+        dq[0, 1, 128:192] = 0.0            # block 2 of head 1: all zero
+        dq[0, 1, 200, :] = -0.0            # block 3 of head 1: a row of negative zeros
+    torch.cuda.synchronize()
+    qk, vq = qa.quant_qkv(case.dq, case.dk, case.dv, w.layout, w.pv)
+    ref = qa.attn_fwd(qk, vq, w.torch_dtype, w.layout, False, None, w.accum)
+    kq, vq2 = qa.quant_kv(case.dk, case.dv, w.layout, w.pv)
+    qi = torch.full_like(qk.q_i8, 0x55)
+    qs = torch.full_like(qk.q_scale, -1.0)
+    out = qa.attn_fwd_fused_q(case.dq, kq, vq2, w.layout, False, None, w.accum, q_codes=(qi, qs))
+    torch.cuda.synchronize()
+    assert torch.equal(qi, qk.q_i8)
+    assert torch.equal(qs.view(torch.int32), qk.q_scale.view(torch.int32))
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    assert qk.q_i8[0, 0, 5, 7] == 0 and torch.isinf(qk.q_scale[0, 0, 1]) and qk.q_scale[0, 1, 2] == 0

@@ -99,7 +99,8 @@ def check_mx_bit_exact(c: MXCase, mq) -> None:
     assert (ve[:, :, w.D:] == 1).all() and (ve[:, :, :, nbt:] == 1).all(), "v4 padding exponents"
 
 
-def check_mx_output(c: MXCase, out: torch.Tensor, rows: np.ndarray, causal: bool, layout=None) -> None:
+def check_mx_output(c: MXCase, out: torch.Tensor, rows: np.ndarray, causal: bool, layout=None,
+                    envelope: bool = True) -> None:
     w = c.w
     got = gather_rows(out, rows, layout or w.layout)
     assert np.isfinite(got).all()
@@ -116,7 +117,11 @@ def check_mx_output(c: MXCase, out: torch.Tensor, rows: np.ndarray, causal: bool
     res["exact"] = metrics(got, ex)
     note(f"[metrics] {res}")
     assert res["emulate"]["worst_excess"] <= 0 and res["emulate"]["cos"] >= 0.9999, res
-    assert res["exact"]["rel_l1"] <= 0.35 and res["exact"]["cos"] >= 0.94, res
+    if envelope:
+        assert res["exact"]["rel_l1"] <= 0.35 and res["exact"]["cos"] >= 0.94, res
+    else:  # as close to exact attention as the scheme itself gets on these inputs
+        me = metrics(oracle.round_to(em_raw, fmt), ex)
+        assert res["exact"]["rel_l1"] <= me["rel_l1"] * 1.02 + 1e-3 and res["exact"]["cos"] >= me["cos"] - 1e-4, (res, me)
 
 
 def _rows(w, rows):
@@ -135,6 +140,25 @@ def test_mxfp4_output_matches_oracle(cid, w, rows):
     c = MXCase(w)
     _, out = c.gpu()
     check_mx_output(c, out, _rows(w, rows), w.causal)
+
+
+MAG_CASES = [
+    ("scaled6_d128", W("seq_sweep", B=1, Hq=2, Hkv=2, Nq=512, Nkv=512, qk_scale=6.0, seed=60)),
+    ("outliers_d64", W("video_dit", Hq=2, Hkv=2, Nq=600, Nkv=600, outliers=(10.0, 3.0), seed=61)),
+    ("scaled8_causal", W("seq_sweep", B=1, Hq=2, Hkv=1, Nq=400, Nkv=400, qk_scale=8.0, causal=True, seed=62)),
+]
+
+
+@pytest.mark.parametrize("cid,w", MAG_CASES, ids=[c[0] for c in MAG_CASES])
+def test_mxfp4_large_magnitudes(cid, w):
+    """Q and K scaled by 6-8, or with outlier channels and tokens: codes and exponents bit
+    for bit, the output at the emulation's bar.  Against exact attention the FP4 scheme
+    itself loses much more here (relative L1 0.38-0.65 in the oracle's own emulation), so
+    the GPU is held to no worse than the emulation rather than to the N(0,1) envelope."""
+    c = MXCase(w)
+    mq, out = c.gpu()
+    check_mx_bit_exact(c, mq)
+    check_mx_output(c, out, oracle.all_rows(w.B, w.Hq, w.Nq), w.causal, envelope=False)
 
 
 def test_mxfp4_full_size_sampled_rows():

@@ -482,9 +482,10 @@ def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: s
     _, _, Nkv, _ = _dims(k, tensor_layout)
     if qk_gran == "block" and accum != "fp16+fp32-split" and \
             lib().sage_attn_fwd_split_choice(B, Hq, Nq, Nkv, D, int(bool(is_causal)), _PV[pv]) == 1:
-        kq, vq = quant_kv(k, v, tensor_layout, pv)
+        _check_input(q, "q")
         if q.dtype != k.dtype or q.device != k.device:
             raise ValueError("q, k and v must share dtype and device")
+        kq, vq = quant_kv(k, v, tensor_layout, pv)
         return attn_fwd_fused_q(q, kq, vq, tensor_layout, is_causal, sm_scale, accum)
     qk, vq = quant_qkv(q, k, v, tensor_layout, pv, gran=qk_gran)
     return attn_fwd(qk, vq, q.dtype, tensor_layout, is_causal, sm_scale, accum, splits="auto")

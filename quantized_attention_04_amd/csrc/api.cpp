@@ -102,12 +102,11 @@ sage_status check_varlen(const int32_t* cu_q, const int32_t* cu_k, int B, int Hq
 }
 
 
-// Checks shared by the dense and the packed attention calls (not the shapes).
-sage_status check_attn_args(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
-                            const void* v_hat, const float* v_scale, void* out, sage_dtype out_dtype, int is_causal,
-                            float sm_scale, sage_pv pv, sage_accum accum, int D, const char* what) {
-    if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v_hat || !out)
-        return fail(SAGE_ERR_INVALID_ARG, "%s: null tensor pointer", what);
+// Checks shared by every attention call except those of the Q operand (not the shapes).
+sage_status check_kv_attn_args(const int8_t* k_i8, const float* k_scale, const void* v_hat, const float* v_scale,
+                               void* out, sage_dtype out_dtype, int is_causal, float sm_scale, sage_pv pv,
+                               sage_accum accum, int D, const char* what) {
+    if (!k_i8 || !k_scale || !v_hat || !out) return fail(SAGE_ERR_INVALID_ARG, "%s: null tensor pointer", what);
     if (out_dtype != SAGE_FP16 && out_dtype != SAGE_BF16)
         return fail(SAGE_ERR_INVALID_ARG, "bad out dtype %d", int(out_dtype));
     if (pv != SAGE_PV_FP16 && pv != SAGE_PV_FP8) return fail(SAGE_ERR_INVALID_ARG, "bad pv mode %d", int(pv));
@@ -122,9 +121,20 @@ sage_status check_attn_args(const int8_t* q_i8, const float* q_scale, const int8
                                           "accumulate FP16/FP8 products in fp32");
     if (pv == SAGE_PV_FP8 && (!v_scale || !aligned(v_scale, 4)))
         return fail(SAGE_ERR_INVALID_ARG, "%s: FP8 mode needs v_scale", what);
-    if (!aligned(q_i8, 16) || !aligned(k_i8, 16) || !aligned(v_hat, 16) || !aligned(q_scale, 4) ||
-        !aligned(k_scale, 4) || !aligned(out, (D % 4) == 0 ? 8 : 2))
+    if (!aligned(k_i8, 16) || !aligned(v_hat, 16) || !aligned(k_scale, 4) || !aligned(out, (D % 4) == 0 ? 8 : 2))
         return fail(SAGE_ERR_INVALID_ARG, "%s: misaligned tensor", what);
+    return SAGE_OK;
+}
+
+// Checks shared by the dense and the packed attention calls on quantised Q (not the shapes).
+sage_status check_attn_args(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                            const void* v_hat, const float* v_scale, void* out, sage_dtype out_dtype, int is_causal,
+                            float sm_scale, sage_pv pv, sage_accum accum, int D, const char* what) {
+    if (!q_i8 || !q_scale) return fail(SAGE_ERR_INVALID_ARG, "%s: null tensor pointer", what);
+    sage_status s = check_kv_attn_args(k_i8, k_scale, v_hat, v_scale, out, out_dtype, is_causal, sm_scale, pv, accum,
+                                       D, what);
+    if (s != SAGE_OK) return s;
+    if (!aligned(q_i8, 16) || !aligned(q_scale, 4)) return fail(SAGE_ERR_INVALID_ARG, "%s: misaligned tensor", what);
     return SAGE_OK;
 }
 
@@ -317,10 +327,8 @@ sage_status sage_attn_fwd_fused_q(const void* q, sage_dtype dtype, sage_layout l
                                   sage_accum accum, int8_t* q_i8_out, float* q_scale_out, void* stream) {
     if (!q) return fail(SAGE_ERR_INVALID_ARG, "sage_attn_fwd_fused_q: null q");
     if (dtype != SAGE_FP16 && dtype != SAGE_BF16) return fail(SAGE_ERR_INVALID_ARG, "bad dtype %d", int(dtype));
-    // the Q operand checks of sage_attn_fwd stand on the K operand's pointers here (q_i8 and
-    // q_scale are not read); q itself is checked below
-    sage_status s = check_attn_args(k_i8, k_scale, k_i8, k_scale, v_hat, v_scale, out, dtype, is_causal, sm_scale, pv,
-                                    accum, D, "sage_attn_fwd_fused_q");
+    sage_status s = check_kv_attn_args(k_i8, k_scale, v_hat, v_scale, out, dtype, is_causal, sm_scale, pv, accum, D,
+                                       "sage_attn_fwd_fused_q");
     if (s != SAGE_OK) return s;
     if (!aligned(q, 16) || (q_i8_out && !aligned(q_i8_out, 16)) || (q_scale_out && !aligned(q_scale_out, 4)))
         return fail(SAGE_ERR_INVALID_ARG, "sage_attn_fwd_fused_q: q and q_i8_out must be 16-byte aligned");

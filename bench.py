@@ -493,12 +493,21 @@ def mxfp4_points(qa, torch, q, k, v, w, steps):
         at = sum(b.elapsed_time(c) for a, b, c in ev) / steps
         qt = sum(a.elapsed_time(b) for a, b, c in ev) / steps
         o = wc.ops()
+        # Q quantised in the attention prologue (quant_mxfp4_kv + attn_fwd_mxfp4_fused_q), graph-timed
+        mk = qa.quant_mxfp4_kv(k, v, w.layout, workspace=ws)
+        out2 = torch.empty_like(q)
+
+        def fstep():
+            qa.quant_mxfp4_kv(k, v, w.layout, workspace=ws, out=mk)
+            qa.attn_fwd_mxfp4_fused_q(q, mk, w.layout, causal, None, out=out2)
+        fs = graph_ms(torch, fstep, reps=3, replays=3)
         res["points"].append({"causal": causal, "attn_ms": round(at, 4), "quant_ms": round(qt, 4),
                               "attn_tops": round(o / (at * 1e-3) / 1e12, 1),
                               "step_tops": round(o / ((at + qt) * 1e-3) / 1e12, 1),
-                              "attn_frac_of_fp4_peak": round(o / (at * 1e-3) / 1e12 / MXFP4_PEAK_TOPS, 4)})
+                              "attn_frac_of_fp4_peak": round(o / (at * 1e-3) / 1e12 / MXFP4_PEAK_TOPS, 4),
+                              "fused_q_step_ms": round(fs, 4), "fused_q_step_tops": round(o / (fs * 1e-3) / 1e12, 1)})
         log(f"[bench] mxfp4 causal={causal}: attn {at:.3f} ms = {res['points'][-1]['attn_tops']} TOPS, "
-            f"quant {qt:.3f} ms")
+            f"quant {qt:.3f} ms; fused-Q step {fs:.3f} ms = {res['points'][-1]['fused_q_step_tops']} TOPS")
     return res
 
 

@@ -426,6 +426,27 @@ sage_status sage_attn_fwd_mxfp4(const uint8_t* q4, const uint8_t* q4_exp, const 
                                 sage_layout out_layout, int B, int H_qo, int H_kv, int Nq, int Nkv, int D,
                                 int is_causal, float sm_scale, void* stream);
 
+/*
+ * The MXFP4 variant with Q quantised inside the attention kernel (the same scheme as
+ * sage_quant_mxfp4 + sage_attn_fwd_mxfp4; SageAttention README, "Project Updates"):
+ * sage_quant_mxfp4_kv writes the K mean and the codes and exponents of the smoothed K
+ * and of V only (arguments, layouts, workspace and errors as sage_quant_mxfp4 without the
+ * Q tensors; results bit-identical), and sage_attn_fwd_mxfp4_fused_q reads q in fp16 /
+ * bf16 (dtype; layout HND or NHD, dense, 16-byte aligned; the output takes q's dtype and
+ * layout): every lane quantises the 32-channel blocks of its own query that it holds as
+ * matrix-instruction operands, in the arithmetic of sage_quant_mxfp4, so codes,
+ * exponents and output are bit-identical to the separate calls.  q4_out [B][H_qo][N_pad]
+ * [Dp/2] (16-byte aligned) and q4_exp_out [B][H_qo][N_pad][Dp/32], both optional (null:
+ * not written), receive the codes and exponent bytes the kernel formed.
+ */
+sage_status sage_quant_mxfp4_kv(const void* k, const void* v, sage_dtype dtype, sage_layout layout, int B, int H_kv,
+                                int Nkv, int D, uint8_t* k4, uint8_t* k4_exp, float* k_mean, uint8_t* v4,
+                                uint8_t* v4_exp, void* workspace, size_t workspace_bytes, void* stream);
+sage_status sage_attn_fwd_mxfp4_fused_q(const void* q, sage_dtype dtype, sage_layout layout, const uint8_t* k4,
+                                        const uint8_t* k4_exp, const uint8_t* v4, const uint8_t* v4_exp, void* out,
+                                        int B, int H_qo, int H_kv, int Nq, int Nkv, int D, int is_causal,
+                                        float sm_scale, uint8_t* q4_out, uint8_t* q4_exp_out, void* stream);
+
 /* The MXFP4 calls on a packed batch (README "Available APIs", sageattn_varlen; the dense
  * scheme per sequence, as for the INT8 calls): q (total_q, H_qo, D), k and v
  * (total_kv, H_kv, D), cu_seqlens as for sage_quant_qk_varlen.  Rows and slots per head

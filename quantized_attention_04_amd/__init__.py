@@ -91,6 +91,10 @@ _EXPORTS = {
                          + [ctypes.c_void_p] * 7 + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "sage_attn_fwd_mxfp4": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] * 2 + [ctypes.c_int] * 7
                             + [ctypes.c_float, ctypes.c_void_p]),
+    "sage_quant_mxfp4_kv": (ctypes.c_int, [ctypes.c_void_p] * 2 + [ctypes.c_int] * 6 + [ctypes.c_void_p] * 6
+                            + [ctypes.c_size_t, ctypes.c_void_p]),
+    "sage_attn_fwd_mxfp4_fused_q": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 5
+                                    + [ctypes.c_int] * 7 + [ctypes.c_float] + [ctypes.c_void_p] * 3),
     "sage_quant_mxfp4_varlen_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
     "sage_quant_mxfp4_varlen": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] + [ctypes.c_void_p] * 2
                                 + [ctypes.c_int] * 8 + [ctypes.c_void_p] * 7 + [ctypes.c_void_p, ctypes.c_size_t,
@@ -461,11 +465,81 @@ def attn_fwd_mxfp4(mq: MXQuant, out_dtype: torch.dtype, layout: str = "HND", is_
     return out
 
 
+@dataclasses.dataclass
+class MXKQuant:
+    """Outputs of sage_quant_mxfp4_kv: MXQuant's K and V parts."""
+    k4: torch.Tensor
+    k4_exp: torch.Tensor
+    k_mean: torch.Tensor
+    v4: torch.Tensor
+    v4_exp: torch.Tensor
+    B: int
+    Hkv: int
+    Nkv: int
+    D: int
+
+
+def quant_mxfp4_kv(k: torch.Tensor, v: torch.Tensor, layout: str = "HND", workspace: Optional[torch.Tensor] = None,
+                   out: Optional[MXKQuant] = None) -> MXKQuant:
+    """sage_quant_mxfp4_kv: the K mean and the MXFP4 codes and exponents of smoothed K and of V
+    (for attn_fwd_mxfp4_fused_q, which quantises Q itself)."""
+    for name, x in (("k", k), ("v", v)):
+        _check_input(x, name)
+    if k.dtype != v.dtype or k.device != v.device:
+        raise ValueError("k and v must share dtype and device")
+    B, Hkv, Nkv, D = _dims(k, layout)
+    if _dims(v, layout) != (B, Hkv, Nkv, D):
+        raise ValueError("k and v disagree on batch, heads, length or head_dim")
+    L = lib()
+    Dp, nbk = max(padded_dim(D), 64), num_blocks(Nkv)
+    dev = k.device
+    if out is None:
+        u8 = dict(dtype=torch.uint8, device=dev)
+        out = MXKQuant(torch.empty(B, Hkv, nbk * 64, Dp // 2, **u8), torch.empty(B, Hkv, nbk * 64, Dp // 32, **u8),
+                       torch.empty(B, Hkv, D, dtype=torch.float32, device=dev),
+                       torch.empty(B, Hkv, nbk, Dp, 32, **u8), torch.empty(B, Hkv, nbk, 2, 32, Dp // 32, **u8),
+                       B, Hkv, Nkv, D)
+    need = L.sage_quant_mxfp4_workspace_bytes(B, Hkv, Nkv, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=dev)
+    _check(L.sage_quant_mxfp4_kv(k.data_ptr(), v.data_ptr(), _DT[k.dtype], _LAYOUT[layout], B, Hkv, Nkv, D,
+                                 out.k4.data_ptr(), out.k4_exp.data_ptr(), out.k_mean.data_ptr(), out.v4.data_ptr(),
+                                 out.v4_exp.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(dev)))
+    return out
+
+
+def attn_fwd_mxfp4_fused_q(q: torch.Tensor, mk: MXKQuant, layout: str = "HND", is_causal: bool = False,
+                           sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                           q_codes: Optional[tuple] = None) -> torch.Tensor:
+    """sage_attn_fwd_mxfp4_fused_q: MXFP4 attention that quantises Q (fp16 / bf16, dense) in
+    its own prologue; output in q's dtype and layout.  q_codes: optional (q4, q4_exp)
+    tensors, shaped as MXQuant's, that receive the codes and exponent bytes."""
+    _check_input(q, "q")
+    B, Hq, Nq, D = _dims(q, layout)
+    if (mk.B, mk.D) != (B, D):
+        raise ValueError("q and the K operand disagree on batch or head_dim")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    qc, qe = (None, None) if q_codes is None else q_codes
+    _check(lib().sage_attn_fwd_mxfp4_fused_q(q.data_ptr(), _DT[q.dtype], _LAYOUT[layout], mk.k4.data_ptr(),
+                                             mk.k4_exp.data_ptr(), mk.v4.data_ptr(), mk.v4_exp.data_ptr(),
+                                             out.data_ptr(), B, Hq, mk.Hkv, Nq, mk.Nkv, D, int(bool(is_causal)),
+                                             float(sm_scale), _ptr(qc), _ptr(qe), _stream(q.device)))
+    return out
+
+
 def sageattn_mxfp4(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: str = "HND",
                    is_causal: bool = False, sm_scale: Optional[float] = None) -> torch.Tensor:
-    """The microscaling FP4 variant: quant_mxfp4 then attn_fwd_mxfp4 (output in q's dtype and layout)."""
-    mq = quant_mxfp4(q, k, v, tensor_layout)
-    return attn_fwd_mxfp4(mq, q.dtype, tensor_layout, is_causal, sm_scale)
+    """The microscaling FP4 variant (output in q's dtype and layout): quant_mxfp4_kv, then
+    attn_fwd_mxfp4_fused_q, which quantises Q in its prologue -- the same codes and output
+    as quant_mxfp4 followed by attn_fwd_mxfp4."""
+    _check_input(q, "q")
+    if q.dtype != k.dtype or q.device != k.device:
+        raise ValueError("q, k and v must share dtype and device")
+    mk = quant_mxfp4_kv(k, v, tensor_layout)
+    return attn_fwd_mxfp4_fused_q(q, mk, tensor_layout, is_causal, sm_scale)
 
 
 def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: str = "HND", is_causal: bool = False,

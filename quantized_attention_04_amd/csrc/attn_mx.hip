@@ -118,6 +118,14 @@ struct MXParams {
     int B, Hq, Hkv, G, D, QT;
     int grp;       // causal: kv heads whose query tiles are interleaved (1, 2 or 4)
     float cscale;  // sm_scale * log2(e)
+    // QF kernels: Q in fp16 / bf16 (q_bf16) with element strides qst, dense batch,
+    // quantised by each lane in the prologue; the codes and exponent bytes also go to
+    // q4_out / q4_exp_out where those are non-null
+    const uint16_t* q16;
+    Strides qst;
+    int q_bf16;
+    uint8_t* q4_out;
+    uint8_t* q4_exp_out;
 };
 
 // three-input maximum of scores straight from the matrix instruction: the
@@ -131,7 +139,71 @@ __device__ __forceinline__ int mx_exp_dev(float amax) {  // floor(log2 amax) - 2
     return max(int((__float_as_uint(amax) >> 23) & 0xffu) - 129, -126);
 }
 
-template <int DP, bool CAUSAL, bool OBF16>
+// MXFP4 Q inside the attention prologue (QF): every block of 32 channels of a query is
+// exactly the 32 k-values one lane holds for one matrix-instruction k-step (channels
+// 64 s + 32 g .. + 31 of query qidx), so each lane quantises its own blocks with no
+// exchange, in the arithmetic of the separate quantiser: amax = max |x| over the block's
+// real elements (absent rows and padding channels are +0), E = floor(log2 amax) - 2
+// held to [-126, 127], codes e2m1(x / 2^E) by the scaled conversion (round to nearest
+// even, saturating at 6), element 2t in the low nibble of byte t.
+template <class C, bool BF16>
+__device__ __forceinline__ void mx_quant_q(const MXParams& p, v4i (&qf)[C::KS], int (&qsc)[C::KS], int b, int h,
+                                           int qidx, int Nq, int64_t row0, int g) {
+    const bool row = qidx < Nq;
+    const uint16_t* src = p.q16 + b * p.qst.b + h * p.qst.h + int64_t(row ? qidx : 0) * p.qst.t;
+    const bool vec = (p.D & 7) == 0;
+#pragma unroll
+    for (int s = 0; s < C::KS; s++) {
+        float y[32];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int c = 64 * s + 32 * g + 8 * u;
+            v8u16 r = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (row && c < p.D) {
+                if (vec) {
+                    r = *(const v8u16*)(src + c);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; e++) r[e] = c + e < p.D ? src[c + e] : (unsigned short)0;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; e++) y[8 * u + e] = in_to_f32<BF16>(r[e]);
+        }
+        float am = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 32; e++) am = fmaxf(am, fabsf(y[e]));
+        const int E = mx_exp_dev(am);
+        const float X = __uint_as_float(uint32_t(E + 127) << 23);
+        int wd[4];
+#pragma unroll
+        for (int w = 0; w < 4; w++) {
+            int x = 0;
+            x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, y[8 * w + 0], y[8 * w + 1], X, 0);
+            x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, y[8 * w + 2], y[8 * w + 3], X, 1);
+            x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, y[8 * w + 4], y[8 * w + 5], X, 2);
+            x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, y[8 * w + 6], y[8 * w + 7], X, 3);
+            wd[w] = x;
+        }
+        qf[s] = v4i{wd[0], wd[1], wd[2], wd[3]};
+        qsc[s] = E + 127;
+    }
+    // the codes and exponent bytes for callers that keep them (rows up to the padded
+    // block end; a padding row quantises +0: codes 0, exponent byte 1)
+    const int npad = (Nq + kBlk - 1) / kBlk * kBlk;
+    if (qidx < npad) {
+        if (p.q4_out != nullptr) {
+#pragma unroll
+            for (int s = 0; s < C::KS; s++) *(v4i*)(p.q4_out + (row0 + qidx) * C::KROW + 32 * s + 16 * g) = qf[s];
+        }
+        if (p.q4_exp_out != nullptr) {
+#pragma unroll
+            for (int s = 0; s < C::KS; s++) p.q4_exp_out[(row0 + qidx) * C::NE + 2 * s + g] = uint8_t(qsc[s]);
+        }
+    }
+}
+
+template <int DP, bool CAUSAL, bool OBF16, bool QF = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MXCfg<DP>::OCC, MXCfg<DP>::OCC))) void
 attn_mx_kernel(MXParams p) {
     using C = MXCfg<DP>;
@@ -167,7 +239,10 @@ attn_mx_kernel(MXParams p) {
     // lane: block 2 s + g of the lane's query
     v4i qf[C::KS];
     int qsc[C::KS];
-    if (active) {
+    if constexpr (QF) {
+        if (p.q_bf16) mx_quant_q<C, true>(p, qf, qsc, b, h, qidx, Nq, qv.row0, g);
+        else mx_quant_q<C, false>(p, qf, qsc, b, h, qidx, Nq, qv.row0, g);
+    } else if (active) {
         const uint8_t* qrow = p.q4 + (qv.row0 + qidx) * C::KROW;
         const uint8_t* qe = p.q4_exp + (qv.row0 + qidx) * C::NE;
 #pragma unroll
@@ -356,7 +431,7 @@ attn_mx_kernel(MXParams p) {
         }
 }
 
-template <int DP, bool CAUSAL, bool OBF16>
+template <int DP, bool CAUSAL, bool OBF16, bool QF>
 hipError_t launch_mx_attn_t(const AttnMXArgs& a, hipStream_t s) {
     using C = MXCfg<DP>;
     MXParams p;
@@ -383,15 +458,25 @@ hipError_t launch_mx_attn_t(const AttnMXArgs& a, hipStream_t s) {
     // K4 and V4 of one kv head: codes (DP / 2 bytes per token each) and exponents
     p.grp = causal_head_group(int64_t((a.Nkv + kBlk - 1) / kBlk) * kBlk * (DP + DP / 16));
     p.cscale = a.sm_scale * 1.4426950408889634f;
+    p.q16 = (const uint16_t*)a.q16;
+    p.qst = make_strides(a.q_nhd, a.Hq, a.Nq, a.D);
+    p.q_bf16 = a.q_bf16;
+    p.q4_out = a.q4_out;
+    p.q4_exp_out = a.q4_exp_out;
     const int64_t grid = int64_t(p.QT) * a.Hq * a.B;
-    attn_mx_kernel<DP, CAUSAL, OBF16><<<dim3(unsigned(grid)), C::THREADS, 0, s>>>(p);
+    attn_mx_kernel<DP, CAUSAL, OBF16, QF><<<dim3(unsigned(grid)), C::THREADS, 0, s>>>(p);
     return hipGetLastError();
 }
 
+template <int DP, bool QF>
+hipError_t launch_mx_attn_q(const AttnMXArgs& a, hipStream_t s) {
+    if (a.causal)
+        return a.out_bf16 ? launch_mx_attn_t<DP, true, true, QF>(a, s) : launch_mx_attn_t<DP, true, false, QF>(a, s);
+    return a.out_bf16 ? launch_mx_attn_t<DP, false, true, QF>(a, s) : launch_mx_attn_t<DP, false, false, QF>(a, s);
+}
 template <int DP>
 hipError_t launch_mx_attn_dp(const AttnMXArgs& a, hipStream_t s) {
-    if (a.causal) return a.out_bf16 ? launch_mx_attn_t<DP, true, true>(a, s) : launch_mx_attn_t<DP, true, false>(a, s);
-    return a.out_bf16 ? launch_mx_attn_t<DP, false, true>(a, s) : launch_mx_attn_t<DP, false, false>(a, s);
+    return a.q16 != nullptr ? launch_mx_attn_q<DP, true>(a, s) : launch_mx_attn_q<DP, false>(a, s);
 }
 
 }  // namespace

@@ -113,6 +113,12 @@ struct AttnMXArgs {
     const int32_t* cu_q;
     const int32_t* cu_k;
     int total_q, total_k;
+    // non-null: Q in fp16 / bf16 (q_bf16), layout q_nhd, dense, quantised in the attention
+    // prologue (q4 / q4_exp unused); codes and exponents also to q4_out / q4_exp_out if set
+    const void* q16;
+    int q_bf16, q_nhd;
+    uint8_t* q4_out;
+    uint8_t* q4_exp_out;
 };
 
 struct DebugQKArgs {

@@ -894,8 +894,9 @@ hipError_t launch_mx_t(const QuantMXArgs& a, hipStream_t s) {
                                                                                 (double*)a.workspace);
     const int tot = a.B * a.Hkv * a.D;
     k_mean_final_kernel<<<(tot + 63) / 64, 64, 0, s>>>((const double*)a.workspace, mk, tot, a.D, a.k_mean);
-    mx_rows_kernel<BF16, DP, VEC8, false><<<dim3((mq.NB + 3) / 4, a.Hq, a.B), 256, 0, s>>>(
-        (const uint16_t*)a.q, mq, a.D, nullptr, a.q4, a.q4_exp);
+    if (a.q != nullptr)  // sage_quant_mxfp4_kv: no Q
+        mx_rows_kernel<BF16, DP, VEC8, false><<<dim3((mq.NB + 3) / 4, a.Hq, a.B), 256, 0, s>>>(
+            (const uint16_t*)a.q, mq, a.D, nullptr, a.q4, a.q4_exp);
     mx_rows_kernel<BF16, DP, VEC8, true><<<dim3((mk.NB + 3) / 4, a.Hkv, a.B), 256, 0, s>>>(
         (const uint16_t*)a.k, mk, a.D, a.k_mean, a.k4, a.k4_exp);
     mx_v_kernel<BF16, DP, VEC8><<<dim3(mk.NB, a.Hkv, a.B), 2 * DP, 0, s>>>((const uint16_t*)a.v, mk, a.D, a.v4,

@@ -534,3 +534,38 @@ def test_fused_q_entry_points_validate_first():
     assert fq(sm=-1.0) == qa.SAGE_ERR_INVALID_ARG
     if not torch.cuda.is_available():
         assert fq() == qa.SAGE_ERR_DEVICE
+
+
+def test_mxfp4_fused_q_entry_points_validate_first():
+    L = qa.lib()
+    need = L.sage_quant_mxfp4_workspace_bytes(1, 2, 500, 128)
+
+    def kv(**kw):
+        a = dict(k=FAKE, dtype=1, layout=0, D=128, wsb=need, km=FAKE)
+        a.update(kw)
+        return L.sage_quant_mxfp4_kv(a["k"], FAKE, a["dtype"], a["layout"], 1, 2, 500, a["D"], FAKE, FAKE, a["km"],
+                                     FAKE, FAKE, FAKE, a["wsb"], None)
+    assert kv(k=None) == qa.SAGE_ERR_INVALID_ARG
+    assert kv(km=None) == qa.SAGE_ERR_INVALID_ARG
+    assert kv(dtype=4) == qa.SAGE_ERR_INVALID_ARG
+    assert kv(layout=2) == qa.SAGE_ERR_INVALID_ARG
+    assert kv(k=FAKE + 4) == qa.SAGE_ERR_INVALID_ARG
+    assert kv(D=257) == qa.SAGE_ERR_UNSUPPORTED
+    assert kv(wsb=need - 8) == qa.SAGE_ERR_WORKSPACE
+    if not torch.cuda.is_available():
+        assert kv() == qa.SAGE_ERR_DEVICE
+
+    def fq(**kw):
+        a = dict(q=FAKE, dtype=0, causal=1, sm=0.1, Hq=4, qc=None)
+        a.update(kw)
+        return L.sage_attn_fwd_mxfp4_fused_q(a["q"], a["dtype"], 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1, a["Hq"], 2, 300,
+                                             500, 128, a["causal"], a["sm"], a["qc"], None, None)
+    assert fq(q=None) == qa.SAGE_ERR_INVALID_ARG
+    assert fq(dtype=9) == qa.SAGE_ERR_INVALID_ARG
+    assert fq(causal=3) == qa.SAGE_ERR_INVALID_ARG
+    assert fq(sm=float("inf")) == qa.SAGE_ERR_INVALID_ARG
+    assert fq(q=FAKE + 2) == qa.SAGE_ERR_INVALID_ARG
+    assert fq(qc=FAKE + 1) == qa.SAGE_ERR_INVALID_ARG
+    assert fq(Hq=3) == qa.SAGE_ERR_INVALID_ARG
+    if not torch.cuda.is_available():
+        assert fq() == qa.SAGE_ERR_DEVICE

@@ -315,3 +315,56 @@ def test_mxfp4_varlen_equals_dense_per_sequence():
         v = c.v[c.ck[b]:c.ck[b + 1]][None].to("cuda:0")
         dense = qa.sageattn_mxfp4(q, k, v, "NHD", True, sm_scale_of(w.D))
         assert torch.equal(dense[0], out[int(c.cq[b]):int(c.cq[b + 1])]), f"sequence {b}"
+
+
+# ----------------------------------------------------------------------------- Q quantised in the attention kernel
+
+FQ_CASES = [c for c in CASES if c[0] in ("tiny_causal", "ragged_fp16_d40", "gqa_nhd_d72_causal_nq_lt_nkv",
+                                          "d128_causal_1000", "d96_gqa_nhd", "one_key", "one_query", "d256_causal",
+                                          "d200_gqa_nhd")]
+
+
+def _fused_vs_separate(w, dq, dk, dv):
+    mq = qa.quant_mxfp4(dq, dk, dv, w.layout)
+    ref = qa.attn_fwd_mxfp4(mq, w.torch_dtype, w.layout, w.causal)
+    mk = qa.quant_mxfp4_kv(dk, dv, w.layout)
+    qc = torch.full_like(mq.q4, 0x5A)
+    qe = torch.full_like(mq.q4_exp, 0xA5)
+    out = qa.attn_fwd_mxfp4_fused_q(dq, mk, w.layout, w.causal, q_codes=(qc, qe))
+    torch.cuda.synchronize()
+    for name in ("k4", "k4_exp", "k_mean", "v4", "v4_exp"):
+        assert torch.equal(getattr(mk, name), getattr(mq, name)), name
+    assert torch.equal(qc, mq.q4), "Q codes (padding rows included)"
+    assert torch.equal(qe, mq.q4_exp), "Q exponents"
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), "output differs from the separate calls"
+    return out
+
+
+@pytest.mark.parametrize("cid,w,rows", FQ_CASES, ids=[c[0] for c in FQ_CASES])
+def test_mxfp4_fused_q_equals_separate(cid, w, rows):
+    c = MXCase(w)
+    note(f"[gpu] mxfp4 fused Q {cid}")
+    dq, dk, dv = (t.to("cuda:0") for t in (c.q, c.k, c.v))
+    _fused_vs_separate(w, dq, dk, dv)
+
+
+def test_mxfp4_fused_q_full_size_and_sageattn():
+    w = W("seq_sweep")
+    c = MXCase(w)
+    dq, dk, dv = (t.to("cuda:0") for t in (c.q, c.k, c.v))
+    out = _fused_vs_separate(w, dq, dk, dv)
+    o2 = qa.sageattn_mxfp4(dq, dk, dv, w.layout, False)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o2)
+
+
+def test_mxfp4_fused_q_nonfinite_and_zero_blocks():
+    w = W("seq_sweep", B=1, Hq=2, Hkv=2, Nq=320, Nkv=320, dtype="fp16", seed=63)
+    c = MXCase(w)
+    dq, dk, dv = (t.to("cuda:0") for t in (c.q, c.k, c.v))
+    dq[0, 0, 5, 7] = float("nan")
+    dq[0, 0, 70, 3] = float("inf")
+    dq[0, 1, 128:192] = 0.0
+    dq[0, 1, 200, :] = -0.0
+    torch.cuda.synchronize()
+    _fused_vs_separate(w, dq, dk, dv)

@@ -376,6 +376,25 @@ sage_status sage_attn_fwd_varlen_g(const int8_t* q_i8, const float* q_scale, con
                                    int is_causal, float sm_scale, sage_pv pv, sage_accum accum, sage_qk_gran gran,
                                    void* stream);
 
+/* Packed-batch forms of sage_quant_kv and sage_attn_fwd_fused_q (block granularity):
+ * K and V quantised as sage_quant_qkv_varlen does (workspace
+ * sage_quant_qkv_varlen_workspace_bytes(B, H_kv, total_kv, D, pv)), and attention that
+ * quantises each sequence's Q (q [total_q][H_qo][D] in fp16 / bf16, 16-byte aligned) in
+ * its prologue; out [total_q][H_qo][D] in q's dtype.  q_i8_out [H_qo][rows][Dp] and
+ * q_scale_out [H_qo][slots] (rows, slots of total_q), both optional, receive the codes
+ * and scales, which equal sage_quant_qkv_varlen's bit for bit, as does the output
+ * sage_attn_fwd_varlen's.  Errors as the calls they mirror. */
+sage_status sage_quant_kv_varlen(const void* k, const void* v, sage_dtype dtype, const int32_t* cu_seqlens_kv, int B,
+                                 int H_kv, int total_kv, int max_seqlen_kv, int D, sage_pv pv, int8_t* k_i8,
+                                 float* k_scale, float* k_mean, void* v_hat, float* v_scale, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+sage_status sage_attn_fwd_varlen_fused_q(const void* q, sage_dtype dtype, const int32_t* cu_seqlens_q,
+                                         const int32_t* cu_seqlens_kv, const int8_t* k_i8, const float* k_scale,
+                                         const void* v_hat, const float* v_scale, void* out, int B, int H_qo, int H_kv,
+                                         int total_q, int total_kv, int max_seqlen_q, int max_seqlen_kv, int D,
+                                         int is_causal, float sm_scale, sage_pv pv, sage_accum accum, int8_t* q_i8_out,
+                                         float* q_scale_out, void* stream);
+
 /* ---- Microscaling FP4 (MXFP4) variant ---------------------------------------------
  * The SageAttention README names a microscaling FP4 attention for inference
  * ("SageAttention3: Microscaling FP4 Attention", project updates and citations) and

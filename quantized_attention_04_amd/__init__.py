@@ -109,6 +109,11 @@ _EXPORTS = {
     "sage_quant_qkv_noalloc_max_bytes": (ctypes.c_size_t, []),
     "sage_quant_qkv_noalloc": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 10
                                + [ctypes.c_void_p] * 8),
+    "sage_quant_kv_varlen": (ctypes.c_int, [ctypes.c_void_p] * 2 + [ctypes.c_int, ctypes.c_void_p] + [ctypes.c_int] * 6
+                             + [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "sage_attn_fwd_varlen_fused_q": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 7
+                                     + [ctypes.c_int] * 9 + [ctypes.c_float, ctypes.c_int, ctypes.c_int]
+                                     + [ctypes.c_void_p] * 3),
     "sage_quant_kv": (ctypes.c_int, [ctypes.c_void_p] * 2 + [ctypes.c_int] * 7 + [ctypes.c_void_p] * 6
                       + [ctypes.c_size_t, ctypes.c_void_p]),
     "sage_attn_fwd_fused_q": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 5
@@ -827,12 +832,89 @@ def attn_fwd_varlen(qk: QKQuantVarlen, vq: VQuantVarlen, out_dtype: torch.dtype,
     return out
 
 
+def quant_kv_varlen(k: torch.Tensor, v: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_k: int,
+                    pv: str = "fp16", workspace: Optional[torch.Tensor] = None, out_k=None, out_v=None):
+    """sage_quant_kv_varlen: the K and V part of quant_qkv_varlen (block granularity);
+    returns (QKQuantVarlen with the K fields set and Q's left None, VQuantVarlen)."""
+    for name, x in (("k", k), ("v", v)):
+        _check_input(x, name)
+    if k.dtype != v.dtype or k.device != v.device:
+        raise ValueError("k and v must share dtype and device")
+    if pv not in _PV:
+        raise ValueError(f"pv must be 'fp16' or 'fp8', got {pv!r}")
+    total_k, Hkv, D = _packed_dims(k, "k")
+    if tuple(v.shape) != (total_k, Hkv, D):
+        raise ValueError("k and v disagree on heads, tokens or head_dim")
+    dev = k.device
+    ck = _cu(cu_seqlens_k, dev, "cu_seqlens_k")
+    B = ck.numel() - 1
+    L = lib()
+    Dp = padded_dim(D)
+    rk, sk = varlen_rows(total_k, B), varlen_slots(total_k, B)
+    elt = 1 if pv == "fp8" else 2
+    kq = out_k
+    if kq is None:
+        kq = QKQuantVarlen(None, None, torch.empty(Hkv, rk, max(Dp, 1), dtype=torch.int8, device=dev),
+                           torch.empty(Hkv, sk, dtype=torch.float32, device=dev),
+                           torch.empty(B, Hkv, D, dtype=torch.float32, device=dev), None, ck, B, None, Hkv, None,
+                           total_k, None, int(max_seqlen_k), D)
+    vq = out_v
+    if vq is None:
+        vq = VQuantVarlen(torch.empty(Hkv, sk, max(Dp, 1), 64 * elt, dtype=torch.uint8, device=dev),
+                          torch.empty(B, Hkv, max(Dp, 1), dtype=torch.float32, device=dev) if pv == "fp8" else None, pv)
+    need = L.sage_quant_qkv_varlen_workspace_bytes(B, Hkv, total_k, D, _PV[pv])
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=dev)
+    _check(L.sage_quant_kv_varlen(k.data_ptr(), v.data_ptr(), _DT[k.dtype], ck.data_ptr(), B, Hkv, total_k,
+                                  int(max_seqlen_k), D, _PV[pv], kq.k_i8.data_ptr(), kq.k_scale.data_ptr(),
+                                  kq.k_mean.data_ptr(), vq.v_hat.data_ptr(), _ptr(vq.v_scale), workspace.data_ptr(),
+                                  workspace.numel(), _stream(dev)))
+    return kq, vq
+
+
+def attn_fwd_varlen_fused_q(q: torch.Tensor, cu_seqlens_q: torch.Tensor, max_seqlen_q: int, kq, vq,
+                            is_causal: bool = False, sm_scale: Optional[float] = None, accum: str = "fp32",
+                            out: Optional[torch.Tensor] = None, q_codes: Optional[tuple] = None) -> torch.Tensor:
+    """sage_attn_fwd_varlen_fused_q: packed attention that quantises each sequence's Q in
+    its own prologue; kq, vq from quant_kv_varlen; output (total_q, Hq, D) in q's dtype.
+    q_codes: optional (q_i8, q_scale) tensors shaped as QKQuantVarlen's."""
+    _check_input(q, "q")
+    if accum not in _ACC:
+        raise ValueError(f"accum must be one of {sorted(_ACC)}, got {accum!r}")
+    total_q, Hq, D = _packed_dims(q, "q")
+    if D != kq.D:
+        raise ValueError("q and the K operand disagree on head_dim")
+    cq = _cu(cu_seqlens_q, q.device, "cu_seqlens_q")
+    if cq.numel() != kq.cu_k.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must describe the same number of sequences")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    qi, qs = (None, None) if q_codes is None else q_codes
+    _check(lib().sage_attn_fwd_varlen_fused_q(q.data_ptr(), _DT[q.dtype], cq.data_ptr(), kq.cu_k.data_ptr(),
+                                              kq.k_i8.data_ptr(), kq.k_scale.data_ptr(), vq.v_hat.data_ptr(),
+                                              _ptr(vq.v_scale), out.data_ptr(), kq.B, Hq, kq.Hkv, total_q,
+                                              kq.total_kv, int(max_seqlen_q), kq.max_k, D, int(bool(is_causal)),
+                                              float(sm_scale), _PV[vq.pv], _ACC[accum], _ptr(qi), _ptr(qs),
+                                              _stream(q.device)))
+    return out
+
+
 def sageattn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
                     cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, is_causal: bool = False,
                     sm_scale: Optional[float] = None, pv: str = "fp16", accum: str = "fp32",
                     qk_gran: str = "block") -> torch.Tensor:
     """Attention over a packed batch of sequences of different lengths (each sequence
-    attends only to its own keys); returns q's dtype, shape (total_q, Hq, D)."""
+    attends only to its own keys); returns q's dtype, shape (total_q, Hq, D).  At block
+    granularity Q is quantised inside the attention kernel (quant_kv_varlen +
+    attn_fwd_varlen_fused_q: the same codes and output as the separate calls)."""
+    if qk_gran == "block" and accum != "fp16+fp32-split":
+        _check_input(q, "q")
+        if q.dtype != k.dtype or q.device != k.device:
+            raise ValueError("q, k and v must share dtype and device")
+        kq, vq = quant_kv_varlen(k, v, cu_seqlens_k, max_seqlen_k, pv)
+        return attn_fwd_varlen_fused_q(q, cu_seqlens_q, max_seqlen_q, kq, vq, is_causal, sm_scale, accum)
     qk, vq = quant_qkv_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, pv, gran=qk_gran)
     return attn_fwd_varlen(qk, vq, q.dtype, is_causal, sm_scale, accum)
 

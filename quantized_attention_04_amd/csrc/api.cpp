@@ -626,6 +626,80 @@ sage_status sage_quant_qkv_varlen(const void* q, const void* k, const void* v, s
     return launch_status(sage::launch_quant_qkv(a, va, (hipStream_t)stream), "sage_quant_qkv_varlen");
 }
 
+sage_status sage_quant_kv_varlen(const void* k, const void* v, sage_dtype dtype, const int32_t* cu_seqlens_kv, int B,
+                                 int H_kv, int total_kv, int max_seqlen_kv, int D, sage_pv pv, int8_t* k_i8,
+                                 float* k_scale, float* k_mean, void* v_hat, float* v_scale, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    if (!k || !v || !k_i8 || !k_scale || !k_mean || !v_hat)
+        return fail(SAGE_ERR_INVALID_ARG, "sage_quant_kv_varlen: null tensor pointer");
+    if (dtype != SAGE_FP16 && dtype != SAGE_BF16) return fail(SAGE_ERR_INVALID_ARG, "bad dtype %d", int(dtype));
+    if (pv != SAGE_PV_FP16 && pv != SAGE_PV_FP8) return fail(SAGE_ERR_INVALID_ARG, "bad pv mode %d", int(pv));
+    if (pv == SAGE_PV_FP8 && (!v_scale || !aligned(v_scale, 4)))
+        return fail(SAGE_ERR_INVALID_ARG, "sage_quant_kv_varlen: FP8 mode needs v_scale");
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_i8, 16) || !aligned(v_hat, 16) || !aligned(k_scale, 4) ||
+        !aligned(k_mean, 4))
+        return fail(SAGE_ERR_INVALID_ARG, "sage_quant_kv_varlen: tensors must be 16-byte aligned (scales 4-byte)");
+    // the K/V sequences stand for both sides of the shared checks
+    sage_status s = check_varlen(cu_seqlens_kv, cu_seqlens_kv, B, H_kv, H_kv, total_kv, total_kv, max_seqlen_kv,
+                                 max_seqlen_kv, D);
+    if (s != SAGE_OK) return s;
+    const size_t need = sage_quant_qkv_varlen_workspace_bytes(B, H_kv, total_kv, D, pv);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 8))
+        return fail(SAGE_ERR_WORKSPACE,
+                    "sage_quant_kv_varlen: workspace of %zu bytes (8-byte aligned) required, got %zu", need,
+                    workspace ? workspace_bytes : size_t(0));
+    s = check_device();
+    if (s != SAGE_OK) return s;
+    sage::QuantQKArgs a{};
+    a.q = nullptr;  // no Q: the K/V part of sage_quant_qkv_varlen's schedule
+    a.k = k;
+    a.bf16 = dtype == SAGE_BF16;
+    a.B = B, a.Hq = H_kv, a.Hkv = H_kv, a.Nq = max_seqlen_kv, a.Nkv = max_seqlen_kv, a.D = D;
+    a.cu_q = cu_seqlens_kv, a.cu_k = cu_seqlens_kv, a.total_q = total_kv, a.total_k = total_kv;
+    a.k_i8 = k_i8, a.k_scale = k_scale, a.k_mean = k_mean;
+    a.workspace = workspace;
+    sage::QuantVArgs va{};
+    va.v = v;
+    va.fp8 = pv == SAGE_PV_FP8;
+    va.v_hat = v_hat, va.v_scale = v_scale;
+    return launch_status(sage::launch_quant_qkv(a, va, (hipStream_t)stream), "sage_quant_kv_varlen");
+}
+
+sage_status sage_attn_fwd_varlen_fused_q(const void* q, sage_dtype dtype, const int32_t* cu_seqlens_q,
+                                         const int32_t* cu_seqlens_kv, const int8_t* k_i8, const float* k_scale,
+                                         const void* v_hat, const float* v_scale, void* out, int B, int H_qo, int H_kv,
+                                         int total_q, int total_kv, int max_seqlen_q, int max_seqlen_kv, int D,
+                                         int is_causal, float sm_scale, sage_pv pv, sage_accum accum, int8_t* q_i8_out,
+                                         float* q_scale_out, void* stream) {
+    if (!q) return fail(SAGE_ERR_INVALID_ARG, "sage_attn_fwd_varlen_fused_q: null q");
+    if (dtype != SAGE_FP16 && dtype != SAGE_BF16) return fail(SAGE_ERR_INVALID_ARG, "bad dtype %d", int(dtype));
+    sage_status s = check_kv_attn_args(k_i8, k_scale, v_hat, v_scale, out, dtype, is_causal, sm_scale, pv, accum, D,
+                                       "sage_attn_fwd_varlen_fused_q");
+    if (s != SAGE_OK) return s;
+    if (!aligned(q, 16) || (q_i8_out && !aligned(q_i8_out, 16)) || (q_scale_out && !aligned(q_scale_out, 4)))
+        return fail(SAGE_ERR_INVALID_ARG, "sage_attn_fwd_varlen_fused_q: q and q_i8_out must be 16-byte aligned");
+    if (accum == SAGE_ACC_FP16_FP32_SPLIT)
+        return fail(SAGE_ERR_UNSUPPORTED, "sage_attn_fwd_varlen_fused_q: SAGE_ACC_FP16_FP32_SPLIT is not offered here");
+    s = check_varlen(cu_seqlens_q, cu_seqlens_kv, B, H_qo, H_kv, total_q, total_kv, max_seqlen_q, max_seqlen_kv, D);
+    if (s != SAGE_OK) return s;
+    s = check_device();
+    if (s != SAGE_OK) return s;
+    sage::AttnArgs a{};
+    a.k_i8 = k_i8, a.k_scale = k_scale, a.v_hat = v_hat, a.v_scale = v_scale;
+    a.out = out;
+    a.out_bf16 = dtype == SAGE_BF16;
+    a.B = B, a.Hq = H_qo, a.Hkv = H_kv, a.Nq = max_seqlen_q, a.Nkv = max_seqlen_kv, a.D = D;
+    a.causal = is_causal;
+    a.sm_scale = sm_scale;
+    a.fp8 = pv == SAGE_PV_FP8;
+    a.cu_q = cu_seqlens_q, a.cu_k = cu_seqlens_kv, a.total_q = total_q, a.total_k = total_kv;
+    a.q16 = q;
+    a.q_bf16 = dtype == SAGE_BF16;
+    a.q_i8_out = q_i8_out;
+    a.q_scale_out = q_scale_out;
+    return launch_status(sage::launch_attn_fwd(a, (hipStream_t)stream), "sage_attn_fwd_varlen_fused_q");
+}
+
 sage_status sage_attn_fwd_varlen(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
                                  const void* v_hat, const float* v_scale, void* out, sage_dtype out_dtype,
                                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int B, int H_qo, int H_kv,

@@ -397,14 +397,14 @@ struct KParams {
 // otherwise the clamping path.
 template <class C, bool BF16>
 __device__ __forceinline__ void quant_q_frags(const KParams& p, v4i (&qf)[C::KS], float& sq, float* blk_amax,
-                                              int b, int h, int q0, int Nq, int64_t row0, int64_t slot0,
-                                              int lane, int wave) {
+                                              const uint16_t* qbase, int64_t tstride, int q0, int Nq, int64_t row0,
+                                              int64_t slot0, int lane, int wave) {
     constexpr int KS = C::KS;
     typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
     const int i = lane & 31, g = lane >> 5;
     const int t = q0 + i;
     const bool row = t < Nq;
-    const uint16_t* src = p.q16 + b * p.qst.b + h * p.qst.h + int64_t(row ? t : 0) * p.qst.t;
+    const uint16_t* src = qbase + int64_t(row ? t : 0) * tstride;
     v8u16 raw[KS][2];
     const bool vec = (p.D & 7) == 0;
 #pragma unroll
@@ -552,8 +552,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
     if constexpr (QF) {
         // every wave takes part (the block maximum goes through LDS and a barrier)
         __shared__ float blk_amax[C::WAVES];
-        if (p.q_bf16) quant_q_frags<C, true>(p, qf, sq, blk_amax, b, h, q0, Nq, qv.row0, qv.slot0, lane, wave);
-        else quant_q_frags<C, false>(p, qf, sq, blk_amax, b, h, q0, Nq, qv.row0, qv.slot0, lane, wave);
+        // token 0 of this (sequence, head) and the token stride: dense, the input's layout;
+        // packed, (total, H_qo, D) as the sequence map describes it
+        const bool packed = p.qm.cu != nullptr;
+        const uint16_t* qbase = packed ? p.q16 + qv.in_off : p.q16 + b * p.qst.b + h * p.qst.h;
+        const int64_t ts = packed ? p.qm.st.t : p.qst.t;
+        if (p.q_bf16) quant_q_frags<C, true>(p, qf, sq, blk_amax, qbase, ts, q0, Nq, qv.row0, qv.slot0, lane, wave);
+        else quant_q_frags<C, false>(p, qf, sq, blk_amax, qbase, ts, q0, Nq, qv.row0, qv.slot0, lane, wave);
     } else if (active) {
         load_q_frags<C>(qf, p.q_i8 + (qv.row0 + q0) * DP, lane);
         if constexpr (TG) sq = p.q_scale[qv.row0 + qidx];  // 0 for padding rows

@@ -569,3 +569,33 @@ def test_mxfp4_fused_q_entry_points_validate_first():
     assert fq(Hq=3) == qa.SAGE_ERR_INVALID_ARG
     if not torch.cuda.is_available():
         assert fq() == qa.SAGE_ERR_DEVICE
+
+
+def test_varlen_fused_q_entry_points_validate_first():
+    L = qa.lib()
+    need = L.sage_quant_qkv_varlen_workspace_bytes(3, 2, 500, 64, 0)
+
+    def kv(**kw):
+        a = dict(k=FAKE, cu=FAKE, pv=0, vs=None, wsb=need)
+        a.update(kw)
+        return L.sage_quant_kv_varlen(a["k"], FAKE, 0, a["cu"], 3, 2, 500, 300, 64, a["pv"], FAKE, FAKE, FAKE, FAKE,
+                                      a["vs"], FAKE, a["wsb"], None)
+    assert kv(k=None) == qa.SAGE_ERR_INVALID_ARG
+    assert kv(cu=None) == qa.SAGE_ERR_INVALID_ARG
+    assert kv(pv=1) == qa.SAGE_ERR_INVALID_ARG  # FP8 without v_scale
+    assert kv(wsb=need - 8) == qa.SAGE_ERR_WORKSPACE
+    if not torch.cuda.is_available():
+        assert kv() == qa.SAGE_ERR_DEVICE
+
+    def fq(**kw):
+        a = dict(q=FAKE, acc=0, causal=1, cu=FAKE)
+        a.update(kw)
+        return L.sage_attn_fwd_varlen_fused_q(a["q"], 1, a["cu"], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 4, 2, 600, 500,
+                                              300, 300, 64, a["causal"], 0.125, 1, a["acc"], None, None, None)
+    assert fq(q=None) == qa.SAGE_ERR_INVALID_ARG
+    assert fq(q=FAKE + 2) == qa.SAGE_ERR_INVALID_ARG
+    assert fq(cu=None) == qa.SAGE_ERR_INVALID_ARG
+    assert fq(causal=5) == qa.SAGE_ERR_INVALID_ARG
+    assert fq(acc=qa.SAGE_ACC_FP16_FP32_SPLIT) == qa.SAGE_ERR_UNSUPPORTED
+    if not torch.cuda.is_available():
+        assert fq() == qa.SAGE_ERR_DEVICE

@@ -148,3 +148,41 @@ def test_varlen_large_sampled_rows():
     o = out.float().cpu().numpy()
     got = o[c.cq[rows[:, 0]] + rows[:, 2], rows[:, 1]].astype(np.float64)
     compare_rows(got, em, amb, ex, oracle.BF16, "fp8")
+
+
+# ----------------------------------------------------------------------------- Q quantised in the attention kernel
+
+@pytest.mark.parametrize("w", CASES, ids=[c.name for c in CASES])
+def test_varlen_fused_q_equals_separate(w):
+    """quant_kv_varlen + attn_fwd_varlen_fused_q against quant_qkv_varlen + attn_fwd_varlen:
+    K/V operands, the Q codes and scales the kernel formed (padding rows included) and
+    the outputs, bit for bit."""
+    c = VCase(w)
+    qk, vq, ref = c.gpu(fused=True)
+    dev = "cuda:0"
+    q, k, v, cq, ck = (x.to(dev) for x in (c.q, c.k, c.v, c.cu_q, c.cu_k))
+    mq, mk = max(w.lens_q + (1,)), max(w.lens_k + (1,))
+    kq, vq2 = qa.quant_kv_varlen(k, v, ck, mk, w.pv)
+    qi = torch.full_like(qk.q_i8, 0x55)
+    qs = torch.full_like(qk.q_scale, -1.0)
+    out = qa.attn_fwd_varlen_fused_q(q, cq, mq, kq, vq2, w.causal, sm_scale_of(w.D), w.accum, q_codes=(qi, qs))
+    torch.cuda.synchronize()
+    # the documented rows and slots of every sequence (rows between sequences are never written)
+    assert torch.equal(kq.k_mean, qk.k_mean)
+    for b in range(w.B):
+        if w.pv == "fp8" and w.lens_k[b] > 0:  # a sequence without keys has no V scale written
+            assert torch.equal(vq2.v_scale[b], vq.v_scale[b]), f"V scales of sequence {b}"
+        R, S = _rows_slots(c.ck, b)
+        nb = (w.lens_k[b] + 63) // 64
+        assert torch.equal(kq.k_i8[:, R:R + 64 * nb], qk.k_i8[:, R:R + 64 * nb]), f"K codes of sequence {b}"
+        assert torch.equal(kq.k_scale[:, S:S + nb], qk.k_scale[:, S:S + nb]), f"K scales of sequence {b}"
+        assert torch.equal(vq2.v_hat[:, S:S + nb], vq.v_hat[:, S:S + nb]), f"V codes of sequence {b}"
+        R, S = _rows_slots(c.cq, b)
+        nb = (w.lens_q[b] + 63) // 64
+        assert torch.equal(qi[:, R:R + 64 * nb], qk.q_i8[:, R:R + 64 * nb]), f"Q codes of sequence {b}"
+        assert torch.equal(qs[:, S:S + nb], qk.q_scale[:, S:S + nb]), f"Q scales of sequence {b}"
+    assert torch.equal(out, ref)
+    # and sageattn_varlen takes this schedule by default
+    o2 = qa.sageattn_varlen(q, k, v, cq, ck, mq, mk, w.causal, sm_scale_of(w.D), w.pv, w.accum)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, ref)

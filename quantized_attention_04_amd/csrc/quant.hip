@@ -402,32 +402,6 @@ __device__ __forceinline__ void kv_stats_block(const uint16_t* __restrict__ k, c
     }
 }
 
-// Pass 1.  nq workgroups quantise four Q blocks each (number x of a (head, batch): x
-// + nq4 * (h + Hq * b)); nkv take one K/V block each (j + NB * (h + H_kv * b)).  The
-// two kinds are spread evenly over the grid, so Q's read-write stream and the K/V
-// read streams run side by side.
-template <bool BF16, int DP, bool VEC8, bool VMAX, int QG>
-__global__ __launch_bounds__(256) void qkv_pass1_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                        const uint16_t* __restrict__ v, SeqMap mq, SeqMap mk, int D,
-                                                        int nq, int nkv, int8_t* __restrict__ q_i8,
-                                                        float* __restrict__ q_scale, double* __restrict__ kpart,
-                                                        float* __restrict__ vpart) {
-    __shared__ __attribute__((aligned(16))) uint16_t tile[kBlk][DP];
-    __shared__ float red[VMAX ? 256 / (DP / 8) : 1][DP];
-    const int64_t wg = blockIdx.x, T = int64_t(nq) + nkv;
-    const int a0 = int(wg * nq / T), a1 = int((wg + 1) * nq / T);  // Q workgroups before wg, before wg + 1
-    if (a1 > a0) {
-        const int nq4 = (mq.NB + 3) / 4;
-        const int x = a0 % nq4, h = (a0 / nq4) % mq.H, b = a0 / (nq4 * mq.H);
-        const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-        quant_block_wave<BF16, DP, VEC8, false, QG>(q, mq, D, nullptr, q_i8, q_scale, x * 4 + wave, h, b, lane);
-    } else {
-        const int r = int(wg) - a1;
-        const int j = r % mk.NB, h = (r / mk.NB) % mk.H, b = r / (mk.NB * mk.H);
-        kv_stats_block<BF16, DP, VEC8, VMAX>(k, v, mk, D, kpart, vpart, j, h, b, tile, red);
-    }
-}
-
 // Pass 2: per (b, kv head, channel): the K mean as k_mean_final_kernel (c < D) and, with
 // VMAX, the V channel maximum over the sequence's blocks as float bits (c < DP), the
 // form quant_v_kernel reads.  One thread per (b, kv head, c < DP).
@@ -468,29 +442,31 @@ __global__ __launch_bounds__(64) void qkv_pass2_kernel(const double* __restrict_
 //         the block-0 workgroup also writes v_scale[c] = fp32(amax[c] / 448).
 // FOLD (FP8, short sequences): amax[c] is reduced here from the per-block channel maxima
 // vpart of qkv_pass1_kernel, as qkv_pass2_kernel would (amax_bits is then unused).
-template <bool BF16, int DP, bool VEC8, bool FP8, bool FOLD = false>
-__global__ __launch_bounds__(2 * DP) void quant_v_kernel(const uint16_t* __restrict__ v, SeqMap m, int D,
-                                                      const uint32_t* __restrict__ amax_bits,
-                                                      void* __restrict__ vhat, float* __restrict__ vscale,
-                                                      const float* __restrict__ vpart = nullptr) {
+// The body of quant_v_kernel for block j of (b, kv head h), run by NT >= 2 DP threads
+// (threads from 2 DP on only help with the final copy and meet the barriers); tile is
+// the workgroup's LDS tile of DP * 64 * (1 | 2) bytes, samax DP floats (FOLD).
+template <bool BF16, int DP, bool VEC8, bool FP8, bool FOLD, int NT>
+__device__ __forceinline__ void v_block(const uint16_t* __restrict__ v, const SeqMap& m, int D,
+                                        const uint32_t* __restrict__ amax_bits, void* __restrict__ vhat,
+                                        float* __restrict__ vscale, const float* __restrict__ vpart, int j, int h,
+                                        int b, uint8_t* __restrict__ tile, float* __restrict__ samax) {
     constexpr int ELT = FP8 ? 1 : 2;
     constexpr int CH = DP / 8;               // 8-channel chunks per token row
     constexpr int THREADS = CH * (kBlk / 4);  // one thread per (token quad, chunk)
     constexpr int ROWB = kBlk * ELT;          // bytes per channel row of the tile
     constexpr int RMASK = FP8 ? 3 : 1;
-    __shared__ __attribute__((aligned(16))) uint8_t tile[DP * ROWB];
-    const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    static_assert(NT == THREADS || (NT > THREADS && !FP8), "extra helper threads in FP16 mode only");
     const SeqView sv = seq_view(m, b, h);
     if (j * kBlk >= sv.n) return;  // the whole workgroup: past this sequence's end
     const int N = sv.n;
     const Strides st = m.st;
     const int64_t bh = int64_t(b) * m.H + h;
+    const bool worker = NT == THREADS || int(threadIdx.x) < THREADS;
     const int q = threadIdx.x % (kBlk / 4), ch = threadIdx.x / (kBlk / 4), c0 = ch * 8;
     const uint16_t* base = v + sv.in_off;
 
     float inv[8];
     if constexpr (FP8) {
-        __shared__ float samax[FOLD ? DP : 1];
         if constexpr (FOLD) {
             if (threadIdx.x < DP) {
                 const int nb = (N + kBlk - 1) / kBlk;
@@ -515,7 +491,7 @@ __global__ __launch_bounds__(2 * DP) void quant_v_kernel(const uint16_t* __restr
     for (int u = 0; u < 4; u++) {
         const int t = j * kBlk + 4 * q + u;
         r[u] = v8u16{0, 0, 0, 0, 0, 0, 0, 0};
-        if (t < N && c0 < D) {
+        if (worker && t < N && c0 < D) {
             const uint16_t* src = base + int64_t(t) * st.t + c0;
             if constexpr (VEC8) {
                 r[u] = *(const v8u16*)src;
@@ -525,31 +501,84 @@ __global__ __launch_bounds__(2 * DP) void quant_v_kernel(const uint16_t* __restr
             }
         }
     }
+    if (worker) {
 #pragma unroll
-    for (int e = 0; e < 8; e++) {
-        const int c = c0 + e;
-        uint8_t* row = tile + (c ^ ((c >> 3) & RMASK)) * ROWB;
-        float y[4];
+        for (int e = 0; e < 8; e++) {
+            const int c = c0 + e;
+            uint8_t* row = tile + (c ^ ((c >> 3) & RMASK)) * ROWB;
+            float y[4];
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const float x = in_to_f32<BF16>(r[u][e]);  // padding elements are +0
-            y[u] = FP8 ? fminf(fmaxf(x * inv[e], -448.0f), 448.0f) : fminf(fmaxf(x, -65504.0f), 65504.0f);
-        }
-        if constexpr (FP8) {
-            const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-            *(int*)(row + 4 * q) = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
-        } else {
-            *(uint2*)(row + 8 * q) = make_uint2(uint32_t(f32_to_f16_bits(y[0])) | (uint32_t(f32_to_f16_bits(y[1])) << 16),
-                                                uint32_t(f32_to_f16_bits(y[2])) | (uint32_t(f32_to_f16_bits(y[3])) << 16));
+            for (int u = 0; u < 4; u++) {
+                const float x = in_to_f32<BF16>(r[u][e]);  // padding elements are +0
+                y[u] = FP8 ? fminf(fmaxf(x * inv[e], -448.0f), 448.0f) : fminf(fmaxf(x, -65504.0f), 65504.0f);
+            }
+            if constexpr (FP8) {
+                const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+                *(int*)(row + 4 * q) = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+            } else {
+                auto h2 = [&](int u) {
+                    return uint32_t(f32_to_f16_bits(y[u])) | (uint32_t(f32_to_f16_bits(y[u + 1])) << 16);
+                };
+                *(uint2*)(row + 8 * q) = make_uint2(h2(0), h2(2));
+            }
         }
     }
     __syncthreads();
     constexpr int CPR = ROWB / 16;  // 16-byte chunks per row
     uint8_t* dst = (uint8_t*)vhat + (sv.slot0 + j) * int64_t(DP * ROWB);
-    for (int i = threadIdx.x; i < DP * CPR; i += THREADS) {
+    for (int i = threadIdx.x; i < DP * CPR; i += NT) {
         const int pr = i / CPR, k = i % CPR;
         const int c = pr ^ ((pr >> 3) & RMASK);
         *(uint4*)(dst + c * ROWB + 16 * k) = *(const uint4*)(tile + pr * ROWB + 16 * k);
+    }
+}
+
+template <bool BF16, int DP, bool VEC8, bool FP8, bool FOLD = false>
+__global__ __launch_bounds__(2 * DP) void quant_v_kernel(const uint16_t* __restrict__ v, SeqMap m, int D,
+                                                      const uint32_t* __restrict__ amax_bits,
+                                                      void* __restrict__ vhat, float* __restrict__ vscale,
+                                                      const float* __restrict__ vpart = nullptr) {
+    __shared__ __attribute__((aligned(16))) uint8_t tile[DP * kBlk * (FP8 ? 1 : 2)];
+    __shared__ float samax[FP8 && FOLD ? DP : 1];
+    v_block<BF16, DP, VEC8, FP8, FOLD, 2 * DP>(v, m, D, amax_bits, vhat, vscale, vpart, blockIdx.x, blockIdx.y,
+                                               blockIdx.z, tile, samax);
+}
+
+// Pass 1.  nq workgroups quantise four Q blocks each (number x of a (head, batch): x
+// + nq4 * (h + Hq * b)); nkv take one K/V block each (j + NB * (h + H_kv * b)).  The
+// two kinds are spread evenly over the grid, so Q's read-write stream and the K/V
+// read streams run side by side.  VCAST (FP16 P.V, head dims up to 128): nkv more
+// workgroups after those cast one V block each to the FP16 operand (quant_v_kernel's
+// FP16 arithmetic, which needs no statistics), so no launch of its own is needed.
+template <bool BF16, int DP, bool VEC8, bool VMAX, int QG, bool VCAST = false>
+__global__ __launch_bounds__(256) void qkv_pass1_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                        const uint16_t* __restrict__ v, SeqMap mq, SeqMap mk, int D,
+                                                        int nq, int nkv, int8_t* __restrict__ q_i8,
+                                                        float* __restrict__ q_scale, double* __restrict__ kpart,
+                                                        float* __restrict__ vpart, void* __restrict__ vhat = nullptr) {
+    static_assert(!VCAST || (!VMAX && 2 * DP <= 256), "the V cast: FP16 mode, head dims up to 128");
+    __shared__ __attribute__((aligned(16))) uint16_t tile[kBlk][DP];
+    __shared__ float red[VMAX ? 256 / (DP / 8) : 1][DP];
+    const int64_t wg = blockIdx.x, T = int64_t(nq) + nkv;
+    if constexpr (VCAST) {
+        if (wg >= T) {
+            const int r = int(wg - T);
+            const int j = r % mk.NB, h = (r / mk.NB) % mk.H, b = r / (mk.NB * mk.H);
+            v_block<BF16, DP, VEC8, false, false, 256>(v, mk, D, nullptr, vhat, nullptr, nullptr, j, h, b,
+                                                       (uint8_t*)&tile[0][0], nullptr);
+            return;
+        }
+    }
+    const int a0 = int(wg * nq / T), a1 = int((wg + 1) * nq / T);  // Q workgroups before wg, before wg + 1
+    if (a1 > a0) {
+        const int nq4 = (mq.NB + 3) / 4;
+        const int x = a0 % nq4, h = (a0 / nq4) % mq.H, b = a0 / (nq4 * mq.H);
+        const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+        quant_block_wave<BF16, DP, VEC8, false, QG>(q, mq, D, nullptr, q_i8, q_scale, x * 4 + wave, h, b, lane);
+    } else {
+        const int r = int(wg) - a1;
+        const int j = r % mk.NB, h = (r / mk.NB) % mk.H, b = r / (mk.NB * mk.H);
+        kv_stats_block<BF16, DP, VEC8, VMAX>(k, v, mk, D, kpart, vpart, j, h, b, tile, red);
     }
 }
 
@@ -631,12 +660,19 @@ hipError_t launch_qkv_t(const QuantQKArgs& a, const QuantVArgs& va, hipStream_t 
     uint32_t* amax = (uint32_t*)(ws + w.amax);
     const int nq = a.q != nullptr ? ((mq.NB + 3) / 4) * a.Hq * a.B : 0;  // sage_quant_kv: no Q
     const int nkv = mk.NB * a.Hkv * a.B;
+    // FP16 P.V at head dims up to 128: the V cast rides in pass 1 (one launch fewer)
+    constexpr bool kVCast = DP <= 128;
     if (mk.NB <= kFoldBlocks) {
-        // short sequences: pass 2 folded into the K and V launches (three launches)
+        // short sequences: pass 2 folded into the K and V launches (three launches, two
+        // in FP16 mode with the V cast in pass 1)
         if (va.fp8)
             qkv_pass1_kernel<BF16, DP, VEC8, true, QG><<<nq + nkv, 256, 0, s>>>(
                 (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)va.v, mq, mk, a.D, nq, nkv, a.q_i8,
                 a.q_scale, kpart, vpart);
+        else if constexpr (kVCast)
+            qkv_pass1_kernel<BF16, DP, VEC8, false, QG, true><<<nq + 2 * nkv, 256, 0, s>>>(
+                (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)va.v, mq, mk, a.D, nq, nkv, a.q_i8,
+                a.q_scale, kpart, nullptr, va.v_hat);
         else
             qkv_pass1_kernel<BF16, DP, VEC8, false, QG><<<nq + nkv, 256, 0, s>>>(
                 (const uint16_t*)a.q, (const uint16_t*)a.k, nullptr, mq, mk, a.D, nq, nkv, a.q_i8, a.q_scale, kpart,
@@ -646,7 +682,7 @@ hipError_t launch_qkv_t(const QuantQKArgs& a, const QuantVArgs& va, hipStream_t 
         if (va.fp8)
             quant_v_kernel<BF16, DP, VEC8, true, true><<<dim3(mk.NB, a.Hkv, a.B), DP * 2, 0, s>>>(
                 (const uint16_t*)va.v, mk, a.D, nullptr, va.v_hat, va.v_scale, vpart);
-        else
+        else if constexpr (!kVCast)
             quant_v_kernel<BF16, DP, VEC8, false><<<dim3(mk.NB, a.Hkv, a.B), DP * 2, 0, s>>>(
                 (const uint16_t*)va.v, mk, a.D, nullptr, va.v_hat, nullptr);
         return hipGetLastError();
@@ -658,9 +694,14 @@ hipError_t launch_qkv_t(const QuantQKArgs& a, const QuantVArgs& va, hipStream_t 
         qkv_pass2_kernel<DP, true><<<(a.B * a.Hkv * DP + 63) / 64, 64, 0, s>>>(kpart, vpart, mk, a.B, a.D, a.k_mean,
                                                                              amax);
     } else {
-        qkv_pass1_kernel<BF16, DP, VEC8, false, QG><<<nq + nkv, 256, 0, s>>>(
-            (const uint16_t*)a.q, (const uint16_t*)a.k, nullptr, mq, mk, a.D, nq, nkv, a.q_i8, a.q_scale, kpart,
-            nullptr);
+        if constexpr (kVCast)
+            qkv_pass1_kernel<BF16, DP, VEC8, false, QG, true><<<nq + 2 * nkv, 256, 0, s>>>(
+                (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)va.v, mq, mk, a.D, nq, nkv, a.q_i8,
+                a.q_scale, kpart, nullptr, va.v_hat);
+        else
+            qkv_pass1_kernel<BF16, DP, VEC8, false, QG><<<nq + nkv, 256, 0, s>>>(
+                (const uint16_t*)a.q, (const uint16_t*)a.k, nullptr, mq, mk, a.D, nq, nkv, a.q_i8, a.q_scale, kpart,
+                nullptr);
         qkv_pass2_kernel<DP, false><<<(a.B * a.Hkv * DP + 63) / 64, 64, 0, s>>>(kpart, nullptr, mk, a.B, a.D,
                                                                               a.k_mean, nullptr);
     }
@@ -669,7 +710,7 @@ hipError_t launch_qkv_t(const QuantQKArgs& a, const QuantVArgs& va, hipStream_t 
     if (va.fp8)
         quant_v_kernel<BF16, DP, VEC8, true><<<dim3(mk.NB, a.Hkv, a.B), DP * 2, 0, s>>>(
             (const uint16_t*)va.v, mk, a.D, amax, va.v_hat, va.v_scale);
-    else
+    else if constexpr (!kVCast)
         quant_v_kernel<BF16, DP, VEC8, false><<<dim3(mk.NB, a.Hkv, a.B), DP * 2, 0, s>>>(
             (const uint16_t*)va.v, mk, a.D, nullptr, va.v_hat, nullptr);
     return hipGetLastError();

@@ -164,9 +164,9 @@ size_t sage_quant_qkv_workspace_bytes(int B, int H_kv, int Nkv, int D, sage_pv p
 /*
  * sage_quant_qk and sage_quant_v in one call: the same outputs, bit for bit, in four
  * kernel launches instead of six or seven (Q quantisation and the K/V statistics
- * stream in one grid; then the K means and V maxima; then K and V quantisation).  With
- * FP16 P.V at head dims up to 128 the V cast runs in the first grid (three launches);
- * sequences of at most 32 blocks need one launch fewer still.
+ * stream in one grid; then the K means and V maxima; then K and V quantisation).  At
+ * head dims up to 128 it takes three: FP16 P.V casts V in the first grid, FP8 P.V writes
+ * the K and V codes in one grid.  Sequences of at most 32 blocks need one launch fewer.
  *   q, k, v, dtype, layout, shapes: as sage_quant_qk and sage_quant_v.
  *   Outputs: q_i8, q_scale, k_i8, k_scale, k_mean, v_hat, v_scale (v_scale only in
  *   FP8 mode, may be NULL otherwise).

@@ -455,7 +455,7 @@ __device__ __forceinline__ void v_block(const uint16_t* __restrict__ v, const Se
     constexpr int THREADS = CH * (kBlk / 4);  // one thread per (token quad, chunk)
     constexpr int ROWB = kBlk * ELT;          // bytes per channel row of the tile
     constexpr int RMASK = FP8 ? 3 : 1;
-    static_assert(NT == THREADS || (NT > THREADS && !FP8), "extra helper threads in FP16 mode only");
+    static_assert(NT >= THREADS, "one thread per (token quad, chunk) at least");
     const SeqView sv = seq_view(m, b, h);
     if (j * kBlk >= sv.n) return;  // the whole workgroup: past this sequence's end
     const int N = sv.n;
@@ -481,7 +481,7 @@ __device__ __forceinline__ void v_block(const uint16_t* __restrict__ v, const Se
         auto amax_of = [&](int c) { return FOLD ? samax[c] : __uint_as_float(amax_bits[bh * DP + c]); };
 #pragma unroll
         for (int e = 0; e < 8; e++) {
-            const float a = amax_of(c0 + e);
+            const float a = worker ? amax_of(c0 + e) : 0.0f;
             inv[e] = a > 0.0f ? 448.0f / a : 0.0f;
         }
         if (j == 0 && threadIdx.x < DP) vscale[bh * DP + threadIdx.x] = amax_of(threadIdx.x) / 448.0f;
@@ -611,6 +611,53 @@ __global__ __launch_bounds__(256) void quant_k_fold_kernel(const uint16_t* __res
     quant_block_wave<BF16, DP, VEC8, true, G, true>(k, m, D, smean, xq, scale, blockIdx.x * 4 + wave, h, b, lane);
 }
 
+// FP8 mode, head dims up to 128: the K codes and the V operand in one grid, once the K
+// means and V maxima exist (after pass 2, or folded from pass 1's partials for short
+// sequences).  The first nk workgroups take four K blocks each (quant_blocks_kernel /
+// quant_k_fold_kernel: x + nb4 * (h + H_kv * b)), the next ones one V block each
+// (quant_v_kernel: j + NB * (h + H_kv * b)); the same arithmetic, one launch instead
+// of two.
+template <bool BF16, int DP, bool VEC8, bool FOLD, int G>
+__global__ __launch_bounds__(256) void kv_codes_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                                       SeqMap m, int D, int nk, const double* __restrict__ kpart,
+                                                       float* __restrict__ mean, int8_t* __restrict__ xq,
+                                                       float* __restrict__ scale, const uint32_t* __restrict__ amax_bits,
+                                                       void* __restrict__ vhat, float* __restrict__ vscale,
+                                                       const float* __restrict__ vpart) {
+    static_assert(DP <= 128, "256 threads: one per (token quad, 8-channel chunk) of a V block");
+    __shared__ float smean[FOLD ? DP : 1];
+    __shared__ __attribute__((aligned(16))) uint8_t tile[DP * kBlk];
+    __shared__ float samax[FOLD ? DP : 1];
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int nb4 = (m.NB + 3) / 4;
+    if (int(blockIdx.x) < nk) {
+        const int r = blockIdx.x;
+        const int x = r % nb4, h = (r / nb4) % m.H, b = r / (nb4 * m.H);
+        if constexpr (FOLD) {
+            const SeqView sv = seq_view(m, b, h);
+            const int c = threadIdx.x;
+            if (c < D) {
+                const int nb = (sv.n + kBlk - 1) / kBlk;
+                const double* pp = kpart + sv.slot0 * D + c;
+                double sum = 0.0;
+#pragma unroll 16
+                for (int i = 0; i < nb; i++) sum += pp[int64_t(i) * D];
+                const float mu = sv.n > 0 ? float(sum / double(sv.n)) : 0.0f;
+                smean[c] = mu;
+                if (x == 0) mean[(int64_t(b) * m.H + h) * D + c] = mu;
+            }
+            __syncthreads();
+            quant_block_wave<BF16, DP, VEC8, true, G, true>(k, m, D, smean, xq, scale, x * 4 + wave, h, b, lane);
+        } else {
+            quant_block_wave<BF16, DP, VEC8, true, G>(k, m, D, mean, xq, scale, x * 4 + wave, h, b, lane);
+        }
+    } else {
+        const int r = int(blockIdx.x) - nk;
+        const int j = r % m.NB, h = (r / m.NB) % m.H, b = r / (m.NB * m.H);
+        v_block<BF16, DP, VEC8, true, FOLD, 256>(v, m, D, amax_bits, vhat, vscale, vpart, j, h, b, tile, samax);
+    }
+}
+
 // ------------------------------------------------------------------------------------------
 // Launchers
 namespace {
@@ -660,11 +707,12 @@ hipError_t launch_qkv_t(const QuantQKArgs& a, const QuantVArgs& va, hipStream_t 
     uint32_t* amax = (uint32_t*)(ws + w.amax);
     const int nq = a.q != nullptr ? ((mq.NB + 3) / 4) * a.Hq * a.B : 0;  // sage_quant_kv: no Q
     const int nkv = mk.NB * a.Hkv * a.B;
-    // FP16 P.V at head dims up to 128: the V cast rides in pass 1 (one launch fewer)
+    // head dims up to 128: FP16 P.V casts V in pass 1, FP8 P.V writes the K and V codes in
+    // one launch (one launch fewer either way)
     constexpr bool kVCast = DP <= 128;
     if (mk.NB <= kFoldBlocks) {
         // short sequences: pass 2 folded into the K and V launches (three launches, two
-        // in FP16 mode with the V cast in pass 1)
+        // at head dims up to 128)
         if (va.fp8)
             qkv_pass1_kernel<BF16, DP, VEC8, true, QG><<<nq + nkv, 256, 0, s>>>(
                 (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)va.v, mq, mk, a.D, nq, nkv, a.q_i8,
@@ -677,6 +725,15 @@ hipError_t launch_qkv_t(const QuantQKArgs& a, const QuantVArgs& va, hipStream_t 
             qkv_pass1_kernel<BF16, DP, VEC8, false, QG><<<nq + nkv, 256, 0, s>>>(
                 (const uint16_t*)a.q, (const uint16_t*)a.k, nullptr, mq, mk, a.D, nq, nkv, a.q_i8, a.q_scale, kpart,
                 nullptr);
+        if constexpr (kVCast) {
+            if (va.fp8) {  // K and V codes in one launch
+                const int nk = (mk.NB + 3) / 4 * a.Hkv * a.B;
+                kv_codes_kernel<BF16, DP, VEC8, true, KG><<<nk + nkv, 256, 0, s>>>(
+                    (const uint16_t*)a.k, (const uint16_t*)va.v, mk, a.D, nk, kpart, a.k_mean, a.k_i8, a.k_scale,
+                    nullptr, va.v_hat, va.v_scale, vpart);
+                return hipGetLastError();
+            }
+        }
         quant_k_fold_kernel<BF16, DP, VEC8, KG><<<dim3((mk.NB + 3) / 4, a.Hkv, a.B), 256, 0, s>>>(
             (const uint16_t*)a.k, mk, a.D, kpart, a.k_mean, a.k_i8, a.k_scale);
         if (va.fp8)
@@ -704,6 +761,15 @@ hipError_t launch_qkv_t(const QuantQKArgs& a, const QuantVArgs& va, hipStream_t 
                 nullptr);
         qkv_pass2_kernel<DP, false><<<(a.B * a.Hkv * DP + 63) / 64, 64, 0, s>>>(kpart, nullptr, mk, a.B, a.D,
                                                                               a.k_mean, nullptr);
+    }
+    if constexpr (kVCast) {
+        if (va.fp8) {  // K and V codes in one launch
+            const int nk = (mk.NB + 3) / 4 * a.Hkv * a.B;
+            kv_codes_kernel<BF16, DP, VEC8, false, KG><<<nk + nkv, 256, 0, s>>>(
+                (const uint16_t*)a.k, (const uint16_t*)va.v, mk, a.D, nk, nullptr, a.k_mean, a.k_i8, a.k_scale, amax,
+                va.v_hat, va.v_scale, nullptr);
+            return hipGetLastError();
+        }
     }
     quant_blocks_kernel<BF16, DP, VEC8, true, KG><<<dim3((mk.NB + 3) / 4, a.Hkv, a.B), 256, 0, s>>>(
         (const uint16_t*)a.k, mk, a.D, a.k_mean, a.k_i8, a.k_scale);

@@ -26,6 +26,8 @@
 #include "common.hpp"
 #include "internal.hpp"
 
+#include <utility>
+
 namespace sage {
 
 namespace {
@@ -133,6 +135,32 @@ struct MXParams {
 // instruction per pair)
 __device__ __forceinline__ float max3f(float a, float b, float c) {
     return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
+// f(integral_constant<0>) .. f(integral_constant<N - 1>): the byte selects of the scaled
+// matrix instruction are immediates, so loops that pick one exponent byte per step are
+// unrolled at compile time
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// NE exponent bytes (2, 4 or 8) from LDS as 32-bit words, byte n in byte n % 4 of word n / 4
+template <int NE>
+__device__ __forceinline__ void load_exp_words(const uint8_t* p, uint32_t (&w)[(NE + 3) / 4]) {
+    if constexpr (NE == 2) {
+        w[0] = *(const uint16_t*)p;
+    } else if constexpr (NE == 4) {
+        w[0] = *(const uint32_t*)p;
+    } else {
+        const uint2 x = *(const uint2*)p;
+        w[0] = x.x;
+        w[1] = x.y;
+    }
 }
 
 __device__ __forceinline__ int mx_exp_dev(float amax) {  // floor(log2 amax) - 2, at least -126
@@ -316,16 +344,20 @@ attn_mx_kernel(MXParams p) {
             const int row = mx_key_of_row(kt, i);
             const int sw = mx_kswz<DP>(row);
             const uint8_t* rbase = st + row * C::KROW;
-            const uint8_t* kerow = kex + row * C::NE;
+            // the row's exponent bytes 2 s + g (this lane half's blocks) moved to bytes 2 s:
+            // k-step s takes byte 2 (s % 2) of word s / 2 through the instruction's byte select
+            uint32_t kw[(C::NE + 3) / 4];
+            load_exp_words<C::NE>(kex + row * C::NE, kw);
 #pragma unroll
-            for (int s = 0; s < C::KS; s++) {
+            for (int u = 0; u < (C::NE + 3) / 4; u++) kw[u] >>= 8 * g;
+            static_for<C::KS>([&](auto sc) {
+                constexpr int s = decltype(sc)::value;
                 const v4i a = lds_read_16(rbase + 16 * ((2 * s + g) ^ sw));
-                const int ks = kerow[2 * s + g];
                 const v8i a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
                 const v8i b8 = {qf[s][0], qf[s][1], qf[s][2], qf[s][3], 0, 0, 0, 0};
-                S[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, s == 0 ? v16f{} : S[kt], 4, 4, 0,
-                                                                        ks, 0, qsc[s]);
-            }
+                S[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, s == 0 ? v16f{} : S[kt], 4, 4,
+                                                                        2 * (s % 2), int(kw[s / 2]), 0, qsc[s]);
+            });
         }
 
         // ---- online softmax; key of lane half g, tile kt, register r: 32 g + 16 kt + r
@@ -350,10 +382,14 @@ attn_mx_kernel(MXParams p) {
         }
         // the tile's row maximum in log2 units, rounded toward -inf, so that the fma
         // t = S c - m of the maximum is >= 0 and below one ulp of m: its p is 1
-        const float tr = halves_max(mx);
+        float tr;
+        {
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            tr = __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+        }
         float mt = tr * c;
         if (__builtin_fmaf(tr, c, -mt) < 0.0f) mt = __uint_as_float(__float_as_uint(mt) + (mt > 0.0f ? -1 : 1));
-        const float mnew = fmaxf(m, mt);
+        const float mnew = __builtin_elementwise_maximum(m, mt);  // both finite or -inf
         const float alpha = __builtin_amdgcn_exp2f(m - mnew);
         m = mnew;
         const int E = mx_exp_dev(__builtin_amdgcn_exp2f(__builtin_fmaf(mx, c, -mnew)));
@@ -369,7 +405,9 @@ attn_mx_kernel(MXParams p) {
                 q[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kt][r0 + e], c, -mnew));
                 acc[e & 3] = (w == 0 && e < 4) ? q[e] : acc[e & 3] + q[e];
             }
-            int x = 0;
+            // the first conversion writes byte 0; the other three overwrite the rest, so the
+            // register's previous contents (q[1]'s, dead after it) do not matter
+            int x = __float_as_int(q[1]);
             x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, q[0], q[1], X, 0);
             x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, q[2], q[3], X, 1);
             x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, q[4], q[5], X, 2);
@@ -385,14 +423,17 @@ attn_mx_kernel(MXParams p) {
         // ---- O^T += V^T P^T
         const v8i b8 = {pk[0], pk[1], pk[2], pk[3], 0, 0, 0, 0};
         const uint8_t* vst = st + C::KBYTES;
-#pragma unroll
-        for (int dt = 0; dt < C::DT; dt++) {
+        // this lane's V exponents, byte dt for channel tile dt, picked by the byte select
+        uint32_t vw[(C::NE + 3) / 4];
+        load_exp_words<C::NE>(vex + (g * 32 + i) * C::NE, vw);
+        static_for<C::DT>([&](auto dc) {
+            constexpr int dt = decltype(dc)::value;
             const int d = 32 * dt + i;
             const v4i a = lds_read_16(vst + d * C::VROW + 16 * (g ^ mx_vswz(d)));
-            const int vs = vex[(g * 32 + i) * C::NE + dt];
             const v8i a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
-            O[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, O[dt], 4, 4, 0, vs, 0, E + 127);
-        }
+            O[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, O[dt], 4, 4, dt % 4, int(vw[dt / 4]), 0,
+                                                                    E + 127);
+        });
     };
     int j = 0;
     for (; j < jm; j++) step(std::false_type{}, j);

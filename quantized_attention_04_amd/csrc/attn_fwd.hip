@@ -684,32 +684,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DP, FP8
     const bool empty = !(ltot > 0.0f);  // a query that sees no key: zeros
     const float inv = empty ? 0.0f : 1.0f / ltot;
     if (qidx >= Nq) return;
+    // FP8: the V scales ([B][H_kv][Dp], so every padded channel is in bounds) of a group of
+    // the lane's channels -- all 64 at head dims up to 128 -- loaded before the group's
+    // first store: interleaved with the stores (which might alias them) each load would
+    // wait out its own latency, 64 times per workgroup
+    constexpr int DTG = DP <= 128 ? C::DT : 2;  // 32-channel tiles per group
     const float* vsc = FP8 ? p.v_scale + (int64_t(b) * p.Hkv + hk) * DP : nullptr;
     const bool vec4 = (p.D & 3) == 0;
     const int64_t obase = p.qm.cu != nullptr ? qv.start * p.osq : b * p.osb;
     uint16_t* orow = (uint16_t*)p.out + obase + h * p.osh + qidx * p.osq;
 #pragma unroll
-    for (int dt = 0; dt < C::DT; dt++)
+    for (int dg = 0; dg < C::DT; dg += DTG) {
+        float vs[FP8 ? DTG : 1][4][4];
+        if constexpr (FP8) {
 #pragma unroll
-        for (int a4 = 0; a4 < 4; a4++) {
-            const int d0 = 32 * dt + 8 * a4 + 4 * g;
-            if (d0 >= p.D) continue;
-            uint16_t hv[4];
+            for (int u = 0; u < DTG; u++)
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                float o = O[dt][4 * a4 + e] * inv;
-                if constexpr (FP8) o = empty ? 0.0f : o * vsc[d0 + e];
-                hv[e] = OBF16 ? f32_to_bf16_bits(o) : f32_to_f16_bits(o);
-            }
-            if (vec4) {
-                *(uint2*)(orow + d0) = make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16),
-                                                  uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
-            } else {
+                for (int a4 = 0; a4 < 4; a4++)
 #pragma unroll
-                for (int e = 0; e < 4; e++)
-                    if (d0 + e < p.D) orow[d0 + e] = hv[e];
-            }
+                    for (int e = 0; e < 4; e++) vs[u][a4][e] = vsc[32 * (dg + u) + 8 * a4 + 4 * g + e];
         }
+#pragma unroll
+        for (int u = 0; u < DTG; u++)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; a4++) {
+                const int dt = dg + u, d0 = 32 * dt + 8 * a4 + 4 * g;
+                if (d0 >= p.D) continue;
+                uint16_t hv[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    float o = O[dt][4 * a4 + e] * inv;
+                    if constexpr (FP8) o = empty ? 0.0f : o * vs[u][a4][e];
+                    hv[e] = OBF16 ? f32_to_bf16_bits(o) : f32_to_f16_bits(o);
+                }
+                if (vec4) {
+                    *(uint2*)(orow + d0) = make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16),
+                                                      uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        if (d0 + e < p.D) orow[d0 + e] = hv[e];
+                }
+            }
+    }
 }
 
 // ---- combining key-range splits ----------------------------------------------------

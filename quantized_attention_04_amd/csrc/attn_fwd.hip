@@ -946,10 +946,9 @@ hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s) {
                       Cfg<256, true>::BM == BM && Cfg<256, false>::BM == BM,
                   "uniform BM");
     p.QT = (a.Nq + BM - 1) / BM;
-    {
-        const int dp = a.D <= 64 ? 64 : (a.D <= 128 ? 128 : 256);  // K^ int8 + V^ fp8 | fp16
-        p.grp = causal_head_group(int64_t((a.Nkv + kBlk - 1) / kBlk) * kBlk * dp * (a.fp8 ? 2 : 3));
-    }
+    const int dp = a.D <= 64 ? 64 : (a.D <= 128 ? 128 : 256);
+    const int64_t head_bytes = int64_t((a.Nkv + kBlk - 1) / kBlk) * kBlk * dp * (a.fp8 ? 2 : 3);  // K^ + V^
+    p.grp = causal_head_group(head_bytes, int64_t(a.B) * a.Hq * p.QT, int64_t(p.G) * p.QT);
     p.cscale = a.sm_scale * kLog2e;
     if (a.cu_q != nullptr) {  // packed (total, H_qo, D)
         p.osb = 0;
@@ -989,6 +988,7 @@ hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s) {
         p.part_ml = (float*)((char*)a.workspace + ws.ml);
         if (p.splits > 1) {
             const int n = nwg * p.splits;
+            p.grp = causal_head_group(head_bytes, n, int64_t(p.G) * p.QT * p.splits);
             if (a.D <= 64) return dispatch_split<64>(a, p, n, s);
             if (a.D <= 128) return dispatch_split<128>(a, p, n, s);
             return dispatch_split<256>(a, p, n, s);

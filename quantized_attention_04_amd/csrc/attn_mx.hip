@@ -497,7 +497,8 @@ hipError_t launch_mx_attn_t(const AttnMXArgs& a, hipStream_t s) {
     p.D = a.D;
     p.QT = (a.Nq + C::BM - 1) / C::BM;
     // K4 and V4 of one kv head: codes (DP / 2 bytes per token each) and exponents
-    p.grp = causal_head_group(int64_t((a.Nkv + kBlk - 1) / kBlk) * kBlk * (DP + DP / 16));
+    p.grp = causal_head_group(int64_t((a.Nkv + kBlk - 1) / kBlk) * kBlk * (DP + DP / 16),
+                              int64_t(p.QT) * a.Hq * a.B, int64_t(p.G) * p.QT);
     p.cscale = a.sm_scale * 1.4426950408889634f;
     p.q16 = (const uint16_t*)a.q16;
     p.qst = make_strides(a.q_nhd, a.Hq, a.Nq, a.D);

@@ -248,11 +248,20 @@ __device__ __forceinline__ void block_tile(int B, int Hkv, int G, int QT, int gr
     h = (bhk % Hkv) * G + hg;
 }
 
-// Host: kv heads per causal group -- as many (up to four) as have their K and V operands
-// (head_bytes each) within 8 MiB together: an XCD's 4 MB L2 plus its share of the MALL.
-inline int causal_head_group(int64_t head_bytes) {
+// Host: kv heads per causal group -- the largest power of two (up to 32) whose K and V
+// operands (head_bytes each) fit 8 MiB together (an XCD's 4 MB L2 plus its share of the
+// MALL).  Groups of more than four heads are taken only where their workgroups
+// (wg_per_kv_head each) fit one XCD's share of the grid: the hardware hands workgroup i
+// to XCD i % 8 and xcd_remap gives each XCD a contiguous range of logical ids, so such a
+// group's longest-first order then spans every head on its XCD (short sequences: 1K
+// causal 12% faster than with groups of four) instead of being cut across XCDs.
+inline int causal_head_group(int64_t head_bytes, int64_t wg_total, int64_t wg_per_kv_head) {
     const int64_t budget = int64_t(8) << 20;
-    return 4 * head_bytes <= budget ? 4 : (2 * head_bytes <= budget ? 2 : 1);
+    const int64_t per_xcd = wg_total / 8;
+    int grp = 1;
+    for (int g = 2; g <= 32; g *= 2)
+        if (g * head_bytes <= budget && (g <= 4 || g * wg_per_kv_head <= per_xcd)) grp = g;
+    return grp;
 }
 
 }  // namespace sage

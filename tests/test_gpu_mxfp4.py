@@ -36,6 +36,10 @@ CASES = [
     ("d256_causal", W("seq_sweep", B=1, Hq=4, Hkv=2, Nq=300, Nkv=300, D=256, causal=True, seed=47), "all"),
     # six kv heads in causal groups of four: a full group, then a partial one
     ("causal_head_groups_4_2", W("seq_sweep", B=3, Hq=4, Hkv=2, Nq=260, Nkv=260, causal=True, seed=55), "all"),
+    # groups of more than four kv heads, where a group fits one XCD's share of the grid:
+    # 68 kv heads (B34, H_kv 2, G 2, two query tiles: 4 workgroups per kv head, 272 in
+    # all, 34 per XCD) make groups of eight -- eight full ones, then a partial one of four
+    ("causal_head_groups_8_4", W("seq_sweep", B=34, Hq=4, Hkv=2, Nq=200, Nkv=200, causal=True, seed=155), 16),
     ("d200_gqa_nhd", W("gqa", B=1, Hq=4, Hkv=2, Nq=200, Nkv=250, D=200, causal=False, seed=48), "all"),
     ("d256_2k", W("seq_sweep", B=1, Hq=4, Hkv=4, Nq=2048, Nkv=2048, D=256, seed=49), 16),
 ]

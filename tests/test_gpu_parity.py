@@ -107,6 +107,10 @@ OUT_CASES = [
     ("causal_chunk_d96", W("gqa", B=1, Nq=200, Nkv=1500, D=96, causal=True, seed=21), "all"),
     # six kv heads in causal groups of four: a full group, then a partial one
     ("causal_head_groups_4_2", W("seq_sweep", B=3, Hq=4, Hkv=2, Nq=260, Nkv=260, causal=True, seed=27), "all"),
+    # groups of more than four kv heads, where a group fits one XCD's share of the grid:
+    # 68 kv heads (B34, H_kv 2, G 2, two query tiles: 4 workgroups per kv head, 272 in
+    # all, 34 per XCD) make groups of eight -- eight full ones, then a partial one of four
+    ("causal_head_groups_8_4", W("seq_sweep", B=34, Hq=4, Hkv=2, Nq=200, Nkv=200, causal=True, seed=127), 16),
     # head dims above 128: Dp = 256
     ("d256_fp8", W("seq_sweep", B=1, Hq=4, Hkv=2, Nq=300, Nkv=300, D=256, seed=22), "all"),
     ("d256_causal_fp16", W("llm_prefill", Hq=2, Hkv=2, Nq=300, Nkv=300, D=256, causal=True, seed=24), "all"),

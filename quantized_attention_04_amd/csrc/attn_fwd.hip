@@ -60,6 +60,9 @@ constexpr int kScoreBias = 0x3E22F983;
 // for t <= 0 even with a one-ulp exp2 error: FP8 P is produced directly as p * 448
 // (the e4m3 maximum), with a relative bias of about 6e-7.
 constexpr float kLog2_448 = 8.807354f;
+// FP16 P.V: how far (log2 units) the running maximum may rise above the reference
+// maximum before the accumulators are rescaled
+constexpr float kLazyLog2 = 8.0f;
 
 
 // Mode constants.  DP = padded head dim (64 | 128 | 256); FP8 = P.V in e4m3 (else fp16).
@@ -222,8 +225,10 @@ struct PPack<false> {
 // Online softmax step for one tile: updates m, l, returns alpha and writes P straight
 // into the P.V operand registers (FP8: e4m3 of p * 448; FP16: fp16 of p), four values
 // at a time, so no array of fp32 probabilities is ever live.  Masked keys get INT32_MIN
-// and p = 0.  The running max m = fp32(S32max c) is the scheme's fp32 score maximum, and
-// t = S32 c - m is formed with one rounding (fma) from the exact score, so p differs from
+// and p = 0.  m is the reference maximum: with FP8 P the running max fp32(S32max c), the
+// scheme's fp32 score maximum; with FP16 P the running max as it stood when it last rose
+// by more than kLazyLog2 (below).  t = S32 c - m is formed with one rounding (fma) from
+// the exact score, so with FP8 P, p differs from
 // the two-rounding fp32 evaluation fp32(2^fp32(fp32(S32 c) - m)) by at most half an ulp
 // of the score (plus half an ulp of m - log2 448 with FP8), a few 1e-5 relative at
 // |S2| < 2^10.  OFS (offset scores, head dims up to 128): S holds the bits of K0 + S32
@@ -279,7 +284,14 @@ __device__ __forceinline__ float softmax_tile(v16i (&S)[2], PPack<FP8>& pk, floa
         tmax = (MASK && mx == INT32_MIN) ? -1e30f : sf(mx) * c0s;
     }
     tmax = halves_max(tmax);
-    const float mnew = fmaxf(m, tmax);
+    float mnew = fmaxf(m, tmax);
+    // FP16 P: the reference maximum moves only when the tile's maximum exceeds it by more
+    // than kLazyLog2 (so p <= 2^kLazyLog2, far inside fp16's range, and the 64-accumulator
+    // rescale runs a few times per row instead of whenever the maximum creeps up).  P is
+    // then fp16(2^(S c - m)) against a reference up to kLazyLog2 below the running maximum:
+    // the same softmax, with fp16's relative rounding of p unchanged.  FP8 P must stay
+    // <= 1 (448 p <= 448), so FP8 keeps the running maximum itself.
+    if constexpr (!FP8) mnew = mnew > m + kLazyLog2 ? mnew : m;
     const float alpha = __builtin_amdgcn_exp2f(m - mnew);
     m = mnew;
     float negm = FP8 ? kLog2_448 - mnew : -mnew;

@@ -152,3 +152,43 @@ def test_two_level_split_against_chained(cid, w):
     rows = oracle.sample_rows(w.B, w.Hq, w.Nq, per_head=8, seed=4)
     check_output(case, b, rows, exact=False)
     check_output(case, a, rows, exact=False)
+
+
+def _case_with_inputs(w, q, k, v):
+    """A Case on given HND fp16 / bf16 host tensors instead of the workload's draw."""
+    case = Case(w)
+    case.q, case.k, case.v = q, k, v
+    case.dq, case.dk, case.dv = (t.to("cuda:0") for t in (q, k, v))
+    case.qf, case.kf, case.vf = (oracle.to_hnd_f32(t, w.layout) for t in (q, k, v))
+    case._oq = None
+    return case
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp16_rising_scores_move_the_reference_maximum(causal):
+    """FP16 P.V moves its reference maximum only when a tile's maximum exceeds it by more
+    than 8 (log2 units).  Keys whose scores rise steadily along the sequence (about 4.5 log2
+    units per 64-key tile, ~140 over the row) make it move every other tile, with p up to
+    ~2^8 in between.  The output follows the emulation (which rounds p against the exact
+    running maximum) at the usual bar, and exact attention as closely as the scheme does."""
+    w = W("llm_prefill", Hq=2, Hkv=2, Nq=320, Nkv=2048, causal=causal, seed=61)
+    g = torch.Generator().manual_seed(61)
+    D, N = w.D, w.Nkv
+    u = torch.ones(D)
+    q = (u + 0.3 * torch.randn(1, w.Hq, w.Nq, D, generator=g)).to(torch.float16)
+    ramp = torch.arange(N, dtype=torch.float32).view(1, 1, N, 1) / N
+    k = (8.8 * ramp * u + torch.randn(1, w.Hkv, N, D, generator=g)).to(torch.float16)
+    v = torch.randn(1, w.Hkv, N, D, generator=g).to(torch.float16)
+    case = _case_with_inputs(w, q, k, v)
+    qk, vq = case.gpu_quant(fused=True)
+    check_quant_bit_exact(case, qk, vq)
+    sm = sm_scale_of(D)
+    out = case.gpu_attn(qk, vq)
+    r = oracle.all_rows(w.B, w.Hq, w.Nq)
+    got = gather_rows(out, r, w.layout)
+    em, amb = oracle.attn_emulate(case.oq, causal, sm, r, with_ambiguity=True)
+    ex = oracle.attn_exact(case.qf, case.kf, case.vf, causal, sm, r)
+    compare_rows(got, em, amb, None, oracle.FP16, w.pv)
+    mg, me = metrics(got, ex), metrics(em, ex)
+    note(f"[metrics] rising causal={causal} gpu-vs-exact {mg} emulation-vs-exact {me}")
+    assert mg["rel_l1"] <= me["rel_l1"] * 1.02 + 1e-3 and mg["cos"] >= me["cos"] - 1e-4, (mg, me)

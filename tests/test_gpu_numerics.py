@@ -81,6 +81,31 @@ def test_huge_scores_fp8_stay_finite(D):
     assert m["cos"] >= 0.9999 and m["max_abs"] <= 5e-2, m
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_huge_scores_fp16(D, causal):
+    """The same scaled inputs with FP16 P.V, whose reference maximum moves only when a
+    tile's maximum exceeds it by more than 8 (log2): here it jumps by thousands, p stays
+    <= 2^8, every output is finite and follows the emulation at the usual bar."""
+    w = W("seq_sweep", B=1, Hq=4, Hkv=4, Nq=700, Nkv=700, D=D, qk_scale=40.0, seed=49, pv="fp16",
+          accum="fp32", causal=causal)
+    case = Case(w)
+    qk, vq = case.gpu_quant()
+    check_quant_bit_exact(case, qk, vq)
+    out = case.gpu_attn(qk, vq)
+    assert torch.isfinite(out.float()).all()
+    r = oracle.all_rows(w.B, w.Hq, w.Nq)
+    got = gather_rows(out, r, w.layout)
+    em = oracle.round_to(oracle.attn_emulate(case.oq, causal, sm_scale_of(D), r), oracle.BF16)
+    m = metrics(got, em)
+    note(f"[metrics] huge fp16 D{D} causal={causal} {m}")
+    # the emulation bar without the tie allowance (whose range these scores leave):
+    # max-abs 1e-2, or one bf16 ulp where that is wider (the rows are nearly one-hot, so
+    # |o| reaches the largest |v|, where both sides round independent fp32 values)
+    ulp = np.ldexp(1.0, np.floor(np.log2(np.maximum(np.abs(em), 1e-30))).astype(int) - 7)
+    assert m["cos"] >= 0.9999 and (np.abs(got - em) <= np.maximum(1e-2, ulp)).all(), m
+
+
 def _all_values(dtype: torch.dtype) -> torch.Tensor:
     """Every finite value of the dtype with |v| <= 448 (both zeros included)."""
     bits = torch.arange(65536, dtype=torch.int32).to(torch.int16)

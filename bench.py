@@ -600,6 +600,15 @@ def config_points(qa, torch, np, si, dev, args):
             quant()
             attn()
 
+        # without a split, sageattn's schedule: Q quantised in the attention prologue
+        if splits == 1:
+            kq, vq2 = qa.quant_kv(dk, dv, w.layout, w.pv, workspace=ws)
+            o2 = qa.attn_fwd_fused_q(dq, kq, vq2, w.layout, w.causal, None, w.accum)
+
+        def fstep():
+            qa.quant_kv(dk, dv, w.layout, w.pv, workspace=ws, out_k=kq, out_v=vq2)
+            qa.attn_fwd_fused_q(dq, kq, vq2, w.layout, w.causal, None, w.accum, out=o2)
+
         t_end = time.perf_counter() + 0.2
         while time.perf_counter() < t_end:
             step()
@@ -609,6 +618,7 @@ def config_points(qa, torch, np, si, dev, args):
         at = graph_ms(torch, attn)
         qt = graph_ms(torch, quant)
         stp = graph_ms(torch, step)
+        fst = graph_ms(torch, fstep) if splits == 1 else None
         ops = w.ops()
         Dp = qa.padded_dim(w.D)
         elems_q, elems_kv = w.B * w.Hq * w.Nq * w.D, w.B * w.Hkv * w.Nkv * w.D
@@ -620,11 +630,16 @@ def config_points(qa, torch, np, si, dev, args):
               "attn_frac_of_mode_ceiling": round(tops / (PEAK_TOPS * ceil), 4),
               "key_range_splits": splits, "quant_ms_median": round(qt, 4),
               "quant_GBps": round(qbytes / (qt * 1e-3) / 1e9, 1),
-              "step_ms": round(stp, 4), "step_tops": round(ops / (stp * 1e-3) / 1e12, 1)}
+              "step_ms": round(stp, 4), "step_tops": round(ops / (stp * 1e-3) / 1e12, 1),
+              "fused_q_step_ms": None if fst is None else round(fst, 4),
+              "fused_q_step_tops": None if fst is None else round(ops / (fst * 1e-3) / 1e12, 1)}
         log(f"[bench] {label}: attn {at * 1e3:.1f} us = {tops:.1f} TOPS ({100 * tops / PEAK_TOPS:.1f}% of peak, "
             f"{100 * pt['attn_frac_of_mode_ceiling']:.1f}% of the mode ceiling), splits {splits}, "
-            f"quant {qt * 1e3:.1f} us = {pt['quant_GBps']} GB/s")
+            f"quant {qt * 1e3:.1f} us = {pt['quant_GBps']} GB/s, step {stp * 1e3:.1f} us"
+            + ("" if fst is None else f", fused-Q step {fst * 1e3:.1f} us"))
         del dq, dk, dv, qk, vq, o, ws, aws
+        if splits == 1:
+            del kq, vq2, o2
         torch.cuda.empty_cache()
         if not args.no_cpu:
             pt["cpu_baseline"] = config_cpu_baseline(oracle, np, w, q, k, v, full=args.cpu_full)
